@@ -1,0 +1,194 @@
+/*
+ * qkmla.h -- C ABI of the MI355X (gfx950) QK-Normed MLA latent decode library.
+ *
+ * The method ("QK-Normed MLA: QK normalization without full key caching"):
+ * post-projection QK RMSNorm folded into MLA's absorbed latent decode path.
+ * RMSNorm(z) = z * gamma / S(z) splits into a static weight gamma and a dynamic
+ * scalar S(z) (technical summary, Methodology: RMSNorm decomposition).  The
+ * static weights gamma_q, gamma_k fold into the query-side latent projection
+ * (Methodology: Static Weight Absorption); the key statistic becomes one
+ * inverse-RMS scalar alpha^k per token and KV group, kept in a small cache
+ * beside the latent cache (Methodology: Dynamic Scalar Caching, Cache Layout).
+ * Decode logits are (q~ . c_t) * alpha^q * alpha^k (Methodology: decode-logit
+ * formula) plus a separately RMS-normed RoPE term (Methodology: Blockwise
+ * Normalization), then softmax, latent-weighted accumulation and the V
+ * up-projection.  The abstract states the absorbed form equals explicit
+ * post-projection QK RMSNorm in exact arithmetic.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument named as "device" is device memory (hipMalloc or a
+ *    torch CUDA tensor) on the current HIP device, 16-byte aligned, row-major
+ *    and contiguous.  "host" pointers are ordinary host memory.
+ *  - Every buffer and the stream are owned by the caller.  The library never
+ *    allocates, frees or synchronises; all work is enqueued on `stream`
+ *    (a hipStream_t passed as void*, NULL = the default stream) and the call
+ *    returns without waiting.
+ *  - Return value: a qkmla_status.  On a non-zero status nothing was enqueued;
+ *    qkmla_last_error() (thread-local) describes the failure.
+ *  - Data errors that only the device can see (a sequence length outside
+ *    [1, cache_capacity], an append position outside the cache) are reported by
+ *    OR-ing QKMLA_DEV_* bits into `*status` (device int32, may be NULL).  The
+ *    caller clears it.  The affected sequence gets no cache writes (append) or
+ *    an all-zero output with lse = -inf (decode).
+ *  - batch == 0 is a valid no-op returning QKMLA_OK.
+ *
+ * Readings of points the pages leave open (the oracle makes the same ones):
+ *  - S(z) = sqrt(mean(z^2) + eps), eps inside the square root.
+ *  - gamma_q, gamma_k are [head_dim] vectors shared by all heads and groups;
+ *    the RoPE part has its own gamma_q_rope, gamma_k_rope of [rope_dim].
+ *  - One RoPE key per token shared by all heads, RMS-normalised and then
+ *    rotated; RoPE rotates interleaved pairs (2i, 2i+1) by p*base^(-2i/rope_dim);
+ *    the key at cache row t has position t, the query position seq_len-1.
+ *  - logit = softmax_scale * (content + rope); the alpha factors scale only the
+ *    content term.  Head h belongs to KV group floor(h*G/H).
+ */
+#ifndef QKMLA_H_
+#define QKMLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKMLA_ABI_VERSION 1
+
+typedef enum {
+  QKMLA_OK = 0,
+  QKMLA_ERR_INVALID_ARG = 1,    /* null / misaligned pointer, bad sizes, H % G != 0, odd rope_dim */
+  QKMLA_ERR_UNSUPPORTED = 2,    /* valid but not compiled (see qkmla_config) */
+  QKMLA_ERR_WORKSPACE = 3,      /* workspace smaller than qkmla_decode_workspace_size() */
+  QKMLA_ERR_HIP = 4             /* a HIP launch failed; message from the HIP runtime */
+} qkmla_status;
+
+typedef enum { QKMLA_F32 = 0, QKMLA_BF16 = 1 } qkmla_dtype;
+
+/* Device-side data-error bits OR-ed into *status. */
+#define QKMLA_DEV_BAD_SEQ_LEN 1   /* decode: seq_len outside [1, cache_capacity] */
+#define QKMLA_DEV_BAD_POSITION 2  /* append: position < 0 or position + n_new > cache_capacity */
+
+/*
+ * Layer shape and mode.
+ *   n_heads H, n_groups G (H % G == 0), latent_rank r, head_dim d_c,
+ *   rope_dim d_r (even), v_head_dim d_v.
+ *   dtype: storage type of the latent and RoPE caches, queries, absorbed query
+ *     weights and W^UV.  The alpha cache, W^UK, all gammas and every output are
+ *     float32.  All arithmetic accumulates in float32.
+ *     QKMLA_F32: any shape with r <= 1024, d_c <= 1024, d_r <= 256, d_v <= 1024.
+ *     QKMLA_BF16: r = 512, d_r = 64, H a multiple of 32 up to 128, H/G = 16
+ *     (the DeepSeek-V3-like MLA layer); d_c, d_v <= 1024.
+ *   qk_norm: 1 = QK-Normed MLA; 0 = plain MLA (no gammas, no alpha, no RoPE
+ *     norm) -- the same kernels with the normalisation compiled out.
+ *   eps: RMSNorm epsilon (>= 0).
+ *   softmax_scale: tau; <= 0 selects 1/sqrt(d_c + d_r).
+ *   rope_base: RoPE base (> 0), e.g. 10000.
+ */
+typedef struct {
+  int32_t n_heads, n_groups, latent_rank, head_dim, rope_dim, v_head_dim;
+  int32_t dtype;
+  int32_t qk_norm;
+  float eps;
+  float softmax_scale;
+  float rope_base;
+} qkmla_config;
+
+/*
+ * Static weight absorption (Methodology: Static Weight Absorption).
+ *   w_uk     device float [G][r][d_c]   key up-projection W^UK (k_g = c W^UK_g)
+ *   gamma_q  device float [d_c]         query RMSNorm weight (ignored if !qk_norm)
+ *   gamma_k  device float [d_c]         key RMSNorm weight   (ignored if !qk_norm)
+ *   w_qabs   device dtype [G][r][d_c]   out: W~_g^T, element (g,i,j) =
+ *            gamma_q[j]*gamma_k[j]*W^UK[g][i][j] rounded to dtype (W^UK itself
+ *            if !qk_norm).  This is diag(gamma_q gamma_k)(W^UK_g)^T stored with
+ *            d_c innermost so the query projection q~ = q^C W~_g reads rows.
+ * One-time; off the per-step clock.
+ */
+int qkmla_absorb_weights(const qkmla_config* cfg, const float* w_uk, const float* gamma_q,
+                         const float* gamma_k, void* w_qabs, void* stream);
+
+/*
+ * Append n_new tokens to every sequence of the batch (Methodology: Dynamic
+ * Scalar Caching, Cache Layout, Blockwise Normalization).  For sequence b and
+ * i < n_new the row t = positions[b] + i of each cache is written:
+ *   latent_cache[b][t][:] = c_new[b][i][:]                       (copy)
+ *   alpha_cache[b][t][g]  = 1/sqrt(mean_j (c_new W^UK_g)_j^2 + eps) for each g,
+ *                           computed in float32 from the stored latent and
+ *                           float32 W^UK (only if qk_norm)
+ *   rope_cache[b][t][:]   = RoPE_t(k_rope_new * gamma_k_rope / S(k_rope_new))
+ *                           (without the norm if !qk_norm), rounded to dtype.
+ *   c_new          device dtype [B][n_new][r]
+ *   k_rope_new     device dtype [B][n_new][d_r]    raw RoPE key (before norm/RoPE)
+ *   w_uk           device float [G][r][d_c]        (unused if !qk_norm)
+ *   gamma_k_rope   device float [d_r]              (unused if !qk_norm)
+ *   positions      device int32 [B]                first cache row per sequence
+ *   cache_capacity L_cap: rows per sequence in each cache
+ *   latent_cache   device dtype [B][L_cap][r]
+ *   rope_cache     device dtype [B][L_cap][d_r]
+ *   alpha_cache    device float [B][L_cap][G]      (may be NULL if !qk_norm)
+ *   status         device int32, nullable: QKMLA_DEV_BAD_POSITION on a bad row
+ */
+int qkmla_append(const qkmla_config* cfg, int32_t batch, int32_t n_new, const void* c_new,
+                 const void* k_rope_new, const float* w_uk, const float* gamma_k_rope,
+                 const int32_t* positions, int32_t cache_capacity, void* latent_cache,
+                 void* rope_cache, float* alpha_cache, int32_t* status, void* stream);
+
+/*
+ * Bytes of device workspace qkmla_decode needs for this batch and length bound
+ * (query staging, split partials and plan data).  0 on invalid arguments.
+ */
+size_t qkmla_decode_workspace_size(const qkmla_config* cfg, int32_t batch, int32_t max_seq_len);
+
+/*
+ * One decode step (s_q = 1) over the latent, RoPE and alpha caches: split-KV
+ * flash-decoding.  Per sequence b (L_b = seq_lens[b]), head h, g = g(h):
+ *   alpha^q_h = 1/S(q_c[b][h]),  q~_h = q_c[b][h] W~_g,
+ *   q^R_h = RoPE_{L_b-1}(q_rope[b][h] * gamma_q_rope / S(q_rope[b][h])),
+ *   logit_t = tau * ((q~_h . c_t) alpha^q_h alpha_cache[b][t][g] + q^R_h . k^R_t),
+ *   p = softmax over t < L_b,
+ *   o_lat[b][h][:] = sum_t p_t c_t,  lse[b][h] = log sum_t exp(logit_t).
+ * (Plain MLA if !qk_norm: no alpha, no norms.)
+ *   q_c          device dtype [B][H][d_c]    content query (projected, before norm)
+ *   q_rope       device dtype [B][H][d_r]    RoPE query (before norm and RoPE)
+ *   w_qabs       device dtype [G][r][d_c]    from qkmla_absorb_weights
+ *   gamma_q_rope device float [d_r]          (unused if !qk_norm)
+ *   latent_cache, rope_cache, alpha_cache    as written by qkmla_append
+ *   seq_lens     device int32 [B]            L_b, valid range [1, L_cap]
+ *   cache_capacity L_cap;  max_seq_len: host upper bound on every L_b (<= L_cap)
+ *   workspace    device, >= qkmla_decode_workspace_size(cfg, batch, max_seq_len) bytes
+ *   o_lat        device float [B][H][r]      out
+ *   lse          device float [B][H]         out, nullable (natural log)
+ *   status       device int32, nullable      QKMLA_DEV_BAD_SEQ_LEN
+ */
+int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const void* q_rope,
+                 const void* w_qabs, const float* gamma_q_rope, const void* latent_cache,
+                 const void* rope_cache, const float* alpha_cache, const int32_t* seq_lens,
+                 int32_t cache_capacity, int32_t max_seq_len, void* workspace,
+                 size_t workspace_bytes, float* o_lat, float* lse, int32_t* status,
+                 void* stream);
+
+/*
+ * V up-projection: out[b][h][:] = o_lat[b][h][:] W^UV_{g(h)}.
+ *   o_lat device float [B][H][r];  w_uv device dtype [G][r][d_v];
+ *   out   device float [B][H][d_v].
+ */
+int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, const void* w_uv,
+                   float* out, void* stream);
+
+/*
+ * Host-only split planner (no device access; usable without a GPU).  For a
+ * decode of `batch` sequences bounded by max_seq_len on a device with n_cu
+ * compute units, returns the number of decode workgroups and the token tile.
+ */
+int qkmla_plan(const qkmla_config* cfg, int32_t batch, int32_t max_seq_len, int32_t n_cu,
+               int32_t* n_workgroups, int32_t* tile_tokens);
+
+const char* qkmla_status_string(int status);
+const char* qkmla_last_error(void);
+int qkmla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QKMLA_H_ */

@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the QK-Normed MLA decode step on one MI355X.
+
+One step = one qkmla_decode call (q-prep, split-KV decode, split merge) over
+the latent + RoPE + alpha caches of every sequence; the workload that also
+appends the new token in the step (batch 4 x 32k) includes that qkmla_append.
+Inputs are resident in HBM before timing starts; caches are rotated over
+enough copies that each step streams from HBM rather than the 256 MB
+memory-side cache.
+
+Prints ONE JSON line: value = algorithmic cache bytes per step / step time
+(GB/s) for the batch-16 x 4096 workload, with microseconds per step, the
+overhead against the same kernels with the normalisation compiled out (plain
+MLA), the hot kernel's roofline position, the fp64 oracle timed on the host,
+and the same figures for the 32k, 256k and ragged workloads under "sweep".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode µs/step + cache HBM GB/s at 4k–256k ctx; % overhead vs plain MLA"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_splitkv_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "mla_latent_decode_amd", "csrc", "decode_mfma.hip")
+
+
+def _lengths(w):
+    import numpy as np
+    if w.lengths:
+        return list(w.lengths)
+    rng = np.random.default_rng(1000 + w.config_id)
+    return [int(x) for x in rng.integers(w.ragged[0], w.ragged[1], size=w.batch, endpoint=True)]
+
+
+class Bench:
+    """Device state of one workload: weights, queries, rotated cache copies."""
+
+    def __init__(self, cid: int):
+        import torch
+        from mla_latent_decode_amd import ops
+        from mla_latent_decode_amd.inputs import WORKLOADS, device_cache_fill_source
+        from mla_latent_decode_amd.layout import cache_bytes_per_token, decode_flops_per_token
+        self.torch, self.ops = torch, ops
+        w = WORKLOADS[cid]
+        self.w, self.cid = w, cid
+        s = w.shape
+        self.lengths = _lengths(w)
+        B, L_cap = len(self.lengths), max(self.lengths)
+        self.B, self.L_cap = B, L_cap
+        self.cfg = ops.Config.from_shape(s)
+        self.cfg_plain = ops.Config.from_shape(s, qk_norm=False)
+        dev = "cuda"
+        g = torch.Generator(device=dev)
+        g.manual_seed(2000 + cid)
+        f32, dt = torch.float32, self.cfg.torch_dtype
+        r, dr, G, H = s.latent_rank, s.rope_dim, s.n_groups, s.n_heads
+        self.w_uk = (torch.randn((G, r, s.head_dim), generator=g, device=dev) / math.sqrt(r)).contiguous()
+        self.gq = torch.rand((s.head_dim,), generator=g, device=dev) + 0.5
+        self.gk = torch.rand((s.head_dim,), generator=g, device=dev) + 0.5
+        self.gqr = torch.rand((dr,), generator=g, device=dev) + 0.5
+        self.gkr = torch.rand((dr,), generator=g, device=dev) + 0.5
+        self.w_qabs = ops.absorb_weights(self.cfg, self.w_uk, self.gq, self.gk)
+        self.w_qabs_plain = ops.absorb_weights(self.cfg_plain, self.w_uk, self.gq, self.gk)
+        self.q_c = torch.randn((B, H, s.head_dim), generator=g, device=dev).to(dt)
+        self.q_rope = torch.randn((B, H, dr), generator=g, device=dev).to(dt)
+        lat = torch.zeros((B, L_cap, r), dtype=dt, device=dev)
+        rope = torch.zeros((B, L_cap, dr), dtype=dt, device=dev)
+        alpha = torch.zeros((B, L_cap, G), dtype=f32, device=dev)
+        self.status = torch.zeros((1,), dtype=torch.int32, device=dev)
+        for b, start, c, k in device_cache_fill_source(s, self.lengths, 3000 + cid, dev,
+                                                       w.row_scale_log10_clip):
+            if b is None:
+                pos = torch.full((B,), start, dtype=torch.int32, device=dev)
+                ops.append(self.cfg, c, k, self.w_uk, self.gkr, pos, lat, rope, alpha, self.status)
+            else:
+                pos = torch.full((1,), start, dtype=torch.int32, device=dev)
+                ops.append(self.cfg, c, k, self.w_uk, self.gkr, pos, lat[b:b + 1], rope[b:b + 1],
+                           alpha[b:b + 1], self.status)
+        torch.cuda.synchronize()
+        self.cache_bytes = lat.numel() * lat.element_size() + rope.numel() * rope.element_size() + \
+            alpha.numel() * 4
+        n_copies = max(1, math.ceil(2 * MALL_BYTES / self.cache_bytes))
+        self.copies = [(lat, rope, alpha)] + [(lat.clone(), rope.clone(), alpha.clone())
+                                              for _ in range(n_copies - 1)]
+        self.n_copies = n_copies
+        self.seq_lens = torch.tensor(self.lengths, dtype=torch.int32, device=dev)
+        ws = max(ops.decode_workspace_size(self.cfg, B, L_cap),
+                 ops.decode_workspace_size(self.cfg_plain, B, L_cap))
+        self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        self.o_lat = torch.empty((B, H, r), dtype=f32, device=dev)
+        self.lse = torch.empty((B, H), dtype=f32, device=dev)
+        self.tokens = sum(self.lengths)
+        self.bytes_qk = self.tokens * cache_bytes_per_token(s, True)
+        self.bytes_plain = self.tokens * cache_bytes_per_token(s, False)
+        self.flops = self.tokens * decode_flops_per_token(s)
+        if w.append_last:
+            self.step_c = torch.randn((B, 1, r), generator=g, device=dev).to(dt)
+            self.step_k = torch.randn((B, 1, dr), generator=g, device=dev).to(dt)
+            self.step_pos = torch.tensor([L - 1 for L in self.lengths], dtype=torch.int32, device=dev)
+        self.i = 0
+
+    def step(self, plain=False):
+        ops = self.ops
+        lat, rope, alpha = self.copies[self.i % self.n_copies]
+        self.i += 1
+        cfg = self.cfg_plain if plain else self.cfg
+        if self.w.append_last:
+            ops.append(cfg, self.step_c, self.step_k, self.w_uk, self.gkr, self.step_pos, lat, rope,
+                       alpha, self.status)
+        ops.decode(cfg, self.q_c, self.q_rope, self.w_qabs_plain if plain else self.w_qabs, self.gqr,
+                   lat, rope, alpha, self.seq_lens, self.L_cap, self.workspace, self.o_lat, self.lse,
+                   self.status)
+
+    def time_steps(self, steps, warmup, plain=False):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(plain)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.step(plain)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    def kernel_ms(self, steps, plain=False):
+        """Average duration of the split-KV kernel over `steps` steps (HIP events
+        recorded by the library around each launch on the launch stream)."""
+        self.ops.profile_begin()
+        for _ in range(steps):
+            self.step(plain)
+        ms, n = self.ops.profile_end()
+        return ms / max(n, 1)
+
+
+def _kernel_src_hash():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(workload_name):
+    """HBM bytes per launch of the split-KV kernel from committed rocprofv3 PMC
+    counters, if they were taken on the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload_name)
+    if not e or e.get("kernel_src_sha256_16") != _kernel_src_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def measure(cid, steps, warmup):
+    b = Bench(cid)
+    ms_qk, wall = b.time_steps(steps, warmup)
+    ms_plain, _ = b.time_steps(steps, warmup, plain=True)
+    k_ms = b.kernel_ms(steps)
+    k_ms_plain = b.kernel_ms(steps, plain=True)
+    us = ms_qk * 1e3
+    res = {
+        "workload": b.w.name,
+        "batch": b.B,
+        "context": b.lengths[0] if len(set(b.lengths)) == 1 else f"ragged sum={b.tokens}",
+        "us_per_step": round(us, 2),
+        "plain_us_per_step": round(ms_plain * 1e3, 2),
+        "overhead_vs_plain_pct": round(100.0 * (ms_qk / ms_plain - 1.0), 2),
+        "cache_GBps": round(b.bytes_qk / (ms_qk * 1e-3) / 1e9, 1),
+        "cache_frac_of_8TBps": round(b.bytes_qk / (ms_qk * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "splitkv_kernel_us": round(k_ms * 1e3, 2),
+        "splitkv_kernel_GBps": round(b.bytes_qk / (k_ms * 1e-3) / 1e9, 1),
+        "splitkv_kernel_plain_us": round(k_ms_plain * 1e3, 2),
+        "splitkv_overhead_vs_plain_pct": round(100.0 * (k_ms / k_ms_plain - 1.0), 2),
+        "mfma_TFLOPs": round(b.flops / (k_ms * 1e-3) / 1e12, 1),
+        "cache_copies_rotated": b.n_copies,
+    }
+    status = int(b.status.item())
+    if status:
+        raise RuntimeError(f"device status {status} during the benchmark")
+    return b, res, ms_qk, k_ms, wall
+
+
+def cpu_baseline(cid, budget_s=15.0):
+    """The fp64 oracle on the host: whole sequences of the same workload, one at
+    a time, until about `budget_s` seconds of CPU work; returns its cache GB/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from mla_latent_decode_amd.inputs import WORKLOADS, make_inputs
+    from mla_latent_decode_amd.layout import cache_bytes_per_token
+    w = WORKLOADS[cid]
+    lengths = _lengths(w)
+    done_tokens, elapsed, n = 0, 0.0, 0
+    for i, L in enumerate(lengths):
+        inp = make_inputs(w.shape, [L], seed=4000 + i, row_scale_log10_clip=w.row_scale_log10_clip)
+        t0 = time.perf_counter()
+        oracle.explicit_decode(inp.q_c, inp.q_rope, inp.latents, inp.k_rope_raw, inp.w_uk, inp.w_uv,
+                               inp.gamma_q, inp.gamma_k, inp.gamma_q_rope, inp.gamma_k_rope)
+        elapsed += time.perf_counter() - t0
+        done_tokens += L
+        n += 1
+        if elapsed >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    gbps = done_tokens * cache_bytes_per_token(w.shape, True) / elapsed / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {len(lengths)} sequences ({done_tokens} cached tokens) of the same "
+                      f"workload, fp64 explicit form, {elapsed:.1f} s",
+            "us_per_step_extrapolated": round(elapsed / done_tokens * sum(lengths) * 1e6, 1),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1, help="headline workload (1-4)")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path is a single-GPU kernel library)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    b, res, ms_qk, k_ms, _ = measure(args.workload, args.steps, args.warmup)
+    print(f"[bench] headline {res}", file=sys.stderr, flush=True)
+    achieved = b.bytes_qk / (k_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": res["cache_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_qk, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": res["workload"], "batch": b.B, "context": res["context"],
+                   "heads": b.w.shape.n_heads, "kv_groups": b.w.shape.n_groups,
+                   "latent_rank": b.w.shape.latent_rank, "rope_dim": b.w.shape.rope_dim,
+                   "caches": "bf16 latent + bf16 rope + fp32 alpha", "parallelism": "single GPU"},
+        "us_per_step": res["us_per_step"],
+        "plain_us_per_step": res["plain_us_per_step"],
+        "overhead_vs_plain_pct": res["overhead_vs_plain_pct"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": _traffic(res["workload"]),
+                     "kernel": "decode_mfma_kernel<true,4> (split-KV)",
+                     "kernel_us": res["splitkv_kernel_us"],
+                     "algorithmic_bytes_per_launch": b.bytes_qk,
+                     "mfma_TFLOPs": res["mfma_TFLOPs"],
+                     "mfma_frac": round(res["mfma_TFLOPs"] / BF16_PEAK_TFLOPS, 4)},
+        "headline": res,
+    }
+    del b
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        sweep = []
+        for cid in (2, 3, 4):
+            if cid == args.workload:
+                continue
+            _b, r, *_ = measure(cid, max(10, args.steps // 2), max(3, args.warmup // 2))
+            print(f"[bench] sweep {r}", file=sys.stderr, flush=True)
+            sweep.append(r)
+            del _b
+            torch.cuda.empty_cache()
+        line["sweep"] = sweep
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,8 +18,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every pointer argument named as "device" is device memory (hipMalloc or a
- *    torch CUDA tensor) on the current HIP device, 16-byte aligned, row-major
- *    and contiguous.  "host" pointers are ordinary host memory.
+ *    torch CUDA tensor) on the current HIP device, row-major and contiguous,
+ *    aligned to its element size.  qkmla_decode in bf16 additionally needs
+ *    16-byte alignment of q_c, q_rope, w_qabs, both caches and o_lat (rows are
+ *    read as 16-byte vectors); every workspace is 16-byte aligned.
  *  - Every buffer and the stream are owned by the caller.  The library never
  *    allocates, frees or synchronises; all work is enqueued on `stream`
  *    (a hipStream_t passed as void*, NULL = the default stream) and the call
@@ -77,8 +79,8 @@ typedef enum { QKMLA_F32 = 0, QKMLA_BF16 = 1 } qkmla_dtype;
  *     weights and W^UV.  The alpha cache, W^UK, all gammas and every output are
  *     float32.  All arithmetic accumulates in float32.
  *     QKMLA_F32: any shape with r <= 1024, d_c <= 1024, d_r <= 256, d_v <= 1024.
- *     QKMLA_BF16: r = 512, d_r = 64, H a multiple of 32 up to 128, H/G = 16
- *     (the DeepSeek-V3-like MLA layer); d_c, d_v <= 1024.
+ *     QKMLA_BF16: r = 512, d_r = 64, H in {32, 64, 128}, H/G = 16, d_c a
+ *     multiple of 32 (the DeepSeek-V3-like MLA layer); d_c, d_v <= 1024.
  *   qk_norm: 1 = QK-Normed MLA; 0 = plain MLA (no gammas, no alpha, no RoPE
  *     norm) -- the same kernels with the normalisation compiled out.
  *   eps: RMSNorm epsilon (>= 0).
@@ -183,6 +185,18 @@ int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, c
  */
 int qkmla_plan(const qkmla_config* cfg, int32_t batch, int32_t max_seq_len, int32_t n_cu,
                int32_t* n_workgroups, int32_t* tile_tokens);
+
+/*
+ * Measurement hook.  Between qkmla_profile_begin() and qkmla_profile_end(),
+ * every qkmla_decode call of this host thread records a HIP event pair on its
+ * stream around the launch of its split-KV kernel (the hot kernel).
+ * qkmla_profile_end() waits for the recorded events and returns the summed
+ * kernel time in milliseconds and the number of launches.  At most 4096
+ * launches are recorded per begin/end window; the events are created on first
+ * use and kept for the life of the process.
+ */
+int qkmla_profile_begin(void);
+int qkmla_profile_end(double* split_kv_ms_total, int32_t* launches);
 
 const char* qkmla_status_string(int status);
 const char* qkmla_last_error(void);

@@ -1,0 +1,325 @@
+// Host side of the C ABI declared in include/qkmla.h: argument validation,
+// the split planner, workspace layout and kernel dispatch.  Nothing here
+// touches the GPU until a launcher is called, so validation errors and the
+// planner can be exercised without a device.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "qkmla_internal.h"
+
+namespace qkmla {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return QKMLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Validate the config and fill the normalised form.
+int check_cfg(const qkmla_config* cfg, Cfg* out) {
+  if (!cfg) return fail(QKMLA_ERR_INVALID_ARG, "cfg is NULL");
+  const qkmla_config& c = *cfg;
+  if (c.n_heads <= 0 || c.n_groups <= 0 || c.latent_rank <= 0 || c.head_dim <= 0 ||
+      c.rope_dim <= 0 || c.v_head_dim <= 0)
+    return fail(QKMLA_ERR_INVALID_ARG, "all dimensions must be positive");
+  if (c.n_heads % c.n_groups != 0)
+    return fail(QKMLA_ERR_INVALID_ARG, "n_heads (%d) must be a multiple of n_groups (%d)",
+                c.n_heads, c.n_groups);
+  if (c.rope_dim % 2 != 0) return fail(QKMLA_ERR_INVALID_ARG, "rope_dim must be even");
+  if (c.dtype != QKMLA_F32 && c.dtype != QKMLA_BF16)
+    return fail(QKMLA_ERR_INVALID_ARG, "unknown dtype %d", c.dtype);
+  if (c.qk_norm != 0 && c.qk_norm != 1) return fail(QKMLA_ERR_INVALID_ARG, "qk_norm must be 0 or 1");
+  if (!(c.eps >= 0.f) || !std::isfinite(c.eps)) return fail(QKMLA_ERR_INVALID_ARG, "eps must be >= 0");
+  if (!(c.rope_base > 0.f) || !std::isfinite(c.rope_base))
+    return fail(QKMLA_ERR_INVALID_ARG, "rope_base must be > 0");
+  if (!std::isfinite(c.softmax_scale)) return fail(QKMLA_ERR_INVALID_ARG, "softmax_scale not finite");
+  if (c.latent_rank > 1024 || c.head_dim > 1024 || c.v_head_dim > 1024 || c.rope_dim > 256)
+    return fail(QKMLA_ERR_UNSUPPORTED, "dimension above the compiled limits (r, d_c, d_v <= 1024, d_r <= 256)");
+  if (c.dtype == QKMLA_BF16) {
+    const int hpg = c.n_heads / c.n_groups;
+    const bool h_ok = c.n_heads == 32 || c.n_heads == 64 || c.n_heads == 128;
+    if (c.latent_rank != 512 || c.rope_dim != 64 || !h_ok || hpg != 16 || c.head_dim % 32 != 0)
+      return fail(QKMLA_ERR_UNSUPPORTED,
+                  "bf16 path is compiled for r=512, d_r=64, H in {32,64,128}, H/G=16, d_c%%32==0 "
+                  "(got r=%d d_r=%d H=%d G=%d d_c=%d)",
+                  c.latent_rank, c.rope_dim, c.n_heads, c.n_groups, c.head_dim);
+  }
+  out->H = c.n_heads;
+  out->G = c.n_groups;
+  out->r = c.latent_rank;
+  out->dc = c.head_dim;
+  out->dr = c.rope_dim;
+  out->dv = c.v_head_dim;
+  out->dtype = c.dtype;
+  out->qk_norm = c.qk_norm;
+  out->eps = c.eps;
+  out->tau = c.softmax_scale > 0.f ? c.softmax_scale
+                                   : (float)(1.0 / std::sqrt((double)(c.head_dim + c.rope_dim)));
+  out->base = c.rope_base;
+  out->hpg = c.n_heads / c.n_groups;
+  return QKMLA_OK;
+}
+
+size_t elem_size(const Cfg& c) { return c.dtype == QKMLA_BF16 ? 2 : 4; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+int plan_n_wg(const Cfg& c, int batch, int max_seq_len, int n_cu) {
+  const int64_t tiles_bound = (int64_t)batch * ((max_seq_len + kTile - 1) / kTile);
+  int forced = env_int("QKMLA_NUM_WG", 0);
+  int64_t n = forced > 0 ? forced : n_cu;
+  if (n > tiles_bound) n = tiles_bound;
+  if (n < 1) n = 1;
+  return (int)n;
+}
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// Measurement hook state (per host thread).
+struct KernelTimer {
+  bool on = false;
+  int n = 0;
+  hipEvent_t ev[2][4096];
+  int created = 0;
+};
+thread_local KernelTimer g_timer;
+
+hipError_t timer_record(hipStream_t s, int which) {
+  KernelTimer& t = g_timer;
+  if (!t.on || t.n >= 4096) return hipSuccess;
+  if (t.n >= t.created) {
+    hipError_t e = hipEventCreate(&t.ev[0][t.n]);
+    if (e == hipSuccess) e = hipEventCreate(&t.ev[1][t.n]);
+    if (e != hipSuccess) return e;
+    t.created = t.n + 1;
+  }
+  hipError_t e = hipEventRecord(t.ev[which][t.n], s);
+  if (which == 1) ++t.n;
+  return e;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QKMLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+WsLayout ws_layout(const Cfg& c, int batch, int n_wg) {
+  WsLayout w;
+  const size_t es = elem_size(c);
+  size_t off = 0;
+  w.q_tilde = off;
+  off = align256(off + (size_t)batch * c.H * c.r * es);
+  w.alpha_q = off;
+  off = align256(off + (size_t)batch * c.H * 4);
+  w.q_rope = off;
+  off = align256(off + (size_t)batch * c.H * c.dr * es);
+  w.partials = off;
+  if (c.dtype == QKMLA_BF16) off = align256(off + (size_t)n_wg * kSlotsPerWg * c.H * (c.r + 2) * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace qkmla
+
+using namespace qkmla;
+
+extern "C" {
+
+int qkmla_abi_version(void) { return QKMLA_ABI_VERSION; }
+
+int qkmla_profile_begin(void) {
+  g_timer.on = true;
+  g_timer.n = 0;
+  return ok();
+}
+
+int qkmla_profile_end(double* split_kv_ms_total, int32_t* launches) {
+  KernelTimer& t = g_timer;
+  t.on = false;
+  double total = 0.0;
+  for (int i = 0; i < t.n; ++i) {
+    hipError_t e = hipEventSynchronize(t.ev[1][i]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.ev[0][i], t.ev[1][i]);
+    if (e != hipSuccess) return hip_status(e, "profile_end");
+    total += ms;
+  }
+  if (split_kv_ms_total) *split_kv_ms_total = total;
+  if (launches) *launches = t.n;
+  t.n = 0;
+  return ok();
+}
+
+const char* qkmla_last_error(void) { return g_err; }
+
+const char* qkmla_status_string(int status) {
+  switch (status) {
+    case QKMLA_OK: return "ok";
+    case QKMLA_ERR_INVALID_ARG: return "invalid argument";
+    case QKMLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QKMLA_ERR_WORKSPACE: return "workspace too small";
+    case QKMLA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int qkmla_plan(const qkmla_config* cfg, int32_t batch, int32_t max_seq_len, int32_t n_cu,
+               int32_t* n_workgroups, int32_t* tile_tokens) {
+  Cfg c;
+  int st = check_cfg(cfg, &c);
+  if (st) return st;
+  if (batch < 0 || max_seq_len < 1 || n_cu < 1 || !n_workgroups || !tile_tokens)
+    return fail(QKMLA_ERR_INVALID_ARG, "bad plan arguments");
+  *tile_tokens = kTile;
+  *n_workgroups = batch == 0 ? 0 : plan_n_wg(c, batch, max_seq_len, n_cu);
+  return ok();
+}
+
+int qkmla_absorb_weights(const qkmla_config* cfg, const float* w_uk, const float* gamma_q,
+                         const float* gamma_k, void* w_qabs, void* stream) {
+  Cfg c;
+  int st = check_cfg(cfg, &c);
+  if (st) return st;
+  if (!w_uk || !w_qabs || (c.qk_norm && (!gamma_q || !gamma_k)))
+    return fail(QKMLA_ERR_INVALID_ARG, "absorb: NULL pointer");
+  if (!aligned(w_uk, 4) || !aligned(w_qabs, elem_size(c)))
+    return fail(QKMLA_ERR_INVALID_ARG, "absorb: pointers must be aligned to their element size");
+  return hip_status(launch_absorb(c, w_uk, gamma_q, gamma_k, w_qabs, as_stream(stream)), "absorb");
+}
+
+int qkmla_append(const qkmla_config* cfg, int32_t batch, int32_t n_new, const void* c_new,
+                 const void* k_rope_new, const float* w_uk, const float* gamma_k_rope,
+                 const int32_t* positions, int32_t cache_capacity, void* latent_cache,
+                 void* rope_cache, float* alpha_cache, int32_t* status, void* stream) {
+  Cfg c;
+  int st = check_cfg(cfg, &c);
+  if (st) return st;
+  if (batch < 0 || n_new < 0 || cache_capacity < 1)
+    return fail(QKMLA_ERR_INVALID_ARG, "append: batch/n_new must be >= 0, cache_capacity >= 1");
+  if (batch == 0 || n_new == 0) return ok();
+  if ((int64_t)batch * n_new > (int64_t)1 << 30)
+    return fail(QKMLA_ERR_UNSUPPORTED, "append: too many tokens in one call");
+  if (!c_new || !k_rope_new || !positions || !latent_cache || !rope_cache ||
+      (c.qk_norm && (!w_uk || !gamma_k_rope || !alpha_cache)))
+    return fail(QKMLA_ERR_INVALID_ARG, "append: NULL pointer");
+  const size_t es = elem_size(c);
+  if (!aligned(c_new, es) || !aligned(k_rope_new, es) || !aligned(latent_cache, es) ||
+      !aligned(rope_cache, es) || (alpha_cache && !aligned(alpha_cache, 4)) ||
+      (w_uk && !aligned(w_uk, 4)))
+    return fail(QKMLA_ERR_INVALID_ARG, "append: pointers must be aligned to their element size");
+  return hip_status(launch_append(c, batch, n_new, c_new, k_rope_new, w_uk, gamma_k_rope, positions,
+                                  cache_capacity, latent_cache, rope_cache, alpha_cache, status,
+                                  as_stream(stream)),
+                    "append");
+}
+
+size_t qkmla_decode_workspace_size(const qkmla_config* cfg, int32_t batch, int32_t max_seq_len) {
+  Cfg c;
+  if (check_cfg(cfg, &c)) return 0;
+  if (batch < 0 || max_seq_len < 1) {
+    fail(QKMLA_ERR_INVALID_ARG, "workspace size: batch >= 0 and max_seq_len >= 1 required");
+    return 0;
+  }
+  if (batch == 0) return 256;
+  const int n_wg = plan_n_wg(c, batch, max_seq_len, device_cu_count());
+  return ws_layout(c, batch, n_wg).total;
+}
+
+int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const void* q_rope,
+                 const void* w_qabs, const float* gamma_q_rope, const void* latent_cache,
+                 const void* rope_cache, const float* alpha_cache, const int32_t* seq_lens,
+                 int32_t cache_capacity, int32_t max_seq_len, void* workspace,
+                 size_t workspace_bytes, float* o_lat, float* lse, int32_t* status,
+                 void* stream) {
+  Cfg c;
+  int st = check_cfg(cfg, &c);
+  if (st) return st;
+  if (batch < 0 || cache_capacity < 1 || max_seq_len < 1 || max_seq_len > cache_capacity)
+    return fail(QKMLA_ERR_INVALID_ARG,
+                "decode: need batch >= 0 and 1 <= max_seq_len (%d) <= cache_capacity (%d)",
+                max_seq_len, cache_capacity);
+  if (batch == 0) return ok();
+  if (batch > 4096) return fail(QKMLA_ERR_UNSUPPORTED, "decode: batch above 4096");
+  if (!q_c || !q_rope || !w_qabs || !latent_cache || !rope_cache || !seq_lens || !workspace ||
+      !o_lat || (c.qk_norm && (!gamma_q_rope || !alpha_cache)))
+    return fail(QKMLA_ERR_INVALID_ARG, "decode: NULL pointer");
+  // The bf16 path reads queries, weights and cache rows as 16-byte vectors.
+  const size_t va = c.dtype == QKMLA_BF16 ? 16 : 4;
+  if (!aligned(q_c, va) || !aligned(q_rope, va) || !aligned(w_qabs, va) ||
+      !aligned(latent_cache, va) || !aligned(rope_cache, va) ||
+      (alpha_cache && !aligned(alpha_cache, 4)) || !aligned16(workspace) || !aligned(o_lat, va) ||
+      (lse && !aligned(lse, 4)) || !aligned(seq_lens, 4))
+    return fail(QKMLA_ERR_INVALID_ARG,
+                "decode: pointers must be %zu-byte aligned (alpha, lse, seq_lens: 4; workspace: 16)", va);
+  hipStream_t s = as_stream(stream);
+  const int n_wg = plan_n_wg(c, batch, max_seq_len, device_cu_count());
+  const WsLayout ws = ws_layout(c, batch, n_wg);
+  if (workspace_bytes < ws.total)
+    return fail(QKMLA_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
+                ws.total);
+  hipError_t e = launch_qprep(c, batch, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens,
+                              cache_capacity, ws, workspace, status, s);
+  if (e != hipSuccess) return hip_status(e, "decode/qprep");
+  if (c.dtype == QKMLA_BF16) {
+    const bool timed = g_timer.on && g_timer.n < 4096;
+    if (timed && (e = timer_record(s, 0)) != hipSuccess) return hip_status(e, "decode/timer");
+    e = launch_decode_mfma(c, batch, seq_lens, cache_capacity, latent_cache, rope_cache,
+                           alpha_cache, ws, workspace, n_wg, o_lat, lse, s);
+    if (e != hipSuccess) return hip_status(e, "decode/splitkv");
+    if (timed && (e = timer_record(s, 1)) != hipSuccess) return hip_status(e, "decode/timer");
+    e = launch_merge(c, batch, seq_lens, cache_capacity, ws, workspace, n_wg, o_lat, lse, s);
+    if (e != hipSuccess) return hip_status(e, "decode/merge");
+  } else {
+    e = launch_decode_generic(c, batch, seq_lens, cache_capacity, latent_cache, rope_cache,
+                              alpha_cache, ws, workspace, o_lat, lse, s);
+    if (e != hipSuccess) return hip_status(e, "decode/generic");
+  }
+  return ok();
+}
+
+int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, const void* w_uv,
+                   float* out, void* stream) {
+  Cfg c;
+  int st = check_cfg(cfg, &c);
+  if (st) return st;
+  if (batch < 0) return fail(QKMLA_ERR_INVALID_ARG, "out_proj: batch must be >= 0");
+  if (batch == 0) return ok();
+  if (!o_lat || !w_uv || !out) return fail(QKMLA_ERR_INVALID_ARG, "out_proj: NULL pointer");
+  if (!aligned(o_lat, 4) || !aligned(w_uv, elem_size(c)) || !aligned(out, 4))
+    return fail(QKMLA_ERR_INVALID_ARG, "out_proj: pointers must be aligned to their element size");
+  return hip_status(launch_out_proj(c, batch, o_lat, w_uv, out, as_stream(stream)), "out_proj");
+}
+
+}  // extern "C"

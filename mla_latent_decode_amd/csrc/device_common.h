@@ -1,0 +1,55 @@
+// Device helpers shared by the HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkmla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define QK_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define QK_GLB(T, p) ((__attribute__((address_space(1))) T*)(p))
+
+// Storage element <-> float.  bf16 is kept as raw 16-bit words in memory.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+// Round to nearest, ties to even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ static void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ static void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// RoPE angle p * base^(-2i/d) evaluated in double so that positions up to
+// 2^18 keep full float accuracy in cos/sin; returns (cos, sin) as floats.
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, float base, float* c,
+                                             float* s) {
+  double inv = pow((double)base, -2.0 * (double)i / (double)d);
+  double ang = (double)pos * inv;
+  *c = (float)cos(ang);
+  *s = (float)sin(ang);
+}
+
+// Sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace qkmla

@@ -1,0 +1,66 @@
+// Internal declarations shared by the host library and the HIP kernels.
+// Everything here targets gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qkmla.h"
+
+namespace qkmla {
+
+// Normalised layer description used by every launcher.
+struct Cfg {
+  int H, G, r, dc, dr, dv;
+  int dtype;     // QKMLA_F32 / QKMLA_BF16
+  int qk_norm;
+  float eps;
+  float tau;     // softmax scale (already defaulted)
+  float base;    // RoPE base
+  int hpg;       // heads per group
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Token tile of the bf16 MFMA decode (rows staged in LDS per step).
+constexpr int kTile = 32;
+// Partial slots per decode workgroup (first and last sequence segment).
+constexpr int kSlotsPerWg = 2;
+
+// ---- workspace layout of the bf16 MFMA decode ------------------------------
+struct WsLayout {
+  size_t q_tilde;    // bf16 [B][H][r]
+  size_t alpha_q;    // f32  [B][H]   (tau*log2e folded in)
+  size_t q_rope;     // bf16 / f32 [B][H][d_r] (normalised, rotated, tau*log2e folded in)
+  size_t partials;   // f32  [n_wg][kSlotsPerWg][H][r+2]  (m[H], l[H], O[H][r])
+  size_t total;
+};
+WsLayout ws_layout(const Cfg& c, int batch, int n_wg);
+
+// ---- launchers (each enqueues on `stream`; returns the launch error) -------
+hipError_t launch_absorb(const Cfg& c, const float* w_uk, const float* gq, const float* gk,
+                         void* w_qabs, hipStream_t s);
+hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
+                         const void* k_rope_new, const float* w_uk, const float* gkr,
+                         const int32_t* positions, int L_cap, void* lat, void* rope, float* alpha,
+                         int32_t* status, hipStream_t s);
+hipError_t launch_qprep(const Cfg& c, int batch, const void* q_c, const void* q_rope,
+                        const void* w_qabs, const float* gqr, const int32_t* seq_lens, int L_cap,
+                        const WsLayout& ws, void* workspace, int32_t* status, hipStream_t s);
+hipError_t launch_decode_mfma(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
+                              const void* lat, const void* rope, const float* alpha,
+                              const WsLayout& ws, void* workspace, int n_wg, float* o_lat,
+                              float* lse, hipStream_t s);
+hipError_t launch_merge(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
+                        const WsLayout& ws, void* workspace, int n_wg, float* o_lat, float* lse,
+                        hipStream_t s);
+hipError_t launch_decode_generic(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
+                                 const void* lat, const void* rope, const float* alpha,
+                                 const WsLayout& ws, void* workspace, float* o_lat, float* lse,
+                                 hipStream_t s);
+hipError_t launch_out_proj(const Cfg& c, int batch, const float* o_lat, const void* w_uv,
+                           float* out, hipStream_t s);
+
+}  // namespace qkmla

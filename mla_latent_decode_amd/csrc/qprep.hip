@@ -1,0 +1,155 @@
+// Query preparation, the first kernel of a decode step.
+//
+// Per sequence b and head h (g = g(h), L_b = seq_lens[b]):
+//   alpha^q_h = 1/S(q^C_h)                       (query-side dynamic scalar)
+//   q~_h      = q^C_h W~_g                       (gammas already absorbed in W~)
+//   q^R_h     = RoPE_{L_b-1}(RMSNorm_{gamma_q_rope}(q^R_h))
+// ("QK-Normed MLA: QK normalization without full key caching", technical
+// summary, Methodology: Static Weight Absorption, the decode-logit formula and
+// Blockwise Normalization).  tau*log2(e) is folded into alpha^q and q^R so the
+// decode kernel works in the exp2 domain.  In plain mode alpha^q = tau*log2(e)
+// and q^R is only rotated.
+#include "device_common.h"
+#include "qkmla_internal.h"
+
+namespace qkmla {
+
+// Shared epilogue: alpha^q and the RoPE query of head h.  Executed by one
+// wavefront per head (lane-strided over dims).
+template <typename TIn, typename TOut>
+__device__ void prep_scalar_and_rope(const TIn* qc, const TIn* qr, const float* gqr, int dc,
+                                     int dr, float eps, float tau, float base, int qk_norm,
+                                     int pos, float* alpha_q_out, TOut* qr_out) {
+  const int lane = threadIdx.x & 63;
+  const float sl = tau * kLog2e;
+  float ss = 0.f;
+  if (qk_norm) {
+    for (int e = lane; e < dc; e += 64) {
+      float v = Elem<TIn>::load(qc, e);
+      ss += v * v;
+    }
+    ss = wave_sum(ss);
+  }
+  float aq = qk_norm ? 1.0f / sqrtf(ss / (float)dc + eps) : 1.0f;
+  if (lane == 0) *alpha_q_out = aq * sl;
+  float rs = 0.f;
+  if (qk_norm) {
+    for (int e = lane; e < dr; e += 64) {
+      float v = Elem<TIn>::load(qr, e);
+      rs += v * v;
+    }
+    rs = wave_sum(rs);
+  }
+  float rscale = qk_norm ? 1.0f / sqrtf(rs / (float)dr + eps) : 1.0f;
+  for (int pi = lane; pi < dr / 2; pi += 64) {
+    float x0 = Elem<TIn>::load(qr, 2 * pi), x1 = Elem<TIn>::load(qr, 2 * pi + 1);
+    if (qk_norm) {
+      x0 *= rscale * gqr[2 * pi];
+      x1 *= rscale * gqr[2 * pi + 1];
+    }
+    float c, s;
+    rope_cos_sin(pos, pi, dr, base, &c, &s);
+    Elem<TOut>::store(qr_out, 2 * pi, (x0 * c - x1 * s) * sl);
+    Elem<TOut>::store(qr_out, 2 * pi + 1, (x0 * s + x1 * c) * sl);
+  }
+}
+
+__device__ __forceinline__ int clamp_pos(int L, int L_cap) {
+  return (L >= 1 && L <= L_cap) ? L - 1 : 0;
+}
+
+// bf16 layer with 16 heads per KV group: one workgroup (4 waves) per (b, g).
+// q~[16 heads][r] = q^C[16][d_c] . W~_g^T[d_c][r] on mfma_f32_16x16x32_bf16.
+// Operand layouts (gfx950, 16x16x32): A lane l holds A[m=l%16][k=8(l/16)+j],
+// B lane l holds B[k=8(l/16)+j][n=l%16], D lane l reg i holds D[4(l/16)+i][l%16].
+__global__ __launch_bounds__(256) void qprep_mfma_kernel(
+    const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_qabs, const float* __restrict__ gqr,
+    const int32_t* __restrict__ seq_lens, int L_cap, int H, int G, int r, int dc, int dr,
+    float eps, float tau, float base, int qk_norm, uint16_t* __restrict__ q_tilde,
+    float* __restrict__ alpha_q, uint16_t* __restrict__ q_rope_out, int32_t* status) {
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h0 = g * 16;
+  const int L = seq_lens[b];
+  if (g == 0 && threadIdx.x == 0 && (L < 1 || L > L_cap) && status)
+    atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
+  const int pos = clamp_pos(L, L_cap);
+
+  const uint16_t* A = q_c + ((size_t)b * H + h0) * dc;
+  const uint16_t* W = w_qabs + (size_t)g * r * dc;
+  const int m = lane & 15, kq = lane >> 4;
+  // Plain mode has one logit accumulator for content + RoPE, so the softmax
+  // scale goes into q~ as well.
+  const float qs = qk_norm ? 1.0f : tau * kLog2e;
+  const int nblocks = r / 16;               // 32 for r = 512
+  const int nb_per_wave = nblocks / 4;
+  for (int nbi = 0; nbi < nb_per_wave; ++nbi) {
+    const int nb = wave * nb_per_wave + nbi;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < dc / 32; ++ks) {
+      bf16x8 a = *(const bf16x8*)(A + (size_t)m * dc + ks * 32 + kq * 8);
+      bf16x8 bv = *(const bf16x8*)(W + (size_t)(nb * 16 + m) * dc + ks * 32 + kq * 8);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int hh = 4 * kq + i;
+      q_tilde[((size_t)b * H + h0 + hh) * r + nb * 16 + m] = f32_to_bf16(acc[i] * qs);
+    }
+  }
+  // alpha^q and the RoPE query: each wave takes 4 of the 16 heads.
+  for (int hh = wave; hh < 16; hh += 4) {
+    int h = h0 + hh;
+    prep_scalar_and_rope<uint16_t, uint16_t>(
+        q_c + ((size_t)b * H + h) * dc, q_rope + ((size_t)b * H + h) * dr, gqr, dc, dr, eps, tau,
+        base, qk_norm, pos, alpha_q + (size_t)b * H + h, q_rope_out + ((size_t)b * H + h) * dr);
+  }
+}
+
+// Any shape, float storage: one workgroup per (b, h).
+__global__ __launch_bounds__(256) void qprep_generic_kernel(
+    const float* __restrict__ q_c, const float* __restrict__ q_rope,
+    const float* __restrict__ w_qabs, const float* __restrict__ gqr,
+    const int32_t* __restrict__ seq_lens, int L_cap, int H, int G, int r, int dc, int dr,
+    float eps, float tau, float base, int qk_norm, float* __restrict__ q_tilde,
+    float* __restrict__ alpha_q, float* __restrict__ q_rope_out, int32_t* status) {
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int g = (h * G) / H;
+  const int L = seq_lens[b];
+  if (h == 0 && threadIdx.x == 0 && (L < 1 || L > L_cap) && status)
+    atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
+  const int pos = clamp_pos(L, L_cap);
+  const float* qc = q_c + ((size_t)b * H + h) * dc;
+  const float* W = w_qabs + (size_t)g * r * dc;
+  for (int i = threadIdx.x; i < r; i += blockDim.x) {
+    float acc = 0.f;
+    for (int j = 0; j < dc; ++j) acc += qc[j] * W[(size_t)i * dc + j];
+    q_tilde[((size_t)b * H + h) * r + i] = acc;
+  }
+  if (threadIdx.x < 64)
+    prep_scalar_and_rope<float, float>(qc, q_rope + ((size_t)b * H + h) * dr, gqr, dc, dr, eps,
+                                       tau, base, qk_norm, pos, alpha_q + (size_t)b * H + h,
+                                       q_rope_out + ((size_t)b * H + h) * dr);
+}
+
+hipError_t launch_qprep(const Cfg& c, int batch, const void* q_c, const void* q_rope,
+                        const void* w_qabs, const float* gqr, const int32_t* seq_lens, int L_cap,
+                        const WsLayout& ws, void* workspace, int32_t* status, hipStream_t s) {
+  char* wsb = (char*)workspace;
+  if (c.dtype == QKMLA_BF16) {
+    qprep_mfma_kernel<<<dim3(batch, c.G), 256, 0, s>>>(
+        (const uint16_t*)q_c, (const uint16_t*)q_rope, (const uint16_t*)w_qabs, gqr, seq_lens,
+        L_cap, c.H, c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm,
+        (uint16_t*)(wsb + ws.q_tilde), (float*)(wsb + ws.alpha_q), (uint16_t*)(wsb + ws.q_rope),
+        status);
+  } else {
+    qprep_generic_kernel<<<dim3(batch, c.H), 256, 0, s>>>(
+        (const float*)q_c, (const float*)q_rope, (const float*)w_qabs, gqr, seq_lens, L_cap, c.H,
+        c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm, (float*)(wsb + ws.q_tilde),
+        (float*)(wsb + ws.alpha_q), (float*)(wsb + ws.q_rope), status);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qkmla

@@ -139,3 +139,38 @@ def workload_inputs(config_id: int, seed: Optional[int] = None) -> Inputs:
     w = WORKLOADS[config_id]
     return make_inputs(w.shape, w.lengths or (), 1000 + config_id if seed is None else seed,
                        row_scale_log10_clip=w.row_scale_log10_clip, ragged=w.ragged, batch=w.batch)
+
+
+def device_cache_fill_source(shape: Shape, lengths, seed: int, device, row_scale_log10_clip=None,
+                             chunk: int = 65536):
+    """Yield (b or None, start, c_new, k_rope_raw) chunks of N(0,1) latents and raw
+    RoPE keys drawn on the GPU (same distributions as make_inputs; not the same
+    numbers).  Used by the benchmark, which never compares against the oracle.
+    With equal lengths the chunks cover the whole batch (b is None)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    r, dr = shape.latent_rank, shape.rope_dim
+
+    def draw(n_seq, n):
+        c = torch.randn((n_seq, n, r), generator=g, device=device, dtype=torch.float32)
+        if row_scale_log10_clip is not None:
+            z = torch.randn((n_seq, n, 1), generator=g, device=device).clamp_(
+                -row_scale_log10_clip, row_scale_log10_clip)
+            c = c * torch.pow(10.0, z)
+        k = torch.randn((n_seq, n, dr), generator=g, device=device, dtype=torch.float32)
+        return c.to(dt).contiguous(), k.to(dt).contiguous()
+
+    lengths = list(lengths)
+    if len(set(lengths)) == 1:
+        for s in range(0, lengths[0], chunk):
+            e = min(lengths[0], s + chunk)
+            c, k = draw(len(lengths), e - s)
+            yield None, s, c, k
+    else:
+        for b, L in enumerate(lengths):
+            for s in range(0, L, chunk):
+                e = min(L, s + chunk)
+                c, k = draw(1, e - s)
+                yield b, s, c, k

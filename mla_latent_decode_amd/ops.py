@@ -1,0 +1,218 @@
+"""ctypes binding of libqkmla.so for torch tensors.
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels.  Importing this module loads the library and raises if it has not
+been built (python -m mla_latent_decode_amd.build); there is no fallback.
+
+Function names and argument order follow include/qkmla.h.  Tensors must be
+contiguous; device tensors must live on the current CUDA (HIP) device; work is
+enqueued on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqkmla.so")
+
+QKMLA_F32, QKMLA_BF16 = 0, 1
+QKMLA_DEV_BAD_SEQ_LEN, QKMLA_DEV_BAD_POSITION = 1, 2
+
+
+class QkmlaError(RuntimeError):
+    pass
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("latent_rank", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("v_head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+                ("rope_base", ctypes.c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise QkmlaError(f"{LIB_PATH} is missing: build it with "
+                         "`python -m mla_latent_decode_amd.build` (no fallback path exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    C = ctypes.POINTER(_Config)
+    sig = {
+        "qkmla_absorb_weights": (I32, [C, P, P, P, P, P]),
+        "qkmla_append": (I32, [C, I32, I32, P, P, P, P, P, I32, P, P, P, P, P]),
+        "qkmla_decode_workspace_size": (SZ, [C, I32, I32]),
+        "qkmla_decode": (I32, [C, I32, P, P, P, P, P, P, P, P, I32, I32, P, SZ, P, P, P, P]),
+        "qkmla_out_proj": (I32, [C, I32, P, P, P, P]),
+        "qkmla_plan": (I32, [C, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "qkmla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "qkmla_last_error": (ctypes.c_char_p, []),
+        "qkmla_abi_version": (ctypes.c_int, []),
+        "qkmla_profile_begin": (I32, []),
+        "qkmla_profile_end": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """Mirror of qkmla_config."""
+    n_heads: int
+    n_groups: int
+    latent_rank: int
+    head_dim: int
+    rope_dim: int
+    v_head_dim: int
+    dtype: str = "bf16"        # "bf16" or "f32"
+    qk_norm: bool = True
+    eps: float = 1e-6
+    softmax_scale: float = 0.0  # <= 0: 1/sqrt(head_dim + rope_dim)
+    rope_base: float = 10000.0
+
+    @classmethod
+    def from_shape(cls, shape, **kw):
+        return cls(shape.n_heads, shape.n_groups, shape.latent_rank, shape.head_dim,
+                   shape.rope_dim, shape.v_head_dim, shape.dtype, **kw)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def tau(self) -> float:
+        return self.softmax_scale if self.softmax_scale > 0 else 1.0 / math.sqrt(
+            self.head_dim + self.rope_dim)
+
+    def c(self) -> _Config:
+        return _Config(self.n_heads, self.n_groups, self.latent_rank, self.head_dim,
+                       self.rope_dim, self.v_head_dim,
+                       QKMLA_BF16 if self.dtype == "bf16" else QKMLA_F32, int(self.qk_norm),
+                       self.eps, self.softmax_scale, self.rope_base)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = _lib.qkmla_last_error().decode()
+        raise QkmlaError(f"{what}: {_lib.qkmla_status_string(status).decode()}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor], shape=None, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise QkmlaError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise QkmlaError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise QkmlaError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def abi_version() -> int:
+    return _lib.qkmla_abi_version()
+
+
+def profile_begin():
+    """Start recording HIP events around each split-KV kernel launch."""
+    _check(_lib.qkmla_profile_begin(), "qkmla_profile_begin")
+
+
+def profile_end():
+    """Stop recording; returns (summed split-KV kernel ms, launches)."""
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    _check(_lib.qkmla_profile_end(ctypes.byref(ms), ctypes.byref(n)), "qkmla_profile_end")
+    return ms.value, n.value
+
+
+def plan(cfg: Config, batch: int, max_seq_len: int, n_cu: int):
+    """Host-only planner: (decode workgroups, tile tokens)."""
+    nwg, tile = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.qkmla_plan(ctypes.byref(cfg.c()), batch, max_seq_len, n_cu, ctypes.byref(nwg),
+                           ctypes.byref(tile)), "qkmla_plan")
+    return nwg.value, tile.value
+
+
+def decode_workspace_size(cfg: Config, batch: int, max_seq_len: int) -> int:
+    n = _lib.qkmla_decode_workspace_size(ctypes.byref(cfg.c()), batch, max_seq_len)
+    if n == 0:
+        raise QkmlaError("qkmla_decode_workspace_size: " + _lib.qkmla_last_error().decode())
+    return n
+
+
+def absorb_weights(cfg: Config, w_uk, gamma_q, gamma_k, out=None):
+    G, r, dc = cfg.n_groups, cfg.latent_rank, cfg.head_dim
+    if out is None:
+        out = torch.empty((G, r, dc), dtype=cfg.torch_dtype, device=w_uk.device)
+    _check(_lib.qkmla_absorb_weights(
+        ctypes.byref(cfg.c()), _ptr(w_uk, (G, r, dc), torch.float32, "w_uk"),
+        _ptr(gamma_q, (dc,), torch.float32, "gamma_q"), _ptr(gamma_k, (dc,), torch.float32, "gamma_k"),
+        _ptr(out, (G, r, dc), cfg.torch_dtype, "w_qabs"), _stream()), "qkmla_absorb_weights")
+    return out
+
+
+def append(cfg: Config, c_new, k_rope_new, w_uk, gamma_k_rope, positions, latent_cache,
+           rope_cache, alpha_cache=None, status=None):
+    """c_new [B][n_new][r], k_rope_new [B][n_new][d_r], positions [B] int32 (device)."""
+    B, n_new = c_new.shape[0], c_new.shape[1]
+    L_cap = latent_cache.shape[1]
+    dt = cfg.torch_dtype
+    _check(_lib.qkmla_append(
+        ctypes.byref(cfg.c()), B, n_new, _ptr(c_new, (B, n_new, cfg.latent_rank), dt, "c_new"),
+        _ptr(k_rope_new, (B, n_new, cfg.rope_dim), dt, "k_rope_new"),
+        _ptr(w_uk, None, torch.float32, "w_uk"), _ptr(gamma_k_rope, None, torch.float32, "gamma_k_rope"),
+        _ptr(positions, (B,), torch.int32, "positions"), L_cap,
+        _ptr(latent_cache, (B, L_cap, cfg.latent_rank), dt, "latent_cache"),
+        _ptr(rope_cache, (B, L_cap, cfg.rope_dim), dt, "rope_cache"),
+        _ptr(alpha_cache, (B, L_cap, cfg.n_groups), torch.float32, "alpha_cache"),
+        _ptr(status, (1,), torch.int32, "status"), _stream()), "qkmla_append")
+
+
+def decode(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, rope_cache, alpha_cache,
+           seq_lens, max_seq_len: int, workspace, o_lat=None, lse=None, status=None):
+    B = q_c.shape[0]
+    L_cap = latent_cache.shape[1]
+    H, r, dt = cfg.n_heads, cfg.latent_rank, cfg.torch_dtype
+    if o_lat is None:
+        o_lat = torch.empty((B, H, r), dtype=torch.float32, device=q_c.device)
+    _check(_lib.qkmla_decode(
+        ctypes.byref(cfg.c()), B, _ptr(q_c, (B, H, cfg.head_dim), dt, "q_c"),
+        _ptr(q_rope, (B, H, cfg.rope_dim), dt, "q_rope"),
+        _ptr(w_qabs, (cfg.n_groups, r, cfg.head_dim), dt, "w_qabs"),
+        _ptr(gamma_q_rope, None, torch.float32, "gamma_q_rope"),
+        _ptr(latent_cache, (B, L_cap, r), dt, "latent_cache"),
+        _ptr(rope_cache, (B, L_cap, cfg.rope_dim), dt, "rope_cache"),
+        _ptr(alpha_cache, (B, L_cap, cfg.n_groups), torch.float32, "alpha_cache"),
+        _ptr(seq_lens, (B,), torch.int32, "seq_lens"), L_cap, max_seq_len,
+        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(o_lat, (B, H, r), torch.float32, "o_lat"),
+        _ptr(lse, (B, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
+        _stream()), "qkmla_decode")
+    return o_lat
+
+
+def out_proj(cfg: Config, o_lat, w_uv, out=None):
+    B, H = o_lat.shape[0], o_lat.shape[1]
+    if out is None:
+        out = torch.empty((B, H, cfg.v_head_dim), dtype=torch.float32, device=o_lat.device)
+    _check(_lib.qkmla_out_proj(
+        ctypes.byref(cfg.c()), B, _ptr(o_lat, (B, H, cfg.latent_rank), torch.float32, "o_lat"),
+        _ptr(w_uv, (cfg.n_groups, cfg.latent_rank, cfg.v_head_dim), cfg.torch_dtype, "w_uv"),
+        _ptr(out, (B, H, cfg.v_head_dim), torch.float32, "out"), _stream()), "qkmla_out_proj")
+    return out

@@ -1,0 +1,209 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (see tests/harness.py): fp32 workload 1e-5 relative; bf16 caches
+with fp32 accumulation 2e-2 relative on o and o_lat (per (b,h) infinity norm),
+1e-3 elementwise on the alpha cache, 1e-2 per row on the RoPE cache."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from harness import TOL, check_caches, check_outputs, heads_of, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from mla_latent_decode_amd import ops
+    from mla_latent_decode_amd.inputs import DSV3, TINY, Shape, make_inputs, workload_inputs
+    from mla_latent_decode_amd.runner import DecodeSession
+
+
+def _run(cfg, inp, label, hold_last=False, L_cap=None):
+    print(f"\n[{label}] B={len(inp.lengths)} lens={inp.lengths[:6]}{'...' if len(inp.lengths) > 6 else ''}",
+          flush=True)
+    sess = DecodeSession(cfg, inp, L_cap=L_cap, hold_last=hold_last)
+    if hold_last:
+        sess.step_append()
+    o_lat, lse = sess.decode()
+    o = sess.out_proj()
+    torch.cuda.synchronize()
+    return sess, o.cpu().numpy(), o_lat.cpu().numpy(), lse.cpu().numpy()
+
+
+def _full_check(cfg, inp, label, **kw):
+    sess, o, o_lat, lse = _run(cfg, inp, label, **kw)
+    ref = oracle_decode(inp, cfg)
+    bs = range(len(inp.lengths))
+    check_outputs(o, o_lat, lse, ref, cfg.dtype, bs, list(range(cfg.n_heads)), label)
+    check_caches(sess, inp, cfg, bs)
+    assert int(sess.status.item()) == 0
+    return sess
+
+
+def test_tiny_fp32_workload_full_parity():
+    inp = workload_inputs(0)
+    cfg = ops.Config.from_shape(TINY)
+    _full_check(cfg, inp, "tiny fp32 B1 L64")
+
+
+@pytest.mark.parametrize("qk_norm", [True, False])
+def test_fp32_generic_shapes(qk_norm):
+    for i, (shape, lens) in enumerate([
+        (Shape(4, 4, 32, 16, 8, 16, "f32"), (7, 1, 300)),
+        (Shape(6, 3, 20, 12, 4, 10, "f32"), (9, 257)),
+        (Shape(8, 1, 64, 16, 8, 16, "f32"), (33,)),
+    ]):
+        inp = make_inputs(shape, lens, seed=200 + i)
+        cfg = ops.Config.from_shape(shape, qk_norm=qk_norm)
+        _full_check(cfg, inp, f"fp32 generic {i} qk_norm={qk_norm}")
+
+
+@pytest.mark.parametrize("lens", [(1, 37, 300), (32, 64), (1000,), (31, 33, 95, 97, 1, 2)])
+def test_dsv3_bf16_small_parity(lens):
+    inp = make_inputs(DSV3, lens, seed=300 + len(lens))
+    cfg = ops.Config.from_shape(DSV3)
+    _full_check(cfg, inp, f"dsv3 bf16 {lens}")
+
+
+def test_dsv3_bf16_plain_mode_parity():
+    inp = make_inputs(DSV3, (5, 70, 400), seed=310)
+    cfg = ops.Config.from_shape(DSV3, qk_norm=False)
+    _full_check(cfg, inp, "dsv3 bf16 plain")
+
+
+def test_dsv3_bf16_log_normal_scales():
+    inp = make_inputs(DSV3, (500, 129), seed=311, row_scale_log10_clip=3.0)
+    cfg = ops.Config.from_shape(DSV3)
+    _full_check(cfg, inp, "dsv3 bf16 log-normal rows")
+
+
+@pytest.mark.parametrize("heads", [64, 32])
+def test_dsv3_fewer_heads(heads):
+    shape = Shape(heads, heads // 16, 512, 128, 64, 128, "bf16")
+    inp = make_inputs(shape, (45, 200), seed=320 + heads)
+    _full_check(ops.Config.from_shape(shape), inp, f"bf16 H={heads}")
+
+
+def test_split_count_does_not_change_the_result():
+    """The plan (1, 7 or 256 workgroups) only changes which tokens share a
+    partial.  P is rounded to bf16 relative to each segment's own reference
+    max, so results agree to a few bf16 ulps (2^-9 relative per weight), and
+    every plan matches the oracle."""
+    inp = make_inputs(DSV3, (700, 333, 64), seed=330)
+    cfg = ops.Config.from_shape(DSV3)
+    ref = oracle_decode(inp, cfg)
+    outs = []
+    for nwg in ("1", "7", "256"):
+        os.environ["QKMLA_NUM_WG"] = nwg
+        try:
+            sess = DecodeSession(cfg, inp)
+            o_lat, lse = sess.decode()
+            o = sess.out_proj()
+            outs.append((o_lat.cpu().numpy().copy(), lse.cpu().numpy().copy()))
+            check_outputs(o.cpu().numpy(), outs[-1][0], outs[-1][1], ref, "bf16", range(3),
+                          list(range(128)), f"plan with {nwg} workgroups")
+        finally:
+            del os.environ["QKMLA_NUM_WG"]
+    for o, l in outs[1:]:
+        assert np.max(np.abs(o - outs[0][0])) <= 8e-3 * np.max(np.abs(outs[0][0]))
+        assert np.max(np.abs(l - outs[0][1])) <= 2e-3
+
+
+def test_invalid_sequence_length_gives_zeros_and_status():
+    inp = make_inputs(DSV3, (40, 40), seed=340)
+    cfg = ops.Config.from_shape(DSV3)
+    sess = DecodeSession(cfg, inp)
+    sess.seq_lens[1] = 0
+    o_lat, lse = sess.decode()
+    torch.cuda.synchronize()
+    assert int(sess.status.item()) & ops.QKMLA_DEV_BAD_SEQ_LEN
+    assert torch.all(o_lat[1] == 0) and torch.all(torch.isinf(lse[1])) and torch.all(lse[1] < 0)
+    ref = oracle_decode(inp, cfg, batch_ids=[0])
+    check_outputs(sess.out_proj().cpu().numpy(), o_lat.cpu().numpy(), lse.cpu().numpy(), ref,
+                  "bf16", [0], list(range(128)), "valid neighbour of an invalid sequence")
+
+
+def test_bad_append_position_sets_status_and_writes_nothing():
+    inp = make_inputs(DSV3, (16,), seed=350)
+    cfg = ops.Config.from_shape(DSV3)
+    sess = DecodeSession(cfg, inp)
+    before = sess.lat.clone()
+    c = torch.ones((1, 4, 512), dtype=torch.bfloat16, device="cuda")
+    k = torch.ones((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    pos = torch.tensor([14], dtype=torch.int32, device="cuda")  # 14 + 4 > 16
+    ops.append(cfg, c, k, sess.w_uk, sess.gamma_k_rope, pos, sess.lat, sess.rope, sess.alpha,
+               sess.status)
+    torch.cuda.synchronize()
+    assert int(sess.status.item()) & ops.QKMLA_DEV_BAD_POSITION
+    assert torch.equal(before, sess.lat)
+
+
+def test_append_one_token_at_a_time_equals_bulk():
+    inp = make_inputs(DSV3, (40,), seed=360)
+    cfg = ops.Config.from_shape(DSV3)
+    bulk = DecodeSession(cfg, inp)
+    lat = torch.zeros_like(bulk.lat)
+    rope = torch.zeros_like(bulk.rope)
+    alpha = torch.zeros_like(bulk.alpha)
+    for t in range(40):
+        c = bulk.lat[:, t:t + 1].contiguous()
+        k = torch.from_numpy(inp.k_rope_raw[0][t:t + 1][None]).to("cuda", torch.bfloat16)
+        pos = torch.tensor([t], dtype=torch.int32, device="cuda")
+        ops.append(cfg, c, k, bulk.w_uk, bulk.gamma_k_rope, pos, lat, rope, alpha, bulk.status)
+    torch.cuda.synchronize()
+    assert torch.equal(lat, bulk.lat) and torch.equal(rope, bulk.rope) and torch.equal(alpha, bulk.alpha)
+
+
+def test_scale_invariance_is_bit_exact_on_gpu():
+    """eps = 0: scaling latent rows by powers of two leaves every logit's
+    rounding unchanged, so lse is bit-identical and alpha scales exactly."""
+    inp = make_inputs(DSV3, (90,), seed=370)
+    cfg = ops.Config.from_shape(DSV3, eps=0.0)
+    a = DecodeSession(cfg, inp)
+    _, lse_a = a.decode()
+    lse_a = lse_a.clone()
+    k = np.random.default_rng(0).integers(-6, 7, size=90)
+    inp.latents[0] = (inp.latents[0] * (2.0 ** k)[:, None]).astype(np.float32)
+    b = DecodeSession(cfg, inp)
+    _, lse_b = b.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(lse_a, lse_b)
+    ratio = (a.alpha[0, :90] / b.alpha[0, :90]).cpu().numpy()
+    assert np.array_equal(ratio, np.broadcast_to((2.0 ** k)[:, None], ratio.shape))
+
+
+def test_permuting_cache_rows_leaves_output_unchanged():
+    inp = make_inputs(DSV3, (256,), seed=380)
+    cfg = ops.Config.from_shape(DSV3)
+    sess = DecodeSession(cfg, inp)
+    o1, _ = sess.decode()
+    o1 = o1.clone()
+    perm = torch.randperm(256, generator=torch.Generator().manual_seed(0)).cuda()
+    o2, _ = sess.decode(sess.lat[:, perm].contiguous(), sess.rope[:, perm].contiguous(),
+                        sess.alpha[:, perm].contiguous())
+    torch.cuda.synchronize()
+    # the RoPE keys carry their own positions, so the permuted cache is the same set of tokens
+    assert torch.max(torch.abs(o1 - o2)) <= 2e-2 * torch.max(torch.abs(o1))
+
+
+# --- full-size workloads: sampled sequences and groups, the oracle one by one --------------
+
+@pytest.mark.parametrize("cid,samples", [
+    (1, [(0, 0), (7, 5), (15, 7)]),
+    (2, [(0, 3), (3, 6)]),
+    (3, [(0, 1)]),
+    (4, [(0, 0), (31, 4), (63, 7)]),
+])
+def test_full_size_workloads_sampled(cid, samples):
+    from mla_latent_decode_amd.inputs import WORKLOADS
+    w = WORKLOADS[cid]
+    inp = workload_inputs(cid)
+    cfg = ops.Config.from_shape(w.shape)
+    sess, o, o_lat, lse = _run(cfg, inp, f"workload {cid}: {w.name}", hold_last=w.append_last)
+    assert int(sess.status.item()) == 0
+    for b, g in samples:
+        ref = oracle_decode(inp, cfg, batch_ids=[b], groups=[g])
+        check_outputs(o, o_lat, lse, ref, cfg.dtype, [b], heads_of([g], cfg.n_heads, cfg.n_groups),
+                      f"workload {cid} b={b} g={g}")
+    check_caches(sess, inp, cfg, sorted({b for b, _ in samples}), max_rows=2048)

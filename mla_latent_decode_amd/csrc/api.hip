@@ -55,10 +55,14 @@ int check_cfg(const qkmla_config* cfg, Cfg* out) {
     return fail(QKMLA_ERR_UNSUPPORTED, "dimension above the compiled limits (r, d_c, d_v <= 1024, d_r <= 256)");
   if (c.dtype == QKMLA_BF16) {
     const int hpg = c.n_heads / c.n_groups;
-    const bool h_ok = c.n_heads == 32 || c.n_heads == 64 || c.n_heads == 128;
-    if (c.latent_rank != 512 || c.rope_dim != 64 || !h_ok || hpg != 16 || c.head_dim % 32 != 0)
+    // H = 32 (one wavefront per workgroup) is switched off: that instantiation
+    // faulted on the GPU with the asm tile loads and its cause is not yet found.
+    const bool h_ok = c.n_heads == 64 || c.n_heads == 128;
+    if (c.latent_rank != 512 || c.rope_dim != 64 || !h_ok || hpg != 16 || c.head_dim % 32 != 0 ||
+        c.head_dim > 256)
       return fail(QKMLA_ERR_UNSUPPORTED,
-                  "bf16 path is compiled for r=512, d_r=64, H in {32,64,128}, H/G=16, d_c%%32==0 "
+                  "bf16 path is compiled for r=512, d_r=64, H in {64,128}, H/G=16, d_c in "
+                  "{32,64,...,256} "
                   "(got r=%d d_r=%d H=%d G=%d d_c=%d)",
                   c.latent_rank, c.rope_dim, c.n_heads, c.n_groups, c.head_dim);
   }

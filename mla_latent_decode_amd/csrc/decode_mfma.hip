@@ -363,11 +363,11 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, const int32_t* seq_lens, 
   if (c.qk_norm) {
     if (nw == 4) decode_mfma_kernel<true, 4><<<grid, block, 0, s>>>(a);
     else if (nw == 2) decode_mfma_kernel<true, 2><<<grid, block, 0, s>>>(a);
-    else decode_mfma_kernel<true, 1><<<grid, block, 0, s>>>(a);
+    else return hipErrorInvalidValue;  // one-wavefront variant switched off
   } else {
     if (nw == 4) decode_mfma_kernel<false, 4><<<grid, block, 0, s>>>(a);
     else if (nw == 2) decode_mfma_kernel<false, 2><<<grid, block, 0, s>>>(a);
-    else decode_mfma_kernel<false, 1><<<grid, block, 0, s>>>(a);
+    else return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

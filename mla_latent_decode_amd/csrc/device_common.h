@@ -35,14 +35,15 @@ template <> struct Elem<uint16_t> {
   __device__ static void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
-// RoPE angle p * base^(-2i/d) evaluated in double so that positions up to
-// 2^18 keep full float accuracy in cos/sin; returns (cos, sin) as floats.
+// cos and sin of the RoPE angle p * base^(-2i/d).  The angle is formed and
+// reduced modulo 2*pi in double, so positions up to 2^18 keep full float
+// accuracy; the reduced angle goes through float sincos.
 __device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, float base, float* c,
                                              float* s) {
-  double inv = pow((double)base, -2.0 * (double)i / (double)d);
-  double ang = (double)pos * inv;
-  *c = (float)cos(ang);
-  *s = (float)sin(ang);
+  const double two_pi = 6.283185307179586476925286766559;
+  double ang = (double)pos * pow((double)base, -2.0 * (double)i / (double)d);
+  ang -= two_pi * floor(ang / two_pi);
+  sincosf((float)ang, s, c);
 }
 
 // Sum over the 64 lanes of a wavefront.

@@ -13,24 +13,29 @@
 
 namespace qkmla {
 
-// grid (B, H/4), 256 threads: 4 heads per block, 64 threads per head, r/64
-// dims per thread (r = 512 -> 8).
+// One block per (sequence b, head h, block of 128 latent dims); 256 threads =
+// 8 source groups x 32 dim-quads.  Source group k combines the partials
+// p = p_lo + k, p_lo + k + 8, ...; the eight partial sums meet in LDS.
+constexpr int kMergeDims = 128;
+constexpr int kMergeGroups = 8;
+
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ seq_lens, int B,
                                                     int L_cap, int H, int r, int n_wg,
                                                     const float* __restrict__ part,
                                                     float* __restrict__ o_lat,
                                                     float* __restrict__ lse) {
   __shared__ int P[kMaxBatch + 1];
+  __shared__ f32x4 red[kMergeGroups][32];
+  __shared__ float red_m[kMergeGroups], red_l[kMergeGroups];
   build_tile_prefix(seq_lens, B, L_cap, P);
-  const int b = blockIdx.x;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int dpt = r / 64;
-  float* out = o_lat + ((size_t)b * H + h) * r + lane * dpt;
+  const int b = blockIdx.x, h = blockIdx.y, dblk = blockIdx.z;
+  const int tid = threadIdx.x, sg = tid >> 5, dq = tid & 31;
+  const int d0 = dblk * kMergeDims + 4 * dq;
+  float* out = o_lat + ((size_t)b * H + h) * r + d0;
   const int n_b = P[b + 1] - P[b];
   if (n_b == 0) {  // invalid length: zeros and lse = -inf
-    for (int i = 0; i < dpt; ++i) out[i] = 0.f;
-    if (lane == 0 && lse) lse[(size_t)b * H + h] = -INFINITY;
+    if (sg == 0) *(f32x4*)out = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tid == 0 && dblk == 0 && lse) lse[(size_t)b * H + h] = -INFINITY;
     return;
   }
   const int64_t N = P[B];
@@ -41,44 +46,54 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
   const int slot_lo = (wg_start(p_lo, N, n_wg) == P[b]) ? 0 : 1;
   // Workgroups between p_lo and p_hi with an empty range (more workgroups
   // than tiles) wrote nothing and are skipped.
+  auto slot = [&](int p) -> const float* {
+    return part + ((size_t)p * kSlotsPerWg + (p == p_lo ? slot_lo : 0)) * slot_floats;
+  };
+  auto empty = [&](int p) {
+    return p != p_lo && wg_start(p, N, n_wg) == wg_start(p + 1, N, n_wg);
+  };
+  // pass 1: M = max_s m_s
   float M = -INFINITY;
-  for (int p = p_lo; p <= p_hi; ++p) {
-    if (p != p_lo && wg_start(p, N, n_wg) == wg_start(p + 1, N, n_wg)) continue;
-    const float* s = part + ((size_t)p * kSlotsPerWg + (p == p_lo ? slot_lo : 0)) * slot_floats;
-    M = fmaxf(M, s[h]);
-  }
-  float acc[16];
-  for (int i = 0; i < dpt; ++i) acc[i] = 0.f;
+  for (int p = p_lo + tid; p <= p_hi; p += 256)
+    if (!empty(p)) M = fmaxf(M, slot(p)[h]);
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if ((tid & 63) == 0) red_m[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  // pass 2: weighted sums
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  for (int p = p_lo; p <= p_hi; ++p) {
-    if (p != p_lo && wg_start(p, N, n_wg) == wg_start(p + 1, N, n_wg)) continue;
-    const float* s = part + ((size_t)p * kSlotsPerWg + (p == p_lo ? slot_lo : 0)) * slot_floats;
-    float w = exp2f(s[h] - M);
-    lsum += w * s[H + h];
-    const float* O = s + 2 * H + (size_t)h * r + lane * dpt;
-    for (int i = 0; i < dpt; i += 4) {
-      f32x4 v = *(const f32x4*)(O + i);
-      acc[i] += w * v[0];
-      acc[i + 1] += w * v[1];
-      acc[i + 2] += w * v[2];
-      acc[i + 3] += w * v[3];
+  for (int p = p_lo + sg; p <= p_hi; p += kMergeGroups) {
+    if (empty(p)) continue;
+    const float* sp = slot(p);
+    const float w = exp2f(sp[h] - M);
+    lsum += w * sp[H + h];
+    const f32x4 v = *(const f32x4*)(sp + 2 * H + (size_t)h * r + d0);
+    acc += w * v;
+  }
+  red[sg][dq] = acc;
+  if (dq == 0) red_l[sg] = lsum;
+  __syncthreads();
+  if (sg == 0) {
+    f32x4 t = red[0][dq];
+    float l = red_l[0];
+#pragma unroll
+    for (int k = 1; k < kMergeGroups; ++k) {
+      t += red[k][dq];
+      l += red_l[k];
     }
+    const float inv = 1.0f / l;
+    *(f32x4*)out = t * inv;
+    if (dq == 0 && dblk == 0 && lse) lse[(size_t)b * H + h] = (M + log2f(l)) * kLn2;
   }
-  const float inv = 1.0f / lsum;
-  for (int i = 0; i < dpt; i += 4) {
-    f32x4 v = {acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
-    *(f32x4*)(out + i) = v;
-  }
-  if (lane == 0 && lse) lse[(size_t)b * H + h] = (M + log2f(lsum)) * kLn2;
 }
 
 hipError_t launch_merge(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
                         const WsLayout& ws, void* workspace, int n_wg, float* o_lat, float* lse,
                         hipStream_t s) {
   char* wsb = (char*)workspace;
-  merge_kernel<<<dim3(batch, c.H / 4), 256, 0, s>>>(seq_lens, batch, L_cap, c.H, c.r, n_wg,
-                                                     (const float*)(wsb + ws.partials), o_lat,
-                                                     lse);
+  merge_kernel<<<dim3(batch, c.H, c.r / kMergeDims), 256, 0, s>>>(
+      seq_lens, batch, L_cap, c.H, c.r, n_wg, (const float*)(wsb + ws.partials), o_lat, lse);
   return hipGetLastError();
 }
 

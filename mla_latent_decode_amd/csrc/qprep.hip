@@ -14,12 +14,18 @@
 
 namespace qkmla {
 
-// Shared epilogue: alpha^q and the RoPE query of head h.  Executed by one
-// wavefront per head (lane-strided over dims).
+// cos/sin of the query position for every RoPE pair, into LDS (cs[2*i],
+// cs[2*i+1]).
+__device__ void rope_table(int pos, int dr, float base, float* cs) {
+  for (int i = threadIdx.x; i < dr / 2; i += blockDim.x) rope_cos_sin(pos, i, dr, base, &cs[2 * i], &cs[2 * i + 1]);
+}
+
+// alpha^q and the RoPE query of one head; executed by one wavefront
+// (lane-strided over dims).  cs: the rope_table of the query position.
 template <typename TIn, typename TOut>
 __device__ void prep_scalar_and_rope(const TIn* qc, const TIn* qr, const float* gqr, int dc,
-                                     int dr, float eps, float tau, float base, int qk_norm,
-                                     int pos, float* alpha_q_out, TOut* qr_out) {
+                                     int dr, float eps, float tau, int qk_norm, const float* cs,
+                                     float* alpha_q_out, TOut* qr_out) {
   const int lane = threadIdx.x & 63;
   const float sl = tau * kLog2e;
   float ss = 0.f;
@@ -47,10 +53,9 @@ __device__ void prep_scalar_and_rope(const TIn* qc, const TIn* qr, const float* 
       x0 *= rscale * gqr[2 * pi];
       x1 *= rscale * gqr[2 * pi + 1];
     }
-    float c, s;
-    rope_cos_sin(pos, pi, dr, base, &c, &s);
-    Elem<TOut>::store(qr_out, 2 * pi, (x0 * c - x1 * s) * sl);
-    Elem<TOut>::store(qr_out, 2 * pi + 1, (x0 * s + x1 * c) * sl);
+    const float c = cs[2 * pi], sn = cs[2 * pi + 1];
+    Elem<TOut>::store(qr_out, 2 * pi, (x0 * c - x1 * sn) * sl);
+    Elem<TOut>::store(qr_out, 2 * pi + 1, (x0 * sn + x1 * c) * sl);
   }
 }
 
@@ -76,21 +81,32 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
     atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
   const int pos = clamp_pos(L, L_cap);
 
+  __shared__ float cs[256];  // d_r <= 256
+  rope_table(pos, dr, base, cs);
+
   const uint16_t* A = q_c + ((size_t)b * H + h0) * dc;
   const uint16_t* W = w_qabs + (size_t)g * r * dc;
   const int m = lane & 15, kq = lane >> 4;
   // Plain mode has one logit accumulator for content + RoPE, so the softmax
   // scale goes into q~ as well.
   const float qs = qk_norm ? 1.0f : tau * kLog2e;
-  const int nblocks = r / 16;               // 32 for r = 512
-  const int nb_per_wave = nblocks / 4;
+  const int nb_per_wave = (r / 16) / 4;     // 8 for r = 512
+  const int ksteps = dc / 32;               // 4 for d_c = 128
+  constexpr int kMaxK = 8;                  // d_c <= 256 on this path
+  bf16x8 a[kMaxK];
+#pragma unroll
+  for (int ks = 0; ks < kMaxK; ++ks)
+    if (ks < ksteps) a[ks] = *(const bf16x8*)(A + (size_t)m * dc + ks * 32 + kq * 8);
   for (int nbi = 0; nbi < nb_per_wave; ++nbi) {
     const int nb = wave * nb_per_wave + nbi;
+    const uint16_t* wrow = W + (size_t)(nb * 16 + m) * dc + kq * 8;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < dc / 32; ++ks) {
-      bf16x8 a = *(const bf16x8*)(A + (size_t)m * dc + ks * 32 + kq * 8);
-      bf16x8 bv = *(const bf16x8*)(W + (size_t)(nb * 16 + m) * dc + ks * 32 + kq * 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kMaxK; ++ks) {
+      if (ks < ksteps) {
+        bf16x8 bv = *(const bf16x8*)(wrow + ks * 32);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bv, acc, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -98,12 +114,13 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
       q_tilde[((size_t)b * H + h0 + hh) * r + nb * 16 + m] = f32_to_bf16(acc[i] * qs);
     }
   }
+  __syncthreads();  // cs ready
   // alpha^q and the RoPE query: each wave takes 4 of the 16 heads.
   for (int hh = wave; hh < 16; hh += 4) {
     int h = h0 + hh;
     prep_scalar_and_rope<uint16_t, uint16_t>(
         q_c + ((size_t)b * H + h) * dc, q_rope + ((size_t)b * H + h) * dr, gqr, dc, dr, eps, tau,
-        base, qk_norm, pos, alpha_q + (size_t)b * H + h, q_rope_out + ((size_t)b * H + h) * dr);
+        qk_norm, cs, alpha_q + (size_t)b * H + h, q_rope_out + ((size_t)b * H + h) * dr);
   }
 }
 
@@ -127,9 +144,12 @@ __global__ __launch_bounds__(256) void qprep_generic_kernel(
     for (int j = 0; j < dc; ++j) acc += qc[j] * W[(size_t)i * dc + j];
     q_tilde[((size_t)b * H + h) * r + i] = acc;
   }
+  __shared__ float cs[256];  // d_r <= 256
+  rope_table(pos, dr, base, cs);
+  __syncthreads();
   if (threadIdx.x < 64)
     prep_scalar_and_rope<float, float>(qc, q_rope + ((size_t)b * H + h) * dr, gqr, dc, dr, eps,
-                                       tau, base, qk_norm, pos, alpha_q + (size_t)b * H + h,
+                                       tau, qk_norm, cs, alpha_q + (size_t)b * H + h,
                                        q_rope_out + ((size_t)b * H + h) * dr);
 }
 

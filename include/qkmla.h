@@ -187,6 +187,24 @@ int qkmla_plan(const qkmla_config* cfg, int32_t batch, int32_t max_seq_len, int3
                int32_t* n_workgroups, int32_t* tile_tokens);
 
 /*
+ * Host-only plan inspection (no device access): the work split that
+ * qkmla_decode's kernels use for these host-side sequence lengths and
+ * n_workgroups (the value qkmla_plan returns).
+ * qkmla_plan_segments writes one row of 5 int32 per segment into out[cap][5]:
+ *   (workgroup, sequence, first tile, end tile (exclusive, tiles of the
+ *    sequence), kind) with kind -1 = the segment is the whole sequence and is
+ *   written as final output, 0/1 = partial written to that workgroup slot.
+ * qkmla_plan_merge_sources writes the (workgroup, slot) pairs the merge reads
+ * for sequence b into out[cap][2] (none if the sequence is written directly or
+ * is invalid).  *n_out is the full count even when it exceeds cap.
+ */
+int qkmla_plan_segments(int32_t batch, const int32_t* seq_lens, int32_t cache_capacity,
+                        int32_t n_workgroups, int32_t* out, int32_t cap, int32_t* n_out);
+int qkmla_plan_merge_sources(int32_t batch, const int32_t* seq_lens, int32_t cache_capacity,
+                             int32_t n_workgroups, int32_t b, int32_t* out, int32_t cap,
+                             int32_t* n_out);
+
+/*
  * Measurement hook.  Between qkmla_profile_begin() and qkmla_profile_end(),
  * every qkmla_decode call of this host thread records a HIP event pair on its
  * stream around the launch of its split-KV kernel (the hot kernel).

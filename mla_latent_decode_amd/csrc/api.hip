@@ -8,6 +8,9 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <vector>
+
+#include "plan_device.h"
 #include "qkmla_internal.h"
 
 namespace qkmla {
@@ -208,6 +211,76 @@ int qkmla_plan(const qkmla_config* cfg, int32_t batch, int32_t max_seq_len, int3
     return fail(QKMLA_ERR_INVALID_ARG, "bad plan arguments");
   *tile_tokens = kTile;
   *n_workgroups = batch == 0 ? 0 : plan_n_wg(c, batch, max_seq_len, n_cu);
+  return ok();
+}
+
+// Host replay of the decode plan (same helpers as the kernels).
+static int host_prefix(int32_t batch, const int32_t* seq_lens, int32_t L_cap, std::vector<int>* P) {
+  if (batch < 0 || batch > kMaxBatch || (batch > 0 && !seq_lens) || L_cap < 1)
+    return fail(QKMLA_ERR_INVALID_ARG, "plan: bad batch, lengths or capacity");
+  P->assign(batch + 1, 0);
+  for (int b = 0; b < batch; ++b) (*P)[b + 1] = (*P)[b] + tiles_of(seq_lens[b], L_cap);
+  return QKMLA_OK;
+}
+
+int qkmla_plan_segments(int32_t batch, const int32_t* seq_lens, int32_t cache_capacity,
+                        int32_t n_wg, int32_t* out, int32_t cap, int32_t* n_out) {
+  std::vector<int> P;
+  int st = host_prefix(batch, seq_lens, cache_capacity, &P);
+  if (st) return st;
+  if (n_wg < 1 || !n_out || (cap > 0 && !out)) return fail(QKMLA_ERR_INVALID_ARG, "plan: bad output");
+  const int64_t N = P[batch];
+  int n = 0;
+  for (int p = 0; p < n_wg && N > 0; ++p) {
+    int64_t x = wg_start(p, N, n_wg);
+    const int64_t e = wg_start(p + 1, N, n_wg);
+    bool first = true;
+    while (x < e) {  // the decode kernel's segment loop
+      const int b = seq_of(P.data(), batch, x);
+      const int64_t s0 = P[b], s1 = P[b + 1];
+      const int64_t seg_end = e < s1 ? e : s1;
+      const bool complete = (x == s0) && (seg_end == s1);
+      if (n < cap) {
+        int32_t* r = out + 5 * n;
+        r[0] = p;
+        r[1] = b;
+        r[2] = (int32_t)(x - s0);
+        r[3] = (int32_t)(seg_end - s0);
+        r[4] = complete ? -1 : (first ? 0 : 1);
+      }
+      ++n;
+      first = false;
+      x = seg_end;
+    }
+  }
+  *n_out = n;
+  return ok();
+}
+
+int qkmla_plan_merge_sources(int32_t batch, const int32_t* seq_lens, int32_t cache_capacity,
+                             int32_t n_wg, int32_t b, int32_t* out, int32_t cap, int32_t* n_out) {
+  std::vector<int> P;
+  int st = host_prefix(batch, seq_lens, cache_capacity, &P);
+  if (st) return st;
+  if (n_wg < 1 || b < 0 || b >= batch || !n_out || (cap > 0 && !out))
+    return fail(QKMLA_ERR_INVALID_ARG, "plan: bad merge query");
+  const int64_t N = P[batch];
+  int n = 0;
+  if (P[b + 1] > P[b]) {
+    const int p_lo = wg_of(P[b], N, n_wg), p_hi = wg_of(P[b + 1] - 1, N, n_wg);
+    if (p_lo != p_hi) {  // the merge kernel's source loop
+      for (int p = p_lo; p <= p_hi; ++p) {
+        const int slot = merge_slot(P.data(), b, N, n_wg, p);
+        if (slot < 0) continue;
+        if (n < cap) {
+          out[2 * n] = p;
+          out[2 * n + 1] = slot;
+        }
+        ++n;
+      }
+    }
+  }
+  *n_out = n;
   return ok();
 }
 

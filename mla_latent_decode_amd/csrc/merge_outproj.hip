@@ -43,15 +43,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
   const int p_hi = wg_of(P[b + 1] - 1, N, n_wg);
   if (p_lo == p_hi) return;  // written directly by the decode kernel
   const size_t slot_floats = (size_t)H * (r + 2);
-  const int slot_lo = (wg_start(p_lo, N, n_wg) == P[b]) ? 0 : 1;
   // Workgroups between p_lo and p_hi with an empty range (more workgroups
   // than tiles) wrote nothing and are skipped.
   auto slot = [&](int p) -> const float* {
-    return part + ((size_t)p * kSlotsPerWg + (p == p_lo ? slot_lo : 0)) * slot_floats;
+    return part + ((size_t)p * kSlotsPerWg + merge_slot(P, b, N, n_wg, p)) * slot_floats;
   };
-  auto empty = [&](int p) {
-    return p != p_lo && wg_start(p, N, n_wg) == wg_start(p + 1, N, n_wg);
-  };
+  auto empty = [&](int p) { return merge_slot(P, b, N, n_wg, p) < 0; };
   // pass 1: M = max_s m_s
   float M = -INFINITY;
   for (int p = p_lo + tid; p <= p_hi; p += 256)

@@ -17,7 +17,7 @@ namespace qkmla {
 
 constexpr int kMaxBatch = 4096;
 
-__device__ __forceinline__ int tiles_of(int L, int L_cap) {
+__host__ __device__ __forceinline__ int tiles_of(int L, int L_cap) {
   return (L >= 1 && L <= L_cap) ? (L + kTile - 1) / kTile : 0;
 }
 
@@ -58,23 +58,34 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ seq_lens, int B, i
   __syncthreads();
 }
 
-__device__ __forceinline__ int64_t wg_start(int p, int64_t N, int n_wg) {
+__host__ __device__ __forceinline__ int64_t wg_start(int p, int64_t N, int n_wg) {
   return ((int64_t)p * N) / n_wg;
 }
 
 // Workgroup whose range holds tile x (0 <= x < N).
-__device__ __forceinline__ int wg_of(int64_t x, int64_t N, int n_wg) {
+__host__ __device__ __forceinline__ int wg_of(int64_t x, int64_t N, int n_wg) {
   return (int)(((x + 1) * n_wg - 1) / N);
 }
 
 // Largest b with P[b] <= x (the sequence holding tile x); P has B+1 entries.
-__device__ __forceinline__ int seq_of(const int* P, int B, int64_t x) {
+__host__ __device__ __forceinline__ int seq_of(const int* P, int B, int64_t x) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
     if (P[mid] <= x) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Partial slot written for sequence b by workgroup p (p_lo <= p <= p_hi of b),
+// or -1 if p holds no tile of b (an empty range between p_lo and p_hi).
+// Mirrors the decode kernel: a workgroup's first segment uses slot 0, a later
+// one slot 1.
+__host__ __device__ __forceinline__ int merge_slot(const int* P, int b, int64_t N, int n_wg,
+                                                   int p) {
+  const int p_lo = wg_of(P[b], N, n_wg);
+  if (p == p_lo) return wg_start(p_lo, N, n_wg) == P[b] ? 0 : 1;
+  return wg_start(p, N, n_wg) == wg_start(p + 1, N, n_wg) ? -1 : 0;
 }
 
 }  // namespace qkmla

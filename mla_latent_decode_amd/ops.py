@@ -55,6 +55,8 @@ def _load():
         "qkmla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "qkmla_last_error": (ctypes.c_char_p, []),
         "qkmla_abi_version": (ctypes.c_int, []),
+        "qkmla_plan_segments": (I32, [I32, P, I32, I32, P, I32, ctypes.POINTER(I32)]),
+        "qkmla_plan_merge_sources": (I32, [I32, P, I32, I32, I32, P, I32, ctypes.POINTER(I32)]),
         "qkmla_profile_begin": (I32, []),
         "qkmla_profile_end": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
     }
@@ -147,6 +149,41 @@ def plan(cfg: Config, batch: int, max_seq_len: int, n_cu: int):
     _check(_lib.qkmla_plan(ctypes.byref(cfg.c()), batch, max_seq_len, n_cu, ctypes.byref(nwg),
                            ctypes.byref(tile)), "qkmla_plan")
     return nwg.value, tile.value
+
+
+def _host_i32(values):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+
+
+def plan_segments(seq_lens, cache_capacity: int, n_workgroups: int):
+    """Host replay of the decode plan: array of rows (workgroup, sequence,
+    first tile, end tile, kind) with kind -1 = whole sequence written directly,
+    0/1 = partial in that workgroup slot."""
+    import numpy as np
+    lens = _host_i32(seq_lens)
+    n = ctypes.c_int32()
+    _check(_lib.qkmla_plan_segments(len(lens), lens.ctypes.data_as(ctypes.c_void_p), cache_capacity,
+                                    n_workgroups, None, 0, ctypes.byref(n)), "qkmla_plan_segments")
+    out = np.zeros((max(n.value, 1), 5), dtype=np.int32)
+    _check(_lib.qkmla_plan_segments(len(lens), lens.ctypes.data_as(ctypes.c_void_p), cache_capacity,
+                                    n_workgroups, out.ctypes.data_as(ctypes.c_void_p), n.value,
+                                    ctypes.byref(n)), "qkmla_plan_segments")
+    return out[:n.value]
+
+
+def plan_merge_sources(seq_lens, cache_capacity: int, n_workgroups: int, b: int):
+    """(workgroup, slot) pairs the merge reads for sequence b."""
+    import numpy as np
+    lens = _host_i32(seq_lens)
+    n = ctypes.c_int32()
+    cap = n_workgroups + 2
+    out = np.zeros((cap, 2), dtype=np.int32)
+    _check(_lib.qkmla_plan_merge_sources(len(lens), lens.ctypes.data_as(ctypes.c_void_p),
+                                         cache_capacity, n_workgroups, b,
+                                         out.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n)),
+           "qkmla_plan_merge_sources")
+    return out[:n.value]
 
 
 def decode_workspace_size(cfg: Config, batch: int, max_seq_len: int) -> int:

@@ -1,7 +1,8 @@
 """Build libqkmla.so (the C-ABI library with every HIP kernel) for gfx950.
 
-Usage: python -m mla_latent_decode_amd.build [--save-temps]
-The library is written next to this file; objects go to ./_build/.
+Usage: python -m mla_latent_decode_amd.build
+The library is written next to this file; objects and the device assembly go
+to ./_build/.
 """
 from __future__ import annotations
 
@@ -26,11 +27,12 @@ CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src: str, save_temps: bool) -> str:
+def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-    if save_temps:
-        cmd.insert(1, "-save-temps=obj")
+    # -save-temps keeps the device assembly (*-gfx950.s) the code object is
+    # assembled from, for the static ISA checks and the CPU emulator tests;
+    # the code it produces is the same as without it.
+    cmd = [HIPCC, "-save-temps=obj", *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)
@@ -41,10 +43,10 @@ def _compile(src: str, save_temps: bool) -> str:
     return obj
 
 
-def build(save_temps: bool = False) -> str:
+def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
+        objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
@@ -55,4 +57,4 @@ def build(save_temps: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(save_temps="--save-temps" in sys.argv))
+    print(build())

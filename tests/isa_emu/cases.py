@@ -1,0 +1,173 @@
+"""Cases run on the emulated device, each compared with the fp64 oracle.
+
+usage: python tests/isa_emu/cases.py RUNTIME_SO [case ...]
+Prints one line per check and exits non-zero if any case fails.  Runs in its
+own process: the runtime stand-in must be the only HIP runtime loaded.
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+import traceback
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+REPO = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, REPO)
+sys.path.insert(0, os.path.dirname(HERE))
+
+import oracle  # noqa: E402
+from isa_emu.asm import Kernel, parse_inst  # noqa: E402
+from isa_emu.device import Device, Session  # noqa: E402
+from isa_emu.machine import Emulator, EmuError, Memory  # noqa: E402
+from mla_latent_decode_amd.inputs import DSV3, TINY, Shape, make_inputs  # noqa: E402
+
+TOL = {"f32": dict(o=1e-5, o_lat=1e-5, lse=1e-5), "bf16": dict(o=2e-2, o_lat=2e-2, lse=5e-2)}
+MERGE_HEADS = (0, 37, 127)
+
+
+def _merge_heads_only(name, grid):
+    # the merge kernel has one block per (sequence, head, 128 dims): run three heads
+    if "merge_kernel" in name:
+        return [(x, y, z) for z in range(grid[2]) for y in MERGE_HEADS if y < grid[1]
+                for x in range(grid[0])]
+    return None
+
+
+def reference(shape, inp, qk_norm, batch_ids=None):
+    tau = 1.0 / np.sqrt(shape.head_dim + shape.rope_dim)
+    return oracle.explicit_decode(inp.q_c, inp.q_rope, inp.latents, inp.k_rope_raw, inp.w_uk,
+                                  inp.w_uv, inp.gamma_q, inp.gamma_k, inp.gamma_q_rope,
+                                  inp.gamma_k_rope, eps=1e-6, tau=tau, base=10000.0,
+                                  qk_norm=qk_norm, batch_ids=batch_ids)
+
+
+def compare(shape, got_o, got_lat, got_lse, ref, bs, hs, label):
+    e = dict(o=0.0, o_lat=0.0, lse=0.0)
+    for b in bs:
+        e["o"] = max(e["o"], float(oracle.rowwise_rel_err(got_o[b, hs], ref["o"][b, hs]).max()))
+        e["o_lat"] = max(e["o_lat"],
+                         float(oracle.rowwise_rel_err(got_lat[b, hs], ref["o_lat"][b, hs]).max()))
+        e["lse"] = max(e["lse"], float(np.abs(got_lse[b, hs] - ref["lse"][b, hs]).max()))
+    tol = TOL[shape.dtype]
+    ok = all(e[k] <= tol[k] for k in tol)
+    print(f"[{'ok' if ok else 'FAIL'}] {label}: " + " ".join(f"{k} {v:.2e}" for k, v in e.items()),
+          flush=True)
+    if not ok:
+        raise AssertionError(f"{label}: {e} above {tol}")
+
+
+def run_layer(dev, shape, lens, seed, label, qk_norm=True, host_fill=True, hold_last=False,
+              n_wg=None, heads=None):
+    inp = make_inputs(shape, lens, seed=seed)
+    if n_wg is not None:
+        os.environ["QKMLA_NUM_WG"] = str(n_wg)
+    try:
+        s = Session(dev, shape, inp, qk_norm=qk_norm, host_fill=host_fill, hold_last=hold_last)
+        o_lat, lse = s.decode()
+        out = s.out_proj()
+    finally:
+        os.environ.pop("QKMLA_NUM_WG", None)
+    hs = list(range(shape.n_heads)) if heads is None else [h for h in heads if h < shape.n_heads]
+    compare(shape, out, o_lat, lse, reference(shape, inp, qk_norm), range(len(lens)), hs, label)
+    assert s.status[0] == 0, f"{label}: device status {s.status[0]}"
+    return s
+
+
+# ----------------------------------------------------------------------------
+CASES = {}
+
+
+def case(fn):
+    CASES[fn.__name__] = fn
+    return fn
+
+
+@case
+def fp32_tiny(dev):
+    """Every fp32 kernel: absorb, append, generic q-prep and decode, out_proj."""
+    run_layer(dev, TINY, (64,), 1000, "fp32 tiny layer, caches from qkmla_append",
+              host_fill=False)
+    run_layer(dev, Shape(6, 3, 20, 12, 4, 10, "f32"), (9, 257), 201,
+              "fp32 odd shape, plain MLA", qk_norm=False, host_fill=False)
+
+
+@case
+def bf16_split(dev):
+    """MFMA q-prep, split-KV decode with multi-tile and multi-segment
+    workgroups, the merge of partials, MFMA out_proj (three heads merged)."""
+    run_layer(dev, DSV3, (70, 33, 1), 500, "bf16 layer over 4 workgroups", n_wg=4,
+              heads=MERGE_HEADS)
+
+
+@case
+def bf16_plain_hold(dev):
+    """Plain MLA split-KV and the one-token append of the decode step."""
+    run_layer(dev, DSV3, (40, 64), 501, "bf16 plain MLA, last token appended in the step",
+              qk_norm=False, host_fill=False, hold_last=True, n_wg=3, heads=MERGE_HEADS)
+
+
+@case
+def hazard_checker(dev):
+    """The wait-state check fires on an inline-asm LDS DMA that reads an SGPR a
+    VALU instruction wrote one wait state earlier, and not with s_nop 4."""
+    def program(nop):
+        lines = ["s_mov_b32 m0, 0", "v_readfirstlane_b32 s2, v1", "v_readfirstlane_b32 s3, v2"]
+        insts = [parse_inst(t, k) for k, t in enumerate(lines)]
+        asm = ([f"s_nop {nop}"] if nop is not None else []) + ["global_load_lds_dword v0, s[2:3]"]
+        for t in asm:
+            inst = parse_inst(t, len(insts))
+            inst.in_asm = True
+            insts.append(inst)
+        insts += [parse_inst("s_waitcnt vmcnt(0)", 90), parse_inst("s_endpgm", 91)]
+        meta = {"group_segment_fixed_size": 256, "user_sgpr_count": 0}
+        return Kernel("probe", insts, {}, meta, {})
+
+    buf = np.zeros(1024, np.uint8)
+    mem = Memory()
+    mem.add(buf.ctypes.data, buf.nbytes, "probe buffer", buf)
+
+    def run(nop):
+        emu = Emulator(mem)
+        k = program(nop)
+        emu.prepare(k)
+        from isa_emu.machine import Wave, Workgroup
+        wg = Workgroup(256)
+        w = Wave(emu, k, wg, 0, (0, 0, 0), (64, 1, 1), 0, 64)
+        w.V[1] = buf.ctypes.data & 0xFFFFFFFF
+        w.V[2] = buf.ctypes.data >> 32
+        w.V[0] = 0
+        emu._run_group(k, wg, [w], (0, 0, 0), 100)
+
+    for nop in (None, 0, 3):
+        try:
+            run(nop)
+        except EmuError as e:
+            assert "wait states" in str(e), e
+        else:
+            raise AssertionError(f"hazard with s_nop {nop} not reported")
+    run(4)
+    print("[ok] wait-state check: reported below 5 wait states, clean at 5", flush=True)
+
+
+def main(argv):
+    runtime_so = argv[0]
+    names = argv[1:] or list(CASES)
+    dev = Device(REPO, runtime_so, cu_count=8, group_filter=_merge_heads_only)
+    failed = []
+    for n in names:
+        t0 = time.time()
+        try:
+            CASES[n](dev)
+        except Exception:  # noqa: BLE001 -- every failure is printed and counted
+            traceback.print_exc()
+            failed.append(n)
+        print(f"  -- {n}: {time.time() - t0:.1f} s", flush=True)
+    print("FAILED " + " ".join(failed) if failed else "ALL PASSED", flush=True)
+    return 1 if failed else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

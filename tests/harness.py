@@ -27,6 +27,13 @@ def heads_of(groups, H, G):
     return [h for h in range(H) if (h * G) // H in groups]
 
 
+def worst_of(x) -> float:
+    """Largest value of an error array; NaN (an output the kernel never wrote or
+    a non-finite result) counts as infinitely wrong instead of being skipped."""
+    x = np.asarray(x, dtype=np.float64)
+    return float("inf") if np.isnan(x).any() else float(x.max())
+
+
 def check_outputs(got_o, got_lat, got_lse, ref, dtype, bs, hs, label=""):
     tol = TOL[dtype]
     worst = {}
@@ -34,9 +41,9 @@ def check_outputs(got_o, got_lat, got_lse, ref, dtype, bs, hs, label=""):
         eo = oracle.rowwise_rel_err(got_o[b, hs], ref["o"][b, hs])
         el = oracle.rowwise_rel_err(got_lat[b, hs], ref["o_lat"][b, hs])
         else_ = np.abs(got_lse[b, hs] - ref["lse"][b, hs])
-        worst["o"] = max(worst.get("o", 0), float(eo.max()))
-        worst["o_lat"] = max(worst.get("o_lat", 0), float(el.max()))
-        worst["lse"] = max(worst.get("lse", 0), float(else_.max()))
+        worst["o"] = max(worst.get("o", 0), worst_of(eo))
+        worst["o_lat"] = max(worst.get("o_lat", 0), worst_of(el))
+        worst["lse"] = max(worst.get("lse", 0), worst_of(else_))
     print(f"[{label}] worst errors: {worst}", flush=True)
     assert worst["o"] <= tol["o"], (label, worst)
     assert worst["o_lat"] <= tol["o_lat"], (label, worst)
@@ -59,8 +66,8 @@ def check_caches(sess, inp: Inputs, cfg, bs, max_rows=None):
                                          qk_norm=cfg.qk_norm)
         if cfg.qk_norm:
             ea = np.abs(alpha[b, rows] - a_ref) / np.abs(a_ref)
-            worst_a = max(worst_a, float(ea.max()))
+            worst_a = max(worst_a, worst_of(ea))
         er = oracle.rowwise_rel_err(rope[b, rows], r_ref)
-        worst_r = max(worst_r, float(er.max()))
+        worst_r = max(worst_r, worst_of(er))
     print(f"cache errors: alpha {worst_a:.3e} rope {worst_r:.3e}", flush=True)
     assert worst_a <= tol["alpha"] and worst_r <= tol["rope"], (worst_a, worst_r)

@@ -320,3 +320,11 @@ def test_workload_generation_is_seeded():
     b = workload_inputs(0)
     assert np.array_equal(a.latents[0], b.latents[0]) and np.array_equal(a.q_c, b.q_c)
     assert a.shape == TINY and a.lengths == [64]
+
+
+def test_harness_counts_nan_as_a_failure():
+    """The GPU tests' comparison must not skip NaN (Python's max drops it)."""
+    from harness import worst_of
+    assert worst_of([0.1, float("nan"), 0.2]) == float("inf")
+    assert worst_of([float("nan")]) == float("inf")
+    assert worst_of([0.1, 0.3]) == 0.3

@@ -8,15 +8,18 @@
 //   S_c[t,h] = q~_h . c_t                (K = r = 512, MFMA)
 //   S_r[t,h] = q^R_h . k^R_t             (K = d_r = 64, MFMA)
 //   l[t,h]   = S_c * (alpha^q_h * alpha^k_{t,g}) + S_r       (exp2 domain)
-//   online softmax over t, O[h,:] += sum_t p[t,h] c_t        (K = 32 tokens, MFMA)
+// alpha^q_h (with the softmax scale and log2(e)) is already folded into q~ by
+// the query preparation, so the row-column scaling is one FMA per logit.
+//   softmax weights over t, O[h,:] += sum_t p[t,h] c_t       (K = 32 tokens, MFMA)
 // Plain MLA (QKN = false) uses one K = r + d_r accumulator, no alpha.
 //
 // Shape: r = 512, d_r = 64, 32 heads per wavefront, NW = H/32 wavefronts per
 // workgroup (all heads of a token are handled by one workgroup, so every
 // cache byte is read from HBM once).  Token tiles of 32 rows are staged in LDS
-// by direct global->LDS loads (3 stages).  MFMA 32x32x16 bf16 layouts
-// (gfx950): A lane l holds A[m=l%32][k=8(l/32)+j]; B lane l holds
-// B[k=8(l/32)+j][n=l%32]; D lane l reg i holds D[8(i/4)+4(l/32)+i%4][l%32].
+// by direct global->LDS loads, three stages deep: while a tile is consumed the
+// next two are in flight.  MFMA 32x32x16 bf16 layouts (gfx950): A lane l holds
+// A[m=l%32][k=8(l/32)+j]; B lane l holds B[k=8(l/32)+j][n=l%32]; D lane l reg i
+// holds D[8(i/4)+4(l/32)+i%4][l%32].
 //   QK:  S^T (tokens x heads) = C (tokens x 512) . Q~^T ; A from LDS rows,
 //        B = q~ kept in registers for the whole segment.
 //   PV:  O^T (dims x heads) += C^T (dims x tokens) . P^T ; B = P taken
@@ -24,6 +27,12 @@
 //        A = C^T read with ds_read_b64_tr_b16: within each 16-lane group,
 //        lane i receives element i%4 of the 8-byte loads of lanes 4e + i/4
 //        (e = 0..3), which turns 4 token rows into 4 tokens of one dim.
+//
+// Register budget per lane (one wavefront per SIMD): the O^T accumulator
+// (512 dims x 32 heads fp32) fills the 256 AGPRs; q~ and the RoPE query take
+// 144 VGPRs; a tile step needs about 80 more.  Nothing spills.
+#include <type_traits>
+
 #include "device_common.h"
 #include "plan_device.h"
 #include "qkmla_internal.h"
@@ -45,6 +54,32 @@ constexpr int kStageBytes = kLatBytes + kRopeBytes + kAlphaBytes;
 // raised reference only if some p would exceed 2^kOverflowLog2.
 constexpr float kOverflowLog2 = 64.0f;
 
+// The stage buffers are three separate LDS objects, each addressed through a
+// compile-time stage index.  The compiler's wait-count insertion can then tell
+// a direct global->LDS load into one stage from an LDS read of another, and
+// the reads of the tile being consumed do not wait for the tiles in flight.
+__shared__ __attribute__((aligned(1024))) char lds_stage0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char lds_stage1[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char lds_stage2[kStageBytes];
+
+// Set by a wave whose logits overflow the segment's reference, one word per
+// wave so that no two waves write the same word; read by all after a barrier
+// (every access is ordered by the barriers' memory clobbers).
+__shared__ int lds_restart[4];
+
+// The RoPE query of every head, as the B operands of the four RoPE K-steps:
+// 16 bytes per lane, [wave][step][lane].  Kept in LDS rather than in VGPRs,
+// which the q~ operands and the tile step fill.
+constexpr int kQropeBytes = 4 * (kDr / 16) * 64 * 16;  // up to 4 wavefronts: 16 KB
+__shared__ __attribute__((aligned(16))) char lds_qrope[kQropeBytes];
+
+template <int S>
+__device__ __forceinline__ char* stage_buf() {
+  static_assert(S >= 0 && S < kStages, "stage index");
+  if constexpr (S == 0) return lds_stage0;
+  else if constexpr (S == 1) return lds_stage1;
+  else return lds_stage2;
+}
 
 // Wait until at most N vector memory operations of this wavefront are in
 // flight.  s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]
@@ -65,6 +100,16 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup index in the plan for hardware workgroup `hw` of `n`.  Workgroups
+// are dispatched round-robin over the 8 XCDs, each with its own L2; this
+// numbering gives every XCD a contiguous block of plan ranges, so the
+// workgroups of one sequence share the L2 that holds its queries.
+__device__ __forceinline__ int plan_wg(int hw, int n) {
+  constexpr int kXcds = 8;
+  if (n % kXcds != 0) return hw;
+  return (hw % kXcds) * (n / kXcds) + hw / kXcds;
+}
+
 struct Args {
   const int32_t* seq_lens;
   int B, H, G, L_cap, n_wg;
@@ -72,7 +117,6 @@ struct Args {
   const uint16_t* rope;
   const float* alpha;
   const uint16_t* q_tilde;
-  const float* alpha_q;
   const uint16_t* q_rope;
   float* part;
   float* o_lat;
@@ -88,59 +132,237 @@ struct TileLoads {
   static constexpr int total = lat + rope + alpha;
 };
 
-// Issue the direct global->LDS loads of one tile into a stage buffer.
-// LDS layout of a stage:
+// The sequence a segment belongs to (wave-uniform values).
+struct Seq {
+  const char* lat;    // latent rows of the sequence, 1 KB each
+  const char* rope;   // RoPE rows, 128 B each
+  const char* alpha;  // alpha rows, 4*G B each
+  int L;              // sequence length
+};
+
+// Per-wavefront state carried across the tiles of a segment.
+struct Wave {
+  bf16x8 qt[kR / 16];   // q~ of the wave's 32 heads (B operand, K = latent dims)
+  f32x16 O[kR / 32];    // O^T accumulator: 16 blocks of 32 dims x 32 heads
+  float m_ref;          // reference max of the lane's head (exp2 domain)
+  float l_run;          // running sum of the softmax weights (this lane's tokens)
+  bool have_ref;
+};
+
+// Issue the direct global->LDS loads of tile `tile` (of its sequence) into
+// stage S.  LDS layout of a stage:
 //   latent: token-major rows of kLatRow bytes (1 KB of data + 48 B pad); one
 //           load instruction moves one row.  The 1072-byte stride (67 16-byte
 //           units, 3 mod 16) spreads both the QK row reads and the transposed
 //           PV reads over distinct bank groups.
 //   rope:   chunk-major, position 32*c + t for 16-byte chunk c of token t.
 //   alpha:  [g][32 tokens] floats.
-template <bool QKN, int NW>
-__device__ __forceinline__ void issue_tile(const Args& a, char* stage, const uint16_t* lat_b,
-                                           const uint16_t* rope_b, const float* alpha_b, int t0,
-                                           int L, int wave, int lane) {
-  // Scalar row base + zero-extended 32-bit lane offset lets the compiler use
-  // the SGPR-base form of the load.
-  const uint32_t lane16 = (uint32_t)lane << 4;
+// Rows past the end of the sequence repeat its last row (masked later).
+template <bool QKN, int NW, int S>
+__device__ __forceinline__ void issue_tile(const Seq& sq, int G, int tile, int wave, int lane) {
+  char* st = stage_buf<S>();
+  // Opaque copies of the tile's first row and the lane offset keep the address
+  // arithmetic here, as a scalar row base plus a 32-bit lane offset (the
+  // scalar-base form of the load).  Otherwise the first two tiles' per-lane
+  // 64-bit addresses are hoisted out of the segment's re-stream loop and stay
+  // live, in spilled registers, across the whole segment.
+  int t0 = tile * kTile;
+  asm volatile("" : "+s"(t0));
+  uint32_t lane16 = (uint32_t)lane << 4;
+  asm volatile("" : "+v"(lane16));
 #pragma unroll
   for (int i = 0; i < TileLoads<QKN, NW>::lat; ++i) {
     const int tr = wave + i * NW;
-    const int row = min(t0 + tr, L - 1);
-    const char* rowp = (const char*)lat_b + (size_t)row * (kR * 2);
-    __builtin_amdgcn_global_load_lds(QK_GLB(void, rowp + lane16),
-                                     QK_LDS(void, stage + tr * kLatRow), 16, 0, 0);
+    const int row = min(t0 + tr, sq.L - 1);
+    __builtin_amdgcn_global_load_lds(QK_GLB(void, sq.lat + (size_t)row * (kR * 2) + lane16),
+                                     QK_LDS(void, st + tr * kLatRow), 16, 0, 0);
   }
   const int t = lane & 31;
-  const uint32_t rrow = (uint32_t)min(t0 + t, L - 1);
+  const uint32_t rrow = (uint32_t)min(t0 + t, sq.L - 1);
   const uint32_t rope_off = rrow * (kDr * 2) + ((uint32_t)(lane >> 5) << 4);
 #pragma unroll
   for (int i = 0; i < TileLoads<QKN, NW>::rope; ++i) {
     const int blk = wave + i * NW;  // chunks 2*blk, 2*blk+1
-    __builtin_amdgcn_global_load_lds(QK_GLB(void, (const char*)rope_b + blk * 32 + rope_off),
-                                     QK_LDS(void, stage + kLatBytes + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(QK_GLB(void, sq.rope + blk * 32 + rope_off),
+                                     QK_LDS(void, st + kLatBytes + blk * 1024), 16, 0, 0);
   }
-  if (QKN) {
-    const uint32_t a_off = rrow * (uint32_t)(a.G * 4);
+  if constexpr (QKN) {
+    const uint32_t a_off = rrow * (uint32_t)(G * 4);
 #pragma unroll
     for (int i = 0; i < TileLoads<QKN, NW>::alpha; ++i) {
       const int blk = wave + i * NW;  // groups 2*blk, 2*blk+1
       int g = 2 * blk + (lane >> 5);
-      g = g < a.G ? g : a.G - 1;
-      __builtin_amdgcn_global_load_lds(QK_GLB(void, (const char*)alpha_b + a_off + (uint32_t)(g * 4)),
-                                       QK_LDS(void, stage + kLatBytes + kRopeBytes + blk * 256),
+      g = g < G ? g : G - 1;
+      __builtin_amdgcn_global_load_lds(QK_GLB(void, sq.alpha + a_off + (uint32_t)(g * 4)),
+                                       QK_LDS(void, st + kLatBytes + kRopeBytes + blk * 256),
                                        4, 0, 0);
     }
   }
 }
 
+// Order fence: the compiler's scheduler keeps instructions on their side, so
+// the software pipelines below issue in the order they are written.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+constexpr int kQkSteps = kR / 16 + kDr / 16;  // 36 K-steps of 16 (latent, then RoPE)
+constexpr int kQkAhead = 4;                    // LDS reads in flight ahead of the QK MFMAs
+constexpr int kPvSteps = 2 * (kR / 32);        // 32: 2 token halves x 16 dim blocks
+constexpr int kPvAhead = 3;                    // C^T operands in flight ahead of the PV MFMAs
+
+// One tile of a segment: wait for its loads, prefetch the tile two ahead into
+// the stage consumed by the previous step, then logits, softmax weights and
+// the P.C accumulation.  i: tile index within the segment (nt tiles), staged
+// in buffer S = i % 3; `tile0` is the segment's first tile in its sequence.
+// Every step waits for its own tile only (the tile after it stays in flight)
+// and prefetches the tile two ahead, clamped to the segment's last tile: near
+// the end of a segment the prefetch re-reads a tile the L2 still holds, into a
+// stage nobody reads.  Keeping the wait and the prefetch free of branches lets
+// the compiler's wait-count insertion track each stage exactly; with
+// branches it merges the paths conservatively and then waits for every load
+// in flight before reading a tile.
+template <bool QKN, int NW, int S>
+__device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, int G, int tile0, int i, int nt,
+                                          int wave, int lane, int g) {
+  if (i + 1 < nt) wait_vmcnt<TileLoads<QKN, NW>::total>();
+  else wait_vmcnt<0>();
+  block_sync();  // the tile is in LDS for every wave; stage (S+2)%3 is free
+  const char* st = stage_buf<S>();
+  const int hf = lane >> 5;
+  const int m = lane & 31;
+
+  // ---- logits S^T[32 tokens][32 heads] ----
+  // K-steps 0..3 read 16 RoPE dims of token m, steps 4..35 16 latent dims; the
+  // A operand of step s + kQkAhead is read while step s multiplies.  The RoPE
+  // sum is finished first and moved to VGPRs, so the latent chain reuses its
+  // accumulator registers: every MFMA result lands in AGPRs, which the O^T
+  // accumulator otherwise fills, so each extra live accumulator costs moves.
+  constexpr int kRopeSteps = kDr / 16;
+  const char* row = st + m * kLatRow + hf * 16;
+  const char* rrow = st + kLatBytes + (32 * hf + m) * 16;
+  auto qk_a = [&](int s) -> const bf16x8* {
+    return (const bf16x8*)(s < kRopeSteps ? rrow + s * 1024 : row + (s - kRopeSteps) * 32);
+  };
+  f32x16 sc, sr;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) { sc[j] = 0.f; sr[j] = 0.f; }
+  f32x4 ak[4];
+  const float* al = (const float*)(st + kLatBytes + kRopeBytes) + g * 32 + 4 * hf;
+  bf16x8 av[kQkAhead];
+  bf16x8 qr[kRopeSteps];
+  fence();
+#pragma unroll
+  for (int k = 0; k < kQkAhead; ++k) av[k] = *qk_a(k);
+  const bf16x8* qrl = (const bf16x8*)(lds_qrope + (wave * kRopeSteps * 64 + lane) * 16);
+#pragma unroll
+  for (int k = 0; k < kRopeSteps; ++k) qr[k] = qrl[k * 64];
+#pragma unroll
+  for (int s = 0; s < kQkSteps; ++s) {
+    fence();
+    if (QKN && s == kRopeSteps) asm volatile("" : "+v"(sr));  // RoPE sum to VGPRs
+    if (s < kRopeSteps) {
+      if constexpr (QKN) sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], qr[s], sr, 0, 0, 0);
+      else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], qr[s], sc, 0, 0, 0);
+    } else {
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], w.qt[s - kRopeSteps], sc, 0, 0, 0);
+    }
+    if (s + kQkAhead < kQkSteps) av[s % kQkAhead] = *qk_a(s + kQkAhead);
+    else if (QKN && s + kQkAhead - kQkSteps < 4) {
+      const int q = s + kQkAhead - kQkSteps;  // alpha^k of the lane's tokens 8q+4hf..+3
+      ak[q] = *(const f32x4*)(al + 8 * q);
+    }
+  }
+  fence();
+
+  // Prefetch the tile two ahead.  Issued after the first reads of this tile:
+  // where the compiler cannot prove which stages have loads in flight it
+  // waits for all of them before the first read, and then only the tile
+  // issued a step ago is still in flight.
+  if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, G, tile0 + i + 2, wave, lane);
+
+  // The first C^T operands of P.C do not depend on the softmax: read them now.
+  // lane (in its 16-lane group): token 4*hf + (s16>>2) of the 16-token step,
+  // 4 dims at 32*mb + 16*dblk + 4*(s16&3); step k = 16*ks + mb.
+  const int s16 = lane & 15, dblk = (lane >> 4) & 1;
+  const char* pvb = st + (4 * hf + (s16 >> 2)) * kLatRow + 32 * dblk + 8 * (s16 & 3);
+  auto pv_a = [&](int k) -> const char* {
+    return pvb + (16 * (k / (kR / 32))) * kLatRow + 64 * (k % (kR / 32));
+  };
+  bf16x4 plo[kPvAhead], phi[kPvAhead];
+#pragma unroll
+  for (int k = 0; k < kPvAhead; ++k) {
+    plo[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k)));
+    phi[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k) + 8 * kLatRow));
+  }
+  fence();
+
+  // ---- row-column scaling, mask, softmax weights (exp2 domain) ----
+  // reg j holds token 8*(j/4) + 4*hf + j%4
+  float lg[16];
+  if constexpr (QKN) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lg[j] = sc[j] * ak[j >> 2][j & 3] + sr[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lg[j] = sc[j];
+  }
+  const int thr = sq.L - (tile0 + i) * kTile - 4 * hf;  // token 4*hf + c is real iff c < thr
+  if (thr < kTile) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (8 * (j >> 2) + (j & 3) >= thr) lg[j] = -INFINITY;
+  }
+  float mt = lg[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) mt = fmaxf(mt, lg[j]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  if (!w.have_ref) {  // the first tile of the segment sets the per-head reference
+    w.m_ref = mt;
+    w.have_ref = true;
+  }
+  if (__ballot(mt > w.m_ref + kOverflowLog2) != 0) {
+    w.m_ref = fmaxf(w.m_ref, mt);
+    lds_restart[wave] = 1;
+  }
+  bf16x8 pb[2];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(lg[j] - w.m_ref);
+  // l sums the weights as rounded for P.C: each dword holds two bf16, whose
+  // fp32 values are the dword's high half and its low half shifted up.
+  float ls = 0.f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t* u = (const uint32_t*)&pb[k];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      ls += __uint_as_float(u[d] << 16) + __uint_as_float(u[d] & 0xFFFF0000u);
+  }
+  w.l_run += ls;
+
+  // ---- O^T[512 dims][32 heads] += C^T . P^T ----
+#pragma unroll
+  for (int k = 0; k < kPvSteps; ++k) {
+    fence();
+    const int slot = k % kPvAhead;
+    const bf16x8 a8 = {plo[slot][0], plo[slot][1], plo[slot][2], plo[slot][3],
+                       phi[slot][0], phi[slot][1], phi[slot][2], phi[slot][3]};
+    const int mb = k % (kR / 32);
+    w.O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[k / (kR / 32)], w.O[mb], 0, 0, 0);
+    if (k + kPvAhead < kPvSteps) {
+      plo[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k + kPvAhead)));
+      phi[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          QK_LDS(bf16x4, pv_a(k + kPvAhead) + 8 * kLatRow));
+    }
+  }
+  fence();
+}
+
 template <bool QKN, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
-  __shared__ int P[kMaxBatch + 1];
-  __shared__ int restart_flag;
-  volatile int* restart = &restart_flag;
-  if (threadIdx.x == 0) restart_flag = 0;
+  // The tile prefix takes LDS offset 0 (largest alignment is placed first): a
+  // stage buffer at offset 0 loses the alias information that lets its reads
+  // run ahead of the loads in flight into the other stages.
+  __shared__ __attribute__((aligned(2048))) int P[kMaxBatch + 1];
+  if (threadIdx.x < 4) lds_restart[threadIdx.x] = 0;
   build_tile_prefix(a.seq_lens, a.B, a.L_cap, P);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -150,156 +372,64 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
   const int head = wave * 32 + n;  // head index in the layer
   const int g = (head * a.G) / a.H;
   const int64_t N = __builtin_amdgcn_readfirstlane(P[a.B]);
-  const int p = blockIdx.x;
+  const int p = plan_wg(blockIdx.x, a.n_wg);
   int64_t x = wg_start(p, N, a.n_wg);
   const int64_t e = wg_start(p + 1, N, a.n_wg);
   bool first_seg = true;
+  Wave w;
 
   while (x < e) {
     const int b = __builtin_amdgcn_readfirstlane(seq_of(P, a.B, x));
-    const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+    Seq sq;
+    sq.L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
     const int64_t s0 = __builtin_amdgcn_readfirstlane(P[b]);
     const int64_t s1 = __builtin_amdgcn_readfirstlane(P[b + 1]);
     const int64_t seg_end = e < s1 ? e : s1;
-    const int tile_first = (int)(x - s0);
+    const int tile0 = (int)(x - s0);
     const int nt = (int)(seg_end - x);
-
-    // Query operands for this sequence, kept in registers for the segment.
+    const size_t seq_row0 = (size_t)b * a.L_cap;
+    sq.lat = (const char*)(a.lat + seq_row0 * kR);
+    sq.rope = (const char*)(a.rope + seq_row0 * kDr);
+    sq.alpha = QKN ? (const char*)(a.alpha + seq_row0 * a.G) : nullptr;
     const size_t qrow = (size_t)b * a.H + head;
-    bf16x8 qt[kR / 16];
+
+    // Query operands for this sequence: q~ in registers, the RoPE query in
+    // LDS, both kept for the segment.
 #pragma unroll
     for (int s = 0; s < kR / 16; ++s)
-      qt[s] = *(const bf16x8*)(a.q_tilde + qrow * kR + s * 16 + hf * 8);
-    bf16x8 qr[kDr / 16];
+      w.qt[s] = *(const bf16x8*)(a.q_tilde + qrow * kR + s * 16 + hf * 8);
+    {
+      bf16x8* qrl = (bf16x8*)(lds_qrope + (wave * (kDr / 16) * 64 + lane) * 16);
 #pragma unroll
-    for (int s = 0; s < kDr / 16; ++s)
-      qr[s] = *(const bf16x8*)(a.q_rope + qrow * kDr + s * 16 + hf * 8);
-    const float aq = QKN ? a.alpha_q[qrow] : 1.0f;
-    const size_t seq_row0 = (size_t)b * a.L_cap;
-    const uint16_t* lat_b = a.lat + seq_row0 * kR;
-    const uint16_t* rope_b = a.rope + seq_row0 * kDr;
-    const float* alpha_b = QKN ? a.alpha + seq_row0 * a.G : nullptr;
-
-    f32x16 O[kR / 32];
-    float m_ref = -INFINITY, l_run = 0.f;
-    bool have_ref = false;
+      for (int s = 0; s < kDr / 16; ++s)
+        qrl[s * 64] = *(const bf16x8*)(a.q_rope + qrow * kDr + s * 16 + hf * 8);
+    }
+    w.m_ref = -INFINITY;
+    w.have_ref = false;
     for (;;) {  // one pass over the segment; repeated only if a logit overflows the reference
 #pragma unroll
       for (int ii = 0; ii < kR / 32; ++ii)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) O[ii][j] = 0.f;
-      l_run = 0.f;
-#pragma unroll
-      for (int j = 0; j < kStages - 1; ++j)
-        if (j < nt) issue_tile<QKN, NW>(a, smem + j * kStageBytes, lat_b, rope_b, alpha_b,
-                                        (tile_first + j) * kTile, L, wave, lane);
-      int cur = 0;
-      for (int i = 0; i < nt; ++i) {
-        if (i + 1 < nt) wait_vmcnt<TileLoads<QKN, NW>::total>();
-        else wait_vmcnt<0>();
-        block_sync();
-        const int nxt = cur == 0 ? kStages - 1 : cur - 1;
-        if (i + kStages - 1 < nt)
-          issue_tile<QKN, NW>(a, smem + nxt * kStageBytes, lat_b, rope_b, alpha_b,
-                              (tile_first + i + kStages - 1) * kTile, L, wave, lane);
-        const char* st = smem + cur * kStageBytes;
-        cur = cur == kStages - 1 ? 0 : cur + 1;
-        const int t0 = (tile_first + i) * kTile;
-        // ---- logits S^T[32 tokens][32 heads] ----
-        f32x16 sc, sr;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) { sc[j] = 0.f; sr[j] = 0.f; }
-        {
-          const int m = lane & 31;
-          const char* row = st + m * kLatRow + hf * 16;
-#pragma unroll
-          for (int s = 0; s < kR / 16; ++s) {
-            bf16x8 av = *(const bf16x8*)(row + s * 32);
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qt[s], sc, 0, 0, 0);
-          }
-          const char* rrow = st + kLatBytes + (32 * hf + m) * 16;
-#pragma unroll
-          for (int s = 0; s < kDr / 16; ++s) {
-            bf16x8 av = *(const bf16x8*)(rrow + s * 1024);
-            if (QKN) sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qr[s], sr, 0, 0, 0);
-            else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qr[s], sc, 0, 0, 0);
-          }
-        }
-
-        // ---- row-column scaling, mask, softmax weights (exp2 domain) ----
-        float lg[16];
-        if (QKN) {
-          const float* al = (const float*)(st + kLatBytes + kRopeBytes) + g * 32 + 4 * hf;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 ak = *(const f32x4*)(al + 8 * q);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) lg[4 * q + j] = sc[4 * q + j] * (aq * ak[j]) + sr[4 * q + j];
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) lg[j] = sc[j];
-        }
-        const int valid = L - t0;  // tokens < valid are real
-        if (valid < kTile) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int tok = 8 * (j >> 2) + 4 * hf + (j & 3);
-            if (tok >= valid) lg[j] = -INFINITY;
-          }
-        }
-        float mt = lg[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) mt = fmaxf(mt, lg[j]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        if (!have_ref) {  // first tile of the segment sets the per-head reference
-          m_ref = mt;
-          have_ref = true;
-        }
-        if (__ballot(mt > m_ref + kOverflowLog2) != 0) {
-          m_ref = fmaxf(m_ref, mt);
-          *restart = 1;
-        }
-        bf16x8 pb[2];
-        float ls = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const __bf16 v = (__bf16)exp2f(lg[j] - m_ref);
-          pb[j >> 3][j & 7] = v;
-          ls += (float)v;
-        }
-        l_run += ls;
-
-        // ---- O^T[512 dims][32 heads] += C^T . P^T ----
-        {
-          // lane (in its 16-lane group): token 4*hf + (s16>>2) of the 16-token
-          // step, 4 dims at 32*mb + 16*dblk + 4*(s16&3)
-          const int s16 = lane & 15, dblk = (lane >> 4) & 1;
-          const char* pvb = st + (4 * hf + (s16 >> 2)) * kLatRow + 32 * dblk + 8 * (s16 & 3);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-            for (int mb = 0; mb < kR / 32; ++mb) {
-              const char* pa = pvb + (16 * ks) * kLatRow + 64 * mb;
-              bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa));
-              bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa + 8 * kLatRow));
-              bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], O[mb], 0, 0, 0);
-            }
-          }
-        }
+        for (int j = 0; j < 16; ++j) w.O[ii][j] = 0.f;
+      w.l_run = 0.f;
+      issue_tile<QKN, NW, 0>(sq, a.G, tile0, wave, lane);
+      if (nt > 1) issue_tile<QKN, NW, 1>(sq, a.G, tile0 + 1, wave, lane);
+      for (int i = 0; i < nt; i += kStages) {
+        tile_step<QKN, NW, 0>(w, sq, a.G, tile0, i, nt, wave, lane, g);
+        if (i + 1 < nt) tile_step<QKN, NW, 1>(w, sq, a.G, tile0, i + 1, nt, wave, lane, g);
+        if (i + 2 < nt) tile_step<QKN, NW, 2>(w, sq, a.G, tile0, i + 2, nt, wave, lane, g);
       }
       block_sync();
-      if (!*restart) break;
+      if (!(lds_restart[0] | lds_restart[1] | lds_restart[2] | lds_restart[3])) break;
       // A logit exceeded the reference by more than 2^kOverflowLog2: stream the
       // segment again with the raised reference (exact; never taken for
       // normalised logits).
       block_sync();
-      if (threadIdx.x == 0) *restart = 0;
+      if (lane == 0) lds_restart[wave] = 0;
     }
     // ---- segment epilogue ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float m_run = m_ref;
+    const float l_tot = w.l_run + __shfl_xor(w.l_run, 32, 64);
+    const float m_run = w.m_ref;
     const bool complete = (x == s0) && (seg_end == s1);
     if (complete) {
       const float inv = 1.0f / l_tot;
@@ -308,8 +438,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
       for (int mb = 0; mb < kR / 32; ++mb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          f32x4 v = {O[mb][4 * q] * inv, O[mb][4 * q + 1] * inv, O[mb][4 * q + 2] * inv,
-                     O[mb][4 * q + 3] * inv};
+          f32x4 v = {w.O[mb][4 * q] * inv, w.O[mb][4 * q + 1] * inv, w.O[mb][4 * q + 2] * inv,
+                     w.O[mb][4 * q + 3] * inv};
           *(f32x4*)(out + 32 * mb + 8 * q + 4 * hf) = v;
         }
       if (hf == 0 && a.lse) a.lse[qrow] = (m_run + log2f(l_tot)) * kLn2;
@@ -325,7 +455,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
       for (int mb = 0; mb < kR / 32; ++mb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          f32x4 v = {O[mb][4 * q], O[mb][4 * q + 1], O[mb][4 * q + 2], O[mb][4 * q + 3]};
+          f32x4 v = {w.O[mb][4 * q], w.O[mb][4 * q + 1], w.O[mb][4 * q + 2], w.O[mb][4 * q + 3]};
           *(f32x4*)(Op + 32 * mb + 8 * q + 4 * hf) = v;
         }
     }
@@ -353,7 +483,6 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, const int32_t* seq_lens, 
   a.rope = (const uint16_t*)rope;
   a.alpha = alpha;
   a.q_tilde = (const uint16_t*)(wsb + ws.q_tilde);
-  a.alpha_q = (const float*)(wsb + ws.alpha_q);
   a.q_rope = (const uint16_t*)(wsb + ws.q_rope);
   a.part = (float*)(wsb + ws.partials);
   a.o_lat = o_lat;

@@ -8,7 +8,7 @@
 // summary, Methodology: Static Weight Absorption, the decode-logit formula and
 // Blockwise Normalization).  tau*log2(e) is folded into alpha^q and q^R so the
 // decode kernel works in the exp2 domain.  In plain mode alpha^q = tau*log2(e)
-// and q^R is only rotated.
+// and q^R is only rotated.  The bf16 path also folds alpha^q into q~.
 #include "device_common.h"
 #include "qkmla_internal.h"
 
@@ -87,9 +87,23 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
   const uint16_t* A = q_c + ((size_t)b * H + h0) * dc;
   const uint16_t* W = w_qabs + (size_t)g * r * dc;
   const int m = lane & 15, kq = lane >> 4;
-  // Plain mode has one logit accumulator for content + RoPE, so the softmax
-  // scale goes into q~ as well.
-  const float qs = qk_norm ? 1.0f : tau * kLog2e;
+  // Per-head scale folded into q~: the decode logit is then one FMA,
+  // S_c * alpha^k + S_r, with alpha^q, the softmax scale and log2(e) already
+  // in q~ (QK-norm); plain mode has one accumulator for content + RoPE, so
+  // only the softmax scale and log2(e) go in.
+  __shared__ float qscale[16];
+  for (int hh = wave; hh < 16; hh += 4) {
+    const uint16_t* qh = A + (size_t)hh * dc;
+    float ss = 0.f;
+    for (int e = lane; e < dc; e += 64) {
+      const float v = bf16_to_f32(qh[e]);
+      ss += v * v;
+    }
+    ss = wave_sum(ss);
+    if (lane == 0)
+      qscale[hh] = (qk_norm ? 1.0f / sqrtf(ss / (float)dc + eps) : 1.0f) * (tau * kLog2e);
+  }
+  __syncthreads();
   const int nb_per_wave = (r / 16) / 4;     // 8 for r = 512
   const int ksteps = dc / 32;               // 4 for d_c = 128
   constexpr int kMaxK = 8;                  // d_c <= 256 on this path
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int hh = 4 * kq + i;
-      q_tilde[((size_t)b * H + h0 + hh) * r + nb * 16 + m] = f32_to_bf16(acc[i] * qs);
+      q_tilde[((size_t)b * H + h0 + hh) * r + nb * 16 + m] = f32_to_bf16(acc[i] * qscale[hh]);
     }
   }
   __syncthreads();  // cs ready

@@ -121,9 +121,10 @@ class Device:
                 kab[off:off + sz] = np.frombuffer(bytes(src), np.uint8)
                 ai += 1
             groups = self.group_filter(name, (gx, gy, gz)) if self.group_filter else None
-            t0, n0 = time.time(), self.emu.stats.insts
+            t0, n0, d0 = time.time(), self.emu.stats.insts, self.emu.stats.lds_dma
             self.emu.run(k, (gx, gy, gz), (bx, by, bz), shmem, kab.ctypes.data, groups)
-            rec = (name, (gx, gy, gz), (bx, by, bz), self.emu.stats.insts - n0, time.time() - t0)
+            rec = (name, (gx, gy, gz), (bx, by, bz), self.emu.stats.insts - n0, time.time() - t0,
+                   self.emu.stats.lds_dma - d0)
             self.launches.append(rec)
             if self.verbose:
                 print(f"  [emu] {name[:70]} grid {rec[1]} block {rec[2]}: {rec[3]} instructions, "

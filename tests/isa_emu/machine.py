@@ -150,6 +150,7 @@ class Memory:
 class Stats:
     def __init__(self):
         self.insts = 0
+        self.lds_dma = 0                    # global->LDS load instructions issued
         self.by_op: collections.Counter = collections.Counter()
         self.warnings: List[str] = []
 

@@ -1539,6 +1539,7 @@ def _gload_lds(nb):
             raise EmuError("LDS DMA into bytes with another DMA still in flight")
         lds_mark(w, np.unique(idx), "w", i.text + " (issue)")
         wg.dma_pending[idx] += 1
+        w.emu.stats.lds_dma += 1
         push_vm(w, Pend(w, dma=(idx, data.reshape(-1, 4)), what=i.text))
     return run
 
@@ -1641,7 +1642,9 @@ def _sstore_priv(nb):
 
 HANDLERS["scratch_load_dword"] = _sload_priv(4)
 HANDLERS["scratch_load_dwordx2"] = _sload_priv(8)
+HANDLERS["scratch_load_dwordx3"] = _sload_priv(12)
 HANDLERS["scratch_load_dwordx4"] = _sload_priv(16)
 HANDLERS["scratch_store_dword"] = _sstore_priv(4)
 HANDLERS["scratch_store_dwordx2"] = _sstore_priv(8)
+HANDLERS["scratch_store_dwordx3"] = _sstore_priv(12)
 HANDLERS["scratch_store_dwordx4"] = _sstore_priv(16)

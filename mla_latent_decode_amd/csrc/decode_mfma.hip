@@ -226,6 +226,8 @@ __device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, int G, int til
   if (i + 1 < nt) wait_vmcnt<TileLoads<QKN, NW>::total>();
   else wait_vmcnt<0>();
   block_sync();  // the tile is in LDS for every wave; stage (S+2)%3 is free
+  if constexpr (S != 0)
+    if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, G, tile0 + i + 2, wave, lane);
   const char* st = stage_buf<S>();
   const int hf = lane >> 5;
   const int m = lane & 31;
@@ -273,11 +275,14 @@ __device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, int G, int til
   }
   fence();
 
-  // Prefetch the tile two ahead.  Issued after the first reads of this tile:
-  // where the compiler cannot prove which stages have loads in flight it
-  // waits for all of them before the first read, and then only the tile
-  // issued a step ago is still in flight.
-  if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, G, tile0 + i + 2, wave, lane);
+  // Prefetch the tile two ahead: right after the barrier in steps 1 and 2,
+  // after the QK reads in step 0.  At step 0 the compiler cannot prove which
+  // stages still have loads in flight (the loop is also left after step 0 or
+  // step 1) and waits for all of them before the first read; issued late, the
+  // prefetch is not among them, and the tile that is has been in flight for a
+  // whole step.
+  if constexpr (S == 0)
+    if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, G, tile0 + i + 2, wave, lane);
 
   // The first C^T operands of P.C do not depend on the softmax: read them now.
   // lane (in its 16-lane group): token 4*hf + (s16>>2) of the 16-token step,

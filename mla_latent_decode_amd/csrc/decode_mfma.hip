@@ -29,8 +29,11 @@
 //        (e = 0..3), which turns 4 token rows into 4 tokens of one dim.
 //
 // Register budget per lane (one wavefront per SIMD): the O^T accumulator
-// (512 dims x 32 heads fp32) fills the 256 AGPRs; q~ and the RoPE query take
-// 144 VGPRs; a tile step needs about 80 more.  Nothing spills.
+// (512 dims x 32 heads fp32) fills the 256 AGPRs and q~ takes 128 VGPRs; the
+// RoPE query sits in LDS.  MFMA results always land in AGPRs here, so each
+// step moves one O^T block (16 AGPRs) out to VGPRs and back while the logits
+// occupy its registers.  The tile loop does not spill; the segment prologue
+// and epilogue do, a few registers once per segment.
 #include <type_traits>
 
 #include "device_common.h"

@@ -41,6 +41,67 @@ hipError_t launch_absorb(const Cfg& c, const float* w_uk, const float* gq, const
   return hipGetLastError();
 }
 
+// Copy the latent rows of tokens tok0..tok0+ntok-1 and write their RoPE keys,
+// RMS-normalised on their own (QK-norm) and rotated by the cache row.  A
+// sequence whose rows would fall outside the cache gets no writes and sets
+// QKMLA_DEV_BAD_POSITION.  Called by every thread of the block; rsum: LDS
+// scratch of ntok floats.
+template <typename T>
+__device__ void copy_rows_and_rope(int tok0, int ntok, int batch, int n_new,
+                                   const T* __restrict__ c_new, const T* __restrict__ kr_new,
+                                   const float* __restrict__ gkr,
+                                   const int32_t* __restrict__ positions, int L_cap,
+                                   T* __restrict__ lat, T* __restrict__ rope, int32_t* status,
+                                   int r, int dr, float eps, float base, int qk_norm,
+                                   float* rsum) {
+  const int T_total = batch * n_new;
+  const int tid = threadIdx.x;
+  for (int k = 0; k < ntok; ++k) {
+    int tok = tok0 + k;
+    if (tok >= T_total) break;
+    int b = tok / n_new, i = tok % n_new;
+    int pos0 = positions[b];
+    bool bad = pos0 < 0 || (int64_t)pos0 + n_new > L_cap;
+    if (bad) {
+      if (tid == 0 && i == 0 && status) atomicOr(status, QKMLA_DEV_BAD_POSITION);
+      continue;
+    }
+    int row = pos0 + i;
+    const T* src = c_new + (size_t)tok * r;
+    T* dst = lat + ((size_t)b * L_cap + row) * r;
+    for (int e = tid; e < r; e += blockDim.x) dst[e] = src[e];
+    // RoPE key: optional RMSNorm over d_r, then rotate pairs by row position.
+    const T* ks = kr_new + (size_t)tok * dr;
+    float scale = 1.f;
+    if (qk_norm) {
+      if (tid < 64) {
+        float acc = 0.f;
+        for (int e = tid; e < dr; e += 64) {
+          float v = Elem<T>::load(ks, e);
+          acc += v * v;
+        }
+        acc = wave_sum(acc);
+        if (tid == 0) rsum[k] = acc;
+      }
+      __syncthreads();
+      scale = 1.0f / sqrtf(rsum[k] / (float)dr + eps);
+    }
+    T* rdst = rope + ((size_t)b * L_cap + row) * dr;
+    for (int pi = tid; pi < dr / 2; pi += blockDim.x) {
+      float x0 = Elem<T>::load(ks, 2 * pi), x1 = Elem<T>::load(ks, 2 * pi + 1);
+      if (qk_norm) {
+        x0 = x0 * scale * gkr[2 * pi];
+        x1 = x1 * scale * gkr[2 * pi + 1];
+      }
+      float cs_, sn_;
+      rope_cos_sin(row, pi, dr, base, &cs_, &sn_);
+      Elem<T>::store(rdst, 2 * pi, x0 * cs_ - x1 * sn_);
+      Elem<T>::store(rdst, 2 * pi + 1, x0 * sn_ + x1 * cs_);
+    }
+    __syncthreads();
+  }
+}
+
 // One workgroup per (block of kAppendTok new tokens, duty).  Duty y < G
 // computes alpha^k for group y; duty y == G (or 0 in plain mode) copies the
 // latent rows and writes the normalised, rotated RoPE key.
@@ -65,50 +126,8 @@ __global__ __launch_bounds__(256) void append_kernel(
   const int tid = threadIdx.x;
 
   if (copy_duty) {
-    for (int k = 0; k < kAppendTok; ++k) {
-      int tok = tok0 + k;
-      if (tok >= T_total) break;
-      int b = tok / n_new, i = tok % n_new;
-      int pos0 = positions[b];
-      bool bad = pos0 < 0 || (int64_t)pos0 + n_new > L_cap;
-      if (bad) {
-        if (tid == 0 && i == 0 && status) atomicOr(status, QKMLA_DEV_BAD_POSITION);
-        continue;
-      }
-      int row = pos0 + i;
-      const T* src = c_new + (size_t)tok * r;
-      T* dst = lat + ((size_t)b * L_cap + row) * r;
-      for (int e = tid; e < r; e += blockDim.x) dst[e] = src[e];
-      // RoPE key: optional RMSNorm over d_r, then rotate pairs by row position.
-      const T* ks = kr_new + (size_t)tok * dr;
-      float scale = 1.f;
-      if (qk_norm) {
-        if (tid < 64) {
-          float acc = 0.f;
-          for (int e = tid; e < dr; e += 64) {
-            float v = Elem<T>::load(ks, e);
-            acc += v * v;
-          }
-          acc = wave_sum(acc);
-          if (tid == 0) rsum[k] = acc;
-        }
-        __syncthreads();
-        scale = 1.0f / sqrtf(rsum[k] / (float)dr + eps);
-      }
-      T* rdst = rope + ((size_t)b * L_cap + row) * dr;
-      for (int pi = tid; pi < dr / 2; pi += blockDim.x) {
-        float x0 = Elem<T>::load(ks, 2 * pi), x1 = Elem<T>::load(ks, 2 * pi + 1);
-        if (qk_norm) {
-          x0 = x0 * scale * gkr[2 * pi];
-          x1 = x1 * scale * gkr[2 * pi + 1];
-        }
-        float cs_, sn_;
-        rope_cos_sin(row, pi, dr, base, &cs_, &sn_);
-        Elem<T>::store(rdst, 2 * pi, x0 * cs_ - x1 * sn_);
-        Elem<T>::store(rdst, 2 * pi + 1, x0 * sn_ + x1 * cs_);
-      }
-      __syncthreads();
-    }
+    copy_rows_and_rope<T>(tok0, kAppendTok, batch, n_new, c_new, kr_new, gkr, positions, L_cap,
+                          lat, rope, status, r, dr, eps, base, qk_norm, rsum);
     return;
   }
 
@@ -156,11 +175,130 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
+// bf16 caches: one workgroup per (kAlphaTok new tokens, duty).  Duty y < G
+// computes alpha^k of group y on MFMA; duty y == G (0 in plain mode) copies
+// the latent rows and writes the RoPE keys.
+//   k^T[n][t] = sum_i W^UK_g[i][n] c_t[i]          (mfma_f32_32x32x16_bf16)
+//   alpha^k_{t,g} = 1 / sqrt(mean_n k^T[n][t]^2 + eps)
+// The four waves take output dims n in blocks of 32 (wave w: blocks w, w+4).
+// W^UK stays accurate to about 2^-16: each weight is split into
+// hi = bf16(W) and lo = bf16(W - hi), and both products with the bf16
+// latent are exact, accumulated in fp32.  W^UK_g is staged in LDS in chunks
+// of 32 rows as row-major hi / lo tiles and read with ds_read_b64_tr_b16,
+// which gives the A operand W^T[n][k] with k contiguous: in each 16-lane
+// group lane i receives element i%4 of the 8-byte loads of lanes 4e + i/4.
+// MFMA 32x32x16 layouts: A lane l holds A[m=l%32][k=8(l/32)+j]; B lane l
+// holds B[k=8(l/32)+j][n=l%32]; D lane l reg i holds D[8(i/4)+4(l/32)+i%4][l%32].
+constexpr int kAlphaTok = 32;
+constexpr int kAlphaChunk = 32;
+constexpr int kAlphaMaxDc = 256;
+
+__global__ __launch_bounds__(256) void append_bf16_kernel(
+    int batch, int n_new, const uint16_t* __restrict__ c_new, const uint16_t* __restrict__ kr_new,
+    const float* __restrict__ w_uk, const float* __restrict__ gkr,
+    const int32_t* __restrict__ positions, int L_cap, uint16_t* __restrict__ lat,
+    uint16_t* __restrict__ rope, float* __restrict__ alpha, int32_t* status, int G, int r,
+    int dc, int dr, float eps, float base, int qk_norm) {
+  __shared__ __attribute__((aligned(16))) uint16_t w_hi[kAlphaChunk][kAlphaMaxDc];
+  __shared__ __attribute__((aligned(16))) uint16_t w_lo[kAlphaChunk][kAlphaMaxDc];
+  __shared__ float ssq[4][kAlphaTok];
+  __shared__ float rsum[kAlphaTok];
+  const int T_total = batch * n_new;
+  const int tok0 = blockIdx.x * kAlphaTok;
+  const int duty = blockIdx.y;
+  if (qk_norm ? duty == G : duty == 0) {
+    copy_rows_and_rope<uint16_t>(tok0, kAlphaTok, batch, n_new, c_new, kr_new, gkr, positions,
+                                 L_cap, lat, rope, status, r, dr, eps, base, qk_norm, rsum);
+    return;
+  }
+  const int g = duty;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hf = lane >> 5, t = lane & 31;
+  const int nblk = dc / 32;  // 1..8
+  // B operand: token t's latent row (rows past the last token repeat it)
+  const uint16_t* crow = c_new + (size_t)min(tok0 + t, T_total - 1) * r + hf * 8;
+  // A operand through the transposing read: this lane loads row e (+4) of the
+  // K-step's 16, columns 4q..4q+3 of its 16-column half
+  const int q16 = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
+  const int a_row = 8 * (q16 >> 1) + e;
+  const int a_col = 16 * (q16 & 1) + 4 * q;
+  const float* W = w_uk + (size_t)g * r * dc;
+  f32x16 acc[2];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) { acc[0][j] = 0.f; acc[1][j] = 0.f; }
+  for (int k0 = 0; k0 < r; k0 += kAlphaChunk) {
+    for (int i = tid; i < kAlphaChunk * dc / 4; i += 256) {
+      const int row = i / (dc / 4), c4 = (i % (dc / 4)) * 4;
+      const f32x4 v = *(const f32x4*)(W + (size_t)(k0 + row) * dc + c4);
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hi[j] = f32_to_bf16(v[j]);
+        lo[j] = f32_to_bf16(v[j] - bf16_to_f32(hi[j]));
+      }
+      *(uint2*)&w_hi[row][c4] = uint2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+      *(uint2*)&w_lo[row][c4] = uint2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kAlphaChunk / 16; ++ks) {
+      const bf16x8 bv = *(const bf16x8*)(crow + k0 + ks * 16);
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        const int blk = wave + 4 * bi;
+        if (blk < nblk) {
+          const int rr = ks * 16 + a_row, cc = blk * 32 + a_col;
+          const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_hi[rr][cc]));
+          const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_hi[rr + 4][cc]));
+          const bf16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_lo[rr][cc]));
+          const bf16x4 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_lo[rr + 4][cc]));
+          const bf16x8 ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          const bf16x8 alo = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+          acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc[bi], 0, 0, 0);
+          acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bv, acc[bi], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // the chunk is consumed before the next one overwrites it
+  }
+  // lane l holds k^T[n][t] for 16 dims n of each of its blocks and token t
+  float sq = 0.f;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sq += acc[bi][j] * acc[bi][j];
+  sq += __shfl_xor(sq, 32, 64);
+  if (hf == 0) ssq[wave][t] = sq;
+  __syncthreads();
+  if (tid < kAlphaTok) {
+    const int tok = tok0 + tid;
+    if (tok < T_total) {
+      const int b = tok / n_new, i = tok % n_new;
+      const int pos0 = positions[b];
+      if (!(pos0 < 0 || (int64_t)pos0 + n_new > L_cap)) {
+        const float ss = ssq[0][tid] + ssq[1][tid] + ssq[2][tid] + ssq[3][tid];
+        alpha[((size_t)b * L_cap + pos0 + i) * G + g] = 1.0f / sqrtf(ss / (float)dc + eps);
+      }
+    }
+  }
+}
+
 hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
                          const void* k_rope_new, const float* w_uk, const float* gkr,
                          const int32_t* positions, int L_cap, void* lat, void* rope, float* alpha,
                          int32_t* status, hipStream_t s) {
   int T_total = batch * n_new;
+  // The MFMA kernel reads latent rows and W^UK as 16-byte vectors.
+  const bool vec_ok = ((uintptr_t)c_new % 16 == 0) && ((uintptr_t)w_uk % 16 == 0 || !c.qk_norm);
+  if (c.dtype == QKMLA_BF16 && vec_ok && c.dc % 32 == 0 && c.dc <= kAlphaMaxDc &&
+      c.r % kAlphaChunk == 0) {
+    dim3 g2((unsigned)((T_total + kAlphaTok - 1) / kAlphaTok), c.qk_norm ? c.G + 1 : 1);
+    append_bf16_kernel<<<g2, 256, 0, s>>>(batch, n_new, (const uint16_t*)c_new,
+                                          (const uint16_t*)k_rope_new, w_uk, gkr, positions,
+                                          L_cap, (uint16_t*)lat, (uint16_t*)rope, alpha, status,
+                                          c.G, c.r, c.dc, c.dr, c.eps, c.base, c.qk_norm);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((T_total + kAppendTok - 1) / kAppendTok), c.qk_norm ? c.G + 1 : 1);
   if (c.dtype == QKMLA_BF16)
     append_kernel<uint16_t><<<grid, 256, 0, s>>>(

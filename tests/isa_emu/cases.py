@@ -118,6 +118,29 @@ def bf16_plain_hold(dev):
 
 
 @case
+def bf16_append_caches(dev):
+    """The bf16 append path: alpha^k on MFMA (W^UK split into bf16 hi and lo),
+    latent copy and RoPE key, filled through qkmla_append (bulk, then the
+    step's one-token append), checked element by element against the oracle's
+    append, then the decode on those caches."""
+    lens = (40, 33, 1)
+    s = run_layer(dev, DSV3, lens, 505, "bf16 caches from qkmla_append, step append",
+                  host_fill=False, hold_last=True, n_wg=3, heads=MERGE_HEADS)
+    inp = s.inp
+    wa, wr = 0.0, 0.0
+    for b, L in enumerate(lens):
+        a_ref, r_ref = oracle.append_ref(inp.latents[b], inp.k_rope_raw[b], np.arange(L), inp.w_uk,
+                                         inp.gamma_k_rope, 1e-6, 10000.0, qk_norm=True)
+        wa = max(wa, float(np.max(np.abs(s.alpha[b, :L] - a_ref) / np.abs(a_ref))))
+        rope = (s.rope[b, :L].astype(np.uint32) << 16).view(np.float32)
+        wr = max(wr, float(np.max(oracle.rowwise_rel_err(rope, r_ref))))
+        assert np.array_equal(s.lat[b, :L], s.store(inp.latents[b])), "latent rows not copied"
+    print(f"[{'ok' if wa <= 1e-3 and wr <= 1e-2 else 'FAIL'}] append caches: alpha {wa:.2e} "
+          f"(bound 1e-3) rope {wr:.2e} (bound 1e-2)", flush=True)
+    assert wa <= 1e-3 and wr <= 1e-2, (wa, wr)
+
+
+@case
 def bf16_long_segments(dev):
     """Segments long enough to run the three-stage tile loop several times:
     one workgroup streaming a 10-tile and a 2-tile sequence (both written

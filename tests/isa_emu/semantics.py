@@ -1372,6 +1372,29 @@ def _dswrite(nb):
     return run
 
 
+def _dswrite2(nb, stride):
+    """ds_write2[st64]_b32/b64: data0 at addr + offset0*stride, data1 at
+    addr + offset1*stride (stride = element size, times 64 for st64)."""
+    def run(w, i):
+        a, d0, d1 = i.ops
+        m = w.exec_mask()
+        base = w.vget(a).astype(np.int64)[m]
+        nd = nb // 4
+        for key, d in (("offset0", d0), ("offset1", d1)):
+            offs = base + stride * int(i.mods.get(key, 0))
+            lds_check(w, offs, nb, "w", i.text)
+            vals = np.stack([w.vget(d, "b32", k)[m] for k in range(nd)], 1).astype("<u4")
+            b = vals.view(np.uint8).reshape(-1, nb)
+            for k in range(len(offs)):
+                w.wg.lds[offs[k]:offs[k] + nb] = b[k]
+        push_lgkm(w, Pend(w, what=i.text))
+    return run
+
+
+HANDLERS["ds_write2_b32"] = _dswrite2(4, 4)
+HANDLERS["ds_write2_b64"] = _dswrite2(8, 8)
+HANDLERS["ds_write2st64_b32"] = _dswrite2(4, 256)
+HANDLERS["ds_write2st64_b64"] = _dswrite2(8, 512)
 HANDLERS["ds_write_b32"] = _dswrite(4)
 HANDLERS["ds_write_b64"] = _dswrite(8)
 HANDLERS["ds_write_b128"] = _dswrite(16)

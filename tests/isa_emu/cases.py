@@ -141,6 +141,15 @@ def bf16_append_caches(dev):
 
 
 @case
+def bf16_64_heads(dev):
+    """The two-wavefront split-KV variant (64 heads in 4 KV groups), caches
+    from qkmla_append, 7 tiles over two workgroups."""
+    shape = Shape(64, 4, 512, 128, 64, 128, "bf16")
+    run_layer(dev, shape, (150, 70), 506, "bf16 H=64 over 2 workgroups", host_fill=False,
+              n_wg=2, heads=(0, 37))  # the merge runs heads 0, 37 (and 127)
+
+
+@case
 def bf16_long_segments(dev):
     """Segments long enough to run the three-stage tile loop several times:
     one workgroup streaming a 10-tile and a 2-tile sequence (both written

@@ -122,6 +122,7 @@ struct Args {
   const uint16_t* q_tilde;
   const uint16_t* q_rope;
   float* part;
+  int32_t* plan;  // [B+1] tile prefix, for the merge
   float* o_lat;
   float* lse;
 };
@@ -372,6 +373,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
   __shared__ __attribute__((aligned(2048))) int P[kMaxBatch + 1];
   if (threadIdx.x < 4) lds_restart[threadIdx.x] = 0;
   build_tile_prefix(a.seq_lens, a.B, a.L_cap, P);
+  if (blockIdx.x == 0)  // the merge reads the prefix instead of rebuilding it per block
+    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.plan[i] = P[i];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -493,6 +496,7 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, const int32_t* seq_lens, 
   a.q_tilde = (const uint16_t*)(wsb + ws.q_tilde);
   a.q_rope = (const uint16_t*)(wsb + ws.q_rope);
   a.part = (float*)(wsb + ws.partials);
+  a.plan = (int32_t*)(wsb + ws.plan);
   a.o_lat = o_lat;
   a.lse = lse;
   const int nw = c.H / 32;

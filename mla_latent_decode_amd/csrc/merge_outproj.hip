@@ -14,83 +14,86 @@
 namespace qkmla {
 
 // One block per (sequence b, head h, block of 128 latent dims); 256 threads =
-// 8 source groups x 32 dim-quads.  Source group k combines the partials
-// p = p_lo + k, p_lo + k + 8, ...; the eight partial sums meet in LDS.
+// 8 source groups x 32 dim-quads.  Source group k folds the partials
+// p = p_lo + k, p_lo + k + 8, ... in one pass with a running maximum (each
+// source's m, l and O are loaded independently, so the loads overlap); the
+// eight groups meet in LDS.  The tile prefix of the plan comes from the
+// workspace, where the split-KV kernel left it.
 constexpr int kMergeDims = 128;
 constexpr int kMergeGroups = 8;
 
-__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ seq_lens, int B,
-                                                    int L_cap, int H, int r, int n_wg,
+__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ plan, int B, int H,
+                                                    int r, int n_wg,
                                                     const float* __restrict__ part,
                                                     float* __restrict__ o_lat,
                                                     float* __restrict__ lse) {
-  __shared__ int P[kMaxBatch + 1];
   __shared__ f32x4 red[kMergeGroups][32];
   __shared__ float red_m[kMergeGroups], red_l[kMergeGroups];
-  build_tile_prefix(seq_lens, B, L_cap, P);
   const int b = blockIdx.x, h = blockIdx.y, dblk = blockIdx.z;
   const int tid = threadIdx.x, sg = tid >> 5, dq = tid & 31;
   const int d0 = dblk * kMergeDims + 4 * dq;
   float* out = o_lat + ((size_t)b * H + h) * r + d0;
-  const int n_b = P[b + 1] - P[b];
-  if (n_b == 0) {  // invalid length: zeros and lse = -inf
+  const int Pb = plan[b], Pb1 = plan[b + 1];
+  if (Pb1 == Pb) {  // invalid length: zeros and lse = -inf
     if (sg == 0) *(f32x4*)out = f32x4{0.f, 0.f, 0.f, 0.f};
     if (tid == 0 && dblk == 0 && lse) lse[(size_t)b * H + h] = -INFINITY;
     return;
   }
-  const int64_t N = P[B];
-  const int p_lo = wg_of(P[b], N, n_wg);
-  const int p_hi = wg_of(P[b + 1] - 1, N, n_wg);
+  const int64_t N = plan[B];
+  const int p_lo = wg_of(Pb, N, n_wg);
+  const int p_hi = wg_of(Pb1 - 1, N, n_wg);
   if (p_lo == p_hi) return;  // written directly by the decode kernel
   const size_t slot_floats = (size_t)H * (r + 2);
-  // Workgroups between p_lo and p_hi with an empty range (more workgroups
-  // than tiles) wrote nothing and are skipped.
-  auto slot = [&](int p) -> const float* {
-    return part + ((size_t)p * kSlotsPerWg + merge_slot(P, b, N, n_wg, p)) * slot_floats;
-  };
-  auto empty = [&](int p) { return merge_slot(P, b, N, n_wg, p) < 0; };
-  // pass 1: M = max_s m_s
-  float M = -INFINITY;
-  for (int p = p_lo + tid; p <= p_hi; p += 256)
-    if (!empty(p)) M = fmaxf(M, slot(p)[h]);
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if ((tid & 63) == 0) red_m[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-  // pass 2: weighted sums
+  float M = -INFINITY, lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
   for (int p = p_lo + sg; p <= p_hi; p += kMergeGroups) {
-    if (empty(p)) continue;
-    const float* sp = slot(p);
-    const float w = exp2f(sp[h] - M);
-    lsum += w * sp[H + h];
+    // Workgroups between p_lo and p_hi with an empty range (more workgroups
+    // than tiles) wrote nothing and are skipped.
+    const int slot = merge_slot_of(Pb, p_lo, N, n_wg, p);
+    if (slot < 0) continue;
+    const float* sp = part + ((size_t)p * kSlotsPerWg + slot) * slot_floats;
+    const float m = sp[h], l = sp[H + h];
     const f32x4 v = *(const f32x4*)(sp + 2 * H + (size_t)h * r + d0);
-    acc += w * v;
+    const float Mn = fmaxf(M, m);
+    const float keep = exp2f(M - Mn), w = exp2f(m - Mn);  // M = -inf: keep = 0
+    acc = acc * keep + v * w;
+    lsum = lsum * keep + l * w;
+    M = Mn;
   }
   red[sg][dq] = acc;
-  if (dq == 0) red_l[sg] = lsum;
+  if (dq == 0) {
+    red_m[sg] = M;
+    red_l[sg] = lsum;
+  }
   __syncthreads();
   if (sg == 0) {
-    f32x4 t = red[0][dq];
-    float l = red_l[0];
+    float Mt = red_m[0];
 #pragma unroll
-    for (int k = 1; k < kMergeGroups; ++k) {
-      t += red[k][dq];
-      l += red_l[k];
+    for (int k = 1; k < kMergeGroups; ++k) Mt = fmaxf(Mt, red_m[k]);
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) {
+      if (red_m[k] == -INFINITY) continue;  // a group that held no source
+      const float w = exp2f(red_m[k] - Mt);
+      t += red[k][dq] * w;
+      l += red_l[k] * w;
     }
     const float inv = 1.0f / l;
     *(f32x4*)out = t * inv;
-    if (dq == 0 && dblk == 0 && lse) lse[(size_t)b * H + h] = (M + log2f(l)) * kLn2;
+    if (dq == 0 && dblk == 0 && lse) lse[(size_t)b * H + h] = (Mt + log2f(l)) * kLn2;
   }
 }
 
 hipError_t launch_merge(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
                         const WsLayout& ws, void* workspace, int n_wg, float* o_lat, float* lse,
                         hipStream_t s) {
+  (void)seq_lens;
+  (void)L_cap;
   char* wsb = (char*)workspace;
   merge_kernel<<<dim3(batch, c.H, c.r / kMergeDims), 256, 0, s>>>(
-      seq_lens, batch, L_cap, c.H, c.r, n_wg, (const float*)(wsb + ws.partials), o_lat, lse);
+      (const int32_t*)(wsb + ws.plan), batch, c.H, c.r, n_wg, (const float*)(wsb + ws.partials),
+      o_lat, lse);
   return hipGetLastError();
 }
 

@@ -81,11 +81,14 @@ __host__ __device__ __forceinline__ int seq_of(const int* P, int B, int64_t x) {
 // or -1 if p holds no tile of b (an empty range between p_lo and p_hi).
 // Mirrors the decode kernel: a workgroup's first segment uses slot 0, a later
 // one slot 1.
+__host__ __device__ __forceinline__ int merge_slot_of(int64_t Pb, int p_lo, int64_t N, int n_wg,
+                                                      int p) {
+  if (p == p_lo) return wg_start(p_lo, N, n_wg) == Pb ? 0 : 1;
+  return wg_start(p, N, n_wg) == wg_start(p + 1, N, n_wg) ? -1 : 0;
+}
 __host__ __device__ __forceinline__ int merge_slot(const int* P, int b, int64_t N, int n_wg,
                                                    int p) {
-  const int p_lo = wg_of(P[b], N, n_wg);
-  if (p == p_lo) return wg_start(p_lo, N, n_wg) == P[b] ? 0 : 1;
-  return wg_start(p, N, n_wg) == wg_start(p + 1, N, n_wg) ? -1 : 0;
+  return merge_slot_of(P[b], wg_of(P[b], N, n_wg), N, n_wg, p);
 }
 
 }  // namespace qkmla

@@ -35,6 +35,7 @@ struct WsLayout {
   size_t alpha_q;    // f32  [B][H]   (tau*log2e folded in)
   size_t q_rope;     // bf16 / f32 [B][H][d_r] (normalised, rotated, tau*log2e folded in)
   size_t partials;   // f32  [n_wg][kSlotsPerWg][H][r+2]  (m[H], l[H], O[H][r])
+  size_t plan;       // i32  [B+1]  tile prefix of the split plan (written by the decode)
   size_t total;
 };
 WsLayout ws_layout(const Cfg& c, int batch, int n_wg);

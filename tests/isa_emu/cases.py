@@ -108,6 +108,12 @@ def bf16_split(dev):
     workgroups, the merge of partials, MFMA out_proj (three heads merged)."""
     run_layer(dev, DSV3, (70, 33, 1), 500, "bf16 layer over 4 workgroups", n_wg=4,
               heads=MERGE_HEADS)
+    # 9 workgroups for 6 tiles: some ranges are empty and the merge skips them
+    run_layer(dev, DSV3, (70, 5, 40), 507, "bf16 9 workgroups over 6 tiles (empty ranges)",
+              n_wg=9, heads=MERGE_HEADS)
+    # a multiple of 8 workgroups: hardware workgroups take plan ranges in XCD order
+    run_layer(dev, DSV3, (100, 90, 60), 508, "bf16 8 workgroups over 9 tiles (XCD order)",
+              n_wg=8, heads=MERGE_HEADS)
 
 
 @case

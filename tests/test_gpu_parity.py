@@ -72,6 +72,23 @@ def test_dsv3_bf16_plain_mode_parity():
     _full_check(cfg, inp, "dsv3 bf16 plain")
 
 
+def test_dsv3_bf16_plain_log_normal_restream():
+    """Plain MLA on latents scaled by up to 1e3: unnormalised logits overflow
+    the first tile's reference and segments are streamed again; o and o_lat
+    must still match, lse within a bound that scales with |lse|."""
+    inp = make_inputs(DSV3, (400, 140), seed=312, row_scale_log10_clip=3.0)
+    cfg = ops.Config.from_shape(DSV3, qk_norm=False)
+    os.environ["QKMLA_NUM_WG"] = "5"
+    try:
+        sess, o, o_lat, lse = _run(cfg, inp, "dsv3 bf16 plain, log-normal rows")
+    finally:
+        del os.environ["QKMLA_NUM_WG"]
+    ref = oracle_decode(inp, cfg)
+    check_outputs(o, o_lat, lse, ref, "bf16", range(2), list(range(128)),
+                  "plain log-normal re-stream", lse_rel=2.0 ** -7)
+    assert int(sess.status.item()) == 0
+
+
 def test_dsv3_bf16_log_normal_scales():
     inp = make_inputs(DSV3, (500, 129), seed=311, row_scale_log10_clip=3.0)
     cfg = ops.Config.from_shape(DSV3)

@@ -135,6 +135,17 @@ def make_inputs(shape: Shape, lengths: Sequence[int], seed: int,
                   latents, k_rope_raw, q_c, q_rope)
 
 
+def multi_query_rows(shape: Shape, batch: int, s_q: int, seed: int):
+    """s_q query rows per sequence for a multi-query decode step: q_c
+    [B][s_q][H][d_c] and q_rope [B][s_q][H][d_r] ~ N(0, 1), storage-rounded,
+    drawn from their own seeded generator."""
+    rng = np.random.default_rng(seed)
+    H, dc, dr = shape.n_heads, shape.head_dim, shape.rope_dim
+    q_c = _store(rng.standard_normal((batch, s_q, H, dc), dtype=np.float32), shape.dtype)
+    q_rope = _store(rng.standard_normal((batch, s_q, H, dr), dtype=np.float32), shape.dtype)
+    return q_c, q_rope
+
+
 def workload_inputs(config_id: int, seed: Optional[int] = None) -> Inputs:
     w = WORKLOADS[config_id]
     return make_inputs(w.shape, w.lengths or (), 1000 + config_id if seed is None else seed,

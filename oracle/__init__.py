@@ -4,9 +4,9 @@ Only tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package; the HIP path never does.
 """
 from .qkmla_oracle import (absorb_weights_ref, absorbed_decode, append_ref, default_tau,
-                           explicit_decode, group_of_head, plain_mla_decode, rms, rmsnorm,
-                           rope, rope_inv_freq, rowwise_rel_err)
+                           explicit_decode, explicit_decode_multi, group_of_head,
+                           plain_mla_decode, rms, rmsnorm, rope, rope_inv_freq, rowwise_rel_err)
 
 __all__ = ["absorb_weights_ref", "absorbed_decode", "append_ref", "default_tau",
-           "explicit_decode", "group_of_head", "plain_mla_decode", "rms", "rmsnorm", "rope",
-           "rope_inv_freq", "rowwise_rel_err"]
+           "explicit_decode", "explicit_decode_multi", "group_of_head", "plain_mla_decode",
+           "rms", "rmsnorm", "rope", "rope_inv_freq", "rowwise_rel_err"]

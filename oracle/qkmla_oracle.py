@@ -210,6 +210,41 @@ def explicit_decode(q_c, q_rope, latents: Sequence[np.ndarray], k_rope_raw: Sequ
     return {"o": o, "o_lat": o_lat, "lse": lse}
 
 
+def explicit_decode_multi(q_c, q_rope, latents: Sequence[np.ndarray],
+                          k_rope_raw: Sequence[np.ndarray], w_uk, w_uv, gamma_q, gamma_k,
+                          gamma_q_rope, gamma_k_rope, **kw):
+    """Decode of s_q query rows per sequence (multi-token prediction or
+    speculative verification), each causal over the cache.
+
+    q_c [B][s_q][H][d_c], q_rope [B][s_q][H][d_r]; latents[b] holds L_b rows,
+    the last s_q of them belonging to the s_q new tokens.  Query row i is the
+    token at position P_i = L_b - s_q + i: it attends cache rows 0..P_i and
+    its RoPE query is rotated by P_i.  That is an ordinary decode step over
+    the causal prefix, so each row is ``explicit_decode`` on rows [0, P_i]
+    ([TS] Methodology: the decode logit carries a query index i).
+    Returns o [B][s_q][H][d_v], o_lat [B][s_q][H][r], lse [B][s_q][H]."""
+    q_c = np.asarray(q_c, dtype=F64)
+    q_rope = np.asarray(q_rope, dtype=F64)
+    B, s_q = q_c.shape[:2]
+    out = None
+    bs = kw.pop("batch_ids", None)
+    bs = range(B) if bs is None else list(bs)
+    for i in range(s_q):
+        prefix_lat, prefix_kr = [], []
+        for b in range(B):
+            P_i = len(latents[b]) - s_q + i
+            keep = max(P_i + 1, 0)
+            prefix_lat.append(np.asarray(latents[b])[:keep])
+            prefix_kr.append(np.asarray(k_rope_raw[b])[:keep])
+        res = explicit_decode(q_c[:, i], q_rope[:, i], prefix_lat, prefix_kr, w_uk, w_uv,
+                              gamma_q, gamma_k, gamma_q_rope, gamma_k_rope, batch_ids=bs, **kw)
+        if out is None:
+            out = {k: np.full((B, s_q) + v.shape[1:], np.nan) for k, v in res.items()}
+        for k, v in res.items():
+            out[k][:, i] = v
+    return out
+
+
 def plain_mla_decode(*args, **kwargs):
     """Plain MLA decode (no QK normalisation): the overhead baseline."""
     kwargs["qk_norm"] = False

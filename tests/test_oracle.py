@@ -12,10 +12,11 @@ import torch
 import torch.nn.functional as F
 
 from oracle import (absorb_weights_ref, absorbed_decode, append_ref, default_tau,
-                    explicit_decode, group_of_head, plain_mla_decode, rms, rmsnorm, rope,
-                    rope_inv_freq)
+                    explicit_decode, explicit_decode_multi, group_of_head, plain_mla_decode, rms,
+                    rmsnorm, rope, rope_inv_freq)
 from oracle.qkmla_oracle import _softmax
-from mla_latent_decode_amd.inputs import DSV3, TINY, Shape, make_inputs, workload_inputs
+from mla_latent_decode_amd.inputs import (DSV3, TINY, Shape, make_inputs, multi_query_rows,
+                                          workload_inputs)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -117,6 +118,57 @@ def test_attention_matches_torch_sdpa():
                                                torch.cat([k, kr], -1)[None, None],
                                                v[None, None], scale=tau)[0, 0, 0].numpy()
             assert _rel(ref["o"][b, h], o) < 1e-12
+
+
+# --- several query rows per sequence (causal) --------------------------------
+
+def test_multi_query_matches_causal_sdpa():
+    """s_q query rows per sequence: torch's fp64 SDPA with an explicit causal
+    mask (row i sees cache rows 0..L-s_q+i) and each RoPE query rotated by its
+    own position, against the multi-query oracle."""
+    shape = Shape(6, 3, 20, 12, 4, 10, "f32")
+    inp = make_inputs(shape, (9, 5, 3), seed=71)
+    s_q = 3
+    q_c, q_rope = multi_query_rows(shape, 3, s_q, seed=72)
+    eps, tau, base = 1e-6, 0.41, 10000.0
+    ref = explicit_decode_multi(q_c, q_rope, inp.latents, inp.k_rope_raw, inp.w_uk, inp.w_uv,
+                                inp.gamma_q, inp.gamma_k, inp.gamma_q_rope, inp.gamma_k_rope,
+                                eps=eps, tau=tau, base=base)
+    H, G, dc, dr = 6, 3, 12, 4
+    t64 = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64))  # noqa: E731
+    for b, L in enumerate(inp.lengths):
+        c = t64(inp.latents[b])
+        kr = F.rms_norm(t64(inp.k_rope_raw[b]), (dr,), weight=t64(inp.gamma_k_rope), eps=eps)
+        kr = t64(rope(kr.numpy(), np.arange(L), base))
+        pos = np.arange(L - s_q, L)                              # query positions
+        mask = torch.from_numpy(np.arange(L)[None, :] <= pos[:, None])   # [s_q][L]
+        for h in range(H):
+            g = h * G // H
+            k = F.rms_norm(c @ t64(inp.w_uk[g]), (dc,), weight=t64(inp.gamma_k), eps=eps)
+            q = F.rms_norm(t64(q_c[b, :, h]), (dc,), weight=t64(inp.gamma_q), eps=eps)
+            qr = F.rms_norm(t64(q_rope[b, :, h]), (dr,), weight=t64(inp.gamma_q_rope), eps=eps)
+            qr = t64(rope(qr.numpy(), pos, base))
+            v = c @ t64(inp.w_uv[g])
+            o = F.scaled_dot_product_attention(torch.cat([q, qr], -1)[None, None],
+                                               torch.cat([k, kr], -1)[None, None], v[None, None],
+                                               attn_mask=mask, scale=tau)[0, 0].numpy()
+            assert _rel(ref["o"][b, :, h], o) < 1e-12, (b, h)
+
+
+def test_multi_query_rows_are_causal():
+    """Changing the cache rows after query row i's position leaves row i (and
+    every earlier row) unchanged and changes the later rows."""
+    shape = Shape(4, 2, 16, 8, 4, 8, "f32")
+    inp = make_inputs(shape, (12,), seed=73)
+    s_q = 4
+    q_c, q_rope = multi_query_rows(shape, 1, s_q, seed=74)
+    args = (inp.w_uk, inp.w_uv, inp.gamma_q, inp.gamma_k, inp.gamma_q_rope, inp.gamma_k_rope)
+    a = explicit_decode_multi(q_c, q_rope, inp.latents, inp.k_rope_raw, *args)
+    lat = [inp.latents[0].copy()]
+    lat[0][10:] *= 3.0                    # rows 10, 11 = positions of query rows 2, 3
+    b = explicit_decode_multi(q_c, q_rope, lat, inp.k_rope_raw, *args)
+    assert np.array_equal(a["o"][0, :2], b["o"][0, :2])
+    assert np.all(np.abs(a["o"][0, 2:] - b["o"][0, 2:]).max(axis=-1) > 1e-6)
 
 
 # --- RoPE closed forms -------------------------------------------------------

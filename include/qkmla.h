@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define QKMLA_ABI_VERSION 1
+#define QKMLA_ABI_VERSION 2
 
 typedef enum {
   QKMLA_OK = 0,
@@ -169,6 +169,32 @@ int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const 
                  int32_t cache_capacity, int32_t max_seq_len, void* workspace,
                  size_t workspace_bytes, float* o_lat, float* lse, int32_t* status,
                  void* stream);
+
+/*
+ * Decode of s_q query rows per sequence (multi-token prediction,
+ * speculative verification), causal over the cache.  The pages' decode logit
+ * carries a query index i ("QK-Normed MLA: QK normalization without full key
+ * caching", technical summary, Methodology: decode-logit formula); here row i
+ * of sequence b is the token at position P_i = L_b - s_q + i, whose latent,
+ * RoPE and alpha rows are already in the cache (appended before the call):
+ * it attends cache rows 0..P_i and its RoPE query is rotated by P_i.  Each
+ * row is exactly the s_q = 1 decode of qkmla_decode with seq_len P_i + 1.
+ *   q_c     device dtype [B][s_q][H][d_c];  q_rope device dtype [B][s_q][H][d_r]
+ *   seq_lens device int32 [B]: L_b, counting the s_q new tokens
+ *   workspace >= qkmla_decode_workspace_size(cfg, batch * s_q, max_seq_len)
+ *   o_lat   device float [B][s_q][H][r] out;  lse device float [B][s_q][H], nullable
+ *   other arguments as for qkmla_decode.
+ * A row whose prefix length P_i + 1 is outside [1, L_cap] (L_b < s_q - i, or
+ * L_b invalid) gets zeros, lse = -inf and sets QKMLA_DEV_BAD_SEQ_LEN.
+ * batch * s_q must not exceed 4096 (QKMLA_ERR_UNSUPPORTED); s_q < 1 is
+ * QKMLA_ERR_INVALID_ARG.  qkmla_decode is this call with s_q = 1.
+ */
+int qkmla_decode_multi(const qkmla_config* cfg, int32_t batch, int32_t s_q, const void* q_c,
+                       const void* q_rope, const void* w_qabs, const float* gamma_q_rope,
+                       const void* latent_cache, const void* rope_cache, const float* alpha_cache,
+                       const int32_t* seq_lens, int32_t cache_capacity, int32_t max_seq_len,
+                       void* workspace, size_t workspace_bytes, float* o_lat, float* lse,
+                       int32_t* status, void* stream);
 
 /*
  * V up-projection: out[b][h][:] = o_lat[b][h][:] W^UV_{g(h)}.

@@ -336,21 +336,23 @@ size_t qkmla_decode_workspace_size(const qkmla_config* cfg, int32_t batch, int32
   return ws_layout(c, batch, n_wg).total;
 }
 
-int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const void* q_rope,
-                 const void* w_qabs, const float* gamma_q_rope, const void* latent_cache,
-                 const void* rope_cache, const float* alpha_cache, const int32_t* seq_lens,
-                 int32_t cache_capacity, int32_t max_seq_len, void* workspace,
-                 size_t workspace_bytes, float* o_lat, float* lse, int32_t* status,
-                 void* stream) {
+int qkmla_decode_multi(const qkmla_config* cfg, int32_t batch, int32_t s_q, const void* q_c,
+                       const void* q_rope, const void* w_qabs, const float* gamma_q_rope,
+                       const void* latent_cache, const void* rope_cache, const float* alpha_cache,
+                       const int32_t* seq_lens, int32_t cache_capacity, int32_t max_seq_len,
+                       void* workspace, size_t workspace_bytes, float* o_lat, float* lse,
+                       int32_t* status, void* stream) {
   Cfg c;
   int st = check_cfg(cfg, &c);
   if (st) return st;
-  if (batch < 0 || cache_capacity < 1 || max_seq_len < 1 || max_seq_len > cache_capacity)
+  if (batch < 0 || s_q < 1 || cache_capacity < 1 || max_seq_len < 1 ||
+      max_seq_len > cache_capacity)
     return fail(QKMLA_ERR_INVALID_ARG,
-                "decode: need batch >= 0 and 1 <= max_seq_len (%d) <= cache_capacity (%d)",
+                "decode: need batch >= 0, s_q >= 1 and 1 <= max_seq_len (%d) <= cache_capacity (%d)",
                 max_seq_len, cache_capacity);
   if (batch == 0) return ok();
-  if (batch > 4096) return fail(QKMLA_ERR_UNSUPPORTED, "decode: batch above 4096");
+  if ((int64_t)batch * s_q > kMaxBatch)
+    return fail(QKMLA_ERR_UNSUPPORTED, "decode: batch * s_q above %d", kMaxBatch);
   if (!q_c || !q_rope || !w_qabs || !latent_cache || !rope_cache || !seq_lens || !workspace ||
       !o_lat || (c.qk_norm && (!gamma_q_rope || !alpha_cache)))
     return fail(QKMLA_ERR_INVALID_ARG, "decode: NULL pointer");
@@ -363,29 +365,41 @@ int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const 
     return fail(QKMLA_ERR_INVALID_ARG,
                 "decode: pointers must be %zu-byte aligned (alpha, lse, seq_lens: 4; workspace: 16)", va);
   hipStream_t s = as_stream(stream);
-  const int n_wg = plan_n_wg(c, batch, max_seq_len, device_cu_count());
-  const WsLayout ws = ws_layout(c, batch, n_wg);
+  const int nv = batch * s_q;  // one virtual sequence per query row
+  const int n_wg = plan_n_wg(c, nv, max_seq_len, device_cu_count());
+  const WsLayout ws = ws_layout(c, nv, n_wg);
   if (workspace_bytes < ws.total)
     return fail(QKMLA_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
                 ws.total);
-  hipError_t e = launch_qprep(c, batch, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens,
+  hipError_t e = launch_qprep(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens,
                               cache_capacity, ws, workspace, status, s);
   if (e != hipSuccess) return hip_status(e, "decode/qprep");
   if (c.dtype == QKMLA_BF16) {
     const bool timed = g_timer.on && g_timer.n < 4096;
     if (timed && (e = timer_record(s, 0)) != hipSuccess) return hip_status(e, "decode/timer");
-    e = launch_decode_mfma(c, batch, seq_lens, cache_capacity, latent_cache, rope_cache,
+    e = launch_decode_mfma(c, batch, s_q, seq_lens, cache_capacity, latent_cache, rope_cache,
                            alpha_cache, ws, workspace, n_wg, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/splitkv");
     if (timed && (e = timer_record(s, 1)) != hipSuccess) return hip_status(e, "decode/timer");
-    e = launch_merge(c, batch, seq_lens, cache_capacity, ws, workspace, n_wg, o_lat, lse, s);
+    e = launch_merge(c, batch, s_q, ws, workspace, n_wg, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/merge");
   } else {
-    e = launch_decode_generic(c, batch, seq_lens, cache_capacity, latent_cache, rope_cache,
+    e = launch_decode_generic(c, batch, s_q, seq_lens, cache_capacity, latent_cache, rope_cache,
                               alpha_cache, ws, workspace, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/generic");
   }
   return ok();
+}
+
+int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const void* q_rope,
+                 const void* w_qabs, const float* gamma_q_rope, const void* latent_cache,
+                 const void* rope_cache, const float* alpha_cache, const int32_t* seq_lens,
+                 int32_t cache_capacity, int32_t max_seq_len, void* workspace,
+                 size_t workspace_bytes, float* o_lat, float* lse, int32_t* status,
+                 void* stream) {
+  return qkmla_decode_multi(cfg, batch, 1, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache,
+                            rope_cache, alpha_cache, seq_lens, cache_capacity, max_seq_len,
+                            workspace, workspace_bytes, o_lat, lse, status, stream);
 }
 
 int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, const void* w_uv,

@@ -5,6 +5,7 @@
 // ("QK-Normed MLA: QK normalization without full key caching", technical
 // summary, Methodology: decode-logit formula and row-column scaling).
 #include "device_common.h"
+#include "plan_device.h"
 #include "qkmla_internal.h"
 
 namespace qkmla {
@@ -14,7 +15,7 @@ constexpr int kGenMaxR = 1024;
 constexpr int kGenMaxDr = 256;
 
 __global__ __launch_bounds__(256) void decode_generic_kernel(
-    const int32_t* __restrict__ seq_lens, int L_cap, int H, int G, int r, int dr, int qk_norm,
+    const int32_t* __restrict__ seq_lens, int s_q, int L_cap, int H, int G, int r, int dr, int qk_norm,
     const float* __restrict__ lat, const float* __restrict__ rope, const float* __restrict__ alpha,
     const float* __restrict__ q_tilde, const float* __restrict__ alpha_q,
     const float* __restrict__ q_rope, float* __restrict__ o_lat, float* __restrict__ lse) {
@@ -22,9 +23,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   __shared__ float qr[kGenMaxDr];
   __shared__ float p[kGenChunk];
   __shared__ float red[4];
+  // b: virtual sequence (query row b % s_q of cache b / s_q)
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int bc = b / s_q;
   const int g = (h * G) / H;
-  const int L = seq_lens[b];
+  const int L = virt_len(seq_lens, b, s_q, L_cap);
   float* out = o_lat + ((size_t)b * H + h) * r;
   if (L < 1 || L > L_cap) {
     for (int i = tid; i < r; i += blockDim.x) out[i] = 0.f;
@@ -35,8 +38,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   for (int i = tid; i < dr; i += blockDim.x) qr[i] = q_rope[((size_t)b * H + h) * dr + i];
   const float aq = alpha_q[(size_t)b * H + h];
   __syncthreads();
-  const float* latb = lat + (size_t)b * L_cap * r;
-  const float* ropeb = rope + (size_t)b * L_cap * dr;
+  const float* latb = lat + (size_t)bc * L_cap * r;
+  const float* ropeb = rope + (size_t)bc * L_cap * dr;
   // each thread owns output dims tid, tid+256, ... (r <= 1024 -> 4 per thread)
   float acc[kGenMaxR / 256];
 #pragma unroll
@@ -52,7 +55,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
       const float* kr = ropeb + (size_t)t * dr;
       float sr = 0.f;
       for (int i = 0; i < dr; ++i) sr += qr[i] * kr[i];
-      float ak = qk_norm ? alpha[((size_t)b * L_cap + t) * G + g] : 1.0f;
+      float ak = qk_norm ? alpha[((size_t)bc * L_cap + t) * G + g] : 1.0f;
       logit = sc * (aq * ak) + sr;
     }
     // chunk max
@@ -92,13 +95,13 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   if (tid == 0 && lse) lse[(size_t)b * H + h] = (m_run + log2f(l_run)) * kLn2;
 }
 
-hipError_t launch_decode_generic(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
-                                 const void* lat, const void* rope, const float* alpha,
+hipError_t launch_decode_generic(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,
+                                 int L_cap, const void* lat, const void* rope, const float* alpha,
                                  const WsLayout& ws, void* workspace, float* o_lat, float* lse,
                                  hipStream_t s) {
   char* wsb = (char*)workspace;
-  decode_generic_kernel<<<dim3(batch, c.H), 256, 0, s>>>(
-      seq_lens, L_cap, c.H, c.G, c.r, c.dr, c.qk_norm, (const float*)lat, (const float*)rope,
+  decode_generic_kernel<<<dim3(batch * s_q, c.H), 256, 0, s>>>(
+      seq_lens, s_q, L_cap, c.H, c.G, c.r, c.dr, c.qk_norm, (const float*)lat, (const float*)rope,
       alpha, (const float*)(wsb + ws.q_tilde), (const float*)(wsb + ws.alpha_q),
       (const float*)(wsb + ws.q_rope), o_lat, lse);
   return hipGetLastError();

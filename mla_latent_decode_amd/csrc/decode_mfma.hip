@@ -115,7 +115,9 @@ __device__ __forceinline__ int plan_wg(int hw, int n) {
 
 struct Args {
   const int32_t* seq_lens;
-  int B, H, G, L_cap, n_wg;
+  int B;    // virtual sequences: batch * s_q (one per query row)
+  int s_q;  // query rows per sequence
+  int H, G, L_cap, n_wg;
   const uint16_t* lat;
   const uint16_t* rope;
   const float* alpha;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
   // run ahead of the loads in flight into the other stages.
   __shared__ __attribute__((aligned(2048))) int P[kMaxBatch + 1];
   if (threadIdx.x < 4) lds_restart[threadIdx.x] = 0;
-  build_tile_prefix(a.seq_lens, a.B, a.L_cap, P);
+  build_tile_prefix(a.seq_lens, a.B, a.s_q, a.L_cap, P);
   if (blockIdx.x == 0)  // the merge reads the prefix instead of rebuilding it per block
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.plan[i] = P[i];
 
@@ -390,15 +392,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
   Wave w;
 
   while (x < e) {
+    // b: virtual sequence (query row b % s_q of cache b / s_q)
     const int b = __builtin_amdgcn_readfirstlane(seq_of(P, a.B, x));
     Seq sq;
-    sq.L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+    sq.L = __builtin_amdgcn_readfirstlane(virt_len(a.seq_lens, b, a.s_q, a.L_cap));
     const int64_t s0 = __builtin_amdgcn_readfirstlane(P[b]);
     const int64_t s1 = __builtin_amdgcn_readfirstlane(P[b + 1]);
     const int64_t seg_end = e < s1 ? e : s1;
     const int tile0 = (int)(x - s0);
     const int nt = (int)(seg_end - x);
-    const size_t seq_row0 = (size_t)b * a.L_cap;
+    const size_t seq_row0 = (size_t)(b / a.s_q) * a.L_cap;
     sq.lat = (const char*)(a.lat + seq_row0 * kR);
     sq.rope = (const char*)(a.rope + seq_row0 * kDr);
     sq.alpha = QKN ? (const char*)(a.alpha + seq_row0 * a.G) : nullptr;
@@ -478,14 +481,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
-                              const void* lat, const void* rope, const float* alpha,
+hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,
+                              int L_cap, const void* lat, const void* rope, const float* alpha,
                               const WsLayout& ws, void* workspace, int n_wg, float* o_lat,
                               float* lse, hipStream_t s) {
   char* wsb = (char*)workspace;
   Args a;
   a.seq_lens = seq_lens;
-  a.B = batch;
+  a.B = batch * s_q;
+  a.s_q = s_q;
   a.H = c.H;
   a.G = c.G;
   a.L_cap = L_cap;

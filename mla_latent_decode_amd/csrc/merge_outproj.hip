@@ -85,14 +85,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
   }
 }
 
-hipError_t launch_merge(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
-                        const WsLayout& ws, void* workspace, int n_wg, float* o_lat, float* lse,
-                        hipStream_t s) {
-  (void)seq_lens;
-  (void)L_cap;
+hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, void* workspace,
+                        int n_wg, float* o_lat, float* lse, hipStream_t s) {
   char* wsb = (char*)workspace;
-  merge_kernel<<<dim3(batch, c.H, c.r / kMergeDims), 256, 0, s>>>(
-      (const int32_t*)(wsb + ws.plan), batch, c.H, c.r, n_wg, (const float*)(wsb + ws.partials),
+  const int nv = batch * s_q;  // virtual sequences
+  merge_kernel<<<dim3(nv, c.H, c.r / kMergeDims), 256, 0, s>>>(
+      (const int32_t*)(wsb + ws.plan), nv, c.H, c.r, n_wg, (const float*)(wsb + ws.partials),
       o_lat, lse);
   return hipGetLastError();
 }

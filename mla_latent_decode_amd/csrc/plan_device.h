@@ -21,9 +21,22 @@ __host__ __device__ __forceinline__ int tiles_of(int L, int L_cap) {
   return (L >= 1 && L <= L_cap) ? (L + kTile - 1) / kTile : 0;
 }
 
-// Exclusive prefix over tiles_of(seq_lens[b]) into P[0..B] (LDS), block-wide.
-// Must be called by every thread of the block (64, 128 or 256 threads).
-__device__ void build_tile_prefix(const int32_t* __restrict__ seq_lens, int B, int L_cap, int* P) {
+// Length of virtual sequence v when every sequence carries s_q query rows:
+// row i = v % s_q of sequence b = v / s_q is the token at position
+// L_b - s_q + i and attends cache rows 0..L_b - s_q + i (causal).  With
+// s_q = 1 this is seq_lens[v].  A sequence length outside [1, L_cap] makes all
+// of its rows invalid (length 0).
+__host__ __device__ __forceinline__ int virt_len(const int32_t* seq_lens, int v, int s_q, int L_cap) {
+  const int L = seq_lens[v / s_q];
+  if (L < 1 || L > L_cap) return 0;
+  return L - s_q + 1 + v % s_q;
+}
+
+// Exclusive prefix over tiles_of(virt_len(v)) into P[0..B] (LDS), block-wide,
+// for the B virtual sequences.  Must be called by every thread of the block
+// (64, 128 or 256 threads).
+__device__ void build_tile_prefix(const int32_t* __restrict__ seq_lens, int B, int s_q, int L_cap,
+                                  int* P) {
   __shared__ int wsum[4];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -32,7 +45,7 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ seq_lens, int B, i
   int local = 0;
   for (int i = 0; i < per; ++i) {
     int b = b0 + i;
-    if (b < B) local += tiles_of(seq_lens[b], L_cap);
+    if (b < B) local += tiles_of(virt_len(seq_lens, b, s_q, L_cap), L_cap);
   }
   // inclusive scan of `local` across the block
   int lane = tid & 63, wave = tid >> 6;
@@ -51,7 +64,7 @@ __device__ void build_tile_prefix(const int32_t* __restrict__ seq_lens, int B, i
     int b = b0 + i;
     if (b < B) {
       P[b] = excl;
-      excl += tiles_of(seq_lens[b], L_cap);
+      excl += tiles_of(virt_len(seq_lens, b, s_q, L_cap), L_cap);
     }
   }
   if (tid == nthr - 1) P[B] = before + v;

@@ -47,18 +47,20 @@ hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
                          const void* k_rope_new, const float* w_uk, const float* gkr,
                          const int32_t* positions, int L_cap, void* lat, void* rope, float* alpha,
                          int32_t* status, hipStream_t s);
-hipError_t launch_qprep(const Cfg& c, int batch, const void* q_c, const void* q_rope,
+// Decode launchers take `batch` sequences with `s_q` query rows each: query
+// row i of sequence b is virtual sequence b*s_q + i (its q rows, q~ rows and
+// outputs), at position seq_lens[b] - s_q + i over cache b (see virt_len).
+hipError_t launch_qprep(const Cfg& c, int batch, int s_q, const void* q_c, const void* q_rope,
                         const void* w_qabs, const float* gqr, const int32_t* seq_lens, int L_cap,
                         const WsLayout& ws, void* workspace, int32_t* status, hipStream_t s);
-hipError_t launch_decode_mfma(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
-                              const void* lat, const void* rope, const float* alpha,
+hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,
+                              int L_cap, const void* lat, const void* rope, const float* alpha,
                               const WsLayout& ws, void* workspace, int n_wg, float* o_lat,
                               float* lse, hipStream_t s);
-hipError_t launch_merge(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
-                        const WsLayout& ws, void* workspace, int n_wg, float* o_lat, float* lse,
-                        hipStream_t s);
-hipError_t launch_decode_generic(const Cfg& c, int batch, const int32_t* seq_lens, int L_cap,
-                                 const void* lat, const void* rope, const float* alpha,
+hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, void* workspace,
+                        int n_wg, float* o_lat, float* lse, hipStream_t s);
+hipError_t launch_decode_generic(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,
+                                 int L_cap, const void* lat, const void* rope, const float* alpha,
                                  const WsLayout& ws, void* workspace, float* o_lat, float* lse,
                                  hipStream_t s);
 hipError_t launch_out_proj(const Cfg& c, int batch, const float* o_lat, const void* w_uv,

@@ -10,6 +10,7 @@
 // decode kernel works in the exp2 domain.  In plain mode alpha^q = tau*log2(e)
 // and q^R is only rotated.  The bf16 path also folds alpha^q into q~.
 #include "device_common.h"
+#include "plan_device.h"
 #include "qkmla_internal.h"
 
 namespace qkmla {
@@ -70,13 +71,13 @@ __device__ __forceinline__ int clamp_pos(int L, int L_cap) {
 __global__ __launch_bounds__(256) void qprep_mfma_kernel(
     const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_qabs, const float* __restrict__ gqr,
-    const int32_t* __restrict__ seq_lens, int L_cap, int H, int G, int r, int dc, int dr,
+    const int32_t* __restrict__ seq_lens, int s_q, int L_cap, int H, int G, int r, int dc, int dr,
     float eps, float tau, float base, int qk_norm, uint16_t* __restrict__ q_tilde,
     float* __restrict__ alpha_q, uint16_t* __restrict__ q_rope_out, int32_t* status) {
-  const int b = blockIdx.x, g = blockIdx.y;
+  const int b = blockIdx.x, g = blockIdx.y;  // b: virtual sequence (query row)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h0 = g * 16;
-  const int L = seq_lens[b];
+  const int L = virt_len(seq_lens, b, s_q, L_cap);
   if (g == 0 && threadIdx.x == 0 && (L < 1 || L > L_cap) && status)
     atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
   const int pos = clamp_pos(L, L_cap);
@@ -142,12 +143,12 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
 __global__ __launch_bounds__(256) void qprep_generic_kernel(
     const float* __restrict__ q_c, const float* __restrict__ q_rope,
     const float* __restrict__ w_qabs, const float* __restrict__ gqr,
-    const int32_t* __restrict__ seq_lens, int L_cap, int H, int G, int r, int dc, int dr,
+    const int32_t* __restrict__ seq_lens, int s_q, int L_cap, int H, int G, int r, int dc, int dr,
     float eps, float tau, float base, int qk_norm, float* __restrict__ q_tilde,
     float* __restrict__ alpha_q, float* __restrict__ q_rope_out, int32_t* status) {
-  const int b = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.x, h = blockIdx.y;  // b: virtual sequence (query row)
   const int g = (h * G) / H;
-  const int L = seq_lens[b];
+  const int L = virt_len(seq_lens, b, s_q, L_cap);
   if (h == 0 && threadIdx.x == 0 && (L < 1 || L > L_cap) && status)
     atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
   const int pos = clamp_pos(L, L_cap);
@@ -167,19 +168,20 @@ __global__ __launch_bounds__(256) void qprep_generic_kernel(
                                        q_rope_out + ((size_t)b * H + h) * dr);
 }
 
-hipError_t launch_qprep(const Cfg& c, int batch, const void* q_c, const void* q_rope,
+hipError_t launch_qprep(const Cfg& c, int batch, int s_q, const void* q_c, const void* q_rope,
                         const void* w_qabs, const float* gqr, const int32_t* seq_lens, int L_cap,
                         const WsLayout& ws, void* workspace, int32_t* status, hipStream_t s) {
   char* wsb = (char*)workspace;
+  const int nv = batch * s_q;  // virtual sequences, one per query row
   if (c.dtype == QKMLA_BF16) {
-    qprep_mfma_kernel<<<dim3(batch, c.G), 256, 0, s>>>(
+    qprep_mfma_kernel<<<dim3(nv, c.G), 256, 0, s>>>(
         (const uint16_t*)q_c, (const uint16_t*)q_rope, (const uint16_t*)w_qabs, gqr, seq_lens,
-        L_cap, c.H, c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm,
+        s_q, L_cap, c.H, c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm,
         (uint16_t*)(wsb + ws.q_tilde), (float*)(wsb + ws.alpha_q), (uint16_t*)(wsb + ws.q_rope),
         status);
   } else {
-    qprep_generic_kernel<<<dim3(batch, c.H), 256, 0, s>>>(
-        (const float*)q_c, (const float*)q_rope, (const float*)w_qabs, gqr, seq_lens, L_cap, c.H,
+    qprep_generic_kernel<<<dim3(nv, c.H), 256, 0, s>>>(
+        (const float*)q_c, (const float*)q_rope, (const float*)w_qabs, gqr, seq_lens, s_q, L_cap, c.H,
         c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm, (float*)(wsb + ws.q_tilde),
         (float*)(wsb + ws.alpha_q), (float*)(wsb + ws.q_rope), status);
   }

@@ -50,6 +50,8 @@ def _load():
         "qkmla_append": (I32, [C, I32, I32, P, P, P, P, P, I32, P, P, P, P, P]),
         "qkmla_decode_workspace_size": (SZ, [C, I32, I32]),
         "qkmla_decode": (I32, [C, I32, P, P, P, P, P, P, P, P, I32, I32, P, SZ, P, P, P, P]),
+        "qkmla_decode_multi": (I32, [C, I32, I32, P, P, P, P, P, P, P, P, I32, I32, P, SZ, P, P,
+                                     P, P]),
         "qkmla_out_proj": (I32, [C, I32, P, P, P, P]),
         "qkmla_plan": (I32, [C, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "qkmla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -241,6 +243,33 @@ def decode(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, rope_ca
         _ptr(o_lat, (B, H, r), torch.float32, "o_lat"),
         _ptr(lse, (B, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
         _stream()), "qkmla_decode")
+    return o_lat
+
+
+def decode_multi(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, rope_cache,
+                 alpha_cache, seq_lens, max_seq_len: int, workspace, o_lat=None, lse=None,
+                 status=None):
+    """s_q query rows per sequence: q_c [B][s_q][H][d_c], q_rope [B][s_q][H][d_r];
+    row i is the token at position seq_lens[b] - s_q + i (causal).  Returns
+    o_lat [B][s_q][H][r].  Workspace: decode_workspace_size(cfg, B * s_q, ...)."""
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    L_cap = latent_cache.shape[1]
+    H, r, dt = cfg.n_heads, cfg.latent_rank, cfg.torch_dtype
+    if o_lat is None:
+        o_lat = torch.empty((B, s_q, H, r), dtype=torch.float32, device=q_c.device)
+    _check(_lib.qkmla_decode_multi(
+        ctypes.byref(cfg.c()), B, s_q, _ptr(q_c, (B, s_q, H, cfg.head_dim), dt, "q_c"),
+        _ptr(q_rope, (B, s_q, H, cfg.rope_dim), dt, "q_rope"),
+        _ptr(w_qabs, (cfg.n_groups, r, cfg.head_dim), dt, "w_qabs"),
+        _ptr(gamma_q_rope, None, torch.float32, "gamma_q_rope"),
+        _ptr(latent_cache, (B, L_cap, r), dt, "latent_cache"),
+        _ptr(rope_cache, (B, L_cap, cfg.rope_dim), dt, "rope_cache"),
+        _ptr(alpha_cache, (B, L_cap, cfg.n_groups), torch.float32, "alpha_cache"),
+        _ptr(seq_lens, (B,), torch.int32, "seq_lens"), L_cap, max_seq_len,
+        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(o_lat, (B, s_q, H, r), torch.float32, "o_lat"),
+        _ptr(lse, (B, s_q, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
+        _stream()), "qkmla_decode_multi")
     return o_lat
 
 

@@ -22,7 +22,8 @@ import oracle  # noqa: E402
 from isa_emu.asm import Kernel, parse_inst  # noqa: E402
 from isa_emu.device import Device, Session  # noqa: E402
 from isa_emu.machine import Emulator, EmuError, Memory  # noqa: E402
-from mla_latent_decode_amd.inputs import DSV3, TINY, Shape, make_inputs  # noqa: E402
+from mla_latent_decode_amd.inputs import (DSV3, TINY, Shape, make_inputs,  # noqa: E402
+                                          multi_query_rows)
 
 TOL = {"f32": dict(o=1e-5, o_lat=1e-5, lse=1e-5), "bf16": dict(o=2e-2, o_lat=2e-2, lse=5e-2)}
 MERGE_HEADS = (0, 37, 127)
@@ -153,6 +154,45 @@ def bf16_64_heads(dev):
     shape = Shape(64, 4, 512, 128, 64, 128, "bf16")
     run_layer(dev, shape, (150, 70), 506, "bf16 H=64 over 2 workgroups", host_fill=False,
               n_wg=2, heads=(0, 37))  # the merge runs heads 0, 37 (and 127)
+
+
+def run_multi(dev, shape, lens, s_q, seed, label, n_wg=None, heads=None):
+    """Decode of s_q causal query rows per sequence against the oracle; rows
+    whose causal prefix is empty must come back as zeros with lse = -inf."""
+    inp = make_inputs(shape, lens, seed=seed)
+    q_c, q_rope = multi_query_rows(shape, len(lens), s_q, seed=seed + 1)
+    if n_wg is not None:
+        os.environ["QKMLA_NUM_WG"] = str(n_wg)
+    try:
+        s = Session(dev, shape, inp, host_fill=True)
+        o_lat, lse, out = s.decode_multi(q_c, q_rope)
+    finally:
+        os.environ.pop("QKMLA_NUM_WG", None)
+    tau = 1.0 / np.sqrt(shape.head_dim + shape.rope_dim)
+    ref = oracle.explicit_decode_multi(q_c, q_rope, inp.latents, inp.k_rope_raw, inp.w_uk,
+                                       inp.w_uv, inp.gamma_q, inp.gamma_k, inp.gamma_q_rope,
+                                       inp.gamma_k_rope, eps=1e-6, tau=tau, base=10000.0)
+    hs = list(range(shape.n_heads)) if heads is None else [h for h in heads if h < shape.n_heads]
+    B = len(lens)
+    valid = [(b, i) for b in range(B) for i in range(s_q) if lens[b] - s_q + i >= 0]
+    flat = lambda x: x.reshape((B * s_q,) + x.shape[2:])  # noqa: E731
+    rows = [b * s_q + i for b, i in valid]
+    compare(shape, flat(out), flat(o_lat), flat(lse), {k: flat(v) for k, v in ref.items()}, rows,
+            hs, label)
+    empty = [b * s_q + i for b in range(B) for i in range(s_q) if lens[b] - s_q + i < 0]
+    for v in empty:
+        assert np.all(flat(o_lat)[v, hs] == 0) and np.all(np.isneginf(flat(lse)[v, hs])), v
+    assert bool(s.status[0] & 1) == bool(empty), s.status[0]
+
+
+@case
+def multi_query(dev):
+    """s_q query rows per sequence (causal): fp32 layer with s_q = 2, bf16
+    layer with s_q = 3 over split segments, including a sequence shorter than
+    s_q whose first row has an empty prefix."""
+    run_multi(dev, Shape(6, 3, 20, 12, 4, 10, "f32"), (9, 33), 2, 510, "fp32 s_q=2")
+    run_multi(dev, DSV3, (70, 40, 2), 3, 511, "bf16 s_q=3 (one row with an empty prefix)",
+              n_wg=5, heads=MERGE_HEADS)
 
 
 @case

@@ -165,6 +165,8 @@ SIGNATURES = {
                             _P, _P]),
     "qkmla_decode_noalloc": (_I32, [_C, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P,
                                     _P, _P]),
+    "qkmla_decode_multi": (_I32, [_C, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P,
+                                  _SZ, _P, _P, _P, _P]),
     "qkmla_out_proj": (_I32, [_C, _I32, _P, _P, _P, _P]),
     "qkmla_last_error": (ctypes.c_char_p, []),
 }
@@ -282,6 +284,31 @@ class Session:
                       P(self.o_lat.ctypes.data), P(self.lse.ctypes.data),
                       P(self.status.ctypes.data), None)
         return self.o_lat.copy(), self.lse.copy()
+
+    def decode_multi(self, q_c, q_rope):
+        """s_q query rows per sequence (q_c [B][s_q][H][d_c], q_rope
+        [B][s_q][H][d_r], host arrays); returns (o_lat [B][s_q][H][r],
+        lse [B][s_q][H], out [B][s_q][H][d_v])."""
+        P = _P
+        B, s_q = q_c.shape[:2]
+        s = self.shape
+        qc = self.dev.put(self.store(q_c), "q_c (several rows)")
+        qr = self.dev.put(self.store(q_rope), "q_rope (several rows)")
+        o_lat = self.dev.empty((B, s_q, s.n_heads, s.latent_rank), np.float32, "o_lat rows",
+                               fill=0xFF)
+        lse = self.dev.empty((B, s_q, s.n_heads), np.float32, "lse rows", fill=0xFF)
+        out = self.dev.empty((B, s_q, s.n_heads, s.v_head_dim), np.float32, "o rows", fill=0xFF)
+        ws = self.lib.qkmla_decode_workspace_size(ctypes.byref(self.cfg), B * s_q, self.max_len)
+        self.ws = self.dev.empty((ws,), np.uint8, "workspace", fill=0xCD)
+        self.call("qkmla_decode_multi", ctypes.byref(self.cfg), B, s_q, P(qc.ctypes.data),
+                  P(qr.ctypes.data), P(self.w_qabs.ctypes.data),
+                  P(self.gamma_q_rope.ctypes.data), P(self.lat.ctypes.data),
+                  P(self.rope.ctypes.data), P(self.alpha.ctypes.data),
+                  P(self.seq_lens.ctypes.data), self.L_cap, self.max_len, P(self.ws.ctypes.data),
+                  ws, P(o_lat.ctypes.data), P(lse.ctypes.data), P(self.status.ctypes.data), None)
+        self.call("qkmla_out_proj", ctypes.byref(self.cfg), B * s_q, P(o_lat.ctypes.data),
+                  P(self.w_uv.ctypes.data), P(out.ctypes.data), None)
+        return o_lat.copy(), lse.copy(), out.copy()
 
     def out_proj(self):
         self.call("qkmla_out_proj", ctypes.byref(self.cfg), self.B, _P(self.o_lat.ctypes.data),

@@ -37,7 +37,7 @@ def _ops():
 
 def test_abi_version_and_status_strings():
     ops = _ops()
-    assert ops.abi_version() == 1
+    assert ops.abi_version() == 2
     assert ops._lib.qkmla_status_string(0) == b"ok"
     assert ops._lib.qkmla_status_string(3) == b"workspace too small"
 
@@ -110,3 +110,21 @@ def test_decode_rejects_bad_length_bound():
     st = lib.qkmla_decode(ctypes.byref(cfg.c()), 1, p, p, p, p, p, p, p, p, 16, 17, p, 1 << 20,
                           p, None, None, None)
     assert st == 1  # max_seq_len > cache_capacity
+
+
+def test_decode_multi_validates_query_rows():
+    """s_q < 1 is an invalid argument, batch * s_q above 4096 unsupported;
+    both are rejected before any pointer is used."""
+    ops = _ops()
+    cfg = _cfg()
+    lib = ops._lib
+    p = ctypes.c_void_p(0x1000)
+    st = lib.qkmla_decode_multi(ctypes.byref(cfg.c()), 2, 0, p, p, p, p, p, p, p, p, 16, 16, p,
+                                1 << 20, p, None, None, None)
+    assert st == 1 and b"s_q" in lib.qkmla_last_error()
+    st = lib.qkmla_decode_multi(ctypes.byref(cfg.c()), 1025, 4, p, p, p, p, p, p, p, p, 16, 16, p,
+                                1 << 20, p, None, None, None)
+    assert st == 2
+    st = lib.qkmla_decode_multi(ctypes.byref(cfg.c()), 0, 3, None, None, None, None, None, None,
+                                None, None, 16, 16, None, 0, None, None, None, None)
+    assert st == 0

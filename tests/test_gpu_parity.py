@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     from mla_latent_decode_amd import ops
-    from mla_latent_decode_amd.inputs import DSV3, TINY, Shape, make_inputs, workload_inputs
+    from mla_latent_decode_amd.inputs import (DSV3, TINY, Shape, make_inputs, multi_query_rows,
+                                              workload_inputs)
     from mla_latent_decode_amd.runner import DecodeSession
 
 
@@ -102,6 +103,45 @@ def test_dsv3_fewer_heads(heads):
     shape = Shape(heads, heads // 16, 512, 128, 64, 128, "bf16")
     inp = make_inputs(shape, (45, 200), seed=320 + heads)
     _full_check(ops.Config.from_shape(shape), inp, f"bf16 H={heads}")
+
+
+@pytest.mark.parametrize("shape_name,lens,s_q", [("tiny", (64, 5), 2), ("dsv3", (300, 70, 2), 3),
+                                                  ("dsv3", (1000,), 8)])
+def test_multi_query_rows_are_causal_decodes(shape_name, lens, s_q):
+    """s_q query rows per sequence (qkmla_decode_multi): row i is the token at
+    position L_b - s_q + i over its causal prefix; rows with an empty prefix
+    come back as zeros with lse = -inf and the status bit."""
+    import oracle
+    shape = TINY if shape_name == "tiny" else DSV3
+    inp = make_inputs(shape, lens, seed=390 + s_q)
+    cfg = ops.Config.from_shape(shape)
+    print(f"\n[multi-query {shape_name} s_q={s_q}] lens={lens}", flush=True)
+    sess = DecodeSession(cfg, inp)
+    q_c, q_rope = multi_query_rows(shape, len(lens), s_q, seed=391 + s_q)
+    qc = torch.from_numpy(q_c).to("cuda", cfg.torch_dtype)
+    qr = torch.from_numpy(q_rope).to("cuda", cfg.torch_dtype)
+    B, H = len(lens), cfg.n_heads
+    ws = torch.empty((ops.decode_workspace_size(cfg, B * s_q, max(lens)),), dtype=torch.uint8,
+                     device="cuda")
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device="cuda")
+    o_lat = ops.decode_multi(cfg, qc, qr, sess.w_qabs, sess.gamma_q_rope, sess.lat, sess.rope,
+                             sess.alpha, sess.seq_lens, max(lens), ws, lse=lse, status=sess.status)
+    o = ops.out_proj(cfg, o_lat.view(B * s_q, H, -1), sess.w_uv).view(B, s_q, H, -1)
+    torch.cuda.synchronize()
+    ref = oracle.explicit_decode_multi(q_c, q_rope, inp.latents, inp.k_rope_raw, inp.w_uk,
+                                       inp.w_uv, inp.gamma_q, inp.gamma_k, inp.gamma_q_rope,
+                                       inp.gamma_k_rope, eps=cfg.eps, tau=cfg.tau,
+                                       base=cfg.rope_base)
+    flat = lambda x: np.asarray(x).reshape((B * s_q,) + np.asarray(x).shape[2:])  # noqa: E731
+    rows = [b * s_q + i for b in range(B) for i in range(s_q) if lens[b] - s_q + i >= 0]
+    empty = [b * s_q + i for b in range(B) for i in range(s_q) if lens[b] - s_q + i < 0]
+    check_outputs(flat(o.cpu().numpy()), flat(o_lat.cpu().numpy()), flat(lse.cpu().numpy()),
+                  {k: flat(v) for k, v in ref.items()}, cfg.dtype, rows, list(range(H)),
+                  f"multi-query s_q={s_q}")
+    for v in empty:
+        assert torch.all(o_lat.view(B * s_q, H, -1)[v] == 0)
+        assert torch.all(torch.isneginf(lse.view(B * s_q, H)[v]))
+    assert bool(int(sess.status.item()) & ops.QKMLA_DEV_BAD_SEQ_LEN) == bool(empty)
 
 
 def test_split_count_does_not_change_the_result():

@@ -153,7 +153,7 @@ WsLayout ws_layout(const Cfg& c, int batch, int n_wg) {
   w.q_rope = off;
   off = align256(off + (size_t)batch * c.H * c.dr * es);
   w.partials = off;
-  if (c.dtype == QKMLA_BF16) off = align256(off + (size_t)n_wg * kSlotsPerWg * c.H * (c.r + 2) * 4);
+  if (c.dtype == QKMLA_BF16) off = align256(off + (size_t)n_wg * kSlotsPerWg * kPartialSlotBytes(c.H, c.r));
   w.plan = off;
   if (c.dtype == QKMLA_BF16) off = align256(off + (size_t)(batch + 1) * 4);
   w.total = off;

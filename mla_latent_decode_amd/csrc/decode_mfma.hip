@@ -123,7 +123,7 @@ struct Args {
   const float* alpha;
   const uint16_t* q_tilde;
   const uint16_t* q_rope;
-  float* part;
+  char* part;   // partial slots, kPartialSlotBytes(H, r) each
   int32_t* plan;  // [B+1] tile prefix, for the merge
   float* o_lat;
   float* lse;
@@ -459,18 +459,21 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
       if (hf == 0 && a.lse) a.lse[qrow] = (m_run + log2f(l_tot)) * kLn2;
     } else {
       const int slot = first_seg ? 0 : 1;
-      float* sp = a.part + ((size_t)p * kSlotsPerWg + slot) * (size_t)a.H * (kR + 2);
+      char* sp = a.part + ((size_t)p * kSlotsPerWg + slot) * kPartialSlotBytes(a.H, kR);
       if (hf == 0) {
-        sp[head] = m_run;
-        sp[a.H + head] = l_tot;
+        ((float*)sp)[head] = m_run;
+        ((float*)sp)[a.H + head] = l_tot;
       }
-      float* Op = sp + 2 * a.H + (size_t)head * kR;
+      uint16_t* Op = (uint16_t*)(sp + (size_t)a.H * 8) + (size_t)head * kR;
 #pragma unroll
       for (int mb = 0; mb < kR / 32; ++mb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          f32x4 v = {w.O[mb][4 * q], w.O[mb][4 * q + 1], w.O[mb][4 * q + 2], w.O[mb][4 * q + 3]};
-          *(f32x4*)(Op + 32 * mb + 8 * q + 4 * hf) = v;
+          const uint2 v = {(uint32_t)f32_to_bf16(w.O[mb][4 * q]) |
+                               ((uint32_t)f32_to_bf16(w.O[mb][4 * q + 1]) << 16),
+                           (uint32_t)f32_to_bf16(w.O[mb][4 * q + 2]) |
+                               ((uint32_t)f32_to_bf16(w.O[mb][4 * q + 3]) << 16)};
+          *(uint2*)(Op + 32 * mb + 8 * q + 4 * hf) = v;
         }
     }
     first_seg = false;
@@ -499,7 +502,7 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* s
   a.alpha = alpha;
   a.q_tilde = (const uint16_t*)(wsb + ws.q_tilde);
   a.q_rope = (const uint16_t*)(wsb + ws.q_rope);
-  a.part = (float*)(wsb + ws.partials);
+  a.part = wsb + ws.partials;
   a.plan = (int32_t*)(wsb + ws.plan);
   a.o_lat = o_lat;
   a.lse = lse;

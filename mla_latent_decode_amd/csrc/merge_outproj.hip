@@ -24,7 +24,7 @@ constexpr int kMergeGroups = 8;
 
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ plan, int B, int H,
                                                     int r, int n_wg,
-                                                    const float* __restrict__ part,
+                                                    const char* __restrict__ part,
                                                     float* __restrict__ o_lat,
                                                     float* __restrict__ lse) {
   __shared__ f32x4 red[kMergeGroups][32];
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
   const int p_lo = wg_of(Pb, N, n_wg);
   const int p_hi = wg_of(Pb1 - 1, N, n_wg);
   if (p_lo == p_hi) return;  // written directly by the decode kernel
-  const size_t slot_floats = (size_t)H * (r + 2);
+  const size_t slot_bytes = kPartialSlotBytes(H, r);
   float M = -INFINITY, lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int p = p_lo + sg; p <= p_hi; p += kMergeGroups) {
@@ -51,9 +51,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
     // than tiles) wrote nothing and are skipped.
     const int slot = merge_slot_of(Pb, p_lo, N, n_wg, p);
     if (slot < 0) continue;
-    const float* sp = part + ((size_t)p * kSlotsPerWg + slot) * slot_floats;
-    const float m = sp[h], l = sp[H + h];
-    const f32x4 v = *(const f32x4*)(sp + 2 * H + (size_t)h * r + d0);
+    const char* sp = part + ((size_t)p * kSlotsPerWg + slot) * slot_bytes;
+    const float m = ((const float*)sp)[h], l = ((const float*)sp)[H + h];
+    const uint2 ob = *(const uint2*)((const uint16_t*)(sp + (size_t)H * 8) + (size_t)h * r + d0);
+    const f32x4 v = {__uint_as_float(ob.x << 16), __uint_as_float(ob.x & 0xFFFF0000u),
+                     __uint_as_float(ob.y << 16), __uint_as_float(ob.y & 0xFFFF0000u)};
     const float Mn = fmaxf(M, m);
     const float keep = exp2f(M - Mn), w = exp2f(m - Mn);  // M = -inf: keep = 0
     acc = acc * keep + v * w;
@@ -90,7 +92,7 @@ hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, vo
   char* wsb = (char*)workspace;
   const int nv = batch * s_q;  // virtual sequences
   merge_kernel<<<dim3(nv, c.H, c.r / kMergeDims), 256, 0, s>>>(
-      (const int32_t*)(wsb + ws.plan), nv, c.H, c.r, n_wg, (const float*)(wsb + ws.partials),
+      (const int32_t*)(wsb + ws.plan), nv, c.H, c.r, n_wg, (const char*)(wsb + ws.partials),
       o_lat, lse);
   return hipGetLastError();
 }

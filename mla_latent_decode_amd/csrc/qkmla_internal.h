@@ -28,13 +28,20 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = 32;
 // Partial slots per decode workgroup (first and last sequence segment).
 constexpr int kSlotsPerWg = 2;
+// Bytes of one partial slot: the running max m and sum l of each head in
+// fp32, the unnormalised O of each head in bf16 (it is rounded once, like the
+// softmax weights, and the merge accumulates in fp32).
+__host__ __device__ constexpr size_t kPartialSlotBytes(int H, int r) {
+  return (size_t)H * 8 + (size_t)H * r * 2;
+}
 
 // ---- workspace layout of the bf16 MFMA decode ------------------------------
 struct WsLayout {
   size_t q_tilde;    // bf16 [B][H][r]
   size_t alpha_q;    // f32  [B][H]   (tau*log2e folded in)
   size_t q_rope;     // bf16 / f32 [B][H][d_r] (normalised, rotated, tau*log2e folded in)
-  size_t partials;   // f32  [n_wg][kSlotsPerWg][H][r+2]  (m[H], l[H], O[H][r])
+  size_t partials;   // [n_wg][kSlotsPerWg] slots of kPartialSlotBytes(H, r):
+                     //   m[H] f32, l[H] f32, O[H][r] bf16
   size_t plan;       // i32  [B+1]  tile prefix of the split plan (written by the decode)
   size_t total;
 };

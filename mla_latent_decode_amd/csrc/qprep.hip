@@ -105,28 +105,39 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
       qscale[hh] = (qk_norm ? 1.0f / sqrtf(ss / (float)dc + eps) : 1.0f) * (tau * kLog2e);
   }
   __syncthreads();
-  const int nb_per_wave = (r / 16) / 4;     // 8 for r = 512
+  // The bf16 path has r = 512: each wave owns 8 blocks of 16 output columns.
+  // The loops are unrolled so that every weight load is issued before the
+  // first MFMA waits (the weights come from L2 or HBM, one latency, not eight).
+  constexpr int kNbPerWave = 512 / 16 / 4;
   const int ksteps = dc / 32;               // 4 for d_c = 128
   constexpr int kMaxK = 8;                  // d_c <= 256 on this path
   bf16x8 a[kMaxK];
 #pragma unroll
   for (int ks = 0; ks < kMaxK; ++ks)
     if (ks < ksteps) a[ks] = *(const bf16x8*)(A + (size_t)m * dc + ks * 32 + kq * 8);
-  for (int nbi = 0; nbi < nb_per_wave; ++nbi) {
-    const int nb = wave * nb_per_wave + nbi;
-    const uint16_t* wrow = W + (size_t)(nb * 16 + m) * dc + kq * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[kNbPerWave];
 #pragma unroll
-    for (int ks = 0; ks < kMaxK; ++ks) {
-      if (ks < ksteps) {
-        bf16x8 bv = *(const bf16x8*)(wrow + ks * 32);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bv, acc, 0, 0, 0);
-      }
+  for (int nbi = 0; nbi < kNbPerWave; ++nbi) acc[nbi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kMaxK; ++ks) {
+    if (ks < ksteps) {
+      bf16x8 bv[kNbPerWave];
+#pragma unroll
+      for (int nbi = 0; nbi < kNbPerWave; ++nbi)
+        bv[nbi] = *(const bf16x8*)(W + (size_t)((wave * kNbPerWave + nbi) * 16 + m) * dc +
+                                   kq * 8 + ks * 32);
+#pragma unroll
+      for (int nbi = 0; nbi < kNbPerWave; ++nbi)
+        acc[nbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bv[nbi], acc[nbi], 0, 0, 0);
     }
+  }
+#pragma unroll
+  for (int nbi = 0; nbi < kNbPerWave; ++nbi) {
+    const int nb = wave * kNbPerWave + nbi;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int hh = 4 * kq + i;
-      q_tilde[((size_t)b * H + h0 + hh) * r + nb * 16 + m] = f32_to_bf16(acc[i] * qscale[hh]);
+      q_tilde[((size_t)b * H + h0 + hh) * r + nb * 16 + m] = f32_to_bf16(acc[nbi][i] * qscale[hh]);
     }
   }
   __syncthreads();  // cs ready

@@ -1332,28 +1332,33 @@ HANDLERS["ds_read_b64"] = _dsread(8)
 HANDLERS["ds_read_b128"] = _dsread(16)
 
 
-def _dsread2(stride):
+def _dsread2(nb, stride):
+    """ds_read2[st64]_b32/b64: two nb-byte elements at addr + offset0*stride
+    and addr + offset1*stride (stride = element size, times 64 for st64)."""
     def run(w, i):
         d, a = i.ops
         m = w.exec_mask()
         base = w.vget(a).astype(np.int64)[m]
-        o0 = base + stride * int(i.mods.get("offset0", 0))
-        o1 = base + stride * int(i.mods.get("offset1", 0))
-        lds_check(w, o0, 4, "r", i.text)
-        lds_check(w, o1, 4, "r", i.text)
-        v0 = w.wg.lds[o0[:, None] + np.arange(4)].copy().view("<u4").reshape(-1)
-        v1 = w.wg.lds[o1[:, None] + np.arange(4)].copy().view("<u4").reshape(-1)
-        rows = [w.vrow(d, 0), w.vrow(d, 1)]
+        nd = nb // 4
+        vals = []
+        for key in ("offset0", "offset1"):
+            o = base + stride * int(i.mods.get(key, 0))
+            lds_check(w, o, nb, "r", i.text)
+            vals.append(w.wg.lds[o[:, None] + np.arange(nb)].copy().view("<u4").reshape(-1, nd))
+        rows = [w.vrow(d, k) for k in range(2 * nd)]
 
         def apply():
-            w.V[rows[0], m] = v0
-            w.V[rows[1], m] = v1
+            for k in range(nd):
+                w.V[rows[k], m] = vals[0][:, k]
+                w.V[rows[nd + k], m] = vals[1][:, k]
         push_lgkm(w, Pend(w, vrows=rows, apply=apply, what=i.text))
     return run
 
 
-HANDLERS["ds_read2_b32"] = _dsread2(4)
-HANDLERS["ds_read2st64_b32"] = _dsread2(256)
+HANDLERS["ds_read2_b32"] = _dsread2(4, 4)
+HANDLERS["ds_read2st64_b32"] = _dsread2(4, 256)
+HANDLERS["ds_read2_b64"] = _dsread2(8, 8)
+HANDLERS["ds_read2st64_b64"] = _dsread2(8, 512)
 
 
 def _dswrite(nb):

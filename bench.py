@@ -8,6 +8,12 @@ Inputs are resident in HBM before timing starts; caches are rotated over
 enough copies that each step streams from HBM rather than the 256 MB
 memory-side cache.
 
+Steps are timed as HIP-graph replays of the captured step (one step per cache
+copy), which keeps the host's launch overhead off the GPU timeline; each
+replay is first checked bit for bit against the eager step, and eager timing
+is used (and said) if capture fails or a replay differs.  The eager figures
+are reported beside them.
+
 Prints ONE JSON line: value = algorithmic cache bytes per step / step time
 (GB/s) for the batch-16 x 4096 workload, with microseconds per step, the
 overhead against the same kernels with the normalisation compiled out (plain
@@ -136,6 +142,53 @@ class Bench:
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
 
+    def graph_time(self, steps, plain=False):
+        """Step time with the step captured in HIP graphs: one step per cache
+        copy captured in turn (torch.cuda.graph on its capture stream, where
+        the library launches), then replayed.  This takes the host's launch
+        overhead out of the timeline, as a serving loop replaying a captured
+        decode step would.  Every checked replay must reproduce the eager
+        step's o_lat and lse bit for bit.  Returns (ms per step, None), or
+        (None, reason) when capture fails or a replay differs."""
+        torch = self.torch
+        try:
+            self.i = self.n_copies - 1
+            self.step(plain)
+            torch.cuda.synchronize()
+            ref_lat, ref_lse = self.o_lat.clone(), self.lse.clone()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self.i = 0
+                for _ in range(self.n_copies):
+                    self.step(plain)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            self.i = 0
+            with torch.cuda.graph(g):
+                for _ in range(self.n_copies):
+                    self.step(plain)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                self.o_lat.fill_(float("nan"))
+                self.lse.fill_(float("nan"))
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                if not (torch.equal(self.o_lat, ref_lat) and torch.equal(self.lse, ref_lse)):
+                    return None, "a graph replay differs from the eager step"
+            reps = max(1, -(-steps // self.n_copies))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / (reps * self.n_copies), None
+        except Exception as ex:  # noqa: BLE001 -- reported in the JSON line, eager timing stands
+            return None, f"graph capture failed: {type(ex).__name__}: {ex}"
+
     def kernel_ms(self, steps, plain=False):
         """Average duration of the split-KV kernel over `steps` steps (HIP events
         recorded by the library around each launch on the launch stream)."""
@@ -164,19 +217,28 @@ def _traffic(workload_name):
     return e.get("hbm_bytes_per_launch")
 
 
-def measure(cid, steps, warmup):
+def measure(cid, steps, warmup, graph=True):
     b = Bench(cid)
-    ms_qk, wall = b.time_steps(steps, warmup)
-    ms_plain, _ = b.time_steps(steps, warmup, plain=True)
+    ms_eager, wall = b.time_steps(steps, warmup)
+    ms_plain_eager, _ = b.time_steps(steps, warmup, plain=True)
     k_ms = b.kernel_ms(steps)
     k_ms_plain = b.kernel_ms(steps, plain=True)
+    g_ms, g_note = b.graph_time(steps) if graph else (None, "not requested")
+    g_ms_plain, g_note_plain = b.graph_time(steps, plain=True) if g_ms else (None, g_note)
+    use_graph = g_ms is not None and g_ms_plain is not None
+    ms_qk = g_ms if use_graph else ms_eager
+    ms_plain = g_ms_plain if use_graph else ms_plain_eager
     us = ms_qk * 1e3
     res = {
         "workload": b.w.name,
         "batch": b.B,
         "context": b.lengths[0] if len(set(b.lengths)) == 1 else f"ragged sum={b.tokens}",
         "us_per_step": round(us, 2),
+        "step_timing": "graph replay" if use_graph else "eager launches",
+        "graph_note": None if use_graph else (g_note or g_note_plain),
+        "us_per_step_eager": round(ms_eager * 1e3, 2),
         "plain_us_per_step": round(ms_plain * 1e3, 2),
+        "plain_us_per_step_eager": round(ms_plain_eager * 1e3, 2),
         "overhead_vs_plain_pct": round(100.0 * (ms_qk / ms_plain - 1.0), 2),
         "cache_GBps": round(b.bytes_qk / (ms_qk * 1e-3) / 1e9, 1),
         "cache_frac_of_8TBps": round(b.bytes_qk / (ms_qk * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -232,6 +294,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="headline workload (1-4)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (no HIP-graph replay of the step)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -241,7 +305,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    b, res, ms_qk, k_ms, _ = measure(args.workload, args.steps, args.warmup)
+    b, res, ms_qk, k_ms, _ = measure(args.workload, args.steps, args.warmup, not args.no_graph)
     print(f"[bench] headline {res}", file=sys.stderr, flush=True)
     achieved = b.bytes_qk / (k_ms * 1e-3) / 1e9
     line = {
@@ -281,7 +345,8 @@ def main():
         for cid in (2, 3, 4):
             if cid == args.workload:
                 continue
-            _b, r, *_ = measure(cid, max(10, args.steps // 2), max(3, args.warmup // 2))
+            _b, r, *_ = measure(cid, max(10, args.steps // 2), max(3, args.warmup // 2),
+                                not args.no_graph)
             print(f"[bench] sweep {r}", file=sys.stderr, flush=True)
             sweep.append(r)
             del _b

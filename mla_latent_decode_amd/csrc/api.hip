@@ -2,6 +2,7 @@
 // the split planner, workspace layout and kernel dispatch.  Nothing here
 // touches the GPU until a launcher is called, so validation errors and the
 // planner can be exercised without a device.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -102,11 +103,18 @@ int plan_n_wg(const Cfg& c, int batch, int max_seq_len, int n_cu) {
   return (int)n;
 }
 
+// Compute units of the current device, queried once per device and kept, so
+// that a decode call recorded into a HIP graph makes no attribute query.
 int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices && (n = cached[dev].load(std::memory_order_relaxed)) > 0)
+    return n;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 256;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

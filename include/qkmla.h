@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define QKMLA_ABI_VERSION 2
+#define QKMLA_ABI_VERSION 3
 
 typedef enum {
   QKMLA_OK = 0,
@@ -70,6 +70,7 @@ typedef enum { QKMLA_F32 = 0, QKMLA_BF16 = 1 } qkmla_dtype;
 /* Device-side data-error bits OR-ed into *status. */
 #define QKMLA_DEV_BAD_SEQ_LEN 1   /* decode: seq_len outside [1, cache_capacity] */
 #define QKMLA_DEV_BAD_POSITION 2  /* append: position < 0 or position + n_new > cache_capacity */
+#define QKMLA_DEV_BAD_PAGE 4      /* paged caches: a needed block-table entry is outside [0, num_pages) */
 
 /*
  * Layer shape and mode.
@@ -193,6 +194,52 @@ int qkmla_decode_multi(const qkmla_config* cfg, int32_t batch, int32_t s_q, cons
                        const void* q_rope, const void* w_qabs, const float* gamma_q_rope,
                        const void* latent_cache, const void* rope_cache, const float* alpha_cache,
                        const int32_t* seq_lens, int32_t cache_capacity, int32_t max_seq_len,
+                       void* workspace, size_t workspace_bytes, float* o_lat, float* lse,
+                       int32_t* status, void* stream);
+
+/*
+ * Paged caches.  The pages lay the caches out as one latent row, one RoPE row
+ * and G alpha scalars per cached token (Methodology: Cache Layout) and say
+ * nothing of how rows are placed; a serving cache keeps them in a shared pool
+ * of fixed-size pages with a block table per sequence.  Here row t of
+ * sequence b lives at pool row
+ *   block_table[b][t / page_size] * page_size + t % page_size
+ * of each of the three pools, so the contiguous layout of qkmla_append /
+ * qkmla_decode is the special case page_size = L_cap, block_table[b][0] = b.
+ *   block_table  device int32 [B][max_blocks]; entries in [0, num_pages)
+ *   max_blocks   blocks per sequence; the capacity L_cap = max_blocks*page_size
+ *   page_size    rows per page (>= 1; bf16 decode needs a multiple of 32, the
+ *                split-KV token tile, else QKMLA_ERR_UNSUPPORTED)
+ *   num_pages    pages in each pool
+ *   pools        latent device dtype [num_pages*page_size][r],
+ *                rope   device dtype [num_pages*page_size][d_r],
+ *                alpha  device float [num_pages*page_size][G]
+ * The caller owns the table and the pools.  An entry that a call needs and
+ * that is outside [0, num_pages) sets QKMLA_DEV_BAD_PAGE: append skips that
+ * row; decode reads page 0 in its place, so that row's output is undefined.
+ */
+typedef struct {
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t page_size;
+  int32_t num_pages;
+} qkmla_pages;
+
+/* qkmla_append into paged pools: as qkmla_append with cache_capacity =
+ * max_blocks * page_size and rows placed by the block table. */
+int qkmla_append_paged(const qkmla_config* cfg, int32_t batch, int32_t n_new, const void* c_new,
+                       const void* k_rope_new, const float* w_uk, const float* gamma_k_rope,
+                       const int32_t* positions, const qkmla_pages* pages, void* latent_pool,
+                       void* rope_pool, float* alpha_pool, int32_t* status, void* stream);
+
+/* qkmla_decode_multi over paged pools: as qkmla_decode_multi with
+ * cache_capacity = max_blocks * page_size and rows read through the block
+ * table.  Same outputs, to the rounding of identical arithmetic, as the
+ * contiguous call over the same rows. */
+int qkmla_decode_paged(const qkmla_config* cfg, int32_t batch, int32_t s_q, const void* q_c,
+                       const void* q_rope, const void* w_qabs, const float* gamma_q_rope,
+                       const void* latent_pool, const void* rope_pool, const float* alpha_pool,
+                       const int32_t* seq_lens, const qkmla_pages* pages, int32_t max_seq_len,
                        void* workspace, size_t workspace_bytes, float* o_lat, float* lse,
                        int32_t* status, void* stream);
 

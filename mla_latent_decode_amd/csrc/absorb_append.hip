@@ -50,7 +50,7 @@ template <typename T>
 __device__ void copy_rows_and_rope(int tok0, int ntok, int batch, int n_new,
                                    const T* __restrict__ c_new, const T* __restrict__ kr_new,
                                    const float* __restrict__ gkr,
-                                   const int32_t* __restrict__ positions, int L_cap,
+                                   const int32_t* __restrict__ positions, const Paging pg,
                                    T* __restrict__ lat, T* __restrict__ rope, int32_t* status,
                                    int r, int dr, float eps, float base, int qk_norm,
                                    float* rsum) {
@@ -61,14 +61,19 @@ __device__ void copy_rows_and_rope(int tok0, int ntok, int batch, int n_new,
     if (tok >= T_total) break;
     int b = tok / n_new, i = tok % n_new;
     int pos0 = positions[b];
-    bool bad = pos0 < 0 || (int64_t)pos0 + n_new > L_cap;
+    bool bad = pos0 < 0 || (int64_t)pos0 + n_new > pg.capacity();
     if (bad) {
       if (tid == 0 && i == 0 && status) atomicOr(status, QKMLA_DEV_BAD_POSITION);
       continue;
     }
     int row = pos0 + i;
+    const int64_t prow = pg.phys_row(b, row);
+    if (prow < 0) {
+      if (tid == 0 && status) atomicOr(status, QKMLA_DEV_BAD_PAGE);
+      continue;
+    }
     const T* src = c_new + (size_t)tok * r;
-    T* dst = lat + ((size_t)b * L_cap + row) * r;
+    T* dst = lat + (size_t)prow * r;
     for (int e = tid; e < r; e += blockDim.x) dst[e] = src[e];
     // RoPE key: optional RMSNorm over d_r, then rotate pairs by row position.
     const T* ks = kr_new + (size_t)tok * dr;
@@ -86,7 +91,7 @@ __device__ void copy_rows_and_rope(int tok0, int ntok, int batch, int n_new,
       __syncthreads();
       scale = 1.0f / sqrtf(rsum[k] / (float)dr + eps);
     }
-    T* rdst = rope + ((size_t)b * L_cap + row) * dr;
+    T* rdst = rope + (size_t)prow * dr;
     for (int pi = tid; pi < dr / 2; pi += blockDim.x) {
       float x0 = Elem<T>::load(ks, 2 * pi), x1 = Elem<T>::load(ks, 2 * pi + 1);
       if (qk_norm) {
@@ -113,9 +118,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void append_kernel(
     int batch, int n_new, const T* __restrict__ c_new, const T* __restrict__ kr_new,
     const float* __restrict__ w_uk, const float* __restrict__ gkr,
-    const int32_t* __restrict__ positions, int L_cap, T* __restrict__ lat, T* __restrict__ rope,
-    float* __restrict__ alpha, int32_t* status, int G, int r, int dc, int dr, float eps,
-    float base, int qk_norm) {
+    const int32_t* __restrict__ positions, const Paging pg, T* __restrict__ lat,
+    T* __restrict__ rope, float* __restrict__ alpha, int32_t* status, int G, int r, int dc, int dr,
+    float eps, float base, int qk_norm) {
   __shared__ float cs[kAppendTok * kMaxR];
   __shared__ float ksq[kAppendTok];
   __shared__ float rsum[kAppendTok];
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(256) void append_kernel(
   const int tid = threadIdx.x;
 
   if (copy_duty) {
-    copy_rows_and_rope<T>(tok0, kAppendTok, batch, n_new, c_new, kr_new, gkr, positions, L_cap,
+    copy_rows_and_rope<T>(tok0, kAppendTok, batch, n_new, c_new, kr_new, gkr, positions, pg,
                           lat, rope, status, r, dr, eps, base, qk_norm, rsum);
     return;
   }
@@ -167,10 +172,11 @@ __global__ __launch_bounds__(256) void append_kernel(
     int tok = tok0 + tid;
     int b = tok / n_new, i = tok % n_new;
     int pos0 = positions[b];
-    bool bad = pos0 < 0 || (int64_t)pos0 + n_new > L_cap;
-    if (!bad) {
+    bool bad = pos0 < 0 || (int64_t)pos0 + n_new > pg.capacity();
+    const int64_t prow = bad ? -1 : pg.phys_row(b, pos0 + i);
+    if (prow >= 0) {
       float a = 1.0f / sqrtf(ksq[tid] / (float)dc + eps);
-      alpha[((size_t)b * L_cap + pos0 + i) * G + g] = a;
+      alpha[(size_t)prow * G + g] = a;
     }
   }
 }
@@ -196,7 +202,7 @@ constexpr int kAlphaMaxDc = 256;
 __global__ __launch_bounds__(256) void append_bf16_kernel(
     int batch, int n_new, const uint16_t* __restrict__ c_new, const uint16_t* __restrict__ kr_new,
     const float* __restrict__ w_uk, const float* __restrict__ gkr,
-    const int32_t* __restrict__ positions, int L_cap, uint16_t* __restrict__ lat,
+    const int32_t* __restrict__ positions, const Paging pg, uint16_t* __restrict__ lat,
     uint16_t* __restrict__ rope, float* __restrict__ alpha, int32_t* status, int G, int r,
     int dc, int dr, float eps, float base, int qk_norm) {
   __shared__ __attribute__((aligned(16))) uint16_t w_hi[kAlphaChunk][kAlphaMaxDc];
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(
   const int duty = blockIdx.y;
   if (qk_norm ? duty == G : duty == 0) {
     copy_rows_and_rope<uint16_t>(tok0, kAlphaTok, batch, n_new, c_new, kr_new, gkr, positions,
-                                 L_cap, lat, rope, status, r, dr, eps, base, qk_norm, rsum);
+                                 pg, lat, rope, status, r, dr, eps, base, qk_norm, rsum);
     return;
   }
   const int g = duty;
@@ -275,9 +281,11 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(
     if (tok < T_total) {
       const int b = tok / n_new, i = tok % n_new;
       const int pos0 = positions[b];
-      if (!(pos0 < 0 || (int64_t)pos0 + n_new > L_cap)) {
+      const bool bad = pos0 < 0 || (int64_t)pos0 + n_new > pg.capacity();
+      const int64_t prow = bad ? -1 : pg.phys_row(b, pos0 + i);
+      if (prow >= 0) {
         const float ss = ssq[0][tid] + ssq[1][tid] + ssq[2][tid] + ssq[3][tid];
-        alpha[((size_t)b * L_cap + pos0 + i) * G + g] = 1.0f / sqrtf(ss / (float)dc + eps);
+        alpha[(size_t)prow * G + g] = 1.0f / sqrtf(ss / (float)dc + eps);
       }
     }
   }
@@ -285,8 +293,8 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(
 
 hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
                          const void* k_rope_new, const float* w_uk, const float* gkr,
-                         const int32_t* positions, int L_cap, void* lat, void* rope, float* alpha,
-                         int32_t* status, hipStream_t s) {
+                         const int32_t* positions, const Paging& pg, void* lat, void* rope,
+                         float* alpha, int32_t* status, hipStream_t s) {
   int T_total = batch * n_new;
   // The MFMA kernel reads latent rows and W^UK as 16-byte vectors.
   const bool vec_ok = ((uintptr_t)c_new % 16 == 0) && ((uintptr_t)w_uk % 16 == 0 || !c.qk_norm);
@@ -295,7 +303,7 @@ hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
     dim3 g2((unsigned)((T_total + kAlphaTok - 1) / kAlphaTok), c.qk_norm ? c.G + 1 : 1);
     append_bf16_kernel<<<g2, 256, 0, s>>>(batch, n_new, (const uint16_t*)c_new,
                                           (const uint16_t*)k_rope_new, w_uk, gkr, positions,
-                                          L_cap, (uint16_t*)lat, (uint16_t*)rope, alpha, status,
+                                          pg, (uint16_t*)lat, (uint16_t*)rope, alpha, status,
                                           c.G, c.r, c.dc, c.dr, c.eps, c.base, c.qk_norm);
     return hipGetLastError();
   }
@@ -303,11 +311,11 @@ hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
   if (c.dtype == QKMLA_BF16)
     append_kernel<uint16_t><<<grid, 256, 0, s>>>(
         batch, n_new, (const uint16_t*)c_new, (const uint16_t*)k_rope_new, w_uk, gkr, positions,
-        L_cap, (uint16_t*)lat, (uint16_t*)rope, alpha, status, c.G, c.r, c.dc, c.dr, c.eps,
+        pg, (uint16_t*)lat, (uint16_t*)rope, alpha, status, c.G, c.r, c.dc, c.dr, c.eps,
         c.base, c.qk_norm);
   else
     append_kernel<float><<<grid, 256, 0, s>>>(
-        batch, n_new, (const float*)c_new, (const float*)k_rope_new, w_uk, gkr, positions, L_cap,
+        batch, n_new, (const float*)c_new, (const float*)k_rope_new, w_uk, gkr, positions, pg,
         (float*)lat, (float*)rope, alpha, status, c.G, c.r, c.dc, c.dr, c.eps, c.base,
         c.qk_norm);
   return hipGetLastError();

@@ -306,6 +306,40 @@ int qkmla_absorb_weights(const qkmla_config* cfg, const float* w_uk, const float
   return hip_status(launch_absorb(c, w_uk, gamma_q, gamma_k, w_qabs, as_stream(stream)), "absorb");
 }
 
+// Checks a caller's page description; on success *pg describes it.
+static int check_pages(const qkmla_pages* pages, const char* who, Paging* pg) {
+  if (!pages || !pages->block_table)
+    return fail(QKMLA_ERR_INVALID_ARG, "%s: NULL page description or block table", who);
+  if (pages->max_blocks < 1 || pages->page_size < 1 || pages->num_pages < 1)
+    return fail(QKMLA_ERR_INVALID_ARG, "%s: max_blocks, page_size and num_pages must be >= 1", who);
+  if ((int64_t)pages->max_blocks * pages->page_size > INT32_MAX)
+    return fail(QKMLA_ERR_INVALID_ARG, "%s: max_blocks * page_size above 2^31 - 1", who);
+  if (!aligned(pages->block_table, 4))
+    return fail(QKMLA_ERR_INVALID_ARG, "%s: block table must be 4-byte aligned", who);
+  *pg = Paging{pages->block_table, pages->max_blocks, pages->page_size, pages->num_pages};
+  return QKMLA_OK;
+}
+
+static int append_impl(const Cfg& c, int32_t batch, int32_t n_new, const void* c_new,
+                       const void* k_rope_new, const float* w_uk, const float* gamma_k_rope,
+                       const int32_t* positions, const Paging& pg, void* latent_cache,
+                       void* rope_cache, float* alpha_cache, int32_t* status, void* stream) {
+  if ((int64_t)batch * n_new > (int64_t)1 << 30)
+    return fail(QKMLA_ERR_UNSUPPORTED, "append: too many tokens in one call");
+  if (!c_new || !k_rope_new || !positions || !latent_cache || !rope_cache ||
+      (c.qk_norm && (!w_uk || !gamma_k_rope || !alpha_cache)))
+    return fail(QKMLA_ERR_INVALID_ARG, "append: NULL pointer");
+  const size_t es = elem_size(c);
+  if (!aligned(c_new, es) || !aligned(k_rope_new, es) || !aligned(latent_cache, es) ||
+      !aligned(rope_cache, es) || (alpha_cache && !aligned(alpha_cache, 4)) ||
+      (w_uk && !aligned(w_uk, 4)) || !aligned(positions, 4))
+    return fail(QKMLA_ERR_INVALID_ARG, "append: pointers must be aligned to their element size");
+  return hip_status(launch_append(c, batch, n_new, c_new, k_rope_new, w_uk, gamma_k_rope, positions,
+                                  pg, latent_cache, rope_cache, alpha_cache, status,
+                                  as_stream(stream)),
+                    "append");
+}
+
 int qkmla_append(const qkmla_config* cfg, int32_t batch, int32_t n_new, const void* c_new,
                  const void* k_rope_new, const float* w_uk, const float* gamma_k_rope,
                  const int32_t* positions, int32_t cache_capacity, void* latent_cache,
@@ -316,20 +350,25 @@ int qkmla_append(const qkmla_config* cfg, int32_t batch, int32_t n_new, const vo
   if (batch < 0 || n_new < 0 || cache_capacity < 1)
     return fail(QKMLA_ERR_INVALID_ARG, "append: batch/n_new must be >= 0, cache_capacity >= 1");
   if (batch == 0 || n_new == 0) return ok();
-  if ((int64_t)batch * n_new > (int64_t)1 << 30)
-    return fail(QKMLA_ERR_UNSUPPORTED, "append: too many tokens in one call");
-  if (!c_new || !k_rope_new || !positions || !latent_cache || !rope_cache ||
-      (c.qk_norm && (!w_uk || !gamma_k_rope || !alpha_cache)))
-    return fail(QKMLA_ERR_INVALID_ARG, "append: NULL pointer");
-  const size_t es = elem_size(c);
-  if (!aligned(c_new, es) || !aligned(k_rope_new, es) || !aligned(latent_cache, es) ||
-      !aligned(rope_cache, es) || (alpha_cache && !aligned(alpha_cache, 4)) ||
-      (w_uk && !aligned(w_uk, 4)))
-    return fail(QKMLA_ERR_INVALID_ARG, "append: pointers must be aligned to their element size");
-  return hip_status(launch_append(c, batch, n_new, c_new, k_rope_new, w_uk, gamma_k_rope, positions,
-                                  cache_capacity, latent_cache, rope_cache, alpha_cache, status,
-                                  as_stream(stream)),
-                    "append");
+  return append_impl(c, batch, n_new, c_new, k_rope_new, w_uk, gamma_k_rope, positions,
+                     contiguous_paging(batch, cache_capacity), latent_cache, rope_cache,
+                     alpha_cache, status, stream);
+}
+
+int qkmla_append_paged(const qkmla_config* cfg, int32_t batch, int32_t n_new, const void* c_new,
+                       const void* k_rope_new, const float* w_uk, const float* gamma_k_rope,
+                       const int32_t* positions, const qkmla_pages* pages, void* latent_pool,
+                       void* rope_pool, float* alpha_pool, int32_t* status, void* stream) {
+  Cfg c;
+  int st = check_cfg(cfg, &c);
+  if (st) return st;
+  if (batch < 0 || n_new < 0)
+    return fail(QKMLA_ERR_INVALID_ARG, "append: batch/n_new must be >= 0");
+  if (batch == 0 || n_new == 0) return ok();
+  Paging pg;
+  if ((st = check_pages(pages, "append", &pg))) return st;
+  return append_impl(c, batch, n_new, c_new, k_rope_new, w_uk, gamma_k_rope, positions, pg,
+                     latent_pool, rope_pool, alpha_pool, status, stream);
 }
 
 size_t qkmla_decode_workspace_size(const qkmla_config* cfg, int32_t batch, int32_t max_seq_len) {
@@ -342,6 +381,55 @@ size_t qkmla_decode_workspace_size(const qkmla_config* cfg, int32_t batch, int32
   if (batch == 0) return 256;
   const int n_wg = plan_n_wg(c, batch, max_seq_len, device_cu_count());
   return ws_layout(c, batch, n_wg).total;
+}
+
+static int decode_impl(const Cfg& c, int32_t batch, int32_t s_q, const void* q_c,
+                       const void* q_rope, const void* w_qabs, const float* gamma_q_rope,
+                       const void* latent_cache, const void* rope_cache, const float* alpha_cache,
+                       const int32_t* seq_lens, const Paging& pg, int32_t max_seq_len,
+                       void* workspace, size_t workspace_bytes, float* o_lat, float* lse,
+                       int32_t* status, void* stream) {
+  if ((int64_t)batch * s_q > kMaxBatch)
+    return fail(QKMLA_ERR_UNSUPPORTED, "decode: batch * s_q above %d", kMaxBatch);
+  if (!q_c || !q_rope || !w_qabs || !latent_cache || !rope_cache || !seq_lens || !workspace ||
+      !o_lat || (c.qk_norm && (!gamma_q_rope || !alpha_cache)))
+    return fail(QKMLA_ERR_INVALID_ARG, "decode: NULL pointer");
+  // The bf16 path reads queries, weights and cache rows as 16-byte vectors.
+  const size_t va = c.dtype == QKMLA_BF16 ? 16 : 4;
+  if (!aligned(q_c, va) || !aligned(q_rope, va) || !aligned(w_qabs, va) ||
+      !aligned(latent_cache, va) || !aligned(rope_cache, va) ||
+      (alpha_cache && !aligned(alpha_cache, 4)) || !aligned16(workspace) || !aligned(o_lat, va) ||
+      (lse && !aligned(lse, 4)) || !aligned(seq_lens, 4))
+    return fail(QKMLA_ERR_INVALID_ARG,
+                "decode: pointers must be %zu-byte aligned (alpha, lse, seq_lens: 4; workspace: 16)", va);
+  // The split-KV kernel loads whole 32-row tiles from one page.
+  if (c.dtype == QKMLA_BF16 && pg.bt && pg.page_size % kTile != 0)
+    return fail(QKMLA_ERR_UNSUPPORTED, "decode: bf16 pages must hold a multiple of %d rows", kTile);
+  hipStream_t s = as_stream(stream);
+  const int nv = batch * s_q;  // one virtual sequence per query row
+  const int n_wg = plan_n_wg(c, nv, max_seq_len, device_cu_count());
+  const WsLayout ws = ws_layout(c, nv, n_wg);
+  if (workspace_bytes < ws.total)
+    return fail(QKMLA_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
+                ws.total);
+  hipError_t e = launch_qprep(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens, pg, ws,
+                              workspace, status, s);
+  if (e != hipSuccess) return hip_status(e, "decode/qprep");
+  if (c.dtype == QKMLA_BF16) {
+    const bool timed = g_timer.on && g_timer.n < 4096;
+    if (timed && (e = timer_record(s, 0)) != hipSuccess) return hip_status(e, "decode/timer");
+    e = launch_decode_mfma(c, batch, s_q, seq_lens, pg, latent_cache, rope_cache, alpha_cache, ws,
+                           workspace, n_wg, o_lat, lse, s);
+    if (e != hipSuccess) return hip_status(e, "decode/splitkv");
+    if (timed && (e = timer_record(s, 1)) != hipSuccess) return hip_status(e, "decode/timer");
+    e = launch_merge(c, batch, s_q, ws, workspace, n_wg, o_lat, lse, s);
+    if (e != hipSuccess) return hip_status(e, "decode/merge");
+  } else {
+    e = launch_decode_generic(c, batch, s_q, seq_lens, pg, latent_cache, rope_cache, alpha_cache,
+                              ws, workspace, o_lat, lse, s);
+    if (e != hipSuccess) return hip_status(e, "decode/generic");
+  }
+  return ok();
 }
 
 int qkmla_decode_multi(const qkmla_config* cfg, int32_t batch, int32_t s_q, const void* q_c,
@@ -359,44 +447,31 @@ int qkmla_decode_multi(const qkmla_config* cfg, int32_t batch, int32_t s_q, cons
                 "decode: need batch >= 0, s_q >= 1 and 1 <= max_seq_len (%d) <= cache_capacity (%d)",
                 max_seq_len, cache_capacity);
   if (batch == 0) return ok();
-  if ((int64_t)batch * s_q > kMaxBatch)
-    return fail(QKMLA_ERR_UNSUPPORTED, "decode: batch * s_q above %d", kMaxBatch);
-  if (!q_c || !q_rope || !w_qabs || !latent_cache || !rope_cache || !seq_lens || !workspace ||
-      !o_lat || (c.qk_norm && (!gamma_q_rope || !alpha_cache)))
-    return fail(QKMLA_ERR_INVALID_ARG, "decode: NULL pointer");
-  // The bf16 path reads queries, weights and cache rows as 16-byte vectors.
-  const size_t va = c.dtype == QKMLA_BF16 ? 16 : 4;
-  if (!aligned(q_c, va) || !aligned(q_rope, va) || !aligned(w_qabs, va) ||
-      !aligned(latent_cache, va) || !aligned(rope_cache, va) ||
-      (alpha_cache && !aligned(alpha_cache, 4)) || !aligned16(workspace) || !aligned(o_lat, va) ||
-      (lse && !aligned(lse, 4)) || !aligned(seq_lens, 4))
-    return fail(QKMLA_ERR_INVALID_ARG,
-                "decode: pointers must be %zu-byte aligned (alpha, lse, seq_lens: 4; workspace: 16)", va);
-  hipStream_t s = as_stream(stream);
-  const int nv = batch * s_q;  // one virtual sequence per query row
-  const int n_wg = plan_n_wg(c, nv, max_seq_len, device_cu_count());
-  const WsLayout ws = ws_layout(c, nv, n_wg);
-  if (workspace_bytes < ws.total)
-    return fail(QKMLA_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
-                ws.total);
-  hipError_t e = launch_qprep(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens,
-                              cache_capacity, ws, workspace, status, s);
-  if (e != hipSuccess) return hip_status(e, "decode/qprep");
-  if (c.dtype == QKMLA_BF16) {
-    const bool timed = g_timer.on && g_timer.n < 4096;
-    if (timed && (e = timer_record(s, 0)) != hipSuccess) return hip_status(e, "decode/timer");
-    e = launch_decode_mfma(c, batch, s_q, seq_lens, cache_capacity, latent_cache, rope_cache,
-                           alpha_cache, ws, workspace, n_wg, o_lat, lse, s);
-    if (e != hipSuccess) return hip_status(e, "decode/splitkv");
-    if (timed && (e = timer_record(s, 1)) != hipSuccess) return hip_status(e, "decode/timer");
-    e = launch_merge(c, batch, s_q, ws, workspace, n_wg, o_lat, lse, s);
-    if (e != hipSuccess) return hip_status(e, "decode/merge");
-  } else {
-    e = launch_decode_generic(c, batch, s_q, seq_lens, cache_capacity, latent_cache, rope_cache,
-                              alpha_cache, ws, workspace, o_lat, lse, s);
-    if (e != hipSuccess) return hip_status(e, "decode/generic");
-  }
-  return ok();
+  return decode_impl(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, rope_cache,
+                     alpha_cache, seq_lens, contiguous_paging(batch, cache_capacity), max_seq_len,
+                     workspace, workspace_bytes, o_lat, lse, status, stream);
+}
+
+int qkmla_decode_paged(const qkmla_config* cfg, int32_t batch, int32_t s_q, const void* q_c,
+                       const void* q_rope, const void* w_qabs, const float* gamma_q_rope,
+                       const void* latent_pool, const void* rope_pool, const float* alpha_pool,
+                       const int32_t* seq_lens, const qkmla_pages* pages, int32_t max_seq_len,
+                       void* workspace, size_t workspace_bytes, float* o_lat, float* lse,
+                       int32_t* status, void* stream) {
+  Cfg c;
+  int st = check_cfg(cfg, &c);
+  if (st) return st;
+  if (batch < 0 || s_q < 1 || max_seq_len < 1)
+    return fail(QKMLA_ERR_INVALID_ARG, "decode: need batch >= 0, s_q >= 1, max_seq_len >= 1");
+  if (batch == 0) return ok();
+  Paging pg;
+  if ((st = check_pages(pages, "decode", &pg))) return st;
+  if (max_seq_len > pg.capacity())
+    return fail(QKMLA_ERR_INVALID_ARG, "decode: max_seq_len (%d) above max_blocks * page_size (%d)",
+                max_seq_len, pg.capacity());
+  return decode_impl(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, latent_pool, rope_pool,
+                     alpha_pool, seq_lens, pg, max_seq_len, workspace, workspace_bytes, o_lat, lse,
+                     status, stream);
 }
 
 int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const void* q_rope,

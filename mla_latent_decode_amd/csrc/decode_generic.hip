@@ -15,18 +15,20 @@ constexpr int kGenMaxR = 1024;
 constexpr int kGenMaxDr = 256;
 
 __global__ __launch_bounds__(256) void decode_generic_kernel(
-    const int32_t* __restrict__ seq_lens, int s_q, int L_cap, int H, int G, int r, int dr, int qk_norm,
+    const int32_t* __restrict__ seq_lens, int s_q, Paging pg, int H, int G, int r, int dr, int qk_norm,
     const float* __restrict__ lat, const float* __restrict__ rope, const float* __restrict__ alpha,
     const float* __restrict__ q_tilde, const float* __restrict__ alpha_q,
     const float* __restrict__ q_rope, float* __restrict__ o_lat, float* __restrict__ lse) {
   __shared__ float qt[kGenMaxR];
   __shared__ float qr[kGenMaxDr];
   __shared__ float p[kGenChunk];
+  __shared__ int64_t prow[kGenChunk];  // physical cache row of each token of the chunk
   __shared__ float red[4];
   // b: virtual sequence (query row b % s_q of cache b / s_q)
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int bc = b / s_q;
   const int g = (h * G) / H;
+  const int L_cap = pg.capacity();
   const int L = virt_len(seq_lens, b, s_q, L_cap);
   float* out = o_lat + ((size_t)b * H + h) * r;
   if (L < 1 || L > L_cap) {
@@ -38,8 +40,6 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   for (int i = tid; i < dr; i += blockDim.x) qr[i] = q_rope[((size_t)b * H + h) * dr + i];
   const float aq = alpha_q[(size_t)b * H + h];
   __syncthreads();
-  const float* latb = lat + (size_t)bc * L_cap * r;
-  const float* ropeb = rope + (size_t)bc * L_cap * dr;
   // each thread owns output dims tid, tid+256, ... (r <= 1024 -> 4 per thread)
   float acc[kGenMaxR / 256];
 #pragma unroll
@@ -49,13 +49,17 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     const int t = t0 + tid;
     float logit = -INFINITY;
     if (t < L) {
-      const float* c = latb + (size_t)t * r;
+      // a block-table entry outside the pool reads page 0 (q-prep reports it)
+      const int64_t pr = pg.phys_row(bc, t);
+      const int64_t row = pr < 0 ? (int64_t)(t % pg.page_size) : pr;
+      prow[tid] = row;
+      const float* c = lat + (size_t)row * r;
       float sc = 0.f;
       for (int i = 0; i < r; ++i) sc += qt[i] * c[i];
-      const float* kr = ropeb + (size_t)t * dr;
+      const float* kr = rope + (size_t)row * dr;
       float sr = 0.f;
       for (int i = 0; i < dr; ++i) sr += qr[i] * kr[i];
-      float ak = qk_norm ? alpha[((size_t)bc * L_cap + t) * G + g] : 1.0f;
+      float ak = qk_norm ? alpha[(size_t)row * G + g] : 1.0f;
       logit = sc * (aq * ak) + sr;
     }
     // chunk max
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
       int i = tid + 256 * k;
       if (i < r) {
         float a = acc[k] * f;
-        for (int tt = 0; tt < n; ++tt) a += p[tt] * latb[(size_t)(t0 + tt) * r + i];
+        for (int tt = 0; tt < n; ++tt) a += p[tt] * lat[(size_t)prow[tt] * r + i];
         acc[k] = a;
       }
     }
@@ -96,12 +100,13 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 }
 
 hipError_t launch_decode_generic(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,
-                                 int L_cap, const void* lat, const void* rope, const float* alpha,
+                                 const Paging& pg, const void* lat, const void* rope,
+                                 const float* alpha,
                                  const WsLayout& ws, void* workspace, float* o_lat, float* lse,
                                  hipStream_t s) {
   char* wsb = (char*)workspace;
   decode_generic_kernel<<<dim3(batch * s_q, c.H), 256, 0, s>>>(
-      seq_lens, s_q, L_cap, c.H, c.G, c.r, c.dr, c.qk_norm, (const float*)lat, (const float*)rope,
+      seq_lens, s_q, pg, c.H, c.G, c.r, c.dr, c.qk_norm, (const float*)lat, (const float*)rope,
       alpha, (const float*)(wsb + ws.q_tilde), (const float*)(wsb + ws.alpha_q),
       (const float*)(wsb + ws.q_rope), o_lat, lse);
   return hipGetLastError();

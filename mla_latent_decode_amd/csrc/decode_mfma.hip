@@ -117,7 +117,8 @@ struct Args {
   const int32_t* seq_lens;
   int B;    // virtual sequences: batch * s_q (one per query row)
   int s_q;  // query rows per sequence
-  int H, G, L_cap, n_wg;
+  int H, G, n_wg;
+  Paging pg;  // where cache rows live (pages of a multiple of kTile rows, or contiguous)
   const uint16_t* lat;
   const uint16_t* rope;
   const float* alpha;
@@ -140,10 +141,11 @@ struct TileLoads {
 
 // The sequence a segment belongs to (wave-uniform values).
 struct Seq {
-  const char* lat;    // latent rows of the sequence, 1 KB each
-  const char* rope;   // RoPE rows, 128 B each
-  const char* alpha;  // alpha rows, 4*G B each
-  int L;              // sequence length
+  const char* lat;    // latent row pool, 1 KB per row
+  const char* rope;   // RoPE row pool, 128 B per row
+  const char* alpha;  // alpha row pool, 4*G B per row
+  int cb;             // cache (sequence of the batch) whose rows are read
+  int L;              // length of the (virtual) sequence
 };
 
 // Per-wavefront state carried across the tiles of a segment.
@@ -165,7 +167,8 @@ struct Wave {
 //   alpha:  [g][32 tokens] floats.
 // Rows past the end of the sequence repeat its last row (masked later).
 template <bool QKN, int NW, int S>
-__device__ __forceinline__ void issue_tile(const Seq& sq, int G, int tile, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(const Seq& sq, const Paging& pg, int G, int tile,
+                                           int wave, int lane) {
   char* st = stage_buf<S>();
   // Opaque copies of the tile's first row and the lane offset keep the address
   // arithmetic here, as a scalar row base plus a 32-bit lane offset (the
@@ -176,31 +179,50 @@ __device__ __forceinline__ void issue_tile(const Seq& sq, int G, int tile, int w
   asm volatile("" : "+s"(t0));
   uint32_t lane16 = (uint32_t)lane << 4;
   asm volatile("" : "+v"(lane16));
+  // The tile lies in one page (page sizes are multiples of kTile; a contiguous
+  // cache is one page per sequence).  A block-table entry outside the pool
+  // reads page 0 instead; q-prep has reported it.
+  int64_t prow0 = (int64_t)sq.cb * pg.page_size + t0;  // contiguous: page cb, no table
+  if (pg.bt) {
+    const int blk = t0 / pg.page_size;
+    // Table entry through the constant address space: a scalar load, waited
+    // on by lgkmcnt rather than vmcnt, so the tile loads in flight keep going.
+    const __attribute__((address_space(4))) int32_t* row =
+        (const __attribute__((address_space(4))) int32_t*)(pg.bt + (size_t)sq.cb * pg.max_blocks);
+    int page = row[blk];
+    page = (page >= 0 && page < pg.num_pages) ? page : 0;
+    prow0 = (int64_t)page * pg.page_size + (t0 - blk * pg.page_size);
+  }
+  const int last = sq.L - 1 - t0;  // rows past the sequence repeat its last row
+  const char* latb = sq.lat + prow0 * (kR * 2);
 #pragma unroll
   for (int i = 0; i < TileLoads<QKN, NW>::lat; ++i) {
     const int tr = wave + i * NW;
-    const int row = min(t0 + tr, sq.L - 1);
-    __builtin_amdgcn_global_load_lds(QK_GLB(void, sq.lat + (size_t)row * (kR * 2) + lane16),
+    const char* rowp = latb + (size_t)min(tr, last) * (kR * 2);
+    asm volatile("" : "+s"(rowp));  // scalar row base, then the lane offset
+    __builtin_amdgcn_global_load_lds(QK_GLB(void, rowp + lane16),
                                      QK_LDS(void, st + tr * kLatRow), 16, 0, 0);
   }
   const int t = lane & 31;
-  const uint32_t rrow = (uint32_t)min(t0 + t, sq.L - 1);
-  const uint32_t rope_off = rrow * (kDr * 2) + ((uint32_t)(lane >> 5) << 4);
+  const uint32_t rr = (uint32_t)min(t, last);
+  const char* ropeb = sq.rope + prow0 * (kDr * 2);
+  const uint32_t rope_off = rr * (kDr * 2) + ((uint32_t)(lane >> 5) << 4);
 #pragma unroll
   for (int i = 0; i < TileLoads<QKN, NW>::rope; ++i) {
-    const int blk = wave + i * NW;  // chunks 2*blk, 2*blk+1
-    __builtin_amdgcn_global_load_lds(QK_GLB(void, sq.rope + blk * 32 + rope_off),
-                                     QK_LDS(void, st + kLatBytes + blk * 1024), 16, 0, 0);
+    const int blk2 = wave + i * NW;  // chunks 2*blk2, 2*blk2+1
+    __builtin_amdgcn_global_load_lds(QK_GLB(void, ropeb + blk2 * 32 + rope_off),
+                                     QK_LDS(void, st + kLatBytes + blk2 * 1024), 16, 0, 0);
   }
   if constexpr (QKN) {
-    const uint32_t a_off = rrow * (uint32_t)(G * 4);
+    const char* alphab = sq.alpha + prow0 * (G * 4);
+    const uint32_t a_off = rr * (uint32_t)(G * 4);
 #pragma unroll
     for (int i = 0; i < TileLoads<QKN, NW>::alpha; ++i) {
-      const int blk = wave + i * NW;  // groups 2*blk, 2*blk+1
-      int g = 2 * blk + (lane >> 5);
+      const int blk2 = wave + i * NW;  // groups 2*blk2, 2*blk2+1
+      int g = 2 * blk2 + (lane >> 5);
       g = g < G ? g : G - 1;
-      __builtin_amdgcn_global_load_lds(QK_GLB(void, sq.alpha + a_off + (uint32_t)(g * 4)),
-                                       QK_LDS(void, st + kLatBytes + kRopeBytes + blk * 256),
+      __builtin_amdgcn_global_load_lds(QK_GLB(void, alphab + a_off + (uint32_t)(g * 4)),
+                                       QK_LDS(void, st + kLatBytes + kRopeBytes + blk2 * 256),
                                        4, 0, 0);
     }
   }
@@ -227,13 +249,13 @@ constexpr int kPvAhead = 3;                    // C^T operands in flight ahead o
 // branches it merges the paths conservatively and then waits for every load
 // in flight before reading a tile.
 template <bool QKN, int NW, int S>
-__device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, int G, int tile0, int i, int nt,
-                                          int wave, int lane, int g) {
+__device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, const Paging& pg, int G,
+                                          int tile0, int i, int nt, int wave, int lane, int g) {
   if (i + 1 < nt) wait_vmcnt<TileLoads<QKN, NW>::total>();
   else wait_vmcnt<0>();
   block_sync();  // the tile is in LDS for every wave; stage (S+2)%3 is free
   if constexpr (S != 0)
-    if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, G, tile0 + i + 2, wave, lane);
+    if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, pg, G, tile0 + i + 2, wave, lane);
   const char* st = stage_buf<S>();
   const int hf = lane >> 5;
   const int m = lane & 31;
@@ -288,7 +310,7 @@ __device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, int G, int til
   // prefetch is not among them, and the tile that is has been in flight for a
   // whole step.
   if constexpr (S == 0)
-    if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, G, tile0 + i + 2, wave, lane);
+    if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, pg, G, tile0 + i + 2, wave, lane);
 
   // The first C^T operands of P.C do not depend on the softmax: read them now.
   // lane (in its 16-lane group): token 4*hf + (s16>>2) of the 16-token step,
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
   // run ahead of the loads in flight into the other stages.
   __shared__ __attribute__((aligned(2048))) int P[kMaxBatch + 1];
   if (threadIdx.x < 4) lds_restart[threadIdx.x] = 0;
-  build_tile_prefix(a.seq_lens, a.B, a.s_q, a.L_cap, P);
+  build_tile_prefix(a.seq_lens, a.B, a.s_q, a.pg.capacity(), P);
   if (blockIdx.x == 0)  // the merge reads the prefix instead of rebuilding it per block
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.plan[i] = P[i];
 
@@ -395,16 +417,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
     // b: virtual sequence (query row b % s_q of cache b / s_q)
     const int b = __builtin_amdgcn_readfirstlane(seq_of(P, a.B, x));
     Seq sq;
-    sq.L = __builtin_amdgcn_readfirstlane(virt_len(a.seq_lens, b, a.s_q, a.L_cap));
+    sq.L = __builtin_amdgcn_readfirstlane(virt_len(a.seq_lens, b, a.s_q, a.pg.capacity()));
     const int64_t s0 = __builtin_amdgcn_readfirstlane(P[b]);
     const int64_t s1 = __builtin_amdgcn_readfirstlane(P[b + 1]);
     const int64_t seg_end = e < s1 ? e : s1;
     const int tile0 = (int)(x - s0);
     const int nt = (int)(seg_end - x);
-    const size_t seq_row0 = (size_t)(b / a.s_q) * a.L_cap;
-    sq.lat = (const char*)(a.lat + seq_row0 * kR);
-    sq.rope = (const char*)(a.rope + seq_row0 * kDr);
-    sq.alpha = QKN ? (const char*)(a.alpha + seq_row0 * a.G) : nullptr;
+    sq.cb = b / a.s_q;
+    sq.lat = (const char*)a.lat;
+    sq.rope = (const char*)a.rope;
+    sq.alpha = QKN ? (const char*)a.alpha : nullptr;
     const size_t qrow = (size_t)b * a.H + head;
 
     // Query operands for this sequence: q~ in registers, the RoPE query in
@@ -426,12 +448,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) w.O[ii][j] = 0.f;
       w.l_run = 0.f;
-      issue_tile<QKN, NW, 0>(sq, a.G, tile0, wave, lane);
-      if (nt > 1) issue_tile<QKN, NW, 1>(sq, a.G, tile0 + 1, wave, lane);
+      issue_tile<QKN, NW, 0>(sq, a.pg, a.G, tile0, wave, lane);
+      if (nt > 1) issue_tile<QKN, NW, 1>(sq, a.pg, a.G, tile0 + 1, wave, lane);
       for (int i = 0; i < nt; i += kStages) {
-        tile_step<QKN, NW, 0>(w, sq, a.G, tile0, i, nt, wave, lane, g);
-        if (i + 1 < nt) tile_step<QKN, NW, 1>(w, sq, a.G, tile0, i + 1, nt, wave, lane, g);
-        if (i + 2 < nt) tile_step<QKN, NW, 2>(w, sq, a.G, tile0, i + 2, nt, wave, lane, g);
+        tile_step<QKN, NW, 0>(w, sq, a.pg, a.G, tile0, i, nt, wave, lane, g);
+        if (i + 1 < nt) tile_step<QKN, NW, 1>(w, sq, a.pg, a.G, tile0, i + 1, nt, wave, lane, g);
+        if (i + 2 < nt) tile_step<QKN, NW, 2>(w, sq, a.pg, a.G, tile0, i + 2, nt, wave, lane, g);
       }
       block_sync();
       if (!(lds_restart[0] | lds_restart[1] | lds_restart[2] | lds_restart[3])) break;
@@ -485,9 +507,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,
-                              int L_cap, const void* lat, const void* rope, const float* alpha,
-                              const WsLayout& ws, void* workspace, int n_wg, float* o_lat,
-                              float* lse, hipStream_t s) {
+                              const Paging& pg, const void* lat, const void* rope,
+                              const float* alpha, const WsLayout& ws, void* workspace, int n_wg,
+                              float* o_lat, float* lse, hipStream_t s) {
   char* wsb = (char*)workspace;
   Args a;
   a.seq_lens = seq_lens;
@@ -495,7 +517,7 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* s
   a.s_q = s_q;
   a.H = c.H;
   a.G = c.G;
-  a.L_cap = L_cap;
+  a.pg = pg;
   a.n_wg = n_wg;
   a.lat = (const uint16_t*)lat;
   a.rope = (const uint16_t*)rope;

@@ -47,29 +47,58 @@ struct WsLayout {
 };
 WsLayout ws_layout(const Cfg& c, int batch, int n_wg);
 
+// ---- cache addressing ---------------------------------------------------------
+// The latent, RoPE and alpha caches are pools of num_pages pages of page_size
+// rows.  Row t of cache b is row t % page_size of page
+// bt[b * max_blocks + t / page_size].  A contiguous cache [B][L_cap] is the
+// case bt == nullptr, page_size = L_cap, page b for cache b.  The capacity of
+// one cache is max_blocks * page_size rows.
+struct Paging {
+  const int32_t* bt;  // device block table [B][max_blocks], or nullptr
+  int max_blocks;
+  int page_size;
+  int num_pages;
+  __host__ __device__ int capacity() const { return max_blocks * page_size; }
+  // Page holding rows [blk * page_size, (blk + 1) * page_size) of cache b;
+  // -1 if the block-table entry is outside [0, num_pages).
+  __device__ int page_of(int b, int blk) const {
+    if (!bt) return b;
+    const int page = bt[(size_t)b * max_blocks + blk];
+    return (page >= 0 && page < num_pages) ? page : -1;
+  }
+  // Physical row of row t of cache b, or -1 (bad block-table entry).
+  __device__ int64_t phys_row(int b, int t) const {
+    const int blk = t / page_size;
+    const int page = page_of(b, blk);
+    return page < 0 ? -1 : (int64_t)page * page_size + (t - blk * page_size);
+  }
+};
+inline Paging contiguous_paging(int batch, int L_cap) { return Paging{nullptr, 1, L_cap, batch}; }
+
 // ---- launchers (each enqueues on `stream`; returns the launch error) -------
 hipError_t launch_absorb(const Cfg& c, const float* w_uk, const float* gq, const float* gk,
                          void* w_qabs, hipStream_t s);
 hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
                          const void* k_rope_new, const float* w_uk, const float* gkr,
-                         const int32_t* positions, int L_cap, void* lat, void* rope, float* alpha,
-                         int32_t* status, hipStream_t s);
+                         const int32_t* positions, const Paging& pg, void* lat, void* rope,
+                         float* alpha, int32_t* status, hipStream_t s);
 // Decode launchers take `batch` sequences with `s_q` query rows each: query
 // row i of sequence b is virtual sequence b*s_q + i (its q rows, q~ rows and
 // outputs), at position seq_lens[b] - s_q + i over cache b (see virt_len).
 hipError_t launch_qprep(const Cfg& c, int batch, int s_q, const void* q_c, const void* q_rope,
-                        const void* w_qabs, const float* gqr, const int32_t* seq_lens, int L_cap,
-                        const WsLayout& ws, void* workspace, int32_t* status, hipStream_t s);
+                        const void* w_qabs, const float* gqr, const int32_t* seq_lens,
+                        const Paging& pg, const WsLayout& ws, void* workspace, int32_t* status,
+                        hipStream_t s);
 hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,
-                              int L_cap, const void* lat, const void* rope, const float* alpha,
-                              const WsLayout& ws, void* workspace, int n_wg, float* o_lat,
-                              float* lse, hipStream_t s);
+                              const Paging& pg, const void* lat, const void* rope,
+                              const float* alpha, const WsLayout& ws, void* workspace, int n_wg,
+                              float* o_lat, float* lse, hipStream_t s);
 hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, void* workspace,
                         int n_wg, float* o_lat, float* lse, hipStream_t s);
 hipError_t launch_decode_generic(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,
-                                 int L_cap, const void* lat, const void* rope, const float* alpha,
-                                 const WsLayout& ws, void* workspace, float* o_lat, float* lse,
-                                 hipStream_t s);
+                                 const Paging& pg, const void* lat, const void* rope,
+                                 const float* alpha, const WsLayout& ws, void* workspace,
+                                 float* o_lat, float* lse, hipStream_t s);
 hipError_t launch_out_proj(const Cfg& c, int batch, const float* o_lat, const void* w_uv,
                            float* out, hipStream_t s);
 

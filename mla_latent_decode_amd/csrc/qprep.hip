@@ -60,6 +60,18 @@ __device__ void prep_scalar_and_rope(const TIn* qc, const TIn* qr, const float* 
   }
 }
 
+// Paged caches: every block-table entry the sequence's rows need must name a
+// page of the pool; otherwise QKMLA_DEV_BAD_PAGE (the decode then reads page 0
+// in its place, and that sequence's output is undefined).  Checked once per
+// sequence, by its last query row (the longest prefix); block-wide.
+__device__ void check_pages(const Paging& pg, int v, int s_q, int L, int32_t* status) {
+  if (!pg.bt || !status || v % s_q != s_q - 1 || L < 1 || L > pg.capacity()) return;
+  const int nblk = (L + pg.page_size - 1) / pg.page_size;
+  bool bad = false;
+  for (int blk = threadIdx.x; blk < nblk; blk += blockDim.x) bad |= pg.page_of(v / s_q, blk) < 0;
+  if (bad) atomicOr(status, QKMLA_DEV_BAD_PAGE);
+}
+
 __device__ __forceinline__ int clamp_pos(int L, int L_cap) {
   return (L >= 1 && L <= L_cap) ? L - 1 : 0;
 }
@@ -71,13 +83,15 @@ __device__ __forceinline__ int clamp_pos(int L, int L_cap) {
 __global__ __launch_bounds__(256) void qprep_mfma_kernel(
     const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_qabs, const float* __restrict__ gqr,
-    const int32_t* __restrict__ seq_lens, int s_q, int L_cap, int H, int G, int r, int dc, int dr,
-    float eps, float tau, float base, int qk_norm, uint16_t* __restrict__ q_tilde,
+    const int32_t* __restrict__ seq_lens, int s_q, const Paging pg, int H, int G, int r, int dc,
+    int dr, float eps, float tau, float base, int qk_norm, uint16_t* __restrict__ q_tilde,
     float* __restrict__ alpha_q, uint16_t* __restrict__ q_rope_out, int32_t* status) {
   const int b = blockIdx.x, g = blockIdx.y;  // b: virtual sequence (query row)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h0 = g * 16;
+  const int L_cap = pg.capacity();
   const int L = virt_len(seq_lens, b, s_q, L_cap);
+  if (g == 0) check_pages(pg, b, s_q, L, status);
   if (g == 0 && threadIdx.x == 0 && (L < 1 || L > L_cap) && status)
     atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
   const int pos = clamp_pos(L, L_cap);
@@ -154,12 +168,14 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
 __global__ __launch_bounds__(256) void qprep_generic_kernel(
     const float* __restrict__ q_c, const float* __restrict__ q_rope,
     const float* __restrict__ w_qabs, const float* __restrict__ gqr,
-    const int32_t* __restrict__ seq_lens, int s_q, int L_cap, int H, int G, int r, int dc, int dr,
-    float eps, float tau, float base, int qk_norm, float* __restrict__ q_tilde,
+    const int32_t* __restrict__ seq_lens, int s_q, const Paging pg, int H, int G, int r, int dc,
+    int dr, float eps, float tau, float base, int qk_norm, float* __restrict__ q_tilde,
     float* __restrict__ alpha_q, float* __restrict__ q_rope_out, int32_t* status) {
   const int b = blockIdx.x, h = blockIdx.y;  // b: virtual sequence (query row)
   const int g = (h * G) / H;
+  const int L_cap = pg.capacity();
   const int L = virt_len(seq_lens, b, s_q, L_cap);
+  if (h == 0) check_pages(pg, b, s_q, L, status);
   if (h == 0 && threadIdx.x == 0 && (L < 1 || L > L_cap) && status)
     atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
   const int pos = clamp_pos(L, L_cap);
@@ -180,19 +196,20 @@ __global__ __launch_bounds__(256) void qprep_generic_kernel(
 }
 
 hipError_t launch_qprep(const Cfg& c, int batch, int s_q, const void* q_c, const void* q_rope,
-                        const void* w_qabs, const float* gqr, const int32_t* seq_lens, int L_cap,
-                        const WsLayout& ws, void* workspace, int32_t* status, hipStream_t s) {
+                        const void* w_qabs, const float* gqr, const int32_t* seq_lens,
+                        const Paging& pg, const WsLayout& ws, void* workspace, int32_t* status,
+                        hipStream_t s) {
   char* wsb = (char*)workspace;
   const int nv = batch * s_q;  // virtual sequences, one per query row
   if (c.dtype == QKMLA_BF16) {
     qprep_mfma_kernel<<<dim3(nv, c.G), 256, 0, s>>>(
         (const uint16_t*)q_c, (const uint16_t*)q_rope, (const uint16_t*)w_qabs, gqr, seq_lens,
-        s_q, L_cap, c.H, c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm,
+        s_q, pg, c.H, c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm,
         (uint16_t*)(wsb + ws.q_tilde), (float*)(wsb + ws.alpha_q), (uint16_t*)(wsb + ws.q_rope),
         status);
   } else {
     qprep_generic_kernel<<<dim3(nv, c.H), 256, 0, s>>>(
-        (const float*)q_c, (const float*)q_rope, (const float*)w_qabs, gqr, seq_lens, s_q, L_cap, c.H,
+        (const float*)q_c, (const float*)q_rope, (const float*)w_qabs, gqr, seq_lens, s_q, pg, c.H,
         c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm, (float*)(wsb + ws.q_tilde),
         (float*)(wsb + ws.alpha_q), (float*)(wsb + ws.q_rope), status);
   }

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqkmla.so")
 
 QKMLA_F32, QKMLA_BF16 = 0, 1
-QKMLA_DEV_BAD_SEQ_LEN, QKMLA_DEV_BAD_POSITION = 1, 2
+QKMLA_DEV_BAD_SEQ_LEN, QKMLA_DEV_BAD_POSITION, QKMLA_DEV_BAD_PAGE = 1, 2, 4
 
 
 class QkmlaError(RuntimeError):
@@ -38,6 +38,11 @@ class _Config(ctypes.Structure):
                 ("rope_base", ctypes.c_float)]
 
 
+class _Pages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise QkmlaError(f"{LIB_PATH} is missing: build it with "
@@ -45,12 +50,16 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     C = ctypes.POINTER(_Config)
+    PG = ctypes.POINTER(_Pages)
     sig = {
         "qkmla_absorb_weights": (I32, [C, P, P, P, P, P]),
         "qkmla_append": (I32, [C, I32, I32, P, P, P, P, P, I32, P, P, P, P, P]),
         "qkmla_decode_workspace_size": (SZ, [C, I32, I32]),
         "qkmla_decode": (I32, [C, I32, P, P, P, P, P, P, P, P, I32, I32, P, SZ, P, P, P, P]),
         "qkmla_decode_multi": (I32, [C, I32, I32, P, P, P, P, P, P, P, P, I32, I32, P, SZ, P, P,
+                                     P, P]),
+        "qkmla_append_paged": (I32, [C, I32, I32, P, P, P, P, P, PG, P, P, P, P, P]),
+        "qkmla_decode_paged": (I32, [C, I32, I32, P, P, P, P, P, P, P, P, PG, I32, P, SZ, P, P,
                                      P, P]),
         "qkmla_out_proj": (I32, [C, I32, P, P, P, P]),
         "qkmla_plan": (I32, [C, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
@@ -270,6 +279,62 @@ def decode_multi(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, r
         _ptr(o_lat, (B, s_q, H, r), torch.float32, "o_lat"),
         _ptr(lse, (B, s_q, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
         _stream()), "qkmla_decode_multi")
+    return o_lat
+
+
+def _pages(block_table, latent_pool):
+    """qkmla_pages for a device block table [B][max_blocks] and a latent pool
+    [num_pages][page_size][r]."""
+    if block_table.dim() != 2:
+        raise QkmlaError("block_table must be [B][max_blocks]")
+    return _Pages(_ptr(block_table, None, torch.int32, "block_table"), block_table.shape[1],
+                  latent_pool.shape[1], latent_pool.shape[0])
+
+
+def append_paged(cfg: Config, c_new, k_rope_new, w_uk, gamma_k_rope, positions, block_table,
+                 latent_pool, rope_pool, alpha_pool=None, status=None):
+    """qkmla_append into paged pools: latent_pool [num_pages][page_size][r],
+    rope_pool [num_pages][page_size][d_r], alpha_pool [num_pages][page_size][G],
+    block_table [B][max_blocks] int32 (device)."""
+    B, n_new = c_new.shape[0], c_new.shape[1]
+    NP, PS = latent_pool.shape[0], latent_pool.shape[1]
+    dt = cfg.torch_dtype
+    pg = _pages(block_table, latent_pool)
+    _check(_lib.qkmla_append_paged(
+        ctypes.byref(cfg.c()), B, n_new, _ptr(c_new, (B, n_new, cfg.latent_rank), dt, "c_new"),
+        _ptr(k_rope_new, (B, n_new, cfg.rope_dim), dt, "k_rope_new"),
+        _ptr(w_uk, None, torch.float32, "w_uk"), _ptr(gamma_k_rope, None, torch.float32, "gamma_k_rope"),
+        _ptr(positions, (B,), torch.int32, "positions"), ctypes.byref(pg),
+        _ptr(latent_pool, (NP, PS, cfg.latent_rank), dt, "latent_pool"),
+        _ptr(rope_pool, (NP, PS, cfg.rope_dim), dt, "rope_pool"),
+        _ptr(alpha_pool, (NP, PS, cfg.n_groups), torch.float32, "alpha_pool"),
+        _ptr(status, (1,), torch.int32, "status"), _stream()), "qkmla_append_paged")
+
+
+def decode_paged(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_pool, rope_pool,
+                 alpha_pool, seq_lens, block_table, max_seq_len: int, workspace, o_lat=None,
+                 lse=None, status=None):
+    """qkmla_decode_paged: q_c [B][s_q][H][d_c], q_rope [B][s_q][H][d_r]; pools and
+    block table as for append_paged.  Returns o_lat [B][s_q][H][r]."""
+    B, s_q = q_c.shape[0], q_c.shape[1]
+    NP, PS = latent_pool.shape[0], latent_pool.shape[1]
+    H, r, dt = cfg.n_heads, cfg.latent_rank, cfg.torch_dtype
+    if o_lat is None:
+        o_lat = torch.empty((B, s_q, H, r), dtype=torch.float32, device=q_c.device)
+    pg = _pages(block_table, latent_pool)
+    _check(_lib.qkmla_decode_paged(
+        ctypes.byref(cfg.c()), B, s_q, _ptr(q_c, (B, s_q, H, cfg.head_dim), dt, "q_c"),
+        _ptr(q_rope, (B, s_q, H, cfg.rope_dim), dt, "q_rope"),
+        _ptr(w_qabs, (cfg.n_groups, r, cfg.head_dim), dt, "w_qabs"),
+        _ptr(gamma_q_rope, None, torch.float32, "gamma_q_rope"),
+        _ptr(latent_pool, (NP, PS, r), dt, "latent_pool"),
+        _ptr(rope_pool, (NP, PS, cfg.rope_dim), dt, "rope_pool"),
+        _ptr(alpha_pool, (NP, PS, cfg.n_groups), torch.float32, "alpha_pool"),
+        _ptr(seq_lens, (B,), torch.int32, "seq_lens"), ctypes.byref(pg), max_seq_len,
+        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(o_lat, (B, s_q, H, r), torch.float32, "o_lat"),
+        _ptr(lse, (B, s_q, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
+        _stream()), "qkmla_decode_paged")
     return o_lat
 
 

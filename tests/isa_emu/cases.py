@@ -6,6 +6,7 @@ own process: the runtime stand-in must be the only HIP runtime loaded.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import sys
 import time
@@ -193,6 +194,110 @@ def multi_query(dev):
     run_multi(dev, Shape(6, 3, 20, 12, 4, 10, "f32"), (9, 33), 2, 510, "fp32 s_q=2")
     run_multi(dev, DSV3, (70, 40, 2), 3, 511, "bf16 s_q=3 (one row with an empty prefix)",
               n_wg=5, heads=MERGE_HEADS)
+
+
+class CPages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
+def scattered_table(B, max_blocks, num_pages, seed):
+    """Block table [B][max_blocks] over a random permutation of the pool's pages."""
+    perm = np.random.default_rng(seed).permutation(num_pages)[:B * max_blocks]
+    return perm.reshape(B, max_blocks).astype(np.int32)
+
+
+def run_paged(dev, shape, lens, s_q, page_size, seed, label, n_wg=None, heads=None,
+              bad_seq=None):
+    """Caches in scattered pages: the paged append must place every row the
+    contiguous append writes, bit for bit, and the paged decode must return
+    the contiguous decode's outputs bit for bit (same tiles, same plan), which
+    are checked against the oracle.  bad_seq: a sequence whose last table
+    entry points outside the pool (QKMLA_DEV_BAD_PAGE; the others unaffected)."""
+    P = ctypes.c_void_p
+    inp = make_inputs(shape, lens, seed=seed)
+    q_c, q_rope = multi_query_rows(shape, len(lens), s_q, seed=seed + 1)
+    if n_wg is not None:
+        os.environ["QKMLA_NUM_WG"] = str(n_wg)
+    try:
+        s = Session(dev, shape, inp, host_fill=False)  # contiguous, from qkmla_append
+        o_ref, lse_ref, out_ref = s.decode_multi(q_c, q_rope)
+        B, G, r, dr, H = len(lens), shape.n_groups, shape.latent_rank, shape.rope_dim, shape.n_heads
+        max_blocks = -(-s.L_cap // page_size)
+        num_pages = B * max_blocks + 3
+        table = scattered_table(B, max_blocks, num_pages, seed + 2)
+        if bad_seq is not None:
+            table[bad_seq, (lens[bad_seq] - 1) // page_size] = num_pages + 7
+        bt = dev.put(table, "block table")
+        pages = CPages(bt.ctypes.data, max_blocks, page_size, num_pages)
+        et = np.uint16 if s.bf else np.float32
+        rows = num_pages * page_size
+        lat = dev.empty((rows, r), et, "latent pool", fill=0)
+        rope = dev.empty((rows, dr), et, "rope pool", fill=0)
+        alpha = dev.empty((rows, G), np.float32, "alpha pool", fill=0)
+        status = dev.empty((1,), np.int32, "paged status", fill=0)
+        # each sequence's rows in one append at position 0, through its table row
+        for b, L in enumerate(lens):
+            c = dev.put(s.store(inp.latents[b][None]), f"paged new latents {b}")
+            k = dev.put(s.store(inp.k_rope_raw[b][None]), f"paged new rope keys {b}")
+            pos = dev.put(np.zeros(1, np.int32), f"paged positions {b}")
+            one = dev.put(table[b:b + 1], f"block table row {b}")
+            pg1 = CPages(one.ctypes.data, max_blocks, page_size, num_pages)
+            s.call("qkmla_append_paged", ctypes.byref(s.cfg), 1, L, P(c.ctypes.data),
+                   P(k.ctypes.data), P(s.w_uk.ctypes.data), P(s.gamma_k_rope.ctypes.data),
+                   P(pos.ctypes.data), ctypes.byref(pg1), P(lat.ctypes.data), P(rope.ctypes.data),
+                   P(alpha.ctypes.data), P(status.ctypes.data), None)
+        for b, L in enumerate(lens):
+            if b == bad_seq:
+                L = (L - 1) // page_size * page_size  # rows before the bad page
+            t = np.arange(L)
+            prow = table[b, t // page_size] * page_size + t % page_size
+            assert np.array_equal(lat[prow], s.lat[b, :L]), f"{label}: latent rows of {b}"
+            assert np.array_equal(rope[prow], s.rope[b, :L]), f"{label}: rope rows of {b}"
+            assert np.array_equal(alpha[prow], s.alpha[b, :L]), f"{label}: alpha rows of {b}"
+        qc = dev.put(s.store(q_c), "paged q_c")
+        qr = dev.put(s.store(q_rope), "paged q_rope")
+        o_lat = dev.empty((B, s_q, H, r), np.float32, "paged o_lat", fill=0xFF)
+        lse = dev.empty((B, s_q, H), np.float32, "paged lse", fill=0xFF)
+        ws = s.lib.qkmla_decode_workspace_size(ctypes.byref(s.cfg), B * s_q, s.max_len)
+        wsb = dev.empty((ws,), np.uint8, "paged workspace", fill=0xCD)
+        s.call("qkmla_decode_paged", ctypes.byref(s.cfg), B, s_q, P(qc.ctypes.data),
+               P(qr.ctypes.data), P(s.w_qabs.ctypes.data), P(s.gamma_q_rope.ctypes.data),
+               P(lat.ctypes.data), P(rope.ctypes.data), P(alpha.ctypes.data),
+               P(s.seq_lens.ctypes.data), ctypes.byref(pages), s.max_len, P(wsb.ctypes.data), ws,
+               P(o_lat.ctypes.data), P(lse.ctypes.data), P(status.ctypes.data), None)
+    finally:
+        os.environ.pop("QKMLA_NUM_WG", None)
+    hs = list(range(H)) if heads is None else [h for h in heads if h < H]
+    good = [b for b in range(B) if b != bad_seq]
+    same = all(np.array_equal(o_lat[b][:, hs], o_ref[b][:, hs]) and
+               np.array_equal(lse[b][:, hs], lse_ref[b][:, hs]) for b in good)
+    print(f"[{'ok' if same else 'FAIL'}] {label}: paged decode bitwise equal to contiguous",
+          flush=True)
+    assert same, label
+    st = int(status[0])
+    assert st == (4 if bad_seq is not None else 0), f"{label}: device status {st}"
+    tau = 1.0 / np.sqrt(shape.head_dim + shape.rope_dim)
+    ref = oracle.explicit_decode_multi(q_c, q_rope, inp.latents, inp.k_rope_raw, inp.w_uk,
+                                       inp.w_uv, inp.gamma_q, inp.gamma_k, inp.gamma_q_rope,
+                                       inp.gamma_k_rope, eps=1e-6, tau=tau, base=10000.0)
+    rows = [b * s_q + i for b in good for i in range(s_q)]
+    flat = lambda x: x.reshape((B * s_q,) + x.shape[2:])  # noqa: E731
+    compare(shape, flat(out_ref), flat(o_lat), flat(lse), {k: flat(v) for k, v in ref.items()},
+            rows, hs, label + " vs oracle")
+
+
+@case
+def paged_caches(dev):
+    """Paged latent, RoPE and alpha pools behind a block table: fp32 with
+    5-row pages and s_q = 2, bf16 with 32-row pages over split segments, each
+    also with one sequence whose table entry lies outside the pool."""
+    run_paged(dev, Shape(6, 3, 20, 12, 4, 10, "f32"), (9, 33, 17), 2, 5, 520,
+              "fp32 5-row pages, s_q=2, bad page in sequence 2", bad_seq=2)
+    run_paged(dev, DSV3, (70, 40, 2), 1, 32, 521, "bf16 32-row pages over 4 workgroups",
+              n_wg=4, heads=MERGE_HEADS)
+    run_paged(dev, DSV3, (70, 40, 2), 1, 32, 522, "bf16 32-row pages, bad page in sequence 0",
+              n_wg=3, heads=MERGE_HEADS, bad_seq=0)
 
 
 @case

@@ -163,9 +163,10 @@ SIGNATURES = {
     "qkmla_decode_workspace_size": (_SZ, [_C, _I32, _I32]),
     "qkmla_decode": (_I32, [_C, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _SZ, _P, _P,
                             _P, _P]),
-    "qkmla_decode_noalloc": (_I32, [_C, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P,
-                                    _P, _P]),
     "qkmla_decode_multi": (_I32, [_C, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P,
+                                  _SZ, _P, _P, _P, _P]),
+    "qkmla_append_paged": (_I32, [_C, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "qkmla_decode_paged": (_I32, [_C, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
                                   _SZ, _P, _P, _P, _P]),
     "qkmla_out_proj": (_I32, [_C, _I32, _P, _P, _P, _P]),
     "qkmla_last_error": (ctypes.c_char_p, []),
@@ -267,22 +268,17 @@ class Session:
                                f"{self.dev.error}")
         return r
 
-    def decode(self, noalloc: bool = False):
+    def decode(self):
         P = _P
-        common = [ctypes.byref(self.cfg), self.B, P(self.q_c.ctypes.data),
+        ws = self.lib.qkmla_decode_workspace_size(ctypes.byref(self.cfg), self.B, self.max_len)
+        self.ws = self.dev.empty((ws,), np.uint8, "workspace", fill=0xCD)
+        self.call("qkmla_decode", ctypes.byref(self.cfg), self.B, P(self.q_c.ctypes.data),
                   P(self.q_rope.ctypes.data), P(self.w_qabs.ctypes.data),
                   P(self.gamma_q_rope.ctypes.data), P(self.lat.ctypes.data),
                   P(self.rope.ctypes.data), P(self.alpha.ctypes.data),
-                  P(self.seq_lens.ctypes.data), self.L_cap, self.max_len]
-        if noalloc:
-            self.call("qkmla_decode_noalloc", *common, P(self.o_lat.ctypes.data),
-                      P(self.lse.ctypes.data), P(self.status.ctypes.data), None)
-        else:
-            ws = self.lib.qkmla_decode_workspace_size(ctypes.byref(self.cfg), self.B, self.max_len)
-            self.ws = self.dev.empty((ws,), np.uint8, "workspace", fill=0xCD)
-            self.call("qkmla_decode", *common, P(self.ws.ctypes.data), ws,
-                      P(self.o_lat.ctypes.data), P(self.lse.ctypes.data),
-                      P(self.status.ctypes.data), None)
+                  P(self.seq_lens.ctypes.data), self.L_cap, self.max_len, P(self.ws.ctypes.data),
+                  ws, P(self.o_lat.ctypes.data), P(self.lse.ctypes.data),
+                  P(self.status.ctypes.data), None)
         return self.o_lat.copy(), self.lse.copy()
 
     def decode_multi(self, q_c, q_rope):

@@ -37,7 +37,7 @@ def _ops():
 
 def test_abi_version_and_status_strings():
     ops = _ops()
-    assert ops.abi_version() == 2
+    assert ops.abi_version() == 3
     assert ops._lib.qkmla_status_string(0) == b"ok"
     assert ops._lib.qkmla_status_string(3) == b"workspace too small"
 
@@ -128,3 +128,61 @@ def test_decode_multi_validates_query_rows():
     st = lib.qkmla_decode_multi(ctypes.byref(cfg.c()), 0, 3, None, None, None, None, None, None,
                                 None, None, 16, 16, None, 0, None, None, None, None)
     assert st == 0
+
+
+def _pages(ops, bt=0x2000, max_blocks=4, page_size=64, num_pages=8):
+    return ops._Pages(ctypes.c_void_p(bt) if bt else None, max_blocks, page_size, num_pages)
+
+
+def test_paged_entry_points_validate_the_page_description():
+    """Bad page descriptions are rejected on the host before any pointer is
+    used: a missing table or non-positive sizes are invalid arguments, a
+    capacity above int32 too, a bf16 page that does not hold whole 32-row
+    tiles is unsupported, and max_seq_len above max_blocks * page_size is
+    invalid."""
+    ops = _ops()
+    cfg = _cfg()
+    lib = ops._lib
+    p = ctypes.c_void_p(0x1000)
+
+    def decode(pages, max_seq_len=64):
+        return lib.qkmla_decode_paged(ctypes.byref(cfg.c()), 1, 1, p, p, p, p, p, p, p, p,
+                                      ctypes.byref(pages) if pages is not None else None,
+                                      max_seq_len, p, 1 << 20, p, None, None, None)
+
+    assert decode(None) == 1
+    assert decode(_pages(ops, bt=0)) == 1 and b"block table" in lib.qkmla_last_error()
+    assert decode(_pages(ops, page_size=0)) == 1
+    assert decode(_pages(ops, num_pages=0)) == 1
+    assert decode(_pages(ops, max_blocks=1 << 16, page_size=1 << 16)) == 1
+    assert decode(_pages(ops, bt=0x2002)) == 1 and b"aligned" in lib.qkmla_last_error()
+    assert decode(_pages(ops, page_size=48)) == 2 and b"multiple of 32" in lib.qkmla_last_error()
+    assert decode(_pages(ops), max_seq_len=257) == 1  # capacity 4 * 64 = 256
+    st = lib.qkmla_decode_paged(ctypes.byref(cfg.c()), 0, 1, None, None, None, None, None, None,
+                                None, None, None, 16, None, 0, None, None, None, None)
+    assert st == 0  # batch 0: no-op, nothing read
+
+    def append(pages):
+        return lib.qkmla_append_paged(ctypes.byref(cfg.c()), 1, 1, p, p, p, p, p,
+                                      ctypes.byref(pages) if pages is not None else None,
+                                      p, p, p, None, None)
+
+    assert append(None) == 1
+    assert append(_pages(ops, page_size=-1)) == 1
+    st = lib.qkmla_append_paged(ctypes.byref(cfg.c()), 0, 1, None, None, None, None, None, None,
+                                None, None, None, None, None)
+    assert st == 0
+
+
+def test_f32_pages_of_any_size_pass_host_validation():
+    """The float path reads rows one by one, so any page size passes the host
+    checks (the call then fails only for want of a device)."""
+    ops = _ops()
+    cfg = _cfg(n_heads=4, n_groups=2, latent_rank=32, head_dim=16, rope_dim=8, v_head_dim=16,
+               dtype="f32")
+    lib = ops._lib
+    p = ctypes.c_void_p(0x1000)
+    pages = _pages(ops, page_size=3)
+    st = lib.qkmla_decode_paged(ctypes.byref(cfg.c()), 1, 1, p, p, p, p, p, p, p, p,
+                                ctypes.byref(pages), 12, p, 0, p, None, None, None)
+    assert st in (3, 4)  # workspace too small, or no device to plan for

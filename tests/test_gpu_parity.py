@@ -266,3 +266,127 @@ def test_full_size_workloads_sampled(cid, samples):
         check_outputs(o, o_lat, lse, ref, cfg.dtype, [b], heads_of([g], cfg.n_heads, cfg.n_groups),
                       f"workload {cid} b={b} g={g}")
     check_caches(sess, inp, cfg, sorted({b for b, _ in samples}), max_rows=2048)
+
+
+# --- paged caches: a block table over shared pools ---------------------------------------
+
+def _paged_pools(cfg, inp, page_size, seed, max_blocks=None, chunk=65536):
+    """Pools of scattered pages filled through qkmla_append_paged, one append
+    per sequence and chunk; returns (block table, latent, rope, alpha pools)."""
+    B, dt = len(inp.lengths), cfg.torch_dtype
+    max_blocks = max_blocks or -(-max(inp.lengths) // page_size)
+    num_pages = B * max_blocks + 5
+    perm = np.random.default_rng(seed).permutation(num_pages)[:B * max_blocks]
+    table = torch.from_numpy(perm.reshape(B, max_blocks).astype(np.int32)).cuda()
+    rows = (num_pages, page_size)
+    lat = torch.zeros(rows + (cfg.latent_rank,), dtype=dt, device="cuda")
+    rope = torch.zeros(rows + (cfg.rope_dim,), dtype=dt, device="cuda")
+    alpha = torch.zeros(rows + (cfg.n_groups,), dtype=torch.float32, device="cuda")
+    status = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    w_uk = torch.from_numpy(inp.w_uk).cuda()
+    gkr = torch.from_numpy(inp.gamma_k_rope).cuda()
+    for b, L in enumerate(inp.lengths):
+        for s in range(0, L, chunk):
+            e = min(L, s + chunk)
+            c = torch.from_numpy(np.ascontiguousarray(inp.latents[b][s:e][None])).to("cuda", dt)
+            k = torch.from_numpy(np.ascontiguousarray(inp.k_rope_raw[b][s:e][None])).to("cuda", dt)
+            pos = torch.full((1,), s, dtype=torch.int32, device="cuda")
+            ops.append_paged(cfg, c, k, w_uk, gkr, pos, table[b:b + 1], lat, rope, alpha, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    return table, lat, rope, alpha
+
+
+def _pool_rows(pool, table, b, L, page_size):
+    t = torch.arange(L, device="cuda")
+    prow = table[b, t // page_size].long() * page_size + t % page_size
+    return pool.view(-1, pool.shape[-1])[prow]
+
+
+@pytest.mark.parametrize("shape_name,lens,page_size", [
+    ("tiny", (64, 5, 37), 5), ("dsv3", (1000, 333, 64, 1), 32), ("dsv3", (700, 90), 64)])
+def test_paged_caches_equal_contiguous_bitwise(shape_name, lens, page_size):
+    """qkmla_append_paged places exactly the rows qkmla_append writes, and
+    qkmla_decode_paged returns the contiguous decode's outputs bit for bit
+    (the same tiles and plan read through the block table); the contiguous
+    outputs are checked against the oracle."""
+    shape = TINY if shape_name == "tiny" else DSV3
+    inp = make_inputs(shape, lens, seed=450 + page_size)
+    cfg = ops.Config.from_shape(shape)
+    sess, o, o_lat, lse = _run(cfg, inp, f"paged {shape_name} page_size={page_size}")
+    check_outputs(o, o_lat, lse, oracle_decode(inp, cfg), cfg.dtype, range(len(lens)),
+                  list(range(cfg.n_heads)), "contiguous decode")
+    table, plat, prope, palpha = _paged_pools(cfg, inp, page_size, seed=451)
+    for b, L in enumerate(lens):
+        assert torch.equal(_pool_rows(plat, table, b, L, page_size), sess.lat[b, :L])
+        assert torch.equal(_pool_rows(prope, table, b, L, page_size), sess.rope[b, :L])
+        assert torch.equal(_pool_rows(palpha, table, b, L, page_size), sess.alpha[b, :L])
+    B, H = len(lens), cfg.n_heads
+    p_lse = torch.empty((B, 1, H), dtype=torch.float32, device="cuda")
+    status = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    p_lat = ops.decode_paged(cfg, sess.q_c.view(B, 1, H, -1), sess.q_rope.view(B, 1, H, -1),
+                             sess.w_qabs, sess.gamma_q_rope, plat, prope, palpha, sess.seq_lens,
+                             table, max(lens), sess.workspace, lse=p_lse, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(p_lat.view(B, H, -1).cpu().numpy(), o_lat)
+    assert np.array_equal(p_lse.view(B, H).cpu().numpy(), lse)
+
+
+def test_paged_multi_query_and_bad_page():
+    """s_q = 3 over 32-row pages equals the contiguous multi-row decode bit for
+    bit; a table entry outside the pool sets QKMLA_DEV_BAD_PAGE and leaves the
+    other sequences' outputs unchanged."""
+    lens, s_q, ps = (300, 70, 2), 3, 32
+    inp = make_inputs(DSV3, lens, seed=460)
+    cfg = ops.Config.from_shape(DSV3)
+    sess = DecodeSession(cfg, inp)
+    q_c, q_rope = multi_query_rows(DSV3, len(lens), s_q, seed=461)
+    qc = torch.from_numpy(q_c).to("cuda", cfg.torch_dtype)
+    qr = torch.from_numpy(q_rope).to("cuda", cfg.torch_dtype)
+    B, H = len(lens), cfg.n_heads
+    ws = torch.empty((ops.decode_workspace_size(cfg, B * s_q, max(lens)),), dtype=torch.uint8,
+                     device="cuda")
+    lse_c = torch.empty((B, s_q, H), dtype=torch.float32, device="cuda")
+    o_c = ops.decode_multi(cfg, qc, qr, sess.w_qabs, sess.gamma_q_rope, sess.lat, sess.rope,
+                           sess.alpha, sess.seq_lens, max(lens), ws, lse=lse_c, status=sess.status)
+    table, plat, prope, palpha = _paged_pools(cfg, inp, ps, seed=462)
+    lse_p = torch.empty_like(lse_c)
+    status = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    o_p = ops.decode_paged(cfg, qc, qr, sess.w_qabs, sess.gamma_q_rope, plat, prope, palpha,
+                           sess.seq_lens, table, max(lens), ws, lse=lse_p, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & ops.QKMLA_DEV_BAD_SEQ_LEN  # sequence 2 is shorter than s_q
+    assert torch.equal(o_p, o_c) and torch.equal(lse_p, lse_c)
+    bad = table.clone()
+    bad[1, (lens[1] - 1) // ps] = plat.shape[0] + 3  # outside the pool
+    status.zero_()
+    o_b = ops.decode_paged(cfg, qc, qr, sess.w_qabs, sess.gamma_q_rope, plat, prope, palpha,
+                           sess.seq_lens, bad, max(lens), ws, lse=lse_p, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & ops.QKMLA_DEV_BAD_PAGE
+    assert torch.equal(o_b[0], o_c[0]) and torch.equal(o_b[2], o_c[2])
+
+
+def test_paged_full_size_long_context():
+    """Four 16384-token sequences in 64-row pages of one pool: bit-equal to the
+    contiguous decode, and sampled groups against the oracle."""
+    lens = (16384, 16384, 9000, 16384)
+    inp = make_inputs(DSV3, lens, seed=470)
+    cfg = ops.Config.from_shape(DSV3)
+    sess, o, o_lat, lse = _run(cfg, inp, "paged long context, contiguous side")
+    for b, g in ((0, 0), (2, 5)):
+        ref = oracle_decode(inp, cfg, batch_ids=[b], groups=[g])
+        check_outputs(o, o_lat, lse, ref, cfg.dtype, [b], heads_of([g], cfg.n_heads, cfg.n_groups),
+                      f"long context b={b} g={g}")
+    table, plat, prope, palpha = _paged_pools(cfg, inp, 64, seed=471)
+    B, H = len(lens), cfg.n_heads
+    status = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    p_lse = torch.empty((B, 1, H), dtype=torch.float32, device="cuda")
+    p_lat = ops.decode_paged(cfg, sess.q_c.view(B, 1, H, -1), sess.q_rope.view(B, 1, H, -1),
+                             sess.w_qabs, sess.gamma_q_rope, plat, prope, palpha, sess.seq_lens,
+                             table, max(lens), sess.workspace, lse=p_lse, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(p_lat.view(B, H, -1).cpu().numpy(), o_lat)
+    assert np.array_equal(p_lse.view(B, H).cpu().numpy(), lse)

@@ -185,3 +185,29 @@ def device_cache_fill_source(shape: Shape, lengths, seed: int, device, row_scale
                 e = min(L, s + chunk)
                 c, k = draw(1, e - s)
                 yield b, s, c, k
+
+
+def train_inputs(shape: Shape, batch: int, seq_len: int, seed: int) -> dict:
+    """Inputs of one training / prefill step over ``batch`` sequences of
+    ``seq_len`` tokens, as a dict of float32 arrays (storage-rounded where the
+    layer stores them in its dtype): c [B][T][r], q_c [B][T][H][d_c],
+    q_rope [B][T][H][d_r], k_rope [B][T][d_r] (raw), w_uk [G][r][d_c] (fp32),
+    w_uv [G][r][d_v], the four RMSNorm weights, and the upstream gradient
+    d_o [B][T][H][d_v] (fp32).  Same distributions as make_inputs (d_o ~ N(0,1)),
+    drawn in that order from default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    s = shape
+    G, r, dc, dr, dv, H = s.n_groups, s.latent_rank, s.head_dim, s.rope_dim, s.v_head_dim, s.n_heads
+    B, T = batch, seq_len
+    out = {}
+    out["w_uk"] = rng.standard_normal((G, r, dc), dtype=np.float32) * np.float32(1.0 / np.sqrt(r))
+    out["w_uv"] = _store(rng.standard_normal((G, r, dv), dtype=np.float32) *
+                         np.float32(1.0 / np.sqrt(r)), s.dtype)
+    for n, d in (("gamma_q", dc), ("gamma_k", dc), ("gamma_q_rope", dr), ("gamma_k_rope", dr)):
+        out[n] = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    out["c"] = _store(rng.standard_normal((B, T, r), dtype=np.float32), s.dtype)
+    out["k_rope"] = _store(rng.standard_normal((B, T, dr), dtype=np.float32), s.dtype)
+    out["q_c"] = _store(rng.standard_normal((B, T, H, dc), dtype=np.float32), s.dtype)
+    out["q_rope"] = _store(rng.standard_normal((B, T, H, dr), dtype=np.float32), s.dtype)
+    out["d_o"] = rng.standard_normal((B, T, H, dv), dtype=np.float32)
+    return out

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define QKMLA_ABI_VERSION 3
+#define QKMLA_ABI_VERSION 4
 
 typedef enum {
   QKMLA_OK = 0,
@@ -250,6 +250,63 @@ int qkmla_decode_paged(const qkmla_config* cfg, int32_t batch, int32_t s_q, cons
  */
 int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, const void* w_uv,
                    float* out, void* stream);
+
+/*
+ * Training and prefill in the explicit form (the form the pages train with:
+ * technical summary, Results; Methodology: RMSNorm decomposition, Blockwise
+ * Normalization).  `batch` sequences of `seq_len` tokens each; token i of a
+ * sequence sits at position i and attends tokens 0..i of its own sequence.
+ * Per token i, head h, g = g(h):
+ *   k_{j,g} = c_j W^UK_g (materialised),  k^ = k * gamma_k / S(k),
+ *   q^ = q_c * gamma_q / S(q_c),
+ *   q^R, k^R: RMS-normalised with gamma_q_rope / gamma_k_rope, rotated by
+ *             their own position (one RoPE key per token, shared by all heads),
+ *   logit_ij = tau (q^_i . k^_j + q^R_i . k^R_j),  j <= i,
+ *   o[b][i][h] = sum_j softmax_j(logit) c_j W^UV_g,  lse = log sum_j exp(logit).
+ * (Plain MLA if !qk_norm: no norms, gammas unused, their gradients zero.)
+ * Shapes: any layer with d_c, d_v <= 256, r <= 1024, d_r <= 256, either
+ * dtype; the bf16 decode restrictions do not apply here.
+ * The workspace is scratch for one call; the backward recomputes what it
+ * needs from the inputs, so no state passes between the two calls except
+ * o and lse.
+ */
+typedef struct {
+  const void* c;       /* device dtype [B][T][r]       latents */
+  const void* q_c;     /* device dtype [B][T][H][d_c]  content queries (projected, before norm) */
+  const void* q_rope;  /* device dtype [B][T][H][d_r]  RoPE queries (before norm and RoPE) */
+  const void* k_rope;  /* device dtype [B][T][d_r]     RoPE keys (before norm and RoPE) */
+  const float* w_uk;   /* device float [G][r][d_c] */
+  const void* w_uv;    /* device dtype [G][r][d_v] */
+  const float* gamma_q;      /* device float [d_c] (unused if !qk_norm) */
+  const float* gamma_k;      /* device float [d_c] */
+  const float* gamma_q_rope; /* device float [d_r] */
+  const float* gamma_k_rope; /* device float [d_r] */
+} qkmla_train_inputs;
+
+/* Gradients of sum(o * d_o) with respect to every input: device float
+ * arrays, each of its input's shape, all required.  Every element is
+ * written (no accumulation into existing values). */
+typedef struct {
+  float *d_c, *d_q_c, *d_q_rope, *d_k_rope, *d_w_uk, *d_w_uv;
+  float *d_gamma_q, *d_gamma_k, *d_gamma_q_rope, *d_gamma_k_rope;
+} qkmla_train_grads;
+
+/* Workspace bytes for qkmla_train_backward (enough for the forward too);
+ * 0 on invalid arguments. */
+size_t qkmla_train_workspace_size(const qkmla_config* cfg, int32_t batch, int32_t seq_len);
+
+/* Forward: o device float [B][T][H][d_v], lse device float [B][T][H]
+ * (natural log; the backward needs it). */
+int qkmla_train_forward(const qkmla_config* cfg, int32_t batch, int32_t seq_len,
+                        const qkmla_train_inputs* inputs, void* workspace, size_t workspace_bytes,
+                        float* o, float* lse, void* stream);
+
+/* Backward of sum(o * d_o): o and lse as the forward wrote them, d_o device
+ * float [B][T][H][d_v]. */
+int qkmla_train_backward(const qkmla_config* cfg, int32_t batch, int32_t seq_len,
+                         const qkmla_train_inputs* inputs, const float* o, const float* lse,
+                         const float* d_o, void* workspace, size_t workspace_bytes,
+                         const qkmla_train_grads* grads, void* stream);
 
 /*
  * Host-only split planner (no device access; usable without a GPU).  For a

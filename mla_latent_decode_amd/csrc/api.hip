@@ -38,7 +38,9 @@ bool aligned16(const void* p) { return aligned(p, 16); }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Validate the config and fill the normalised form.
-int check_cfg(const qkmla_config* cfg, Cfg* out) {
+// decode_shapes: apply the bf16 decode kernels' shape restrictions (the
+// training kernels take any shape within their own limits).
+int check_cfg(const qkmla_config* cfg, Cfg* out, bool decode_shapes = true) {
   if (!cfg) return fail(QKMLA_ERR_INVALID_ARG, "cfg is NULL");
   const qkmla_config& c = *cfg;
   if (c.n_heads <= 0 || c.n_groups <= 0 || c.latent_rank <= 0 || c.head_dim <= 0 ||
@@ -57,7 +59,7 @@ int check_cfg(const qkmla_config* cfg, Cfg* out) {
   if (!std::isfinite(c.softmax_scale)) return fail(QKMLA_ERR_INVALID_ARG, "softmax_scale not finite");
   if (c.latent_rank > 1024 || c.head_dim > 1024 || c.v_head_dim > 1024 || c.rope_dim > 256)
     return fail(QKMLA_ERR_UNSUPPORTED, "dimension above the compiled limits (r, d_c, d_v <= 1024, d_r <= 256)");
-  if (c.dtype == QKMLA_BF16) {
+  if (c.dtype == QKMLA_BF16 && decode_shapes) {
     const int hpg = c.n_heads / c.n_groups;
     // H = 32 (one wavefront per workgroup) is switched off: that instantiation
     // faulted on the GPU with the asm tile loads and its cause is not yet found.
@@ -483,6 +485,92 @@ int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const 
   return qkmla_decode_multi(cfg, batch, 1, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache,
                             rope_cache, alpha_cache, seq_lens, cache_capacity, max_seq_len,
                             workspace, workspace_bytes, o_lat, lse, status, stream);
+}
+
+// ---- training / prefill -------------------------------------------------------------
+static int check_train(const qkmla_config* cfg, int32_t batch, int32_t seq_len, Cfg* c) {
+  int st = check_cfg(cfg, c, false);
+  if (st) return st;
+  if (batch < 0 || seq_len < 1)
+    return fail(QKMLA_ERR_INVALID_ARG, "train: need batch >= 0 and seq_len >= 1");
+  if (c->dc > 256 || c->dv > 256)
+    return fail(QKMLA_ERR_UNSUPPORTED, "train: d_c and d_v must be <= 256 (got %d, %d)", c->dc,
+                c->dv);
+  if ((int64_t)batch * seq_len * c->H > INT32_MAX / 2)
+    return fail(QKMLA_ERR_UNSUPPORTED, "train: batch * seq_len * n_heads too large");
+  return QKMLA_OK;
+}
+
+static int check_train_inputs(const Cfg& c, const qkmla_train_inputs* in, TrainPtrs* p) {
+  if (!in) return fail(QKMLA_ERR_INVALID_ARG, "train: NULL inputs");
+  if (!in->c || !in->q_c || !in->q_rope || !in->k_rope || !in->w_uk || !in->w_uv ||
+      (c.qk_norm && (!in->gamma_q || !in->gamma_k || !in->gamma_q_rope || !in->gamma_k_rope)))
+    return fail(QKMLA_ERR_INVALID_ARG, "train: NULL input pointer");
+  const size_t es = elem_size(c);
+  if (!aligned(in->c, es) || !aligned(in->q_c, es) || !aligned(in->q_rope, es) ||
+      !aligned(in->k_rope, es) || !aligned(in->w_uv, es) || !aligned(in->w_uk, 4))
+    return fail(QKMLA_ERR_INVALID_ARG, "train: inputs must be aligned to their element size");
+  *p = TrainPtrs{in->c, in->q_c, in->q_rope, in->k_rope, in->w_uk, in->w_uv,
+                 in->gamma_q, in->gamma_k, in->gamma_q_rope, in->gamma_k_rope};
+  return QKMLA_OK;
+}
+
+size_t qkmla_train_workspace_size(const qkmla_config* cfg, int32_t batch, int32_t seq_len) {
+  Cfg c;
+  if (check_train(cfg, batch, seq_len, &c)) return 0;
+  if (batch == 0) return 256;
+  return train_ws_layout(c, batch, seq_len).total;
+}
+
+int qkmla_train_forward(const qkmla_config* cfg, int32_t batch, int32_t seq_len,
+                        const qkmla_train_inputs* inputs, void* workspace, size_t workspace_bytes,
+                        float* o, float* lse, void* stream) {
+  Cfg c;
+  int st = check_train(cfg, batch, seq_len, &c);
+  if (st) return st;
+  if (batch == 0) return ok();
+  TrainPtrs in;
+  if ((st = check_train_inputs(c, inputs, &in))) return st;
+  if (!workspace || !o || !lse) return fail(QKMLA_ERR_INVALID_ARG, "train: NULL pointer");
+  if (!aligned16(workspace) || !aligned(o, 4) || !aligned(lse, 4))
+    return fail(QKMLA_ERR_INVALID_ARG, "train: misaligned workspace or output");
+  const TrainWs ws = train_ws_layout(c, batch, seq_len);
+  if (workspace_bytes < ws.fwd_total)
+    return fail(QKMLA_ERR_WORKSPACE, "train forward: workspace %zu bytes, need %zu",
+                workspace_bytes, ws.fwd_total);
+  return hip_status(launch_train_forward(c, batch, seq_len, in, ws, workspace, o, lse,
+                                         as_stream(stream)),
+                    "train forward");
+}
+
+int qkmla_train_backward(const qkmla_config* cfg, int32_t batch, int32_t seq_len,
+                         const qkmla_train_inputs* inputs, const float* o, const float* lse,
+                         const float* d_o, void* workspace, size_t workspace_bytes,
+                         const qkmla_train_grads* grads, void* stream) {
+  Cfg c;
+  int st = check_train(cfg, batch, seq_len, &c);
+  if (st) return st;
+  if (batch == 0) return ok();
+  TrainPtrs in;
+  if ((st = check_train_inputs(c, inputs, &in))) return st;
+  if (!o || !lse || !d_o || !workspace || !grads)
+    return fail(QKMLA_ERR_INVALID_ARG, "train: NULL pointer");
+  const qkmla_train_grads& g = *grads;
+  float* outs[] = {g.d_c, g.d_q_c, g.d_q_rope, g.d_k_rope, g.d_w_uk, g.d_w_uv,
+                   g.d_gamma_q, g.d_gamma_k, g.d_gamma_q_rope, g.d_gamma_k_rope};
+  for (float* p : outs)
+    if (!p || !aligned(p, 4)) return fail(QKMLA_ERR_INVALID_ARG, "train: NULL or misaligned gradient");
+  if (!aligned16(workspace) || !aligned(o, 4) || !aligned(lse, 4) || !aligned(d_o, 4))
+    return fail(QKMLA_ERR_INVALID_ARG, "train: misaligned workspace, o, lse or d_o");
+  const TrainWs ws = train_ws_layout(c, batch, seq_len);
+  if (workspace_bytes < ws.total)
+    return fail(QKMLA_ERR_WORKSPACE, "train backward: workspace %zu bytes, need %zu",
+                workspace_bytes, ws.total);
+  const TrainGrads gr{g.d_c, g.d_q_c, g.d_q_rope, g.d_k_rope, g.d_w_uk, g.d_w_uv,
+                      g.d_gamma_q, g.d_gamma_k, g.d_gamma_q_rope, g.d_gamma_k_rope};
+  return hip_status(launch_train_backward(c, batch, seq_len, in, o, lse, d_o, ws, workspace, gr,
+                                          as_stream(stream)),
+                    "train backward");
 }
 
 int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, const void* w_uv,

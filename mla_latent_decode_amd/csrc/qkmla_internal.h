@@ -75,6 +75,30 @@ struct Paging {
 };
 inline Paging contiguous_paging(int batch, int L_cap) { return Paging{nullptr, 1, L_cap, batch}; }
 
+// ---- training / prefill (explicit form) ---------------------------------------
+struct TrainPtrs {  // layer inputs (dtype = storage type unless noted)
+  const void* c;       // [B][T][r]
+  const void* q_c;     // [B][T][H][d_c]
+  const void* q_rope;  // [B][T][H][d_r]
+  const void* k_rope;  // [B][T][d_r]
+  const float* w_uk;   // [G][r][d_c] fp32
+  const void* w_uv;    // [G][r][d_v]
+  const float *gamma_q, *gamma_k, *gamma_q_rope, *gamma_k_rope;  // fp32
+};
+struct TrainGrads {  // fp32 gradients, same shapes as the inputs
+  float *d_c, *d_q_c, *d_q_rope, *d_k_rope, *d_w_uk, *d_w_uv;
+  float *d_gamma_q, *d_gamma_k, *d_gamma_q_rope, *d_gamma_k_rope;
+};
+// Byte offsets of the fp32 training intermediates (d_qk = d_c + d_r):
+//   Qh [BT][H][d_qk], Kh [BT][G][d_qk], V [BT][G][d_v], Kraw [BT][G][d_c],
+//   aq, aqr [BT][H], ak [BT][G], akr [BT]  (the forward needs these: fwd_total)
+//   dQh, dKh, dV, Dsum [BT][H], dK [BT][G][d_c], dKr [BT][d_r], gamma partials.
+struct TrainWs {
+  size_t Qh, Kh, V, Kraw, aq, aqr, ak, akr, fwd_total;
+  size_t dQh, dKh, dV, Dsum, dK, dKr, gamma_partial, total;
+};
+TrainWs train_ws_layout(const Cfg& c, int B, int T);
+
 // ---- launchers (each enqueues on `stream`; returns the launch error) -------
 hipError_t launch_absorb(const Cfg& c, const float* w_uk, const float* gq, const float* gk,
                          void* w_qabs, hipStream_t s);
@@ -99,6 +123,12 @@ hipError_t launch_decode_generic(const Cfg& c, int batch, int s_q, const int32_t
                                  const Paging& pg, const void* lat, const void* rope,
                                  const float* alpha, const WsLayout& ws, void* workspace,
                                  float* o_lat, float* lse, hipStream_t s);
+hipError_t launch_train_forward(const Cfg& c, int B, int T, const TrainPtrs& in,
+                                const TrainWs& ws, void* workspace, float* o, float* lse,
+                                hipStream_t s);
+hipError_t launch_train_backward(const Cfg& c, int B, int T, const TrainPtrs& in, const float* o,
+                                 const float* lse, const float* d_o, const TrainWs& ws,
+                                 void* workspace, const TrainGrads& gr, hipStream_t s);
 hipError_t launch_out_proj(const Cfg& c, int batch, const float* o_lat, const void* w_uv,
                            float* out, hipStream_t s);
 

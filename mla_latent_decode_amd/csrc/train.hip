@@ -1,0 +1,797 @@
+// Training / prefill of QK-Normed MLA in the explicit form: causal attention
+// over whole sequences with materialised, RMS-normalised keys, forward and
+// backward ("QK-Normed MLA: QK normalization without full key caching",
+// technical summary, Methodology: RMSNorm decomposition and Blockwise
+// Normalization; Results: the models are trained in this form).
+//
+// Row-parallel kernels for any layer shape and either storage type.  Every
+// intermediate is fp32 in the workspace; every gradient is fp32.
+//
+// Forward, per sequence b, token i, head h in group g (positions are token
+// indices):
+//   K^_{j,g} = [RMSNorm_{gk}(c_j W^UK_g) | RoPE_j(RMSNorm_{gkr}(k^R_j))]
+//   Q^_{i,h} = [RMSNorm_{gq}(q^C_{i,h})  | RoPE_i(RMSNorm_{gqr}(q^R_{i,h}))]
+//   V_{j,g}  = c_j W^UV_g
+//   s_{ij} = tau Q^_{i,h} . K^_{j,g} (j <= i),  o_{i,h} = sum_j softmax_j(s) V_{j,g}
+// Backward (loss gradient d_o): D_i = d_o_i . o_i, p_ij = exp(s_ij - lse_i),
+//   ds_ij = p_ij (d_o_i . V_j - D_i);  dQ^_i = tau sum_j ds_ij K^_j;
+//   dK^_j = tau sum_{i,h in g} ds_ij Q^_i;  dV_j = sum_{i,h in g} p_ij d_o_i;
+// then back through RoPE (the transposed rotation), the RMSNorms
+// (y = gamma x a with a = 1/S(x):  dx = a gamma dy - x a^3 (sum gamma dy x)/n,
+// dgamma = sum dy x a) and the up-projections.
+#include "device_common.h"
+#include "qkmla_internal.h"
+
+namespace qkmla {
+
+namespace {
+
+constexpr int kChunk = 256;   // keys (queries) per chunk of the attention kernels
+constexpr int kKvTok = 8;     // tokens per workgroup of the key/value projection
+constexpr int kLatTok = 4;    // tokens per workgroup of the latent gradient
+constexpr int kWgRows = 16;   // latent rows per workgroup of the weight gradients
+constexpr int kWgTok = 32;    // tokens per LDS chunk of the weight gradients
+constexpr int kGammaSplit = 64;
+
+struct TrainDims {
+  int B, T, H, G, r, dc, dr, dv, dqk, hpg;
+  int qk_norm;
+  float eps, tau, base;
+};
+
+TrainDims dims_of(const Cfg& c, int B, int T) {
+  return TrainDims{B, T, c.H, c.G, c.r, c.dc, c.dr, c.dv, c.dc + c.dr, c.hpg, c.qk_norm,
+                   c.eps, c.tau, c.base};
+}
+
+// Sum over the block (blockDim.x = 256); `red` holds 4 floats.  Every thread
+// gets the total.
+__device__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// ---- forward: normalised, rotated queries ----------------------------------
+// One wavefront per (token row, head).  Qh[row][h] = [q^ content | q^R], and
+// the inverse RMS values for the backward.
+template <typename T>
+__global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __restrict__ q_c,
+                                                     const T* __restrict__ q_rope,
+                                                     const float* __restrict__ gq,
+                                                     const float* __restrict__ gqr,
+                                                     float* __restrict__ Qh, float* __restrict__ aq,
+                                                     float* __restrict__ aqr) {
+  const size_t row = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (h >= d.H) return;
+  const int pos = (int)(row % d.T);
+  const size_t qh = row * d.H + h;
+  const T* qc = q_c + qh * d.dc;
+  const T* qr = q_rope + qh * d.dr;
+  float* out = Qh + qh * d.dqk;
+  float a = 1.f, ar = 1.f;
+  if (d.qk_norm) {
+    float ss = 0.f, sr = 0.f;
+    for (int e = lane; e < d.dc; e += 64) {
+      const float v = Elem<T>::load(qc, e);
+      ss += v * v;
+    }
+    for (int e = lane; e < d.dr; e += 64) {
+      const float v = Elem<T>::load(qr, e);
+      sr += v * v;
+    }
+    a = 1.0f / sqrtf(wave_sum(ss) / (float)d.dc + d.eps);
+    ar = 1.0f / sqrtf(wave_sum(sr) / (float)d.dr + d.eps);
+    if (lane == 0) {
+      aq[qh] = a;
+      aqr[qh] = ar;
+    }
+  }
+  for (int e = lane; e < d.dc; e += 64)
+    out[e] = Elem<T>::load(qc, e) * (d.qk_norm ? gq[e] * a : 1.f);
+  for (int i = lane; i < d.dr / 2; i += 64) {
+    float x0 = Elem<T>::load(qr, 2 * i), x1 = Elem<T>::load(qr, 2 * i + 1);
+    if (d.qk_norm) {
+      x0 *= gqr[2 * i] * ar;
+      x1 *= gqr[2 * i + 1] * ar;
+    }
+    float cs, sn;
+    rope_cos_sin(pos, i, d.dr, d.base, &cs, &sn);
+    out[d.dc + 2 * i] = x0 * cs - x1 * sn;
+    out[d.dc + 2 * i + 1] = x0 * sn + x1 * cs;
+  }
+}
+
+// ---- forward: keys and values -----------------------------------------------
+// Workgroup = kKvTok token rows x one group g.  Thread e owns output dim e of
+// k = c W^UK_g and v = c W^UV_g for the workgroup's tokens.  Writes the raw
+// key (for the backward), the normalised key with the normalised, rotated
+// RoPE key after it, the value, and the inverse RMS values.
+template <typename T>
+__global__ __launch_bounds__(256) void prep_kv_kernel(
+    TrainDims d, int n_rows, const T* __restrict__ c, const T* __restrict__ k_rope,
+    const float* __restrict__ w_uk, const T* __restrict__ w_uv, const float* __restrict__ gk,
+    const float* __restrict__ gkr, float* __restrict__ Kh, float* __restrict__ Kraw,
+    float* __restrict__ V, float* __restrict__ ak, float* __restrict__ akr) {
+  extern __shared__ float lds[];  // c rows [kKvTok][r], then kKvTok * 8 reduction slots
+  float* cs = lds;
+  float* red = lds + kKvTok * d.r;
+  const size_t row0 = (size_t)blockIdx.x * kKvTok;
+  const int g = blockIdx.y, tid = threadIdx.x;
+  const int ntok = (int)min((size_t)kKvTok, (size_t)n_rows - row0);
+  for (int i = tid; i < kKvTok * d.r; i += 256) {
+    const int tk = i / d.r, e = i % d.r;
+    cs[i] = tk < ntok ? Elem<T>::load(c, (row0 + tk) * d.r + e) : 0.f;
+  }
+  __syncthreads();
+  // content key: dims e = tid, tid + 256, ...; sum of squares per token
+  float ssq[kKvTok];
+#pragma unroll
+  for (int t = 0; t < kKvTok; ++t) ssq[t] = 0.f;
+  const float* wk = w_uk + (size_t)g * d.r * d.dc;
+  for (int e = tid; e < d.dc; e += 256) {
+    float acc[kKvTok];
+#pragma unroll
+    for (int t = 0; t < kKvTok; ++t) acc[t] = 0.f;
+    for (int i = 0; i < d.r; ++i) {
+      const float w = wk[(size_t)i * d.dc + e];
+#pragma unroll
+      for (int t = 0; t < kKvTok; ++t) acc[t] += cs[t * d.r + i] * w;
+    }
+#pragma unroll
+    for (int t = 0; t < kKvTok; ++t) {
+      ssq[t] += acc[t] * acc[t];
+      if (t < ntok) Kraw[((row0 + t) * d.G + g) * d.dc + e] = acc[t];
+    }
+  }
+  // per-token totals over the block (one reduction slot per wave and token)
+#pragma unroll
+  for (int t = 0; t < kKvTok; ++t) {
+    const float s = wave_sum(ssq[t]);
+    if ((tid & 63) == 0) red[t * 4 + (tid >> 6)] = s;
+  }
+  // value
+  const T* wv = w_uv + (size_t)g * d.r * d.dv;
+  for (int e = tid; e < d.dv; e += 256) {
+    float acc[kKvTok];
+#pragma unroll
+    for (int t = 0; t < kKvTok; ++t) acc[t] = 0.f;
+    for (int i = 0; i < d.r; ++i) {
+      const float w = Elem<T>::load(wv, (size_t)i * d.dv + e);
+#pragma unroll
+      for (int t = 0; t < kKvTok; ++t) acc[t] += cs[t * d.r + i] * w;
+    }
+#pragma unroll
+    for (int t = 0; t < kKvTok; ++t)
+      if (t < ntok) V[((row0 + t) * d.G + g) * d.dv + e] = acc[t];
+  }
+  __syncthreads();
+  // normalised content key (reads back this thread's own raw values)
+  for (int t = 0; t < ntok; ++t) {
+    const size_t kg = (row0 + t) * d.G + g;
+    const float a = d.qk_norm
+                        ? 1.0f / sqrtf((red[t * 4] + red[t * 4 + 1] + red[t * 4 + 2] +
+                                        red[t * 4 + 3]) / (float)d.dc + d.eps)
+                        : 1.f;
+    if (tid == 0 && d.qk_norm) ak[kg] = a;
+    for (int e = tid; e < d.dc; e += 256)
+      Kh[kg * d.dqk + e] = Kraw[kg * d.dc + e] * (d.qk_norm ? gk[e] * a : 1.f);
+  }
+  // RoPE key: wave w handles tokens w, w + 4, ...
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int t = wave; t < ntok; t += 4) {
+    const size_t row = row0 + t;
+    const int pos = (int)(row % d.T);
+    const T* kr = k_rope + row * d.dr;
+    float ar = 1.f;
+    if (d.qk_norm) {
+      float s = 0.f;
+      for (int e = lane; e < d.dr; e += 64) {
+        const float v = Elem<T>::load(kr, e);
+        s += v * v;
+      }
+      ar = 1.0f / sqrtf(wave_sum(s) / (float)d.dr + d.eps);
+      if (g == 0 && lane == 0) akr[row] = ar;
+    }
+    float* out = Kh + (row * d.G + g) * d.dqk + d.dc;
+    for (int i = lane; i < d.dr / 2; i += 64) {
+      float x0 = Elem<T>::load(kr, 2 * i), x1 = Elem<T>::load(kr, 2 * i + 1);
+      if (d.qk_norm) {
+        x0 *= gkr[2 * i] * ar;
+        x1 *= gkr[2 * i + 1] * ar;
+      }
+      float c0, s0;
+      rope_cos_sin(pos, i, d.dr, d.base, &c0, &s0);
+      out[2 * i] = x0 * c0 - x1 * s0;
+      out[2 * i + 1] = x0 * s0 + x1 * c0;
+    }
+  }
+}
+
+// ---- forward attention ---------------------------------------------------------
+// One workgroup per (query row, head): exact online softmax over chunks of
+// kChunk keys j <= i (exp2 domain).
+__global__ __launch_bounds__(256) void attn_fwd_kernel(TrainDims d, const float* __restrict__ Qh,
+                                                       const float* __restrict__ Kh,
+                                                       const float* __restrict__ V,
+                                                       float* __restrict__ o,
+                                                       float* __restrict__ lse) {
+  extern __shared__ float lds[];  // q [dqk], p [kChunk], red [4]
+  float* q = lds;
+  float* p = lds + d.dqk;
+  float* red = p + kChunk;
+  const size_t row = blockIdx.x;
+  const int h = blockIdx.y, tid = threadIdx.x, g = h / d.hpg;
+  const int i = (int)(row % d.T);
+  const size_t seq0 = row - i;  // first row of the sequence
+  const float sc = d.tau * kLog2e;
+  for (int e = tid; e < d.dqk; e += 256) q[e] = Qh[(row * d.H + h) * d.dqk + e] * sc;
+  __syncthreads();
+  float acc = 0.f, m_run = -INFINITY, l_run = 0.f;
+  const int e_out = tid;  // output dim owned by this thread (d_v <= 256)
+  for (int j0 = 0; j0 <= i; j0 += kChunk) {
+    const int j = j0 + tid;
+    float s = -INFINITY;
+    if (j <= i) {
+      const float* k = Kh + ((seq0 + j) * d.G + g) * d.dqk;
+      float a = 0.f;
+      for (int e = 0; e < d.dqk; ++e) a += q[e] * k[e];
+      s = a;
+    }
+    const float m_new = fmaxf(m_run, block_max(s, red));
+    const float f = exp2f(m_run - m_new);
+    const float pv = j <= i ? exp2f(s - m_new) : 0.f;
+    p[tid] = pv;
+    l_run = l_run * f + block_sum(pv, red);
+    m_run = m_new;
+    const int n = min(kChunk, i + 1 - j0);
+    if (e_out < d.dv) {
+      float a = acc * f;
+      for (int jj = 0; jj < n; ++jj) a += p[jj] * V[((seq0 + j0 + jj) * d.G + g) * d.dv + e_out];
+      acc = a;
+    }
+    __syncthreads();
+  }
+  if (e_out < d.dv) o[(row * d.H + h) * d.dv + e_out] = acc / l_run;
+  if (tid == 0) lse[row * d.H + h] = (m_run + log2f(l_run)) * kLn2;
+}
+
+// ---- backward attention: query side ---------------------------------------------
+// One workgroup per (query row i, head h): D = d_o . o, then
+// dQ^ = tau sum_j ds_ij K^_j over j <= i.
+__global__ __launch_bounds__(256) void attn_bwd_q_kernel(
+    TrainDims d, const float* __restrict__ Qh, const float* __restrict__ Kh,
+    const float* __restrict__ V, const float* __restrict__ o, const float* __restrict__ lse,
+    const float* __restrict__ d_o, float* __restrict__ dQh, float* __restrict__ Dsum) {
+  extern __shared__ float lds[];  // q [dqk], do [dv], ds [kChunk], red [4]
+  float* q = lds;
+  float* dov = q + d.dqk;
+  float* ds = dov + d.dv;
+  float* red = ds + kChunk;
+  const size_t row = blockIdx.x;
+  const int h = blockIdx.y, tid = threadIdx.x, g = h / d.hpg;
+  const int i = (int)(row % d.T);
+  const size_t seq0 = row - i;
+  const size_t qh = row * d.H + h;
+  for (int e = tid; e < d.dqk; e += 256) q[e] = Qh[qh * d.dqk + e];
+  float dd = 0.f;
+  for (int e = tid; e < d.dv; e += 256) {
+    const float g_o = d_o[qh * d.dv + e];
+    dov[e] = g_o;
+    dd += g_o * o[qh * d.dv + e];
+  }
+  const float D = block_sum(dd, red);  // also orders the LDS writes above
+  if (tid == 0) Dsum[qh] = D;
+  const float L = lse[qh];
+  float acc0 = 0.f, acc1 = 0.f;  // dims tid, tid + 256 (dqk <= 512)
+  for (int j0 = 0; j0 <= i; j0 += kChunk) {
+    const int j = j0 + tid;
+    float v_ds = 0.f;
+    if (j <= i) {
+      const size_t kg = (seq0 + j) * d.G + g;
+      const float* k = Kh + kg * d.dqk;
+      float s = 0.f;
+      for (int e = 0; e < d.dqk; ++e) s += q[e] * k[e];
+      const float pj = expf(d.tau * s - L);
+      const float* v = V + kg * d.dv;
+      float dp = 0.f;
+      for (int e = 0; e < d.dv; ++e) dp += dov[e] * v[e];
+      v_ds = pj * (dp - D);
+    }
+    ds[tid] = v_ds;
+    __syncthreads();
+    const int n = min(kChunk, i + 1 - j0);
+    for (int jj = 0; jj < n; ++jj) {
+      const float* k = Kh + ((seq0 + j0 + jj) * d.G + g) * d.dqk;
+      const float w = ds[jj];
+      if (tid < d.dqk) acc0 += w * k[tid];
+      if (tid + 256 < d.dqk) acc1 += w * k[tid + 256];
+    }
+    __syncthreads();
+  }
+  if (tid < d.dqk) dQh[qh * d.dqk + tid] = d.tau * acc0;
+  if (tid + 256 < d.dqk) dQh[qh * d.dqk + tid + 256] = d.tau * acc1;
+}
+
+// ---- backward attention: key/value side ------------------------------------------
+// One workgroup per (key row j, group g): over the group's heads and queries
+// i >= j, dK^_j = tau sum ds_ij Q^_i and dV_j = sum p_ij d_o_i.
+__global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
+    TrainDims d, const float* __restrict__ Qh, const float* __restrict__ Kh,
+    const float* __restrict__ V, const float* __restrict__ lse, const float* __restrict__ d_o,
+    const float* __restrict__ Dsum, float* __restrict__ dKh, float* __restrict__ dV) {
+  extern __shared__ float lds[];  // k [dqk], v [dv], p [kChunk], ds [kChunk]
+  float* k = lds;
+  float* v = k + d.dqk;
+  float* p = v + d.dv;
+  float* ds = p + kChunk;
+  const size_t row = blockIdx.x;
+  const int g = blockIdx.y, tid = threadIdx.x;
+  const int j = (int)(row % d.T);
+  const size_t seq0 = row - j;
+  const size_t kg = row * d.G + g;
+  for (int e = tid; e < d.dqk; e += 256) k[e] = Kh[kg * d.dqk + e];
+  for (int e = tid; e < d.dv; e += 256) v[e] = V[kg * d.dv + e];
+  __syncthreads();
+  float dk0 = 0.f, dk1 = 0.f, dvv = 0.f;
+  for (int hh = 0; hh < d.hpg; ++hh) {
+    const int h = g * d.hpg + hh;
+    for (int i0 = j; i0 < d.T; i0 += kChunk) {
+      const int i = i0 + tid;
+      float pv = 0.f, dsv = 0.f;
+      if (i < d.T) {
+        const size_t qh = (seq0 + i) * d.H + h;
+        const float* q = Qh + qh * d.dqk;
+        float s = 0.f;
+        for (int e = 0; e < d.dqk; ++e) s += q[e] * k[e];
+        pv = expf(d.tau * s - lse[qh]);
+        const float* go = d_o + qh * d.dv;
+        float dp = 0.f;
+        for (int e = 0; e < d.dv; ++e) dp += go[e] * v[e];
+        dsv = pv * (dp - Dsum[qh]);
+      }
+      p[tid] = pv;
+      ds[tid] = dsv;
+      __syncthreads();
+      const int n = min(kChunk, d.T - i0);
+      for (int ii = 0; ii < n; ++ii) {
+        const size_t qh = (seq0 + i0 + ii) * d.H + h;
+        const float* q = Qh + qh * d.dqk;
+        const float w = ds[ii];
+        if (tid < d.dqk) dk0 += w * q[tid];
+        if (tid + 256 < d.dqk) dk1 += w * q[tid + 256];
+        if (tid < d.dv) dvv += p[ii] * d_o[qh * d.dv + tid];
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < d.dqk) dKh[kg * d.dqk + tid] = d.tau * dk0;
+  if (tid + 256 < d.dqk) dKh[kg * d.dqk + tid + 256] = d.tau * dk1;
+  if (tid < d.dv) dV[kg * d.dv + tid] = dvv;
+}
+
+// RMSNorm backward of one row held by a wavefront: y = gamma x a (a = 1/S):
+//   dx = a gamma dy - x a^3 (sum_j gamma_j dy_j x_j) / n.
+// dy, x are read through the accessors; dx is written by `put`.
+template <typename DY, typename X, typename PUT>
+__device__ void rmsnorm_bwd_wave(int n, float a, const float* gamma, DY dy, X x, PUT put,
+                                 int lane) {
+  float s = 0.f;
+  for (int e = lane; e < n; e += 64) s += gamma[e] * dy(e) * x(e);
+  s = wave_sum(s);
+  const float k = a * a * a * s / (float)n;
+  for (int e = lane; e < n; e += 64) put(e, a * gamma[e] * dy(e) - x(e) * k);
+}
+
+// ---- backward: query norms and rotation -------------------------------------------
+// One wavefront per (token row, head).  Each lane turns back (transposed
+// rotation) the RoPE-part gradient of its own pairs, keeps it in registers
+// for the RMSNorm backward and stores it over dQ^ for the gamma reduction.
+template <typename T>
+__global__ __launch_bounds__(256) void q_norm_bwd_kernel(
+    TrainDims d, const T* __restrict__ q_c, const T* __restrict__ q_rope,
+    const float* __restrict__ gq, const float* __restrict__ gqr, const float* __restrict__ aq,
+    const float* __restrict__ aqr, float* __restrict__ dQh, float* __restrict__ d_q_c,
+    float* __restrict__ d_q_rope) {
+  const size_t row = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (h >= d.H) return;
+  const int pos = (int)(row % d.T);
+  const size_t qh = row * d.H + h;
+  float* dy = dQh + qh * d.dqk;
+  float* dyr = dy + d.dc;
+  const T* xc = q_c + qh * d.dc;
+  const T* xr = q_rope + qh * d.dr;
+  float* oc = d_q_c + qh * d.dc;
+  float* orr = d_q_rope + qh * d.dr;
+  // content part
+  if (d.qk_norm)
+    rmsnorm_bwd_wave(
+        d.dc, aq[qh], gq, [&](int e) { return dy[e]; },
+        [&](int e) { return Elem<T>::load(xc, e); }, [&](int e, float v) { oc[e] = v; }, lane);
+  else
+    for (int e = lane; e < d.dc; e += 64) oc[e] = dy[e];
+  // RoPE part: pairs lane, lane + 64 (d_r <= 256)
+  float u0[2], u1[2];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = lane + 64 * k;
+    u0[k] = u1[k] = 0.f;
+    if (i < d.dr / 2) {
+      float cs, sn;
+      rope_cos_sin(pos, i, d.dr, d.base, &cs, &sn);
+      const float y0 = dyr[2 * i], y1 = dyr[2 * i + 1];
+      u0[k] = y0 * cs + y1 * sn;
+      u1[k] = -y0 * sn + y1 * cs;
+      dyr[2 * i] = u0[k];
+      dyr[2 * i + 1] = u1[k];
+      if (d.qk_norm)
+        s += gqr[2 * i] * u0[k] * Elem<T>::load(xr, 2 * i) +
+             gqr[2 * i + 1] * u1[k] * Elem<T>::load(xr, 2 * i + 1);
+    }
+  }
+  if (!d.qk_norm) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = lane + 64 * k;
+      if (i < d.dr / 2) {
+        orr[2 * i] = u0[k];
+        orr[2 * i + 1] = u1[k];
+      }
+    }
+    return;
+  }
+  const float a = aqr[qh];
+  const float kk = a * a * a * wave_sum(s) / (float)d.dr;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = lane + 64 * k;
+    if (i < d.dr / 2) {
+      orr[2 * i] = a * gqr[2 * i] * u0[k] - Elem<T>::load(xr, 2 * i) * kk;
+      orr[2 * i + 1] = a * gqr[2 * i + 1] * u1[k] - Elem<T>::load(xr, 2 * i + 1) * kk;
+    }
+  }
+}
+
+// ---- backward: key norms and the shared RoPE key -------------------------------------
+// One workgroup per token row.  Wave w runs the content-key RMSNorm backward
+// of groups w, w+4, ...; then the RoPE key gradient is summed over the
+// groups (the key is shared by every head), turned back, stored for the
+// gamma reduction and taken through its RMSNorm backward.
+template <typename T>
+__global__ __launch_bounds__(256) void k_norm_bwd_kernel(
+    TrainDims d, const T* __restrict__ k_rope, const float* __restrict__ gk,
+    const float* __restrict__ gkr, const float* __restrict__ Kraw, const float* __restrict__ ak,
+    const float* __restrict__ akr, const float* __restrict__ dKh, float* __restrict__ dK,
+    float* __restrict__ dKr, float* __restrict__ d_k_rope) {
+  const size_t row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int pos = (int)(row % d.T);
+  for (int g = wave; g < d.G; g += 4) {
+    const size_t kg = row * d.G + g;
+    const float* dy = dKh + kg * d.dqk;
+    const float* x = Kraw + kg * d.dc;
+    float* out = dK + kg * d.dc;
+    if (d.qk_norm)
+      rmsnorm_bwd_wave(
+          d.dc, ak[kg], gk, [&](int e) { return dy[e]; }, [&](int e) { return x[e]; },
+          [&](int e, float v) { out[e] = v; }, lane);
+    else
+      for (int e = lane; e < d.dc; e += 64) out[e] = dy[e];
+  }
+  // RoPE key: sum over groups, then the transposed rotation, pair by pair
+  float* dyr = dKr + row * d.dr;
+  for (int i = tid; i < d.dr / 2; i += 256) {
+    float y0 = 0.f, y1 = 0.f;
+    for (int g = 0; g < d.G; ++g) {
+      const float* src = dKh + (row * d.G + g) * d.dqk + d.dc;
+      y0 += src[2 * i];
+      y1 += src[2 * i + 1];
+    }
+    float cs, sn;
+    rope_cos_sin(pos, i, d.dr, d.base, &cs, &sn);
+    dyr[2 * i] = y0 * cs + y1 * sn;
+    dyr[2 * i + 1] = -y0 * sn + y1 * cs;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const T* xr = k_rope + row * d.dr;
+  float* out = d_k_rope + row * d.dr;
+  if (d.qk_norm)
+    rmsnorm_bwd_wave(
+        d.dr, akr[row], gkr, [&](int e) { return dyr[e]; },
+        [&](int e) { return Elem<T>::load(xr, e); }, [&](int e, float v) { out[e] = v; }, lane);
+  else
+    for (int e = lane; e < d.dr; e += 64) out[e] = dyr[e];
+}
+
+// ---- backward: latent gradient --------------------------------------------------------
+// d_c_t = sum_g (dk_{t,g} W^UK_g^T + dV_{t,g} W^UV_g^T).  Workgroup = kLatTok
+// token rows; thread i owns latent dims i, i + 256, ...
+template <typename T>
+__global__ __launch_bounds__(256) void latent_bwd_kernel(TrainDims d, int n_rows,
+                                                         const float* __restrict__ w_uk,
+                                                         const T* __restrict__ w_uv,
+                                                         const float* __restrict__ dK,
+                                                         const float* __restrict__ dV,
+                                                         float* __restrict__ d_c) {
+  extern __shared__ float lds[];  // [kLatTok][dc + dv] for one group
+  const size_t row0 = (size_t)blockIdx.x * kLatTok;
+  const int tid = threadIdx.x;
+  const int ntok = (int)min((size_t)kLatTok, (size_t)n_rows - row0);
+  const int w = d.dc + d.dv;
+  constexpr int kPer = 4;  // r <= 1024
+  float acc[kLatTok][kPer];
+#pragma unroll
+  for (int t = 0; t < kLatTok; ++t)
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc[t][k] = 0.f;
+  for (int g = 0; g < d.G; ++g) {
+    __syncthreads();
+    for (int e = tid; e < kLatTok * w; e += 256) {
+      const int t = e / w, x = e % w;
+      float v = 0.f;
+      if (t < ntok)
+        v = x < d.dc ? dK[((row0 + t) * d.G + g) * d.dc + x]
+                     : dV[((row0 + t) * d.G + g) * d.dv + (x - d.dc)];
+      lds[e] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + 256 * k;
+      if (i >= d.r) break;
+      const float* wk = w_uk + ((size_t)g * d.r + i) * d.dc;
+      for (int x = 0; x < d.dc; ++x) {
+        const float wv = wk[x];
+#pragma unroll
+        for (int t = 0; t < kLatTok; ++t) acc[t][k] += lds[t * w + x] * wv;
+      }
+      const T* wv_row = w_uv + ((size_t)g * d.r + i) * d.dv;
+      for (int x = 0; x < d.dv; ++x) {
+        const float wv = Elem<T>::load(wv_row, x);
+#pragma unroll
+        for (int t = 0; t < kLatTok; ++t) acc[t][k] += lds[t * w + d.dc + x] * wv;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = tid + 256 * k;
+    if (i >= d.r) break;
+#pragma unroll
+    for (int t = 0; t < kLatTok; ++t)
+      if (t < ntok) d_c[(row0 + t) * d.r + i] = acc[t][k];
+  }
+}
+
+// ---- backward: up-projection weight gradients -----------------------------------------
+// dW_g[i][x] = sum_t c_t[i] dY_{t,g}[x] with dY = dk (W^UK, blockIdx.z = 0) or
+// dV (W^UV, blockIdx.z = 1).  Workgroup = kWgRows latent rows of one group;
+// thread x owns column x (<= 256).  Deterministic: one sum per output.
+template <typename T>
+__global__ __launch_bounds__(256) void weight_grad_kernel(TrainDims d, int n_rows,
+                                                          const T* __restrict__ c,
+                                                          const float* __restrict__ dK,
+                                                          const float* __restrict__ dV,
+                                                          float* __restrict__ d_w_uk,
+                                                          float* __restrict__ d_w_uv) {
+  __shared__ float cs[kWgTok][kWgRows];
+  __shared__ float ys[kWgTok][256];
+  const int i0 = blockIdx.x * kWgRows, g = blockIdx.y, which = blockIdx.z;
+  const int D = which == 0 ? d.dc : d.dv;
+  const float* Y = which == 0 ? dK : dV;
+  const int tid = threadIdx.x;
+  float acc[kWgRows];
+#pragma unroll
+  for (int k = 0; k < kWgRows; ++k) acc[k] = 0.f;
+  for (size_t t0 = 0; t0 < (size_t)n_rows; t0 += kWgTok) {
+    __syncthreads();
+    for (int e = tid; e < kWgTok * kWgRows; e += 256) {
+      const int t = e / kWgRows, k = e % kWgRows;
+      const bool in = t0 + t < (size_t)n_rows && i0 + k < d.r;
+      cs[t][k] = in ? Elem<T>::load(c, (t0 + t) * d.r + i0 + k) : 0.f;
+    }
+    for (int e = tid; e < kWgTok * D; e += 256) {
+      const int t = e / D, x = e % D;
+      ys[t][x] = t0 + t < (size_t)n_rows ? Y[((t0 + t) * d.G + g) * D + x] : 0.f;
+    }
+    __syncthreads();
+    if (tid < D) {
+      for (int t = 0; t < kWgTok; ++t) {
+        const float y = ys[t][tid];
+#pragma unroll
+        for (int k = 0; k < kWgRows; ++k) acc[k] += cs[t][k] * y;
+      }
+    }
+  }
+  if (tid >= D) return;
+  float* out = (which == 0 ? d_w_uk : d_w_uv) + (size_t)g * d.r * D;
+#pragma unroll
+  for (int k = 0; k < kWgRows; ++k)
+    if (i0 + k < d.r) out[(size_t)(i0 + k) * D + tid] = acc[k];
+}
+
+// ---- backward: RMSNorm weight gradients ------------------------------------------------
+// dgamma[x] = sum_rows dy[row][x] x[row][x] a[row]; kGammaSplit partial sums
+// per column (blockIdx.y), then gamma_final_kernel adds them in order.
+template <typename X>
+__global__ __launch_bounds__(256) void gamma_partial_kernel(int rows, int n, const float* dy,
+                                                            int dy_stride, const X* x,
+                                                            int x_stride, const float* a,
+                                                            float* partial) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= n) return;
+  float s = 0.f;
+  for (int row = blockIdx.y; row < rows; row += kGammaSplit)
+    s += dy[(size_t)row * dy_stride + col] * Elem<X>::load(x, (size_t)row * x_stride + col) *
+         a[row];
+  partial[(size_t)blockIdx.y * n + col] = s;
+}
+
+__global__ __launch_bounds__(256) void gamma_final_kernel(int n, const float* partial,
+                                                          float* out, int zero) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= n) return;
+  float s = 0.f;
+  if (!zero)
+    for (int k = 0; k < kGammaSplit; ++k) s += partial[(size_t)k * n + col];
+  out[col] = s;
+}
+
+}  // namespace
+
+// ---- workspace ------------------------------------------------------------------------
+TrainWs train_ws_layout(const Cfg& c, int B, int T) {
+  const size_t BT = (size_t)B * T, dqk = c.dc + c.dr;
+  TrainWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = (off + bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  w.Qh = take(BT * c.H * dqk * 4);
+  w.Kh = take(BT * c.G * dqk * 4);
+  w.V = take(BT * c.G * c.dv * 4);
+  w.Kraw = take(BT * c.G * c.dc * 4);
+  w.aq = take(BT * c.H * 4);
+  w.aqr = take(BT * c.H * 4);
+  w.ak = take(BT * c.G * 4);
+  w.akr = take(BT * 4);
+  w.fwd_total = off;
+  w.dQh = take(BT * c.H * dqk * 4);
+  w.dKh = take(BT * c.G * dqk * 4);
+  w.dV = take(BT * c.G * c.dv * 4);
+  w.Dsum = take(BT * c.H * 4);
+  w.dK = take(BT * c.G * c.dc * 4);
+  w.dKr = take(BT * c.dr * 4);
+  w.gamma_partial = take((size_t)kGammaSplit * (c.dc > c.dr ? c.dc : c.dr) * 4);
+  w.total = off;
+  return w;
+}
+
+#define WS(type, field) ((type*)(wsb + ws.field))
+
+template <typename T>
+static hipError_t forward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in, const TrainWs& ws,
+                               char* wsb, float* o, float* lse, hipStream_t s) {
+  const TrainDims d = dims_of(c, B, T_);
+  const int n_rows = B * T_;
+  hipLaunchKernelGGL(prep_q_kernel<T>, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
+                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
+                     WS(float, Qh), WS(float, aq), WS(float, aqr));
+  hipLaunchKernelGGL(prep_kv_kernel<T>, dim3((n_rows + kKvTok - 1) / kKvTok, d.G), dim3(256),
+                     (kKvTok * d.r + kKvTok * 4) * sizeof(float), s, d, n_rows, (const T*)in.c,
+                     (const T*)in.k_rope, in.w_uk, (const T*)in.w_uv, in.gamma_k, in.gamma_k_rope,
+                     WS(float, Kh), WS(float, Kraw), WS(float, V), WS(float, ak), WS(float, akr));
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(n_rows, d.H), dim3(256),
+                     (d.dqk + kChunk + 4) * sizeof(float), s, d, WS(const float, Qh),
+                     WS(const float, Kh), WS(const float, V), o, lse);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t backward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in,
+                                const float* o, const float* lse, const float* d_o,
+                                const TrainWs& ws, char* wsb, const TrainGrads& gr,
+                                hipStream_t s) {
+  const TrainDims d = dims_of(c, B, T_);
+  const int n_rows = B * T_;
+  hipLaunchKernelGGL(prep_q_kernel<T>, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
+                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
+                     WS(float, Qh), WS(float, aq), WS(float, aqr));
+  hipLaunchKernelGGL(prep_kv_kernel<T>, dim3((n_rows + kKvTok - 1) / kKvTok, d.G), dim3(256),
+                     (kKvTok * d.r + kKvTok * 4) * sizeof(float), s, d, n_rows, (const T*)in.c,
+                     (const T*)in.k_rope, in.w_uk, (const T*)in.w_uv, in.gamma_k, in.gamma_k_rope,
+                     WS(float, Kh), WS(float, Kraw), WS(float, V), WS(float, ak), WS(float, akr));
+  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3(n_rows, d.H), dim3(256),
+                     (d.dqk + d.dv + kChunk + 4) * sizeof(float), s, d, WS(const float, Qh),
+                     WS(const float, Kh), WS(const float, V), o, lse, d_o, WS(float, dQh),
+                     WS(float, Dsum));
+  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(n_rows, d.G), dim3(256),
+                     (d.dqk + d.dv + 2 * kChunk) * sizeof(float), s, d, WS(const float, Qh),
+                     WS(const float, Kh), WS(const float, V), lse, d_o, WS(const float, Dsum),
+                     WS(float, dKh), WS(float, dV));
+  hipLaunchKernelGGL(q_norm_bwd_kernel<T>, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
+                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
+                     WS(const float, aq), WS(const float, aqr), WS(float, dQh), gr.d_q_c,
+                     gr.d_q_rope);
+  hipLaunchKernelGGL(k_norm_bwd_kernel<T>, dim3(n_rows), dim3(256), 0, s, d, (const T*)in.k_rope,
+                     in.gamma_k, in.gamma_k_rope, WS(const float, Kraw), WS(const float, ak),
+                     WS(const float, akr), WS(const float, dKh), WS(float, dK), WS(float, dKr),
+                     gr.d_k_rope);
+  hipLaunchKernelGGL(latent_bwd_kernel<T>, dim3((n_rows + kLatTok - 1) / kLatTok), dim3(256),
+                     (size_t)kLatTok * (d.dc + d.dv) * sizeof(float), s, d, n_rows, in.w_uk,
+                     (const T*)in.w_uv, WS(const float, dK), WS(const float, dV), gr.d_c);
+  hipLaunchKernelGGL(weight_grad_kernel<T>, dim3((d.r + kWgRows - 1) / kWgRows, d.G, 2), dim3(256),
+                     0, s, d, n_rows, (const T*)in.c, WS(const float, dK), WS(const float, dV),
+                     gr.d_w_uk, gr.d_w_uv);
+  // RMSNorm weights: (dy, x, a) per gamma; all zero in plain mode
+  float* part = WS(float, gamma_partial);
+  struct G4 {
+    int rows, n;
+    const float* dy;
+    int dys;
+    const void* x;
+    int xs;
+    bool x_f32;
+    const float* a;
+    float* out;
+  } gs[4] = {
+      {n_rows * d.H, d.dc, WS(const float, dQh), d.dqk, in.q_c, d.dc, false, WS(const float, aq),
+       gr.d_gamma_q},
+      {n_rows * d.G, d.dc, WS(const float, dKh), d.dqk, WS(const float, Kraw), d.dc, true,
+       WS(const float, ak), gr.d_gamma_k},
+      {n_rows * d.H, d.dr, WS(const float, dQh) + d.dc, d.dqk, in.q_rope, d.dr, false,
+       WS(const float, aqr), gr.d_gamma_q_rope},
+      {n_rows, d.dr, WS(const float, dKr), d.dr, in.k_rope, d.dr, false, WS(const float, akr),
+       gr.d_gamma_k_rope},
+  };
+  for (const G4& q : gs) {
+    const int nb = (q.n + 255) / 256;
+    if (d.qk_norm) {
+      if (q.x_f32)
+        hipLaunchKernelGGL(gamma_partial_kernel<float>, dim3(nb, kGammaSplit), dim3(256), 0, s,
+                           q.rows, q.n, q.dy, q.dys, (const float*)q.x, q.xs, q.a, part);
+      else
+        hipLaunchKernelGGL(gamma_partial_kernel<T>, dim3(nb, kGammaSplit), dim3(256), 0, s,
+                           q.rows, q.n, q.dy, q.dys, (const T*)q.x, q.xs, q.a, part);
+    }
+    hipLaunchKernelGGL(gamma_final_kernel, dim3(nb), dim3(256), 0, s, q.n, part, q.out,
+                       d.qk_norm ? 0 : 1);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_train_forward(const Cfg& c, int B, int T, const TrainPtrs& in,
+                                const TrainWs& ws, void* workspace, float* o, float* lse,
+                                hipStream_t s) {
+  char* wsb = (char*)workspace;
+  return c.dtype == QKMLA_BF16 ? forward_impl<uint16_t>(c, B, T, in, ws, wsb, o, lse, s)
+                               : forward_impl<float>(c, B, T, in, ws, wsb, o, lse, s);
+}
+
+hipError_t launch_train_backward(const Cfg& c, int B, int T, const TrainPtrs& in, const float* o,
+                                 const float* lse, const float* d_o, const TrainWs& ws,
+                                 void* workspace, const TrainGrads& gr, hipStream_t s) {
+  char* wsb = (char*)workspace;
+  return c.dtype == QKMLA_BF16
+             ? backward_impl<uint16_t>(c, B, T, in, o, lse, d_o, ws, wsb, gr, s)
+             : backward_impl<float>(c, B, T, in, o, lse, d_o, ws, wsb, gr, s);
+}
+
+}  // namespace qkmla

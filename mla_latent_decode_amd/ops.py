@@ -43,6 +43,20 @@ class _Pages(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
+class _TrainInputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("c", "q_c", "q_rope", "k_rope", "w_uk", "w_uv",
+                                               "gamma_q", "gamma_k", "gamma_q_rope",
+                                               "gamma_k_rope")]
+
+
+TRAIN_GRAD_NAMES = ("d_c", "d_q_c", "d_q_rope", "d_k_rope", "d_w_uk", "d_w_uv", "d_gamma_q",
+                    "d_gamma_k", "d_gamma_q_rope", "d_gamma_k_rope")
+
+
+class _TrainGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in TRAIN_GRAD_NAMES]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise QkmlaError(f"{LIB_PATH} is missing: build it with "
@@ -61,6 +75,10 @@ def _load():
         "qkmla_append_paged": (I32, [C, I32, I32, P, P, P, P, P, PG, P, P, P, P, P]),
         "qkmla_decode_paged": (I32, [C, I32, I32, P, P, P, P, P, P, P, P, PG, I32, P, SZ, P, P,
                                      P, P]),
+        "qkmla_train_workspace_size": (SZ, [C, I32, I32]),
+        "qkmla_train_forward": (I32, [C, I32, I32, ctypes.POINTER(_TrainInputs), P, SZ, P, P, P]),
+        "qkmla_train_backward": (I32, [C, I32, I32, ctypes.POINTER(_TrainInputs), P, P, P, P, SZ,
+                                       ctypes.POINTER(_TrainGrads), P]),
         "qkmla_out_proj": (I32, [C, I32, P, P, P, P]),
         "qkmla_plan": (I32, [C, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "qkmla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -347,3 +365,63 @@ def out_proj(cfg: Config, o_lat, w_uv, out=None):
         _ptr(w_uv, (cfg.n_groups, cfg.latent_rank, cfg.v_head_dim), cfg.torch_dtype, "w_uv"),
         _ptr(out, (B, H, cfg.v_head_dim), torch.float32, "out"), _stream()), "qkmla_out_proj")
     return out
+
+
+# --- training / prefill (explicit form) ---------------------------------------------------
+
+def train_workspace_size(cfg: Config, batch: int, seq_len: int) -> int:
+    n = _lib.qkmla_train_workspace_size(ctypes.byref(cfg.c()), batch, seq_len)
+    if n == 0:
+        raise QkmlaError("qkmla_train_workspace_size: " + _lib.qkmla_last_error().decode())
+    return n
+
+
+def _train_inputs(cfg: Config, t: dict, B: int, T: int) -> _TrainInputs:
+    H, G, r, dc, dr, dv = (cfg.n_heads, cfg.n_groups, cfg.latent_rank, cfg.head_dim,
+                           cfg.rope_dim, cfg.v_head_dim)
+    dt, f32 = cfg.torch_dtype, torch.float32
+    spec = {"c": ((B, T, r), dt), "q_c": ((B, T, H, dc), dt), "q_rope": ((B, T, H, dr), dt),
+            "k_rope": ((B, T, dr), dt), "w_uk": ((G, r, dc), f32), "w_uv": ((G, r, dv), dt),
+            "gamma_q": ((dc,), f32), "gamma_k": ((dc,), f32), "gamma_q_rope": ((dr,), f32),
+            "gamma_k_rope": ((dr,), f32)}
+    return _TrainInputs(*[_ptr(t.get(n), shp, dtp, n) for n, (shp, dtp) in spec.items()])
+
+
+def train_forward(cfg: Config, inputs: dict, workspace, o=None, lse=None):
+    """Causal explicit-form forward over inputs["c"] [B][T][r] etc. (dict of
+    device tensors named as in qkmla_train_inputs).  Returns (o, lse)."""
+    B, T = inputs["c"].shape[:2]
+    H, dev = cfg.n_heads, inputs["c"].device
+    if o is None:
+        o = torch.empty((B, T, H, cfg.v_head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    ins = _train_inputs(cfg, inputs, B, T)
+    _check(_lib.qkmla_train_forward(
+        ctypes.byref(cfg.c()), B, T, ctypes.byref(ins),
+        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(o, (B, T, H, cfg.v_head_dim), torch.float32, "o"),
+        _ptr(lse, (B, T, H), torch.float32, "lse"), _stream()), "qkmla_train_forward")
+    return o, lse
+
+
+def train_backward(cfg: Config, inputs: dict, o, lse, d_o, workspace, grads: Optional[dict] = None):
+    """Gradients of sum(o * d_o) with respect to every input: dict
+    d_<name> -> fp32 tensor of that input's shape."""
+    B, T = inputs["c"].shape[:2]
+    H, dev = cfg.n_heads, inputs["c"].device
+    if grads is None:
+        grads = {"d_" + n: torch.empty(tuple(inputs[n].shape), dtype=torch.float32, device=dev)
+                 for n in ("c", "q_c", "q_rope", "k_rope", "w_uk", "w_uv", "gamma_q", "gamma_k",
+                           "gamma_q_rope", "gamma_k_rope")}
+    ins = _train_inputs(cfg, inputs, B, T)
+    gs = _TrainGrads(*[_ptr(grads[n], tuple(inputs[n[2:]].shape), torch.float32, n)
+                       for n in TRAIN_GRAD_NAMES])
+    _check(_lib.qkmla_train_backward(
+        ctypes.byref(cfg.c()), B, T, ctypes.byref(ins),
+        _ptr(o, (B, T, H, cfg.v_head_dim), torch.float32, "o"),
+        _ptr(lse, (B, T, H), torch.float32, "lse"),
+        _ptr(d_o, (B, T, H, cfg.v_head_dim), torch.float32, "d_o"),
+        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(), ctypes.byref(gs),
+        _stream()), "qkmla_train_backward")
+    return grads

@@ -300,6 +300,95 @@ def paged_caches(dev):
               n_wg=3, heads=MERGE_HEADS, bad_seq=0)
 
 
+TRAIN_IN = ("c", "q_c", "q_rope", "k_rope", "w_uk", "w_uv", "gamma_q", "gamma_k", "gamma_q_rope",
+            "gamma_k_rope")
+TRAIN_TOL = dict(o=2e-5, lse=2e-5, grad=1e-4)
+
+
+class CTrainInputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in TRAIN_IN]
+
+
+class CTrainGrads(ctypes.Structure):
+    _fields_ = [("d_" + n, ctypes.c_void_p) for n in TRAIN_IN]
+
+
+def run_train(dev, shape, B, T, seed, label, qk_norm=True):
+    """Training forward and backward through the C ABI against the oracle's
+    forward and autograd backward.  All arithmetic on the device is fp32 (bf16
+    storage only rounds the inputs, which the oracle sees rounded), so o and
+    lse are held to 2e-5 relative and every gradient to 1e-4 of its largest
+    element."""
+    from oracle.qkmla_train_oracle import train_reference
+    from mla_latent_decode_amd.inputs import train_inputs
+    from isa_emu.device import CConfig, SIGNATURES, bf16_bits
+    P = ctypes.c_void_p
+    lib = dev.lib
+    for n, (rt, at) in SIGNATURES.items():
+        if hasattr(lib, n):
+            getattr(lib, n).restype, getattr(lib, n).argtypes = rt, at
+    bf = shape.dtype == "bf16"
+    cfg = CConfig(shape.n_heads, shape.n_groups, shape.latent_rank, shape.head_dim,
+                  shape.rope_dim, shape.v_head_dim, 1 if bf else 0, int(qk_norm), 1e-6, 0.0,
+                  10000.0)
+    inp = train_inputs(shape, B, T, seed)
+    d_o = inp.pop("d_o")
+    store = (lambda x: bf16_bits(np.asarray(x, np.float32))) if bf else (
+        lambda x: np.asarray(x, np.float32))
+    dv = {}
+    for n in TRAIN_IN:
+        fp32 = n.startswith("gamma") or n == "w_uk"
+        dv[n] = dev.put(np.asarray(inp[n], np.float32) if fp32 else store(inp[n]), "train " + n)
+    ins = CTrainInputs(*[dv[n].ctypes.data for n in TRAIN_IN])
+    H, dvh = shape.n_heads, shape.v_head_dim
+    o = dev.empty((B, T, H, dvh), np.float32, "train o", fill=0xFF)
+    lse = dev.empty((B, T, H), np.float32, "train lse", fill=0xFF)
+    gdo = dev.put(d_o.astype(np.float32), "train d_o")
+    ws_n = lib.qkmla_train_workspace_size(ctypes.byref(cfg), B, T)
+    ws = dev.empty((ws_n,), np.uint8, "train workspace", fill=0xCD)
+
+    def call(name, *args):
+        r = getattr(lib, name)(*args)
+        if r != 0:
+            raise RuntimeError(f"{name} returned {r}: {lib.qkmla_last_error().decode()}")
+
+    call("qkmla_train_forward", ctypes.byref(cfg), B, T, ctypes.byref(ins), P(ws.ctypes.data),
+         ws_n, P(o.ctypes.data), P(lse.ctypes.data), None)
+    grads = {n: dev.empty(np.shape(inp[n]), np.float32, "train d_" + n, fill=0xFF)
+             for n in TRAIN_IN}
+    gs = CTrainGrads(*[grads[n].ctypes.data for n in TRAIN_IN])
+    call("qkmla_train_backward", ctypes.byref(cfg), B, T, ctypes.byref(ins), P(o.ctypes.data),
+         P(lse.ctypes.data), P(gdo.ctypes.data), P(ws.ctypes.data), ws_n, ctypes.byref(gs), None)
+    ref = train_reference(inp, d_o, qk_norm=qk_norm, eps=1e-6, base=10000.0)
+    err = {"o": float(np.max(oracle.rowwise_rel_err(o.reshape(-1, dvh),
+                                                    ref["o"].reshape(-1, dvh)))),
+           "lse": float(np.max(np.abs(lse - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))))}
+    gerr = {}
+    for n in TRAIN_IN:
+        r_ = ref["d_" + n]
+        scale = float(np.max(np.abs(r_))) if np.any(r_) else 1.0
+        gerr[n] = float(np.max(np.abs(grads[n] - r_))) / scale
+    ok = (err["o"] <= TRAIN_TOL["o"] and err["lse"] <= TRAIN_TOL["lse"] and
+          all(v <= TRAIN_TOL["grad"] for v in gerr.values()))
+    print(f"[{'ok' if ok else 'FAIL'}] {label}: o {err['o']:.2e} lse {err['lse']:.2e} grads " +
+          " ".join(f"{k} {v:.1e}" for k, v in gerr.items()), flush=True)
+    if not ok:
+        raise AssertionError(f"{label}: {err} {gerr}")
+
+
+@case
+def train_fwd_bwd(dev):
+    """Training forward and backward (explicit form, causal): fp32 and bf16
+    storage on small layers, QK-norm and plain, two sequences, one longer
+    than a 256-key chunk."""
+    run_train(dev, Shape(4, 2, 12, 6, 4, 5, "f32"), 2, 7, 600, "train fp32 small, QK-norm")
+    run_train(dev, Shape(4, 2, 12, 6, 4, 5, "f32"), 2, 7, 601, "train fp32 small, plain",
+              qk_norm=False)
+    run_train(dev, Shape(6, 3, 40, 16, 8, 12, "bf16"), 1, 19, 602, "train bf16 storage, G=3")
+    run_train(dev, Shape(2, 1, 8, 4, 4, 4, "f32"), 1, 300, 603,
+              "train fp32, 300 tokens (two chunks)")
+
+
 @case
 def bf16_long_segments(dev):
     """Segments long enough to run the three-stage tile loop several times:

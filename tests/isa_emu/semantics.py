@@ -243,6 +243,21 @@ def _(w, i):
     _setscc(w, r)
 
 
+@h("s_bfe_i64")
+def _(w, i):
+    a = w.sget(i.ops[1], "b64")
+    b = w.sget(i.ops[2])
+    off, width = b & 63, (b >> 16) & 127
+    r = 0
+    if width:
+        r = (a >> off) & ((1 << width) - 1)
+        if (r >> (width - 1)) & 1:
+            r -= 1 << width
+        r &= M64
+    w.sset(i.ops[0], r, 2)
+    _setscc(w, r)
+
+
 @h("s_lshr_b32")
 def _(w, i):
     a, b = _s2(w, i)
@@ -636,6 +651,15 @@ for _n, (_f, _k) in _V.items():
 def _(w, i):
     d, a, b = i.ops
     w.vset(d, (_i(w, b) >> (_u(w, a) & U64(31)).astype(np.int64)).astype(np.int64) & M32)
+
+
+@h("v_mul_i32_i24")
+def _(w, i):
+    def s24(x):
+        x = x & 0xFFFFFF
+        return np.where(x & 0x800000, x - (1 << 24), x)
+    r = s24(_i(w, i.ops[1])) * s24(_i(w, i.ops[2]))
+    w.vset(i.ops[0], (r & M32).astype(U32))
 
 
 @h("v_min_i32")

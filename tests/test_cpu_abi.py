@@ -37,7 +37,7 @@ def _ops():
 
 def test_abi_version_and_status_strings():
     ops = _ops()
-    assert ops.abi_version() == 3
+    assert ops.abi_version() == 4
     assert ops._lib.qkmla_status_string(0) == b"ok"
     assert ops._lib.qkmla_status_string(3) == b"workspace too small"
 
@@ -186,3 +186,43 @@ def test_f32_pages_of_any_size_pass_host_validation():
     st = lib.qkmla_decode_paged(ctypes.byref(cfg.c()), 1, 1, p, p, p, p, p, p, p, p,
                                 ctypes.byref(pages), 12, p, 0, p, None, None, None)
     assert st in (3, 4)  # workspace too small, or no device to plan for
+
+
+def test_train_entry_points_validate_on_the_host():
+    """Training calls: shape limits of their own (any bf16 shape, d_c and d_v
+    up to 256), NULL inputs and gradients, workspace size, batch 0 no-op;
+    all checked before any device access."""
+    ops = _ops()
+    lib = ops._lib
+    small_bf16 = _cfg(n_heads=6, n_groups=3, latent_rank=40, head_dim=16, rope_dim=8,
+                      v_head_dim=12)
+    assert ops.train_workspace_size(small_bf16, 2, 45) > 0  # no decode shape restriction
+    big = _cfg(head_dim=512, dtype="f32")
+    assert lib.qkmla_train_workspace_size(ctypes.byref(big.c()), 1, 8) == 0
+    assert b"d_c and d_v" in lib.qkmla_last_error()
+    cfg = _cfg(n_heads=4, n_groups=2, latent_rank=12, head_dim=6, rope_dim=4, v_head_dim=5,
+               dtype="f32")
+    p = 0x1000
+    ins = ops._TrainInputs(*([p] * 10))
+    st = lib.qkmla_train_forward(ctypes.byref(cfg.c()), 0, 7, None, None, 0, None, None, None)
+    assert st == 0  # batch 0
+    st = lib.qkmla_train_forward(ctypes.byref(cfg.c()), 1, 0, ctypes.byref(ins), p, 1 << 20, p, p,
+                                 None)
+    assert st == 1  # seq_len 0
+    st = lib.qkmla_train_forward(ctypes.byref(cfg.c()), 1, 7, None, p, 1 << 20, p, p, None)
+    assert st == 1 and b"inputs" in lib.qkmla_last_error()
+    missing = ops._TrainInputs(*([p] * 9 + [0]))  # gamma_k_rope NULL with qk_norm
+    st = lib.qkmla_train_forward(ctypes.byref(cfg.c()), 1, 7, ctypes.byref(missing), p, 1 << 20,
+                                 p, p, None)
+    assert st == 1
+    st = lib.qkmla_train_forward(ctypes.byref(cfg.c()), 1, 7, ctypes.byref(ins), p, 16, p, p, None)
+    assert st == 3  # workspace too small
+    grads = ops._TrainGrads(*([p] * 9 + [0]))
+    need = ops.train_workspace_size(cfg, 1, 7)
+    st = lib.qkmla_train_backward(ctypes.byref(cfg.c()), 1, 7, ctypes.byref(ins), p, p, p, p, need,
+                                  ctypes.byref(grads), None)
+    assert st == 1 and b"gradient" in lib.qkmla_last_error()
+    grads = ops._TrainGrads(*([p] * 10))
+    st = lib.qkmla_train_backward(ctypes.byref(cfg.c()), 1, 7, ctypes.byref(ins), p, p, p, p,
+                                  need - 256, ctypes.byref(grads), None)
+    assert st == 3

@@ -35,7 +35,8 @@ def runtime(tmp_path_factory):
 
 @pytest.mark.parametrize("case", ["hazard_checker", "fp32_tiny", "bf16_split", "bf16_plain_hold",
                                   "bf16_long_segments", "bf16_plain_overflow", "bf16_append_caches",
-                                  "bf16_64_heads", "multi_query", "paged_caches"])
+                                  "bf16_64_heads", "multi_query", "paged_caches",
+                                  "train_fwd_bwd"])
 def test_kernels_on_the_emulator(runtime, case):
     env = {k: v for k, v in os.environ.items() if k != "QKMLA_NUM_WG"}
     r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "isa_emu", "cases.py"),

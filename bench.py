@@ -19,6 +19,8 @@ Prints ONE JSON line: value = algorithmic cache bytes per step / step time
 overhead against the same kernels with the normalisation compiled out (plain
 MLA), the hot kernel's roofline position, the fp64 oracle timed on the host,
 and the same figures for the 32k, 256k and ragged workloads under "sweep".
+Under "next_rows": bulk append, s_q = 2 decode, paged-cache decode and the
+explicit-form training forward and backward, each timed on its own.
 """
 from __future__ import annotations
 
@@ -255,6 +257,134 @@ def measure(cid, steps, warmup, graph=True):
     return b, res, ms_qk, k_ms, wall
 
 
+def _event_ms(torch, fn, reps, warmup=2):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_next_rows(steps):
+    """The rows beyond the decode step, each on the batch-16 x 4096 layer
+    unless stated: bulk append of every cached token in one call, decode with
+    s_q = 2 query rows per sequence, decode over 64-row pages of a shuffled
+    pool, and the explicit-form training forward and backward (1 x 1024
+    tokens).  Eager launches timed with HIP events; cache copies rotated as
+    in the headline."""
+    import torch
+    from mla_latent_decode_amd import ops
+    from mla_latent_decode_amd.layout import (append_bytes_per_token, cache_bytes_per_token,
+                                              train_attention_flops)
+    out = {}
+    b = Bench(1)
+    s, B, L, H = b.w.shape, b.B, b.L_cap, b.w.shape.n_heads
+    r, dr, G, dt = s.latent_rank, s.rope_dim, s.n_groups, b.cfg.torch_dtype
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5000)
+    per_tok = cache_bytes_per_token(s, True)
+    # N1: bulk append (all 16 x 4096 tokens in one call)
+    c_new = torch.randn((B, L, r), generator=g, device="cuda").to(dt)
+    k_new = torch.randn((B, L, dr), generator=g, device="cuda").to(dt)
+    pos0 = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    lat, rope, alpha = b.copies[0]
+    ms = _event_ms(torch, lambda: ops.append(b.cfg, c_new, k_new, b.w_uk, b.gkr, pos0, lat, rope,
+                                             alpha, b.status), 3)
+    out["bulk_append"] = {"tokens": B * L, "us": round(ms * 1e3, 1),
+                          "Mtokens_per_s": round(B * L / (ms * 1e-3) / 1e6, 1),
+                          "GBps": round(B * L * append_bytes_per_token(s) / (ms * 1e-3) / 1e9, 1)}
+    del c_new, k_new
+    # N2: s_q = 2 rows per sequence (causal), over the rotated cache copies
+    s_q = 2
+    qc = torch.randn((B, s_q, H, s.head_dim), generator=g, device="cuda").to(dt)
+    qr = torch.randn((B, s_q, H, dr), generator=g, device="cuda").to(dt)
+    ws = torch.empty((ops.decode_workspace_size(b.cfg, B * s_q, L),), dtype=torch.uint8,
+                     device="cuda")
+    o2 = torch.empty((B, s_q, H, r), dtype=torch.float32, device="cuda")
+    it = [0]
+
+    def multi():
+        la, ro, al = b.copies[it[0] % b.n_copies]
+        it[0] += 1
+        ops.decode_multi(b.cfg, qc, qr, b.w_qabs, b.gqr, la, ro, al, b.seq_lens, L, ws, o2,
+                         status=b.status)
+    ms = _event_ms(torch, multi, steps)
+    rows_tokens = sum(sum(max(0, Lb - s_q + i + 1) for i in range(s_q)) for Lb in b.lengths)
+    out["multi_query_s_q2"] = {"us_per_step": round(ms * 1e3, 2),
+                               "cache_GBps_per_row": round(rows_tokens * per_tok / (ms * 1e-3) / 1e9, 1),
+                               "note": "each query row streams its own causal prefix"}
+    del qc, qr, o2
+    # N3: the same caches in 64-row pages of a shuffled pool (copies rotated)
+    ps = 64
+    nblk = L // ps
+    pools = []
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(5001)
+    for ci in range(b.n_copies):
+        la, ro, al = b.copies[ci]
+        perm = torch.randperm(B * nblk, generator=gen).to("cuda")
+        table = perm.view(B, nblk).to(torch.int32).contiguous()
+        plat = torch.empty((B * nblk, ps, r), dtype=dt, device="cuda")
+        prope = torch.empty((B * nblk, ps, dr), dtype=dt, device="cuda")
+        palpha = torch.empty((B * nblk, ps, G), dtype=torch.float32, device="cuda")
+        plat[perm] = la.view(B * nblk, ps, r)
+        prope[perm] = ro.view(B * nblk, ps, dr)
+        palpha[perm] = al.view(B * nblk, ps, G)
+        pools.append((table, plat, prope, palpha))
+    o1 = torch.empty((B, 1, H, r), dtype=torch.float32, device="cuda")
+    q1c, q1r = b.q_c.view(B, 1, H, -1), b.q_rope.view(B, 1, H, -1)
+
+    def paged():
+        t_, pl, pr, pa = pools[it[0] % len(pools)]
+        it[0] += 1
+        ops.decode_paged(b.cfg, q1c, q1r, b.w_qabs, b.gqr, pl, pr, pa, b.seq_lens, t_, L,
+                         b.workspace, o1, status=b.status)
+    ms_p = _event_ms(torch, paged, steps)
+    ms_c, _ = b.time_steps(steps, 3)
+    out["paged_64"] = {"us_per_step": round(ms_p * 1e3, 2),
+                       "contiguous_us_per_step_eager": round(ms_c * 1e3, 2),
+                       "cache_GBps": round(b.bytes_qk / (ms_p * 1e-3) / 1e9, 1)}
+    status = int(b.status.item())
+    del pools, b
+    torch.cuda.empty_cache()
+    if status:
+        raise RuntimeError(f"device status {status} in the next-row measurements")
+    # N4: training forward and backward, DeepSeek-V3-like layer, 1 x 1024 tokens
+    Bt, T = 1, 1024
+    cfg = ops.Config.from_shape(s)
+    shp = {"c": (Bt, T, r), "q_c": (Bt, T, H, s.head_dim), "q_rope": (Bt, T, H, dr),
+           "k_rope": (Bt, T, dr), "w_uk": (G, r, s.head_dim), "w_uv": (G, r, s.v_head_dim),
+           "gamma_q": (s.head_dim,), "gamma_k": (s.head_dim,), "gamma_q_rope": (dr,),
+           "gamma_k_rope": (dr,)}
+    ins = {}
+    for n, sh in shp.items():
+        x = torch.randn(sh, generator=g, device="cuda")
+        if n.startswith("gamma"):
+            x = x.abs() * 0.5 + 0.5
+        elif n.startswith("w_"):
+            x = x / math.sqrt(r)
+        ins[n] = x if (n == "w_uk" or n.startswith("gamma")) else x.to(dt)
+    wst = torch.empty((ops.train_workspace_size(cfg, Bt, T),), dtype=torch.uint8, device="cuda")
+    o, lse = ops.train_forward(cfg, ins, wst)
+    d_o = torch.randn(tuple(o.shape), generator=g, device="cuda")
+    grads = ops.train_backward(cfg, ins, o, lse, d_o, wst)
+    ms_f = _event_ms(torch, lambda: ops.train_forward(cfg, ins, wst, o, lse), 3, warmup=1)
+    ms_b = _event_ms(torch, lambda: ops.train_backward(cfg, ins, o, lse, d_o, wst, grads), 3,
+                     warmup=1)
+    ff, fb = train_attention_flops(s, Bt, T)
+    out["train_fwd_bwd"] = {"batch": Bt, "seq_len": T, "fwd_ms": round(ms_f, 3),
+                            "bwd_ms": round(ms_b, 3),
+                            "fwd_attention_TFLOPs": round(ff / (ms_f * 1e-3) / 1e12, 2),
+                            "bwd_attention_TFLOPs": round(fb / (ms_b * 1e-3) / 1e12, 2),
+                            "kernels": "row-parallel fp32 VALU (reference structure)"}
+    return out
+
+
 def cpu_baseline(cid, budget_s=15.0):
     """The fp64 oracle on the host: whole sequences of the same workload, one at
     a time, until about `budget_s` seconds of CPU work; returns its cache GB/s."""
@@ -294,6 +424,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="headline workload (1-4)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the bulk-append, s_q=2, paged and training measurements")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP-graph replay of the step)")
     args = ap.parse_args()
@@ -352,6 +484,13 @@ def main():
             del _b
             torch.cuda.empty_cache()
         line["sweep"] = sweep
+    if not args.no_next:
+        try:
+            line["next_rows"] = measure_next_rows(max(10, args.steps // 2))
+        except Exception as ex:  # noqa: BLE001 -- the headline line is still printed
+            line["next_rows"] = {"error": f"{type(ex).__name__}: {ex}"}
+        print(f"[bench] next rows {line['next_rows']}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)

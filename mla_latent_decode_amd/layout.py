@@ -25,3 +25,20 @@ def decode_flops_per_token(shape) -> int:
     contraction over latent + RoPE dims and the P.C accumulation, all heads."""
     H, r, dr = shape.n_heads, shape.latent_rank, shape.rope_dim
     return 2 * H * (r + dr) + 2 * H * r
+
+
+def train_attention_flops(shape, batch: int, seq_len: int) -> tuple:
+    """Algorithmic attention FLOPs of one causal training step (forward,
+    backward): every head scores T(T+1)/2 (query, key) pairs.  Forward per
+    pair: the logit over d_c + d_r and the value sum over d_v.  Backward per
+    pair: the recomputed logit, d_o . V, dV, dK^ and dQ^."""
+    pairs = batch * shape.n_heads * seq_len * (seq_len + 1) // 2
+    dqk, dv = shape.head_dim + shape.rope_dim, shape.v_head_dim
+    return 2 * pairs * (dqk + dv), 2 * pairs * (3 * dqk + 2 * dv)
+
+
+def append_bytes_per_token(shape, qk_norm: bool = True) -> int:
+    """Bytes one appended token moves: new latent and raw RoPE key read, the
+    three cache rows written."""
+    e = elem_bytes(shape.dtype)
+    return e * (shape.latent_rank + shape.rope_dim) + cache_bytes_per_token(shape, qk_norm)

@@ -381,7 +381,7 @@ def measure_next_rows(steps):
                             "bwd_ms": round(ms_b, 3),
                             "fwd_attention_TFLOPs": round(ff / (ms_f * 1e-3) / 1e12, 2),
                             "bwd_attention_TFLOPs": round(fb / (ms_b * 1e-3) / 1e12, 2),
-                            "kernels": "row-parallel fp32 VALU (reference structure)"}
+                            "kernels": "MFMA flash attention (bf16 operands), row-parallel norm and projection gradients"}
     return out
 
 

@@ -93,11 +93,26 @@ struct TrainGrads {  // fp32 gradients, same shapes as the inputs
 //   Qh [BT][H][d_qk], Kh [BT][G][d_qk], V [BT][G][d_v], Kraw [BT][G][d_c],
 //   aq, aqr [BT][H], ak [BT][G], akr [BT]  (the forward needs these: fwd_total)
 //   dQh, dKh, dV, Dsum [BT][H], dK [BT][G][d_c], dKr [BT][d_r], gamma partials.
+//   (bf16 layer with the MFMA attention also: Qb [BT][H][d_qk] scaled by
+//   tau*log2(e), Kb [B][G][T][d_qk], Vb [B][G][T][d_v], all bf16)
 struct TrainWs {
-  size_t Qh, Kh, V, Kraw, aq, aqr, ak, akr, fwd_total;
-  size_t dQh, dKh, dV, Dsum, dK, dKr, gamma_partial, total;
+  size_t Qh, Kh, V, Kraw, aq, aqr, ak, akr, Qb, Kb, Vb, fwd_total;
+  size_t dQh, dKh, dV, Dsum, dK, dKr, gamma_partial;
+  size_t dOb, stat;  // MFMA backward: d_o bf16 [BT][H][d_v], (lse*log2 e, D) [BT][H]
+  size_t total;
 };
 TrainWs train_ws_layout(const Cfg& c, int B, int T);
+// The layer shape the MFMA attention is compiled for (bf16, 16 heads per
+// group, d_c + d_r = 192, d_v = 128).
+bool train_mfma_shape(const Cfg& c);
+hipError_t launch_flash_fwd(const Cfg& c, int B, int T, const void* Qb, const void* Kb,
+                            const void* Vb, float* o, float* lse, hipStream_t s);
+// dK^ and dV (key side) and dQ^ (query side) of the attention, fp32, in the
+// row-major layouts of the row-parallel kernels.
+hipError_t launch_flash_bwd(const Cfg& c, int B, int T, const void* Qb, const void* Kb,
+                            const void* Vb, const float* o, const float* lse, const float* d_o,
+                            void* dOb, void* stat, float* dKh, float* dV, float* dQh,
+                            hipStream_t s);
 
 // ---- launchers (each enqueues on `stream`; returns the launch error) -------
 hipError_t launch_absorb(const Cfg& c, const float* w_uk, const float* gq, const float* gk,

@@ -66,12 +66,16 @@ __device__ float block_max(float v, float* red) {
 // ---- forward: normalised, rotated queries ----------------------------------
 // One wavefront per (token row, head).  Qh[row][h] = [q^ content | q^R], and
 // the inverse RMS values for the backward.
-template <typename T>
+// MF: write the bf16 operand of the MFMA attention instead (same layout,
+// scaled by tau*log2(e)).
+template <typename T, bool MF>
 __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __restrict__ q_c,
                                                      const T* __restrict__ q_rope,
                                                      const float* __restrict__ gq,
                                                      const float* __restrict__ gqr,
-                                                     float* __restrict__ Qh, float* __restrict__ aq,
+                                                     float* __restrict__ Qh,
+                                                     uint16_t* __restrict__ Qb,
+                                                     float* __restrict__ aq,
                                                      float* __restrict__ aqr) {
   const size_t row = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -80,7 +84,11 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
   const size_t qh = row * d.H + h;
   const T* qc = q_c + qh * d.dc;
   const T* qr = q_rope + qh * d.dr;
-  float* out = Qh + qh * d.dqk;
+  const float qs = d.tau * kLog2e;
+  auto put = [&](int e, float v) {
+    if constexpr (MF) Qb[qh * d.dqk + e] = f32_to_bf16(v * qs);
+    else Qh[qh * d.dqk + e] = v;
+  };
   float a = 1.f, ar = 1.f;
   if (d.qk_norm) {
     float ss = 0.f, sr = 0.f;
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
     }
   }
   for (int e = lane; e < d.dc; e += 64)
-    out[e] = Elem<T>::load(qc, e) * (d.qk_norm ? gq[e] * a : 1.f);
+    put(e, Elem<T>::load(qc, e) * (d.qk_norm ? gq[e] * a : 1.f));
   for (int i = lane; i < d.dr / 2; i += 64) {
     float x0 = Elem<T>::load(qr, 2 * i), x1 = Elem<T>::load(qr, 2 * i + 1);
     if (d.qk_norm) {
@@ -109,8 +117,8 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
     }
     float cs, sn;
     rope_cos_sin(pos, i, d.dr, d.base, &cs, &sn);
-    out[d.dc + 2 * i] = x0 * cs - x1 * sn;
-    out[d.dc + 2 * i + 1] = x0 * sn + x1 * cs;
+    put(d.dc + 2 * i, x0 * cs - x1 * sn);
+    put(d.dc + 2 * i + 1, x0 * sn + x1 * cs);
   }
 }
 
@@ -119,18 +127,27 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
 // k = c W^UK_g and v = c W^UV_g for the workgroup's tokens.  Writes the raw
 // key (for the backward), the normalised key with the normalised, rotated
 // RoPE key after it, the value, and the inverse RMS values.
-template <typename T>
+// MF: write the bf16 operands of the MFMA attention instead, key-major per
+// group: Kb [B][G][T][d_qk], Vb [B][G][T][d_v].
+template <typename T, bool MF>
 __global__ __launch_bounds__(256) void prep_kv_kernel(
     TrainDims d, int n_rows, const T* __restrict__ c, const T* __restrict__ k_rope,
     const float* __restrict__ w_uk, const T* __restrict__ w_uv, const float* __restrict__ gk,
     const float* __restrict__ gkr, float* __restrict__ Kh, float* __restrict__ Kraw,
-    float* __restrict__ V, float* __restrict__ ak, float* __restrict__ akr) {
+    float* __restrict__ V, uint16_t* __restrict__ Kb, uint16_t* __restrict__ Vb,
+    float* __restrict__ ak, float* __restrict__ akr) {
   extern __shared__ float lds[];  // c rows [kKvTok][r], then kKvTok * 8 reduction slots
   float* cs = lds;
   float* red = lds + kKvTok * d.r;
   const size_t row0 = (size_t)blockIdx.x * kKvTok;
   const int g = blockIdx.y, tid = threadIdx.x;
   const int ntok = (int)min((size_t)kKvTok, (size_t)n_rows - row0);
+  // row-major index of (row, g) in the MFMA operands' key-major layout
+  auto kmaj = [&](size_t row) { return ((row / d.T) * d.G + g) * d.T + row % d.T; };
+  auto put_k = [&](size_t row, int e, float v) {
+    if constexpr (MF) Kb[kmaj(row) * d.dqk + e] = f32_to_bf16(v);
+    else Kh[(row * d.G + g) * d.dqk + e] = v;
+  };
   for (int i = tid; i < kKvTok * d.r; i += 256) {
     const int tk = i / d.r, e = i % d.r;
     cs[i] = tk < ntok ? Elem<T>::load(c, (row0 + tk) * d.r + e) : 0.f;
@@ -174,8 +191,11 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(
       for (int t = 0; t < kKvTok; ++t) acc[t] += cs[t * d.r + i] * w;
     }
 #pragma unroll
-    for (int t = 0; t < kKvTok; ++t)
-      if (t < ntok) V[((row0 + t) * d.G + g) * d.dv + e] = acc[t];
+    for (int t = 0; t < kKvTok; ++t) {
+      if (t >= ntok) continue;
+      if constexpr (MF) Vb[kmaj(row0 + t) * d.dv + e] = f32_to_bf16(acc[t]);
+      else V[((row0 + t) * d.G + g) * d.dv + e] = acc[t];
+    }
   }
   __syncthreads();
   // normalised content key (reads back this thread's own raw values)
@@ -187,7 +207,7 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(
                         : 1.f;
     if (tid == 0 && d.qk_norm) ak[kg] = a;
     for (int e = tid; e < d.dc; e += 256)
-      Kh[kg * d.dqk + e] = Kraw[kg * d.dc + e] * (d.qk_norm ? gk[e] * a : 1.f);
+      put_k(row0 + t, e, Kraw[kg * d.dc + e] * (d.qk_norm ? gk[e] * a : 1.f));
   }
   // RoPE key: wave w handles tokens w, w + 4, ...
   const int wave = tid >> 6, lane = tid & 63;
@@ -205,7 +225,6 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(
       ar = 1.0f / sqrtf(wave_sum(s) / (float)d.dr + d.eps);
       if (g == 0 && lane == 0) akr[row] = ar;
     }
-    float* out = Kh + (row * d.G + g) * d.dqk + d.dc;
     for (int i = lane; i < d.dr / 2; i += 64) {
       float x0 = Elem<T>::load(kr, 2 * i), x1 = Elem<T>::load(kr, 2 * i + 1);
       if (d.qk_norm) {
@@ -214,8 +233,8 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(
       }
       float c0, s0;
       rope_cos_sin(pos, i, d.dr, d.base, &c0, &s0);
-      out[2 * i] = x0 * c0 - x1 * s0;
-      out[2 * i + 1] = x0 * s0 + x1 * c0;
+      put_k(row, d.dc + 2 * i, x0 * c0 - x1 * s0);
+      put_k(row, d.dc + 2 * i + 1, x0 * s0 + x1 * c0);
     }
   }
 }
@@ -672,6 +691,10 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
   w.aqr = take(BT * c.H * 4);
   w.ak = take(BT * c.G * 4);
   w.akr = take(BT * 4);
+  const bool mf = train_mfma_shape(c);
+  w.Qb = take(mf ? BT * c.H * dqk * 2 : 0);
+  w.Kb = take(mf ? BT * c.G * dqk * 2 : 0);
+  w.Vb = take(mf ? BT * c.G * c.dv * 2 : 0);
   w.fwd_total = off;
   w.dQh = take(BT * c.H * dqk * 4);
   w.dKh = take(BT * c.G * dqk * 4);
@@ -680,25 +703,40 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
   w.dK = take(BT * c.G * c.dc * 4);
   w.dKr = take(BT * c.dr * 4);
   w.gamma_partial = take((size_t)kGammaSplit * (c.dc > c.dr ? c.dc : c.dr) * 4);
+  w.dOb = take(mf ? BT * c.H * c.dv * 2 : 0);
+  w.stat = take(mf ? BT * c.H * 8 : 0);
   w.total = off;
   return w;
 }
 
 #define WS(type, field) ((type*)(wsb + ws.field))
 
+// Normalised, rotated queries and keys, values and the inverse RMS values:
+// fp32 for the row-parallel kernels, or (MF) the bf16 MFMA operands.
+template <typename T, bool MF>
+static void launch_prep(const TrainDims& d, const TrainPtrs& in, const TrainWs& ws, char* wsb,
+                        hipStream_t s) {
+  const int n_rows = d.B * d.T;
+  hipLaunchKernelGGL((prep_q_kernel<T, MF>), dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
+                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
+                     WS(float, Qh), WS(uint16_t, Qb), WS(float, aq), WS(float, aqr));
+  hipLaunchKernelGGL((prep_kv_kernel<T, MF>), dim3((n_rows + kKvTok - 1) / kKvTok, d.G),
+                     dim3(256), (kKvTok * d.r + kKvTok * 4) * sizeof(float), s, d, n_rows,
+                     (const T*)in.c, (const T*)in.k_rope, in.w_uk, (const T*)in.w_uv, in.gamma_k,
+                     in.gamma_k_rope, WS(float, Kh), WS(float, Kraw), WS(float, V),
+                     WS(uint16_t, Kb), WS(uint16_t, Vb), WS(float, ak), WS(float, akr));
+}
+
 template <typename T>
 static hipError_t forward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in, const TrainWs& ws,
                                char* wsb, float* o, float* lse, hipStream_t s) {
   const TrainDims d = dims_of(c, B, T_);
-  const int n_rows = B * T_;
-  hipLaunchKernelGGL(prep_q_kernel<T>, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
-                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
-                     WS(float, Qh), WS(float, aq), WS(float, aqr));
-  hipLaunchKernelGGL(prep_kv_kernel<T>, dim3((n_rows + kKvTok - 1) / kKvTok, d.G), dim3(256),
-                     (kKvTok * d.r + kKvTok * 4) * sizeof(float), s, d, n_rows, (const T*)in.c,
-                     (const T*)in.k_rope, in.w_uk, (const T*)in.w_uv, in.gamma_k, in.gamma_k_rope,
-                     WS(float, Kh), WS(float, Kraw), WS(float, V), WS(float, ak), WS(float, akr));
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(n_rows, d.H), dim3(256),
+  if (train_mfma_shape(c)) {
+    launch_prep<T, true>(d, in, ws, wsb, s);
+    return launch_flash_fwd(c, B, T_, wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o, lse, s);
+  }
+  launch_prep<T, false>(d, in, ws, wsb, s);
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(B * T_, d.H), dim3(256),
                      (d.dqk + kChunk + 4) * sizeof(float), s, d, WS(const float, Qh),
                      WS(const float, Kh), WS(const float, V), o, lse);
   return hipGetLastError();
@@ -711,21 +749,23 @@ static hipError_t backward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in
                                 hipStream_t s) {
   const TrainDims d = dims_of(c, B, T_);
   const int n_rows = B * T_;
-  hipLaunchKernelGGL(prep_q_kernel<T>, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
-                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
-                     WS(float, Qh), WS(float, aq), WS(float, aqr));
-  hipLaunchKernelGGL(prep_kv_kernel<T>, dim3((n_rows + kKvTok - 1) / kKvTok, d.G), dim3(256),
-                     (kKvTok * d.r + kKvTok * 4) * sizeof(float), s, d, n_rows, (const T*)in.c,
-                     (const T*)in.k_rope, in.w_uk, (const T*)in.w_uv, in.gamma_k, in.gamma_k_rope,
-                     WS(float, Kh), WS(float, Kraw), WS(float, V), WS(float, ak), WS(float, akr));
-  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3(n_rows, d.H), dim3(256),
-                     (d.dqk + d.dv + kChunk + 4) * sizeof(float), s, d, WS(const float, Qh),
-                     WS(const float, Kh), WS(const float, V), o, lse, d_o, WS(float, dQh),
-                     WS(float, Dsum));
-  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(n_rows, d.G), dim3(256),
-                     (d.dqk + d.dv + 2 * kChunk) * sizeof(float), s, d, WS(const float, Qh),
-                     WS(const float, Kh), WS(const float, V), lse, d_o, WS(const float, Dsum),
-                     WS(float, dKh), WS(float, dV));
+  if (train_mfma_shape(c)) {
+    launch_prep<T, true>(d, in, ws, wsb, s);
+    const hipError_t e = launch_flash_bwd(c, B, T_, wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o, lse,
+                                          d_o, wsb + ws.dOb, wsb + ws.stat, WS(float, dKh),
+                                          WS(float, dV), WS(float, dQh), s);
+    if (e != hipSuccess) return e;
+  } else {
+    launch_prep<T, false>(d, in, ws, wsb, s);
+    hipLaunchKernelGGL(attn_bwd_q_kernel, dim3(n_rows, d.H), dim3(256),
+                       (d.dqk + d.dv + kChunk + 4) * sizeof(float), s, d, WS(const float, Qh),
+                       WS(const float, Kh), WS(const float, V), o, lse, d_o, WS(float, dQh),
+                       WS(float, Dsum));
+    hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(n_rows, d.G), dim3(256),
+                       (d.dqk + d.dv + 2 * kChunk) * sizeof(float), s, d, WS(const float, Qh),
+                       WS(const float, Kh), WS(const float, V), lse, d_o, WS(const float, Dsum),
+                       WS(float, dKh), WS(float, dV));
+  }
   hipLaunchKernelGGL(q_norm_bwd_kernel<T>, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
                      (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
                      WS(const float, aq), WS(const float, aqr), WS(float, dQh), gr.d_q_c,

@@ -214,6 +214,13 @@ def _(w, i):
     w.sset(i.ops[0], (sext32(a) * sext32(b)) & M32)
 
 
+@h("s_mulk_i32")
+def _(w, i):
+    k = i.ops[1].ival & 0xFFFF
+    k = k - 0x10000 if k & 0x8000 else k
+    w.sset(i.ops[0], (sext32(w.sget(i.ops[0])) * k) & M32)
+
+
 @h("s_mul_hi_u32")
 def _(w, i):
     a, b = _s2(w, i)
@@ -637,6 +644,11 @@ _V = {
     "v_mul_lo_u32": (lambda a, b: a * b, 2),
     "v_mul_hi_u32": (lambda a, b: (a * b) >> U64(32), 2),
     "v_mul_u32_u24": (lambda a, b: (a & U64(0xFFFFFF)) * (b & U64(0xFFFFFF)), 2),
+    # 16-bit integer ops (gfx9 family): low halves in, the high half of the
+    # destination zeroed
+    "v_mul_lo_u16": (lambda a, b: ((a & U64(0xFFFF)) * (b & U64(0xFFFF))) & U64(0xFFFF), 2),
+    "v_add_u16": (lambda a, b: ((a & U64(0xFFFF)) + (b & U64(0xFFFF))) & U64(0xFFFF), 2),
+    "v_sub_u16": (lambda a, b: ((a & U64(0xFFFF)) - (b & U64(0xFFFF))) & U64(0xFFFF), 2),
     "v_mad_u32_u24": (lambda a, b, c: (a & U64(0xFFFFFF)) * (b & U64(0xFFFFFF)) + c, 3),
     "v_min_u32": (lambda a, b: np.minimum(a, b), 2),
     "v_max_u32": (lambda a, b: np.maximum(a, b), 2),

@@ -2,11 +2,15 @@
 qkmla_train_backward through the C ABI) against the fp64 oracle's forward and
 autograd backward.
 
-All device arithmetic is fp32; bf16 storage only rounds the inputs, and the
-oracle is given the same rounded values.  Bounds: o per (token, head) row
-2e-5 relative to its largest element, lse 2e-5 relative (at least 1), every
-gradient tensor 1e-4 of its largest element (fp32 sums of up to a few
-thousand terms against fp64)."""
+Row-parallel path (any shape): all device arithmetic is fp32; bf16 storage
+only rounds the inputs, and the oracle is given the same rounded values.
+Bounds: o per (token, head) row 2e-5 relative to its largest element, lse
+2e-5 relative (at least 1), every gradient tensor 1e-4 of its largest element
+(fp32 sums of up to a few thousand terms against fp64).
+MFMA path (the bf16 layer with 16 heads per group, d_c + d_r = 192,
+d_v = 128): normalised queries and keys, values, softmax weights, dS and d_o
+are rounded to bf16 (2^-9 relative), so o is held to 2e-2, lse to 5e-2
+(absolute) and every gradient to 2e-2 of its largest element."""
 import numpy as np
 import pytest
 import torch
@@ -23,7 +27,11 @@ NAMES = ("c", "q_c", "q_rope", "k_rope", "w_uk", "w_uv", "gamma_q", "gamma_k", "
          "gamma_k_rope")
 
 
-def _run(shape, B, T, seed, qk_norm=True, ref_rows=None):
+FP32_TOL = dict(o=2e-5, lse=2e-5, grad=1e-4)
+BF16_TOL = dict(o=2e-2, lse=5e-2, grad=2e-2)
+
+
+def _run(shape, B, T, seed, qk_norm=True, tol=FP32_TOL):
     import oracle
     from oracle.qkmla_train_oracle import train_reference
     print(f"\n[train {shape} B={B} T={T} qk_norm={qk_norm}]", flush=True)
@@ -44,6 +52,8 @@ def _run(shape, B, T, seed, qk_norm=True, ref_rows=None):
                                             ref["o"].reshape(-1, dv)))
     lse_np = lse.cpu().numpy()
     err_l = worst_of(np.abs(lse_np - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"])))
+    if tol is BF16_TOL:
+        err_l = worst_of(np.abs(lse_np - ref["lse"]))
     errs = {}
     for n in NAMES:
         r_ = ref["d_" + n]
@@ -51,9 +61,9 @@ def _run(shape, B, T, seed, qk_norm=True, ref_rows=None):
         errs[n] = worst_of(np.abs(grads["d_" + n].cpu().numpy() - r_)) / scale
     print(f"  o {err_o:.2e} lse {err_l:.2e} " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()),
           flush=True)
-    assert err_o <= 2e-5 and err_l <= 2e-5
+    assert err_o <= tol["o"] and err_l <= tol["lse"], (err_o, err_l)
     for n, e in errs.items():
-        assert e <= 1e-4, (n, e)
+        assert e <= tol["grad"], (n, e)
 
 
 @pytest.mark.parametrize("qk_norm", [True, False])
@@ -69,7 +79,57 @@ def test_train_sequences_longer_than_a_chunk():
     _run(Shape(4, 2, 32, 16, 8, 16, "f32"), 2, 600, 702)
 
 
-def test_train_deepseek_like_layer():
+@pytest.mark.parametrize("B,T,qk_norm", [(2, 96, True), (1, 300, True), (2, 77, False)])
+def test_train_deepseek_like_layer_mfma(B, T, qk_norm):
     """The DeepSeek-V3-like layer (H=128, G=8, r=512, d_c=128, d_r=64,
-    d_v=128) in bf16 storage, two sequences of 96 tokens."""
-    _run(DSV3, 2, 96, 703)
+    d_v=128) in bf16 storage, on the MFMA attention: whole and partial key
+    tiles and query blocks."""
+    _run(DSV3, B, T, 703 + T, qk_norm=qk_norm, tol=BF16_TOL)
+
+
+def test_train_full_length_sampled_and_invariants():
+    """2048 tokens of the bf16 layer: sampled forward rows against the decode
+    oracle over their prefix (a training row is a decode step), and the
+    backward against properties that hold at any size: the RMSNorm scale
+    invariance makes each gradient row of q_c, q_rope and k_rope, and each
+    group's W^UK gradient, orthogonal to its input (up to eps = 1e-6)."""
+    import oracle
+    B, T = 1, 2048
+    cfg = ops.Config.from_shape(DSV3)
+    inp = train_inputs(DSV3, B, T, 720)
+    d_o = inp.pop("d_o")
+    dt = cfg.torch_dtype
+    dev = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).to(
+        "cuda", torch.float32 if (n == "w_uk" or n.startswith("gamma")) else dt) for n in NAMES}
+    ws = torch.empty((ops.train_workspace_size(cfg, B, T),), dtype=torch.uint8, device="cuda")
+    print(f"\n[train full length T={T}]", flush=True)
+    o, lse = ops.train_forward(cfg, dev, ws)
+    grads = ops.train_backward(cfg, dev, o, lse, torch.from_numpy(d_o).cuda(), ws)
+    torch.cuda.synchronize()
+    o_np, lse_np = o.cpu().numpy(), lse.cpu().numpy()
+    G, hpg = DSV3.n_groups, DSV3.n_heads // DSV3.n_groups
+    for i, g in ((0, 0), (777, 3), (T - 1, 7)):
+        ref = oracle.explicit_decode(inp["q_c"][:, i], inp["q_rope"][:, i],
+                                     [inp["c"][0, :i + 1]], [inp["k_rope"][0, :i + 1]],
+                                     inp["w_uk"], inp["w_uv"], inp["gamma_q"], inp["gamma_k"],
+                                     inp["gamma_q_rope"], inp["gamma_k_rope"], groups=[g])
+        hs = list(range(g * hpg, (g + 1) * hpg))
+        e = worst_of(oracle.rowwise_rel_err(o_np[0, i, hs], ref["o"][0, hs]))
+        el = worst_of(np.abs(lse_np[0, i, hs] - ref["lse"][0, hs]))
+        print(f"  row {i} group {g}: o {e:.2e} lse {el:.2e}", flush=True)
+        assert e <= BF16_TOL["o"] and el <= BF16_TOL["lse"]
+    def cos(a, b, axes):
+        num = np.abs(np.sum(a * b, axis=axes))
+        den = np.sqrt(np.sum(a * a, axis=axes) * np.sum(b * b, axis=axes)) + 1e-30
+        return float(np.max(num / den))
+    g_np = {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
+    worst = {"q_c": cos(g_np["d_q_c"], inp["q_c"].astype(np.float64), -1),
+             "q_rope": cos(g_np["d_q_rope"], inp["q_rope"].astype(np.float64), -1),
+             "k_rope": cos(g_np["d_k_rope"], inp["k_rope"].astype(np.float64), -1),
+             "w_uk": cos(g_np["d_w_uk"], inp["w_uk"].astype(np.float64), (1, 2))}
+    print("  |cos(grad, input)| " + " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
+    # the RMSNorm backward makes these exact up to fp32 rounding, whatever
+    # the accuracy of the attention gradient that enters it
+    for k, v in worst.items():
+        assert v <= 1e-3, (k, v)
+    assert all(np.isfinite(v).all() for v in g_np.values())

@@ -84,16 +84,16 @@ __global__ __launch_bounds__(256) void flash_fwd_kernel(FaArgs a) {
 
   // tile loads: K 768 chunks (3 per thread), V 512 (2 per thread); rows past
   // the sequence repeat its last row (masked below)
-  uint4 kr[3], vr[2];
+  uint4 kr[kKChunks / 256], vr[kVChunks / 256];
   auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+    for (int u = 0; u < kKChunks / 256; ++u) {
       const int c = tid + 256 * u, row = c / 24, col = c % 24;
       const int key = min(kt * kFaKeys + row, a.T - 1);
       kr[u] = load16(kbase + (size_t)key * kFaDqk + col * 8);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kVChunks / 256; ++u) {
       const int c = tid + 256 * u, row = c / 16, col = c % 16;
       const int key = min(kt * kFaKeys + row, a.T - 1);
       vr[u] = load16(vbase + (size_t)key * kFaDv + col * 8);

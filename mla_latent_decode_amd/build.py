@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "absorb_append.hip", "qprep.hip", "decode_mfma.hip",
            "decode_generic.hip", "merge_outproj.hip", "train.hip",
-           "train_mfma.hip"]
+           "train_mfma.hip", "gemm_mfma.hip"]
 
 # -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_*_f32).
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

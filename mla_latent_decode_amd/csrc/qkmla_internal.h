@@ -99,6 +99,8 @@ struct TrainWs {
   size_t Qh, Kh, V, Kraw, aq, aqr, ak, akr, Qb, Kb, Vb, fwd_total;
   size_t dQh, dKh, dV, Dsum, dK, dKr, gamma_partial;
   size_t dOb, stat;  // MFMA backward: d_o bf16 [BT][H][d_v], (lse*log2 e, D) [BT][H]
+  size_t Wk16;       // MFMA path: W^UK in bf16 [G][r][d_c]
+  size_t dKb, dVb;   // MFMA backward: dk, dV in bf16 [BT][G][d_c], [BT][G][d_v]
   size_t total;
 };
 TrainWs train_ws_layout(const Cfg& c, int B, int T);
@@ -113,6 +115,28 @@ hipError_t launch_flash_bwd(const Cfg& c, int B, int T, const void* Qb, const vo
                             const void* Vb, const float* o, const float* lse, const float* d_o,
                             void* dOb, void* stat, float* dKh, float* dV, float* dQh,
                             hipStream_t s);
+
+// ---- bf16 MFMA GEMM (training projections) --------------------------------------
+// Operand element (mn, k) of batch z sits at p + z*batch_stride +
+//   K-contiguous:  mn*ld + (k / kgrp)*kgrp_stride + k % kgrp  (kgrp a multiple of 8)
+//   MN-contiguous: k*ld + mn                                  (ld, MN multiples of 8)
+struct GemmOperand {
+  const uint16_t* p;
+  int64_t ld;
+  int kgrp;
+  int64_t kgrp_stride;
+  int64_t batch_stride;
+};
+// C[z][m][n] = (C[z][m][n] if accumulate) + sum_k A[z][m][k] B[z][k][n], fp32 C at
+// C + z*c_batch_stride + m*ldc + n.
+struct GemmArgs {
+  GemmOperand A, B;
+  float* C;
+  int64_t ldc, c_batch_stride;
+  int M, N, K;
+  int accumulate;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& g, bool a_kc, bool b_kc, int batch, hipStream_t s);
 
 // ---- launchers (each enqueues on `stream`; returns the launch error) -------
 hipError_t launch_absorb(const Cfg& c, const float* w_uk, const float* gq, const float* gk,

@@ -127,27 +127,19 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
 // k = c W^UK_g and v = c W^UV_g for the workgroup's tokens.  Writes the raw
 // key (for the backward), the normalised key with the normalised, rotated
 // RoPE key after it, the value, and the inverse RMS values.
-// MF: write the bf16 operands of the MFMA attention instead, key-major per
-// group: Kb [B][G][T][d_qk], Vb [B][G][T][d_v].
-template <typename T, bool MF>
+template <typename T>
 __global__ __launch_bounds__(256) void prep_kv_kernel(
     TrainDims d, int n_rows, const T* __restrict__ c, const T* __restrict__ k_rope,
     const float* __restrict__ w_uk, const T* __restrict__ w_uv, const float* __restrict__ gk,
     const float* __restrict__ gkr, float* __restrict__ Kh, float* __restrict__ Kraw,
-    float* __restrict__ V, uint16_t* __restrict__ Kb, uint16_t* __restrict__ Vb,
-    float* __restrict__ ak, float* __restrict__ akr) {
+    float* __restrict__ V, float* __restrict__ ak, float* __restrict__ akr) {
   extern __shared__ float lds[];  // c rows [kKvTok][r], then kKvTok * 8 reduction slots
   float* cs = lds;
   float* red = lds + kKvTok * d.r;
   const size_t row0 = (size_t)blockIdx.x * kKvTok;
   const int g = blockIdx.y, tid = threadIdx.x;
   const int ntok = (int)min((size_t)kKvTok, (size_t)n_rows - row0);
-  // row-major index of (row, g) in the MFMA operands' key-major layout
-  auto kmaj = [&](size_t row) { return ((row / d.T) * d.G + g) * d.T + row % d.T; };
-  auto put_k = [&](size_t row, int e, float v) {
-    if constexpr (MF) Kb[kmaj(row) * d.dqk + e] = f32_to_bf16(v);
-    else Kh[(row * d.G + g) * d.dqk + e] = v;
-  };
+  auto put_k = [&](size_t row, int e, float v) { Kh[(row * d.G + g) * d.dqk + e] = v; };
   for (int i = tid; i < kKvTok * d.r; i += 256) {
     const int tk = i / d.r, e = i % d.r;
     cs[i] = tk < ntok ? Elem<T>::load(c, (row0 + tk) * d.r + e) : 0.f;
@@ -191,11 +183,8 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(
       for (int t = 0; t < kKvTok; ++t) acc[t] += cs[t * d.r + i] * w;
     }
 #pragma unroll
-    for (int t = 0; t < kKvTok; ++t) {
-      if (t >= ntok) continue;
-      if constexpr (MF) Vb[kmaj(row0 + t) * d.dv + e] = f32_to_bf16(acc[t]);
-      else V[((row0 + t) * d.G + g) * d.dv + e] = acc[t];
-    }
+    for (int t = 0; t < kKvTok; ++t)
+      if (t < ntok) V[((row0 + t) * d.G + g) * d.dv + e] = acc[t];
   }
   __syncthreads();
   // normalised content key (reads back this thread's own raw values)
@@ -671,6 +660,83 @@ __global__ __launch_bounds__(256) void gamma_final_kernel(int n, const float* pa
   out[col] = s;
 }
 
+// ---- MFMA path: keys and values from the GEMM results ------------------------------
+// One workgroup per token row: the RMSNorm of each group's raw key (wave per
+// group), the normalised, rotated RoPE key (computed once, written into every
+// group's row), and the values, all to the bf16 key-major operands.
+__global__ __launch_bounds__(256) void kv_norm_kernel(
+    TrainDims d, const uint16_t* __restrict__ k_rope, const float* __restrict__ gk,
+    const float* __restrict__ gkr, const float* __restrict__ Kraw, const float* __restrict__ V,
+    uint16_t* __restrict__ Kb, uint16_t* __restrict__ Vb, float* __restrict__ ak,
+    float* __restrict__ akr) {
+  const size_t row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t b = row / d.T, t = row % d.T;
+  auto kmaj = [&](int g) { return ((b * d.G + g) * d.T + t); };
+  for (int g = wave; g < d.G; g += 4) {
+    const float* x = Kraw + (row * d.G + g) * d.dc;
+    float a = 1.f;
+    if (d.qk_norm) {
+      float ss = 0.f;
+      for (int e = lane; e < d.dc; e += 64) ss += x[e] * x[e];
+      a = 1.0f / sqrtf(wave_sum(ss) / (float)d.dc + d.eps);
+      if (lane == 0) ak[row * d.G + g] = a;
+    }
+    uint16_t* out = Kb + kmaj(g) * d.dqk;
+    for (int e = lane; e < d.dc; e += 64) out[e] = f32_to_bf16(x[e] * (d.qk_norm ? gk[e] * a : 1.f));
+  }
+  for (int e = tid; e < d.G * d.dv; e += 256) {
+    const int g = e / d.dv, v = e % d.dv;
+    Vb[kmaj(g) * d.dv + v] = f32_to_bf16(V[row * d.G * d.dv + e]);
+  }
+  if (wave != 0) return;
+  const uint16_t* kr = k_rope + row * d.dr;
+  float ar = 1.f;
+  if (d.qk_norm) {
+    float s = 0.f;
+    for (int e = lane; e < d.dr; e += 64) {
+      const float v = bf16_to_f32(kr[e]);
+      s += v * v;
+    }
+    ar = 1.0f / sqrtf(wave_sum(s) / (float)d.dr + d.eps);
+    if (lane == 0) akr[row] = ar;
+  }
+  for (int i = lane; i < d.dr / 2; i += 64) {
+    float x0 = bf16_to_f32(kr[2 * i]), x1 = bf16_to_f32(kr[2 * i + 1]);
+    if (d.qk_norm) {
+      x0 *= gkr[2 * i] * ar;
+      x1 *= gkr[2 * i + 1] * ar;
+    }
+    float c0, s0;
+    rope_cos_sin((int)t, i, d.dr, d.base, &c0, &s0);
+    const uint16_t y0 = f32_to_bf16(x0 * c0 - x1 * s0), y1 = f32_to_bf16(x0 * s0 + x1 * c0);
+    for (int g = 0; g < d.G; ++g) {
+      uint16_t* out = Kb + kmaj(g) * d.dqk + d.dc;
+      out[2 * i] = y0;
+      out[2 * i + 1] = y1;
+    }
+  }
+}
+
+// fp32 -> bf16 (round to nearest even); with `lo`, also the rounding
+// remainder in bf16, so that hi + lo carries about 16 bits of the value.
+__global__ __launch_bounds__(256) void to_bf16_kernel(size_t n, const float* __restrict__ src,
+                                                      uint16_t* __restrict__ hi,
+                                                      uint16_t* __restrict__ lo) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const uint16_t h = f32_to_bf16(src[i]);
+    hi[i] = h;
+    if (lo) lo[i] = f32_to_bf16(src[i] - bf16_to_f32(h));
+  }
+}
+
+hipError_t launch_to_bf16(size_t n, const float* src, void* hi, void* lo, hipStream_t s) {
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                     0, s, n, src, (uint16_t*)hi, (uint16_t*)lo);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // ---- workspace ------------------------------------------------------------------------
@@ -683,18 +749,19 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
     off = (off + bytes + 255) & ~(size_t)255;
     return at;
   };
-  w.Qh = take(BT * c.H * dqk * 4);
-  w.Kh = take(BT * c.G * dqk * 4);
+  const bool mf = train_mfma_shape(c);
+  w.Qh = take(mf ? 0 : BT * c.H * dqk * 4);  // the MFMA path keeps bf16 operands instead
+  w.Kh = take(mf ? 0 : BT * c.G * dqk * 4);
   w.V = take(BT * c.G * c.dv * 4);
   w.Kraw = take(BT * c.G * c.dc * 4);
   w.aq = take(BT * c.H * 4);
   w.aqr = take(BT * c.H * 4);
   w.ak = take(BT * c.G * 4);
   w.akr = take(BT * 4);
-  const bool mf = train_mfma_shape(c);
   w.Qb = take(mf ? BT * c.H * dqk * 2 : 0);
   w.Kb = take(mf ? BT * c.G * dqk * 2 : 0);
   w.Vb = take(mf ? BT * c.G * c.dv * 2 : 0);
+  w.Wk16 = take(mf ? (size_t)c.G * c.r * c.dc * 2 * 2 : 0);  // bf16 hi, then lo
   w.fwd_total = off;
   w.dQh = take(BT * c.H * dqk * 4);
   w.dKh = take(BT * c.G * dqk * 4);
@@ -705,26 +772,104 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
   w.gamma_partial = take((size_t)kGammaSplit * (c.dc > c.dr ? c.dc : c.dr) * 4);
   w.dOb = take(mf ? BT * c.H * c.dv * 2 : 0);
   w.stat = take(mf ? BT * c.H * 8 : 0);
+  w.dKb = take(mf ? BT * c.G * c.dc * 2 : 0);
+  w.dVb = take(mf ? BT * c.G * c.dv * 2 : 0);
   w.total = off;
   return w;
 }
 
 #define WS(type, field) ((type*)(wsb + ws.field))
 
-// Normalised, rotated queries and keys, values and the inverse RMS values:
-// fp32 for the row-parallel kernels, or (MF) the bf16 MFMA operands.
+// Normalised, rotated queries: fp32 for the row-parallel kernels, or (MF) the
+// bf16 operand of the MFMA attention.
 template <typename T, bool MF>
+static void launch_prep_q(const TrainDims& d, const TrainPtrs& in, const TrainWs& ws, char* wsb,
+                          hipStream_t s) {
+  hipLaunchKernelGGL((prep_q_kernel<T, MF>), dim3(d.B * d.T, (d.H + 3) / 4), dim3(256), 0, s, d,
+                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
+                     WS(float, Qh), WS(uint16_t, Qb), WS(float, aq), WS(float, aqr));
+}
+
+// Row-parallel path: fp32 normalised, rotated queries and keys, values and
+// the inverse RMS values.
+template <typename T>
 static void launch_prep(const TrainDims& d, const TrainPtrs& in, const TrainWs& ws, char* wsb,
                         hipStream_t s) {
   const int n_rows = d.B * d.T;
-  hipLaunchKernelGGL((prep_q_kernel<T, MF>), dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
-                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
-                     WS(float, Qh), WS(uint16_t, Qb), WS(float, aq), WS(float, aqr));
-  hipLaunchKernelGGL((prep_kv_kernel<T, MF>), dim3((n_rows + kKvTok - 1) / kKvTok, d.G),
-                     dim3(256), (kKvTok * d.r + kKvTok * 4) * sizeof(float), s, d, n_rows,
-                     (const T*)in.c, (const T*)in.k_rope, in.w_uk, (const T*)in.w_uv, in.gamma_k,
-                     in.gamma_k_rope, WS(float, Kh), WS(float, Kraw), WS(float, V),
+  launch_prep_q<T, false>(d, in, ws, wsb, s);
+  hipLaunchKernelGGL((prep_kv_kernel<T>), dim3((n_rows + kKvTok - 1) / kKvTok, d.G), dim3(256),
+                     (kKvTok * d.r + kKvTok * 4) * sizeof(float), s, d, n_rows, (const T*)in.c,
+                     (const T*)in.k_rope, in.w_uk, (const T*)in.w_uv, in.gamma_k, in.gamma_k_rope,
+                     WS(float, Kh), WS(float, Kraw), WS(float, V), WS(float, ak), WS(float, akr));
+}
+
+// MFMA path (bf16 layer): Q^ from prep_q; k = c W^UK_g and v = c W^UV_g as
+// batched GEMMs (batch = group) into Kraw and V, then kv_norm_kernel forms
+// the bf16 key-major operands.
+static hipError_t mfma_prep(const Cfg& c, const TrainDims& d, const TrainPtrs& in,
+                            const TrainWs& ws, char* wsb, hipStream_t s) {
+  const int BT = d.B * d.T;
+  launch_prep_q<uint16_t, true>(d, in, ws, wsb, s);
+  // W^UK in bf16 hi and lo: c is exact in bf16, so k = c W_hi + c W_lo keeps
+  // the key (and its RMS) close to fp32
+  const size_t nw = (size_t)d.G * d.r * d.dc;
+  const uint16_t* w_hi = WS(const uint16_t, Wk16);
+  hipError_t e = launch_to_bf16(nw, in.w_uk, wsb + ws.Wk16, wsb + ws.Wk16 + nw * 2, s);
+  if (e != hipSuccess) return e;
+  const GemmOperand A{(const uint16_t*)in.c, d.r, 1 << 30, 0, 0};  // c [BT][r], K-contiguous
+  GemmArgs g{A, GemmOperand{w_hi, d.dc, 1 << 30, 0, (int64_t)d.r * d.dc}, WS(float, Kraw),
+             (int64_t)d.G * d.dc, d.dc, BT, d.dc, d.r, 0};
+  if ((e = launch_gemm_bf16(g, true, false, d.G, s)) != hipSuccess) return e;
+  g.B.p = w_hi + nw;
+  g.accumulate = 1;
+  if ((e = launch_gemm_bf16(g, true, false, d.G, s)) != hipSuccess) return e;
+  g.accumulate = 0;
+  g.B = GemmOperand{(const uint16_t*)in.w_uv, d.dv, 1 << 30, 0, (int64_t)d.r * d.dv};
+  g.C = WS(float, V);
+  g.ldc = (int64_t)d.G * d.dv;
+  g.c_batch_stride = d.dv;
+  g.N = d.dv;
+  if ((e = launch_gemm_bf16(g, true, false, d.G, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(kv_norm_kernel, dim3(BT), dim3(256), 0, s, d, (const uint16_t*)in.k_rope,
+                     in.gamma_k, in.gamma_k_rope, WS(const float, Kraw), WS(const float, V),
                      WS(uint16_t, Kb), WS(uint16_t, Vb), WS(float, ak), WS(float, akr));
+  (void)c;
+  return hipGetLastError();
+}
+
+// MFMA path: dc = dk W^UK^T + dV W^UV^T (K runs over (group, dim)) and
+// dW_g = c^T dY_g, from bf16 copies of dk and dV.
+static hipError_t mfma_projection_grads(const TrainDims& d, const TrainPtrs& in,
+                                        const TrainWs& ws, char* wsb, const TrainGrads& gr,
+                                        hipStream_t s) {
+  const int BT = d.B * d.T;
+  hipError_t e =
+      launch_to_bf16((size_t)BT * d.G * d.dc, WS(const float, dK), wsb + ws.dKb, nullptr, s);
+  if (e != hipSuccess) return e;
+  if ((e = launch_to_bf16((size_t)BT * d.G * d.dv, WS(const float, dV), wsb + ws.dVb, nullptr,
+                          s)) != hipSuccess)
+    return e;
+  // latent gradient: A = dk [BT][G*dc] (K-contiguous), B(k=(g,j), n=i) = W^UK[g][i][j]
+  GemmArgs g{GemmOperand{WS(const uint16_t, dKb), (int64_t)d.G * d.dc, 1 << 30, 0, 0},
+             GemmOperand{WS(const uint16_t, Wk16), d.dc, d.dc, (int64_t)d.r * d.dc, 0},
+             gr.d_c, d.r, 0, BT, d.r, d.G * d.dc, 0};
+  if ((e = launch_gemm_bf16(g, true, true, 1, s)) != hipSuccess) return e;
+  g.A = GemmOperand{WS(const uint16_t, dVb), (int64_t)d.G * d.dv, 1 << 30, 0, 0};
+  g.B = GemmOperand{(const uint16_t*)in.w_uv, d.dv, d.dv, (int64_t)d.r * d.dv, 0};
+  g.K = d.G * d.dv;
+  g.accumulate = 1;
+  if ((e = launch_gemm_bf16(g, true, true, 1, s)) != hipSuccess) return e;
+  // weight gradients, batch = group: A(m=i, k=t) = c[t][i], B(k=t, n=j) = dk[t][g][j]
+  GemmArgs w{GemmOperand{(const uint16_t*)in.c, d.r, 1 << 30, 0, 0},
+             GemmOperand{WS(const uint16_t, dKb), (int64_t)d.G * d.dc, 1 << 30, 0, d.dc},
+             gr.d_w_uk, d.dc, (int64_t)d.r * d.dc, d.r, d.dc, BT, 0};
+  if ((e = launch_gemm_bf16(w, false, false, d.G, s)) != hipSuccess) return e;
+  w.B = GemmOperand{WS(const uint16_t, dVb), (int64_t)d.G * d.dv, 1 << 30, 0, d.dv};
+  w.C = gr.d_w_uv;
+  w.ldc = d.dv;
+  w.c_batch_stride = (int64_t)d.r * d.dv;
+  w.N = d.dv;
+  return launch_gemm_bf16(w, false, false, d.G, s);
 }
 
 template <typename T>
@@ -732,10 +877,11 @@ static hipError_t forward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in,
                                char* wsb, float* o, float* lse, hipStream_t s) {
   const TrainDims d = dims_of(c, B, T_);
   if (train_mfma_shape(c)) {
-    launch_prep<T, true>(d, in, ws, wsb, s);
+    const hipError_t e = mfma_prep(c, d, in, ws, wsb, s);
+    if (e != hipSuccess) return e;
     return launch_flash_fwd(c, B, T_, wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o, lse, s);
   }
-  launch_prep<T, false>(d, in, ws, wsb, s);
+  launch_prep<T>(d, in, ws, wsb, s);
   hipLaunchKernelGGL(attn_fwd_kernel, dim3(B * T_, d.H), dim3(256),
                      (d.dqk + kChunk + 4) * sizeof(float), s, d, WS(const float, Qh),
                      WS(const float, Kh), WS(const float, V), o, lse);
@@ -749,14 +895,16 @@ static hipError_t backward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in
                                 hipStream_t s) {
   const TrainDims d = dims_of(c, B, T_);
   const int n_rows = B * T_;
-  if (train_mfma_shape(c)) {
-    launch_prep<T, true>(d, in, ws, wsb, s);
-    const hipError_t e = launch_flash_bwd(c, B, T_, wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o, lse,
+  const bool mf = train_mfma_shape(c);
+  if (mf) {
+    hipError_t e = mfma_prep(c, d, in, ws, wsb, s);
+    if (e != hipSuccess) return e;
+    e = launch_flash_bwd(c, B, T_, wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o, lse,
                                           d_o, wsb + ws.dOb, wsb + ws.stat, WS(float, dKh),
                                           WS(float, dV), WS(float, dQh), s);
     if (e != hipSuccess) return e;
   } else {
-    launch_prep<T, false>(d, in, ws, wsb, s);
+    launch_prep<T>(d, in, ws, wsb, s);
     hipLaunchKernelGGL(attn_bwd_q_kernel, dim3(n_rows, d.H), dim3(256),
                        (d.dqk + d.dv + kChunk + 4) * sizeof(float), s, d, WS(const float, Qh),
                        WS(const float, Kh), WS(const float, V), o, lse, d_o, WS(float, dQh),
@@ -774,12 +922,17 @@ static hipError_t backward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in
                      in.gamma_k, in.gamma_k_rope, WS(const float, Kraw), WS(const float, ak),
                      WS(const float, akr), WS(const float, dKh), WS(float, dK), WS(float, dKr),
                      gr.d_k_rope);
-  hipLaunchKernelGGL(latent_bwd_kernel<T>, dim3((n_rows + kLatTok - 1) / kLatTok), dim3(256),
-                     (size_t)kLatTok * (d.dc + d.dv) * sizeof(float), s, d, n_rows, in.w_uk,
-                     (const T*)in.w_uv, WS(const float, dK), WS(const float, dV), gr.d_c);
-  hipLaunchKernelGGL(weight_grad_kernel<T>, dim3((d.r + kWgRows - 1) / kWgRows, d.G, 2), dim3(256),
-                     0, s, d, n_rows, (const T*)in.c, WS(const float, dK), WS(const float, dV),
-                     gr.d_w_uk, gr.d_w_uv);
+  if (mf) {
+    const hipError_t e = mfma_projection_grads(d, in, ws, wsb, gr, s);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL(latent_bwd_kernel<T>, dim3((n_rows + kLatTok - 1) / kLatTok), dim3(256),
+                       (size_t)kLatTok * (d.dc + d.dv) * sizeof(float), s, d, n_rows, in.w_uk,
+                       (const T*)in.w_uv, WS(const float, dK), WS(const float, dV), gr.d_c);
+    hipLaunchKernelGGL(weight_grad_kernel<T>, dim3((d.r + kWgRows - 1) / kWgRows, d.G, 2),
+                       dim3(256), 0, s, d, n_rows, (const T*)in.c, WS(const float, dK),
+                       WS(const float, dV), gr.d_w_uk, gr.d_w_uv);
+  }
   // RMSNorm weights: (dy, x, a) per gamma; all zero in plain mode
   float* part = WS(float, gamma_partial);
   struct G4 {

@@ -250,6 +250,16 @@ def _(w, i):
     _setscc(w, r)
 
 
+@h("s_bfe_u32")
+def _(w, i):
+    a, b = _s2(w, i)
+    off, width = b & 31, (b >> 16) & 127
+    r = (a >> off) & ((1 << width) - 1) if width else 0
+    r &= M32
+    w.sset(i.ops[0], r)
+    _setscc(w, r)
+
+
 @h("s_bfe_i64")
 def _(w, i):
     a = w.sget(i.ops[1], "b64")
@@ -671,6 +681,15 @@ def _(w, i):
         x = x & 0xFFFFFF
         return np.where(x & 0x800000, x - (1 << 24), x)
     r = s24(_i(w, i.ops[1])) * s24(_i(w, i.ops[2]))
+    w.vset(i.ops[0], (r & M32).astype(U32))
+
+
+@h("v_mad_i32_i24")
+def _(w, i):
+    def s24(x):
+        x = x & 0xFFFFFF
+        return np.where(x & 0x800000, x - (1 << 24), x)
+    r = s24(_i(w, i.ops[1])) * s24(_i(w, i.ops[2])) + _i(w, i.ops[3])
     w.vset(i.ops[0], (r & M32).astype(U32))
 
 

@@ -266,6 +266,10 @@ int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, c
  * (Plain MLA if !qk_norm: no norms, gammas unused, their gradients zero.)
  * Shapes: any layer with d_c, d_v <= 256, r <= 1024, d_r <= 256, either
  * dtype; the bf16 decode restrictions do not apply here.
+ * Arithmetic: fp32 throughout, except for the bf16 layer with 16 heads per
+ * group, d_c + d_r = 192 and d_v = 128, whose attention and projections run
+ * on MFMA with bf16 operands (normalised queries and keys, values, softmax
+ * weights, their gradients, W^UK as a bf16 pair) and fp32 accumulation.
  * The workspace is scratch for one call; the backward recomputes what it
  * needs from the inputs, so no state passes between the two calls except
  * o and lse.

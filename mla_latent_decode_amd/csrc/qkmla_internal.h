@@ -91,15 +91,17 @@ struct TrainGrads {  // fp32 gradients, same shapes as the inputs
 };
 // Byte offsets of the fp32 training intermediates (d_qk = d_c + d_r):
 //   Qh [BT][H][d_qk], Kh [BT][G][d_qk], V [BT][G][d_v], Kraw [BT][G][d_c],
-//   aq, aqr [BT][H], ak [BT][G], akr [BT]  (the forward needs these: fwd_total)
+//   aq, aqr [BT][H], ak [BT][G], akr [BT], RoPE (cos, sin) [T][d_r/2]
+//   (the forward needs these: fwd_total)
 //   dQh, dKh, dV, Dsum [BT][H], dK [BT][G][d_c], dKr [BT][d_r], gamma partials.
 //   (bf16 layer with the MFMA attention also: Qb [BT][H][d_qk] scaled by
 //   tau*log2(e), Kb [B][G][T][d_qk], Vb [B][G][T][d_v], all bf16)
 struct TrainWs {
-  size_t Qh, Kh, V, Kraw, aq, aqr, ak, akr, Qb, Kb, Vb, fwd_total;
+  size_t Qh, Kh, V, Kraw, aq, aqr, ak, akr, rope_cs, Qb, Kb, Vb;
+  size_t Wk16;  // MFMA path: W^UK in bf16 hi [G][r][d_c], then lo
+  size_t fwd_total;
   size_t dQh, dKh, dV, Dsum, dK, dKr, gamma_partial;
   size_t dOb, stat;  // MFMA backward: d_o bf16 [BT][H][d_v], (lse*log2 e, D) [BT][H]
-  size_t Wk16;       // MFMA path: W^UK in bf16 [G][r][d_c]
   size_t dKb, dVb;   // MFMA backward: dk, dV in bf16 [BT][G][d_c], [BT][G][d_v]
   size_t total;
 };

@@ -37,11 +37,29 @@ struct TrainDims {
   int B, T, H, G, r, dc, dr, dv, dqk, hpg;
   int qk_norm;
   float eps, tau, base;
+  const float2* rope_cs;  // [T][d_r/2]: (cos, sin) of the angle of position t, pair i
 };
 
-TrainDims dims_of(const Cfg& c, int B, int T) {
+TrainDims dims_of(const Cfg& c, int B, int T, const float2* rope_cs) {
   return TrainDims{B, T, c.H, c.G, c.r, c.dc, c.dr, c.dv, c.dc + c.dr, c.hpg, c.qk_norm,
-                   c.eps, c.tau, c.base};
+                   c.eps, c.tau, c.base, rope_cs};
+}
+
+// The RoPE angles of every position once per call (each is used by every
+// head and group of that position, forward and backward).
+__global__ __launch_bounds__(256) void rope_table_kernel(int T, int dr, float base, float2* cs) {
+  const int half = dr / 2;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)T * half) return;
+  float c, s;
+  rope_cos_sin((int)(i / half), (int)(i % half), dr, base, &c, &s);
+  cs[i] = make_float2(c, s);
+}
+
+__device__ __forceinline__ void rope_at(const TrainDims& d, int pos, int i, float* c, float* s) {
+  const float2 t = d.rope_cs[(size_t)pos * (d.dr / 2) + i];
+  *c = t.x;
+  *s = t.y;
 }
 
 // Sum over the block (blockDim.x = 256); `red` holds 4 floats.  Every thread
@@ -116,7 +134,7 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
       x1 *= gqr[2 * i + 1] * ar;
     }
     float cs, sn;
-    rope_cos_sin(pos, i, d.dr, d.base, &cs, &sn);
+    rope_at(d, pos, i, &cs, &sn);
     put(d.dc + 2 * i, x0 * cs - x1 * sn);
     put(d.dc + 2 * i + 1, x0 * sn + x1 * cs);
   }
@@ -221,7 +239,7 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(
         x1 *= gkr[2 * i + 1] * ar;
       }
       float c0, s0;
-      rope_cos_sin(pos, i, d.dr, d.base, &c0, &s0);
+      rope_at(d, pos, i, &c0, &s0);
       put_k(row, d.dc + 2 * i, x0 * c0 - x1 * s0);
       put_k(row, d.dc + 2 * i + 1, x0 * s0 + x1 * c0);
     }
@@ -440,7 +458,7 @@ __global__ __launch_bounds__(256) void q_norm_bwd_kernel(
     u0[k] = u1[k] = 0.f;
     if (i < d.dr / 2) {
       float cs, sn;
-      rope_cos_sin(pos, i, d.dr, d.base, &cs, &sn);
+      rope_at(d, pos, i, &cs, &sn);
       const float y0 = dyr[2 * i], y1 = dyr[2 * i + 1];
       u0[k] = y0 * cs + y1 * sn;
       u1[k] = -y0 * sn + y1 * cs;
@@ -510,7 +528,7 @@ __global__ __launch_bounds__(256) void k_norm_bwd_kernel(
       y1 += src[2 * i + 1];
     }
     float cs, sn;
-    rope_cos_sin(pos, i, d.dr, d.base, &cs, &sn);
+    rope_at(d, pos, i, &cs, &sn);
     dyr[2 * i] = y0 * cs + y1 * sn;
     dyr[2 * i + 1] = -y0 * sn + y1 * cs;
   }
@@ -708,7 +726,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(
       x1 *= gkr[2 * i + 1] * ar;
     }
     float c0, s0;
-    rope_cos_sin((int)t, i, d.dr, d.base, &c0, &s0);
+    rope_at(d, (int)t, i, &c0, &s0);
     const uint16_t y0 = f32_to_bf16(x0 * c0 - x1 * s0), y1 = f32_to_bf16(x0 * s0 + x1 * c0);
     for (int g = 0; g < d.G; ++g) {
       uint16_t* out = Kb + kmaj(g) * d.dqk + d.dc;
@@ -758,6 +776,7 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
   w.aqr = take(BT * c.H * 4);
   w.ak = take(BT * c.G * 4);
   w.akr = take(BT * 4);
+  w.rope_cs = take((size_t)T * (c.dr / 2) * 8);
   w.Qb = take(mf ? BT * c.H * dqk * 2 : 0);
   w.Kb = take(mf ? BT * c.G * dqk * 2 : 0);
   w.Vb = take(mf ? BT * c.G * c.dv * 2 : 0);
@@ -779,6 +798,12 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
 }
 
 #define WS(type, field) ((type*)(wsb + ws.field))
+
+static void launch_rope_table(const TrainDims& d, float2* cs, hipStream_t s) {
+  const size_t n = (size_t)d.T * (d.dr / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, d.T,
+                     d.dr, d.base, cs);
+}
 
 // Normalised, rotated queries: fp32 for the row-parallel kernels, or (MF) the
 // bf16 operand of the MFMA attention.
@@ -875,7 +900,8 @@ static hipError_t mfma_projection_grads(const TrainDims& d, const TrainPtrs& in,
 template <typename T>
 static hipError_t forward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in, const TrainWs& ws,
                                char* wsb, float* o, float* lse, hipStream_t s) {
-  const TrainDims d = dims_of(c, B, T_);
+  const TrainDims d = dims_of(c, B, T_, WS(const float2, rope_cs));
+  launch_rope_table(d, WS(float2, rope_cs), s);
   if (train_mfma_shape(c)) {
     const hipError_t e = mfma_prep(c, d, in, ws, wsb, s);
     if (e != hipSuccess) return e;
@@ -893,9 +919,10 @@ static hipError_t backward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in
                                 const float* o, const float* lse, const float* d_o,
                                 const TrainWs& ws, char* wsb, const TrainGrads& gr,
                                 hipStream_t s) {
-  const TrainDims d = dims_of(c, B, T_);
+  const TrainDims d = dims_of(c, B, T_, WS(const float2, rope_cs));
   const int n_rows = B * T_;
   const bool mf = train_mfma_shape(c);
+  launch_rope_table(d, WS(float2, rope_cs), s);
   if (mf) {
     hipError_t e = mfma_prep(c, d, in, ws, wsb, s);
     if (e != hipSuccess) return e;

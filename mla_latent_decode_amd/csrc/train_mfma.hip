@@ -21,7 +21,9 @@
 // 4e + i/4), which turns 4 key rows into 4 keys of one dim.
 //
 // K^ and V tiles are loaded to registers one tile ahead and written to a
-// double-buffered, padded LDS stage: one barrier per tile.
+// double-buffered, padded LDS stage: one barrier per tile.  The forward fits
+// in 256 registers without spills, so two workgroups share a CU (two waves
+// per SIMD hide each other's tile loads).
 #include "device_common.h"
 #include "qkmla_internal.h"
 
@@ -54,7 +56,7 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *(const uint4*)p;
 }
 
-__global__ __launch_bounds__(256) void flash_fwd_kernel(FaArgs a) {
+__global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
   __shared__ __attribute__((aligned(16))) char k_st[2][kFaKeys * kKPitch];
   __shared__ __attribute__((aligned(16))) char v_st[2][kFaKeys * kVPitch];
   const int qb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;

@@ -145,9 +145,14 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
     const int key0 = kt * kFaKeys + 4 * hf;
     float lg[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + (r & 3);
-      lg[r] = key <= i && key < a.T ? sacc[r] : -INFINITY;
+    for (int r = 0; r < 16; ++r) lg[r] = sacc[r];
+    // only a tile reaching past the wave's first token (or the sequence) masks
+    if (kt * kFaKeys + kFaKeys - 1 > qb * kFaTok + 2 * wave) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + (r & 3);
+        if (key > i || key >= a.T) lg[r] = -INFINITY;
+      }
     }
     float mt = lg[0];
 #pragma unroll
@@ -169,10 +174,12 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
         ls += __uint_as_float(u[d] << 16) + __uint_as_float(u[d] & 0xFFFF0000u);
     }
     l_run = l_run * f + ls;
+    if (__ballot(f != 1.0f) != 0) {  // some row's max moved: rescale its O
 #pragma unroll
-    for (int mb = 0; mb < kDvBlocks; ++mb)
+      for (int mb = 0; mb < kDvBlocks; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) O[mb][r] *= f;
+        for (int r = 0; r < 16; ++r) O[mb][r] *= f;
+    }
 
     // ---- O^T[128 dims][32 rows] += V^T . P^T ----
     const int s16 = lane & 15, dblk = (lane >> 4) & 1;
@@ -322,14 +329,17 @@ __global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
       dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(orow + 32 * s), vreg[s],
                                                       dpacc, 0, 0, 0);
     // reg r holds row 8(r/4) + 4hf + r%4 = token i0 + row/16, head row%16
+    // wave-uniform: only steps whose tokens can precede a key of the tile, or
+    // run past the sequence, or a tile past the sequence, mask
+    const bool masked = i0 < key0 + kFaKeys - 1 || i0 + 1 >= a.T || key0 + kFaKeys > a.T;
     bf16x8 pb[2], db[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
       const int tok = i0 + (row >> 4);
       const float2 sd = st_s[row];
-      const bool live = key <= tok && tok < a.T && key < a.T;
-      const float p = live ? __builtin_amdgcn_exp2f(sacc[r] - sd.x) : 0.f;
+      float p = __builtin_amdgcn_exp2f(sacc[r] - sd.x);
+      if (masked && !(key <= tok && tok < a.T && key < a.T)) p = 0.f;
       pb[r >> 3][r & 7] = (__bf16)p;
       db[r >> 3][r & 7] = (__bf16)(p * (dpacc[r] - sd.y));
     }
@@ -469,11 +479,13 @@ __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
       dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vrow + 32 * s), go[s],
                                                       dpacc, 0, 0, 0);
     const int key0 = kt * kFaKeys + 4 * hf;
+    const bool masked = kt * kFaKeys + kFaKeys - 1 > qb * kFaTok + 2 * wave;  // wave-uniform
     bf16x8 db[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = key0 + 8 * (r >> 2) + (r & 3);
-      const float p = key <= i && key < a.T ? __builtin_amdgcn_exp2f(sacc[r] - sd.x) : 0.f;
+      float p = __builtin_amdgcn_exp2f(sacc[r] - sd.x);
+      if (masked && (key > i || key >= a.T)) p = 0.f;
       db[r >> 3][r & 7] = (__bf16)(p * (dpacc[r] - sd.y));
     }
     const char* tkb = ks + (4 * hf + (s16 >> 2)) * kKPitch + 32 * dblk + 8 * (s16 & 3);

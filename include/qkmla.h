@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define QKMLA_ABI_VERSION 4
+#define QKMLA_ABI_VERSION 5
 
 typedef enum {
   QKMLA_OK = 0,
@@ -311,6 +311,34 @@ int qkmla_train_backward(const qkmla_config* cfg, int32_t batch, int32_t seq_len
                          const qkmla_train_inputs* inputs, const float* o, const float* lse,
                          const float* d_o, void* workspace, size_t workspace_bytes,
                          const qkmla_train_grads* grads, void* stream);
+
+/*
+ * Packed sequences of different lengths (prefill of a batch of prompts):
+ * n_seqs sequences laid end to end over total_tokens token rows.  Every
+ * [B][T]... array above becomes [total_tokens]...; sequence s holds rows
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1 and its token i sits at position i.
+ *   cu_seqlens   device int32 [n_seqs + 1]: 0 = cu[0] <= cu[1] <= ... <=
+ *                cu[n_seqs] = total_tokens
+ *   max_seq_len  host bound on every cu[s+1] - cu[s] (>= 1)
+ *   status       device int32, nullable: QKMLA_DEV_BAD_SEQ_LEN if cu_seqlens
+ *                breaks the rules above; every access stays in bounds, the
+ *                outputs are then undefined
+ * The fixed-length calls are these with cu_seqlens[s] = s * seq_len.  At most
+ * 65535 sequences (QKMLA_ERR_UNSUPPORTED).  o must be 16-byte aligned.
+ */
+size_t qkmla_train_workspace_size_varlen(const qkmla_config* cfg, int32_t n_seqs,
+                                         int32_t total_tokens, int32_t max_seq_len);
+int qkmla_train_forward_varlen(const qkmla_config* cfg, int32_t n_seqs, const int32_t* cu_seqlens,
+                               int32_t total_tokens, int32_t max_seq_len,
+                               const qkmla_train_inputs* inputs, void* workspace,
+                               size_t workspace_bytes, float* o, float* lse, int32_t* status,
+                               void* stream);
+int qkmla_train_backward_varlen(const qkmla_config* cfg, int32_t n_seqs,
+                                const int32_t* cu_seqlens, int32_t total_tokens,
+                                int32_t max_seq_len, const qkmla_train_inputs* inputs,
+                                const float* o, const float* lse, const float* d_o,
+                                void* workspace, size_t workspace_bytes,
+                                const qkmla_train_grads* grads, int32_t* status, void* stream);
 
 /*
  * Host-only split planner (no device access; usable without a GPU).  For a

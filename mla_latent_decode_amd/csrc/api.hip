@@ -488,16 +488,19 @@ int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const 
 }
 
 // ---- training / prefill -------------------------------------------------------------
-static int check_train(const qkmla_config* cfg, int32_t batch, int32_t seq_len, Cfg* c) {
+// Packed form: n_seq sequences over n_rows rows, each at most max_len long.
+static int check_train(const qkmla_config* cfg, int64_t n_seq, int64_t n_rows, int64_t max_len,
+                       Cfg* c) {
   int st = check_cfg(cfg, c, false);
   if (st) return st;
-  if (batch < 0 || seq_len < 1)
-    return fail(QKMLA_ERR_INVALID_ARG, "train: need batch >= 0 and seq_len >= 1");
+  if (n_seq < 0 || n_rows < 0 || max_len < 1)
+    return fail(QKMLA_ERR_INVALID_ARG, "train: need sequences >= 0, tokens >= 0, max length >= 1");
   if (c->dc > 256 || c->dv > 256)
     return fail(QKMLA_ERR_UNSUPPORTED, "train: d_c and d_v must be <= 256 (got %d, %d)", c->dc,
                 c->dv);
-  if ((int64_t)batch * seq_len * c->H > INT32_MAX / 2)
-    return fail(QKMLA_ERR_UNSUPPORTED, "train: batch * seq_len * n_heads too large");
+  if (n_rows * c->H > INT32_MAX / 2 || max_len > INT32_MAX / 2)
+    return fail(QKMLA_ERR_UNSUPPORTED, "train: tokens * n_heads too large");
+  if (n_seq > 65535) return fail(QKMLA_ERR_UNSUPPORTED, "train: more than 65535 sequences");
   return QKMLA_OK;
 }
 
@@ -510,49 +513,39 @@ static int check_train_inputs(const Cfg& c, const qkmla_train_inputs* in, TrainP
   if (!aligned(in->c, es) || !aligned(in->q_c, es) || !aligned(in->q_rope, es) ||
       !aligned(in->k_rope, es) || !aligned(in->w_uv, es) || !aligned(in->w_uk, 4))
     return fail(QKMLA_ERR_INVALID_ARG, "train: inputs must be aligned to their element size");
+  // the MFMA path reads latents, W^UV and the bf16 operands as 16-byte vectors
+  if (train_mfma_shape(c) && (!aligned(in->c, 16) || !aligned(in->w_uv, 16)))
+    return fail(QKMLA_ERR_INVALID_ARG, "train: bf16 latents and W^UV must be 16-byte aligned");
   *p = TrainPtrs{in->c, in->q_c, in->q_rope, in->k_rope, in->w_uk, in->w_uv,
                  in->gamma_q, in->gamma_k, in->gamma_q_rope, in->gamma_k_rope};
   return QKMLA_OK;
 }
 
-size_t qkmla_train_workspace_size(const qkmla_config* cfg, int32_t batch, int32_t seq_len) {
-  Cfg c;
-  if (check_train(cfg, batch, seq_len, &c)) return 0;
-  if (batch == 0) return 256;
-  return train_ws_layout(c, batch, seq_len).total;
-}
-
-int qkmla_train_forward(const qkmla_config* cfg, int32_t batch, int32_t seq_len,
-                        const qkmla_train_inputs* inputs, void* workspace, size_t workspace_bytes,
-                        float* o, float* lse, void* stream) {
-  Cfg c;
-  int st = check_train(cfg, batch, seq_len, &c);
-  if (st) return st;
-  if (batch == 0) return ok();
+static int train_forward(const Cfg& c, const TrainSeqs& q, const qkmla_train_inputs* inputs,
+                         void* workspace, size_t workspace_bytes, float* o, float* lse,
+                         int32_t* status, void* stream) {
   TrainPtrs in;
-  if ((st = check_train_inputs(c, inputs, &in))) return st;
+  int st = check_train_inputs(c, inputs, &in);
+  if (st) return st;
   if (!workspace || !o || !lse) return fail(QKMLA_ERR_INVALID_ARG, "train: NULL pointer");
-  if (!aligned16(workspace) || !aligned(o, 4) || !aligned(lse, 4))
-    return fail(QKMLA_ERR_INVALID_ARG, "train: misaligned workspace or output");
-  const TrainWs ws = train_ws_layout(c, batch, seq_len);
+  if (!aligned16(workspace) || !aligned(o, 16) || !aligned(lse, 4) || (status && !aligned(status, 4)))
+    return fail(QKMLA_ERR_INVALID_ARG, "train: misaligned workspace or output (o: 16 bytes)");
+  const TrainWs ws = train_ws_layout(c, q);
   if (workspace_bytes < ws.fwd_total)
     return fail(QKMLA_ERR_WORKSPACE, "train forward: workspace %zu bytes, need %zu",
                 workspace_bytes, ws.fwd_total);
-  return hip_status(launch_train_forward(c, batch, seq_len, in, ws, workspace, o, lse,
-                                         as_stream(stream)),
-                    "train forward");
+  return hip_status(
+      launch_train_forward(c, q, in, ws, workspace, o, lse, status, as_stream(stream)),
+      "train forward");
 }
 
-int qkmla_train_backward(const qkmla_config* cfg, int32_t batch, int32_t seq_len,
-                         const qkmla_train_inputs* inputs, const float* o, const float* lse,
-                         const float* d_o, void* workspace, size_t workspace_bytes,
-                         const qkmla_train_grads* grads, void* stream) {
-  Cfg c;
-  int st = check_train(cfg, batch, seq_len, &c);
-  if (st) return st;
-  if (batch == 0) return ok();
+static int train_backward(const Cfg& c, const TrainSeqs& q, const qkmla_train_inputs* inputs,
+                          const float* o, const float* lse, const float* d_o, void* workspace,
+                          size_t workspace_bytes, const qkmla_train_grads* grads, int32_t* status,
+                          void* stream) {
   TrainPtrs in;
-  if ((st = check_train_inputs(c, inputs, &in))) return st;
+  int st = check_train_inputs(c, inputs, &in);
+  if (st) return st;
   if (!o || !lse || !d_o || !workspace || !grads)
     return fail(QKMLA_ERR_INVALID_ARG, "train: NULL pointer");
   const qkmla_train_grads& g = *grads;
@@ -560,17 +553,91 @@ int qkmla_train_backward(const qkmla_config* cfg, int32_t batch, int32_t seq_len
                    g.d_gamma_q, g.d_gamma_k, g.d_gamma_q_rope, g.d_gamma_k_rope};
   for (float* p : outs)
     if (!p || !aligned(p, 4)) return fail(QKMLA_ERR_INVALID_ARG, "train: NULL or misaligned gradient");
-  if (!aligned16(workspace) || !aligned(o, 4) || !aligned(lse, 4) || !aligned(d_o, 4))
+  if (!aligned16(workspace) || !aligned(o, 8) || !aligned(lse, 4) || !aligned(d_o, 8) ||
+      (status && !aligned(status, 4)))
     return fail(QKMLA_ERR_INVALID_ARG, "train: misaligned workspace, o, lse or d_o");
-  const TrainWs ws = train_ws_layout(c, batch, seq_len);
+  const TrainWs ws = train_ws_layout(c, q);
   if (workspace_bytes < ws.total)
     return fail(QKMLA_ERR_WORKSPACE, "train backward: workspace %zu bytes, need %zu",
                 workspace_bytes, ws.total);
   const TrainGrads gr{g.d_c, g.d_q_c, g.d_q_rope, g.d_k_rope, g.d_w_uk, g.d_w_uv,
                       g.d_gamma_q, g.d_gamma_k, g.d_gamma_q_rope, g.d_gamma_k_rope};
-  return hip_status(launch_train_backward(c, batch, seq_len, in, o, lse, d_o, ws, workspace, gr,
+  return hip_status(launch_train_backward(c, q, in, o, lse, d_o, ws, workspace, gr, status,
                                           as_stream(stream)),
                     "train backward");
+}
+
+size_t qkmla_train_workspace_size(const qkmla_config* cfg, int32_t batch, int32_t seq_len) {
+  Cfg c;
+  if (check_train(cfg, batch, (int64_t)batch * seq_len, seq_len, &c)) return 0;
+  if (batch == 0) return 256;
+  return train_ws_layout(c, TrainSeqs{batch * seq_len, batch, seq_len, nullptr}).total;
+}
+
+int qkmla_train_forward(const qkmla_config* cfg, int32_t batch, int32_t seq_len,
+                        const qkmla_train_inputs* inputs, void* workspace, size_t workspace_bytes,
+                        float* o, float* lse, void* stream) {
+  Cfg c;
+  int st = check_train(cfg, batch, (int64_t)batch * seq_len, seq_len, &c);
+  if (st) return st;
+  if (batch == 0) return ok();
+  return train_forward(c, TrainSeqs{batch * seq_len, batch, seq_len, nullptr}, inputs, workspace,
+                       workspace_bytes, o, lse, nullptr, stream);
+}
+
+int qkmla_train_backward(const qkmla_config* cfg, int32_t batch, int32_t seq_len,
+                         const qkmla_train_inputs* inputs, const float* o, const float* lse,
+                         const float* d_o, void* workspace, size_t workspace_bytes,
+                         const qkmla_train_grads* grads, void* stream) {
+  Cfg c;
+  int st = check_train(cfg, batch, (int64_t)batch * seq_len, seq_len, &c);
+  if (st) return st;
+  if (batch == 0) return ok();
+  return train_backward(c, TrainSeqs{batch * seq_len, batch, seq_len, nullptr}, inputs, o, lse,
+                        d_o, workspace, workspace_bytes, grads, nullptr, stream);
+}
+
+size_t qkmla_train_workspace_size_varlen(const qkmla_config* cfg, int32_t n_seqs,
+                                         int32_t total_tokens, int32_t max_seq_len) {
+  Cfg c;
+  if (check_train(cfg, n_seqs, total_tokens, max_seq_len, &c)) return 0;
+  if (n_seqs == 0 || total_tokens == 0) return 256;
+  return train_ws_layout(c, TrainSeqs{total_tokens, n_seqs, max_seq_len, nullptr}).total;
+}
+
+static int check_cu(const int32_t* cu_seqlens) {
+  if (!cu_seqlens || !aligned(cu_seqlens, 4))
+    return fail(QKMLA_ERR_INVALID_ARG, "train: cu_seqlens NULL or misaligned");
+  return QKMLA_OK;
+}
+
+int qkmla_train_forward_varlen(const qkmla_config* cfg, int32_t n_seqs, const int32_t* cu_seqlens,
+                               int32_t total_tokens, int32_t max_seq_len,
+                               const qkmla_train_inputs* inputs, void* workspace,
+                               size_t workspace_bytes, float* o, float* lse, int32_t* status,
+                               void* stream) {
+  Cfg c;
+  int st = check_train(cfg, n_seqs, total_tokens, max_seq_len, &c);
+  if (st) return st;
+  if (n_seqs == 0 || total_tokens == 0) return ok();
+  if ((st = check_cu(cu_seqlens))) return st;
+  return train_forward(c, TrainSeqs{total_tokens, n_seqs, max_seq_len, cu_seqlens}, inputs,
+                       workspace, workspace_bytes, o, lse, status, stream);
+}
+
+int qkmla_train_backward_varlen(const qkmla_config* cfg, int32_t n_seqs,
+                                const int32_t* cu_seqlens, int32_t total_tokens,
+                                int32_t max_seq_len, const qkmla_train_inputs* inputs,
+                                const float* o, const float* lse, const float* d_o,
+                                void* workspace, size_t workspace_bytes,
+                                const qkmla_train_grads* grads, int32_t* status, void* stream) {
+  Cfg c;
+  int st = check_train(cfg, n_seqs, total_tokens, max_seq_len, &c);
+  if (st) return st;
+  if (n_seqs == 0 || total_tokens == 0) return ok();
+  if ((st = check_cu(cu_seqlens))) return st;
+  return train_backward(c, TrainSeqs{total_tokens, n_seqs, max_seq_len, cu_seqlens}, inputs, o,
+                        lse, d_o, workspace, workspace_bytes, grads, status, stream);
 }
 
 int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, const void* w_uv,

@@ -95,8 +95,21 @@ struct TrainGrads {  // fp32 gradients, same shapes as the inputs
 //   (the forward needs these: fwd_total)
 //   dQh, dKh, dV, Dsum [BT][H], dK [BT][G][d_c], dKr [BT][d_r], gamma partials.
 //   (bf16 layer with the MFMA attention also: Qb [BT][H][d_qk] scaled by
-//   tau*log2(e), Kb [B][G][T][d_qk], Vb [B][G][T][d_v], all bf16)
+//   tau*log2(e), Kb [G][BT][d_qk], Vb [G][BT][d_v], all bf16)
+// Packed sequences: n_seq sequences over n_rows token rows, each at most
+// max_len long; cu (device, [n_seq+1]) holds their start rows and the total,
+// or is nullptr for n_seq sequences of exactly max_len rows.
+struct TrainSeqs {
+  int n_rows, n_seq, max_len;
+  const int32_t* cu;
+};
+// The flash kernels' view: validated (start, len) per sequence.
+struct FlashSeqs {
+  int n_rows, n_seq, max_len;
+  const int2* seqs;
+};
 struct TrainWs {
+  size_t seqs, rpos, rlen;  // (start, len) [n_seq] int2; per row: position, sequence length
   size_t Qh, Kh, V, Kraw, aq, aqr, ak, akr, rope_cs, Qb, Kb, Vb;
   size_t Wk16;  // MFMA path: W^UK in bf16 hi [G][r][d_c], then lo
   size_t fwd_total;
@@ -105,15 +118,15 @@ struct TrainWs {
   size_t dKb, dVb;   // MFMA backward: dk, dV in bf16 [BT][G][d_c], [BT][G][d_v]
   size_t total;
 };
-TrainWs train_ws_layout(const Cfg& c, int B, int T);
+TrainWs train_ws_layout(const Cfg& c, const TrainSeqs& q);
 // The layer shape the MFMA attention is compiled for (bf16, 16 heads per
 // group, d_c + d_r = 192, d_v = 128).
 bool train_mfma_shape(const Cfg& c);
-hipError_t launch_flash_fwd(const Cfg& c, int B, int T, const void* Qb, const void* Kb,
+hipError_t launch_flash_fwd(const Cfg& c, const FlashSeqs& q, const void* Qb, const void* Kb,
                             const void* Vb, float* o, float* lse, hipStream_t s);
 // dK^ and dV (key side) and dQ^ (query side) of the attention, fp32, in the
 // row-major layouts of the row-parallel kernels.
-hipError_t launch_flash_bwd(const Cfg& c, int B, int T, const void* Qb, const void* Kb,
+hipError_t launch_flash_bwd(const Cfg& c, const FlashSeqs& q, const void* Qb, const void* Kb,
                             const void* Vb, const float* o, const float* lse, const float* d_o,
                             void* dOb, void* stat, float* dKh, float* dV, float* dQh,
                             hipStream_t s);
@@ -164,12 +177,13 @@ hipError_t launch_decode_generic(const Cfg& c, int batch, int s_q, const int32_t
                                  const Paging& pg, const void* lat, const void* rope,
                                  const float* alpha, const WsLayout& ws, void* workspace,
                                  float* o_lat, float* lse, hipStream_t s);
-hipError_t launch_train_forward(const Cfg& c, int B, int T, const TrainPtrs& in,
+hipError_t launch_train_forward(const Cfg& c, const TrainSeqs& q, const TrainPtrs& in,
                                 const TrainWs& ws, void* workspace, float* o, float* lse,
-                                hipStream_t s);
-hipError_t launch_train_backward(const Cfg& c, int B, int T, const TrainPtrs& in, const float* o,
-                                 const float* lse, const float* d_o, const TrainWs& ws,
-                                 void* workspace, const TrainGrads& gr, hipStream_t s);
+                                int32_t* status, hipStream_t s);
+hipError_t launch_train_backward(const Cfg& c, const TrainSeqs& q, const TrainPtrs& in,
+                                 const float* o, const float* lse, const float* d_o,
+                                 const TrainWs& ws, void* workspace, const TrainGrads& gr,
+                                 int32_t* status, hipStream_t s);
 hipError_t launch_out_proj(const Cfg& c, int batch, const float* o_lat, const void* w_uv,
                            float* out, hipStream_t s);
 

@@ -33,16 +33,63 @@ constexpr int kWgRows = 16;   // latent rows per workgroup of the weight gradien
 constexpr int kWgTok = 32;    // tokens per LDS chunk of the weight gradients
 constexpr int kGammaSplit = 64;
 
+// Token rows are packed: sequence s holds rows [start_s, start_s + len_s).
 struct TrainDims {
-  int B, T, H, G, r, dc, dr, dv, dqk, hpg;
+  int n_rows, n_seq, max_len, H, G, r, dc, dr, dv, dqk, hpg;
   int qk_norm;
   float eps, tau, base;
-  const float2* rope_cs;  // [T][d_r/2]: (cos, sin) of the angle of position t, pair i
+  const float2* rope_cs;  // [max_len][d_r/2]: (cos, sin) of the angle of position t, pair i
+  const int32_t* rpos;    // [n_rows] position of the row in its sequence
+  const int32_t* rlen;    // [n_rows] length of the row's sequence
 };
 
-TrainDims dims_of(const Cfg& c, int B, int T, const float2* rope_cs) {
-  return TrainDims{B, T, c.H, c.G, c.r, c.dc, c.dr, c.dv, c.dc + c.dr, c.hpg, c.qk_norm,
-                   c.eps, c.tau, c.base, rope_cs};
+TrainDims dims_of(const Cfg& c, const TrainSeqs& q, const float2* rope_cs, const int32_t* rpos,
+                  const int32_t* rlen) {
+  return TrainDims{q.n_rows, q.n_seq, q.max_len, c.H, c.G, c.r, c.dc, c.dr, c.dv, c.dc + c.dr,
+                   c.hpg, c.qk_norm, c.eps, c.tau, c.base, rope_cs, rpos, rlen};
+}
+
+// ---- sequence tables --------------------------------------------------------
+// seq_table_kernel: per sequence s, its start and length from the caller's
+// cu_seqlens (or, with cu == nullptr, equal lengths max_len), clamped so that
+// 0 <= start, start + len <= n_rows and len <= max_len; a clamp, a gap or an
+// overlap sets QKMLA_DEV_BAD_SEQ_LEN (the outputs are then undefined, every
+// access stays in bounds).
+__global__ __launch_bounds__(256) void seq_table_kernel(int n_seq, const int32_t* __restrict__ cu,
+                                                        int n_rows, int max_len,
+                                                        int2* __restrict__ seqs,
+                                                        int32_t* __restrict__ status) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= n_seq) return;
+  int a = cu ? cu[s] : s * max_len, b = cu ? cu[s + 1] : (s + 1) * max_len;
+  bool bad = cu && ((s == 0 && a != 0) || (s == n_seq - 1 && b != n_rows));
+  const int start = min(max(a, 0), n_rows);
+  const int end = min(max(b, start), n_rows);
+  const int len = min(end - start, max_len);
+  bad |= start != a || end != b || len != end - start;
+  seqs[s] = make_int2(start, len);
+  if (bad && status) atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
+}
+
+// Rows first become one-token sequences of their own; then every sequence
+// claims its rows.  A row ends with rpos <= row and row - rpos + rlen <= n_rows
+// whatever cu held.
+__global__ __launch_bounds__(256) void row_init_kernel(int n_rows, int32_t* __restrict__ rpos,
+                                                       int32_t* __restrict__ rlen) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= n_rows) return;
+  rpos[r] = 0;
+  rlen[r] = 1;
+}
+
+__global__ __launch_bounds__(256) void row_fill_kernel(const int2* __restrict__ seqs,
+                                                       int32_t* __restrict__ rpos,
+                                                       int32_t* __restrict__ rlen) {
+  const int2 sl = seqs[blockIdx.x];
+  for (int t = threadIdx.x; t < sl.y; t += 256) {
+    rpos[sl.x + t] = t;
+    rlen[sl.x + t] = sl.y;
+  }
 }
 
 // The RoPE angles of every position once per call (each is used by every
@@ -98,7 +145,7 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
   const size_t row = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (h >= d.H) return;
-  const int pos = (int)(row % d.T);
+  const int pos = d.rpos[row];
   const size_t qh = row * d.H + h;
   const T* qc = q_c + qh * d.dc;
   const T* qr = q_rope + qh * d.dr;
@@ -220,7 +267,7 @@ __global__ __launch_bounds__(256) void prep_kv_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   for (int t = wave; t < ntok; t += 4) {
     const size_t row = row0 + t;
-    const int pos = (int)(row % d.T);
+    const int pos = d.rpos[row];
     const T* kr = k_rope + row * d.dr;
     float ar = 1.f;
     if (d.qk_norm) {
@@ -260,7 +307,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(TrainDims d, const float*
   float* red = p + kChunk;
   const size_t row = blockIdx.x;
   const int h = blockIdx.y, tid = threadIdx.x, g = h / d.hpg;
-  const int i = (int)(row % d.T);
+  const int i = d.rpos[row];
   const size_t seq0 = row - i;  // first row of the sequence
   const float sc = d.tau * kLog2e;
   for (int e = tid; e < d.dqk; e += 256) q[e] = Qh[(row * d.H + h) * d.dqk + e] * sc;
@@ -308,7 +355,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(
   float* red = ds + kChunk;
   const size_t row = blockIdx.x;
   const int h = blockIdx.y, tid = threadIdx.x, g = h / d.hpg;
-  const int i = (int)(row % d.T);
+  const int i = d.rpos[row];
   const size_t seq0 = row - i;
   const size_t qh = row * d.H + h;
   for (int e = tid; e < d.dqk; e += 256) q[e] = Qh[qh * d.dqk + e];
@@ -365,7 +412,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
   float* ds = p + kChunk;
   const size_t row = blockIdx.x;
   const int g = blockIdx.y, tid = threadIdx.x;
-  const int j = (int)(row % d.T);
+  const int j = d.rpos[row];
+  const int L = d.rlen[row];
   const size_t seq0 = row - j;
   const size_t kg = row * d.G + g;
   for (int e = tid; e < d.dqk; e += 256) k[e] = Kh[kg * d.dqk + e];
@@ -374,10 +422,10 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
   float dk0 = 0.f, dk1 = 0.f, dvv = 0.f;
   for (int hh = 0; hh < d.hpg; ++hh) {
     const int h = g * d.hpg + hh;
-    for (int i0 = j; i0 < d.T; i0 += kChunk) {
+    for (int i0 = j; i0 < L; i0 += kChunk) {
       const int i = i0 + tid;
       float pv = 0.f, dsv = 0.f;
-      if (i < d.T) {
+      if (i < L) {
         const size_t qh = (seq0 + i) * d.H + h;
         const float* q = Qh + qh * d.dqk;
         float s = 0.f;
@@ -391,7 +439,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(
       p[tid] = pv;
       ds[tid] = dsv;
       __syncthreads();
-      const int n = min(kChunk, d.T - i0);
+      const int n = min(kChunk, L - i0);
       for (int ii = 0; ii < n; ++ii) {
         const size_t qh = (seq0 + i0 + ii) * d.H + h;
         const float* q = Qh + qh * d.dqk;
@@ -434,7 +482,7 @@ __global__ __launch_bounds__(256) void q_norm_bwd_kernel(
   const size_t row = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (h >= d.H) return;
-  const int pos = (int)(row % d.T);
+  const int pos = d.rpos[row];
   const size_t qh = row * d.H + h;
   float* dy = dQh + qh * d.dqk;
   float* dyr = dy + d.dc;
@@ -505,7 +553,7 @@ __global__ __launch_bounds__(256) void k_norm_bwd_kernel(
     float* __restrict__ dKr, float* __restrict__ d_k_rope) {
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int pos = (int)(row % d.T);
+  const int pos = d.rpos[row];
   for (int g = wave; g < d.G; g += 4) {
     const size_t kg = row * d.G + g;
     const float* dy = dKh + kg * d.dqk;
@@ -689,8 +737,8 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(
     float* __restrict__ akr) {
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const size_t b = row / d.T, t = row % d.T;
-  auto kmaj = [&](int g) { return ((b * d.G + g) * d.T + t); };
+  const int t = d.rpos[row];
+  auto kmaj = [&](int g) { return (size_t)g * d.n_rows + row; };  // group-major rows
   for (int g = wave; g < d.G; g += 4) {
     const float* x = Kraw + (row * d.G + g) * d.dc;
     float a = 1.f;
@@ -726,7 +774,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(
       x1 *= gkr[2 * i + 1] * ar;
     }
     float c0, s0;
-    rope_at(d, (int)t, i, &c0, &s0);
+    rope_at(d, t, i, &c0, &s0);
     const uint16_t y0 = f32_to_bf16(x0 * c0 - x1 * s0), y1 = f32_to_bf16(x0 * s0 + x1 * c0);
     for (int g = 0; g < d.G; ++g) {
       uint16_t* out = Kb + kmaj(g) * d.dqk + d.dc;
@@ -758,8 +806,8 @@ hipError_t launch_to_bf16(size_t n, const float* src, void* hi, void* lo, hipStr
 }  // namespace
 
 // ---- workspace ------------------------------------------------------------------------
-TrainWs train_ws_layout(const Cfg& c, int B, int T) {
-  const size_t BT = (size_t)B * T, dqk = c.dc + c.dr;
+TrainWs train_ws_layout(const Cfg& c, const TrainSeqs& q) {
+  const size_t BT = (size_t)q.n_rows, dqk = c.dc + c.dr;
   TrainWs w;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -768,6 +816,9 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
     return at;
   };
   const bool mf = train_mfma_shape(c);
+  w.seqs = take((size_t)q.n_seq * 8);
+  w.rpos = take(BT * 4);
+  w.rlen = take(BT * 4);
   w.Qh = take(mf ? 0 : BT * c.H * dqk * 4);  // the MFMA path keeps bf16 operands instead
   w.Kh = take(mf ? 0 : BT * c.G * dqk * 4);
   w.V = take(BT * c.G * c.dv * 4);
@@ -776,7 +827,7 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
   w.aqr = take(BT * c.H * 4);
   w.ak = take(BT * c.G * 4);
   w.akr = take(BT * 4);
-  w.rope_cs = take((size_t)T * (c.dr / 2) * 8);
+  w.rope_cs = take((size_t)q.max_len * (c.dr / 2) * 8);
   w.Qb = take(mf ? BT * c.H * dqk * 2 : 0);
   w.Kb = take(mf ? BT * c.G * dqk * 2 : 0);
   w.Vb = take(mf ? BT * c.G * c.dv * 2 : 0);
@@ -799,10 +850,21 @@ TrainWs train_ws_layout(const Cfg& c, int B, int T) {
 
 #define WS(type, field) ((type*)(wsb + ws.field))
 
-static void launch_rope_table(const TrainDims& d, float2* cs, hipStream_t s) {
-  const size_t n = (size_t)d.T * (d.dr / 2);
-  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, d.T,
-                     d.dr, d.base, cs);
+// Sequence and row tables, RoPE angles; returns the dims every kernel takes.
+static TrainDims launch_tables(const Cfg& c, const TrainSeqs& q, const TrainWs& ws, char* wsb,
+                               int32_t* status, hipStream_t s) {
+  const TrainDims d =
+      dims_of(c, q, WS(const float2, rope_cs), WS(const int32_t, rpos), WS(const int32_t, rlen));
+  hipLaunchKernelGGL(seq_table_kernel, dim3((q.n_seq + 255) / 256), dim3(256), 0, s, q.n_seq,
+                     q.cu, q.n_rows, q.max_len, WS(int2, seqs), status);
+  hipLaunchKernelGGL(row_init_kernel, dim3((q.n_rows + 255) / 256), dim3(256), 0, s, q.n_rows,
+                     WS(int32_t, rpos), WS(int32_t, rlen));
+  hipLaunchKernelGGL(row_fill_kernel, dim3(q.n_seq), dim3(256), 0, s, WS(const int2, seqs),
+                     WS(int32_t, rpos), WS(int32_t, rlen));
+  const size_t n = (size_t)q.max_len * (d.dr / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     q.max_len, d.dr, d.base, WS(float2, rope_cs));
+  return d;
 }
 
 // Normalised, rotated queries: fp32 for the row-parallel kernels, or (MF) the
@@ -810,7 +872,7 @@ static void launch_rope_table(const TrainDims& d, float2* cs, hipStream_t s) {
 template <typename T, bool MF>
 static void launch_prep_q(const TrainDims& d, const TrainPtrs& in, const TrainWs& ws, char* wsb,
                           hipStream_t s) {
-  hipLaunchKernelGGL((prep_q_kernel<T, MF>), dim3(d.B * d.T, (d.H + 3) / 4), dim3(256), 0, s, d,
+  hipLaunchKernelGGL((prep_q_kernel<T, MF>), dim3(d.n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
                      (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
                      WS(float, Qh), WS(uint16_t, Qb), WS(float, aq), WS(float, aqr));
 }
@@ -820,7 +882,7 @@ static void launch_prep_q(const TrainDims& d, const TrainPtrs& in, const TrainWs
 template <typename T>
 static void launch_prep(const TrainDims& d, const TrainPtrs& in, const TrainWs& ws, char* wsb,
                         hipStream_t s) {
-  const int n_rows = d.B * d.T;
+  const int n_rows = d.n_rows;
   launch_prep_q<T, false>(d, in, ws, wsb, s);
   hipLaunchKernelGGL((prep_kv_kernel<T>), dim3((n_rows + kKvTok - 1) / kKvTok, d.G), dim3(256),
                      (kKvTok * d.r + kKvTok * 4) * sizeof(float), s, d, n_rows, (const T*)in.c,
@@ -830,10 +892,10 @@ static void launch_prep(const TrainDims& d, const TrainPtrs& in, const TrainWs& 
 
 // MFMA path (bf16 layer): Q^ from prep_q; k = c W^UK_g and v = c W^UV_g as
 // batched GEMMs (batch = group) into Kraw and V, then kv_norm_kernel forms
-// the bf16 key-major operands.
-static hipError_t mfma_prep(const Cfg& c, const TrainDims& d, const TrainPtrs& in,
-                            const TrainWs& ws, char* wsb, hipStream_t s) {
-  const int BT = d.B * d.T;
+// the bf16 group-major operands.
+static hipError_t mfma_prep(const TrainDims& d, const TrainPtrs& in, const TrainWs& ws, char* wsb,
+                            hipStream_t s) {
+  const int BT = d.n_rows;
   launch_prep_q<uint16_t, true>(d, in, ws, wsb, s);
   // W^UK in bf16 hi and lo: c is exact in bf16, so k = c W_hi + c W_lo keeps
   // the key (and its RMS) close to fp32
@@ -858,7 +920,6 @@ static hipError_t mfma_prep(const Cfg& c, const TrainDims& d, const TrainPtrs& i
   hipLaunchKernelGGL(kv_norm_kernel, dim3(BT), dim3(256), 0, s, d, (const uint16_t*)in.k_rope,
                      in.gamma_k, in.gamma_k_rope, WS(const float, Kraw), WS(const float, V),
                      WS(uint16_t, Kb), WS(uint16_t, Vb), WS(float, ak), WS(float, akr));
-  (void)c;
   return hipGetLastError();
 }
 
@@ -867,7 +928,7 @@ static hipError_t mfma_prep(const Cfg& c, const TrainDims& d, const TrainPtrs& i
 static hipError_t mfma_projection_grads(const TrainDims& d, const TrainPtrs& in,
                                         const TrainWs& ws, char* wsb, const TrainGrads& gr,
                                         hipStream_t s) {
-  const int BT = d.B * d.T;
+  const int BT = d.n_rows;
   hipError_t e =
       launch_to_bf16((size_t)BT * d.G * d.dc, WS(const float, dK), wsb + ws.dKb, nullptr, s);
   if (e != hipSuccess) return e;
@@ -897,38 +958,42 @@ static hipError_t mfma_projection_grads(const TrainDims& d, const TrainPtrs& in,
   return launch_gemm_bf16(w, false, false, d.G, s);
 }
 
+static FlashSeqs flash_seqs(const TrainDims& d, const TrainWs& ws, char* wsb) {
+  return FlashSeqs{d.n_rows, d.n_seq, d.max_len, WS(const int2, seqs)};
+}
+
 template <typename T>
-static hipError_t forward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in, const TrainWs& ws,
-                               char* wsb, float* o, float* lse, hipStream_t s) {
-  const TrainDims d = dims_of(c, B, T_, WS(const float2, rope_cs));
-  launch_rope_table(d, WS(float2, rope_cs), s);
+static hipError_t forward_impl(const Cfg& c, const TrainSeqs& q, const TrainPtrs& in,
+                               const TrainWs& ws, char* wsb, float* o, float* lse,
+                               int32_t* status, hipStream_t s) {
+  const TrainDims d = launch_tables(c, q, ws, wsb, status, s);
   if (train_mfma_shape(c)) {
-    const hipError_t e = mfma_prep(c, d, in, ws, wsb, s);
+    const hipError_t e = mfma_prep(d, in, ws, wsb, s);
     if (e != hipSuccess) return e;
-    return launch_flash_fwd(c, B, T_, wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o, lse, s);
+    return launch_flash_fwd(c, flash_seqs(d, ws, wsb), wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o,
+                            lse, s);
   }
   launch_prep<T>(d, in, ws, wsb, s);
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(B * T_, d.H), dim3(256),
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(d.n_rows, d.H), dim3(256),
                      (d.dqk + kChunk + 4) * sizeof(float), s, d, WS(const float, Qh),
                      WS(const float, Kh), WS(const float, V), o, lse);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t backward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in,
+static hipError_t backward_impl(const Cfg& c, const TrainSeqs& q, const TrainPtrs& in,
                                 const float* o, const float* lse, const float* d_o,
                                 const TrainWs& ws, char* wsb, const TrainGrads& gr,
-                                hipStream_t s) {
-  const TrainDims d = dims_of(c, B, T_, WS(const float2, rope_cs));
-  const int n_rows = B * T_;
+                                int32_t* status, hipStream_t s) {
+  const TrainDims d = launch_tables(c, q, ws, wsb, status, s);
+  const int n_rows = d.n_rows;
   const bool mf = train_mfma_shape(c);
-  launch_rope_table(d, WS(float2, rope_cs), s);
   if (mf) {
-    hipError_t e = mfma_prep(c, d, in, ws, wsb, s);
+    hipError_t e = mfma_prep(d, in, ws, wsb, s);
     if (e != hipSuccess) return e;
-    e = launch_flash_bwd(c, B, T_, wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o, lse,
-                                          d_o, wsb + ws.dOb, wsb + ws.stat, WS(float, dKh),
-                                          WS(float, dV), WS(float, dQh), s);
+    e = launch_flash_bwd(c, flash_seqs(d, ws, wsb), wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o,
+                         lse, d_o, wsb + ws.dOb, wsb + ws.stat, WS(float, dKh), WS(float, dV),
+                         WS(float, dQh), s);
     if (e != hipSuccess) return e;
   } else {
     launch_prep<T>(d, in, ws, wsb, s);
@@ -997,21 +1062,23 @@ static hipError_t backward_impl(const Cfg& c, int B, int T_, const TrainPtrs& in
   return hipGetLastError();
 }
 
-hipError_t launch_train_forward(const Cfg& c, int B, int T, const TrainPtrs& in,
+hipError_t launch_train_forward(const Cfg& c, const TrainSeqs& q, const TrainPtrs& in,
                                 const TrainWs& ws, void* workspace, float* o, float* lse,
-                                hipStream_t s) {
-  char* wsb = (char*)workspace;
-  return c.dtype == QKMLA_BF16 ? forward_impl<uint16_t>(c, B, T, in, ws, wsb, o, lse, s)
-                               : forward_impl<float>(c, B, T, in, ws, wsb, o, lse, s);
-}
-
-hipError_t launch_train_backward(const Cfg& c, int B, int T, const TrainPtrs& in, const float* o,
-                                 const float* lse, const float* d_o, const TrainWs& ws,
-                                 void* workspace, const TrainGrads& gr, hipStream_t s) {
+                                int32_t* status, hipStream_t s) {
   char* wsb = (char*)workspace;
   return c.dtype == QKMLA_BF16
-             ? backward_impl<uint16_t>(c, B, T, in, o, lse, d_o, ws, wsb, gr, s)
-             : backward_impl<float>(c, B, T, in, o, lse, d_o, ws, wsb, gr, s);
+             ? forward_impl<uint16_t>(c, q, in, ws, wsb, o, lse, status, s)
+             : forward_impl<float>(c, q, in, ws, wsb, o, lse, status, s);
+}
+
+hipError_t launch_train_backward(const Cfg& c, const TrainSeqs& q, const TrainPtrs& in,
+                                 const float* o, const float* lse, const float* d_o,
+                                 const TrainWs& ws, void* workspace, const TrainGrads& gr,
+                                 int32_t* status, hipStream_t s) {
+  char* wsb = (char*)workspace;
+  return c.dtype == QKMLA_BF16
+             ? backward_impl<uint16_t>(c, q, in, o, lse, d_o, ws, wsb, gr, status, s)
+             : backward_impl<float>(c, q, in, o, lse, d_o, ws, wsb, gr, status, s);
 }
 
 }  // namespace qkmla

@@ -5,7 +5,7 @@
 // RoPE parts of each normalised query and key sit side by side, so one
 // 192-dim dot product gives the whole logit).
 //
-// Workgroup = (sequence b, group g, block of 8 query tokens); wave w owns 32
+// Workgroup = (sequence s, group g, block of 8 query tokens); wave w owns 32
 // query rows = tokens 2w, 2w+1 of the block x the group's 16 heads, so all
 // four waves share every 32-key tile of K^ and V.  Per key tile:
 //   S^T (32 keys x 32 rows) = K^ (32 x 192) . Q^T      (12 MFMA 32x32x16)
@@ -43,13 +43,15 @@ constexpr int kVChunks = kFaKeys * kFaDv * 2 / 16;   // 512 per V tile
 constexpr int kQkSteps = kFaDqk / 16;       // 12
 constexpr int kDvBlocks = kFaDv / 32;       // 4
 
+// Token rows are packed: sequence s holds rows seqs[s].x .. + seqs[s].y - 1.
 struct FaArgs {
-  const uint16_t* Qb;  // [B*T][H][192] bf16, scaled by tau*log2(e)
-  const uint16_t* Kb;  // [B][G][T][192] bf16
-  const uint16_t* Vb;  // [B][G][T][128] bf16
-  float* o;            // [B*T][H][128]
-  float* lse;          // [B*T][H], natural log
-  int T, H, G;
+  const uint16_t* Qb;  // [rows][H][192] bf16, scaled by tau*log2(e)
+  const uint16_t* Kb;  // [G][rows][192] bf16
+  const uint16_t* Vb;  // [G][rows][128] bf16
+  float* o;            // [rows][H][128]
+  float* lse;          // [rows][H], natural log
+  const int2* seqs;    // [n_seq] (start row, length)
+  int n_rows, H, G;
 };
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
@@ -59,14 +61,17 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
   __shared__ __attribute__((aligned(16))) char k_st[2][kFaKeys * kKPitch];
   __shared__ __attribute__((aligned(16))) char v_st[2][kFaKeys * kVPitch];
-  const int qb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int qb = blockIdx.x, g = blockIdx.y;
+  const int2 sq = a.seqs[blockIdx.z];  // (start row, length), uniform
+  const int T = sq.y;
+  if (qb * kFaTok >= T) return;  // whole workgroup: past this sequence
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hf = lane >> 5, n = lane & 31;
   const int i = qb * kFaTok + 2 * wave + (n >> 4);  // query token of this lane's column
   const int h = g * kFaHpg + (n & 15);
-  const bool valid = i < a.T;
-  const size_t qrow = ((size_t)b * a.T + (valid ? i : a.T - 1)) * a.H + h;
+  const bool valid = i < T;
+  const size_t qrow = ((size_t)sq.x + (valid ? i : T - 1)) * a.H + h;
 
   // Q^T as the B operand of the QK MFMAs, for the whole key loop
   bf16x8 q[kQkSteps];
@@ -79,10 +84,10 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
     }
   }
 
-  const int i_last = min(qb * kFaTok + kFaTok - 1, a.T - 1);
+  const int i_last = min(qb * kFaTok + kFaTok - 1, T - 1);
   const int n_kt = i_last / kFaKeys + 1;  // key tiles 0 .. i_last / 32 (all 8 tokens in one)
-  const uint16_t* kbase = a.Kb + ((size_t)b * a.G + g) * a.T * kFaDqk;
-  const uint16_t* vbase = a.Vb + ((size_t)b * a.G + g) * a.T * kFaDv;
+  const uint16_t* kbase = a.Kb + ((size_t)g * a.n_rows + sq.x) * kFaDqk;
+  const uint16_t* vbase = a.Vb + ((size_t)g * a.n_rows + sq.x) * kFaDv;
 
   // tile loads: K 768 chunks (3 per thread), V 512 (2 per thread); rows past
   // the sequence repeat its last row (masked below)
@@ -91,13 +96,13 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
 #pragma unroll
     for (int u = 0; u < kKChunks / 256; ++u) {
       const int c = tid + 256 * u, row = c / 24, col = c % 24;
-      const int key = min(kt * kFaKeys + row, a.T - 1);
+      const int key = min(kt * kFaKeys + row, T - 1);
       kr[u] = load16(kbase + (size_t)key * kFaDqk + col * 8);
     }
 #pragma unroll
     for (int u = 0; u < kVChunks / 256; ++u) {
       const int c = tid + 256 * u, row = c / 16, col = c % 16;
-      const int key = min(kt * kFaKeys + row, a.T - 1);
+      const int key = min(kt * kFaKeys + row, T - 1);
       vr[u] = load16(vbase + (size_t)key * kFaDv + col * 8);
     }
   };
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + (r & 3);
-        if (key > i || key >= a.T) lg[r] = -INFINITY;
+        if (key > i || key >= T) lg[r] = -INFINITY;
       }
     }
     float mt = lg[0];
@@ -236,15 +241,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int n_rows_h, const float
 }
 
 struct FbArgs {
-  const uint16_t* Qb;   // [B*T][H][192] bf16, scaled by tau*log2(e)
-  const uint16_t* Kb;   // [B][G][T][192]
-  const uint16_t* Vb;   // [B][G][T][128]
-  const uint16_t* dOb;  // [B*T][H][128] bf16
-  const float2* stat;   // [B*T][H]: (lse*log2(e), D)
-  float* dKh;           // [B*T][G][192] fp32: dK^ (content | RoPE)
-  float* dV;            // [B*T][G][128] fp32
-  float* dQh;           // [B*T][H][192] fp32: dQ^
-  int T, H, G;
+  const uint16_t* Qb;   // [rows][H][192] bf16, scaled by tau*log2(e)
+  const uint16_t* Kb;   // [G][rows][192]
+  const uint16_t* Vb;   // [G][rows][128]
+  const uint16_t* dOb;  // [rows][H][128] bf16
+  const float2* stat;   // [rows][H]: (lse*log2(e), D)
+  float* dKh;           // [rows][G][192] fp32: dK^ (content | RoPE)
+  float* dV;            // [rows][G][128] fp32
+  float* dQh;           // [rows][H][192] fp32: dQ^
+  const int2* seqs;     // [n_seq] (start row, length)
+  int n_rows, H, G;
   float tau;
 };
 
@@ -259,12 +265,15 @@ __global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
   __shared__ __attribute__((aligned(16))) char q_st[32 * kKPitch];
   __shared__ __attribute__((aligned(16))) char o_st[32 * kVPitch];
   __shared__ float2 st_s[32];
-  const int kt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x, hf = lane >> 5, n = lane & 31;
+  const int kt = blockIdx.x, g = blockIdx.y;
+  const int2 sq = a.seqs[blockIdx.z];  // (start row, length), uniform
+  const int T = sq.y;
   const int key0 = kt * kFaKeys;
+  if (key0 >= T) return;  // whole workgroup: past this sequence
+  const int lane = threadIdx.x, hf = lane >> 5, n = lane & 31;
   const int key = key0 + n;
-  const int keyc = min(key, a.T - 1);
-  const size_t kv_row = ((size_t)b * a.G + g) * a.T + keyc;
+  const int keyc = min(key, T - 1);
+  const size_t kv_row = (size_t)g * a.n_rows + sq.x + keyc;
   bf16x8 kreg[kQkSteps], vreg[kFaDv / 16];
 #pragma unroll
   for (int s = 0; s < kQkSteps; ++s) {
@@ -286,28 +295,28 @@ __global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dVT[mb][r] = 0.f;
 
-  const size_t seq_row0 = (size_t)b * a.T;
+  const size_t seq_row0 = sq.x;
   const int s16 = lane & 15, dblk = (lane >> 4) & 1;
-  for (int i0 = key0; i0 < a.T; i0 += 2) {
+  for (int i0 = key0; i0 < T; i0 += 2) {
     // stage 32 rows: token i0 + r/16, head 16g + r%16 (16 heads of a token are
     // contiguous); tokens past the sequence repeat its last token (masked)
     __syncthreads();  // the previous step's LDS reads are done
 #pragma unroll
     for (int u = 0; u < 12; ++u) {  // Q^: 768 chunks
       const int c = lane + 64 * u, row = c / 24, col = c % 24;
-      const int tok = min(i0 + (row >> 4), a.T - 1);
+      const int tok = min(i0 + (row >> 4), T - 1);
       const size_t qr = (seq_row0 + tok) * a.H + g * kFaHpg + (row & 15);
       *(uint4*)(q_st + row * kKPitch + col * 16) = load16(a.Qb + qr * kFaDqk + col * 8);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {  // d_o: 512 chunks
       const int c = lane + 64 * u, row = c / 16, col = c % 16;
-      const int tok = min(i0 + (row >> 4), a.T - 1);
+      const int tok = min(i0 + (row >> 4), T - 1);
       const size_t qr = (seq_row0 + tok) * a.H + g * kFaHpg + (row & 15);
       *(uint4*)(o_st + row * kVPitch + col * 16) = load16(a.dOb + qr * kFaDv + col * 8);
     }
     if (lane < 32) {
-      const int tok = min(i0 + (lane >> 4), a.T - 1);
+      const int tok = min(i0 + (lane >> 4), T - 1);
       st_s[lane] = a.stat[(seq_row0 + tok) * a.H + g * kFaHpg + (lane & 15)];
     }
     __syncthreads();
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
     // reg r holds row 8(r/4) + 4hf + r%4 = token i0 + row/16, head row%16
     // wave-uniform: only steps whose tokens can precede a key of the tile, or
     // run past the sequence, or a tile past the sequence, mask
-    const bool masked = i0 < key0 + kFaKeys - 1 || i0 + 1 >= a.T || key0 + kFaKeys > a.T;
+    const bool masked = i0 < key0 + kFaKeys - 1 || i0 + 1 >= T || key0 + kFaKeys > T;
     bf16x8 pb[2], db[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
       const int tok = i0 + (row >> 4);
       const float2 sd = st_s[row];
       float p = __builtin_amdgcn_exp2f(sacc[r] - sd.x);
-      if (masked && !(key <= tok && tok < a.T && key < a.T)) p = 0.f;
+      if (masked && !(key <= tok && tok < T && key < T)) p = 0.f;
       pb[r >> 3][r & 7] = (__bf16)p;
       db[r >> 3][r & 7] = (__bf16)(p * (dpacc[r] - sd.y));
     }
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
       }
     }
   }
-  if (key >= a.T) return;
+  if (key >= T) return;
   // lane holds column `key`; reg r of block mb is dim 32mb + 8(r/4) + 4hf + r%4.
   // Q^ carries tau*log2(e): dK^ = tau sum dS Q^ = (sum dS Qb) / log2(e).
   const size_t out_row = (seq_row0 + key) * a.G + g;
@@ -399,14 +408,17 @@ __global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
 __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
   __shared__ __attribute__((aligned(16))) char k_st[2][kFaKeys * kKPitch];
   __shared__ __attribute__((aligned(16))) char v_st[2][kFaKeys * kVPitch];
-  const int qb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int qb = blockIdx.x, g = blockIdx.y;
+  const int2 sq = a.seqs[blockIdx.z];  // (start row, length), uniform
+  const int T = sq.y;
+  if (qb * kFaTok >= T) return;  // whole workgroup: past this sequence
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hf = lane >> 5, n = lane & 31;
   const int i = qb * kFaTok + 2 * wave + (n >> 4);
   const int h = g * kFaHpg + (n & 15);
-  const bool valid = i < a.T;
-  const size_t qrow = ((size_t)b * a.T + (valid ? i : a.T - 1)) * a.H + h;
+  const bool valid = i < T;
+  const size_t qrow = ((size_t)sq.x + (valid ? i : T - 1)) * a.H + h;
   bf16x8 q[kQkSteps], go[kFaDv / 16];
 #pragma unroll
   for (int s = 0; s < kQkSteps; ++s) {
@@ -419,21 +431,21 @@ __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
     go[s] = *(const bf16x8*)&v;
   }
   const float2 sd = a.stat[qrow];
-  const int i_last = min(qb * kFaTok + kFaTok - 1, a.T - 1);
+  const int i_last = min(qb * kFaTok + kFaTok - 1, T - 1);
   const int n_kt = i_last / kFaKeys + 1;
-  const uint16_t* kbase = a.Kb + ((size_t)b * a.G + g) * a.T * kFaDqk;
-  const uint16_t* vbase = a.Vb + ((size_t)b * a.G + g) * a.T * kFaDv;
+  const uint16_t* kbase = a.Kb + ((size_t)g * a.n_rows + sq.x) * kFaDqk;
+  const uint16_t* vbase = a.Vb + ((size_t)g * a.n_rows + sq.x) * kFaDv;
   uint4 kr[3], vr[2];
   auto load_tile = [&](int kt) {
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int c = tid + 256 * u, row = c / 24, col = c % 24;
-      kr[u] = load16(kbase + (size_t)min(kt * kFaKeys + row, a.T - 1) * kFaDqk + col * 8);
+      kr[u] = load16(kbase + (size_t)min(kt * kFaKeys + row, T - 1) * kFaDqk + col * 8);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int c = tid + 256 * u, row = c / 16, col = c % 16;
-      vr[u] = load16(vbase + (size_t)min(kt * kFaKeys + row, a.T - 1) * kFaDv + col * 8);
+      vr[u] = load16(vbase + (size_t)min(kt * kFaKeys + row, T - 1) * kFaDv + col * 8);
     }
   };
   auto store_tile = [&](int buf) {
@@ -485,7 +497,7 @@ __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int key = key0 + 8 * (r >> 2) + (r & 3);
       float p = __builtin_amdgcn_exp2f(sacc[r] - sd.x);
-      if (masked && (key > i || key >= a.T)) p = 0.f;
+      if (masked && (key > i || key >= T)) p = 0.f;
       db[r >> 3][r & 7] = (__bf16)(p * (dpacc[r] - sd.y));
     }
     const char* tkb = ks + (4 * hf + (s16 >> 2)) * kKPitch + 32 * dblk + 8 * (s16 & 3);
@@ -522,10 +534,12 @@ bool train_mfma_shape(const Cfg& c) {
   return c.dtype == QKMLA_BF16 && c.hpg == kFaHpg && c.dc + c.dr == kFaDqk && c.dv == kFaDv;
 }
 
-hipError_t launch_flash_fwd(const Cfg& c, int B, int T, const void* Qb, const void* Kb,
+hipError_t launch_flash_fwd(const Cfg& c, const FlashSeqs& q, const void* Qb, const void* Kb,
                             const void* Vb, float* o, float* lse, hipStream_t s) {
-  FaArgs a{(const uint16_t*)Qb, (const uint16_t*)Kb, (const uint16_t*)Vb, o, lse, T, c.H, c.G};
-  hipLaunchKernelGGL(flash_fwd_kernel, dim3((T + kFaTok - 1) / kFaTok, c.G, B), dim3(256), 0, s, a);
+  FaArgs a{(const uint16_t*)Qb, (const uint16_t*)Kb, (const uint16_t*)Vb, o, lse, q.seqs,
+           q.n_rows, c.H, c.G};
+  hipLaunchKernelGGL(flash_fwd_kernel, dim3((q.max_len + kFaTok - 1) / kFaTok, c.G, q.n_seq),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -533,19 +547,19 @@ hipError_t launch_flash_fwd(const Cfg& c, int B, int T, const void* Qb, const vo
 
 namespace qkmla {
 
-hipError_t launch_flash_bwd(const Cfg& c, int B, int T, const void* Qb, const void* Kb,
+hipError_t launch_flash_bwd(const Cfg& c, const FlashSeqs& q, const void* Qb, const void* Kb,
                             const void* Vb, const float* o, const float* lse, const float* d_o,
                             void* dOb, void* stat, float* dKh, float* dV, float* dQh,
                             hipStream_t s) {
-  const int rows_h = B * T * c.H;
+  const int rows_h = q.n_rows * c.H;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((rows_h + 3) / 4), dim3(256), 0, s, rows_h, o, lse,
                      d_o, (uint16_t*)dOb, (float2*)stat);
   FbArgs a{(const uint16_t*)Qb, (const uint16_t*)Kb, (const uint16_t*)Vb, (const uint16_t*)dOb,
-           (const float2*)stat, dKh, dV, dQh, T, c.H, c.G, c.tau};
-  hipLaunchKernelGGL(flash_bwd_kv_kernel, dim3((T + kFaKeys - 1) / kFaKeys, c.G, B), dim3(64), 0,
-                     s, a);
-  hipLaunchKernelGGL(flash_bwd_q_kernel, dim3((T + kFaTok - 1) / kFaTok, c.G, B), dim3(256), 0, s,
-                     a);
+           (const float2*)stat, dKh, dV, dQh, q.seqs, q.n_rows, c.H, c.G, c.tau};
+  hipLaunchKernelGGL(flash_bwd_kv_kernel,
+                     dim3((q.max_len + kFaKeys - 1) / kFaKeys, c.G, q.n_seq), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(flash_bwd_q_kernel, dim3((q.max_len + kFaTok - 1) / kFaTok, c.G, q.n_seq),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -211,3 +211,14 @@ def train_inputs(shape: Shape, batch: int, seq_len: int, seed: int) -> dict:
     out["q_rope"] = _store(rng.standard_normal((B, T, H, dr), dtype=np.float32), s.dtype)
     out["d_o"] = rng.standard_normal((B, T, H, dv), dtype=np.float32)
     return out
+
+
+def train_inputs_varlen(shape: Shape, lengths: Sequence[int], seed: int) -> dict:
+    """train_inputs for packed sequences of the given lengths: the per-token
+    arrays become [sum(lengths)][...] (sequence s on the rows after those of
+    sequences 0..s-1), drawn as one batch of sum(lengths) tokens."""
+    total = int(sum(int(L) for L in lengths))
+    d = train_inputs(shape, 1, max(total, 1), seed)
+    for n in ("c", "q_c", "q_rope", "k_rope", "d_o"):
+        d[n] = np.ascontiguousarray(d[n][0, :total])
+    return d

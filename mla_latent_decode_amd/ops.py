@@ -79,6 +79,11 @@ def _load():
         "qkmla_train_forward": (I32, [C, I32, I32, ctypes.POINTER(_TrainInputs), P, SZ, P, P, P]),
         "qkmla_train_backward": (I32, [C, I32, I32, ctypes.POINTER(_TrainInputs), P, P, P, P, SZ,
                                        ctypes.POINTER(_TrainGrads), P]),
+        "qkmla_train_workspace_size_varlen": (SZ, [C, I32, I32, I32]),
+        "qkmla_train_forward_varlen": (I32, [C, I32, P, I32, I32, ctypes.POINTER(_TrainInputs), P,
+                                             SZ, P, P, P, P]),
+        "qkmla_train_backward_varlen": (I32, [C, I32, P, I32, I32, ctypes.POINTER(_TrainInputs),
+                                              P, P, P, P, SZ, ctypes.POINTER(_TrainGrads), P, P]),
         "qkmla_out_proj": (I32, [C, I32, P, P, P, P]),
         "qkmla_plan": (I32, [C, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "qkmla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -376,12 +381,13 @@ def train_workspace_size(cfg: Config, batch: int, seq_len: int) -> int:
     return n
 
 
-def _train_inputs(cfg: Config, t: dict, B: int, T: int) -> _TrainInputs:
+def _train_inputs(cfg: Config, t: dict, lead: tuple) -> _TrainInputs:
+    """lead: the token dims, (B, T) or (total,) for packed sequences."""
     H, G, r, dc, dr, dv = (cfg.n_heads, cfg.n_groups, cfg.latent_rank, cfg.head_dim,
                            cfg.rope_dim, cfg.v_head_dim)
     dt, f32 = cfg.torch_dtype, torch.float32
-    spec = {"c": ((B, T, r), dt), "q_c": ((B, T, H, dc), dt), "q_rope": ((B, T, H, dr), dt),
-            "k_rope": ((B, T, dr), dt), "w_uk": ((G, r, dc), f32), "w_uv": ((G, r, dv), dt),
+    spec = {"c": (lead + (r,), dt), "q_c": (lead + (H, dc), dt), "q_rope": (lead + (H, dr), dt),
+            "k_rope": (lead + (dr,), dt), "w_uk": ((G, r, dc), f32), "w_uv": ((G, r, dv), dt),
             "gamma_q": ((dc,), f32), "gamma_k": ((dc,), f32), "gamma_q_rope": ((dr,), f32),
             "gamma_k_rope": ((dr,), f32)}
     return _TrainInputs(*[_ptr(t.get(n), shp, dtp, n) for n, (shp, dtp) in spec.items()])
@@ -396,7 +402,7 @@ def train_forward(cfg: Config, inputs: dict, workspace, o=None, lse=None):
         o = torch.empty((B, T, H, cfg.v_head_dim), dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    ins = _train_inputs(cfg, inputs, B, T)
+    ins = _train_inputs(cfg, inputs, (B, T))
     _check(_lib.qkmla_train_forward(
         ctypes.byref(cfg.c()), B, T, ctypes.byref(ins),
         _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
@@ -414,7 +420,7 @@ def train_backward(cfg: Config, inputs: dict, o, lse, d_o, workspace, grads: Opt
         grads = {"d_" + n: torch.empty(tuple(inputs[n].shape), dtype=torch.float32, device=dev)
                  for n in ("c", "q_c", "q_rope", "k_rope", "w_uk", "w_uv", "gamma_q", "gamma_k",
                            "gamma_q_rope", "gamma_k_rope")}
-    ins = _train_inputs(cfg, inputs, B, T)
+    ins = _train_inputs(cfg, inputs, (B, T))
     gs = _TrainGrads(*[_ptr(grads[n], tuple(inputs[n[2:]].shape), torch.float32, n)
                        for n in TRAIN_GRAD_NAMES])
     _check(_lib.qkmla_train_backward(
@@ -424,4 +430,56 @@ def train_backward(cfg: Config, inputs: dict, o, lse, d_o, workspace, grads: Opt
         _ptr(d_o, (B, T, H, cfg.v_head_dim), torch.float32, "d_o"),
         _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(), ctypes.byref(gs),
         _stream()), "qkmla_train_backward")
+    return grads
+
+
+def train_workspace_size_varlen(cfg: Config, n_seqs: int, total_tokens: int,
+                                max_seq_len: int) -> int:
+    n = _lib.qkmla_train_workspace_size_varlen(ctypes.byref(cfg.c()), n_seqs, total_tokens,
+                                               max_seq_len)
+    if n == 0:
+        raise QkmlaError("qkmla_train_workspace_size_varlen: " + _lib.qkmla_last_error().decode())
+    return n
+
+
+def train_forward_varlen(cfg: Config, inputs: dict, cu_seqlens, max_seq_len: int, workspace,
+                         o=None, lse=None, status=None):
+    """Packed sequences: per-token inputs [total][...], cu_seqlens device int32
+    [n_seqs + 1].  Returns (o [total][H][d_v], lse [total][H])."""
+    total = inputs["c"].shape[0]
+    n_seqs = cu_seqlens.numel() - 1
+    H, dev = cfg.n_heads, inputs["c"].device
+    if o is None:
+        o = torch.empty((total, H, cfg.v_head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((total, H), dtype=torch.float32, device=dev)
+    ins = _train_inputs(cfg, inputs, (total,))
+    _check(_lib.qkmla_train_forward_varlen(
+        ctypes.byref(cfg.c()), n_seqs, _ptr(cu_seqlens, None, torch.int32, "cu_seqlens"), total,
+        max_seq_len, ctypes.byref(ins), _ptr(workspace, None, torch.uint8, "workspace"),
+        workspace.numel(), _ptr(o, (total, H, cfg.v_head_dim), torch.float32, "o"),
+        _ptr(lse, (total, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
+        _stream()), "qkmla_train_forward_varlen")
+    return o, lse
+
+
+def train_backward_varlen(cfg: Config, inputs: dict, cu_seqlens, max_seq_len: int, o, lse, d_o,
+                          workspace, grads: Optional[dict] = None, status=None):
+    total = inputs["c"].shape[0]
+    n_seqs = cu_seqlens.numel() - 1
+    H, dev = cfg.n_heads, inputs["c"].device
+    if grads is None:
+        grads = {"d_" + n: torch.empty(tuple(inputs[n].shape), dtype=torch.float32, device=dev)
+                 for n in ("c", "q_c", "q_rope", "k_rope", "w_uk", "w_uv", "gamma_q", "gamma_k",
+                           "gamma_q_rope", "gamma_k_rope")}
+    ins = _train_inputs(cfg, inputs, (total,))
+    gs = _TrainGrads(*[_ptr(grads[n], tuple(inputs[n[2:]].shape), torch.float32, n)
+                       for n in TRAIN_GRAD_NAMES])
+    _check(_lib.qkmla_train_backward_varlen(
+        ctypes.byref(cfg.c()), n_seqs, _ptr(cu_seqlens, None, torch.int32, "cu_seqlens"), total,
+        max_seq_len, ctypes.byref(ins), _ptr(o, (total, H, cfg.v_head_dim), torch.float32, "o"),
+        _ptr(lse, (total, H), torch.float32, "lse"),
+        _ptr(d_o, (total, H, cfg.v_head_dim), torch.float32, "d_o"),
+        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(), ctypes.byref(gs),
+        _ptr(status, (1,), torch.int32, "status"), _stream()), "qkmla_train_backward_varlen")
     return grads

@@ -122,3 +122,39 @@ def train_reference(inputs: Dict[str, np.ndarray], d_o: Optional[np.ndarray] = N
         for n, g in zip(INPUT_NAMES, grads):
             out["d_" + n] = (np.zeros(ts[n].shape) if g is None else g.numpy())
     return out
+
+
+def train_reference_varlen(inputs: Dict[str, np.ndarray], lengths, d_o: Optional[np.ndarray] = None,
+                           **kw):
+    """Packed sequences: the per-token arrays are [total][...] with sequence s
+    on rows sum(lengths[:s]) .. + lengths[s] - 1, each token at its position
+    in its own sequence.  Each sequence is ``train_reference`` on its rows
+    (batch 1); the loss is the sum over sequences, so the per-token gradients
+    are those of each sequence and the weight gradients their sums.
+    Returns the same keys as ``train_reference``, per-token arrays packed."""
+    per_tok = ("c", "q_c", "q_rope", "k_rope")
+    weights = [n for n in INPUT_NAMES if n not in per_tok]
+    total = sum(int(L) for L in lengths)
+    first = inputs["q_c"]
+    H, dv = first.shape[1], inputs["w_uv"].shape[-1]
+    out = {"o": np.zeros((total, H, dv)), "lse": np.zeros((total, H))}
+    if d_o is not None:
+        for n in INPUT_NAMES:
+            out["d_" + n] = np.zeros(np.shape(inputs[n]))
+    row = 0
+    for L in lengths:
+        L = int(L)
+        if L == 0:
+            continue
+        seq = {n: inputs[n][row:row + L][None] for n in per_tok}
+        seq.update({n: inputs[n] for n in weights})
+        r = train_reference(seq, None if d_o is None else d_o[row:row + L][None], **kw)
+        out["o"][row:row + L] = r["o"][0]
+        out["lse"][row:row + L] = r["lse"][0]
+        if d_o is not None:
+            for n in per_tok:
+                out["d_" + n][row:row + L] = r["d_" + n][0]
+            for n in weights:
+                out["d_" + n] += r["d_" + n]
+        row += L
+    return out

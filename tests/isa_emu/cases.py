@@ -387,6 +387,94 @@ def run_train(dev, shape, B, T, seed, label, qk_norm=True, forward_only=False, t
         raise AssertionError(f"{label}: {err} {gerr}")
 
 
+def run_train_varlen(dev, shape, lengths, seed, label, tol, qk_norm=True, bad_cu=False):
+    """Packed sequences through the *_varlen entry points against the oracle's
+    per-sequence sum.  bad_cu: cu_seqlens that overrun the packed rows must
+    set the status bit and stay in bounds (outputs not compared)."""
+    from oracle.qkmla_train_oracle import train_reference_varlen
+    from mla_latent_decode_amd.inputs import train_inputs_varlen
+    from isa_emu.device import CConfig, SIGNATURES, bf16_bits
+    P = ctypes.c_void_p
+    lib = dev.lib
+    for n, (rt, at) in SIGNATURES.items():
+        if hasattr(lib, n):
+            getattr(lib, n).restype, getattr(lib, n).argtypes = rt, at
+    bf = shape.dtype == "bf16"
+    cfg = CConfig(shape.n_heads, shape.n_groups, shape.latent_rank, shape.head_dim,
+                  shape.rope_dim, shape.v_head_dim, 1 if bf else 0, int(qk_norm), 1e-6, 0.0,
+                  10000.0)
+    inp = train_inputs_varlen(shape, lengths, seed)
+    d_o = inp.pop("d_o")
+    total, n_seq, max_len = int(sum(lengths)), len(lengths), max(max(lengths), 1)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    if bad_cu:
+        cu[-1] = total + 5  # overruns the packed rows
+    store = (lambda x: bf16_bits(np.asarray(x, np.float32))) if bf else (
+        lambda x: np.asarray(x, np.float32))
+    dv = {}
+    for n in TRAIN_IN:
+        fp32 = n.startswith("gamma") or n == "w_uk"
+        dv[n] = dev.put(np.asarray(inp[n], np.float32) if fp32 else store(inp[n]), "varlen " + n)
+    ins = CTrainInputs(*[dv[n].ctypes.data for n in TRAIN_IN])
+    H, dvh = shape.n_heads, shape.v_head_dim
+    o = dev.empty((total, H, dvh), np.float32, "varlen o", fill=0xFF)
+    lse = dev.empty((total, H), np.float32, "varlen lse", fill=0xFF)
+    gdo = dev.put(d_o.astype(np.float32), "varlen d_o")
+    cud = dev.put(cu, "cu_seqlens")
+    status = dev.empty((1,), np.int32, "varlen status", fill=0)
+    ws_n = lib.qkmla_train_workspace_size_varlen(ctypes.byref(cfg), n_seq, total, max_len)
+    ws = dev.empty((ws_n,), np.uint8, "varlen workspace", fill=0xCD)
+
+    def call(name, *args):
+        r = getattr(lib, name)(*args)
+        if r != 0:
+            raise RuntimeError(f"{name} returned {r}: {lib.qkmla_last_error().decode()}")
+
+    call("qkmla_train_forward_varlen", ctypes.byref(cfg), n_seq, P(cud.ctypes.data), total,
+         max_len, ctypes.byref(ins), P(ws.ctypes.data), ws_n, P(o.ctypes.data),
+         P(lse.ctypes.data), P(status.ctypes.data), None)
+    grads = {n: dev.empty(np.shape(inp[n]), np.float32, "varlen d_" + n, fill=0xFF)
+             for n in TRAIN_IN}
+    gs = CTrainGrads(*[grads[n].ctypes.data for n in TRAIN_IN])
+    call("qkmla_train_backward_varlen", ctypes.byref(cfg), n_seq, P(cud.ctypes.data), total,
+         max_len, ctypes.byref(ins), P(o.ctypes.data), P(lse.ctypes.data), P(gdo.ctypes.data),
+         P(ws.ctypes.data), ws_n, ctypes.byref(gs), P(status.ctypes.data), None)
+    if bad_cu:
+        ok = int(status[0]) == 1
+        print(f"[{'ok' if ok else 'FAIL'}] {label}: status {int(status[0])} (expected 1), "
+              "all accesses in bounds", flush=True)
+        assert ok, label
+        return
+    assert int(status[0]) == 0, f"{label}: status {int(status[0])}"
+    ref = train_reference_varlen(inp, lengths, d_o, qk_norm=qk_norm, eps=1e-6, base=10000.0)
+    eo = float(np.max(oracle.rowwise_rel_err(o.reshape(-1, dvh), ref["o"].reshape(-1, dvh))))
+    el = float(np.max(np.abs(lse - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))))
+    gerr = {}
+    for n in TRAIN_IN:
+        r_ = ref["d_" + n]
+        scale = float(np.max(np.abs(r_))) if np.any(r_) else 1.0
+        gerr[n] = float(np.max(np.abs(grads[n] - r_))) / scale
+    ok = eo <= tol["o"] and el <= tol["lse"] and all(v <= tol["grad"] for v in gerr.values())
+    print(f"[{'ok' if ok else 'FAIL'}] {label}: o {eo:.2e} lse {el:.2e} grads " +
+          " ".join(f"{k} {v:.1e}" for k, v in gerr.items()), flush=True)
+    if not ok:
+        raise AssertionError(f"{label}: o {eo} lse {el} {gerr}")
+
+
+@case
+def train_varlen(dev):
+    """Packed sequences of different lengths (one empty) through the
+    *_varlen entry points: row-parallel fp32 path and the MFMA path of the
+    bf16 layer (sequences spanning key tiles and query blocks), and
+    cu_seqlens overrunning the rows (status bit, accesses in bounds)."""
+    run_train_varlen(dev, Shape(4, 2, 12, 6, 4, 5, "f32"), [5, 0, 9, 1], 620,
+                     "train varlen fp32 (5, 0, 9, 1)", TRAIN_TOL)
+    run_train_varlen(dev, DSV3, [19, 0, 34], 621, "train varlen MFMA (19, 0, 34)",
+                     dict(o=2e-2, lse=5e-2, grad=2e-2))
+    run_train_varlen(dev, Shape(4, 2, 12, 6, 4, 5, "f32"), [3, 4], 622,
+                     "train varlen fp32, cu past the rows", TRAIN_TOL, bad_cu=True)
+
+
 @case
 def train_fwd_bwd(dev):
     """Training forward and backward (explicit form, causal): fp32 and bf16

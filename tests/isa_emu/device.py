@@ -171,6 +171,11 @@ SIGNATURES = {
     "qkmla_train_workspace_size": (_SZ, [_C, _I32, _I32]),
     "qkmla_train_forward": (_I32, [_C, _I32, _I32, _P, _P, _SZ, _P, _P, _P]),
     "qkmla_train_backward": (_I32, [_C, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "qkmla_train_workspace_size_varlen": (_SZ, [_C, _I32, _I32, _I32]),
+    "qkmla_train_forward_varlen": (_I32, [_C, _I32, _P, _I32, _I32, _P, _P, _SZ, _P, _P, _P,
+                                          _P]),
+    "qkmla_train_backward_varlen": (_I32, [_C, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
+                                           _P, _P, _P]),
     "qkmla_out_proj": (_I32, [_C, _I32, _P, _P, _P, _P]),
     "qkmla_last_error": (ctypes.c_char_p, []),
 }

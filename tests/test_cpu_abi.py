@@ -37,7 +37,7 @@ def _ops():
 
 def test_abi_version_and_status_strings():
     ops = _ops()
-    assert ops.abi_version() == 4
+    assert ops.abi_version() == 5
     assert ops._lib.qkmla_status_string(0) == b"ok"
     assert ops._lib.qkmla_status_string(3) == b"workspace too small"
 
@@ -226,3 +226,36 @@ def test_train_entry_points_validate_on_the_host():
     st = lib.qkmla_train_backward(ctypes.byref(cfg.c()), 1, 7, ctypes.byref(ins), p, p, p, p,
                                   need - 256, ctypes.byref(grads), None)
     assert st == 3
+
+
+def test_varlen_train_entry_points_validate_on_the_host():
+    """Packed-sequence training calls: empty batches are no-ops, cu_seqlens
+    must be given and aligned, max_seq_len >= 1, at most 65535 sequences,
+    and the workspace is checked against the packed size."""
+    ops = _ops()
+    lib = ops._lib
+    cfg = _cfg(n_heads=4, n_groups=2, latent_rank=12, head_dim=6, rope_dim=4, v_head_dim=5,
+               dtype="f32")
+    p = 0x1000
+    ins = ops._TrainInputs(*([p] * 10))
+    c = ctypes.byref(cfg.c())
+    assert lib.qkmla_train_forward_varlen(c, 0, None, 0, 1, None, None, 0, None, None, None,
+                                          None) == 0
+    assert lib.qkmla_train_forward_varlen(c, 3, None, 0, 4, None, None, 0, None, None, None,
+                                          None) == 0  # no tokens
+    assert lib.qkmla_train_forward_varlen(c, 2, None, 9, 5, ctypes.byref(ins), p, 1 << 20, p, p,
+                                          None, None) == 1
+    assert b"cu_seqlens" in lib.qkmla_last_error()
+    assert lib.qkmla_train_forward_varlen(c, 2, p + 2, 9, 5, ctypes.byref(ins), p, 1 << 20, p, p,
+                                          None, None) == 1
+    assert lib.qkmla_train_forward_varlen(c, 2, p, 9, 0, ctypes.byref(ins), p, 1 << 20, p, p,
+                                          None, None) == 1
+    assert lib.qkmla_train_forward_varlen(c, 70000, p, 70000, 1, ctypes.byref(ins), p, 1 << 30, p,
+                                          p, None, None) == 2
+    need = ops.train_workspace_size_varlen(cfg, 2, 9, 5)
+    assert need > 0
+    assert lib.qkmla_train_forward_varlen(c, 2, p, 9, 5, ctypes.byref(ins), p, 16, p, p, None,
+                                          None) == 3
+    grads = ops._TrainGrads(*([p] * 10))
+    assert lib.qkmla_train_backward_varlen(c, 2, p, 9, 5, ctypes.byref(ins), p, p, p, p, need - 256,
+                                           ctypes.byref(grads), None, None) == 3

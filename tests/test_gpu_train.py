@@ -133,3 +133,45 @@ def test_train_full_length_sampled_and_invariants():
     for k, v in worst.items():
         assert v <= 1e-3, (k, v)
     assert all(np.isfinite(v).all() for v in g_np.values())
+
+
+@pytest.mark.parametrize("shape_name,lengths,tol", [
+    ("small", (5, 0, 130, 1, 33), "fp32"), ("dsv3", (70, 0, 1, 257, 8), "bf16")])
+def test_train_packed_sequences(shape_name, lengths, tol):
+    """Packed sequences of different lengths (one empty, one of a single
+    token) through qkmla_train_forward_varlen / _backward_varlen against the
+    oracle's per-sequence sum."""
+    from oracle.qkmla_train_oracle import train_reference_varlen
+    import oracle
+    from mla_latent_decode_amd.inputs import train_inputs_varlen
+    shape = Shape(4, 2, 32, 16, 8, 16, "f32") if shape_name == "small" else DSV3
+    tl = FP32_TOL if tol == "fp32" else BF16_TOL
+    print(f"\n[train varlen {shape_name} {lengths}]", flush=True)
+    cfg = ops.Config.from_shape(shape)
+    inp = train_inputs_varlen(shape, lengths, 730)
+    d_o = inp.pop("d_o")
+    dt = cfg.torch_dtype
+    dev = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).to(
+        "cuda", torch.float32 if (n == "w_uk" or n.startswith("gamma")) else dt) for n in NAMES}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    total, mx = int(sum(lengths)), max(lengths)
+    ws = torch.empty((ops.train_workspace_size_varlen(cfg, len(lengths), total, mx),),
+                     dtype=torch.uint8, device="cuda")
+    status = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    o, lse = ops.train_forward_varlen(cfg, dev, cu, mx, ws, status=status)
+    grads = ops.train_backward_varlen(cfg, dev, cu, mx, o, lse, torch.from_numpy(d_o).cuda(), ws,
+                                      status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ref = train_reference_varlen(inp, lengths, d_o, eps=cfg.eps, base=cfg.rope_base)
+    dv = shape.v_head_dim
+    err_o = worst_of(oracle.rowwise_rel_err(o.cpu().numpy().reshape(-1, dv),
+                                            ref["o"].reshape(-1, dv)))
+    err_l = worst_of(np.abs(lse.cpu().numpy() - ref["lse"]))
+    print(f"  o {err_o:.2e} lse {err_l:.2e}", flush=True)
+    assert err_o <= tl["o"] and err_l <= max(tl["lse"], 2e-5)
+    for n in NAMES:
+        r_ = ref["d_" + n]
+        scale = float(np.max(np.abs(r_))) if np.any(r_) else 1.0
+        e = worst_of(np.abs(grads["d_" + n].cpu().numpy() - r_)) / scale
+        assert e <= tl["grad"], (n, e)

@@ -119,3 +119,34 @@ def test_future_tokens_do_not_change_earlier_rows():
     b = train_reference(inp)
     assert np.array_equal(a["o"][:, :-1], b["o"][:, :-1])
     assert not np.allclose(a["o"][:, -1], b["o"][:, -1])
+
+
+def test_packed_sequences_equal_the_batched_form():
+    """Equal lengths packed end to end give the batched forward and gradients
+    (the per-sequence sum is the batch's loss)."""
+    from oracle.qkmla_train_oracle import train_reference_varlen
+    B, T = 3, 5
+    inp = train_inputs(SMALL, B, T, seed=61)
+    d_o = inp.pop("d_o")
+    ref = train_reference(inp, d_o)
+    packed = {n: (v.reshape((B * T,) + v.shape[2:]) if n in ("c", "q_c", "q_rope", "k_rope")
+                  else v) for n, v in inp.items()}
+    var = train_reference_varlen(packed, [T] * B, d_o.reshape((B * T,) + d_o.shape[2:]))
+    np.testing.assert_allclose(var["o"], ref["o"].reshape(var["o"].shape), rtol=1e-13, atol=1e-13)
+    for n in INPUT_NAMES:
+        np.testing.assert_allclose(var["d_" + n], ref["d_" + n].reshape(var["d_" + n].shape),
+                                   rtol=1e-12, atol=1e-12, err_msg=n)
+
+
+def test_packed_rows_do_not_see_other_sequences():
+    """A row of sequence 1 is unchanged when sequence 0's tokens change."""
+    from oracle.qkmla_train_oracle import train_reference_varlen
+    from mla_latent_decode_amd.inputs import train_inputs_varlen
+    lens = [4, 0, 3]
+    inp = train_inputs_varlen(SMALL, lens, seed=62)
+    a = train_reference_varlen(inp, lens)
+    for n in ("c", "q_c", "q_rope", "k_rope"):
+        inp[n][:4] += 1.0
+    b = train_reference_varlen(inp, lens)
+    assert np.array_equal(a["o"][4:], b["o"][4:])
+    assert not np.allclose(a["o"][:4], b["o"][:4])

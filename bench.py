@@ -274,9 +274,10 @@ def measure_next_rows(steps):
     """The rows beyond the decode step, each on the batch-16 x 4096 layer
     unless stated: bulk append of every cached token in one call, decode with
     s_q = 2 query rows per sequence, decode over 64-row pages of a shuffled
-    pool, and the explicit-form training forward and backward (1 x 1024
-    tokens).  Eager launches timed with HIP events; cache copies rotated as
-    in the headline."""
+    pool, the explicit-form training forward and backward (1 x 1024 tokens)
+    and a packed prefill forward (16 prompts of 256..2048 tokens).  Eager
+    launches timed with HIP events; cache copies rotated as in the
+    headline."""
     import torch
     from mla_latent_decode_amd import ops
     from mla_latent_decode_amd.layout import (append_bytes_per_token, cache_bytes_per_token,
@@ -377,6 +378,27 @@ def measure_next_rows(steps):
     ms_b = _event_ms(torch, lambda: ops.train_backward(cfg, ins, o, lse, d_o, wst, grads), 3,
                      warmup=1)
     ff, fb = train_attention_flops(s, Bt, T)
+    # packed prefill: 16 prompts of 256..2048 tokens, forward only
+    import numpy as np
+    lens = [int(x) for x in np.random.default_rng(5002).integers(256, 2048, size=16,
+                                                                 endpoint=True)]
+    total = sum(lens)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    pre = {n: (torch.randn((total,) + sh[2:], generator=g, device="cuda").to(dt)
+               if n in ("c", "q_c", "q_rope", "k_rope") else ins[n]) for n, sh in shp.items()}
+    wsv = torch.empty((ops.train_workspace_size_varlen(cfg, len(lens), total, max(lens)),),
+                      dtype=torch.uint8, device="cuda")
+    stv = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    ov, lv = ops.train_forward_varlen(cfg, pre, cu, max(lens), wsv, status=stv)
+    ms_v = _event_ms(torch, lambda: ops.train_forward_varlen(cfg, pre, cu, max(lens), wsv, ov, lv,
+                                                            stv), 3, warmup=1)
+    pairs_flops = sum(2 * H * L * (L + 1) // 2 * (s.head_dim + dr + s.v_head_dim) for L in lens)
+    out["prefill_packed_fwd"] = {"sequences": len(lens), "tokens": total, "ms": round(ms_v, 3),
+                                 "Mtokens_per_s": round(total / (ms_v * 1e-3) / 1e6, 2),
+                                 "attention_TFLOPs": round(pairs_flops / (ms_v * 1e-3) / 1e12, 2)}
+    if int(stv.item()):
+        raise RuntimeError(f"device status {int(stv.item())} in the packed prefill")
+    del pre, wsv, ov, lv
     out["train_fwd_bwd"] = {"batch": Bt, "seq_len": T, "fwd_ms": round(ms_f, 3),
                             "bwd_ms": round(ms_b, 3),
                             "fwd_attention_TFLOPs": round(ff / (ms_f * 1e-3) / 1e12, 2),

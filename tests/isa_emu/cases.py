@@ -473,6 +473,8 @@ def train_varlen(dev):
                      dict(o=2e-2, lse=5e-2, grad=2e-2))
     run_train_varlen(dev, Shape(4, 2, 12, 6, 4, 5, "f32"), [3, 4], 622,
                      "train varlen fp32, cu past the rows", TRAIN_TOL, bad_cu=True)
+    run_train_varlen(dev, DSV3, [3, 6], 623, "train varlen MFMA, cu past the rows", TRAIN_TOL,
+                     bad_cu=True)
 
 
 @case

@@ -390,3 +390,45 @@ def test_paged_full_size_long_context():
     assert int(status.item()) == 0
     assert np.array_equal(p_lat.view(B, H, -1).cpu().numpy(), o_lat)
     assert np.array_equal(p_lse.view(B, H).cpu().numpy(), lse)
+
+
+def test_decode_step_replays_in_a_hip_graph():
+    """The decode step (one-token append, decode, out_proj) captured in a HIP
+    graph: every replay, with eager work and synchronisations between them,
+    reproduces the eager step bit for bit.  The library issues no memset or
+    allocation, so nothing in the graph depends on a previous replay."""
+    inp = make_inputs(DSV3, (300, 77, 1000), seed=480)
+    cfg = ops.Config.from_shape(DSV3)
+    print("\n[graph replay] lens=(300, 77, 1000)", flush=True)
+    sess = DecodeSession(cfg, inp, hold_last=True)
+    sess.step_append()
+    o_lat, lse = sess.decode()
+    o = sess.out_proj()
+    torch.cuda.synchronize()
+    ref = (o_lat.clone(), lse.clone(), o.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        sess.step_append()
+        sess.decode()
+        out = sess.out_proj()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sess.step_append()
+        sess.decode()
+        out = sess.out_proj()
+    torch.cuda.synchronize()
+    for k in range(3):
+        sess.o_lat.fill_(float("nan"))
+        sess.lse.fill_(float("nan"))
+        out.fill_(float("nan"))
+        _ = torch.randn(1024, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sess.o_lat, ref[0]), k
+        assert torch.equal(sess.lse, ref[1]), k
+        assert torch.equal(out, ref[2]), k
+    assert int(sess.status.item()) == 0

@@ -403,7 +403,7 @@ def measure_next_rows(steps):
                             "bwd_ms": round(ms_b, 3),
                             "fwd_attention_TFLOPs": round(ff / (ms_f * 1e-3) / 1e12, 2),
                             "bwd_attention_TFLOPs": round(fb / (ms_b * 1e-3) / 1e12, 2),
-                            "kernels": "MFMA flash attention (bf16 operands), row-parallel norm and projection gradients"}
+                            "kernels": "MFMA attention and projection GEMMs (bf16 operands), row-parallel norms"}
     return out
 
 

@@ -219,6 +219,76 @@ def _traffic(workload_name):
     return e.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
+
+
+def pmc_workload(steps=5):
+    """What the two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) count:
+    `steps` headline decode steps over rotated cache copies, then three plain
+    copies of COPY_BYTES (torch's copy kernel) to calibrate the counters.
+    Prints one line naming the workload; no timing."""
+    import torch
+    b = Bench(1)
+    for _ in range(steps):
+        b.step()
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_workload": b.w.name, "decode_steps": steps, "copy_bytes": COPY_BYTES,
+                      "algorithmic_bytes_per_launch": b.bytes_qk}), flush=True)
+
+
+def _pmc_per_dispatch(csv_path, counter):
+    """{kernel name: mean counter value per dispatch} from a rocprofv3
+    counter-collection CSV (columns Dispatch_Id, Kernel_Name, Counter_Name,
+    Counter_Value; several rows of one dispatch are summed)."""
+    import csv
+    per = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name", "").split("[")[0] != counter:
+                continue
+            key = (row["Kernel_Name"], row.get("Dispatch_Id", ""))
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {k: sum(v) / len(v) for k, v in out.items()}
+
+
+def _is_qk_splitkv(name):
+    """The QK-norm instantiation of the split-KV kernel, demangled or not."""
+    return "decode_mfma_kernel" in name and ("<true" in name or "ILb1E" in name)
+
+
+def traffic_from_pmc(fetch_csv, write_csv, workload, algorithmic_bytes):
+    """HBM bytes per launch of the QK-norm split-KV kernel: its FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for the plain copy of COPY_BYTES in the same run."""
+    fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+
+    def pick(d, want, what):
+        names = [k for k in d if want(k)]
+        if len(names) != 1:
+            raise ValueError(f"expected one {what} kernel, found {names}")
+        return d[names[0]]
+    is_copy = lambda k: "copy" in k.lower() and "decode" not in k  # noqa: E731
+    f_dec, w_dec = pick(fetch, _is_qk_splitkv, "split-KV"), pick(write, _is_qk_splitkv, "split-KV")
+    f_cp, w_cp = pick(fetch, is_copy, "copy"), pick(write, is_copy, "copy")
+    kf, kw = COPY_BYTES / (f_cp * 1024.0), COPY_BYTES / (w_cp * 1024.0)
+    hbm = f_dec * 1024.0 * kf + w_dec * 1024.0 * kw
+    return {workload: {"hbm_bytes_per_launch": round(hbm), "fetch_KiB": f_dec, "write_KiB": w_dec,
+                       "copy_fetch_KiB": f_cp, "copy_write_KiB": w_cp,
+                       "scale_fetch": kf, "scale_write": kw,
+                       "algorithmic_bytes_per_launch": algorithmic_bytes,
+                       "traffic_over_algorithmic": round(hbm / algorithmic_bytes, 4),
+                       "kernel_src_sha256_16": _kernel_src_hash()}}
+
+
 def measure(cid, steps, warmup, graph=True):
     b = Bench(cid)
     ms_eager, wall = b.time_steps(steps, warmup)
@@ -450,7 +520,20 @@ def main():
                     help="skip the bulk-append, s_q=2, paged and training measurements")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP-graph replay of the step)")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="run only what the rocprofv3 --pmc passes count (decode steps and a "
+                         "calibration copy)")
+    ap.add_argument("--traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "ALGO_BYTES"),
+                    help="write the split-KV kernel's HBM traffic from two --pmc runs' CSVs "
+                         "into profiles/decode_splitkv_traffic.json (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic:
+        from mla_latent_decode_amd.inputs import WORKLOADS
+        t = traffic_from_pmc(args.traffic[0], args.traffic[1], WORKLOADS[1].name,
+                             int(args.traffic[2]))
+        json.dump(t, open(TRAFFIC_FILE, "w"), indent=1)
+        print(json.dumps(t))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path is a single-GPU kernel library)", file=sys.stderr)
@@ -459,6 +542,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_workload:
+        pmc_workload()
+        return
     b, res, ms_qk, k_ms, _ = measure(args.workload, args.steps, args.warmup, not args.no_graph)
     print(f"[bench] headline {res}", file=sys.stderr, flush=True)
     achieved = b.bytes_qk / (k_ms * 1e-3) / 1e9

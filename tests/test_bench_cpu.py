@@ -32,3 +32,31 @@ def test_training_flops_count_every_causal_pair():
     f, bwd = train_attention_flops(DSV3, B, T)
     assert f == 2 * pairs * (192 + 128)
     assert bwd == 2 * pairs * (3 * 192 + 2 * 128)
+
+
+def test_traffic_from_pmc_counters(tmp_path):
+    """The split-KV kernel's HBM bytes from two counter-collection CSVs: each
+    counter is scaled by what it reads for the 1 GiB calibration copy, rows of
+    one dispatch are summed and dispatches averaged."""
+    import bench
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+    dec = "void qkmla::(anonymous namespace)::decode_mfma_kernel<true, 4>(Args)"
+    plain = "void qkmla::(anonymous namespace)::decode_mfma_kernel<false, 4>(Args)"
+    cp = "void at::native::direct_copy_kernel_cuda(at::TensorIteratorBase&)"
+    gib_kib = (1 << 30) / 1024
+    fetch = head + "".join([
+        f'1,"{dec}",FETCH_SIZE,60000\n', f'1,"{dec}",FETCH_SIZE,20000\n',  # one dispatch, 2 rows
+        f'2,"{dec}",FETCH_SIZE,82000\n',
+        f'3,"{plain}",FETCH_SIZE,1\n',
+        f'4,"{cp}",FETCH_SIZE,{gib_kib * 1.25}\n'])   # the counter reads 25% high
+    write = head + "".join([
+        f'1,"{dec}",WRITE_SIZE,4000\n', f'2,"{dec}",WRITE_SIZE,6000\n',
+        f'4,"{cp}",WRITE_SIZE,{gib_kib}\n'])
+    (tmp_path / "f.csv").write_text(fetch)
+    (tmp_path / "w.csv").write_text(write)
+    t = bench.traffic_from_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "w1", 77594624)
+    e = t["w1"]
+    assert abs(e["fetch_KiB"] - 81000) < 1e-9 and abs(e["write_KiB"] - 5000) < 1e-9
+    expect = 81000 * 1024 / 1.25 + 5000 * 1024
+    assert abs(e["hbm_bytes_per_launch"] - expect) <= 1
+    assert e["kernel_src_sha256_16"] == bench._kernel_src_hash()

@@ -58,6 +58,37 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *(const uint4*)p;
 }
 
+// One 32-key tile of K^ and V: 768 + 512 chunks of 16 B, 3 + 2 per thread of a
+// 256-thread workgroup, loaded to registers and stored to a padded LDS stage.
+// Keys past the sequence repeat its last key (the callers mask them).
+struct KvStage {
+  uint4 kr[kKChunks / 256], vr[kVChunks / 256];
+  __device__ void load(const uint16_t* kbase, const uint16_t* vbase, int kt, int T, int tid) {
+#pragma unroll
+    for (int u = 0; u < kKChunks / 256; ++u) {
+      const int c = tid + 256 * u, row = c / 24, col = c % 24;
+      kr[u] = load16(kbase + (size_t)min(kt * kFaKeys + row, T - 1) * kFaDqk + col * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kVChunks / 256; ++u) {
+      const int c = tid + 256 * u, row = c / 16, col = c % 16;
+      vr[u] = load16(vbase + (size_t)min(kt * kFaKeys + row, T - 1) * kFaDv + col * 8);
+    }
+  }
+  __device__ void store(char* k_st, char* v_st, int tid) const {
+#pragma unroll
+    for (int u = 0; u < kKChunks / 256; ++u) {
+      const int c = tid + 256 * u, row = c / 24, col = c % 24;
+      *(uint4*)(k_st + row * kKPitch + col * 16) = kr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kVChunks / 256; ++u) {
+      const int c = tid + 256 * u, row = c / 16, col = c % 16;
+      *(uint4*)(v_st + row * kVPitch + col * 16) = vr[u];
+    }
+  }
+};
+
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
   __shared__ __attribute__((aligned(16))) char k_st[2][kFaKeys * kKPitch];
   __shared__ __attribute__((aligned(16))) char v_st[2][kFaKeys * kVPitch];
@@ -89,36 +120,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
   const uint16_t* kbase = a.Kb + ((size_t)g * a.n_rows + sq.x) * kFaDqk;
   const uint16_t* vbase = a.Vb + ((size_t)g * a.n_rows + sq.x) * kFaDv;
 
-  // tile loads: K 768 chunks (3 per thread), V 512 (2 per thread); rows past
-  // the sequence repeat its last row (masked below)
-  uint4 kr[kKChunks / 256], vr[kVChunks / 256];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < kKChunks / 256; ++u) {
-      const int c = tid + 256 * u, row = c / 24, col = c % 24;
-      const int key = min(kt * kFaKeys + row, T - 1);
-      kr[u] = load16(kbase + (size_t)key * kFaDqk + col * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < kVChunks / 256; ++u) {
-      const int c = tid + 256 * u, row = c / 16, col = c % 16;
-      const int key = min(kt * kFaKeys + row, T - 1);
-      vr[u] = load16(vbase + (size_t)key * kFaDv + col * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int c = tid + 256 * u, row = c / 24, col = c % 24;
-      *(uint4*)(k_st[buf] + row * kKPitch + col * 16) = kr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + 256 * u, row = c / 16, col = c % 16;
-      *(uint4*)(v_st[buf] + row * kVPitch + col * 16) = vr[u];
-    }
-  };
-
+  KvStage stage;
   f32x16 O[kDvBlocks];
 #pragma unroll
   for (int mb = 0; mb < kDvBlocks; ++mb)
@@ -126,12 +128,12 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
     for (int r = 0; r < 16; ++r) O[mb][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  stage.load(kbase, vbase, 0, T, tid);
+  stage.store(k_st[0], v_st[0], tid);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 1 < n_kt) stage.load(kbase, vbase, kt + 1, T, tid);
     const char* ks = k_st[buf];
     const char* vs = v_st[buf];
 
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
         O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[kk], O[mb], 0, 0, 0);
       }
     }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    if (kt + 1 < n_kt) stage.store(k_st[buf ^ 1], v_st[buf ^ 1], tid);
     __syncthreads();
   }
 
@@ -435,43 +437,19 @@ __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
   const int n_kt = i_last / kFaKeys + 1;
   const uint16_t* kbase = a.Kb + ((size_t)g * a.n_rows + sq.x) * kFaDqk;
   const uint16_t* vbase = a.Vb + ((size_t)g * a.n_rows + sq.x) * kFaDv;
-  uint4 kr[3], vr[2];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int c = tid + 256 * u, row = c / 24, col = c % 24;
-      kr[u] = load16(kbase + (size_t)min(kt * kFaKeys + row, T - 1) * kFaDqk + col * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + 256 * u, row = c / 16, col = c % 16;
-      vr[u] = load16(vbase + (size_t)min(kt * kFaKeys + row, T - 1) * kFaDv + col * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int c = tid + 256 * u, row = c / 24, col = c % 24;
-      *(uint4*)(k_st[buf] + row * kKPitch + col * 16) = kr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + 256 * u, row = c / 16, col = c % 16;
-      *(uint4*)(v_st[buf] + row * kVPitch + col * 16) = vr[u];
-    }
-  };
+  KvStage stage;
   f32x16 dQT[kFaDqk / 32];
 #pragma unroll
   for (int mb = 0; mb < kFaDqk / 32; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dQT[mb][r] = 0.f;
   const int s16 = lane & 15, dblk = (lane >> 4) & 1;
-  load_tile(0);
-  store_tile(0);
+  stage.load(kbase, vbase, 0, T, tid);
+  stage.store(k_st[0], v_st[0], tid);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 1 < n_kt) stage.load(kbase, vbase, kt + 1, T, tid);
     const char* ks = k_st[buf];
     const char* vs = v_st[buf];
     f32x16 sacc, dpacc;
@@ -511,7 +489,7 @@ __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
         const bf16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         dQT[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, db[kk], dQT[mb], 0, 0, 0);
       }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    if (kt + 1 < n_kt) stage.store(k_st[buf ^ 1], v_st[buf ^ 1], tid);
     __syncthreads();
   }
   if (!valid) return;

@@ -659,6 +659,13 @@ _V = {
     "v_mul_lo_u16": (lambda a, b: ((a & U64(0xFFFF)) * (b & U64(0xFFFF))) & U64(0xFFFF), 2),
     "v_add_u16": (lambda a, b: ((a & U64(0xFFFF)) + (b & U64(0xFFFF))) & U64(0xFFFF), 2),
     "v_sub_u16": (lambda a, b: ((a & U64(0xFFFF)) - (b & U64(0xFFFF))) & U64(0xFFFF), 2),
+    "v_subrev_u16": (lambda a, b: ((b & U64(0xFFFF)) - (a & U64(0xFFFF))) & U64(0xFFFF), 2),
+    "v_lshlrev_b16": (lambda a, b: ((b & U64(0xFFFF)) << (a & U64(15))) & U64(0xFFFF), 2),
+    "v_lshrrev_b16": (lambda a, b: (b & U64(0xFFFF)) >> (a & U64(15)), 2),
+    "v_max_u16": (lambda a, b: np.maximum(a & U64(0xFFFF), b & U64(0xFFFF)), 2),
+    "v_min_u16": (lambda a, b: np.minimum(a & U64(0xFFFF), b & U64(0xFFFF)), 2),
+    "v_mad_u16": (lambda a, b, c: ((a & U64(0xFFFF)) * (b & U64(0xFFFF)) + (c & U64(0xFFFF)))
+                  & U64(0xFFFF), 3),
     "v_mad_u32_u24": (lambda a, b, c: (a & U64(0xFFFFFF)) * (b & U64(0xFFFFFF)) + c, 3),
     "v_min_u32": (lambda a, b: np.minimum(a, b), 2),
     "v_max_u32": (lambda a, b: np.maximum(a, b), 2),

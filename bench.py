@@ -340,6 +340,28 @@ def _event_ms(torch, fn, reps, warmup=2):
     return e0.elapsed_time(e1) / reps
 
 
+def wg_sweep(b, steps, counts=(128, 256, 384, 512, 768)):
+    """Split-KV kernel time (library event hook) for several workgroup counts
+    of the plan (QKMLA_NUM_WG), each with a workspace sized for it."""
+    from mla_latent_decode_amd import ops
+    import torch
+    res, keep = {}, b.workspace
+    try:
+        for n in counts:
+            os.environ["QKMLA_NUM_WG"] = str(n)
+            b.workspace = torch.empty((ops.decode_workspace_size(b.cfg, b.B, b.L_cap),),
+                                      dtype=torch.uint8, device="cuda")
+            for _ in range(3):
+                b.step()
+            k_ms = b.kernel_ms(steps)
+            res[str(n)] = {"kernel_us": round(k_ms * 1e3, 2),
+                           "GBps": round(b.bytes_qk / (k_ms * 1e-3) / 1e9, 1)}
+    finally:
+        os.environ.pop("QKMLA_NUM_WG", None)
+        b.workspace = keep
+    return res
+
+
 def measure_next_rows(steps):
     """The rows beyond the decode step, each on the batch-16 x 4096 layer
     unless stated: bulk append of every cached token in one call, decode with
@@ -421,7 +443,15 @@ def measure_next_rows(steps):
                        "contiguous_us_per_step_eager": round(ms_c * 1e3, 2),
                        "cache_GBps": round(b.bytes_qk / (ms_p * 1e-3) / 1e9, 1)}
     status = int(b.status.item())
-    del pools, b
+    del pools
+    # split-KV workgroup count: the plan's default is one per CU
+    out["splitkv_wg_sweep"] = {b.w.name: wg_sweep(b, steps)}
+    del b
+    torch.cuda.empty_cache()
+    b3 = Bench(3)
+    out["splitkv_wg_sweep"][b3.w.name] = wg_sweep(b3, max(5, steps // 2))
+    status |= int(b3.status.item())
+    del b3
     torch.cuda.empty_cache()
     if status:
         raise RuntimeError(f"device status {status} in the next-row measurements")

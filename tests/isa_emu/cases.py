@@ -290,14 +290,17 @@ def run_paged(dev, shape, lens, s_q, page_size, seed, label, n_wg=None, heads=No
 @case
 def paged_caches(dev):
     """Paged latent, RoPE and alpha pools behind a block table: fp32 with
-    5-row pages and s_q = 2, bf16 with 32-row pages over split segments, each
-    also with one sequence whose table entry lies outside the pool."""
+    5-row pages and s_q = 2, bf16 with 32-row pages over split segments (also
+    with s_q = 2), each also with one sequence whose table entry lies outside
+    the pool."""
     run_paged(dev, Shape(6, 3, 20, 12, 4, 10, "f32"), (9, 33, 17), 2, 5, 520,
               "fp32 5-row pages, s_q=2, bad page in sequence 2", bad_seq=2)
     run_paged(dev, DSV3, (70, 40, 2), 1, 32, 521, "bf16 32-row pages over 4 workgroups",
               n_wg=4, heads=MERGE_HEADS)
     run_paged(dev, DSV3, (70, 40, 2), 1, 32, 522, "bf16 32-row pages, bad page in sequence 0",
               n_wg=3, heads=MERGE_HEADS, bad_seq=0)
+    run_paged(dev, DSV3, (45, 33), 2, 32, 523, "bf16 32-row pages, s_q=2", n_wg=3,
+              heads=MERGE_HEADS)
 
 
 TRAIN_IN = ("c", "q_c", "q_rope", "k_rope", "w_uk", "w_uv", "gamma_q", "gamma_k", "gamma_q_rope",

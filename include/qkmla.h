@@ -33,7 +33,8 @@
  *    OR-ing QKMLA_DEV_* bits into `*status` (device int32, may be NULL).  The
  *    caller clears it.  The affected sequence gets no cache writes (append) or
  *    an all-zero output with lse = -inf (decode).
- *  - batch == 0 is a valid no-op returning QKMLA_OK.
+ *  - batch == 0 (packed training: no sequences or no tokens) is a valid no-op
+ *    returning QKMLA_OK.
  *
  * Readings of points the pages leave open (the oracle makes the same ones):
  *  - S(z) = sqrt(mean(z^2) + eps), eps inside the square root.
@@ -68,7 +69,8 @@ typedef enum {
 typedef enum { QKMLA_F32 = 0, QKMLA_BF16 = 1 } qkmla_dtype;
 
 /* Device-side data-error bits OR-ed into *status. */
-#define QKMLA_DEV_BAD_SEQ_LEN 1   /* decode: seq_len outside [1, cache_capacity] */
+#define QKMLA_DEV_BAD_SEQ_LEN 1   /* decode: seq_len outside [1, cache_capacity];
+                                     packed training: cu_seqlens breaks its rules */
 #define QKMLA_DEV_BAD_POSITION 2  /* append: position < 0 or position + n_new > cache_capacity */
 #define QKMLA_DEV_BAD_PAGE 4      /* paged caches: a needed block-table entry is outside [0, num_pages) */
 

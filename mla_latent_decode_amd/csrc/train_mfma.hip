@@ -256,23 +256,67 @@ struct FbArgs {
   float tau;
 };
 
-// Key side: one wavefront per (sequence b, group g, tile of 32 keys).  K^ and V
-// of the tile stay in registers as B operands; query rows stream through LDS
-// two tokens (x 16 heads = 32 rows) at a time, from the tile's first key on.
+// Key side: workgroup = (sequence, group, 128 keys); wave w owns the 32-key
+// tile 4*blockIdx.x + w, whose K^ and V stay in its registers as B operands.
+// All four waves share the query rows, which stream through a double-buffered
+// LDS stage two tokens (x 16 heads = 32 rows) at a time from the block's
+// first key on; the next step's rows are in flight during each step.
 //   S  (rows x keys) = Q^ . K^T,  dP = d_o . V^T       (lane = key, regs = rows)
 //   p = 2^(S - lse2) (0 where key > token), dS = p (dP - D)
 //   dV^T (128 x keys) += d_o^T . P,   dK^T (192 x keys) += Q^T . dS
 // with d_o^T and Q^T read by ds_read_b64_tr_b16 in the row order of P's regs.
-__global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
-  __shared__ __attribute__((aligned(16))) char q_st[32 * kKPitch];
-  __shared__ __attribute__((aligned(16))) char o_st[32 * kVPitch];
-  __shared__ float2 st_s[32];
-  const int kt = blockIdx.x, g = blockIdx.y;
+// A wave skips the MFMAs of steps that lie wholly before its keys.
+struct RowStage {  // 32 rows: Q^ 768 + d_o 512 chunks of 16 B, 3 + 2 per thread
+  uint4 q[3], o[2];
+  float2 st;
+  __device__ void load(const FbArgs& a, size_t seq_row0, int T, int g, int i0, int tid) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int c = tid + 256 * u, row = c / 24, col = c % 24;
+      const int tok = min(i0 + (row >> 4), T - 1);
+      const size_t qr = (seq_row0 + tok) * a.H + g * kFaHpg + (row & 15);
+      q[u] = load16(a.Qb + qr * kFaDqk + col * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + 256 * u, row = c / 16, col = c % 16;
+      const int tok = min(i0 + (row >> 4), T - 1);
+      const size_t qr = (seq_row0 + tok) * a.H + g * kFaHpg + (row & 15);
+      o[u] = load16(a.dOb + qr * kFaDv + col * 8);
+    }
+    if (tid < 32) {
+      const int tok = min(i0 + (tid >> 4), T - 1);
+      st = a.stat[(seq_row0 + tok) * a.H + g * kFaHpg + (tid & 15)];
+    }
+  }
+  __device__ void store(char* q_st, char* o_st, float2* st_s, int tid) const {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int c = tid + 256 * u, row = c / 24, col = c % 24;
+      *(uint4*)(q_st + row * kKPitch + col * 16) = q[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + 256 * u, row = c / 16, col = c % 16;
+      *(uint4*)(o_st + row * kVPitch + col * 16) = o[u];
+    }
+    if (tid < 32) st_s[tid] = st;
+  }
+};
+
+__global__ __launch_bounds__(256) void flash_bwd_kv_kernel(FbArgs a) {
+  __shared__ __attribute__((aligned(16))) char q_st[2][32 * kKPitch];
+  __shared__ __attribute__((aligned(16))) char o_st[2][32 * kVPitch];
+  __shared__ float2 st_s[2][32];
+  const int g = blockIdx.y;
   const int2 sq = a.seqs[blockIdx.z];  // (start row, length), uniform
   const int T = sq.y;
-  const int key0 = kt * kFaKeys;
-  if (key0 >= T) return;  // whole workgroup: past this sequence
-  const int lane = threadIdx.x, hf = lane >> 5, n = lane & 31;
+  const int kblk0 = blockIdx.x * 4 * kFaKeys;  // first key of the workgroup
+  if (kblk0 >= T) return;  // whole workgroup: past this sequence
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hf = lane >> 5, n = lane & 31;
+  const int key0 = kblk0 + wave * kFaKeys;
   const int key = key0 + n;
   const int keyc = min(key, T - 1);
   const size_t kv_row = (size_t)g * a.n_rows + sq.x + keyc;
@@ -299,82 +343,73 @@ __global__ __launch_bounds__(64) void flash_bwd_kv_kernel(FbArgs a) {
 
   const size_t seq_row0 = sq.x;
   const int s16 = lane & 15, dblk = (lane >> 4) & 1;
-  for (int i0 = key0; i0 < T; i0 += 2) {
-    // stage 32 rows: token i0 + r/16, head 16g + r%16 (16 heads of a token are
-    // contiguous); tokens past the sequence repeat its last token (masked)
-    __syncthreads();  // the previous step's LDS reads are done
+  RowStage rs;
+  rs.load(a, seq_row0, T, g, kblk0, tid);
+  rs.store(q_st[0], o_st[0], st_s[0], tid);
+  __syncthreads();
+  for (int i0 = kblk0, buf = 0; i0 < T; i0 += 2, buf ^= 1) {
+    if (i0 + 2 < T) rs.load(a, seq_row0, T, g, i0 + 2, tid);
+    // wave-uniform: the step's tokens all precede this wave's keys
+    if (i0 + 1 >= key0 && key0 < T) {
+      const char* qs = q_st[buf];
+      const char* os = o_st[buf];
+      f32x16 sacc, dpacc;
 #pragma unroll
-    for (int u = 0; u < 12; ++u) {  // Q^: 768 chunks
-      const int c = lane + 64 * u, row = c / 24, col = c % 24;
-      const int tok = min(i0 + (row >> 4), T - 1);
-      const size_t qr = (seq_row0 + tok) * a.H + g * kFaHpg + (row & 15);
-      *(uint4*)(q_st + row * kKPitch + col * 16) = load16(a.Qb + qr * kFaDqk + col * 8);
-    }
+      for (int r = 0; r < 16; ++r) {
+        sacc[r] = 0.f;
+        dpacc[r] = 0.f;
+      }
+      const char* qrow = qs + n * kKPitch + 16 * hf;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // d_o: 512 chunks
-      const int c = lane + 64 * u, row = c / 16, col = c % 16;
-      const int tok = min(i0 + (row >> 4), T - 1);
-      const size_t qr = (seq_row0 + tok) * a.H + g * kFaHpg + (row & 15);
-      *(uint4*)(o_st + row * kVPitch + col * 16) = load16(a.dOb + qr * kFaDv + col * 8);
+      for (int s = 0; s < kQkSteps; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qrow + 32 * s), kreg[s],
+                                                       sacc, 0, 0, 0);
+      const char* orow = os + n * kVPitch + 16 * hf;
+#pragma unroll
+      for (int s = 0; s < kFaDv / 16; ++s)
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(orow + 32 * s), vreg[s],
+                                                        dpacc, 0, 0, 0);
+      // reg r holds row 8(r/4) + 4hf + r%4 = token i0 + row/16, head row%16; only
+      // steps whose tokens can precede a key of the tile, or run past the
+      // sequence, or a tile past the sequence, mask (wave-uniform)
+      const bool masked = i0 < key0 + kFaKeys - 1 || i0 + 1 >= T || key0 + kFaKeys > T;
+      bf16x8 pb[2], db[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int tok = i0 + (row >> 4);
+        const float2 sd = st_s[buf][row];
+        float p = __builtin_amdgcn_exp2f(sacc[r] - sd.x);
+        if (masked && !(key <= tok && tok < T && key < T)) p = 0.f;
+        pb[r >> 3][r & 7] = (__bf16)p;
+        db[r >> 3][r & 7] = (__bf16)(p * (dpacc[r] - sd.y));
+      }
+      const char* tvb = os + (4 * hf + (s16 >> 2)) * kVPitch + 32 * dblk + 8 * (s16 & 3);
+      const char* tqb = qs + (4 * hf + (s16 >> 2)) * kKPitch + 32 * dblk + 8 * (s16 & 3);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < kDvBlocks; ++mb) {
+          const char* pa = tvb + 16 * kk * kVPitch + 64 * mb;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa));
+          const bf16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa + 8 * kVPitch));
+          const bf16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          dVT[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[kk], dVT[mb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mb = 0; mb < kFaDqk / 32; ++mb) {
+          const char* pa = tqb + 16 * kk * kKPitch + 64 * mb;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa));
+          const bf16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa + 8 * kKPitch));
+          const bf16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          dKT[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, db[kk], dKT[mb], 0, 0, 0);
+        }
+      }
     }
-    if (lane < 32) {
-      const int tok = min(i0 + (lane >> 4), T - 1);
-      st_s[lane] = a.stat[(seq_row0 + tok) * a.H + g * kFaHpg + (lane & 15)];
-    }
+    if (i0 + 2 < T) rs.store(q_st[buf ^ 1], o_st[buf ^ 1], st_s[buf ^ 1], tid);
     __syncthreads();
-
-    f32x16 sacc, dpacc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sacc[r] = 0.f;
-      dpacc[r] = 0.f;
-    }
-    const char* qrow = q_st + n * kKPitch + 16 * hf;
-#pragma unroll
-    for (int s = 0; s < kQkSteps; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qrow + 32 * s), kreg[s],
-                                                     sacc, 0, 0, 0);
-    const char* orow = o_st + n * kVPitch + 16 * hf;
-#pragma unroll
-    for (int s = 0; s < kFaDv / 16; ++s)
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(orow + 32 * s), vreg[s],
-                                                      dpacc, 0, 0, 0);
-    // reg r holds row 8(r/4) + 4hf + r%4 = token i0 + row/16, head row%16
-    // wave-uniform: only steps whose tokens can precede a key of the tile, or
-    // run past the sequence, or a tile past the sequence, mask
-    const bool masked = i0 < key0 + kFaKeys - 1 || i0 + 1 >= T || key0 + kFaKeys > T;
-    bf16x8 pb[2], db[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
-      const int tok = i0 + (row >> 4);
-      const float2 sd = st_s[row];
-      float p = __builtin_amdgcn_exp2f(sacc[r] - sd.x);
-      if (masked && !(key <= tok && tok < T && key < T)) p = 0.f;
-      pb[r >> 3][r & 7] = (__bf16)p;
-      db[r >> 3][r & 7] = (__bf16)(p * (dpacc[r] - sd.y));
-    }
-    const char* tvb = o_st + (4 * hf + (s16 >> 2)) * kVPitch + 32 * dblk + 8 * (s16 & 3);
-    const char* tqb = q_st + (4 * hf + (s16 >> 2)) * kKPitch + 32 * dblk + 8 * (s16 & 3);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int mb = 0; mb < kDvBlocks; ++mb) {
-        const char* pa = tvb + 16 * kk * kVPitch + 64 * mb;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa + 8 * kVPitch));
-        const bf16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dVT[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[kk], dVT[mb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int mb = 0; mb < kFaDqk / 32; ++mb) {
-        const char* pa = tqb + 16 * kk * kKPitch + 64 * mb;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pa + 8 * kKPitch));
-        const bf16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dKT[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, db[kk], dKT[mb], 0, 0, 0);
-      }
-    }
   }
   if (key >= T) return;
   // lane holds column `key`; reg r of block mb is dim 32mb + 8(r/4) + 4hf + r%4.
@@ -535,7 +570,8 @@ hipError_t launch_flash_bwd(const Cfg& c, const FlashSeqs& q, const void* Qb, co
   FbArgs a{(const uint16_t*)Qb, (const uint16_t*)Kb, (const uint16_t*)Vb, (const uint16_t*)dOb,
            (const float2*)stat, dKh, dV, dQh, q.seqs, q.n_rows, c.H, c.G, c.tau};
   hipLaunchKernelGGL(flash_bwd_kv_kernel,
-                     dim3((q.max_len + kFaKeys - 1) / kFaKeys, c.G, q.n_seq), dim3(64), 0, s, a);
+                     dim3((q.max_len + 4 * kFaKeys - 1) / (4 * kFaKeys), c.G, q.n_seq), dim3(256),
+                     0, s, a);
   hipLaunchKernelGGL(flash_bwd_q_kernel, dim3((q.max_len + kFaTok - 1) / kFaTok, c.G, q.n_seq),
                      dim3(256), 0, s, a);
   return hipGetLastError();

@@ -341,6 +341,50 @@ class Wave:
 
 
 # ----------------------------------------------------------------------------
+def _sdwa_wrap(h, base, inst):
+    """SDWA form of a plain integer VOP handler: its src0_sel / src1_sel pick a
+    byte or word of the source (zero-extended) before the operation.  Only
+    handlers that read their sources through vget (the integer VOP table) and
+    a full-dword destination are modelled; anything else stops the run."""
+    from .semantics import _V
+    sels = {}
+    for k, key in ((1, "src0_sel"), (2, "src1_sel")):
+        sel = inst.mods.get(key, "DWORD")
+        if sel != "DWORD":
+            sels[k] = sel
+    if inst.mods.get("dst_sel", "DWORD") != "DWORD" or "sext(" in inst.text:
+        raise EmuError(f"sdwa dst_sel / sext not modelled (line {inst.line}: {inst.text})")
+    if not sels:
+        return h
+    if base not in _V:
+        raise EmuError(f"sdwa source select on {base} not modelled (line {inst.line}: {inst.text})")
+
+    def pick(x, sel):
+        x = x.astype(np.uint32)
+        if sel == "WORD_0":
+            return x & np.uint32(0xFFFF)
+        if sel == "WORD_1":
+            return (x >> np.uint32(16)) & np.uint32(0xFFFF)
+        if sel.startswith("BYTE_"):
+            return (x >> np.uint32(8 * int(sel[5:]))) & np.uint32(0xFF)
+        raise EmuError(f"sdwa sel {sel}")
+
+    def run(w, i):
+        ops = {id(i.ops[k]): sel for k, sel in sels.items() if k < len(i.ops)}
+        orig = w.vget
+
+        def vget(o, ty="b32", idx=0):
+            v = orig(o, ty, idx)
+            sel = ops.get(id(o))
+            return v if sel is None else pick(v, sel)
+        w.vget = vget
+        try:
+            h(w, i)
+        finally:
+            del w.vget
+    return run
+
+
 class Emulator:
     def __init__(self, mem: Memory):
         from .semantics import HANDLERS
@@ -362,6 +406,8 @@ class Emulator:
                 h = self.handlers.get(base)
                 if h is None:
                     raise EmuError(f"no semantics for {inst.op} (line {inst.line}: {inst.text})")
+                if inst.op.endswith("_sdwa") and base != "v_and_b32":  # v_and_b32 does its own
+                    h = _sdwa_wrap(h, base, inst)
                 inst.handler = h
 
     def run(self, kern: Kernel, grid, block, shmem: int, kernarg_addr: int,

@@ -194,11 +194,16 @@ class Bench:
     def kernel_ms(self, steps, plain=False):
         """Average duration of the split-KV kernel over `steps` steps (HIP events
         recorded by the library around each launch on the launch stream)."""
+        return self.kernel_breakdown_ms(steps, plain)[1]
+
+    def kernel_breakdown_ms(self, steps, plain=False):
+        """Average (q-prep, split-KV, merge) durations per decode call over
+        `steps` steps, from the library's events on the launch stream."""
         self.ops.profile_begin()
         for _ in range(steps):
             self.step(plain)
-        ms, n = self.ops.profile_end()
-        return ms / max(n, 1)
+        ms, n = self.ops.profile_end_detail()
+        return tuple(m / max(n, 1) for m in ms)
 
 
 def _kernel_src_hash():
@@ -293,7 +298,7 @@ def measure(cid, steps, warmup, graph=True):
     b = Bench(cid)
     ms_eager, wall = b.time_steps(steps, warmup)
     ms_plain_eager, _ = b.time_steps(steps, warmup, plain=True)
-    k_ms = b.kernel_ms(steps)
+    qp_ms, k_ms, mg_ms = b.kernel_breakdown_ms(steps)
     k_ms_plain = b.kernel_ms(steps, plain=True)
     g_ms, g_note = b.graph_time(steps) if graph else (None, "not requested")
     g_ms_plain, g_note_plain = b.graph_time(steps, plain=True) if g_ms else (None, g_note)
@@ -316,6 +321,8 @@ def measure(cid, steps, warmup, graph=True):
         "cache_frac_of_8TBps": round(b.bytes_qk / (ms_qk * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "splitkv_kernel_us": round(k_ms * 1e3, 2),
         "splitkv_kernel_GBps": round(b.bytes_qk / (k_ms * 1e-3) / 1e9, 1),
+        "qprep_kernel_us": round(qp_ms * 1e3, 2),
+        "merge_kernel_us": round(mg_ms * 1e3, 2),
         "splitkv_kernel_plain_us": round(k_ms_plain * 1e3, 2),
         "splitkv_overhead_vs_plain_pct": round(100.0 * (k_ms / k_ms_plain - 1.0), 2),
         "mfma_TFLOPs": round(b.flops / (k_ms * 1e-3) / 1e12, 1),

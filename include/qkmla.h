@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define QKMLA_ABI_VERSION 5
+#define QKMLA_ABI_VERSION 6
 
 typedef enum {
   QKMLA_OK = 0,
@@ -370,8 +370,9 @@ int qkmla_plan_merge_sources(int32_t batch, const int32_t* seq_lens, int32_t cac
 
 /*
  * Measurement hook.  Between qkmla_profile_begin() and qkmla_profile_end(),
- * every qkmla_decode call of this host thread records a HIP event pair on its
- * stream around the launch of its split-KV kernel (the hot kernel).
+ * every decode call (qkmla_decode, _multi, _paged) of this host thread
+ * records HIP events on its stream around its q-prep, split-KV and merge
+ * launches.
  * qkmla_profile_end() waits for the recorded events and returns the summed
  * kernel time in milliseconds and the number of launches.  At most 4096
  * launches are recorded per begin/end window; the events are created on first
@@ -379,6 +380,11 @@ int qkmla_plan_merge_sources(int32_t batch, const int32_t* seq_lens, int32_t cac
  */
 int qkmla_profile_begin(void);
 int qkmla_profile_end(double* split_kv_ms_total, int32_t* launches);
+/* The same window split by kernel: ms_total[0] q-prep, [1] the split-KV
+ * kernel (the row-parallel decode for float storage), [2] the merge (0 for
+ * float storage), summed over the recorded decode calls.  Ends the window
+ * like qkmla_profile_end; use one of the two. */
+int qkmla_profile_end_detail(double* ms_total, int32_t* launches);
 
 const char* qkmla_status_string(int status);
 const char* qkmla_last_error(void);

@@ -122,26 +122,30 @@ int device_cu_count() {
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-// Measurement hook state (per host thread).
+// Measurement hook state (per host thread): per recorded decode call, events
+// before q-prep (0), before the split-KV kernel (1), after it (2) and after
+// the merge (3).
+constexpr int kTimedMax = 4096;
 struct KernelTimer {
   bool on = false;
   int n = 0;
-  hipEvent_t ev[2][4096];
+  hipEvent_t ev[4][kTimedMax];
   int created = 0;
 };
 thread_local KernelTimer g_timer;
 
 hipError_t timer_record(hipStream_t s, int which) {
   KernelTimer& t = g_timer;
-  if (!t.on || t.n >= 4096) return hipSuccess;
+  if (!t.on || t.n >= kTimedMax) return hipSuccess;
   if (t.n >= t.created) {
-    hipError_t e = hipEventCreate(&t.ev[0][t.n]);
-    if (e == hipSuccess) e = hipEventCreate(&t.ev[1][t.n]);
-    if (e != hipSuccess) return e;
+    for (int k = 0; k < 4; ++k) {
+      const hipError_t e = hipEventCreate(&t.ev[k][t.n]);
+      if (e != hipSuccess) return e;
+    }
     t.created = t.n + 1;
   }
-  hipError_t e = hipEventRecord(t.ev[which][t.n], s);
-  if (which == 1) ++t.n;
+  const hipError_t e = hipEventRecord(t.ev[which][t.n], s);
+  if (which == 3) ++t.n;
   return e;
 }
 
@@ -184,20 +188,31 @@ int qkmla_profile_begin(void) {
   return ok();
 }
 
-int qkmla_profile_end(double* split_kv_ms_total, int32_t* launches) {
+int qkmla_profile_end_detail(double* ms_total, int32_t* launches) {
   KernelTimer& t = g_timer;
   t.on = false;
-  double total = 0.0;
+  double total[3] = {0.0, 0.0, 0.0};
   for (int i = 0; i < t.n; ++i) {
-    hipError_t e = hipEventSynchronize(t.ev[1][i]);
-    float ms = 0.f;
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.ev[0][i], t.ev[1][i]);
+    hipError_t e = hipEventSynchronize(t.ev[3][i]);
+    for (int k = 0; k < 3 && e == hipSuccess; ++k) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, t.ev[k][i], t.ev[k + 1][i]);
+      total[k] += ms;
+    }
     if (e != hipSuccess) return hip_status(e, "profile_end");
-    total += ms;
   }
-  if (split_kv_ms_total) *split_kv_ms_total = total;
+  if (ms_total)
+    for (int k = 0; k < 3; ++k) ms_total[k] = total[k];
   if (launches) *launches = t.n;
   t.n = 0;
+  return ok();
+}
+
+int qkmla_profile_end(double* split_kv_ms_total, int32_t* launches) {
+  double ms[3];
+  const int st = qkmla_profile_end_detail(ms, launches);
+  if (st) return st;
+  if (split_kv_ms_total) *split_kv_ms_total = ms[1];
   return ok();
 }
 
@@ -414,23 +429,27 @@ static int decode_impl(const Cfg& c, int32_t batch, int32_t s_q, const void* q_c
   if (workspace_bytes < ws.total)
     return fail(QKMLA_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
                 ws.total);
-  hipError_t e = launch_qprep(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens, pg, ws,
-                              workspace, status, s);
+  const bool timed = g_timer.on && g_timer.n < kTimedMax;
+  hipError_t e = hipSuccess;
+  if (timed && (e = timer_record(s, 0)) != hipSuccess) return hip_status(e, "decode/timer");
+  e = launch_qprep(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens, pg, ws, workspace,
+                   status, s);
   if (e != hipSuccess) return hip_status(e, "decode/qprep");
+  if (timed && (e = timer_record(s, 1)) != hipSuccess) return hip_status(e, "decode/timer");
   if (c.dtype == QKMLA_BF16) {
-    const bool timed = g_timer.on && g_timer.n < 4096;
-    if (timed && (e = timer_record(s, 0)) != hipSuccess) return hip_status(e, "decode/timer");
     e = launch_decode_mfma(c, batch, s_q, seq_lens, pg, latent_cache, rope_cache, alpha_cache, ws,
                            workspace, n_wg, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/splitkv");
-    if (timed && (e = timer_record(s, 1)) != hipSuccess) return hip_status(e, "decode/timer");
+    if (timed && (e = timer_record(s, 2)) != hipSuccess) return hip_status(e, "decode/timer");
     e = launch_merge(c, batch, s_q, ws, workspace, n_wg, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/merge");
   } else {
     e = launch_decode_generic(c, batch, s_q, seq_lens, pg, latent_cache, rope_cache, alpha_cache,
                               ws, workspace, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/generic");
+    if (timed && (e = timer_record(s, 2)) != hipSuccess) return hip_status(e, "decode/timer");
   }
+  if (timed && (e = timer_record(s, 3)) != hipSuccess) return hip_status(e, "decode/timer");
   return ok();
 }
 

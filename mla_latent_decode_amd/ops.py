@@ -93,6 +93,7 @@ def _load():
         "qkmla_plan_merge_sources": (I32, [I32, P, I32, I32, I32, P, I32, ctypes.POINTER(I32)]),
         "qkmla_profile_begin": (I32, []),
         "qkmla_profile_end": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
+        "qkmla_profile_end_detail": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -166,15 +167,24 @@ def abi_version() -> int:
 
 
 def profile_begin():
-    """Start recording HIP events around each split-KV kernel launch."""
+    """Start recording HIP events around the q-prep, split-KV and merge
+    launches of each decode call."""
     _check(_lib.qkmla_profile_begin(), "qkmla_profile_begin")
 
 
 def profile_end():
-    """Stop recording; returns (summed split-KV kernel ms, launches)."""
+    """Stop recording; returns (summed split-KV kernel ms, decode calls)."""
     ms, n = ctypes.c_double(), ctypes.c_int32()
     _check(_lib.qkmla_profile_end(ctypes.byref(ms), ctypes.byref(n)), "qkmla_profile_end")
     return ms.value, n.value
+
+
+def profile_end_detail():
+    """Stop recording; returns ((q-prep ms, split-KV ms, merge ms) summed,
+    decode calls)."""
+    ms, n = (ctypes.c_double * 3)(), ctypes.c_int32()
+    _check(_lib.qkmla_profile_end_detail(ms, ctypes.byref(n)), "qkmla_profile_end_detail")
+    return (ms[0], ms[1], ms[2]), n.value
 
 
 def plan(cfg: Config, batch: int, max_seq_len: int, n_cu: int):

@@ -21,6 +21,11 @@ MLA), the hot kernel's roofline position, the fp64 oracle timed on the host,
 and the same figures for the 32k, 256k and ragged workloads under "sweep".
 Under "next_rows": bulk append, s_q = 2 decode, paged-cache decode and the
 explicit-form training forward and backward, each timed on its own.
+
+The default run takes the headline (with its sweep) and the next rows from two
+child processes (``--part headline`` / ``--part next``, which also run alone,
+e.g. under a profiler), so that a failure in a next-row measurement leaves
+the headline standing; the parent process never touches the GPU.
 """
 from __future__ import annotations
 
@@ -398,6 +403,7 @@ def measure_next_rows(steps):
     out["bulk_append"] = {"tokens": B * L, "us": round(ms * 1e3, 1),
                           "Mtokens_per_s": round(B * L / (ms * 1e-3) / 1e6, 1),
                           "GBps": round(B * L * append_bytes_per_token(s) / (ms * 1e-3) / 1e9, 1)}
+    _progress(out, "bulk_append")
     del c_new, k_new
     # N2: s_q = 2 rows per sequence (causal), over the rotated cache copies
     s_q = 2
@@ -418,6 +424,7 @@ def measure_next_rows(steps):
     out["multi_query_s_q2"] = {"us_per_step": round(ms * 1e3, 2),
                                "cache_GBps_per_row": round(rows_tokens * per_tok / (ms * 1e-3) / 1e9, 1),
                                "note": "each query row streams its own causal prefix"}
+    _progress(out, "multi_query_s_q2")
     del qc, qr, o2
     # N3: the same caches in 64-row pages of a shuffled pool (copies rotated)
     ps = 64
@@ -449,6 +456,7 @@ def measure_next_rows(steps):
     out["paged_64"] = {"us_per_step": round(ms_p * 1e3, 2),
                        "contiguous_us_per_step_eager": round(ms_c * 1e3, 2),
                        "cache_GBps": round(b.bytes_qk / (ms_p * 1e-3) / 1e9, 1)}
+    _progress(out, "paged_64")
     status = int(b.status.item())
     del pools
     # split-KV workgroup count: the plan's default is one per CU
@@ -457,6 +465,7 @@ def measure_next_rows(steps):
     torch.cuda.empty_cache()
     b3 = Bench(3)
     out["splitkv_wg_sweep"][b3.w.name] = wg_sweep(b3, max(5, steps // 2))
+    _progress(out, "splitkv_wg_sweep")
     status |= int(b3.status.item())
     del b3
     torch.cuda.empty_cache()
@@ -503,6 +512,7 @@ def measure_next_rows(steps):
     out["prefill_packed_fwd"] = {"sequences": len(lens), "tokens": total, "ms": round(ms_v, 3),
                                  "Mtokens_per_s": round(total / (ms_v * 1e-3) / 1e6, 2),
                                  "attention_TFLOPs": round(pairs_flops / (ms_v * 1e-3) / 1e12, 2)}
+    _progress(out, "prefill_packed_fwd")
     if int(stv.item()):
         raise RuntimeError(f"device status {int(stv.item())} in the packed prefill")
     del pre, wsv, ov, lv
@@ -511,7 +521,12 @@ def measure_next_rows(steps):
                             "fwd_attention_TFLOPs": round(ff / (ms_f * 1e-3) / 1e12, 2),
                             "bwd_attention_TFLOPs": round(fb / (ms_b * 1e-3) / 1e12, 2),
                             "kernels": "MFMA attention and projection GEMMs (bf16 operands), row-parallel norms"}
+    _progress(out, "train_fwd_bwd")
     return out
+
+
+def _progress(out, name):
+    print(f"[bench] {name} {out[name]}", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(cid, budget_s=15.0):
@@ -563,6 +578,10 @@ def main():
     ap.add_argument("--traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "ALGO_BYTES"),
                     help="write the split-KV kernel's HBM traffic from two --pmc runs' CSVs "
                          "into profiles/decode_splitkv_traffic.json (no GPU needed)")
+    ap.add_argument("--part", choices=("all", "headline", "next"), default="all",
+                    help="all: run the headline (with its sweep) and the next-row measurements "
+                         "each in a child process and print the combined line; headline / next: "
+                         "run only that part in this process and print its JSON")
     args = ap.parse_args()
     if args.traffic:
         from mla_latent_decode_amd.inputs import WORKLOADS
@@ -575,12 +594,22 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path is a single-GPU kernel library)", file=sys.stderr)
         sys.exit(2)
+    if args.part == "all" and not args.pmc_workload:
+        run_parts(args)
+        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     if args.pmc_workload:
         pmc_workload()
+        return
+    if args.part == "next":
+        try:
+            nxt = measure_next_rows(max(10, args.steps // 2))
+        except Exception as ex:  # noqa: BLE001 -- reported in the JSON line
+            nxt = {"error": f"{type(ex).__name__}: {ex}"}
+        print(json.dumps({"next_rows": nxt}), flush=True)
         return
     b, res, ms_qk, k_ms, _ = measure(args.workload, args.steps, args.warmup, not args.no_graph)
     print(f"[bench] headline {res}", file=sys.stderr, flush=True)
@@ -629,13 +658,43 @@ def main():
             del _b
             torch.cuda.empty_cache()
         line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+def _run_child(part, args, timeout_s):
+    """Run one part of the benchmark in a child process.  Its stderr (the
+    progress lines) passes through; its last JSON line on stdout is the
+    result.  Returns (result or None, error text)."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--part", part, "--steps", str(args.steps),
+           "--warmup", str(args.warmup), "--workload", str(args.workload)]
+    if args.no_sweep:
+        cmd.append("--no-sweep")
+    if args.no_graph:
+        cmd.append("--no-graph")
+    try:
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        return None, f"the {part} part did not finish within {timeout_s} s"
+    lines = [ln for ln in p.stdout.splitlines() if ln.startswith("{")]
+    if p.returncode != 0 or not lines:
+        return None, f"the {part} part exited with status {p.returncode}"
+    return json.loads(lines[-1]), None
+
+
+def run_parts(args):
+    """The default run.  The headline (and its sweep) and the next-row
+    measurements each run in a child process, so that a failure in one of the
+    next rows cannot take the headline with it; this process never touches
+    the GPU and adds the host baseline."""
+    line, err = _run_child("headline", args, 900)
+    if line is None:
+        print(f"bench.py: {err}", file=sys.stderr)
+        sys.exit(1)
     if not args.no_next:
-        try:
-            line["next_rows"] = measure_next_rows(max(10, args.steps // 2))
-        except Exception as ex:  # noqa: BLE001 -- the headline line is still printed
-            line["next_rows"] = {"error": f"{type(ex).__name__}: {ex}"}
+        nxt, err = _run_child("next", args, 900)
+        line["next_rows"] = nxt["next_rows"] if nxt else {"error": err}
         print(f"[bench] next rows {line['next_rows']}", file=sys.stderr, flush=True)
-        torch.cuda.empty_cache()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)

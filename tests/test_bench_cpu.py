@@ -60,3 +60,39 @@ def test_traffic_from_pmc_counters(tmp_path):
     expect = 81000 * 1024 / 1.25 + 5000 * 1024
     assert abs(e["hbm_bytes_per_launch"] - expect) <= 1
     assert e["kernel_src_sha256_16"] == bench._kernel_src_hash()
+
+
+def test_default_run_keeps_the_headline_when_the_next_rows_fail(monkeypatch, capsys):
+    """The default run takes the headline and the next-row measurements from
+    two child processes; a next-row child that dies leaves an error entry and
+    the headline line is still printed."""
+    import argparse
+    import json
+
+    import bench
+    calls = []
+
+    def fake_child(part, args, timeout_s):
+        calls.append(part)
+        if part == "headline":
+            return {"metric": bench.METRIC, "value": 1.0}, None
+        return None, "the next part exited with status -11"
+    monkeypatch.setattr(bench, "_run_child", fake_child)
+    args = argparse.Namespace(no_next=False, no_cpu=True)
+    bench.run_parts(args)
+    line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert calls == ["headline", "next"]
+    assert line["value"] == 1.0 and "status -11" in line["next_rows"]["error"]
+
+
+def test_default_run_fails_without_a_gpu_headline(monkeypatch):
+    import argparse
+
+    import bench
+    monkeypatch.setattr(bench, "_run_child", lambda part, args, t: (None, "exited with status 2"))
+    try:
+        bench.run_parts(argparse.Namespace(no_next=False, no_cpu=True))
+    except SystemExit as e:
+        assert e.code == 1
+    else:
+        raise AssertionError("run_parts returned without a headline")

@@ -326,7 +326,8 @@ int qkmla_train_backward(const qkmla_config* cfg, int32_t batch, int32_t seq_len
  *                breaks the rules above; every access stays in bounds, the
  *                outputs are then undefined
  * The fixed-length calls are these with cu_seqlens[s] = s * seq_len.  At most
- * 65535 sequences (QKMLA_ERR_UNSUPPORTED).  o must be 16-byte aligned.
+ * 65535 sequences and 2^24 token rows per call (QKMLA_ERR_UNSUPPORTED).  o
+ * must be 16-byte aligned.
  */
 size_t qkmla_train_workspace_size_varlen(const qkmla_config* cfg, int32_t n_seqs,
                                          int32_t total_tokens, int32_t max_seq_len);

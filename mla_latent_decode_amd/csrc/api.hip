@@ -517,8 +517,10 @@ static int check_train(const qkmla_config* cfg, int64_t n_seq, int64_t n_rows, i
   if (c->dc > 256 || c->dv > 256)
     return fail(QKMLA_ERR_UNSUPPORTED, "train: d_c and d_v must be <= 256 (got %d, %d)", c->dc,
                 c->dv);
-  if (n_rows * c->H > INT32_MAX / 2 || max_len > INT32_MAX / 2)
-    return fail(QKMLA_ERR_UNSUPPORTED, "train: tokens * n_heads too large");
+  // row-per-block kernels launch n_rows blocks of 256 threads; the dispatch
+  // size in work-items must fit 32 bits
+  if (n_rows * c->H > INT32_MAX / 2 || max_len > INT32_MAX / 2 || n_rows > (1 << 24))
+    return fail(QKMLA_ERR_UNSUPPORTED, "train: more than 2^24 tokens or tokens * n_heads too large");
   if (n_seq > 65535) return fail(QKMLA_ERR_UNSUPPORTED, "train: more than 65535 sequences");
   return QKMLA_OK;
 }

@@ -230,7 +230,7 @@ def test_train_entry_points_validate_on_the_host():
 
 def test_varlen_train_entry_points_validate_on_the_host():
     """Packed-sequence training calls: empty batches are no-ops, cu_seqlens
-    must be given and aligned, max_seq_len >= 1, at most 65535 sequences,
+    must be given and aligned, max_seq_len >= 1, at most 65535 sequences and 2^24 rows,
     and the workspace is checked against the packed size."""
     ops = _ops()
     lib = ops._lib
@@ -252,6 +252,10 @@ def test_varlen_train_entry_points_validate_on_the_host():
                                           None, None) == 1
     assert lib.qkmla_train_forward_varlen(c, 70000, p, 70000, 1, ctypes.byref(ins), p, 1 << 30, p,
                                           p, None, None) == 2
+    # more than 2^24 token rows: the row-per-block launches would overflow
+    assert lib.qkmla_train_forward_varlen(c, 1, p, (1 << 24) + 1, 8, ctypes.byref(ins), p, 1 << 30,
+                                          p, p, None, None) == 2
+    assert b"2^24" in lib.qkmla_last_error()
     need = ops.train_workspace_size_varlen(cfg, 2, 9, 5)
     assert need > 0
     assert lib.qkmla_train_forward_varlen(c, 2, p, 9, 5, ctypes.byref(ins), p, 16, p, p, None,

@@ -147,8 +147,12 @@ def _check(status: int, what: str):
 
 
 def _ptr(t: Optional[torch.Tensor], shape=None, dtype=None, name="tensor"):
+    """Device address of a contiguous tensor on the current GPU, after checking
+    its dtype and shape (the library reads and writes exactly that extent)."""
     if t is None:
         return None
+    if t.device.type != "cuda" or t.device.index != torch.cuda.current_device():
+        raise QkmlaError(f"{name} must be a tensor on the current GPU, got {t.device}")
     if not t.is_contiguous():
         raise QkmlaError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -257,7 +261,8 @@ def append(cfg: Config, c_new, k_rope_new, w_uk, gamma_k_rope, positions, latent
     _check(_lib.qkmla_append(
         ctypes.byref(cfg.c()), B, n_new, _ptr(c_new, (B, n_new, cfg.latent_rank), dt, "c_new"),
         _ptr(k_rope_new, (B, n_new, cfg.rope_dim), dt, "k_rope_new"),
-        _ptr(w_uk, None, torch.float32, "w_uk"), _ptr(gamma_k_rope, None, torch.float32, "gamma_k_rope"),
+        _ptr(w_uk, (cfg.n_groups, cfg.latent_rank, cfg.head_dim), torch.float32, "w_uk"),
+        _ptr(gamma_k_rope, (cfg.rope_dim,), torch.float32, "gamma_k_rope"),
         _ptr(positions, (B,), torch.int32, "positions"), L_cap,
         _ptr(latent_cache, (B, L_cap, cfg.latent_rank), dt, "latent_cache"),
         _ptr(rope_cache, (B, L_cap, cfg.rope_dim), dt, "rope_cache"),
@@ -276,12 +281,12 @@ def decode(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, rope_ca
         ctypes.byref(cfg.c()), B, _ptr(q_c, (B, H, cfg.head_dim), dt, "q_c"),
         _ptr(q_rope, (B, H, cfg.rope_dim), dt, "q_rope"),
         _ptr(w_qabs, (cfg.n_groups, r, cfg.head_dim), dt, "w_qabs"),
-        _ptr(gamma_q_rope, None, torch.float32, "gamma_q_rope"),
+        _ptr(gamma_q_rope, (cfg.rope_dim,), torch.float32, "gamma_q_rope"),
         _ptr(latent_cache, (B, L_cap, r), dt, "latent_cache"),
         _ptr(rope_cache, (B, L_cap, cfg.rope_dim), dt, "rope_cache"),
         _ptr(alpha_cache, (B, L_cap, cfg.n_groups), torch.float32, "alpha_cache"),
         _ptr(seq_lens, (B,), torch.int32, "seq_lens"), L_cap, max_seq_len,
-        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(workspace, (workspace.numel(),), torch.uint8, "workspace"), workspace.numel(),
         _ptr(o_lat, (B, H, r), torch.float32, "o_lat"),
         _ptr(lse, (B, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
         _stream()), "qkmla_decode")
@@ -303,12 +308,12 @@ def decode_multi(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, r
         ctypes.byref(cfg.c()), B, s_q, _ptr(q_c, (B, s_q, H, cfg.head_dim), dt, "q_c"),
         _ptr(q_rope, (B, s_q, H, cfg.rope_dim), dt, "q_rope"),
         _ptr(w_qabs, (cfg.n_groups, r, cfg.head_dim), dt, "w_qabs"),
-        _ptr(gamma_q_rope, None, torch.float32, "gamma_q_rope"),
+        _ptr(gamma_q_rope, (cfg.rope_dim,), torch.float32, "gamma_q_rope"),
         _ptr(latent_cache, (B, L_cap, r), dt, "latent_cache"),
         _ptr(rope_cache, (B, L_cap, cfg.rope_dim), dt, "rope_cache"),
         _ptr(alpha_cache, (B, L_cap, cfg.n_groups), torch.float32, "alpha_cache"),
         _ptr(seq_lens, (B,), torch.int32, "seq_lens"), L_cap, max_seq_len,
-        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(workspace, (workspace.numel(),), torch.uint8, "workspace"), workspace.numel(),
         _ptr(o_lat, (B, s_q, H, r), torch.float32, "o_lat"),
         _ptr(lse, (B, s_q, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
         _stream()), "qkmla_decode_multi")
@@ -336,7 +341,8 @@ def append_paged(cfg: Config, c_new, k_rope_new, w_uk, gamma_k_rope, positions, 
     _check(_lib.qkmla_append_paged(
         ctypes.byref(cfg.c()), B, n_new, _ptr(c_new, (B, n_new, cfg.latent_rank), dt, "c_new"),
         _ptr(k_rope_new, (B, n_new, cfg.rope_dim), dt, "k_rope_new"),
-        _ptr(w_uk, None, torch.float32, "w_uk"), _ptr(gamma_k_rope, None, torch.float32, "gamma_k_rope"),
+        _ptr(w_uk, (cfg.n_groups, cfg.latent_rank, cfg.head_dim), torch.float32, "w_uk"),
+        _ptr(gamma_k_rope, (cfg.rope_dim,), torch.float32, "gamma_k_rope"),
         _ptr(positions, (B,), torch.int32, "positions"), ctypes.byref(pg),
         _ptr(latent_pool, (NP, PS, cfg.latent_rank), dt, "latent_pool"),
         _ptr(rope_pool, (NP, PS, cfg.rope_dim), dt, "rope_pool"),
@@ -359,12 +365,12 @@ def decode_paged(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_pool, ro
         ctypes.byref(cfg.c()), B, s_q, _ptr(q_c, (B, s_q, H, cfg.head_dim), dt, "q_c"),
         _ptr(q_rope, (B, s_q, H, cfg.rope_dim), dt, "q_rope"),
         _ptr(w_qabs, (cfg.n_groups, r, cfg.head_dim), dt, "w_qabs"),
-        _ptr(gamma_q_rope, None, torch.float32, "gamma_q_rope"),
+        _ptr(gamma_q_rope, (cfg.rope_dim,), torch.float32, "gamma_q_rope"),
         _ptr(latent_pool, (NP, PS, r), dt, "latent_pool"),
         _ptr(rope_pool, (NP, PS, cfg.rope_dim), dt, "rope_pool"),
         _ptr(alpha_pool, (NP, PS, cfg.n_groups), torch.float32, "alpha_pool"),
         _ptr(seq_lens, (B,), torch.int32, "seq_lens"), ctypes.byref(pg), max_seq_len,
-        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(workspace, (workspace.numel(),), torch.uint8, "workspace"), workspace.numel(),
         _ptr(o_lat, (B, s_q, H, r), torch.float32, "o_lat"),
         _ptr(lse, (B, s_q, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
         _stream()), "qkmla_decode_paged")
@@ -415,7 +421,7 @@ def train_forward(cfg: Config, inputs: dict, workspace, o=None, lse=None):
     ins = _train_inputs(cfg, inputs, (B, T))
     _check(_lib.qkmla_train_forward(
         ctypes.byref(cfg.c()), B, T, ctypes.byref(ins),
-        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(),
+        _ptr(workspace, (workspace.numel(),), torch.uint8, "workspace"), workspace.numel(),
         _ptr(o, (B, T, H, cfg.v_head_dim), torch.float32, "o"),
         _ptr(lse, (B, T, H), torch.float32, "lse"), _stream()), "qkmla_train_forward")
     return o, lse
@@ -438,7 +444,7 @@ def train_backward(cfg: Config, inputs: dict, o, lse, d_o, workspace, grads: Opt
         _ptr(o, (B, T, H, cfg.v_head_dim), torch.float32, "o"),
         _ptr(lse, (B, T, H), torch.float32, "lse"),
         _ptr(d_o, (B, T, H, cfg.v_head_dim), torch.float32, "d_o"),
-        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(), ctypes.byref(gs),
+        _ptr(workspace, (workspace.numel(),), torch.uint8, "workspace"), workspace.numel(), ctypes.byref(gs),
         _stream()), "qkmla_train_backward")
     return grads
 
@@ -465,8 +471,8 @@ def train_forward_varlen(cfg: Config, inputs: dict, cu_seqlens, max_seq_len: int
         lse = torch.empty((total, H), dtype=torch.float32, device=dev)
     ins = _train_inputs(cfg, inputs, (total,))
     _check(_lib.qkmla_train_forward_varlen(
-        ctypes.byref(cfg.c()), n_seqs, _ptr(cu_seqlens, None, torch.int32, "cu_seqlens"), total,
-        max_seq_len, ctypes.byref(ins), _ptr(workspace, None, torch.uint8, "workspace"),
+        ctypes.byref(cfg.c()), n_seqs, _ptr(cu_seqlens, (n_seqs + 1,), torch.int32, "cu_seqlens"), total,
+        max_seq_len, ctypes.byref(ins), _ptr(workspace, (workspace.numel(),), torch.uint8, "workspace"),
         workspace.numel(), _ptr(o, (total, H, cfg.v_head_dim), torch.float32, "o"),
         _ptr(lse, (total, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
         _stream()), "qkmla_train_forward_varlen")
@@ -486,10 +492,10 @@ def train_backward_varlen(cfg: Config, inputs: dict, cu_seqlens, max_seq_len: in
     gs = _TrainGrads(*[_ptr(grads[n], tuple(inputs[n[2:]].shape), torch.float32, n)
                        for n in TRAIN_GRAD_NAMES])
     _check(_lib.qkmla_train_backward_varlen(
-        ctypes.byref(cfg.c()), n_seqs, _ptr(cu_seqlens, None, torch.int32, "cu_seqlens"), total,
+        ctypes.byref(cfg.c()), n_seqs, _ptr(cu_seqlens, (n_seqs + 1,), torch.int32, "cu_seqlens"), total,
         max_seq_len, ctypes.byref(ins), _ptr(o, (total, H, cfg.v_head_dim), torch.float32, "o"),
         _ptr(lse, (total, H), torch.float32, "lse"),
         _ptr(d_o, (total, H, cfg.v_head_dim), torch.float32, "d_o"),
-        _ptr(workspace, None, torch.uint8, "workspace"), workspace.numel(), ctypes.byref(gs),
+        _ptr(workspace, (workspace.numel(),), torch.uint8, "workspace"), workspace.numel(), ctypes.byref(gs),
         _ptr(status, (1,), torch.int32, "status"), _stream()), "qkmla_train_backward_varlen")
     return grads

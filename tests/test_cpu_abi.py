@@ -263,3 +263,19 @@ def test_varlen_train_entry_points_validate_on_the_host():
     grads = ops._TrainGrads(*([p] * 10))
     assert lib.qkmla_train_backward_varlen(c, 2, p, 9, 5, ctypes.byref(ins), p, p, p, p, need - 256,
                                            ctypes.byref(grads), None, None) == 3
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """A host tensor's address handed to a kernel would be a device memory
+    fault; the binding refuses it (and wrong shapes) with an error instead."""
+    import torch
+    ops = _ops()
+    cfg = _cfg(n_heads=4, n_groups=2, latent_rank=32, head_dim=16, rope_dim=8, v_head_dim=16,
+               dtype="f32")
+    w = torch.zeros((2, 32, 16))
+    g = torch.ones((16,))
+    with pytest.raises(ops.QkmlaError, match="current GPU"):
+        ops.absorb_weights(cfg, w, g, g, out=torch.empty((2, 32, 16)))
+    with pytest.raises(ops.QkmlaError, match="current GPU"):
+        ops.out_proj(cfg, torch.zeros((1, 4, 32)), torch.zeros((2, 32, 16)),
+                     out=torch.empty((1, 4, 16)))

@@ -580,9 +580,10 @@ def hazard_checker(dev):
 @case
 def isa_semantics(dev):
     """Emulator semantics that the compiled kernels lean on, against numpy on
-    random registers: SDWA source selects (word / byte of a source) on integer
-    VOP ops, and the gfx9 16-bit integer ops (low halves in, high half of the
-    destination zeroed)."""
+    random registers: SDWA source selects (word / byte of a VGPR or SGPR
+    source) on integer VOP ops, the gfx9 16-bit integer ops (low halves in,
+    high half of the destination zeroed) and v_bitop3_b32's truth table (bit
+    4a + 2b + c)."""
     from isa_emu.machine import Wave, Workgroup
     lines = [
         "v_mul_lo_u16_sdwa v3, v1, v2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 "
@@ -594,6 +595,14 @@ def isa_semantics(dev):
         "v_lshlrev_b16_e32 v6, 3, v1",
         "v_sub_u16_e32 v7, v1, v2",
         "v_mul_lo_u16_e32 v8, v1, v2",
+        # SGPR sources in SDWA forms, and the three-input bit table
+        "v_and_b32_sdwa v9, s3, v2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+        "src1_sel:WORD_1",
+        "v_mul_u32_u24_sdwa v10, v1, s3 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 "
+        "src1_sel:DWORD",
+        "v_or_b32_sdwa v11, s3, v2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+        "src1_sel:WORD_1",
+        "v_bitop3_b32 v12, v1, v2, s3 bitop3:0x78",
         "s_endpgm",
     ]
     insts = [parse_inst(t, k) for k, t in enumerate(lines)]
@@ -607,8 +616,11 @@ def isa_semantics(dev):
     a = rng.integers(0, 2**32, 64, dtype=np.uint64).astype(np.uint32)
     b = rng.integers(0, 2**32, 64, dtype=np.uint64).astype(np.uint32)
     w.V[1], w.V[2] = a, b
+    sc = 0x9E3779B9
+    w.S[3] = sc
     emu._run_group(k, wg, [w], (0, 0, 0), 100)
     a64, b64 = a.astype(np.uint64), b.astype(np.uint64)
+    s64 = np.uint64(sc)
     m16 = np.uint64(0xFFFF)
     expect = {
         3: (((a64 >> np.uint64(16)) & m16) * (b64 & m16)) & m16,
@@ -617,10 +629,15 @@ def isa_semantics(dev):
         6: ((a64 & m16) << np.uint64(3)) & m16,
         7: ((a64 & m16) - (b64 & m16)) & m16,
         8: ((a64 & m16) * (b64 & m16)) & m16,
+        9: s64 & ((b64 >> np.uint64(16)) & m16),
+        10: ((a64 & m16) * (s64 & np.uint64(0xFFFFFF))) & np.uint64(0xFFFFFFFF),
+        11: s64 | ((b64 >> np.uint64(16)) & m16),
+        12: a64 ^ (b64 & s64),  # table 0x78: bit (a b c) set for 011, 100, 101, 110
     }
     for r, e in expect.items():
         assert np.array_equal(w.V[r].astype(np.uint64), e), f"v{r}: {lines[r - 3]}"
-    print("[ok] SDWA source selects and 16-bit integer ops match numpy", flush=True)
+    print("[ok] SDWA source selects (VGPR and SGPR sources), 16-bit integer ops and the "
+          "three-input bit table match numpy", flush=True)
 
 
 def main(argv):

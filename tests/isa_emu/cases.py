@@ -518,6 +518,71 @@ def bf16_long_segments(dev):
               heads=MERGE_HEADS)
 
 
+def _plan_rows(dev, lens, cap, n_wg):
+    """Host replay of the decode plan through the library: rows (workgroup,
+    sequence, first tile, end tile, kind), kind -1 = written directly."""
+    f = dev.lib.qkmla_plan_segments
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    ln = np.ascontiguousarray(lens, np.int32)
+    n = ctypes.c_int32()
+    assert f(len(ln), ln.ctypes.data, cap, n_wg, None, 0, ctypes.byref(n)) == 0
+    out = np.zeros((n.value, 5), np.int32)
+    assert f(len(ln), ln.ctypes.data, cap, n_wg, out.ctypes.data, n.value, ctypes.byref(n)) == 0
+    return out
+
+
+def _hw_of_plan(p, n):
+    """Hardware workgroup that takes plan range p (the XCD order of the split-KV
+    kernel: range (hw mod 8) * n/8 + hw/8 when n is a multiple of 8)."""
+    return p if n % 8 else (p % (n // 8)) * 8 + p // (n // 8)
+
+
+@case
+def bf16_max_batch(dev):
+    """The largest batch a decode call takes, 4096 sequences of 1..96 tokens,
+    in the launch configuration of a 256-CU GPU (256 split-KV workgroups,
+    hardware workgroups in XCD order).  The first and the last plan range run
+    (each streams about 32 tiles of 16 sequences), with the q-prep blocks of
+    the sequences they read; every sequence they complete is checked."""
+    B, n_wg = 4096, 256
+    lens = [int(x) for x in np.random.default_rng(510).integers(1, 97, size=B)]
+    rows = _plan_rows(dev, lens, max(lens), n_wg)
+    ranges = (0, n_wg - 1)
+    mine = rows[np.isin(rows[:, 0], ranges)]
+    read = {int(b) for b in mine[:, 1]}
+    whole = sorted({int(b) for b in mine[mine[:, 4] < 0][:, 1]})
+    assert len(whole) >= 8 and any(mine[:, 4] >= 0), "want whole and split sequences"
+    hws = [_hw_of_plan(p, n_wg) for p in ranges]
+    assert hws == [0, n_wg - 1]
+
+    def groups(name, grid):
+        if "decode_mfma_kernel" in name:
+            assert grid[0] == n_wg, grid
+            return [(hw, 0, 0) for hw in hws]
+        if "qprep" in name:
+            return [(b, y, 0) for b in sorted(read) for y in range(grid[1])]
+        if "merge_kernel" in name or "out_proj" in name:
+            ys = [y for y in MERGE_HEADS if y < grid[1]] if "merge" in name else range(grid[1])
+            return [(b, y, z) for b in whole for y in ys for z in range(grid[2])]
+        return None
+    inp = make_inputs(DSV3, lens, seed=510)
+    keep = dev.group_filter
+    dev.group_filter = groups
+    os.environ["QKMLA_NUM_WG"] = str(n_wg)
+    try:
+        s = Session(dev, DSV3, inp, host_fill=True, fill_only=read)
+        o_lat, lse = s.decode()
+        out = s.out_proj()
+    finally:
+        os.environ.pop("QKMLA_NUM_WG", None)
+        dev.group_filter = keep
+    compare(DSV3, out, o_lat, lse, reference(DSV3, inp, True, batch_ids=whole), whole,
+            list(MERGE_HEADS), f"bf16 batch 4096, {len(whole)} whole sequences of two workgroups")
+    assert s.status[0] == 0
+
+
 @case
 def bf16_plain_overflow(dev):
     """Plain MLA on latents scaled by up to 1e3: unnormalised logits exceed the

@@ -186,10 +186,11 @@ class Session:
     driven through the C ABI exactly as the GPU tests drive it.
 
     ``host_fill`` writes the caches from the oracle's append instead of
-    running the append kernel (to keep long cases short)."""
+    running the append kernel (to keep long cases short); ``fill_only``
+    limits that to the listed sequences (the others keep zero rows)."""
 
     def __init__(self, dev: Device, shape, inp, qk_norm: bool = True, host_fill: bool = False,
-                 hold_last: bool = False):
+                 hold_last: bool = False, fill_only=None):
         self.dev, self.shape, self.inp = dev, shape, inp
         s = shape
         self.bf = s.dtype == "bf16"
@@ -231,7 +232,7 @@ class Session:
         if host_fill:
             import oracle
             for b, n in enumerate(fill):
-                if n > 0:
+                if n > 0 and (fill_only is None or b in fill_only):
                     a_ref, r_ref = oracle.append_ref(inp.latents[b][:n], inp.k_rope_raw[b][:n],
                                                      np.arange(n), inp.w_uk, inp.gamma_k_rope, 1e-6,
                                                      10000.0, qk_norm=qk_norm)

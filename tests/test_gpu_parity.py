@@ -268,6 +268,31 @@ def test_full_size_workloads_sampled(cid, samples):
     check_caches(sess, inp, cfg, sorted({b for b, _ in samples}), max_rows=2048)
 
 
+def test_maximum_batch_sampled():
+    """The largest batch one decode call takes: 4096 sequences of 1..96 tokens
+    (one to three tiles; some straddle two workgroups and are merged), caches
+    from qkmla_append, the default plan.  Whole and merged sequences sampled
+    against the oracle; every lse finite."""
+    B = 4096
+    lens = tuple(int(x) for x in np.random.default_rng(620).integers(1, 97, size=B))
+    inp = make_inputs(DSV3, lens, seed=620)
+    cfg = ops.Config.from_shape(DSV3)
+    sess, o, o_lat, lse = _run(cfg, inp, "bf16 batch 4096 (maximum)")
+    assert int(sess.status.item()) == 0
+    assert np.isfinite(lse).all()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    n_wg = ops.plan(cfg, B, max(lens), n_cu)[0]
+    rows = ops.plan_segments(lens, max(lens), n_wg)
+    split = sorted({int(r[1]) for r in rows if r[4] >= 0})
+    whole = sorted({int(r[1]) for r in rows if r[4] < 0})
+    assert split and whole
+    sample = split[::max(1, len(split) // 24)][:24] + whole[::max(1, len(whole) // 24)][:24]
+    ref = oracle_decode(inp, cfg, batch_ids=sample)
+    check_outputs(o, o_lat, lse, ref, cfg.dtype, sample, list(range(cfg.n_heads)),
+                  f"batch 4096: {len(sample)} sampled of {len(split)} merged, {len(whole)} whole")
+    check_caches(sess, inp, cfg, sample)
+
+
 # --- paged caches: a block table over shared pools ---------------------------------------
 
 def _paged_pools(cfg, inp, page_size, seed, max_blocks=None, chunk=65536):

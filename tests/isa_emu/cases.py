@@ -496,12 +496,14 @@ def train_fwd_bwd(dev):
 @case
 def train_mfma(dev):
     """The MFMA attention of the bf16 layer (H=128, G=8, d_c+d_r=192,
-    d_v=128), forward and backward, over 37 tokens: a full and a partial key
-    tile, five query blocks (the last partly past the sequence).  Q^, K^, V,
-    P, dS and d_o are rounded to bf16: bounds 2e-2 on o (per row, relative),
-    5e-2 on lse and 2e-2 on every gradient (of its largest element).  Also
-    plain MLA (no norms, zero gamma gradients) over 21 tokens."""
-    run_train(dev, DSV3, 1, 37, 612, "train MFMA forward + backward, 37 tokens",
+    d_v=128), forward and backward, over 70 tokens: two full key tiles and a
+    partial one, so the double-buffered tile stages are each refilled, nine
+    query blocks (the last partly past the sequence), and key-side waves that
+    skip the query steps before their keys.  Q^, K^, V, P, dS and d_o are
+    rounded to bf16: bounds 2e-2 on o (per row, relative), 5e-2 on lse and
+    2e-2 on every gradient (of its largest element).  Also plain MLA (no
+    norms, zero gamma gradients) over 21 tokens."""
+    run_train(dev, DSV3, 1, 70, 612, "train MFMA forward + backward, 70 tokens",
               tol=dict(o=2e-2, lse=5e-2, grad=2e-2))
     run_train(dev, DSV3, 1, 21, 613, "train MFMA forward + backward, plain MLA, 21 tokens",
               qk_norm=False, tol=dict(o=2e-2, lse=5e-2, grad=2e-2))

@@ -13,24 +13,30 @@
 
 namespace qkmla {
 
-// One block per (sequence b, head h, block of 128 latent dims); 256 threads =
-// 8 source groups x 32 dim-quads.  Source group k folds the partials
-// p = p_lo + k, p_lo + k + 8, ... in one pass with a running maximum (each
-// source's m, l and O are loaded independently, so the loads overlap); the
-// eight groups meet in LDS.  The tile prefix of the plan comes from the
-// workspace, where the split-KV kernel left it.
-constexpr int kMergeDims = 128;
-constexpr int kMergeGroups = 8;
+// One block per (sequence b, head h, block of 64 latent dims); 256 threads =
+// 16 source groups x 16 dim-quads.  The block first lists its sources in LDS
+// (the partial slot each workgroup of the sequence wrote, one thread per
+// workgroup, so the slot arithmetic is off the load path), then source group
+// k folds the sources k, k + 16, ... with a running maximum, issuing the
+// loads of up to four sources before it folds them.  The 16 groups meet in
+// LDS.  The tile prefix of the plan comes from the workspace, where the
+// split-KV kernel left it.
+constexpr int kMergeDims = 64;
+constexpr int kMergeGroups = 16;
+constexpr int kMergeQuads = kMergeDims / 4;   // lanes per source group
+constexpr int kMergeBatch = 4;                // sources in flight per thread
+constexpr int kMergeList = 256;               // sources listed per pass
 
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ plan, int B, int H,
                                                     int r, int n_wg,
                                                     const char* __restrict__ part,
                                                     float* __restrict__ o_lat,
                                                     float* __restrict__ lse) {
-  __shared__ f32x4 red[kMergeGroups][32];
+  __shared__ f32x4 red[kMergeGroups][kMergeQuads];
   __shared__ float red_m[kMergeGroups], red_l[kMergeGroups];
+  __shared__ int src[kMergeList];  // slot index p * kSlotsPerWg + slot, or -1 (nothing written)
   const int b = blockIdx.x, h = blockIdx.y, dblk = blockIdx.z;
-  const int tid = threadIdx.x, sg = tid >> 5, dq = tid & 31;
+  const int tid = threadIdx.x, sg = tid / kMergeQuads, dq = tid % kMergeQuads;
   const int d0 = dblk * kMergeDims + 4 * dq;
   float* out = o_lat + ((size_t)b * H + h) * r + d0;
   const int Pb = plan[b], Pb1 = plan[b + 1];
@@ -44,23 +50,51 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
   const int p_hi = wg_of(Pb1 - 1, N, n_wg);
   if (p_lo == p_hi) return;  // written directly by the decode kernel
   const size_t slot_bytes = kPartialSlotBytes(H, r);
+  const size_t o_off = (size_t)H * 8 + ((size_t)h * r + d0) * 2;
   float M = -INFINITY, lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int p = p_lo + sg; p <= p_hi; p += kMergeGroups) {
+  const int n_src = p_hi - p_lo + 1;
+  const int first = p_lo * kSlotsPerWg + merge_slot_of(Pb, p_lo, N, n_wg, p_lo);
+  for (int c0 = 0; c0 < n_src; c0 += kMergeList) {
+    const int cn = min(kMergeList, n_src - c0);
     // Workgroups between p_lo and p_hi with an empty range (more workgroups
     // than tiles) wrote nothing and are skipped.
-    const int slot = merge_slot_of(Pb, p_lo, N, n_wg, p);
-    if (slot < 0) continue;
-    const char* sp = part + ((size_t)p * kSlotsPerWg + slot) * slot_bytes;
-    const float m = ((const float*)sp)[h], l = ((const float*)sp)[H + h];
-    const uint2 ob = *(const uint2*)((const uint16_t*)(sp + (size_t)H * 8) + (size_t)h * r + d0);
-    const f32x4 v = {__uint_as_float(ob.x << 16), __uint_as_float(ob.x & 0xFFFF0000u),
-                     __uint_as_float(ob.y << 16), __uint_as_float(ob.y & 0xFFFF0000u)};
-    const float Mn = fmaxf(M, m);
-    const float keep = exp2f(M - Mn), w = exp2f(m - Mn);  // M = -inf: keep = 0
-    acc = acc * keep + v * w;
-    lsum = lsum * keep + l * w;
-    M = Mn;
+    if (tid < cn) {
+      const int p = p_lo + c0 + tid;
+      const int slot = merge_slot_of(Pb, p_lo, N, n_wg, p);
+      src[tid] = slot < 0 ? -1 : p * kSlotsPerWg + slot;
+    }
+    __syncthreads();
+    for (int k0 = sg; k0 < cn; k0 += kMergeBatch * kMergeGroups) {
+      // Branch-free: an entry past the list or without a partial reads the
+      // first workgroup's slot (always written) and gets weight 0, so the
+      // loads of all kMergeBatch sources are issued before the first fold.
+      float m[kMergeBatch], l[kMergeBatch];
+      uint2 ob[kMergeBatch];
+      bool ok[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int k = k0 + u * kMergeGroups;
+        const int e = src[k < cn ? k : cn - 1];
+        ok[u] = k < cn && e >= 0;
+        const char* sp = part + (size_t)(ok[u] ? e : first) * slot_bytes;
+        m[u] = ((const float*)sp)[h];
+        l[u] = ((const float*)sp)[H + h];
+        ob[u] = *(const uint2*)(sp + o_off);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const f32x4 v = {__uint_as_float(ob[u].x << 16), __uint_as_float(ob[u].x & 0xFFFF0000u),
+                         __uint_as_float(ob[u].y << 16), __uint_as_float(ob[u].y & 0xFFFF0000u)};
+        const float Mn = ok[u] ? fmaxf(M, m[u]) : M;
+        const float keep = Mn == M ? 1.f : exp2f(M - Mn);  // also M = Mn = -inf
+        const float w = ok[u] ? exp2f(m[u] - Mn) : 0.f;
+        acc = acc * keep + v * w;
+        lsum = lsum * keep + l[u] * w;
+        M = Mn;
+      }
+    }
+    __syncthreads();  // the list is rewritten by the next pass
   }
   red[sg][dq] = acc;
   if (dq == 0) {

@@ -119,6 +119,23 @@ def bf16_split(dev):
 
 
 @case
+def bf16_many_splits(dev):
+    """The merge over many sources: one sequence split over 80 workgroups
+    (each source group folds two batches of sources), then 170 tiles of two
+    sequences over 300 workgroups, of which 130 hold no tile: the long
+    sequence lists more than 256 sources (two passes of the list), many of
+    them empty."""
+    run_layer(dev, DSV3, (80 * 32,), 509, "bf16 one sequence over 80 workgroups", n_wg=80,
+              heads=MERGE_HEADS)
+    lens = (150 * 32 - 5, 20 * 32 - 7)
+    rows = _plan_rows(dev, list(lens), max(lens), 300)
+    p0 = rows[rows[:, 1] == 0][:, 0]
+    assert p0.max() - p0.min() + 1 > 256, "want more than one pass of the source list"
+    run_layer(dev, DSV3, lens, 511, "bf16 170 tiles over 300 workgroups (empty ranges)",
+              n_wg=300, heads=MERGE_HEADS)
+
+
+@case
 def bf16_plain_hold(dev):
     """Plain MLA split-KV and the one-token append of the decode step."""
     run_layer(dev, DSV3, (40, 64), 501, "bf16 plain MLA, last token appended in the step",

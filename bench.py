@@ -112,6 +112,8 @@ class Bench:
         self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
         self.o_lat = torch.empty((B, H, r), dtype=f32, device=dev)
         self.lse = torch.empty((B, H), dtype=f32, device=dev)
+        self.w_uv = (torch.randn((G, r, s.v_head_dim), generator=g, device=dev) / math.sqrt(r)).to(dt)
+        self.o_out = torch.empty((B, H, s.v_head_dim), dtype=f32, device=dev)
         self.tokens = sum(self.lengths)
         self.bytes_qk = self.tokens * cache_bytes_per_token(s, True)
         self.bytes_plain = self.tokens * cache_bytes_per_token(s, False)
@@ -122,9 +124,9 @@ class Bench:
             self.step_pos = torch.tensor([L - 1 for L in self.lengths], dtype=torch.int32, device=dev)
         self.i = 0
 
-    def step(self, plain=False):
+    def step(self, plain=False, rotate=True):
         ops = self.ops
-        lat, rope, alpha = self.copies[self.i % self.n_copies]
+        lat, rope, alpha = self.copies[self.i % self.n_copies if rotate else 0]
         self.i += 1
         cfg = self.cfg_plain if plain else self.cfg
         if self.w.append_last:
@@ -148,6 +150,30 @@ class Bench:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
+
+    def step_spread(self, steps, rotate=True):
+        """Per-step times (eager launches, a HIP event pair around each step):
+        (p10, p50, p90) in ms.  rotate=False streams one cache copy every
+        step, which the memory-side cache may then hold ("warm")."""
+        torch = self.torch
+        for _ in range(3):
+            self.step(rotate=rotate)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record()
+            self.step(rotate=rotate)
+            e1.record()
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        pick = lambda q: t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))]
+        return pick(0.1), pick(0.5), pick(0.9)
+
+    def out_proj_ms(self, steps):
+        """qkmla_out_proj (the V up-projection) on this batch, eager, HIP events."""
+        return _event_ms(self.torch, lambda: self.ops.out_proj(self.cfg, self.o_lat, self.w_uv,
+                                                               self.o_out), steps)
 
     def graph_time(self, steps, plain=False):
         """Step time with the step captured in HIP graphs: one step per cache
@@ -305,6 +331,9 @@ def measure(cid, steps, warmup, graph=True):
     ms_plain_eager, _ = b.time_steps(steps, warmup, plain=True)
     qp_ms, k_ms, mg_ms = b.kernel_breakdown_ms(steps)
     k_ms_plain = b.kernel_ms(steps, plain=True)
+    p10, p50, p90 = b.step_spread(steps)
+    w10, w50, w90 = b.step_spread(steps, rotate=False)
+    op_ms = b.out_proj_ms(steps)
     g_ms, g_note = b.graph_time(steps) if graph else (None, "not requested")
     g_ms_plain, g_note_plain = b.graph_time(steps, plain=True) if g_ms else (None, g_note)
     use_graph = g_ms is not None and g_ms_plain is not None
@@ -319,6 +348,10 @@ def measure(cid, steps, warmup, graph=True):
         "step_timing": "graph replay" if use_graph else "eager launches",
         "graph_note": None if use_graph else (g_note or g_note_plain),
         "us_per_step_eager": round(ms_eager * 1e3, 2),
+        "us_per_step_eager_p10_p50_p90": [round(x * 1e3, 2) for x in (p10, p50, p90)],
+        "warm_us_per_step_eager_p50": round(w50 * 1e3, 2),
+        "out_proj_us": round(op_ms * 1e3, 2),
+        "full_step_us": round((ms_qk + op_ms) * 1e3, 2),
         "plain_us_per_step": round(ms_plain * 1e3, 2),
         "plain_us_per_step_eager": round(ms_plain_eager * 1e3, 2),
         "overhead_vs_plain_pct": round(100.0 * (ms_qk / ms_plain - 1.0), 2),
@@ -337,6 +370,25 @@ def measure(cid, steps, warmup, graph=True):
     if status:
         raise RuntimeError(f"device status {status} during the benchmark")
     return b, res, ms_qk, k_ms, wall
+
+
+def read_probe(reps=10):
+    """The read-stream peak this GPU reaches with a plain kernel: a
+    float32-accumulated sum over 4 GiB of bf16 (every byte read once), and a
+    1 GiB copy (read + write), both timed with HIP events."""
+    import torch
+    x = torch.ones((2 << 30,), dtype=torch.bfloat16, device="cuda")
+    ms_sum = _event_ms(torch, lambda: torch.sum(x, dtype=torch.float32), reps)
+    sum_gbps = x.numel() * 2 / (ms_sum * 1e-3) / 1e9
+    del x
+    a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda")
+    c = torch.empty_like(a)
+    ms_copy = _event_ms(torch, lambda: c.copy_(a), reps)
+    copy_gbps = 2 * a.numel() / (ms_copy * 1e-3) / 1e9
+    del a, c
+    torch.cuda.empty_cache()
+    return {"sum_read_GBps": round(sum_gbps, 1), "copy_read_write_GBps": round(copy_gbps, 1),
+            "what": "torch sum over 4 GiB bf16 (fp32 accumulation); torch copy of 1 GiB"}
 
 
 def _event_ms(torch, fn, reps, warmup=2):
@@ -646,6 +698,10 @@ def main():
     }
     del b
     torch.cuda.empty_cache()
+    probe = read_probe()
+    line["read_probe"] = probe
+    line["roofline"]["frac_of_read_probe"] = round(achieved / probe["sum_read_GBps"], 4)
+    print(f"[bench] read probe {probe}", file=sys.stderr, flush=True)
     if not args.no_sweep:
         sweep = []
         for cid in (2, 3, 4):

@@ -592,24 +592,40 @@ def cpu_baseline(cid, budget_s=15.0):
     from mla_latent_decode_amd.layout import cache_bytes_per_token
     w = WORKLOADS[cid]
     lengths = _lengths(w)
-    done_tokens, elapsed, n = 0, 0.0, 0
+    done_tokens, elapsed, n, t_alpha = 0, 0.0, 0, 0.0
     for i, L in enumerate(lengths):
         inp = make_inputs(w.shape, [L], seed=4000 + i, row_scale_log10_clip=w.row_scale_log10_clip)
         t0 = time.perf_counter()
         oracle.explicit_decode(inp.q_c, inp.q_rope, inp.latents, inp.k_rope_raw, inp.w_uk, inp.w_uv,
                                inp.gamma_q, inp.gamma_k, inp.gamma_q_rope, inp.gamma_k_rope)
         elapsed += time.perf_counter() - t0
+        # the alpha / RoPE-key part (what qkmla_append computes), timed on its own
+        t0 = time.perf_counter()
+        oracle.append_ref(inp.latents[0], inp.k_rope_raw[0], np.arange(L), inp.w_uk,
+                          inp.gamma_k_rope, 1e-6, 10000.0)
+        t_alpha += time.perf_counter() - t0
         done_tokens += L
         n += 1
-        if elapsed >= budget_s:
+        if elapsed + t_alpha >= budget_s:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    info = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in info] + [1])
+    blas = sorted({f"{p.get('internal_api')} {p.get('version')}" for p in info
+                   if p.get("user_api") == "blas"})
+    cpu = "unknown"
+    try:
+        cpu = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
+                   if ln.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     gbps = done_tokens * cache_bytes_per_token(w.shape, True) / elapsed / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {len(lengths)} sequences ({done_tokens} cached tokens) of the same "
                       f"workload, fp64 explicit form, {elapsed:.1f} s",
             "us_per_step_extrapolated": round(elapsed / done_tokens * sum(lengths) * 1e6, 1),
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+            "alpha_append_us_per_step_extrapolated":
+                round(t_alpha / done_tokens * sum(lengths) * 1e6, 1),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu, "blas": blas}
 
 
 def main():
@@ -714,6 +730,12 @@ def main():
             del _b
             torch.cuda.empty_cache()
         line["sweep"] = sweep
+        # mean QK-norm overhead over the 4k, 32k and 256k workloads
+        from mla_latent_decode_amd.inputs import WORKLOADS
+        over = [r["overhead_vs_plain_pct"] for r in [res] + sweep
+                if r["workload"] in {WORKLOADS[c].name for c in (1, 2, 3)}]
+        if len(over) == 3:
+            line["overhead_vs_plain_pct_mean_4k_32k_256k"] = round(sum(over) / 3, 2)
     print(json.dumps(line), flush=True)
 
 

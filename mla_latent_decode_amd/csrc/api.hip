@@ -62,7 +62,9 @@ int check_cfg(const qkmla_config* cfg, Cfg* out, bool decode_shapes = true) {
   if (c.dtype == QKMLA_BF16 && decode_shapes) {
     const int hpg = c.n_heads / c.n_groups;
     // H = 32 (one wavefront per workgroup) is switched off: that instantiation
-    // faulted on the GPU with the asm tile loads and its cause is not yet found.
+    // faulted on the GPU when the tile loads were inline asm (a VALU write of the
+    // load's scalar base too few wait states ahead of it). The builtin loads used
+    // now do not have that hazard, but this variant has not run on a GPU since.
     const bool h_ok = c.n_heads == 64 || c.n_heads == 128;
     if (c.latent_rank != 512 || c.rope_dim != 64 || !h_ok || hpg != 16 || c.head_dim % 32 != 0 ||
         c.head_dim > 256)

@@ -35,6 +35,34 @@ def build_runtime(out_dir: str) -> str:
     return out
 
 
+# gfx950 limits a launch must respect, or the runtime rejects it
+GFX950_LDS_BYTES = 160 * 1024      # LDS per workgroup (static + dynamic)
+GFX950_REGS_PER_SIMD_LANE = 512    # unified VGPR + AGPR file, per lane of a SIMD
+GFX950_SIMDS_PER_CU = 4
+
+
+def check_launch_fits(name, md, static_lds, grid, block, dyn_lds):
+    """Raise EmuError for a launch configuration that the device would refuse:
+    a workgroup above the kernel's compiled maximum size, more LDS than a
+    workgroup can have, registers that do not fit one CU, or grid dimensions
+    out of range.  The emulator itself would run such a launch."""
+    short = name[:60]
+    threads = block[0] * block[1] * block[2]
+    if min(block) < 1 or min(grid) < 1:
+        raise EmuError(f"{short}: empty grid {grid} or block {block}")
+    if grid[0] >= 2 ** 31 or grid[1] > 65535 or grid[2] > 65535:
+        raise EmuError(f"{short}: grid {grid} out of range")
+    maxw = md.get(".max_flat_workgroup_size", 1024)
+    if threads > maxw:
+        raise EmuError(f"{short}: block of {threads} threads above the compiled maximum {maxw}")
+    if static_lds + dyn_lds > GFX950_LDS_BYTES:
+        raise EmuError(f"{short}: {static_lds} + {dyn_lds} B of LDS above {GFX950_LDS_BYTES}")
+    waves = -(-threads // 64)
+    per_simd = -(-waves // GFX950_SIMDS_PER_CU)
+    vg = md.get(".vgpr_count", 0)
+    if per_simd * vg > GFX950_REGS_PER_SIMD_LANE:
+        raise EmuError(f"{short}: {waves} waves of {vg} registers do not fit one CU")
+
 class Device:
     def __init__(self, repo: str, runtime_so: str, cu_count: int = 8, verbose: bool = False,
                  group_filter=None):
@@ -101,6 +129,7 @@ class Device:
             self._refresh_vars()
             k = self.kernels[name]
             md = k.md
+            check_launch_fits(name, md, k.lds_bytes, (gx, gy, gz), (bx, by, bz), shmem)
             ksz = md[".kernarg_segment_size"]
             # the runtime pads the argument segment; kernels may load past its end
             kab = self.alloc(((ksz + 63) // 64) * 64 + 64, "kernel arguments of " + name[:40])

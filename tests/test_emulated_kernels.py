@@ -68,3 +68,39 @@ def test_kernels_on_the_emulator(runtime, case):
     rc, out = _result(runtime, case)
     print(out)
     assert rc == 0, out[-4000:]
+
+
+def test_launch_limit_check_refuses_what_the_device_would():
+    """The emulator refuses launches the device would reject, so every case
+    above also checks its launch configurations."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from isa_emu.device import check_launch_fits
+    from isa_emu.machine import EmuError
+    md = {".max_flat_workgroup_size": 256, ".vgpr_count": 512}
+    check_launch_fits("k", md, 153088, (256, 1, 1), (256, 1, 1), 0)
+    bad = [((1, 1, 1), (512, 1, 1), 0, 0),        # above the compiled block size
+           ((1, 1, 1), (256, 1, 1), 160000, 4096),  # LDS over 160 KiB
+           ((0, 1, 1), (64, 1, 1), 0, 0),          # empty grid
+           ((1, 70000, 1), (64, 1, 1), 0, 0)]      # grid y out of range
+    for grid, block, lds, dyn in bad:
+        with pytest.raises(EmuError):
+            check_launch_fits("k", md, lds, grid, block, dyn)
+    with pytest.raises(EmuError):  # 8 waves of 512 registers need two waves per SIMD
+        check_launch_fits("k", {".max_flat_workgroup_size": 1024, ".vgpr_count": 512}, 0,
+                          (1, 1, 1), (512, 1, 1), 0)
+
+
+def test_every_compiled_kernel_fits_a_gfx950_cu():
+    """Static LDS and registers of every kernel in the library, at its compiled
+    maximum workgroup size, fit one gfx950 compute unit."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from isa_emu.asm import load_kernels
+    from isa_emu.device import GFX950_LDS_BYTES, check_launch_fits
+    n = 0
+    for f in ASM:
+        for name, k in load_kernels(f).items():
+            maxw = k.md.get(".max_flat_workgroup_size", 1024)
+            check_launch_fits(name, k.md, k.lds_bytes, (1, 1, 1), (maxw, 1, 1), 0)
+            assert k.lds_bytes <= GFX950_LDS_BYTES
+            n += 1
+    assert n >= 20, n

@@ -602,6 +602,148 @@ def bf16_max_batch(dev):
     assert s.status[0] == 0
 
 
+def _partials_offset(B, H, r, dr):
+    """Byte offset of the partial slots in the bf16 decode workspace: after
+    q~ (bf16 [B][H][r]), alpha^q (f32 [B][H]) and the RoPE query (bf16
+    [B][H][d_r]), each region aligned to 256 bytes."""
+    def up(x):
+        return (x + 255) // 256 * 256
+    return up(up(up(B * H * r * 2) + B * H * 4) + B * H * dr * 2)
+
+
+@case
+def bf16_long_context(dev):
+    """One sequence of 262144 tokens, the longest decode workload, in the
+    launch configuration of a 256-CU GPU: 256 split-KV workgroups of 32 tiles
+    each, hardware workgroups in XCD order.  The first and the last plan range
+    run, so rows near both ends of a 256 MB latent cache are addressed.  The
+    last range's partial (m, l, O) is checked against the oracle over the same
+    tokens: a sequence of the range's rows only has the same key-to-query
+    position differences, which is all its RoPE logits depend on."""
+    L, n_wg = 262144, 256
+    H, r = DSV3.n_heads, DSV3.latent_rank
+    rows = _plan_rows(dev, [L], L, n_wg)
+    ranges = (0, n_wg - 1)
+    mine = rows[np.isin(rows[:, 0], ranges)]
+    assert len(mine) == 2 and (mine[:, 4] >= 0).all(), mine
+    t_first = int(mine[mine[:, 0] == n_wg - 1][0, 2]) * 32
+    assert int(mine[mine[:, 0] == n_wg - 1][0, 3]) * 32 == L
+    hws = [_hw_of_plan(p, n_wg) for p in ranges]
+
+    def groups(name, grid):
+        if "decode_mfma_kernel" in name:
+            assert grid[0] == n_wg, grid
+            return [(hw, 0, 0) for hw in hws]
+        if "merge_kernel" in name:
+            return []  # the other 254 partials are not computed
+        return None
+    inp = make_inputs(DSV3, [L], seed=520)
+    keep = dev.group_filter
+    dev.group_filter = groups
+    os.environ["QKMLA_NUM_WG"] = str(n_wg)
+    try:
+        s = Session(dev, DSV3, inp, host_fill=True)
+        s.decode()
+    finally:
+        os.environ.pop("QKMLA_NUM_WG", None)
+        dev.group_filter = keep
+    assert s.status[0] == 0
+    # slot 0 of plan range n_wg - 1
+    got_lat, got_lse = _slot_partial(np.asarray(s.ws), 2 * (n_wg - 1), H, r, DSV3.rope_dim, 1)
+    tail = make_inputs(DSV3, [L], seed=520)
+    tail.latents[0] = tail.latents[0][t_first:]
+    tail.k_rope_raw[0] = tail.k_rope_raw[0][t_first:]
+    tail.lengths[0] = L - t_first
+    ref = reference(DSV3, tail, True)
+    e_lat = float(np.max(oracle.rowwise_rel_err(got_lat, ref["o_lat"][0])))
+    e_lse = float(np.max(np.abs(got_lse - ref["lse"][0])))
+    ok = e_lat <= TOL["bf16"]["o_lat"] and e_lse <= TOL["bf16"]["lse"]
+    print(f"[{'ok' if ok else 'FAIL'}] bf16 1 x 262144, partial of tokens {t_first}..{L - 1}: "
+          f"o_lat {e_lat:.2e} lse {e_lse:.2e}", flush=True)
+    assert ok, (e_lat, e_lse)
+
+
+def _slot_partial(ws, slot, H, r, dr, B):
+    """(o_lat, lse) of one partial slot of the bf16 decode workspace:
+    m[H], l[H] fp32 in the exp2 domain, then O[H][r] bf16, unnormalised."""
+    nbytes = H * 8 + H * r * 2
+    start = _partials_offset(B, H, r, dr) + slot * nbytes
+    assert start + nbytes <= ws.size
+    sp = ws[start:start + nbytes]
+    m = sp[:4 * H].view(np.float32).astype(np.float64)
+    l_sum = sp[4 * H:8 * H].view(np.float32).astype(np.float64)
+    O = (sp[8 * H:].view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    O = O.reshape(H, r).astype(np.float64)
+    return O / l_sum[:, None], (m + np.log2(l_sum)) * np.log(2.0)
+
+
+@case
+def bf16_ragged_full(dev):
+    """The ragged workload at full size: 64 sequences of 1024..16384 tokens
+    (577k in all), latent rows scaled by log-normal factors up to 1e3, in the
+    launch configuration of a 256-CU GPU.  The first and the last plan range
+    run (about 70 tiles each).  Every sequence such a range covers whole is
+    checked against the oracle; a partial that ends its sequence is checked
+    over its own tokens (the same key-to-query position differences)."""
+    n_wg = 256
+    H, r, dr = DSV3.n_heads, DSV3.latent_rank, DSV3.rope_dim
+    inp = make_inputs(DSV3, (), 1004, row_scale_log10_clip=3.0, ragged=(1024, 16384), batch=64)
+    lens = list(inp.lengths)
+    B = len(lens)
+    rows = _plan_rows(dev, lens, max(lens), n_wg)
+    ranges = (0, n_wg - 1)
+    mine = rows[np.isin(rows[:, 0], ranges)]
+    read = sorted({int(b) for b in mine[:, 1]})
+    whole = sorted({int(b) for b in mine[mine[:, 4] < 0][:, 1]})
+    tails = [(int(p), int(b), int(t0) * 32, int(k)) for p, b, t0, t1, k in mine
+             if k >= 0 and t1 * 32 >= lens[b]]
+    assert tails, mine
+    hws = [_hw_of_plan(p, n_wg) for p in ranges]
+
+    def groups(name, grid):
+        if "decode_mfma_kernel" in name:
+            assert grid[0] == n_wg, grid
+            return [(hw, 0, 0) for hw in hws]
+        if "qprep" in name:
+            return [(b, y, 0) for b in read for y in range(grid[1])]
+        if "merge_kernel" in name:
+            return []  # the other ranges' partials are not computed
+        return None
+    keep = dev.group_filter
+    dev.group_filter = groups
+    os.environ["QKMLA_NUM_WG"] = str(n_wg)
+    try:
+        s = Session(dev, DSV3, inp, host_fill=True, fill_only=set(read))
+        o_lat, lse = s.decode()
+    finally:
+        os.environ.pop("QKMLA_NUM_WG", None)
+        dev.group_filter = keep
+    assert s.status[0] == 0
+    if whole:
+        ref = reference(DSV3, inp, True, batch_ids=whole)
+        for b in whole:
+            e_lat = float(np.max(oracle.rowwise_rel_err(o_lat[b], ref["o_lat"][b])))
+            e_lse = float(np.max(np.abs(lse[b] - ref["lse"][b])))
+            print(f"  whole sequence {b} ({lens[b]} tokens): o_lat {e_lat:.2e} lse {e_lse:.2e}")
+            assert e_lat <= TOL["bf16"]["o_lat"] and e_lse <= TOL["bf16"]["lse"], (b, e_lat, e_lse)
+    ws = np.asarray(s.ws)
+    for p, b, t_first, kind in tails:
+        got_lat, got_lse = _slot_partial(ws, 2 * p + kind, H, r, dr, B)
+        tail = make_inputs(DSV3, (), 1004, row_scale_log10_clip=3.0, ragged=(1024, 16384),
+                           batch=64)
+        tail.latents[b] = tail.latents[b][t_first:]
+        tail.k_rope_raw[b] = tail.k_rope_raw[b][t_first:]
+        tail.lengths[b] = lens[b] - t_first
+        ref = reference(DSV3, tail, True, batch_ids=[b])
+        e_lat = float(np.max(oracle.rowwise_rel_err(got_lat, ref["o_lat"][b])))
+        e_lse = float(np.max(np.abs(got_lse - ref["lse"][b])))
+        print(f"  partial of sequence {b}, tokens {t_first}..{lens[b] - 1}: o_lat {e_lat:.2e} "
+              f"lse {e_lse:.2e}")
+        assert e_lat <= TOL["bf16"]["o_lat"] and e_lse <= TOL["bf16"]["lse"], (b, e_lat, e_lse)
+    print(f"[ok] bf16 ragged 64 sequences ({sum(lens)} tokens), ranges 0 and {n_wg - 1}: "
+          f"{len(whole)} whole, {len(tails)} ending partials", flush=True)
+
+
 @case
 def bf16_plain_overflow(dev):
     """Plain MLA on latents scaled by up to 1e3: unnormalised logits exceed the

@@ -309,7 +309,7 @@ def paged_caches(dev):
     """Paged latent, RoPE and alpha pools behind a block table: fp32 with
     5-row pages and s_q = 2, bf16 with 32-row pages over split segments (also
     with s_q = 2), each also with one sequence whose table entry lies outside
-    the pool."""
+    the pool, and bf16 with 64-row pages (two tiles per page)."""
     run_paged(dev, Shape(6, 3, 20, 12, 4, 10, "f32"), (9, 33, 17), 2, 5, 520,
               "fp32 5-row pages, s_q=2, bad page in sequence 2", bad_seq=2)
     run_paged(dev, DSV3, (70, 40, 2), 1, 32, 521, "bf16 32-row pages over 4 workgroups",
@@ -317,6 +317,9 @@ def paged_caches(dev):
     run_paged(dev, DSV3, (70, 40, 2), 1, 32, 522, "bf16 32-row pages, bad page in sequence 0",
               n_wg=3, heads=MERGE_HEADS, bad_seq=0)
     run_paged(dev, DSV3, (45, 33), 2, 32, 523, "bf16 32-row pages, s_q=2", n_wg=3,
+              heads=MERGE_HEADS)
+    run_paged(dev, DSV3, (150, 64, 97), 1, 64, 524,
+              "bf16 64-row pages (two tiles per page) over 5 workgroups", n_wg=5,
               heads=MERGE_HEADS)
 
 

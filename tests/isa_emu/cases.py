@@ -207,10 +207,15 @@ def run_multi(dev, shape, lens, s_q, seed, label, n_wg=None, heads=None):
 def multi_query(dev):
     """s_q query rows per sequence (causal): fp32 layer with s_q = 2, bf16
     layer with s_q = 3 over split segments, including a sequence shorter than
-    s_q whose first row has an empty prefix."""
+    s_q whose first row has an empty prefix, and s_q = 8 rows of a 1000-token
+    sequence split over 256 workgroups."""
     run_multi(dev, Shape(6, 3, 20, 12, 4, 10, "f32"), (9, 33), 2, 510, "fp32 s_q=2")
     run_multi(dev, DSV3, (70, 40, 2), 3, 511, "bf16 s_q=3 (one row with an empty prefix)",
               n_wg=5, heads=MERGE_HEADS)
+    # the GPU test's s_q = 8 case in a 256-CU launch: 8 rows of about 31 tiles
+    # over 256 workgroups, so most workgroups stream one tile of one row
+    run_multi(dev, DSV3, (1000,), 8, 512, "bf16 s_q=8 over 256 workgroups", n_wg=256,
+              heads=MERGE_HEADS)
 
 
 class CPages(ctypes.Structure):

@@ -341,7 +341,8 @@ class CTrainGrads(ctypes.Structure):
     _fields_ = [("d_" + n, ctypes.c_void_p) for n in TRAIN_IN]
 
 
-def run_train(dev, shape, B, T, seed, label, qk_norm=True, forward_only=False, tol=None):
+def run_train(dev, shape, B, T, seed, label, qk_norm=True, forward_only=False, tol=None,
+              rows=None, heads=None):
     """Training forward and backward through the C ABI against the oracle's
     forward and autograd backward.  All arithmetic on the device is fp32 (bf16
     storage only rounds the inputs, which the oracle sees rounded), so o and
@@ -385,8 +386,12 @@ def run_train(dev, shape, B, T, seed, label, qk_norm=True, forward_only=False, t
     tol = tol or TRAIN_TOL
     if forward_only:
         ref = train_reference(inp, qk_norm=qk_norm, eps=1e-6, base=10000.0)
-        eo = float(np.max(oracle.rowwise_rel_err(o.reshape(-1, dvh), ref["o"].reshape(-1, dvh))))
-        el = float(np.max(np.abs(lse - ref["lse"])))
+        # rows, heads: compare only these token rows and heads (a filtered launch)
+        sel = (slice(None), slice(None) if rows is None else list(rows))
+        hs = slice(None) if heads is None else list(heads)
+        go, ro = o[sel][:, :, hs], np.asarray(ref["o"])[sel][:, :, hs]
+        eo = float(np.max(oracle.rowwise_rel_err(go.reshape(-1, dvh), ro.reshape(-1, dvh))))
+        el = float(np.max(np.abs(lse[sel][:, :, hs] - np.asarray(ref["lse"])[sel][:, :, hs])))
         ok = eo <= tol["o"] and el <= tol["lse"]
         print(f"[{'ok' if ok else 'FAIL'}] {label}: o {eo:.2e} (bound {tol['o']}) lse {el:.2e} "
               f"(bound {tol['lse']})", flush=True)
@@ -792,6 +797,30 @@ def bf16_headline_sequence(dev):
     compare(DSV3, out, o_lat, lse, reference(DSV3, inp, True, batch_ids=[0]), [0],
             list(MERGE_HEADS), "bf16 16 x 4096, sequence 0 over its 16 workgroups and merge")
     assert s.status[0] == 0
+
+
+@case
+def train_mfma_long(dev):
+    """The MFMA training forward at 1024 tokens (the training measurement's
+    length): the last query block of KV group 0 (8 rows) streams every key
+    tile, so the key and value rows at the far end of the sequence are
+    addressed; its rows and heads are checked against the oracle.  About 15
+    minutes of CPU (the projections and norms run in full), so it is run on
+    demand rather than in the test suite."""
+    T = 1024
+
+    def groups(name, grid):
+        if "flash_fwd_kernel" in name:
+            return [(grid[0] - 1, 0, 0)]
+        return None
+    keep = dev.group_filter
+    dev.group_filter = groups
+    try:
+        run_train(dev, DSV3, 1, T, 614, "train MFMA forward, 1024 tokens, last query block",
+                  forward_only=True, tol=dict(o=2e-2, lse=5e-2),
+                  rows=range(T - 8, T), heads=range(16))  # 8 query rows per workgroup
+    finally:
+        dev.group_filter = keep
 
 
 @case

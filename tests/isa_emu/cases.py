@@ -690,27 +690,23 @@ def _slot_partial(ws, slot, H, r, dr, B):
     return O / l_sum[:, None], (m + np.log2(l_sum)) * np.log(2.0)
 
 
-@case
-def bf16_ragged_full(dev):
-    """The ragged workload at full size: 64 sequences of 1024..16384 tokens
-    (577k in all), latent rows scaled by log-normal factors up to 1e3, in the
-    launch configuration of a 256-CU GPU.  The first and the last plan range
-    run (about 70 tiles each).  Every sequence such a range covers whole is
-    checked against the oracle; a partial that ends its sequence is checked
-    over its own tokens (the same key-to-query position differences)."""
-    n_wg = 256
+def _run_plan_ranges(dev, inp, ranges, n_wg, label, regen, hold_last=False):
+    """Run the split-KV plan ranges `ranges` of a decode in the launch
+    configuration of a GPU with n_wg CUs (hardware workgroups in XCD order),
+    with the q-prep of the sequences they read.  Every sequence a range covers
+    whole is checked against the oracle; a partial that ends its sequence is
+    checked over its own tokens, which keep their key-to-query position
+    differences.  regen() draws the same inputs again (for the sliced copy)."""
     H, r, dr = DSV3.n_heads, DSV3.latent_rank, DSV3.rope_dim
-    inp = make_inputs(DSV3, (), 1004, row_scale_log10_clip=3.0, ragged=(1024, 16384), batch=64)
     lens = list(inp.lengths)
     B = len(lens)
     rows = _plan_rows(dev, lens, max(lens), n_wg)
-    ranges = (0, n_wg - 1)
     mine = rows[np.isin(rows[:, 0], ranges)]
     read = sorted({int(b) for b in mine[:, 1]})
     whole = sorted({int(b) for b in mine[mine[:, 4] < 0][:, 1]})
     tails = [(int(p), int(b), int(t0) * 32, int(k)) for p, b, t0, t1, k in mine
              if k >= 0 and t1 * 32 >= lens[b]]
-    assert tails, mine
+    assert tails or whole, mine
     hws = [_hw_of_plan(p, n_wg) for p in ranges]
 
     def groups(name, grid):
@@ -726,7 +722,7 @@ def bf16_ragged_full(dev):
     dev.group_filter = groups
     os.environ["QKMLA_NUM_WG"] = str(n_wg)
     try:
-        s = Session(dev, DSV3, inp, host_fill=True, fill_only=set(read))
+        s = Session(dev, DSV3, inp, host_fill=True, hold_last=hold_last, fill_only=set(read))
         o_lat, lse = s.decode()
     finally:
         os.environ.pop("QKMLA_NUM_WG", None)
@@ -742,8 +738,7 @@ def bf16_ragged_full(dev):
     ws = np.asarray(s.ws)
     for p, b, t_first, kind in tails:
         got_lat, got_lse = _slot_partial(ws, 2 * p + kind, H, r, dr, B)
-        tail = make_inputs(DSV3, (), 1004, row_scale_log10_clip=3.0, ragged=(1024, 16384),
-                           batch=64)
+        tail = regen()
         tail.latents[b] = tail.latents[b][t_first:]
         tail.k_rope_raw[b] = tail.k_rope_raw[b][t_first:]
         tail.lengths[b] = lens[b] - t_first
@@ -753,74 +748,32 @@ def bf16_ragged_full(dev):
         print(f"  partial of sequence {b}, tokens {t_first}..{lens[b] - 1}: o_lat {e_lat:.2e} "
               f"lse {e_lse:.2e}")
         assert e_lat <= TOL["bf16"]["o_lat"] and e_lse <= TOL["bf16"]["lse"], (b, e_lat, e_lse)
-    print(f"[ok] bf16 ragged 64 sequences ({sum(lens)} tokens), ranges 0 and {n_wg - 1}: "
-          f"{len(whole)} whole, {len(tails)} ending partials", flush=True)
+    print(f"[ok] {label}: ranges {list(ranges)}, {len(whole)} whole sequences, {len(tails)} "
+          f"ending partials", flush=True)
 
 
 @case
-def bf16_headline_sequence(dev):
-    """The 16 x 4096 workload in the launch configuration of a 256-CU GPU:
-    every one of sequence 0's 16 split-KV workgroups (8 tiles each, hardware
-    workgroups in XCD order), its q-prep, and the merge of its 16 partials,
-    checked whole against the oracle."""
-    B, L, n_wg = 16, 4096, 256
-    lens = [L] * B
-    rows = _plan_rows(dev, lens, L, n_wg)
-    mine = rows[rows[:, 1] == 0]
-    ranges = sorted({int(p) for p in mine[:, 0]})
-    assert len(ranges) == 16 and (mine[:, 4] >= 0).all(), mine
-    assert not (rows[np.isin(rows[:, 0], ranges)][:, 1] != 0).any()
-    hws = [_hw_of_plan(p, n_wg) for p in ranges]
-
-    def groups(name, grid):
-        if "decode_mfma_kernel" in name:
-            assert grid[0] == n_wg, grid
-            return [(hw, 0, 0) for hw in hws]
-        if "qprep" in name:
-            return [(0, y, 0) for y in range(grid[1])]
-        if "merge_kernel" in name:
-            return [(0, y, z) for y in MERGE_HEADS for z in range(grid[2])]
-        if "out_proj" in name:
-            return [(0, y, z) for y in range(grid[1]) for z in range(grid[2])]
-        return None
-    inp = make_inputs(DSV3, lens, seed=530)
-    keep = dev.group_filter
-    dev.group_filter = groups
-    os.environ["QKMLA_NUM_WG"] = str(n_wg)
-    try:
-        s = Session(dev, DSV3, inp, host_fill=True, fill_only={0})
-        o_lat, lse = s.decode()
-        out = s.out_proj()
-    finally:
-        os.environ.pop("QKMLA_NUM_WG", None)
-        dev.group_filter = keep
-    compare(DSV3, out, o_lat, lse, reference(DSV3, inp, True, batch_ids=[0]), [0],
-            list(MERGE_HEADS), "bf16 16 x 4096, sequence 0 over its 16 workgroups and merge")
-    assert s.status[0] == 0
+def bf16_ragged_full(dev):
+    """The ragged workload at full size: 64 sequences of 1024..16384 tokens
+    (577k in all), latent rows scaled by log-normal factors up to 1e3, in the
+    launch configuration of a 256-CU GPU.  The first and the last plan range
+    run (about 70 tiles each)."""
+    def regen():
+        return make_inputs(DSV3, (), 1004, row_scale_log10_clip=3.0, ragged=(1024, 16384),
+                           batch=64)
+    _run_plan_ranges(dev, regen(), (0, 255), 256, "bf16 ragged 64 sequences", regen)
 
 
 @case
-def train_mfma_long(dev):
-    """The MFMA training forward at 1024 tokens (the training measurement's
-    length): the last query block of KV group 0 (8 rows) streams every key
-    tile, so the key and value rows at the far end of the sequence are
-    addressed; its rows and heads are checked against the oracle.  About 15
-    minutes of CPU (the projections and norms run in full), so it is run on
-    demand rather than in the test suite."""
-    T = 1024
-
-    def groups(name, grid):
-        if "flash_fwd_kernel" in name:
-            return [(grid[0] - 1, 0, 0)]
-        return None
-    keep = dev.group_filter
-    dev.group_filter = groups
-    try:
-        run_train(dev, DSV3, 1, T, 614, "train MFMA forward, 1024 tokens, last query block",
-                  forward_only=True, tol=dict(o=2e-2, lse=5e-2),
-                  rows=range(T - 8, T), heads=range(16))  # 8 query rows per workgroup
-    finally:
-        dev.group_filter = keep
+def bf16_32k_step(dev):
+    """The 4 x 32768 workload's step in the launch configuration of a 256-CU
+    GPU: each sequence's last token is appended by the library (at row
+    32767), then the first plan range and the last ranges of sequences 0 and
+    3 run (16 tiles each)."""
+    def regen():
+        return make_inputs(DSV3, (32768,) * 4, 1002)
+    _run_plan_ranges(dev, regen(), (0, 63, 255), 256, "bf16 4 x 32768 with the step's append",
+                     regen, hold_last=True)
 
 
 @case

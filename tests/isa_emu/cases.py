@@ -777,6 +777,72 @@ def bf16_32k_step(dev):
 
 
 @case
+def bf16_headline_sequence(dev):
+    """The 16 x 4096 workload in the launch configuration of a 256-CU GPU:
+    every one of sequence 0's 16 split-KV workgroups (8 tiles each, hardware
+    workgroups in XCD order), its q-prep, and the merge of its 16 partials,
+    checked whole against the oracle."""
+    B, L, n_wg = 16, 4096, 256
+    lens = [L] * B
+    rows = _plan_rows(dev, lens, L, n_wg)
+    mine = rows[rows[:, 1] == 0]
+    ranges = sorted({int(p) for p in mine[:, 0]})
+    assert len(ranges) == 16 and (mine[:, 4] >= 0).all(), mine
+    assert not (rows[np.isin(rows[:, 0], ranges)][:, 1] != 0).any()
+    hws = [_hw_of_plan(p, n_wg) for p in ranges]
+
+    def groups(name, grid):
+        if "decode_mfma_kernel" in name:
+            assert grid[0] == n_wg, grid
+            return [(hw, 0, 0) for hw in hws]
+        if "qprep" in name:
+            return [(0, y, 0) for y in range(grid[1])]
+        if "merge_kernel" in name:
+            return [(0, y, z) for y in MERGE_HEADS for z in range(grid[2])]
+        if "out_proj" in name:
+            return [(0, y, z) for y in range(grid[1]) for z in range(grid[2])]
+        return None
+    inp = make_inputs(DSV3, lens, seed=530)
+    keep = dev.group_filter
+    dev.group_filter = groups
+    os.environ["QKMLA_NUM_WG"] = str(n_wg)
+    try:
+        s = Session(dev, DSV3, inp, host_fill=True, fill_only={0})
+        o_lat, lse = s.decode()
+        out = s.out_proj()
+    finally:
+        os.environ.pop("QKMLA_NUM_WG", None)
+        dev.group_filter = keep
+    compare(DSV3, out, o_lat, lse, reference(DSV3, inp, True, batch_ids=[0]), [0],
+            list(MERGE_HEADS), "bf16 16 x 4096, sequence 0 over its 16 workgroups and merge")
+    assert s.status[0] == 0
+
+
+@case
+def train_mfma_long(dev):
+    """The MFMA training forward at 1024 tokens (the training measurement's
+    length): the last query block of KV group 0 (8 rows) streams every key
+    tile, so the key and value rows at the far end of the sequence are
+    addressed; its rows and heads are checked against the oracle.  About 15
+    minutes of CPU (the projections and norms run in full), so it is run on
+    demand rather than in the test suite."""
+    T = 1024
+
+    def groups(name, grid):
+        if "flash_fwd_kernel" in name:
+            return [(grid[0] - 1, 0, 0)]
+        return None
+    keep = dev.group_filter
+    dev.group_filter = groups
+    try:
+        run_train(dev, DSV3, 1, T, 614, "train MFMA forward, 1024 tokens, last query block",
+                  forward_only=True, tol=dict(o=2e-2, lse=5e-2),
+                  rows=range(T - 8, T), heads=range(16))  # 8 query rows per workgroup
+    finally:
+        dev.group_filter = keep
+
+
+@case
 def bf16_plain_overflow(dev):
     """Plain MLA on latents scaled by up to 1e3: unnormalised logits exceed the
     first tile's reference by far more than 2^64, so segments are streamed

@@ -137,6 +137,67 @@ def append_ref(latent: np.ndarray, k_rope_raw: np.ndarray, positions: np.ndarray
 # Explicit form: the oracle's answer.
 # ---------------------------------------------------------------------------
 
+def _group_logits(q_hat, qr_hat, c, k_rope_hat, w_uk_g, gamma_k, eps, tau, qk_norm, chunk):
+    """tau (q^_h . k^_{t,g} + q^R_h . k^R_t) for the heads of one group over
+    every token t of one sequence, the keys materialised chunk by chunk
+    ([TS] Problem Statement: k_{t,g} = c_t W^K_g, normalised after the
+    up-projection).  Returns [heads][L]."""
+    L = c.shape[0]
+    logits = np.empty((q_hat.shape[0], L))
+    wk = np.asarray(w_uk_g, dtype=F64)
+    for t0 in range(0, L, chunk):
+        t1 = min(L, t0 + chunk)
+        k = c[t0:t1] @ wk                                 # materialised keys [n][d_c]
+        k_hat = rmsnorm(k, gamma_k, eps) if qk_norm else k
+        logits[:, t0:t1] = tau * (q_hat @ k_hat.T + qr_hat @ k_rope_hat[t0:t1].T)
+    return logits
+
+
+def _rope_keys(k_rope_raw_b, gamma_k_rope, eps, base, qk_norm):
+    """Stored RoPE keys of one sequence: RMS-normalised with gamma_k_rope (QK
+    norm only), then rotated by their cache row ([TS] Methodology, Blockwise
+    Normalization)."""
+    kr = np.asarray(k_rope_raw_b, dtype=F64)
+    pos = np.arange(kr.shape[0], dtype=F64)
+    if qk_norm:
+        return rope(rmsnorm(kr, gamma_k_rope, eps), pos, base)
+    return rope(kr, pos, base)
+
+
+def _queries(qc, qr, L, gamma_q, gamma_q_rope, eps, base, qk_norm):
+    """Content and RoPE queries of some heads of one sequence of length L:
+    RMS-normalised (QK norm only); the RoPE query is rotated to position L-1."""
+    if qk_norm:
+        q_hat = rmsnorm(qc, gamma_q, eps)
+        qr_hat = rope(rmsnorm(qr, gamma_q_rope, eps), L - 1, base)
+    else:
+        q_hat = qc
+        qr_hat = rope(qr, L - 1, base)
+    return q_hat, qr_hat
+
+
+def explicit_logits(q_c, q_rope, latent, k_rope_raw, w_uk, gamma_q, gamma_k, gamma_q_rope,
+                    gamma_k_rope, b: int, g: int, *, eps: float = 1e-6,
+                    tau: Optional[float] = None, base: float = 10000.0, qk_norm: bool = True,
+                    chunk: int = 65536):
+    """The natural-log logits l_{h,t} that ``explicit_decode`` feeds its
+    softmax, for the heads of group g of sequence b: [H/G][L_b].  latent and
+    k_rope_raw are that sequence's [L_b][r] and [L_b][d_r] arrays."""
+    q_c = np.asarray(q_c, dtype=F64)
+    q_rope = np.asarray(q_rope, dtype=F64)
+    _, H, dc = q_c.shape
+    G = w_uk.shape[0]
+    dr = q_rope.shape[-1]
+    if tau is None:
+        tau = default_tau(dc, dr)
+    c = np.asarray(latent, dtype=F64)
+    heads = [h for h in range(H) if group_of_head(h, H, G) == g]
+    k_rope_hat = _rope_keys(k_rope_raw, gamma_k_rope, eps, base, qk_norm)
+    q_hat, qr_hat = _queries(q_c[b, heads], q_rope[b, heads], c.shape[0], gamma_q, gamma_q_rope,
+                             eps, base, qk_norm)
+    return _group_logits(q_hat, qr_hat, c, k_rope_hat, w_uk[g], gamma_k, eps, tau, qk_norm, chunk)
+
+
 def explicit_decode(q_c, q_rope, latents: Sequence[np.ndarray], k_rope_raw: Sequence[np.ndarray],
                     w_uk, w_uv, gamma_q, gamma_k, gamma_q_rope, gamma_k_rope, *,
                     eps: float = 1e-6, tau: Optional[float] = None, base: float = 10000.0,
@@ -176,29 +237,13 @@ def explicit_decode(q_c, q_rope, latents: Sequence[np.ndarray], k_rope_raw: Sequ
         L = c.shape[0]
         if L == 0:
             continue
-        pos = np.arange(L, dtype=F64)
-        kr = np.asarray(k_rope_raw[b], dtype=F64)
-        if qk_norm:
-            k_rope_hat = rope(rmsnorm(kr, gamma_k_rope, eps), pos, base)
-        else:
-            k_rope_hat = rope(kr, pos, base)
+        k_rope_hat = _rope_keys(k_rope_raw[b], gamma_k_rope, eps, base, qk_norm)
         for g in gs:
             heads = [h for h in range(H) if group_of_head(h, H, G) == g]
-            qc = q_c[b, heads]                               # [hpg][d_c]
-            qr = q_rope[b, heads]
-            if qk_norm:
-                q_hat = rmsnorm(qc, gamma_q, eps)
-                qr_hat = rope(rmsnorm(qr, gamma_q_rope, eps), L - 1, base)
-            else:
-                q_hat = qc
-                qr_hat = rope(qr, L - 1, base)
-            logits = np.empty((len(heads), L))
-            wk = np.asarray(w_uk[g], dtype=F64)
-            for t0 in range(0, L, chunk):
-                t1 = min(L, t0 + chunk)
-                k = c[t0:t1] @ wk                             # materialised keys [n][d_c]
-                k_hat = rmsnorm(k, gamma_k, eps) if qk_norm else k
-                logits[:, t0:t1] = tau * (q_hat @ k_hat.T + qr_hat @ k_rope_hat[t0:t1].T)
+            q_hat, qr_hat = _queries(q_c[b, heads], q_rope[b, heads], L, gamma_q, gamma_q_rope,
+                                     eps, base, qk_norm)
+            logits = _group_logits(q_hat, qr_hat, c, k_rope_hat, w_uk[g], gamma_k, eps, tau,
+                                   qk_norm, chunk)
             p, lse_g = _softmax(logits)
             v_lat = p @ c                                     # [hpg][r]
             o_lat[b, heads] = v_lat

@@ -12,8 +12,8 @@ import torch
 import torch.nn.functional as F
 
 from oracle import (absorb_weights_ref, absorbed_decode, append_ref, default_tau,
-                    explicit_decode, explicit_decode_multi, group_of_head, plain_mla_decode, rms,
-                    rmsnorm, rope, rope_inv_freq)
+                    explicit_decode, explicit_decode_multi, explicit_logits, group_of_head,
+                    plain_mla_decode, rms, rmsnorm, rope, rope_inv_freq)
 from oracle.qkmla_oracle import _softmax
 from mla_latent_decode_amd.inputs import (DSV3, TINY, Shape, make_inputs, multi_query_rows,
                                           workload_inputs)
@@ -118,6 +118,44 @@ def test_attention_matches_torch_sdpa():
                                                torch.cat([k, kr], -1)[None, None],
                                                v[None, None], scale=tau)[0, 0, 0].numpy()
             assert _rel(ref["o"][b, h], o) < 1e-12
+
+
+def test_token_chunk_loop_matches_one_chunk():
+    """The keys are materialised chunk by chunk (the loop only runs more than
+    once past 65536 tokens).  Chunks of 7 over 50 and 23 tokens (several full
+    chunks and a ragged tail) must give the one-chunk result; in QK-norm mode
+    both must also equal the absorbed form, which has no chunk loop."""
+    inp = make_inputs(Shape(8, 2, 24, 12, 6, 10, "f32"), (50, 23), seed=71)
+    for qk_norm in (True, False):
+        one = explicit_decode(*_decode_args(inp), qk_norm=qk_norm)
+        for chunk in (7, 16, 49, 50):
+            many = explicit_decode(*_decode_args(inp), qk_norm=qk_norm, chunk=chunk)
+            for k in ("o", "o_lat", "lse"):
+                assert _rel(many[k], one[k]) < 1e-13, (qk_norm, chunk, k)
+    ab = absorbed_decode(*_decode_args(inp))
+    many = explicit_decode(*_decode_args(inp), chunk=7)
+    assert _rel(many["o"], ab["o"]) < 1e-12 and _rel(many["o_lat"], ab["o_lat"]) < 1e-12
+
+
+def test_explicit_logits_are_the_softmax_inputs():
+    """explicit_logits (what the GPU tests use to state conditions on the
+    inputs) gives logits whose log-sum-exp is the oracle's lse and whose
+    softmax-weighted latents are its o_lat; with chunk=5 the same."""
+    inp = make_inputs(Shape(8, 4, 24, 12, 6, 10, "f32"), (19, 30), seed=72)
+    H, G = 8, 4
+    for qk_norm, b in ((True, 0), (True, 1), (False, 0), (False, 1)):
+        ref = explicit_decode(*_decode_args(inp), qk_norm=qk_norm)
+        for g in range(G):
+            heads = [h for h in range(H) if group_of_head(h, H, G) == g]
+            for chunk in (65536, 5):
+                lg = explicit_logits(inp.q_c, inp.q_rope, inp.latents[b], inp.k_rope_raw[b],
+                                     inp.w_uk, inp.gamma_q, inp.gamma_k, inp.gamma_q_rope,
+                                     inp.gamma_k_rope, b, g, qk_norm=qk_norm, chunk=chunk)
+                assert lg.shape == (len(heads), inp.lengths[b])
+                lse = scipy.special.logsumexp(lg, axis=-1)
+                assert np.max(np.abs(lse - ref["lse"][b, heads])) < 1e-12
+                p = scipy.special.softmax(lg, axis=-1)
+                assert _rel(p @ inp.latents[b].astype(np.float64), ref["o_lat"][b, heads]) < 1e-12
 
 
 # --- several query rows per sequence (causal) --------------------------------

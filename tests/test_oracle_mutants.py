@@ -36,12 +36,17 @@ DECODE_MUTANTS = [
      "return h % n_groups"),
     ("RoPE query at position L", "qr_hat = rope(rmsnorm(qr, gamma_q_rope, eps), L - 1, base)",
      "qr_hat = rope(rmsnorm(qr, gamma_q_rope, eps), L, base)"),
+    ("plain-MLA RoPE query at position 0", "qr_hat = rope(qr, L - 1, base)",
+     "qr_hat = rope(qr, 0, base)"),
     ("RoPE term dropped", "tau * (q_hat @ k_hat.T + qr_hat @ k_rope_hat[t0:t1].T)",
      "tau * (q_hat @ k_hat.T)"),
     ("softmax scale dropped", "tau * (q_hat @ k_hat.T + qr_hat @ k_rope_hat[t0:t1].T)",
      "(q_hat @ k_hat.T + qr_hat @ k_rope_hat[t0:t1].T)"),
-    ("RoPE key not normalised", "k_rope_hat = rope(rmsnorm(kr, gamma_k_rope, eps), pos, base)",
-     "k_rope_hat = rope(kr, pos, base)"),
+    ("RoPE key not normalised", "return rope(rmsnorm(kr, gamma_k_rope, eps), pos, base)",
+     "return rope(kr, pos, base)"),
+    ("token chunk one row short", "t1 = min(L, t0 + chunk)", "t1 = min(L, t0 + chunk - 1)"),
+    ("every chunk takes the first chunk's RoPE keys",
+     "qr_hat @ k_rope_hat[t0:t1].T)", "qr_hat @ k_rope_hat[0:t1 - t0].T)"),
     ("key normalised with the query gamma", "k_hat = rmsnorm(k, gamma_k, eps) if qk_norm else k",
      "k_hat = rmsnorm(k, gamma_q, eps) if qk_norm else k"),
     ("log-sum-exp without its shift", "return e / s, (m + np.log(s))[..., 0]",

@@ -258,13 +258,13 @@ def _traffic(workload_name):
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
 
 
-def pmc_workload(steps=5):
+def pmc_workload(steps=5, cid=1):
     """What the two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) count:
     `steps` headline decode steps over rotated cache copies, then three plain
     copies of COPY_BYTES (torch's copy kernel) to calibrate the counters.
     Prints one line naming the workload; no timing."""
     import torch
-    b = Bench(1)
+    b = Bench(cid)
     for _ in range(steps):
         b.step()
     torch.cuda.synchronize()
@@ -670,7 +670,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     if args.pmc_workload:
-        pmc_workload()
+        pmc_workload(cid=args.workload)
         return
     if args.part == "next":
         try:

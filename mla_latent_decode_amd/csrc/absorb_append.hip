@@ -44,66 +44,70 @@ hipError_t launch_absorb(const Cfg& c, const float* w_uk, const float* gq, const
 // Copy the latent rows of tokens tok0..tok0+ntok-1 and write their RoPE keys,
 // RMS-normalised on their own (QK-norm) and rotated by the cache row.  A
 // sequence whose rows would fall outside the cache gets no writes and sets
-// QKMLA_DEV_BAD_POSITION.  Called by every thread of the block; rsum: LDS
-// scratch of ntok floats.
+// QKMLA_DEV_BAD_POSITION.  Called by every thread of the block: each
+// wavefront takes whole tokens (wave w: tokens w, w + waves, ...), so no
+// token waits on a block barrier; a bf16 row of r = 512 is one 16-byte piece
+// per lane.
 template <typename T>
 __device__ void copy_rows_and_rope(int tok0, int ntok, int batch, int n_new,
                                    const T* __restrict__ c_new, const T* __restrict__ kr_new,
                                    const float* __restrict__ gkr,
                                    const int32_t* __restrict__ positions, const Paging pg,
                                    T* __restrict__ lat, T* __restrict__ rope, int32_t* status,
-                                   int r, int dr, float eps, float base, int qk_norm,
-                                   float* rsum) {
+                                   int r, int dr, float eps, const RopeFreq& rf, int qk_norm) {
   const int T_total = batch * n_new;
-  const int tid = threadIdx.x;
-  for (int k = 0; k < ntok; ++k) {
-    int tok = tok0 + k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  // 16-byte pieces of a latent row, when rows are whole pieces and aligned
+  const bool vec = (r * sizeof(T)) % 16 == 0 && ((uintptr_t)c_new % 16) == 0 &&
+                   ((uintptr_t)lat % 16) == 0;
+  const int n16 = (int)(r * sizeof(T) / 16);
+  for (int k = wave; k < ntok; k += nwaves) {
+    const int tok = tok0 + k;
     if (tok >= T_total) break;
-    int b = tok / n_new, i = tok % n_new;
-    int pos0 = positions[b];
-    bool bad = pos0 < 0 || (int64_t)pos0 + n_new > pg.capacity();
-    if (bad) {
-      if (tid == 0 && i == 0 && status) atomicOr(status, QKMLA_DEV_BAD_POSITION);
+    const int b = tok / n_new, i = tok % n_new;
+    const int pos0 = positions[b];
+    if (pos0 < 0 || (int64_t)pos0 + n_new > pg.capacity()) {
+      if (lane == 0 && i == 0 && status) atomicOr(status, QKMLA_DEV_BAD_POSITION);
       continue;
     }
-    int row = pos0 + i;
+    const int row = pos0 + i;
     const int64_t prow = pg.phys_row(b, row);
     if (prow < 0) {
-      if (tid == 0 && status) atomicOr(status, QKMLA_DEV_BAD_PAGE);
+      if (lane == 0 && status) atomicOr(status, QKMLA_DEV_BAD_PAGE);
       continue;
     }
-    const T* src = c_new + (size_t)tok * r;
-    T* dst = lat + (size_t)prow * r;
-    for (int e = tid; e < r; e += blockDim.x) dst[e] = src[e];
+    if (vec) {
+      const uint4* src = (const uint4*)(c_new + (size_t)tok * r);
+      uint4* dst = (uint4*)(lat + (size_t)prow * r);
+      for (int e = lane; e < n16; e += 64) dst[e] = src[e];
+    } else {
+      const T* src = c_new + (size_t)tok * r;
+      T* dst = lat + (size_t)prow * r;
+      for (int e = lane; e < r; e += 64) dst[e] = src[e];
+    }
     // RoPE key: optional RMSNorm over d_r, then rotate pairs by row position.
     const T* ks = kr_new + (size_t)tok * dr;
     float scale = 1.f;
     if (qk_norm) {
-      if (tid < 64) {
-        float acc = 0.f;
-        for (int e = tid; e < dr; e += 64) {
-          float v = Elem<T>::load(ks, e);
-          acc += v * v;
-        }
-        acc = wave_sum(acc);
-        if (tid == 0) rsum[k] = acc;
+      float acc = 0.f;
+      for (int e = lane; e < dr; e += 64) {
+        const float v = Elem<T>::load(ks, e);
+        acc += v * v;
       }
-      __syncthreads();
-      scale = 1.0f / sqrtf(rsum[k] / (float)dr + eps);
+      scale = 1.0f / sqrtf(wave_sum(acc) / (float)dr + eps);
     }
     T* rdst = rope + (size_t)prow * dr;
-    for (int pi = tid; pi < dr / 2; pi += blockDim.x) {
+    for (int pi = lane; pi < dr / 2; pi += 64) {
       float x0 = Elem<T>::load(ks, 2 * pi), x1 = Elem<T>::load(ks, 2 * pi + 1);
       if (qk_norm) {
         x0 = x0 * scale * gkr[2 * pi];
         x1 = x1 * scale * gkr[2 * pi + 1];
       }
       float cs_, sn_;
-      rope_cos_sin(row, pi, dr, base, &cs_, &sn_);
+      rope_cos_sin_freq(row, rf.f[pi], &cs_, &sn_);
       Elem<T>::store(rdst, 2 * pi, x0 * cs_ - x1 * sn_);
       Elem<T>::store(rdst, 2 * pi + 1, x0 * sn_ + x1 * cs_);
     }
-    __syncthreads();
   }
 }
 
@@ -120,10 +124,9 @@ __global__ __launch_bounds__(256) void append_kernel(
     const float* __restrict__ w_uk, const float* __restrict__ gkr,
     const int32_t* __restrict__ positions, const Paging pg, T* __restrict__ lat,
     T* __restrict__ rope, float* __restrict__ alpha, int32_t* status, int G, int r, int dc, int dr,
-    float eps, float base, int qk_norm) {
+    float eps, const RopeFreq rf, int qk_norm) {
   __shared__ float cs[kAppendTok * kMaxR];
   __shared__ float ksq[kAppendTok];
-  __shared__ float rsum[kAppendTok];
   const int T_total = batch * n_new;
   const int tok0 = blockIdx.x * kAppendTok;
   const int duty = blockIdx.y;
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(256) void append_kernel(
 
   if (copy_duty) {
     copy_rows_and_rope<T>(tok0, kAppendTok, batch, n_new, c_new, kr_new, gkr, positions, pg,
-                          lat, rope, status, r, dr, eps, base, qk_norm, rsum);
+                          lat, rope, status, r, dr, eps, rf, qk_norm);
     return;
   }
 
@@ -204,17 +207,16 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(
     const float* __restrict__ w_uk, const float* __restrict__ gkr,
     const int32_t* __restrict__ positions, const Paging pg, uint16_t* __restrict__ lat,
     uint16_t* __restrict__ rope, float* __restrict__ alpha, int32_t* status, int G, int r,
-    int dc, int dr, float eps, float base, int qk_norm) {
+    int dc, int dr, float eps, const RopeFreq rf, int qk_norm) {
   __shared__ __attribute__((aligned(16))) uint16_t w_hi[kAlphaChunk][kAlphaMaxDc];
   __shared__ __attribute__((aligned(16))) uint16_t w_lo[kAlphaChunk][kAlphaMaxDc];
   __shared__ float ssq[4][kAlphaTok];
-  __shared__ float rsum[kAlphaTok];
   const int T_total = batch * n_new;
   const int tok0 = blockIdx.x * kAlphaTok;
   const int duty = blockIdx.y;
   if (qk_norm ? duty == G : duty == 0) {
     copy_rows_and_rope<uint16_t>(tok0, kAlphaTok, batch, n_new, c_new, kr_new, gkr, positions,
-                                 pg, lat, rope, status, r, dr, eps, base, qk_norm, rsum);
+                                 pg, lat, rope, status, r, dr, eps, rf, qk_norm);
     return;
   }
   const int g = duty;
@@ -291,11 +293,133 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(
   }
 }
 
+// Few new tokens (the decode step's append): alpha^k on VALU with every
+// weight load in flight at once.  One block of 1024 threads per (chunk of up
+// to kStepTok tokens, group g).  Thread (row group rg, column quad c4) owns
+// columns 4 c4..4 c4+3 of W^UK_g (fp32, 16-byte loads) and rows rg, rg + RG,
+// ... (RG = 1024 / (d_c / 4) row groups); it accumulates k over its rows for
+// every token of the chunk, the two row groups of a wavefront meet by a
+// cross-lane add and the wavefronts in LDS, then k^2 is summed over d_c.
+// The copy of the latent rows and the RoPE key is the extra duty y = G of
+// the same launch.  W^UK_g (fp32 [r][d_c]) is read once per chunk: for the
+// 128-dim groups of the DeepSeek-V3-like layer, 256 KB per block, one round
+// of loads.
+constexpr int kStepTok = 4;
+constexpr int kStepThreads = 1024;
+constexpr int kStepMaxDc = 256;
+constexpr int kStepMaxRowsPerThread = 16;  // r / RG
+
+template <typename T>
+__global__ __launch_bounds__(kStepThreads) void append_step_kernel(
+    int batch, int n_new, const T* __restrict__ c_new, const T* __restrict__ kr_new,
+    const float* __restrict__ w_uk, const float* __restrict__ gkr,
+    const int32_t* __restrict__ positions, const Paging pg, T* __restrict__ lat,
+    T* __restrict__ rope, float* __restrict__ alpha, int32_t* status, int G, int r, int dc, int dr,
+    float eps, const RopeFreq rf, int qk_norm) {
+  __shared__ float cs[kStepTok][kMaxR];                         // 16 KB
+  __shared__ float kp[kStepThreads / 64][kStepTok][kStepMaxDc];  // 64 KB
+  __shared__ float sqv[kStepTok][kStepMaxDc];
+  const int T_total = batch * n_new;
+  const int tok0 = blockIdx.x * kStepTok;
+  const int ntok = min(kStepTok, T_total - tok0);
+  const int duty = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (qk_norm ? duty == G : duty == 0) {
+    copy_rows_and_rope<T>(tok0, kStepTok, batch, n_new, c_new, kr_new, gkr, positions, pg, lat,
+                          rope, status, r, dr, eps, rf, qk_norm);
+    return;
+  }
+  const int g = duty;
+  const int nq = dc / 4;               // column quads
+  const int RG = kStepThreads / nq;    // row groups
+  const int rg = tid / nq, c4 = tid % nq;
+  const int rows = r / RG;             // rows per thread (<= kStepMaxRowsPerThread)
+  const float* W = w_uk + (size_t)g * r * dc + 4 * c4;
+  // Branch-free: rows past r / RG re-read the last one and are not summed.
+  f32x4 wv[kStepMaxRowsPerThread];
+#pragma unroll
+  for (int n = 0; n < kStepMaxRowsPerThread; ++n)
+    wv[n] = *(const f32x4*)(W + (size_t)(rg + min(n, rows - 1) * RG) * dc);
+  for (int i = tid; i < kStepTok * r; i += kStepThreads) {
+    const int k = i / r, e = i % r;
+    cs[k][e] = k < ntok ? Elem<T>::load(c_new, (size_t)(tok0 + k) * r + e) : 0.f;
+  }
+  __syncthreads();
+  f32x4 acc[kStepTok];
+#pragma unroll
+  for (int k = 0; k < kStepTok; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int n = 0; n < kStepMaxRowsPerThread; ++n)
+    if (n < rows) {
+      const int i = rg + n * RG;
+#pragma unroll
+      for (int k = 0; k < kStepTok; ++k) acc[k] += cs[k][i] * wv[n];
+    }
+  // the two row groups of a wavefront (nq = 32: lanes l and l ^ 32) meet here
+  // when a wavefront spans two of them
+  const bool pair = nq == 32;
+#pragma unroll
+  for (int k = 0; k < kStepTok; ++k) {
+    f32x4 v = acc[k];
+    if (pair) {
+      v[0] += __shfl_xor(v[0], 32, 64);
+      v[1] += __shfl_xor(v[1], 32, 64);
+      v[2] += __shfl_xor(v[2], 32, 64);
+      v[3] += __shfl_xor(v[3], 32, 64);
+    }
+    if (!pair || lane < 32) *(f32x4*)&kp[wave][k][4 * c4] = v;
+  }
+  __syncthreads();
+  // k[t][j] = sum of the partials of the wavefronts that hold column j: all
+  // of them when a wavefront spans two row groups (d_c = 128), else every
+  // nq / 64-th one (a row group spans nq / 64 wavefronts).
+  // Every sum has a fixed order, so the result is the same on every call.
+  const int wstep = pair ? 1 : nq / 64;
+  for (int i = tid; i < kStepTok * dc; i += kStepThreads) {
+    const int k = i / dc, j = i % dc;
+    float v = 0.f;
+    for (int w = pair ? 0 : (j / 4) / 64; w < kStepThreads / 64; w += wstep) v += kp[w][k][j];
+    sqv[k][j] = v * v;
+  }
+  __syncthreads();
+  if (wave < ntok) {  // wavefront k: sum over d_c of token k's k^2
+    float ss = 0.f;
+    for (int j = lane; j < dc; j += 64) ss += sqv[wave][j];
+    ss = wave_sum(ss);
+    const int tok = tok0 + wave;
+    const int b = tok / n_new, i = tok % n_new;
+    const int pos0 = positions[b];
+    const bool bad = pos0 < 0 || (int64_t)pos0 + n_new > pg.capacity();
+    const int64_t prow = bad ? -1 : pg.phys_row(b, pos0 + i);
+    if (lane == 0 && prow >= 0) alpha[(size_t)prow * G + g] = 1.0f / sqrtf(ss / (float)dc + eps);
+  }
+}
+
 hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
                          const void* k_rope_new, const float* w_uk, const float* gkr,
                          const int32_t* positions, const Paging& pg, void* lat, void* rope,
                          float* alpha, int32_t* status, hipStream_t s) {
   int T_total = batch * n_new;
+  const RopeFreq rf = rope_freq(c.dr, c.base);
+  // A decode step's few tokens: the latency-bound path with all of W^UK_g's
+  // loads in flight; it reads W^UK as 16-byte vectors.
+  const int nq = c.dc / 4;
+  if (T_total <= 4 * kStepTok && c.dc % 4 == 0 && c.dc <= kStepMaxDc && (nq == 32 || nq % 64 == 0) &&
+      c.r <= kMaxR && c.r % (kStepThreads / nq) == 0 &&
+      c.r / (kStepThreads / nq) <= kStepMaxRowsPerThread &&
+      ((uintptr_t)w_uk % 16 == 0 || !c.qk_norm)) {
+    dim3 g1((unsigned)((T_total + kStepTok - 1) / kStepTok), c.qk_norm ? c.G + 1 : 1);
+    if (c.dtype == QKMLA_BF16)
+      append_step_kernel<uint16_t><<<g1, kStepThreads, 0, s>>>(
+          batch, n_new, (const uint16_t*)c_new, (const uint16_t*)k_rope_new, w_uk, gkr,
+          positions, pg, (uint16_t*)lat, (uint16_t*)rope, alpha, status, c.G, c.r, c.dc, c.dr,
+          c.eps, rf, c.qk_norm);
+    else
+      append_step_kernel<float><<<g1, kStepThreads, 0, s>>>(
+          batch, n_new, (const float*)c_new, (const float*)k_rope_new, w_uk, gkr, positions, pg,
+          (float*)lat, (float*)rope, alpha, status, c.G, c.r, c.dc, c.dr, c.eps, rf, c.qk_norm);
+    return hipGetLastError();
+  }
   // The MFMA kernel reads latent rows and W^UK as 16-byte vectors.
   const bool vec_ok = ((uintptr_t)c_new % 16 == 0) && ((uintptr_t)w_uk % 16 == 0 || !c.qk_norm);
   if (c.dtype == QKMLA_BF16 && vec_ok && c.dc % 32 == 0 && c.dc <= kAlphaMaxDc &&
@@ -304,7 +428,7 @@ hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
     append_bf16_kernel<<<g2, 256, 0, s>>>(batch, n_new, (const uint16_t*)c_new,
                                           (const uint16_t*)k_rope_new, w_uk, gkr, positions,
                                           pg, (uint16_t*)lat, (uint16_t*)rope, alpha, status,
-                                          c.G, c.r, c.dc, c.dr, c.eps, c.base, c.qk_norm);
+                                          c.G, c.r, c.dc, c.dr, c.eps, rf, c.qk_norm);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((T_total + kAppendTok - 1) / kAppendTok), c.qk_norm ? c.G + 1 : 1);
@@ -312,11 +436,11 @@ hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
     append_kernel<uint16_t><<<grid, 256, 0, s>>>(
         batch, n_new, (const uint16_t*)c_new, (const uint16_t*)k_rope_new, w_uk, gkr, positions,
         pg, (uint16_t*)lat, (uint16_t*)rope, alpha, status, c.G, c.r, c.dc, c.dr, c.eps,
-        c.base, c.qk_norm);
+        rf, c.qk_norm);
   else
     append_kernel<float><<<grid, 256, 0, s>>>(
         batch, n_new, (const float*)c_new, (const float*)k_rope_new, w_uk, gkr, positions, pg,
-        (float*)lat, (float*)rope, alpha, status, c.G, c.r, c.dc, c.dr, c.eps, c.base,
+        (float*)lat, (float*)rope, alpha, status, c.G, c.r, c.dc, c.dr, c.eps, rf,
         c.qk_norm);
   return hipGetLastError();
 }

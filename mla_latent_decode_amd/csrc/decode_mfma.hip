@@ -53,6 +53,12 @@ constexpr int kRopeBytes = kTile * kDr * 2;   // 4 KB
 constexpr int kAlphaMaxG = 8;
 constexpr int kAlphaBytes = kTile * kAlphaMaxG * 4;  // 1 KB
 constexpr int kStageBytes = kLatBytes + kRopeBytes + kAlphaBytes;
+// Epilogue transpose: a wave's 32 head rows of 512 bytes per round (128 fp32
+// or 256 bf16 dims) plus 16 bytes of pad against bank conflicts; two such
+// regions per stage buffer.
+constexpr int kEpiRow = 512 + 16;
+constexpr int kEpiRegion = 32 * kEpiRow;
+static_assert(2 * kEpiRegion <= kStageBytes, "two epilogue regions per stage buffer");
 // p = 2^(logit - m_ref) may exceed 1; a segment is streamed again with a
 // raised reference only if some p would exceed 2^kOverflowLog2.
 constexpr float kOverflowLog2 = 64.0f;
@@ -145,7 +151,8 @@ struct Seq {
   const char* rope;   // RoPE row pool, 128 B per row
   const char* alpha;  // alpha row pool, 4*G B per row
   int cb;             // cache (sequence of the batch) whose rows are read
-  int L;              // length of the (virtual) sequence
+  int last_tile;      // index of the sequence's last tile (from the tile prefix)
+  int L;              // length of the (virtual) sequence; read only for its last tile
 };
 
 // Per-wavefront state carried across the tiles of a segment.
@@ -193,7 +200,14 @@ __device__ __forceinline__ void issue_tile(const Seq& sq, const Paging& pg, int 
     page = (page >= 0 && page < pg.num_pages) ? page : 0;
     prow0 = (int64_t)page * pg.page_size + (t0 - blk * pg.page_size);
   }
-  const int last = sq.L - 1 - t0;  // rows past the sequence repeat its last row
+  // Rows past the sequence repeat its last row; only its last tile has such
+  // rows, and only there is the length needed (a uniform branch, so the
+  // length's load is waited for only on that tile).
+  int last = kTile;
+  if (tile == sq.last_tile) {
+    asm volatile("" ::: "memory");
+    last = sq.L - 1 - t0;
+  }
   const char* latb = sq.lat + prow0 * (kR * 2);
 #pragma unroll
   for (int i = 0; i < TileLoads<QKN, NW>::lat; ++i) {
@@ -338,8 +352,12 @@ __device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, const Paging& 
 #pragma unroll
     for (int j = 0; j < 16; ++j) lg[j] = sc[j];
   }
-  const int thr = sq.L - (tile0 + i) * kTile - 4 * hf;  // token 4*hf + c is real iff c < thr
-  if (thr < kTile) {
+  // Rows of this tile inside the sequence (wave-uniform): only a sequence's
+  // last tile has rows to mask, and the uniform test keeps the mask code off
+  // the other tiles' path.
+  if (tile0 + i == sq.last_tile) {
+    const int tail = __builtin_amdgcn_readfirstlane(sq.L - (tile0 + i) * kTile);
+    const int thr = tail - 4 * hf;  // token 4*hf + c is real iff c < thr
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       if (8 * (j >> 2) + (j & 3) >= thr) lg[j] = -INFINITY;
@@ -424,11 +442,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
     const int tile0 = (int)(x - s0);
     const int nt = (int)(seg_end - x);
     sq.cb = b / a.s_q;
+    sq.last_tile = (int)(s1 - s0) - 1;
     sq.lat = (const char*)a.lat;
     sq.rope = (const char*)a.rope;
     sq.alpha = QKN ? (const char*)a.alpha : nullptr;
     const size_t qrow = (size_t)b * a.H + head;
 
+    // The segment's first two tiles go out first, so that their latency
+    // overlaps the query loads below.
+    issue_tile<QKN, NW, 0>(sq, a.pg, a.G, tile0, wave, lane);
+    if (nt > 1) issue_tile<QKN, NW, 1>(sq, a.pg, a.G, tile0 + 1, wave, lane);
     // Query operands for this sequence: q~ in registers, the RoPE query in
     // LDS, both kept for the segment.
 #pragma unroll
@@ -448,8 +471,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) w.O[ii][j] = 0.f;
       w.l_run = 0.f;
-      issue_tile<QKN, NW, 0>(sq, a.pg, a.G, tile0, wave, lane);
-      if (nt > 1) issue_tile<QKN, NW, 1>(sq, a.pg, a.G, tile0 + 1, wave, lane);
       for (int i = 0; i < nt; i += kStages) {
         tile_step<QKN, NW, 0>(w, sq, a.pg, a.G, tile0, i, nt, wave, lane, g);
         if (i + 1 < nt) tile_step<QKN, NW, 1>(w, sq, a.pg, a.G, tile0, i + 1, nt, wave, lane, g);
@@ -462,41 +483,75 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
       // normalised logits).
       block_sync();
       if (lane == 0) lds_restart[wave] = 0;
+      issue_tile<QKN, NW, 0>(sq, a.pg, a.G, tile0, wave, lane);
+      if (nt > 1) issue_tile<QKN, NW, 1>(sq, a.pg, a.G, tile0 + 1, wave, lane);
     }
     // ---- segment epilogue ----
+    // The accumulator holds, in lane (head 32 wave + lane % 32, hf = lane / 32)
+    // and register i of block mb, latent dim 32 mb + 8 (i / 4) + 4 hf + i % 4.
+    // It goes out through LDS, so that each store writes whole rows: the
+    // stage buffers are idle here (every wave is past the segment's last
+    // tile), and wave w transposes through its own 32-row region of them,
+    // one round of kEpiDims dims at a time.
     const float l_tot = w.l_run + __shfl_xor(w.l_run, 32, 64);
     const float m_run = w.m_ref;
     const bool complete = (x == s0) && (seg_end == s1);
-    if (complete) {
+    // The lane values are re-derived through an opaque copy, so that the
+    // epilogue's addresses are formed here rather than hoisted above the tile
+    // loop (where they would stay live, in spilled registers).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int en = ln & 31, ehf = ln >> 5;
+    char* region = (wave >> 1 == 0 ? stage_buf<0>() : stage_buf<1>()) + (wave & 1) * kEpiRegion;
+    if (complete) {  // normalised o_lat, fp32 rows of 2 KB: four rounds of 128 dims
       const float inv = 1.0f / l_tot;
-      float* out = a.o_lat + qrow * kR;
+      char* out = (char*)(a.o_lat + (size_t)b * a.H * kR) + (size_t)(wave * 32) * kR * 4;
 #pragma unroll
-      for (int mb = 0; mb < kR / 32; ++mb)
+      for (int rnd = 0; rnd < kR / 128; ++rnd) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v = {w.O[mb][4 * q] * inv, w.O[mb][4 * q + 1] * inv, w.O[mb][4 * q + 2] * inv,
-                     w.O[mb][4 * q + 3] * inv};
-          *(f32x4*)(out + 32 * mb + 8 * q + 4 * hf) = v;
+        for (int mbl = 0; mbl < 4; ++mbl)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int mb = rnd * 4 + mbl;
+            const f32x4 v = {w.O[mb][4 * q] * inv, w.O[mb][4 * q + 1] * inv,
+                             w.O[mb][4 * q + 2] * inv, w.O[mb][4 * q + 3] * inv};
+            *(f32x4*)(region + en * kEpiRow + (32 * mbl + 8 * q + 4 * ehf) * 4) = v;
+          }
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int row = 2 * it + ehf;
+          *(uint4*)(out + (size_t)row * kR * 4 + rnd * 512 + en * 16) =
+              *(const uint4*)(region + row * kEpiRow + en * 16);
         }
+      }
       if (hf == 0 && a.lse) a.lse[qrow] = (m_run + log2f(l_tot)) * kLn2;
-    } else {
+    } else {  // partial: m, l and the unnormalised O in bf16, rows of 1 KB: two rounds of 256 dims
       const int slot = first_seg ? 0 : 1;
       char* sp = a.part + ((size_t)p * kSlotsPerWg + slot) * kPartialSlotBytes(a.H, kR);
       if (hf == 0) {
         ((float*)sp)[head] = m_run;
         ((float*)sp)[a.H + head] = l_tot;
       }
-      uint16_t* Op = (uint16_t*)(sp + (size_t)a.H * 8) + (size_t)head * kR;
+      char* Op = sp + (size_t)a.H * 8 + (size_t)(wave * 32) * kR * 2;
 #pragma unroll
-      for (int mb = 0; mb < kR / 32; ++mb)
+      for (int rnd = 0; rnd < kR / 256; ++rnd) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint2 v = {(uint32_t)f32_to_bf16(w.O[mb][4 * q]) |
-                               ((uint32_t)f32_to_bf16(w.O[mb][4 * q + 1]) << 16),
-                           (uint32_t)f32_to_bf16(w.O[mb][4 * q + 2]) |
-                               ((uint32_t)f32_to_bf16(w.O[mb][4 * q + 3]) << 16)};
-          *(uint2*)(Op + 32 * mb + 8 * q + 4 * hf) = v;
+        for (int mbl = 0; mbl < 8; ++mbl)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int mb = rnd * 8 + mbl;
+            bf16x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (__bf16)w.O[mb][4 * q + j];
+            *(bf16x4*)(region + en * kEpiRow + (32 * mbl + 8 * q + 4 * ehf) * 2) = v;
+          }
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int row = 2 * it + ehf;
+          *(uint4*)(Op + (size_t)row * kR * 2 + rnd * 512 + en * 16) =
+              *(const uint4*)(region + row * kEpiRow + en * 16);
         }
+      }
     }
     first_seg = false;
     x = seg_end;

@@ -46,6 +46,17 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, float base, 
   sincosf((float)ang, s, c);
 }
 
+// cos and sin of pos * freq, freq one of the host's RoPE frequencies
+// (RopeFreq): the angle is formed and reduced modulo 2*pi in double (exact to
+// about 2^-35 rad for positions below 2^18), then float sincos.
+__device__ __forceinline__ void rope_cos_sin_freq(int pos, double freq, float* c, float* s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const double inv_two_pi = 0.15915494309189533576888376337251;
+  const double ang = (double)pos * freq;
+  const double red = fma(-floor(ang * inv_two_pi), two_pi, ang);
+  sincosf((float)red, s, c);
+}
+
 // Sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -13,36 +13,42 @@
 
 namespace qkmla {
 
-// One block per (sequence b, head h, block of 64 latent dims); 256 threads =
-// 16 source groups x 16 dim-quads.  The block first lists its sources in LDS
-// (the partial slot each workgroup of the sequence wrote, one thread per
-// workgroup, so the slot arithmetic is off the load path), then source group
-// k folds the sources k, k + 16, ... with a running maximum, issuing the
-// loads of up to four sources before it folds them.  The 16 groups meet in
-// LDS.  The tile prefix of the plan comes from the workspace, where the
-// split-KV kernel left it.
-constexpr int kMergeDims = 64;
-constexpr int kMergeGroups = 16;
-constexpr int kMergeQuads = kMergeDims / 4;   // lanes per source group
-constexpr int kMergeBatch = 4;                // sources in flight per thread
-constexpr int kMergeList = 256;               // sources listed per pass
+// The log-sum-exp merge.  WPH wavefronts share head h of virtual sequence
+// b; a block holds max(4, WPH) wavefronts, so 4 / WPH heads when WPH < 4.
+// The block first lists the sequence's partial slots in LDS (the slot each
+// workgroup holding its tiles wrote, one thread per workgroup, so the slot
+// arithmetic is off the load path).  Wave w of a head folds the sources w,
+// w + WPH, ... with a running maximum, kMergeBatch at a time with all of
+// their loads in flight; lane l holds latent dims 8l..8l+7, one 16-byte piece
+// of the source's 1 KB bf16 O row (r = 512).  The WPH waves of a head meet in LDS.
+// The host picks WPH so that a wave folds about kMergeBatch sources and the
+// grid is resident at once: the kernel's time is then about one round of
+// loads rather than several.  The tile prefix of the plan comes from the
+// workspace, where the split-KV kernel left it.
+constexpr int kMergeBatch = 8;     // sources in flight per wave
+constexpr int kMergeList = 1024;   // sources listed per pass
 
-__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ plan, int B, int H,
-                                                    int r, int n_wg,
-                                                    const char* __restrict__ part,
-                                                    float* __restrict__ o_lat,
-                                                    float* __restrict__ lse) {
-  __shared__ f32x4 red[kMergeGroups][kMergeQuads];
-  __shared__ float red_m[kMergeGroups], red_l[kMergeGroups];
-  __shared__ int src[kMergeList];  // slot index p * kSlotsPerWg + slot, or -1 (nothing written)
-  const int b = blockIdx.x, h = blockIdx.y, dblk = blockIdx.z;
-  const int tid = threadIdx.x, sg = tid / kMergeQuads, dq = tid % kMergeQuads;
-  const int d0 = dblk * kMergeDims + 4 * dq;
-  float* out = o_lat + ((size_t)b * H + h) * r + d0;
+template <int WPH>
+__global__ __launch_bounds__((WPH < 4 ? 4 : WPH) * 64) void merge_kernel(
+    const int32_t* __restrict__ plan, int B, int H, int r, int n_wg,
+    const char* __restrict__ part, float* __restrict__ o_lat, float* __restrict__ lse) {
+  constexpr int kWaves = WPH < 4 ? 4 : WPH;
+  constexpr int kHeads = kWaves / WPH;  // heads per block
+  __shared__ int src[kMergeList];       // slot index p * kSlotsPerWg + slot, or -1 (nothing written)
+  __shared__ f32x4 red[WPH > 1 ? kWaves : 1][2][64];
+  __shared__ float red_m[kWaves], red_l[kWaves];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = blockIdx.y * kHeads + wave / WPH;  // this wave's head
+  const int wi = wave % WPH;                        // its index among the head's waves
+  float* out = o_lat + ((size_t)b * H + h) * r + 8 * lane;
   const int Pb = plan[b], Pb1 = plan[b + 1];
   if (Pb1 == Pb) {  // invalid length: zeros and lse = -inf
-    if (sg == 0) *(f32x4*)out = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tid == 0 && dblk == 0 && lse) lse[(size_t)b * H + h] = -INFINITY;
+    if (wi == 0) {
+      *(f32x4*)out = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)(out + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (lane == 0 && lse) lse[(size_t)b * H + h] = -INFINITY;
+    }
     return;
   }
   const int64_t N = plan[B];
@@ -50,84 +56,119 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
   const int p_hi = wg_of(Pb1 - 1, N, n_wg);
   if (p_lo == p_hi) return;  // written directly by the decode kernel
   const size_t slot_bytes = kPartialSlotBytes(H, r);
-  const size_t o_off = (size_t)H * 8 + ((size_t)h * r + d0) * 2;
+  const size_t o_off = (size_t)H * 8 + ((size_t)h * r + 8 * lane) * 2;
   float M = -INFINITY, lsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int n_src = p_hi - p_lo + 1;
   const int first = p_lo * kSlotsPerWg + merge_slot_of(Pb, p_lo, N, n_wg, p_lo);
   for (int c0 = 0; c0 < n_src; c0 += kMergeList) {
     const int cn = min(kMergeList, n_src - c0);
     // Workgroups between p_lo and p_hi with an empty range (more workgroups
     // than tiles) wrote nothing and are skipped.
-    if (tid < cn) {
-      const int p = p_lo + c0 + tid;
+    for (int i = tid; i < cn; i += kWaves * 64) {
+      const int p = p_lo + c0 + i;
       const int slot = merge_slot_of(Pb, p_lo, N, n_wg, p);
-      src[tid] = slot < 0 ? -1 : p * kSlotsPerWg + slot;
+      src[i] = slot < 0 ? -1 : p * kSlotsPerWg + slot;
     }
     __syncthreads();
-    for (int k0 = sg; k0 < cn; k0 += kMergeBatch * kMergeGroups) {
+    for (int k0 = wi; k0 < cn; k0 += kMergeBatch * WPH) {
       // Branch-free: an entry past the list or without a partial reads the
       // first workgroup's slot (always written) and gets weight 0, so the
       // loads of all kMergeBatch sources are issued before the first fold.
       float m[kMergeBatch], l[kMergeBatch];
-      uint2 ob[kMergeBatch];
+      uint4 ob[kMergeBatch];
       bool ok[kMergeBatch];
 #pragma unroll
       for (int u = 0; u < kMergeBatch; ++u) {
-        const int k = k0 + u * kMergeGroups;
+        const int k = k0 + u * WPH;
         const int e = src[k < cn ? k : cn - 1];
         ok[u] = k < cn && e >= 0;
         const char* sp = part + (size_t)(ok[u] ? e : first) * slot_bytes;
         m[u] = ((const float*)sp)[h];
         l[u] = ((const float*)sp)[H + h];
-        ob[u] = *(const uint2*)(sp + o_off);
+        ob[u] = *(const uint4*)(sp + o_off);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the folds
 #pragma unroll
       for (int u = 0; u < kMergeBatch; ++u) {
-        const f32x4 v = {__uint_as_float(ob[u].x << 16), __uint_as_float(ob[u].x & 0xFFFF0000u),
-                         __uint_as_float(ob[u].y << 16), __uint_as_float(ob[u].y & 0xFFFF0000u)};
+        const f32x4 v0 = {__uint_as_float(ob[u].x << 16), __uint_as_float(ob[u].x & 0xFFFF0000u),
+                          __uint_as_float(ob[u].y << 16), __uint_as_float(ob[u].y & 0xFFFF0000u)};
+        const f32x4 v1 = {__uint_as_float(ob[u].z << 16), __uint_as_float(ob[u].z & 0xFFFF0000u),
+                          __uint_as_float(ob[u].w << 16), __uint_as_float(ob[u].w & 0xFFFF0000u)};
         const float Mn = ok[u] ? fmaxf(M, m[u]) : M;
         const float keep = Mn == M ? 1.f : exp2f(M - Mn);  // also M = Mn = -inf
         const float w = ok[u] ? exp2f(m[u] - Mn) : 0.f;
-        acc = acc * keep + v * w;
+        acc0 = acc0 * keep + v0 * w;
+        acc1 = acc1 * keep + v1 * w;
         lsum = lsum * keep + l[u] * w;
         M = Mn;
       }
     }
-    __syncthreads();  // the list is rewritten by the next pass
+    if (c0 + kMergeList < n_src) __syncthreads();  // the list is rewritten by the next pass
   }
-  red[sg][dq] = acc;
-  if (dq == 0) {
-    red_m[sg] = M;
-    red_l[sg] = lsum;
-  }
-  __syncthreads();
-  if (sg == 0) {
-    float Mt = red_m[0];
-#pragma unroll
-    for (int k = 1; k < kMergeGroups; ++k) Mt = fmaxf(Mt, red_m[k]);
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMergeGroups; ++k) {
-      if (red_m[k] == -INFINITY) continue;  // a group that held no source
-      const float w = exp2f(red_m[k] - Mt);
-      t += red[k][dq] * w;
-      l += red_l[k] * w;
+  if constexpr (WPH > 1) {
+    red[wave][0][lane] = acc0;
+    red[wave][1][lane] = acc1;
+    if (lane == 0) {
+      red_m[wave] = M;
+      red_l[wave] = lsum;
     }
-    const float inv = 1.0f / l;
-    *(f32x4*)out = t * inv;
-    if (dq == 0 && dblk == 0 && lse) lse[(size_t)b * H + h] = (Mt + log2f(l)) * kLn2;
+    __syncthreads();
+    if (wi != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < WPH; ++k) Mt = fmaxf(Mt, red_m[wave + k]);
+    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+    float lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < WPH; ++k) {
+      const float mk = red_m[wave + k];
+      if (mk == -INFINITY) continue;  // a wave that held no source
+      const float w = exp2f(mk - Mt);
+      t0 += red[wave + k][0][lane] * w;
+      t1 += red[wave + k][1][lane] * w;
+      lt += red_l[wave + k] * w;
+    }
+    acc0 = t0;
+    acc1 = t1;
+    lsum = lt;
+    M = Mt;
   }
+  const float inv = 1.0f / lsum;
+  *(f32x4*)out = acc0 * inv;
+  *(f32x4*)(out + 4) = acc1 * inv;
+  if (lane == 0 && lse) lse[(size_t)b * H + h] = (M + log2f(lsum)) * kLn2;
+}
+
+template <int WPH>
+static void launch_merge_wph(int nv, int H, int r, int n_wg, const int32_t* plan,
+                             const char* part, float* o_lat, float* lse, hipStream_t s) {
+  constexpr int kWaves = WPH < 4 ? 4 : WPH;
+  constexpr int kHeads = kWaves / WPH;
+  merge_kernel<WPH><<<dim3(nv, H / kHeads), kWaves * 64, 0, s>>>(plan, nv, H, r, n_wg, part,
+                                                                 o_lat, lse);
 }
 
 hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, void* workspace,
                         int n_wg, float* o_lat, float* lse, hipStream_t s) {
   char* wsb = (char*)workspace;
   const int nv = batch * s_q;  // virtual sequences
-  merge_kernel<<<dim3(nv, c.H, c.r / kMergeDims), 256, 0, s>>>(
-      (const int32_t*)(wsb + ws.plan), nv, c.H, c.r, n_wg, (const char*)(wsb + ws.partials),
-      o_lat, lse);
+  if (c.r != 8 * 64 || c.H % 4 != 0) return hipErrorInvalidValue;  // one 16-byte piece per lane
+  // Sources of a sequence: the workgroups its tiles span, about n_wg / nv + 1
+  // when the lengths are even.  WPH = the power of two that gives each wave
+  // about kMergeBatch of them (at most 16 waves per head).
+  const int per_seq = (n_wg + nv - 1) / nv + 1;
+  int wph = 1;
+  while (wph < 16 && wph * kMergeBatch < per_seq) wph *= 2;
+  const int32_t* plan = (const int32_t*)(wsb + ws.plan);
+  const char* part = (const char*)(wsb + ws.partials);
+  switch (wph) {
+    case 1: launch_merge_wph<1>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
+    case 2: launch_merge_wph<2>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
+    case 4: launch_merge_wph<4>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
+    case 8: launch_merge_wph<8>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
+    default: launch_merge_wph<16>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
+  }
   return hipGetLastError();
 }
 

@@ -21,6 +21,15 @@ struct Cfg {
   int hpg;       // heads per group
 };
 
+// RoPE inverse frequencies theta_i = base^(-2i/d_r), i < d_r/2, in double.
+// Formed once on the host per call and passed by value to the kernels that
+// rotate, so no kernel evaluates a double-precision power.
+constexpr int kMaxRopePairs = 128;
+struct RopeFreq {
+  double f[kMaxRopePairs];
+};
+RopeFreq rope_freq(int dr, float base);
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -30,7 +39,7 @@ constexpr int kTile = 32;
 constexpr int kSlotsPerWg = 2;
 // Bytes of one partial slot: the running max m and sum l of each head in
 // fp32, the unnormalised O of each head in bf16 (it is rounded once, like the
-// softmax weights, and the merge accumulates in fp32).
+// softmax weights, and the merge accumulates in fp32), head-major [H][r].
 __host__ __device__ constexpr size_t kPartialSlotBytes(int H, int r) {
   return (size_t)H * 8 + (size_t)H * r * 2;
 }

@@ -9,55 +9,19 @@
 // Blockwise Normalization).  tau*log2(e) is folded into alpha^q and q^R so the
 // decode kernel works in the exp2 domain.  In plain mode alpha^q = tau*log2(e)
 // and q^R is only rotated.  The bf16 path also folds alpha^q into q~.
+#include <cmath>
+
 #include "device_common.h"
 #include "plan_device.h"
 #include "qkmla_internal.h"
 
 namespace qkmla {
 
-// cos/sin of the query position for every RoPE pair, into LDS (cs[2*i],
-// cs[2*i+1]).
-__device__ void rope_table(int pos, int dr, float base, float* cs) {
-  for (int i = threadIdx.x; i < dr / 2; i += blockDim.x) rope_cos_sin(pos, i, dr, base, &cs[2 * i], &cs[2 * i + 1]);
-}
-
-// alpha^q and the RoPE query of one head; executed by one wavefront
-// (lane-strided over dims).  cs: the rope_table of the query position.
-template <typename TIn, typename TOut>
-__device__ void prep_scalar_and_rope(const TIn* qc, const TIn* qr, const float* gqr, int dc,
-                                     int dr, float eps, float tau, int qk_norm, const float* cs,
-                                     float* alpha_q_out, TOut* qr_out) {
-  const int lane = threadIdx.x & 63;
-  const float sl = tau * kLog2e;
-  float ss = 0.f;
-  if (qk_norm) {
-    for (int e = lane; e < dc; e += 64) {
-      float v = Elem<TIn>::load(qc, e);
-      ss += v * v;
-    }
-    ss = wave_sum(ss);
-  }
-  float aq = qk_norm ? 1.0f / sqrtf(ss / (float)dc + eps) : 1.0f;
-  if (lane == 0) *alpha_q_out = aq * sl;
-  float rs = 0.f;
-  if (qk_norm) {
-    for (int e = lane; e < dr; e += 64) {
-      float v = Elem<TIn>::load(qr, e);
-      rs += v * v;
-    }
-    rs = wave_sum(rs);
-  }
-  float rscale = qk_norm ? 1.0f / sqrtf(rs / (float)dr + eps) : 1.0f;
-  for (int pi = lane; pi < dr / 2; pi += 64) {
-    float x0 = Elem<TIn>::load(qr, 2 * pi), x1 = Elem<TIn>::load(qr, 2 * pi + 1);
-    if (qk_norm) {
-      x0 *= rscale * gqr[2 * pi];
-      x1 *= rscale * gqr[2 * pi + 1];
-    }
-    const float c = cs[2 * pi], sn = cs[2 * pi + 1];
-    Elem<TOut>::store(qr_out, 2 * pi, (x0 * c - x1 * sn) * sl);
-    Elem<TOut>::store(qr_out, 2 * pi + 1, (x0 * sn + x1 * c) * sl);
-  }
+RopeFreq rope_freq(int dr, float base) {
+  RopeFreq rf;
+  for (int i = 0; i < kMaxRopePairs; ++i)
+    rf.f[i] = i < dr / 2 ? std::pow((double)base, -2.0 * (double)i / (double)dr) : 0.0;
+  return rf;
 }
 
 // Paged caches: every block-table entry the sequence's rows need must name a
@@ -76,92 +40,195 @@ __device__ __forceinline__ int clamp_pos(int L, int L_cap) {
   return (L >= 1 && L <= L_cap) ? L - 1 : 0;
 }
 
-// bf16 layer with 16 heads per KV group: one workgroup (4 waves) per (b, g).
-// q~[16 heads][r] = q^C[16][d_c] . W~_g^T[d_c][r] on mfma_f32_16x16x32_bf16.
-// Operand layouts (gfx950, 16x16x32): A lane l holds A[m=l%16][k=8(l/16)+j],
-// B lane l holds B[k=8(l/16)+j][n=l%16], D lane l reg i holds D[4(l/16)+i][l%16].
+// Sequence-level status bits (length outside [1, L_cap], bad pages); called
+// by one block per virtual sequence, block-wide.
+__device__ void check_sequence(const Paging& pg, int v, int s_q, int L, int32_t* status) {
+  check_pages(pg, v, s_q, L, status);
+  if (threadIdx.x == 0 && (L < 1 || L > pg.capacity()) && status)
+    atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
+}
+
+// bf16 layer with 16 heads per KV group.  For group g the query projection
+// is a GEMM  q~[(sequence, head)][r] = q^C[(sequence, head)][d_c] . W~_g^T
+// (mfma_f32_16x16x32_bf16, fp32 accumulation).  Grid (ceil(nv / SPB), G,
+// r / kQpCols + 1), 256 threads: block (x, g, z < r / kQpCols) takes the
+// group's 16 heads of SPB sequences (M = 16 SPB rows) and output columns
+// [z kQpCols, (z+1) kQpCols); wave w owns two 16-wide column blocks at
+// z kQpCols + 32 w for all M rows, so each W~ element the block needs is
+// loaded once and serves SPB sequences.  Every operand load is issued before
+// the first MFMA.  Each lane also holds a quarter of its row's q^C (the A
+// operand), so alpha^q comes from the same registers with two cross-lane
+// sums.  The tile goes out through LDS as 16-byte stores.  The last z-slice
+// writes the normalised, rotated RoPE query of the block's rows and the
+// sequences' status bits, its loads likewise issued together.
+// Layouts (gfx950, 16x16x32): A lane l holds A[m=l%16][k=8(l/16)+j], B lane l
+// holds B[k=8(l/16)+j][n=l%16], D lane l reg i holds D[4(l/16)+i][l%16].
+constexpr int kQpCols = 128;
+constexpr int kQpRopeSlots = 4;  // RoPE pairs per thread and sequence: 16 threads per head, d_r / 2 <= 64
+
+template <int SPB, int KS>
 __global__ __launch_bounds__(256) void qprep_mfma_kernel(
     const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_qabs, const float* __restrict__ gqr,
-    const int32_t* __restrict__ seq_lens, int s_q, const Paging pg, int H, int G, int r, int dc,
-    int dr, float eps, float tau, float base, int qk_norm, uint16_t* __restrict__ q_tilde,
+    const int32_t* __restrict__ seq_lens, int nv, int s_q, const Paging pg, int H, int r, int dr,
+    float eps, float tau, int qk_norm, const RopeFreq rf, uint16_t* __restrict__ q_tilde,
     float* __restrict__ alpha_q, uint16_t* __restrict__ q_rope_out, int32_t* status) {
-  const int b = blockIdx.x, g = blockIdx.y;  // b: virtual sequence (query row)
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int dc = KS * 32;
+  const int b0 = blockIdx.x * SPB, g = blockIdx.y, z = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h0 = g * 16;
-  const int L_cap = pg.capacity();
-  const int L = virt_len(seq_lens, b, s_q, L_cap);
-  if (g == 0) check_pages(pg, b, s_q, L, status);
-  if (g == 0 && threadIdx.x == 0 && (L < 1 || L > L_cap) && status)
-    atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
-  const int pos = clamp_pos(L, L_cap);
+  const float sl = tau * kLog2e;
 
-  __shared__ float cs[256];  // d_r <= 256
-  rope_table(pos, dr, base, cs);
+  if (z == r / kQpCols) {
+    // ---- RoPE query: thread -> head hh of each sequence, pairs p0, p0 + 16, ... ----
+    const int hh = tid >> 4, p0 = tid & 15;
+    const int np = dr / 2;
+    const int L_cap = pg.capacity();
+    uint32_t u[SPB][kQpRopeSlots];
+    float2 gg[kQpRopeSlots];
+    double fr[kQpRopeSlots];
+    int L[SPB];
+#pragma unroll
+    for (int k = 0; k < kQpRopeSlots; ++k) {
+      const int pi = min(p0 + 16 * k, np - 1);  // pairs past d_r / 2 re-read the last one
+      gg[k] = *(const float2*)(gqr + 2 * pi);
+      fr[k] = rf.f[pi];
+#pragma unroll
+      for (int sq = 0; sq < SPB; ++sq) {
+        const int b = min(b0 + sq, nv - 1);
+        u[sq][k] = *(const uint32_t*)(q_rope + ((size_t)b * H + h0 + hh) * dr + 2 * pi);
+      }
+    }
+#pragma unroll
+    for (int sq = 0; sq < SPB; ++sq) L[sq] = virt_len(seq_lens, min(b0 + sq, nv - 1), s_q, L_cap);
+#pragma unroll
+    for (int sq = 0; sq < SPB; ++sq) {
+      const int b = b0 + sq;
+      float rs = 0.f;
+#pragma unroll
+      for (int k = 0; k < kQpRopeSlots; ++k) {
+        const float x0 = bf16_to_f32((uint16_t)u[sq][k]), x1 = bf16_to_f32((uint16_t)(u[sq][k] >> 16));
+        rs += p0 + 16 * k < np ? x0 * x0 + x1 * x1 : 0.f;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) rs += __shfl_xor(rs, o, 64);
+      const float rscale = qk_norm ? 1.0f / sqrtf(rs / (float)dr + eps) : 1.0f;
+      const int pos = clamp_pos(L[sq], L_cap);
+      uint16_t* qo = q_rope_out + ((size_t)b * H + h0 + hh) * dr;
+#pragma unroll
+      for (int k = 0; k < kQpRopeSlots; ++k) {
+        const int pi = p0 + 16 * k;
+        if (pi < np && b < nv) {
+          float x0 = bf16_to_f32((uint16_t)u[sq][k]), x1 = bf16_to_f32((uint16_t)(u[sq][k] >> 16));
+          if (qk_norm) {
+            x0 *= rscale * gg[k].x;
+            x1 *= rscale * gg[k].y;
+          }
+          float c, sn;
+          rope_cos_sin_freq(pos, fr[k], &c, &sn);
+          *(uint32_t*)(qo + 2 * pi) = (uint32_t)f32_to_bf16((x0 * c - x1 * sn) * sl) |
+                                      ((uint32_t)f32_to_bf16((x0 * sn + x1 * c) * sl) << 16);
+        }
+      }
+    }
+    if (g == 0)
+      for (int sq = 0; sq < SPB; ++sq)
+        if (b0 + sq < nv) check_sequence(pg, b0 + sq, s_q, L[sq], status);
+    return;
+  }
 
-  const uint16_t* A = q_c + ((size_t)b * H + h0) * dc;
-  const uint16_t* W = w_qabs + (size_t)g * r * dc;
+  // ---- q~ columns [z kQpCols, (z+1) kQpCols) of SPB sequences ----
+  __shared__ __attribute__((aligned(16))) uint16_t tile[16 * SPB][kQpCols];
   const int m = lane & 15, kq = lane >> 4;
-  // Per-head scale folded into q~: the decode logit is then one FMA,
-  // S_c * alpha^k + S_r, with alpha^q, the softmax scale and log2(e) already
-  // in q~ (QK-norm); plain mode has one accumulator for content + RoPE, so
-  // only the softmax scale and log2(e) go in.
-  __shared__ float qscale[16];
-  for (int hh = wave; hh < 16; hh += 4) {
-    const uint16_t* qh = A + (size_t)hh * dc;
+  const uint16_t* W = w_qabs + (size_t)g * r * dc;
+  const int n0 = z * kQpCols + wave * 32;
+  bf16x8 a[SPB][KS], bv[2][KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      bv[nb][ks] = *(const bf16x8*)(W + (size_t)(n0 + nb * 16 + m) * dc + ks * 32 + kq * 8);
+#pragma unroll
+    for (int sq = 0; sq < SPB; ++sq) {
+      const int b = min(b0 + sq, nv - 1);  // rows past the batch repeat its last one, unstored
+      a[sq][ks] = *(const bf16x8*)(q_c + ((size_t)b * H + h0 + m) * dc + ks * 32 + kq * 8);
+    }
+  }
+  f32x4 acc[SPB][2];
+  float aq[SPB];
+#pragma unroll
+  for (int sq = 0; sq < SPB; ++sq) {
+    // alpha^q of row m (lanes m, m+16, m+32, m+48 hold a quarter of q^C each),
+    // times the softmax scale and log2(e)
     float ss = 0.f;
-    for (int e = lane; e < dc; e += 64) {
-      const float v = bf16_to_f32(qh[e]);
-      ss += v * v;
-    }
-    ss = wave_sum(ss);
-    if (lane == 0)
-      qscale[hh] = (qk_norm ? 1.0f / sqrtf(ss / (float)dc + eps) : 1.0f) * (tau * kLog2e);
-  }
-  __syncthreads();
-  // The bf16 path has r = 512: each wave owns 8 blocks of 16 output columns.
-  // The loops are unrolled so that every weight load is issued before the
-  // first MFMA waits (the weights come from L2 or HBM, one latency, not eight).
-  constexpr int kNbPerWave = 512 / 16 / 4;
-  const int ksteps = dc / 32;               // 4 for d_c = 128
-  constexpr int kMaxK = 8;                  // d_c <= 256 on this path
-  bf16x8 a[kMaxK];
 #pragma unroll
-  for (int ks = 0; ks < kMaxK; ++ks)
-    if (ks < ksteps) a[ks] = *(const bf16x8*)(A + (size_t)m * dc + ks * 32 + kq * 8);
-  f32x4 acc[kNbPerWave];
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-  for (int nbi = 0; nbi < kNbPerWave; ++nbi) acc[nbi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < kMaxK; ++ks) {
-    if (ks < ksteps) {
-      bf16x8 bv[kNbPerWave];
-#pragma unroll
-      for (int nbi = 0; nbi < kNbPerWave; ++nbi)
-        bv[nbi] = *(const bf16x8*)(W + (size_t)((wave * kNbPerWave + nbi) * 16 + m) * dc +
-                                   kq * 8 + ks * 32);
-#pragma unroll
-      for (int nbi = 0; nbi < kNbPerWave; ++nbi)
-        acc[nbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bv[nbi], acc[nbi], 0, 0, 0);
-    }
+      for (int j = 0; j < 8; ++j) {
+        const float v = (float)a[sq][ks][j];
+        ss += v * v;
+      }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    aq[sq] = (qk_norm ? 1.0f / sqrtf(ss / (float)dc + eps) : 1.0f) * sl;
+    if (z == 0 && wave == 0 && kq == 0 && b0 + sq < nv) alpha_q[(size_t)(b0 + sq) * H + h0 + m] = aq[sq];
+    acc[sq][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[sq][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
-  for (int nbi = 0; nbi < kNbPerWave; ++nbi) {
-    const int nb = wave * kNbPerWave + nbi;
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int sq = 0; sq < SPB; ++sq)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[sq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[sq][ks], bv[nb][ks], acc[sq][nb], 0, 0, 0);
+#pragma unroll
+  for (int sq = 0; sq < SPB; ++sq)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int hh = 4 * kq + i;
-      q_tilde[((size_t)b * H + h0 + hh) * r + nb * 16 + m] = f32_to_bf16(acc[nbi][i] * qscale[hh]);
+      const int hh = 4 * kq + i;
+      const float sc = __shfl(aq[sq], hh, 64);  // lane hh (< 16) holds row hh's scale
+      tile[16 * sq + hh][wave * 32 + m] = f32_to_bf16(acc[sq][0][i] * sc);
+      tile[16 * sq + hh][wave * 32 + 16 + m] = f32_to_bf16(acc[sq][1][i] * sc);
     }
+  __syncthreads();
+  // 16 SPB rows x 128 columns of bf16, 16 bytes per thread and step
+#pragma unroll
+  for (int it = 0; it < SPB; ++it) {
+    const int row = it * 16 + (tid >> 4), c8 = (tid & 15) * 8;
+    const int b = b0 + row / 16;
+    if (b < nv)
+      *(uint4*)(q_tilde + ((size_t)b * H + h0 + row % 16) * r + z * kQpCols + c8) =
+          *(const uint4*)&tile[row][c8];
   }
-  __syncthreads();  // cs ready
-  // alpha^q and the RoPE query: each wave takes 4 of the 16 heads.
-  for (int hh = wave; hh < 16; hh += 4) {
-    int h = h0 + hh;
-    prep_scalar_and_rope<uint16_t, uint16_t>(
-        q_c + ((size_t)b * H + h) * dc, q_rope + ((size_t)b * H + h) * dr, gqr, dc, dr, eps, tau,
-        qk_norm, cs, alpha_q + (size_t)b * H + h, q_rope_out + ((size_t)b * H + h) * dr);
+}
+
+template <int SPB, int KS>
+static void launch_qprep_bf16(const Cfg& c, int nv, int s_q, const void* q_c, const void* q_rope,
+                              const void* w_qabs, const float* gqr, const int32_t* seq_lens,
+                              const Paging& pg, const RopeFreq& rf, char* wsb, const WsLayout& ws,
+                              int32_t* status, hipStream_t s) {
+  qprep_mfma_kernel<SPB, KS><<<dim3((nv + SPB - 1) / SPB, c.G, c.r / kQpCols + 1), 256, 0, s>>>(
+      (const uint16_t*)q_c, (const uint16_t*)q_rope, (const uint16_t*)w_qabs, gqr, seq_lens, nv,
+      s_q, pg, c.H, c.r, c.dr, c.eps, c.tau, c.qk_norm, rf, (uint16_t*)(wsb + ws.q_tilde),
+      (float*)(wsb + ws.alpha_q), (uint16_t*)(wsb + ws.q_rope), status);
+}
+
+template <int SPB>
+static void launch_qprep_spb(const Cfg& c, int nv, int s_q, const void* q_c, const void* q_rope,
+                             const void* w_qabs, const float* gqr, const int32_t* seq_lens,
+                             const Paging& pg, const RopeFreq& rf, char* wsb, const WsLayout& ws,
+                             int32_t* status, hipStream_t s) {
+#define QP_CASE(K)                                                                            \
+  case K:                                                                                     \
+    launch_qprep_bf16<SPB, K>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws, \
+                              status, s);                                                     \
+    break;
+  switch (c.dc / 32) {
+    QP_CASE(1) QP_CASE(2) QP_CASE(3) QP_CASE(4) QP_CASE(5) QP_CASE(6) QP_CASE(7) QP_CASE(8)
+    default: break;
   }
+#undef QP_CASE
 }
 
 // Any shape, float storage: one workgroup per (b, h).
@@ -169,15 +236,13 @@ __global__ __launch_bounds__(256) void qprep_generic_kernel(
     const float* __restrict__ q_c, const float* __restrict__ q_rope,
     const float* __restrict__ w_qabs, const float* __restrict__ gqr,
     const int32_t* __restrict__ seq_lens, int s_q, const Paging pg, int H, int G, int r, int dc,
-    int dr, float eps, float tau, float base, int qk_norm, float* __restrict__ q_tilde,
+    int dr, float eps, float tau, int qk_norm, const RopeFreq rf, float* __restrict__ q_tilde,
     float* __restrict__ alpha_q, float* __restrict__ q_rope_out, int32_t* status) {
   const int b = blockIdx.x, h = blockIdx.y;  // b: virtual sequence (query row)
   const int g = (h * G) / H;
   const int L_cap = pg.capacity();
   const int L = virt_len(seq_lens, b, s_q, L_cap);
-  if (h == 0) check_pages(pg, b, s_q, L, status);
-  if (h == 0 && threadIdx.x == 0 && (L < 1 || L > L_cap) && status)
-    atomicOr(status, QKMLA_DEV_BAD_SEQ_LEN);
+  if (h == 0) check_sequence(pg, b, s_q, L, status);
   const int pos = clamp_pos(L, L_cap);
   const float* qc = q_c + ((size_t)b * H + h) * dc;
   const float* W = w_qabs + (size_t)g * r * dc;
@@ -186,13 +251,33 @@ __global__ __launch_bounds__(256) void qprep_generic_kernel(
     for (int j = 0; j < dc; ++j) acc += qc[j] * W[(size_t)i * dc + j];
     q_tilde[((size_t)b * H + h) * r + i] = acc;
   }
-  __shared__ float cs[256];  // d_r <= 256
-  rope_table(pos, dr, base, cs);
-  __syncthreads();
-  if (threadIdx.x < 64)
-    prep_scalar_and_rope<float, float>(qc, q_rope + ((size_t)b * H + h) * dr, gqr, dc, dr, eps,
-                                       tau, qk_norm, cs, alpha_q + (size_t)b * H + h,
-                                       q_rope_out + ((size_t)b * H + h) * dr);
+  if (threadIdx.x >= 64) return;
+  // alpha^q and the RoPE query, one wavefront (lane-strided over dims)
+  const int lane = threadIdx.x;
+  const float sl = tau * kLog2e;
+  const float* qr = q_rope + ((size_t)b * H + h) * dr;
+  float ss = 0.f, rs = 0.f;
+  if (qk_norm) {
+    for (int e = lane; e < dc; e += 64) ss += qc[e] * qc[e];
+    for (int e = lane; e < dr; e += 64) rs += qr[e] * qr[e];
+    ss = wave_sum(ss);
+    rs = wave_sum(rs);
+  }
+  const float aq = qk_norm ? 1.0f / sqrtf(ss / (float)dc + eps) : 1.0f;
+  if (lane == 0) alpha_q[(size_t)b * H + h] = aq * sl;
+  const float rscale = qk_norm ? 1.0f / sqrtf(rs / (float)dr + eps) : 1.0f;
+  float* qo = q_rope_out + ((size_t)b * H + h) * dr;
+  for (int pi = lane; pi < dr / 2; pi += 64) {
+    float x0 = qr[2 * pi], x1 = qr[2 * pi + 1];
+    if (qk_norm) {
+      x0 *= rscale * gqr[2 * pi];
+      x1 *= rscale * gqr[2 * pi + 1];
+    }
+    float c, sn;
+    rope_cos_sin_freq(pos, rf.f[pi], &c, &sn);
+    qo[2 * pi] = (x0 * c - x1 * sn) * sl;
+    qo[2 * pi + 1] = (x0 * sn + x1 * c) * sl;
+  }
 }
 
 hipError_t launch_qprep(const Cfg& c, int batch, int s_q, const void* q_c, const void* q_rope,
@@ -201,16 +286,17 @@ hipError_t launch_qprep(const Cfg& c, int batch, int s_q, const void* q_c, const
                         hipStream_t s) {
   char* wsb = (char*)workspace;
   const int nv = batch * s_q;  // virtual sequences, one per query row
+  const RopeFreq rf = rope_freq(c.dr, c.base);
   if (c.dtype == QKMLA_BF16) {
-    qprep_mfma_kernel<<<dim3(nv, c.G), 256, 0, s>>>(
-        (const uint16_t*)q_c, (const uint16_t*)q_rope, (const uint16_t*)w_qabs, gqr, seq_lens,
-        s_q, pg, c.H, c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm,
-        (uint16_t*)(wsb + ws.q_tilde), (float*)(wsb + ws.alpha_q), (uint16_t*)(wsb + ws.q_rope),
-        status);
+    // SPB sequences share a block's W~ loads once the batch gives enough blocks.
+    if (nv >= 16)
+      launch_qprep_spb<4>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws, status, s);
+    else
+      launch_qprep_spb<1>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws, status, s);
   } else {
     qprep_generic_kernel<<<dim3(nv, c.H), 256, 0, s>>>(
         (const float*)q_c, (const float*)q_rope, (const float*)w_qabs, gqr, seq_lens, s_q, pg, c.H,
-        c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.base, c.qk_norm, (float*)(wsb + ws.q_tilde),
+        c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.qk_norm, rf, (float*)(wsb + ws.q_tilde),
         (float*)(wsb + ws.alpha_q), (float*)(wsb + ws.q_rope), status);
   }
   return hipGetLastError();

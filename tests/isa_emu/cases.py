@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import re
 import sys
 import time
 import traceback
@@ -30,10 +31,28 @@ TOL = {"f32": dict(o=1e-5, o_lat=1e-5, lse=1e-5), "bf16": dict(o=2e-2, o_lat=2e-
 MERGE_HEADS = (0, 37, 127)
 
 
+def _merge_rows(name, grid, heads=MERGE_HEADS):
+    """Block rows (grid y) of merge_kernel<WPH> that hold the given heads: a
+    block holds max(4, WPH) / WPH heads."""
+    m = re.search(r"merge_kernelILi(\d+)E", name) or re.search(r"merge_kernel<(\d+)>", name)
+    wph = int(m.group(1))
+    per = max(4, wph) // wph
+    return sorted({h // per for h in heads if h // per < grid[1]})
+
+
+def _qprep_blocks(name, grid, seqs):
+    """Blocks of qprep_mfma_kernel<SPB, KS> (or the generic kernel, one
+    sequence per block) that hold the given sequences: x = sequence // SPB."""
+    m = re.search(r"qprep_mfma_kernelILi(\d+)E", name) or re.search(r"qprep_mfma_kernel<(\d+)", name)
+    spb = int(m.group(1)) if m else 1
+    xs = sorted({b // spb for b in seqs})
+    return [(x, y, z) for x in xs for y in range(grid[1]) for z in range(grid[2])]
+
+
 def _merge_heads_only(name, grid):
-    # the merge kernel has one block per (sequence, head, 128 dims): run three heads
+    # the merge kernel has one block per (sequence, head group): run three heads
     if "merge_kernel" in name:
-        return [(x, y, z) for z in range(grid[2]) for y in MERGE_HEADS if y < grid[1]
+        return [(x, y, z) for z in range(grid[2]) for y in _merge_rows(name, grid)
                 for x in range(grid[0])]
     return None
 
@@ -594,9 +613,9 @@ def bf16_max_batch(dev):
             assert grid[0] == n_wg, grid
             return [(hw, 0, 0) for hw in hws]
         if "qprep" in name:
-            return [(b, y, 0) for b in sorted(read) for y in range(grid[1])]
+            return _qprep_blocks(name, grid, read)
         if "merge_kernel" in name or "out_proj" in name:
-            ys = [y for y in MERGE_HEADS if y < grid[1]] if "merge" in name else range(grid[1])
+            ys = _merge_rows(name, grid) if "merge" in name else range(grid[1])
             return [(b, y, z) for b in whole for y in ys for z in range(grid[2])]
         return None
     inp = make_inputs(DSV3, lens, seed=510)
@@ -714,7 +733,7 @@ def _run_plan_ranges(dev, inp, ranges, n_wg, label, regen, hold_last=False):
             assert grid[0] == n_wg, grid
             return [(hw, 0, 0) for hw in hws]
         if "qprep" in name:
-            return [(b, y, 0) for b in read for y in range(grid[1])]
+            return _qprep_blocks(name, grid, read)
         if "merge_kernel" in name:
             return []  # the other ranges' partials are not computed
         return None
@@ -796,11 +815,11 @@ def bf16_headline_sequence(dev):
             assert grid[0] == n_wg, grid
             return [(hw, 0, 0) for hw in hws]
         if "qprep" in name:
-            return [(0, y, 0) for y in range(grid[1])]
+            return _qprep_blocks(name, grid, [0])
         if "merge_kernel" in name:
-            return [(0, y, z) for y in MERGE_HEADS for z in range(grid[2])]
+            return [(0, y, z) for y in _merge_rows(name, grid) for z in range(grid[2])]
         if "out_proj" in name:
-            return [(0, y, z) for y in range(grid[1]) for z in range(grid[2])]
+            return _qprep_blocks(name, grid, [0])
         return None
     inp = make_inputs(DSV3, lens, seed=530)
     keep = dev.group_filter

@@ -1423,15 +1423,21 @@ HANDLERS["ds_read2_b64"] = _dsread2(8, 8)
 HANDLERS["ds_read2st64_b64"] = _dsread2(8, 512)
 
 
-def _dswrite(nb):
+def _dswrite(nb, hi16=False):
+    """ds_write_b32/b64/b128 and the 16-bit forms (ds_write_b16 stores bits
+    15:0 of the data VGPR, ds_write_b16_d16_hi bits 31:16)."""
     def run(w, i):
         a, d = i.ops
         m = w.exec_mask()
         offs = _lds_addr(w, i, a)[m]
         lds_check(w, offs, nb, "w", i.text)
-        nd = nb // 4
-        vals = np.stack([w.vget(d, "b32", k)[m] for k in range(nd)], 1).astype("<u4")
-        b = vals.view(np.uint8).reshape(-1, nb)
+        if nb >= 4:
+            vals = np.stack([w.vget(d, "b32", k)[m] for k in range(nb // 4)], 1).astype("<u4")
+            b = vals.view(np.uint8).reshape(-1, nb)
+        else:
+            x = w.vget(d)[m]
+            x = (x >> 16) if hi16 else x
+            b = (x & 0xFFFF).astype("<u2").view(np.uint8).reshape(-1, 2)
         # lane order: later lanes win on overlap
         for k in range(len(offs)):
             w.wg.lds[offs[k]:offs[k] + nb] = b[k]
@@ -1465,6 +1471,8 @@ HANDLERS["ds_write2st64_b64"] = _dswrite2(8, 512)
 HANDLERS["ds_write_b32"] = _dswrite(4)
 HANDLERS["ds_write_b64"] = _dswrite(8)
 HANDLERS["ds_write_b128"] = _dswrite(16)
+HANDLERS["ds_write_b16"] = _dswrite(2)
+HANDLERS["ds_write_b16_d16_hi"] = _dswrite(2, hi16=True)
 
 
 @h("ds_add_f32")

@@ -67,26 +67,101 @@ def test_dsv3_bf16_small_parity(lens):
     _full_check(cfg, inp, f"dsv3 bf16 {lens}")
 
 
+@pytest.mark.parametrize("n_wg", [1, 3, 6])
+def test_dsv3_qk_multi_tile_segments(n_wg, monkeypatch):
+    """QK-norm mode through the whole split-KV pipeline: with 1, 3 or 5
+    workgroups, segments of 2 to 32 tiles (the three-stage loop turns over
+    several times), workgroups holding two or three segments, and the partial
+    slot of a workgroup's later segment; every head of every sequence against
+    the oracle."""
+    lens = (1000, 450, 200)
+    rows = ops.plan_segments(lens, max(lens), n_wg)
+    assert max(int(r[3] - r[2]) for r in rows) >= 7
+    assert max(np.bincount(rows[:, 0])) >= 2
+    if n_wg > 1:
+        assert (rows[:, 4] == 1).any() and (rows[:, 4] == 0).any()
+    inp = make_inputs(DSV3, lens, seed=315)
+    cfg = ops.Config.from_shape(DSV3)
+    monkeypatch.setenv("QKMLA_NUM_WG", str(n_wg))
+    _full_check(cfg, inp, f"dsv3 bf16 QK-norm, {n_wg} workgroups")
+
+
 def test_dsv3_bf16_plain_mode_parity():
     inp = make_inputs(DSV3, (5, 70, 400), seed=310)
     cfg = ops.Config.from_shape(DSV3, qk_norm=False)
     _full_check(cfg, inp, "dsv3 bf16 plain")
 
 
-def test_dsv3_bf16_plain_log_normal_restream():
-    """Plain MLA on latents scaled by up to 1e3: unnormalised logits overflow
-    the first tile's reference and segments are streamed again; o and o_lat
-    must still match, lse within a bound that scales with |lse|."""
-    inp = make_inputs(DSV3, (400, 140), seed=312, row_scale_log10_clip=3.0)
+def _plain_logit_error_bound(inp, cfg, b, heads, lat):
+    """Bound, from the inputs alone, on how far the kernel's plain-MLA logits
+    (natural log) can sit from the oracle's: W~ = W^UK^T and q~ = q^C W~ are
+    rounded to bf16 (2^-9 relative each), so the content logit of token t
+    moves by at most tau 2^-8 sum_j |c_tj| sum_i |q_i W_ji|; the RoPE query
+    and key are bf16 too.  Doubled for the fp32 sums and the P rounding.
+    Returns [heads][L]."""
+    from oracle import rope
+    G, H = cfg.n_groups, cfg.n_heads
+    c = np.abs(lat.astype(np.float64))
+    L = lat.shape[0]
+    kr = np.abs(rope(inp.k_rope_raw[b], np.arange(L), cfg.rope_base))
+    out = np.empty((len(heads), L))
+    for i, h in enumerate(heads):
+        a = np.abs(inp.w_uk[(h * G) // H].astype(np.float64)) @ np.abs(inp.q_c[b, h].astype(np.float64))
+        qr = np.abs(rope(inp.q_rope[b, h], L - 1, cfg.rope_base))
+        out[i] = cfg.tau * 2.0 ** -7 * (c @ a + kr @ qr)
+    return out
+
+
+def test_dsv3_bf16_plain_planted_restream(monkeypatch):
+    """Plain MLA, where logits are not bounded.  Every head h gets one planted
+    latent row, along its own content-query direction W^UK_g q^C_h, whose
+    logit for h is 100 nats; the rows sit in tiles that are not the first of
+    their split-KV segment.  For h that row's logit exceeds every other logit
+    of the sequence by more than the kernel's 2^64 reference margin, so the
+    segment holding it is streamed again with a raised reference.  Checked on
+    the oracle's own logits, with the kernel's logit error bound applied
+    against the test: the gap exceeds 64 ln 2 and the other rows' total weight
+    stays below 1e-6, so o, o_lat and lse are well posed; lse is compared
+    within the planted logit's own error bound."""
+    from oracle import explicit_logits
+    from mla_latent_decode_amd.inputs import round_bf16
+    lens, n_wg = (400, 300), 5
+    rows = ops.plan_segments(lens, max(lens), n_wg)
+    inp = make_inputs(DSV3, lens, seed=312)
     cfg = ops.Config.from_shape(DSV3, qk_norm=False)
-    os.environ["QKMLA_NUM_WG"] = "5"
-    try:
-        sess, o, o_lat, lse = _run(cfg, inp, "dsv3 bf16 plain, log-normal rows")
-    finally:
-        del os.environ["QKMLA_NUM_WG"]
+    H, G = cfg.n_heads, cfg.n_groups
+    rng = np.random.default_rng(313)
+    planted = {}
+    for b, L in enumerate(lens):
+        cand = [t for r in rows if r[1] == b for t in range((r[2] + 1) * 32, min(r[3] * 32, L))]
+        planted[b] = rng.choice(cand, size=H, replace=False)
+        for h, t in enumerate(planted[b]):
+            u = inp.w_uk[(h * G) // H].astype(np.float64) @ inp.q_c[b, h].astype(np.float64)
+            inp.latents[b][t] = round_bf16((u * (100.0 / cfg.tau) / (u @ u)).astype(np.float32))
+    bound_lse = {}
+    for b in range(len(lens)):
+        for g in range(G):
+            heads = heads_of([g], H, G)
+            lg = explicit_logits(inp.q_c, inp.q_rope, inp.latents[b], inp.k_rope_raw[b], inp.w_uk,
+                                 inp.gamma_q, inp.gamma_k, inp.gamma_q_rope, inp.gamma_k_rope,
+                                 b, g, qk_norm=False, tau=cfg.tau, base=cfg.rope_base)
+            err = _plain_logit_error_bound(inp, cfg, b, heads, inp.latents[b])
+            for i, h in enumerate(heads):
+                t = planted[b][h]
+                low = lg[i, t] - err[i, t]
+                others = np.delete(lg[i] + err[i], t)
+                assert low - others.max() > 64 * np.log(2.0), (b, h, low - others.max())
+                assert np.sum(np.exp(others - low)) < 1e-6, (b, h)
+                bound_lse[(b, h)] = err[i, t]
+    monkeypatch.setenv("QKMLA_NUM_WG", str(n_wg))
+    sess, o, o_lat, lse = _run(cfg, inp, "dsv3 bf16 plain, planted dominant rows")
     ref = oracle_decode(inp, cfg)
-    check_outputs(o, o_lat, lse, ref, "bf16", range(2), list(range(128)),
-                  "plain log-normal re-stream", lse_rel=2.0 ** -7)
+    check_outputs(o, o_lat, np.zeros_like(lse), {**ref, "lse": np.zeros_like(ref["lse"])}, "bf16",
+                  range(len(lens)), list(range(H)), "plain planted re-stream (o, o_lat)")
+    worst = max(abs(lse[b, h] - ref["lse"][b, h]) - e for (b, h), e in bound_lse.items())
+    print(f"planted rows: lse error bound up to {max(bound_lse.values()):.2f} nats; "
+          f"largest error beyond it {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]["lse"]
     assert int(sess.status.item()) == 0
 
 
@@ -199,6 +274,13 @@ def test_bad_append_position_sets_status_and_writes_nothing():
 
 
 def test_append_one_token_at_a_time_equals_bulk():
+    """Forty one-token appends (the decode step's path: alpha^k on the VALU
+    with fp32 W^UK) against one bulk append of the same rows (alpha^k on MFMA
+    with W^UK split into bf16 high and low parts): latent and RoPE rows are
+    bit-equal; alpha agrees to 2^-14 relative, far inside the 1e-3 bound both
+    meet against the oracle (the MFMA path carries W^UK to 16 significant
+    bits, the VALU path to 24, and they sum in different orders); a repeated
+    one-token append is bit-equal to the first."""
     inp = make_inputs(DSV3, (40,), seed=360)
     cfg = ops.Config.from_shape(DSV3)
     bulk = DecodeSession(cfg, inp)
@@ -211,7 +293,17 @@ def test_append_one_token_at_a_time_equals_bulk():
         pos = torch.tensor([t], dtype=torch.int32, device="cuda")
         ops.append(cfg, c, k, bulk.w_uk, bulk.gamma_k_rope, pos, lat, rope, alpha, bulk.status)
     torch.cuda.synchronize()
-    assert torch.equal(lat, bulk.lat) and torch.equal(rope, bulk.rope) and torch.equal(alpha, bulk.alpha)
+    assert torch.equal(lat, bulk.lat) and torch.equal(rope, bulk.rope)
+    rel = ((alpha[0, :40] - bulk.alpha[0, :40]).abs() / bulk.alpha[0, :40].abs()).max().item()
+    assert rel <= 2.0 ** -14, rel
+    again = alpha.clone()
+    for t in (0, 17, 39):
+        c = bulk.lat[:, t:t + 1].contiguous()
+        k = torch.from_numpy(inp.k_rope_raw[0][t:t + 1][None]).to("cuda", torch.bfloat16)
+        pos = torch.tensor([t], dtype=torch.int32, device="cuda")
+        ops.append(cfg, c, k, bulk.w_uk, bulk.gamma_k_rope, pos, lat, rope, again, bulk.status)
+    torch.cuda.synchronize()
+    assert torch.equal(again, alpha)
 
 
 def test_scale_invariance_is_bit_exact_on_gpu():

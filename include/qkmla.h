@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define QKMLA_ABI_VERSION 6
+#define QKMLA_ABI_VERSION 7
 
 typedef enum {
   QKMLA_OK = 0,
@@ -172,6 +172,31 @@ int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const 
                  int32_t cache_capacity, int32_t max_seq_len, void* workspace,
                  size_t workspace_bytes, float* o_lat, float* lse, int32_t* status,
                  void* stream);
+
+/*
+ * qkmla_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and outputs as qkmla_decode, without the workspace: the library
+ * uses its own scratch array of QKMLA_NOALLOC_SCRATCH_BYTES per GPU (static
+ * device memory, held by every GPU the library runs on until the process
+ * ends; its address is looked up once per device on the first call there).
+ * The call allocates nothing, neither device nor host memory.
+ *   Limit: a call whose qkmla_decode_workspace_size(cfg, batch, max_seq_len)
+ *   exceeds QKMLA_NOALLOC_SCRATCH_BYTES returns QKMLA_ERR_WORKSPACE (e.g. the
+ *   bf16 128-head layer fits up to a few hundred sequences); nothing is
+ *   enqueued.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ *   one GPU (on different streams, or from different host threads without
+ *   ordering) race and their outputs are undefined.  Calls enqueued in order
+ *   on one stream are safe.  Nothing in the scratch needs to start at zero.
+ */
+#define QKMLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int qkmla_decode_noalloc(const qkmla_config* cfg, int32_t batch, const void* q_c,
+                         const void* q_rope, const void* w_qabs, const float* gamma_q_rope,
+                         const void* latent_cache, const void* rope_cache,
+                         const float* alpha_cache, const int32_t* seq_lens,
+                         int32_t cache_capacity, int32_t max_seq_len, float* o_lat, float* lse,
+                         int32_t* status, void* stream);
 
 /*
  * Decode of s_q query rows per sequence (multi-token prediction,

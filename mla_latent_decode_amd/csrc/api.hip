@@ -508,6 +508,73 @@ int qkmla_decode(const qkmla_config* cfg, int32_t batch, const void* q_c, const 
                             workspace, workspace_bytes, o_lat, lse, status, stream);
 }
 
+// ---- decode without a caller workspace ------------------------------------------------
+// The workspace of qkmla_decode_noalloc: one array per GPU, placed by the code
+// object loader and held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol); each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is what the kernels receive.
+static __device__ __align__(256) char scratch[QKMLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// This device's address of `scratch`, or nullptr with the error recorded.
+void* scratch_address(int* st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_status(e, "decode_noalloc/hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    *st = fail(QKMLA_ERR_UNSUPPORTED, "decode_noalloc: device %d beyond the %d the library serves",
+               dev, kMaxScratchDevices);
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    *st = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "decode_noalloc/hipGetSymbolAddress");
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+}  // namespace
+
+int qkmla_decode_noalloc(const qkmla_config* cfg, int32_t batch, const void* q_c,
+                         const void* q_rope, const void* w_qabs, const float* gamma_q_rope,
+                         const void* latent_cache, const void* rope_cache,
+                         const float* alpha_cache, const int32_t* seq_lens,
+                         int32_t cache_capacity, int32_t max_seq_len, float* o_lat, float* lse,
+                         int32_t* status, void* stream) {
+  Cfg c;
+  int st = check_cfg(cfg, &c);
+  if (st) return st;
+  if (batch < 0 || cache_capacity < 1 || max_seq_len < 1 || max_seq_len > cache_capacity)
+    return fail(QKMLA_ERR_INVALID_ARG,
+                "decode_noalloc: need batch >= 0 and 1 <= max_seq_len (%d) <= cache_capacity (%d)",
+                max_seq_len, cache_capacity);
+  if (batch == 0) return ok();
+  if (batch > kMaxBatch)
+    return fail(QKMLA_ERR_UNSUPPORTED, "decode_noalloc: batch above %d", kMaxBatch);
+  const size_t need = qkmla_decode_workspace_size(cfg, batch, max_seq_len);
+  if (need == 0) return QKMLA_ERR_INVALID_ARG;  // message set by the size query
+  if (need > (size_t)QKMLA_NOALLOC_SCRATCH_BYTES)
+    return fail(QKMLA_ERR_WORKSPACE,
+                "decode_noalloc: this batch needs %zu bytes of workspace, above the %zu-byte "
+                "scratch array; use qkmla_decode with a caller workspace",
+                need, (size_t)QKMLA_NOALLOC_SCRATCH_BYTES);
+  void* ws = scratch_address(&st);
+  if (!ws) return st;
+  return decode_impl(c, batch, 1, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, rope_cache,
+                     alpha_cache, seq_lens, contiguous_paging(batch, cache_capacity), max_seq_len,
+                     ws, (size_t)QKMLA_NOALLOC_SCRATCH_BYTES, o_lat, lse, status, stream);
+}
+
 // ---- training / prefill -------------------------------------------------------------
 // Packed form: n_seq sequences over n_rows rows, each at most max_len long.
 static int check_train(const qkmla_config* cfg, int64_t n_seq, int64_t n_rows, int64_t max_len,

@@ -72,6 +72,7 @@ def _load():
         "qkmla_decode": (I32, [C, I32, P, P, P, P, P, P, P, P, I32, I32, P, SZ, P, P, P, P]),
         "qkmla_decode_multi": (I32, [C, I32, I32, P, P, P, P, P, P, P, P, I32, I32, P, SZ, P, P,
                                      P, P]),
+        "qkmla_decode_noalloc": (I32, [C, I32, P, P, P, P, P, P, P, P, I32, I32, P, P, P, P]),
         "qkmla_append_paged": (I32, [C, I32, I32, P, P, P, P, P, PG, P, P, P, P, P]),
         "qkmla_decode_paged": (I32, [C, I32, I32, P, P, P, P, P, P, P, P, PG, I32, P, SZ, P, P,
                                      P, P]),
@@ -290,6 +291,28 @@ def decode(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, rope_ca
         _ptr(o_lat, (B, H, r), torch.float32, "o_lat"),
         _ptr(lse, (B, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
         _stream()), "qkmla_decode")
+    return o_lat
+
+
+def decode_noalloc(cfg: Config, q_c, q_rope, w_qabs, gamma_q_rope, latent_cache, rope_cache,
+                   alpha_cache, seq_lens, max_seq_len: int, o_lat, lse=None, status=None):
+    """qkmla_decode without a workspace argument (the library's per-GPU scratch
+    array); o_lat must be given, so the call allocates nothing."""
+    B = q_c.shape[0]
+    L_cap = latent_cache.shape[1]
+    H, r, dt = cfg.n_heads, cfg.latent_rank, cfg.torch_dtype
+    _check(_lib.qkmla_decode_noalloc(
+        ctypes.byref(cfg.c()), B, _ptr(q_c, (B, H, cfg.head_dim), dt, "q_c"),
+        _ptr(q_rope, (B, H, cfg.rope_dim), dt, "q_rope"),
+        _ptr(w_qabs, (cfg.n_groups, r, cfg.head_dim), dt, "w_qabs"),
+        _ptr(gamma_q_rope, (cfg.rope_dim,), torch.float32, "gamma_q_rope"),
+        _ptr(latent_cache, (B, L_cap, r), dt, "latent_cache"),
+        _ptr(rope_cache, (B, L_cap, cfg.rope_dim), dt, "rope_cache"),
+        _ptr(alpha_cache, (B, L_cap, cfg.n_groups), torch.float32, "alpha_cache"),
+        _ptr(seq_lens, (B,), torch.int32, "seq_lens"), L_cap, max_seq_len,
+        _ptr(o_lat, (B, H, r), torch.float32, "o_lat"),
+        _ptr(lse, (B, H), torch.float32, "lse"), _ptr(status, (1,), torch.int32, "status"),
+        _stream()), "qkmla_decode_noalloc")
     return o_lat
 
 

@@ -37,7 +37,7 @@ def _ops():
 
 def test_abi_version_and_status_strings():
     ops = _ops()
-    assert ops.abi_version() == 6
+    assert ops.abi_version() == 7
     assert ops._lib.qkmla_status_string(0) == b"ok"
     assert ops._lib.qkmla_status_string(3) == b"workspace too small"
 

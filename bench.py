@@ -278,21 +278,21 @@ def pmc_workload(steps=5, cid=1):
 
 
 def _pmc_per_dispatch(csv_path, counter):
-    """{kernel name: mean counter value per dispatch} from a rocprofv3
-    counter-collection CSV (columns Dispatch_Id, Kernel_Name, Counter_Name,
-    Counter_Value; several rows of one dispatch are summed)."""
+    """{kernel name: [counter value of each dispatch, in dispatch order]} from a
+    rocprofv3 counter-collection CSV (columns Dispatch_Id, Kernel_Name,
+    Counter_Name, Counter_Value; several rows of one dispatch are summed)."""
     import csv
     per = {}
     with open(csv_path, newline="") as f:
         for row in csv.DictReader(f):
             if row.get("Counter_Name", "").split("[")[0] != counter:
                 continue
-            key = (row["Kernel_Name"], row.get("Dispatch_Id", ""))
+            key = (row["Kernel_Name"], int(row.get("Dispatch_Id", "0") or 0))
             per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
     out = {}
-    for (name, _), v in per.items():
+    for (name, _), v in sorted(per.items(), key=lambda kv: kv[0][1]):
         out.setdefault(name, []).append(v)
-    return {k: sum(v) / len(v) for k, v in out.items()}
+    return out
 
 
 def _is_qk_splitkv(name):
@@ -312,9 +312,12 @@ def traffic_from_pmc(fetch_csv, write_csv, workload, algorithmic_bytes):
         if len(names) != 1:
             raise ValueError(f"expected one {what} kernel, found {names}")
         return d[names[0]]
+    # the calibration copies are the workload's last three copy dispatches
+    # (the cache fill before the decode steps also copies, in other sizes)
     is_copy = lambda k: "copy" in k.lower() and "decode" not in k  # noqa: E731
-    f_dec, w_dec = pick(fetch, _is_qk_splitkv, "split-KV"), pick(write, _is_qk_splitkv, "split-KV")
-    f_cp, w_cp = pick(fetch, is_copy, "copy"), pick(write, is_copy, "copy")
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    f_dec, w_dec = mean(pick(fetch, _is_qk_splitkv, "split-KV")), mean(pick(write, _is_qk_splitkv, "split-KV"))
+    f_cp, w_cp = mean(pick(fetch, is_copy, "copy")[-3:]), mean(pick(write, is_copy, "copy")[-3:])
     kf, kw = COPY_BYTES / (f_cp * 1024.0), COPY_BYTES / (w_cp * 1024.0)
     hbm = f_dec * 1024.0 * kf + w_dec * 1024.0 * kw
     return {workload: {"hbm_bytes_per_launch": round(hbm), "fetch_KiB": f_dec, "write_KiB": w_dec,
@@ -581,9 +584,11 @@ def _progress(out, name):
     print(f"[bench] {name} {out[name]}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cid, budget_s=15.0):
-    """The fp64 oracle on the host: whole sequences of the same workload, one at
-    a time, until about `budget_s` seconds of CPU work; returns its cache GB/s."""
+def cpu_baseline(cid, budget_s=15.0, max_tokens=65536):
+    """The fp64 oracle on the host: sequences of the same workload (each cut to
+    at most `max_tokens` tokens, so one sequence of a long-context workload
+    stays within the budget), one at a time, until about `budget_s` seconds of
+    CPU work; returns its cache GB/s."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -594,6 +599,7 @@ def cpu_baseline(cid, budget_s=15.0):
     lengths = _lengths(w)
     done_tokens, elapsed, n, t_alpha = 0, 0.0, 0, 0.0
     for i, L in enumerate(lengths):
+        L = min(L, max_tokens)
         inp = make_inputs(w.shape, [L], seed=4000 + i, row_scale_log10_clip=w.row_scale_log10_clip)
         t0 = time.perf_counter()
         oracle.explicit_decode(inp.q_c, inp.q_rope, inp.latents, inp.k_rope_raw, inp.w_uk, inp.w_uv,
@@ -620,8 +626,9 @@ def cpu_baseline(cid, budget_s=15.0):
         pass
     gbps = done_tokens * cache_bytes_per_token(w.shape, True) / elapsed / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {len(lengths)} sequences ({done_tokens} cached tokens) of the same "
-                      f"workload, fp64 explicit form, {elapsed:.1f} s",
+            "sample": f"{n} of {len(lengths)} sequences ({done_tokens} cached tokens, each cut to "
+                      f"at most {max_tokens}) of the same workload, fp64 explicit form, "
+                      f"{elapsed:.1f} s",
             "us_per_step_extrapolated": round(elapsed / done_tokens * sum(lengths) * 1e6, 1),
             "alpha_append_us_per_step_extrapolated":
                 round(t_alpha / done_tokens * sum(lengths) * 1e6, 1),
@@ -633,7 +640,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, help="headline workload (1-4)")
+    ap.add_argument("--workload", type=int, default=3, help="headline workload (1-4)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-next", action="store_true",
@@ -653,9 +660,14 @@ def main():
     args = ap.parse_args()
     if args.traffic:
         from mla_latent_decode_amd.inputs import WORKLOADS
-        t = traffic_from_pmc(args.traffic[0], args.traffic[1], WORKLOADS[1].name,
+        t = traffic_from_pmc(args.traffic[0], args.traffic[1], WORKLOADS[args.workload].name,
                              int(args.traffic[2]))
-        json.dump(t, open(TRAFFIC_FILE, "w"), indent=1)
+        try:
+            prev = json.load(open(TRAFFIC_FILE))
+        except (OSError, ValueError):
+            prev = {}
+        prev.update(t)
+        json.dump(prev, open(TRAFFIC_FILE, "w"), indent=1)
         print(json.dumps(t))
         return
     if args.gpus != 1:
@@ -720,7 +732,7 @@ def main():
     print(f"[bench] read probe {probe}", file=sys.stderr, flush=True)
     if not args.no_sweep:
         sweep = []
-        for cid in (2, 3, 4):
+        for cid in (1, 2, 3, 4):
             if cid == args.workload:
                 continue
             _b, r, *_ = measure(cid, max(10, args.steps // 2), max(3, args.warmup // 2),

@@ -11,7 +11,7 @@
 // alpha^q_h (with the softmax scale and log2(e)) is already folded into q~ by
 // the query preparation, so the row-column scaling is one FMA per logit.
 //   softmax weights over t, O[h,:] += sum_t p[t,h] c_t       (K = 32 tokens, MFMA)
-// Plain MLA (QKN = false) uses one K = r + d_r accumulator, no alpha.
+// Plain MLA (QKN = false) runs the same two sums and adds them, with no alpha.
 //
 // Shape: r = 512, d_r = 64, 32 heads per wavefront, NW = H/32 wavefronts per
 // workgroup (all heads of a token are handled by one workgroup, so every
@@ -246,41 +246,86 @@ __device__ __forceinline__ void issue_tile(const Seq& sq, const Paging& pg, int 
 // the software pipelines below issue in the order they are written.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-constexpr int kQkSteps = kR / 16 + kDr / 16;  // 36 K-steps of 16 (latent, then RoPE)
-constexpr int kQkAhead = 4;                    // LDS reads in flight ahead of the QK MFMAs
-constexpr int kPvSteps = 2 * (kR / 32);        // 32: 2 token halves x 16 dim blocks
-constexpr int kPvAhead = 3;                    // C^T operands in flight ahead of the PV MFMAs
+constexpr int kRopeSteps = kDr / 16;            // 4 K-steps over the RoPE dims
+constexpr int kQkSteps = kR / 16 + kRopeSteps;  // 36 K-steps of 16 (RoPE, then latent)
+constexpr int kQkAhead = 4;                     // LDS reads in flight ahead of the QK MFMAs
+constexpr int kPvSteps = 2 * (kR / 32);         // 32: 2 token halves x 16 dim blocks
+constexpr int kPvAhead = 3;                     // C^T operands in flight ahead of the PV MFMAs
 
-// One tile of a segment: wait for its loads, prefetch the tile two ahead into
-// the stage consumed by the previous step, then logits, softmax weights and
-// the P.C accumulation.  i: tile index within the segment (nt tiles), staged
-// in buffer S = i % 3; `tile0` is the segment's first tile in its sequence.
-// Every step waits for its own tile only (the tile after it stays in flight)
-// and prefetches the tile two ahead, clamped to the segment's last tile: near
-// the end of a segment the prefetch re-reads a tile the L2 still holds, into a
-// stage nobody reads.  Keeping the wait and the prefetch free of branches lets
-// the compiler's wait-count insertion track each stage exactly; with
-// branches it merges the paths conservatively and then waits for every load
-// in flight before reading a tile.
-template <bool QKN, int NW, int S>
-__device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, const Paging& pg, int G,
-                                          int tile0, int i, int nt, int wave, int lane, int g) {
-  if (i + 1 < nt) wait_vmcnt<TileLoads<QKN, NW>::total>();
-  else wait_vmcnt<0>();
-  block_sync();  // the tile is in LDS for every wave; stage (S+2)%3 is free
-  if constexpr (S != 0)
-    if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, pg, G, tile0 + i + 2, wave, lane);
+// Softmax weights of one tile (exp2 domain), computed a few instructions at a
+// time between the MFMAs of the next tile's logits.  In: lg, the lane's 16
+// logits (reg j: token 8(j/4) + 4hf + j%4 of its head), row-column scaled and
+// masked.  Out: pb, the bf16 weights p = 2^(lg - m_ref) as the B operand of
+// P.C, and the running sum of the weights as rounded.
+struct Soft {
+  float lg[16];
+  float mx[4];
+  float e[16];
+  bf16x8 pb[2];
+};
+
+// Step s (0 <= s < kQkSteps) of the softmax schedule.  The first tile of a
+// segment sets the per-head reference m_ref (the only place where the two
+// halves of a head, lanes l and l ^ 32, exchange their maxima); a later tile
+// only checks its own lanes against it: a logit more than 2^kOverflowLog2
+// above the reference makes the workgroup stream the segment again with the
+// reference raised.
+// Each result is pinned where it is computed by an empty asm that uses it:
+// otherwise the compiler sinks the exponentials and conversions below the
+// MFMAs, next to their use in P.C, and nothing overlaps.
+__device__ __forceinline__ void soft_step(int s, Wave& w, Soft& sf, int wave) {
+  if (s < 4) {
+    sf.mx[s] = fmaxf(fmaxf(sf.lg[4 * s], sf.lg[4 * s + 1]), fmaxf(sf.lg[4 * s + 2], sf.lg[4 * s + 3]));
+    asm volatile("" : "+v"(sf.mx[s]));
+  } else if (s == 4) {
+    const float mt = fmaxf(fmaxf(sf.mx[0], sf.mx[1]), fmaxf(sf.mx[2], sf.mx[3]));
+    if (!w.have_ref) {  // first tile of the segment: the per-head reference
+      w.m_ref = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      w.have_ref = true;
+    }
+    sf.mx[0] = mt;
+  } else if (s == 5) {
+    if (__ballot(sf.mx[0] > w.m_ref + kOverflowLog2) != 0) {
+      w.m_ref = fmaxf(w.m_ref, fmaxf(sf.mx[0], __shfl_xor(sf.mx[0], 32, 64)));
+      lds_restart[wave] = 1;
+    }
+  } else if (s < 22) {
+    const int j = s - 6;
+    sf.e[j] = __builtin_amdgcn_exp2f(sf.lg[j] - w.m_ref);
+    asm volatile("" : "+v"(sf.e[j]));
+  } else if (s < 30) {
+    const int k = s - 22;  // weights 2k, 2k + 1
+    sf.pb[k >> 2][2 * (k & 3)] = (__bf16)sf.e[2 * k];
+    sf.pb[k >> 2][2 * (k & 3) + 1] = (__bf16)sf.e[2 * k + 1];
+    if ((k & 3) == 3) asm volatile("" : "+v"(sf.pb[k >> 2]));
+  } else if (s < 32) {
+    // l sums the weights as rounded for P.C: each dword holds two bf16,
+    // whose fp32 values are the dword's high half and its low half shifted up
+    const uint32_t* u = (const uint32_t*)&sf.pb[s - 30];
+    float ls = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      ls += __uint_as_float(u[d] << 16) + __uint_as_float(u[d] & 0xFFFF0000u);
+    w.l_run += ls;
+    asm volatile("" : "+v"(w.l_run));
+  }
+}
+
+// Logits of the tile in stage S: S^T[32 tokens][32 heads] on MFMA, K-steps
+// 0..3 over the 64 RoPE dims into sr, then 32 over the latent into sc (the
+// A operand of step s + kQkAhead is read while step s multiplies); then the
+// row-column scaling l = S_c * alpha^k + S_r (QK norm) or S_c + S_r (plain
+// MLA), and the mask of a sequence's last tile.  With SOFT, the softmax of
+// the previous tile (sf) runs between the MFMAs.  The RoPE sum is finished
+// first and moved to VGPRs, so the latent chain reuses its accumulator
+// registers: every MFMA result lands in AGPRs, which the O^T accumulator
+// otherwise fills, so each extra live accumulator costs moves.
+template <bool QKN, bool SOFT, int S>
+__device__ __forceinline__ void qk_tile(Wave& w, Soft& sf, float* lg_out, bool last, int tail,
+                                        int wave, int lane, int g) {
   const char* st = stage_buf<S>();
   const int hf = lane >> 5;
   const int m = lane & 31;
-
-  // ---- logits S^T[32 tokens][32 heads] ----
-  // K-steps 0..3 read 16 RoPE dims of token m, steps 4..35 16 latent dims; the
-  // A operand of step s + kQkAhead is read while step s multiplies.  The RoPE
-  // sum is finished first and moved to VGPRs, so the latent chain reuses its
-  // accumulator registers: every MFMA result lands in AGPRs, which the O^T
-  // accumulator otherwise fills, so each extra live accumulator costs moves.
-  constexpr int kRopeSteps = kDr / 16;
   const char* row = st + m * kLatRow + hf * 16;
   const char* rrow = st + kLatBytes + (32 * hf + m) * 16;
   auto qk_a = [&](int s) -> const bf16x8* {
@@ -302,94 +347,59 @@ __device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, const Paging& 
 #pragma unroll
   for (int s = 0; s < kQkSteps; ++s) {
     fence();
-    if (QKN && s == kRopeSteps) asm volatile("" : "+v"(sr));  // RoPE sum to VGPRs
-    if (s < kRopeSteps) {
-      if constexpr (QKN) sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], qr[s], sr, 0, 0, 0);
-      else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], qr[s], sc, 0, 0, 0);
-    } else {
+    if (s == kRopeSteps) asm volatile("" : "+v"(sr));  // RoPE sum to VGPRs
+    if (s < kRopeSteps)
+      sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], qr[s], sr, 0, 0, 0);
+    else
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], w.qt[s - kRopeSteps], sc, 0, 0, 0);
-    }
     if (s + kQkAhead < kQkSteps) av[s % kQkAhead] = *qk_a(s + kQkAhead);
     else if (QKN && s + kQkAhead - kQkSteps < 4) {
       const int q = s + kQkAhead - kQkSteps;  // alpha^k of the lane's tokens 8q+4hf..+3
       ak[q] = *(const f32x4*)(al + 8 * q);
     }
+    if constexpr (SOFT) soft_step(s, w, sf, wave);
   }
   fence();
+  // reg j holds token 8*(j/4) + 4*hf + j%4
+  if constexpr (QKN) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lg_out[j] = sc[j] * ak[j >> 2][j & 3] + sr[j];
+  } else {  // plain MLA: the same two sums, without the row-column scaling
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lg_out[j] = sc[j] + sr[j];
+  }
+  // Only a sequence's last tile has rows to mask (tail: its rows inside the
+  // sequence, wave-uniform), and the uniform test keeps the mask code off the
+  // other tiles' path.
+  if (last) {
+    const int thr = tail - 4 * hf;  // token 4*hf + c is real iff c < thr
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (8 * (j >> 2) + (j & 3) >= thr) lg_out[j] = -INFINITY;
+  }
+}
 
-  // Prefetch the tile two ahead: right after the barrier in steps 1 and 2,
-  // after the QK reads in step 0.  At step 0 the compiler cannot prove which
-  // stages still have loads in flight (the loop is also left after step 0 or
-  // step 1) and waits for all of them before the first read; issued late, the
-  // prefetch is not among them, and the tile that is has been in flight for a
-  // whole step.
-  if constexpr (S == 0)
-    if (i + 2 < nt) issue_tile<QKN, NW, (S + 2) % kStages>(sq, pg, G, tile0 + i + 2, wave, lane);
-
-  // The first C^T operands of P.C do not depend on the softmax: read them now.
-  // lane (in its 16-lane group): token 4*hf + (s16>>2) of the 16-token step,
-  // 4 dims at 32*mb + 16*dblk + 4*(s16&3); step k = 16*ks + mb.
+// O^T[512 dims][32 heads] += C^T . P^T over the tile in stage S, with B = P
+// straight from the softmax registers (token order permuted to match) and
+// A = C^T from ds_read_b64_tr_b16: lane (in its 16-lane group) reads token
+// 4*hf + (s16>>2) of the 16-token step, 4 dims at 32*mb + 16*dblk +
+// 4*(s16&3); step k = 16*ks + mb.
+template <int S>
+__device__ __forceinline__ void pv_tile(Wave& w, const bf16x8 (&pb)[2], int lane) {
+  const char* st = stage_buf<S>();
+  const int hf = lane >> 5;
   const int s16 = lane & 15, dblk = (lane >> 4) & 1;
   const char* pvb = st + (4 * hf + (s16 >> 2)) * kLatRow + 32 * dblk + 8 * (s16 & 3);
   auto pv_a = [&](int k) -> const char* {
     return pvb + (16 * (k / (kR / 32))) * kLatRow + 64 * (k % (kR / 32));
   };
   bf16x4 plo[kPvAhead], phi[kPvAhead];
+  fence();
 #pragma unroll
   for (int k = 0; k < kPvAhead; ++k) {
     plo[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k)));
     phi[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k) + 8 * kLatRow));
   }
-  fence();
-
-  // ---- row-column scaling, mask, softmax weights (exp2 domain) ----
-  // reg j holds token 8*(j/4) + 4*hf + j%4
-  float lg[16];
-  if constexpr (QKN) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) lg[j] = sc[j] * ak[j >> 2][j & 3] + sr[j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) lg[j] = sc[j];
-  }
-  // Rows of this tile inside the sequence (wave-uniform): only a sequence's
-  // last tile has rows to mask, and the uniform test keeps the mask code off
-  // the other tiles' path.
-  if (tile0 + i == sq.last_tile) {
-    const int tail = __builtin_amdgcn_readfirstlane(sq.L - (tile0 + i) * kTile);
-    const int thr = tail - 4 * hf;  // token 4*hf + c is real iff c < thr
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (8 * (j >> 2) + (j & 3) >= thr) lg[j] = -INFINITY;
-  }
-  float mt = lg[0];
-#pragma unroll
-  for (int j = 1; j < 16; ++j) mt = fmaxf(mt, lg[j]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  if (!w.have_ref) {  // the first tile of the segment sets the per-head reference
-    w.m_ref = mt;
-    w.have_ref = true;
-  }
-  if (__ballot(mt > w.m_ref + kOverflowLog2) != 0) {
-    w.m_ref = fmaxf(w.m_ref, mt);
-    lds_restart[wave] = 1;
-  }
-  bf16x8 pb[2];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(lg[j] - w.m_ref);
-  // l sums the weights as rounded for P.C: each dword holds two bf16, whose
-  // fp32 values are the dword's high half and its low half shifted up.
-  float ls = 0.f;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t* u = (const uint32_t*)&pb[k];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      ls += __uint_as_float(u[d] << 16) + __uint_as_float(u[d] & 0xFFFF0000u);
-  }
-  w.l_run += ls;
-
-  // ---- O^T[512 dims][32 heads] += C^T . P^T ----
 #pragma unroll
   for (int k = 0; k < kPvSteps; ++k) {
     fence();
@@ -405,6 +415,36 @@ __device__ __forceinline__ void tile_step(Wave& w, const Seq& sq, const Paging& 
     }
   }
   fence();
+}
+
+// One step of the software pipeline over a segment's nt tiles, tile i in
+// stage i % 3 (SP), tile i + 1 in SQ, the stage of tile i - 1 free (SN):
+//   wait for tile i + 1 and synchronise the workgroup (every wave is past
+//   tile i - 1, so stage SN is free), prefetch tile i + 2 into SN; the logits
+//   of tile i + 1 on MFMA with the softmax of tile i between them; then the
+//   P.C of tile i.  lg holds the logits of tile i on entry and of tile i + 1
+//   on exit.  The prefetch of tile 2 is issued by the segment's first step
+//   (stage 2 is free from the start), so step 0 does not issue one.
+template <bool QKN, int NW, int SP, int SQ, int SN>
+__device__ __forceinline__ void pipe_step(Wave& w, Soft& sf, const Seq& sq, const Paging& pg,
+                                          int G, int tile0, int i, int nt, int wave, int lane,
+                                          int g) {
+  wait_vmcnt<0>();
+  block_sync();
+  if (i >= 1 && i + 2 < nt) issue_tile<QKN, NW, SN>(sq, pg, G, tile0 + i + 2, wave, lane);
+  if (i + 1 < nt) {
+    const int t = tile0 + i + 1;
+    const bool last = t == sq.last_tile;
+    const int tail = last ? __builtin_amdgcn_readfirstlane(sq.L - t * kTile) : kTile;
+    float lg_next[16];
+    qk_tile<QKN, true, SQ>(w, sf, lg_next, last, tail, wave, lane, g);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sf.lg[j] = lg_next[j];
+  } else {
+#pragma unroll
+    for (int s = 0; s < kQkSteps; ++s) soft_step(s, w, sf, wave);
+  }
+  pv_tile<SP>(w, sf.pb, lane);
 }
 
 template <bool QKN, int NW>
@@ -471,10 +511,19 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) w.O[ii][j] = 0.f;
       w.l_run = 0.f;
+      Soft sf;
+      {  // the first tile's logits; stage 2 is free, so tile 2 goes out now
+        wait_vmcnt<0>();
+        block_sync();
+        if (nt > 2) issue_tile<QKN, NW, 2>(sq, a.pg, a.G, tile0 + 2, wave, lane);
+        const bool last = tile0 == sq.last_tile;
+        const int tail = last ? __builtin_amdgcn_readfirstlane(sq.L - tile0 * kTile) : kTile;
+        qk_tile<QKN, false, 0>(w, sf, sf.lg, last, tail, wave, lane, g);
+      }
       for (int i = 0; i < nt; i += kStages) {
-        tile_step<QKN, NW, 0>(w, sq, a.pg, a.G, tile0, i, nt, wave, lane, g);
-        if (i + 1 < nt) tile_step<QKN, NW, 1>(w, sq, a.pg, a.G, tile0, i + 1, nt, wave, lane, g);
-        if (i + 2 < nt) tile_step<QKN, NW, 2>(w, sq, a.pg, a.G, tile0, i + 2, nt, wave, lane, g);
+        pipe_step<QKN, NW, 0, 1, 2>(w, sf, sq, a.pg, a.G, tile0, i, nt, wave, lane, g);
+        if (i + 1 < nt) pipe_step<QKN, NW, 1, 2, 0>(w, sf, sq, a.pg, a.G, tile0, i + 1, nt, wave, lane, g);
+        if (i + 2 < nt) pipe_step<QKN, NW, 2, 0, 1>(w, sf, sq, a.pg, a.G, tile0, i + 2, nt, wave, lane, g);
       }
       block_sync();
       if (!(lds_restart[0] | lds_restart[1] | lds_restart[2] | lds_restart[3])) break;

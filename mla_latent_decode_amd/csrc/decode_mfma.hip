@@ -164,6 +164,17 @@ struct Wave {
   bool have_ref;
 };
 
+// Buffer descriptor (raw: stride 0) for `bytes` bytes from `base`.  Dword 3
+// sets the 32-bit data format that untyped gfx9 buffer loads require.  The
+// tile loads go through buffer instructions rather than global ones: the
+// compiler counts a global load into LDS as a possible LDS access of unknown
+// order, and while one is in flight it turns every LDS wait into a full drain,
+// which would stall the MFMA pipelines on each wait.
+constexpr int kBufDword3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufDword3);
+}
+
 // Issue the direct global->LDS loads of tile `tile` (of its sequence) into
 // stage S.  LDS layout of a stage:
 //   latent: token-major rows of kLatRow bytes (1 KB of data + 48 B pad); one
@@ -208,36 +219,40 @@ __device__ __forceinline__ void issue_tile(const Seq& sq, const Paging& pg, int 
     asm volatile("" ::: "memory");
     last = sq.L - 1 - t0;
   }
-  const char* latb = sq.lat + prow0 * (kR * 2);
+  // One buffer descriptor per part of the tile, based at the tile's first row
+  // and sized to the tile; the row and lane offsets go in the scalar and
+  // vector offset fields.
+  const __amdgpu_buffer_rsrc_t lat_rsrc =
+      tile_rsrc(sq.lat + prow0 * (kR * 2), kTile * kR * 2);
 #pragma unroll
   for (int i = 0; i < TileLoads<QKN, NW>::lat; ++i) {
     const int tr = wave + i * NW;
-    const char* rowp = latb + (size_t)min(tr, last) * (kR * 2);
-    asm volatile("" : "+s"(rowp));  // scalar row base, then the lane offset
-    __builtin_amdgcn_global_load_lds(QK_GLB(void, rowp + lane16),
-                                     QK_LDS(void, st + tr * kLatRow), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rsrc, QK_LDS(void, st + tr * kLatRow), 16,
+                                             (int)lane16, min(tr, last) * (kR * 2), 0, 0);
   }
   const int t = lane & 31;
   const uint32_t rr = (uint32_t)min(t, last);
-  const char* ropeb = sq.rope + prow0 * (kDr * 2);
+  const __amdgpu_buffer_rsrc_t rope_rsrc =
+      tile_rsrc(sq.rope + prow0 * (kDr * 2), kTile * kDr * 2);
   const uint32_t rope_off = rr * (kDr * 2) + ((uint32_t)(lane >> 5) << 4);
 #pragma unroll
   for (int i = 0; i < TileLoads<QKN, NW>::rope; ++i) {
     const int blk2 = wave + i * NW;  // chunks 2*blk2, 2*blk2+1
-    __builtin_amdgcn_global_load_lds(QK_GLB(void, ropeb + blk2 * 32 + rope_off),
-                                     QK_LDS(void, st + kLatBytes + blk2 * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rsrc, QK_LDS(void, st + kLatBytes + blk2 * 1024),
+                                             16, (int)rope_off, blk2 * 32, 0, 0);
   }
   if constexpr (QKN) {
-    const char* alphab = sq.alpha + prow0 * (G * 4);
+    const __amdgpu_buffer_rsrc_t alpha_rsrc =
+        tile_rsrc(sq.alpha + prow0 * (G * 4), kTile * G * 4);
     const uint32_t a_off = rr * (uint32_t)(G * 4);
 #pragma unroll
     for (int i = 0; i < TileLoads<QKN, NW>::alpha; ++i) {
       const int blk2 = wave + i * NW;  // groups 2*blk2, 2*blk2+1
       int g = 2 * blk2 + (lane >> 5);
       g = g < G ? g : G - 1;
-      __builtin_amdgcn_global_load_lds(QK_GLB(void, alphab + a_off + (uint32_t)(g * 4)),
-                                       QK_LDS(void, st + kLatBytes + kRopeBytes + blk2 * 256),
-                                       4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          alpha_rsrc, QK_LDS(void, st + kLatBytes + kRopeBytes + blk2 * 256), 4,
+          (int)(a_off + (uint32_t)(g * 4)), 0, 0, 0);
     }
   }
 }

@@ -140,7 +140,7 @@ def _split_top(s: str) -> List[str]:
 
 _MOD = re.compile(r"^(offset|offset0|offset1|bitop3|dst_sel|dst_unused|src0_sel|src1_sel|"
                   r"op_sel|op_sel_hi|cbsz|abid|blgp|neg_lo|neg_hi):(.+)$")
-_FLAGS = {"sc0", "sc1", "nt", "glc", "slc", "dlc", "clamp", "lds", "gds"}
+_FLAGS = {"sc0", "sc1", "nt", "glc", "slc", "dlc", "clamp", "lds", "gds", "offen", "idxen"}
 
 
 def parse_inst(line: str, lineno: int) -> Inst:

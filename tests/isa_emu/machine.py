@@ -28,6 +28,12 @@ VCC, M0, EXEC = 106, 124, 126
 LDS_LIMIT = 160 * 1024                   # bytes of LDS per workgroup on gfx950
 
 
+# Wait states between an MFMA writing VGPRs and a VALU access to them (the
+# 16-pass figure with margin), and between a VALU write and an MFMA reading it.
+XDL_RESULT_WAITS = 19
+VALU_TO_XDL_WAITS = 2
+
+
 class EmuError(Exception):
     """A kernel did something the hardware would fault on or race on."""
 
@@ -185,6 +191,13 @@ class Wave:
         self.clock = 0                      # wait states issued so far
         self.valu_sgpr_write: Dict[int, int] = {}
         self.salu_m0_write = -100
+        # Hazards of MFMAs written as inline asm, which the compiler does not
+        # see as MFMAs: register -> wait-state clock of the MFMA that wrote it,
+        # and of the last VALU write (MFMA operands need wait states after one)
+        self.xdl_write = {}
+        self.valu_vgpr_write = {}
+        self.cur_inst = None
+        self.in_mfma_srcc = False
         self.vm_q: collections.deque = collections.deque()
         self.lgkm_q: collections.deque = collections.deque()
         self.pend_v: Dict[int, int] = {}
@@ -277,6 +290,12 @@ class Wave:
             name = f"a{row - 256}" if row >= 256 else f"v{row}"
             raise EmuError(f"{what} {name} while its load is still in flight")
 
+    def check_xdl_result(self, r: int, what: str):
+        t = self.xdl_write.get(r)
+        if t is not None and not self.in_mfma_srcc and self.clock - t - 1 < XDL_RESULT_WAITS:
+            raise EmuError(f"{what} v{r} {self.clock - t - 1} wait states after an inline-asm "
+                           f"MFMA wrote it (needs {XDL_RESULT_WAITS})")
+
     def vget(self, o: Op, ty: str = "b32", i: int = 0) -> np.ndarray:
         """Dword i of operand o for all 64 lanes."""
         k = o.kind
@@ -284,6 +303,8 @@ class Wave:
             r = (256 if k == "a" else 0) + o.idx + i
             if r in self.pend_v:
                 self.check_pend_v(r, "read of")
+            if self.xdl_write:
+                self.check_xdl_result(r, "read of")
             return self.V[r]
         if k == "s":
             self._check_pend_s(o.idx + i, 1, "read of")
@@ -303,6 +324,12 @@ class Wave:
         r = (256 if o.kind == "a" else 0) + o.idx + i
         if r in self.pend_v:
             self.check_pend_v(r, "write of")
+        op = self.cur_inst.op if self.cur_inst is not None else ""
+        if not op.startswith("v_mfma"):
+            if self.xdl_write:
+                self.check_xdl_result(r, "write of")
+            if op.startswith("v_"):
+                self.valu_vgpr_write[r] = self.clock
         if mask is None:
             e = self.exec
             if e == FULL:
@@ -450,6 +477,7 @@ class Emulator:
                         raise EmuError(f"wave {w.wid} ran past the end of {kern.name}")
                     inst = insts[w.pc]
                     w.pc += 1
+                    w.cur_inst = inst
                     try:
                         inst.handler(w, inst)
                     except EmuError as e:

@@ -5,7 +5,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .machine import (M32, M64, SHARED_BASE, U32, EmuError, bf16_rne, bf16_to_f32, f32,
+from .machine import (M32, M64, SHARED_BASE, U32, VALU_TO_XDL_WAITS, EmuError, bf16_rne, bf16_to_f32, f32,
                       mask_to_bool, sext32)
 
 HANDLERS = {}
@@ -1293,6 +1293,18 @@ def _mfma(M):
         d, a, b, c = i.ops
         if w.exec != (1 << 64) - 1:
             w.emu.stats.warnings.append(f"MFMA with partial exec at line {i.line}")
+        if i.in_asm:
+            # operands written by a VALU too recently; the accumulator may be
+            # the previous MFMA's result only when it is exactly that range
+            for o, n in ((a, 4), (b, 4), (c, nreg)):
+                if o.kind not in ("v", "a"):
+                    continue
+                for k in range(n):
+                    r = w.vrow(o, k)
+                    t = w.valu_vgpr_write.get(r)
+                    if t is not None and w.clock - t - 1 < VALU_TO_XDL_WAITS:
+                        raise EmuError(f"MFMA reads v{r} {w.clock - t - 1} wait states after a "
+                                       f"VALU wrote it (needs {VALU_TO_XDL_WAITS})")
         Av = _read_bf16x8(w, a)
         Bv = _read_bf16x8(w, b)
         Am = np.zeros((M, K))
@@ -1302,7 +1314,11 @@ def _mfma(M):
         if c.kind == "imm" and c.ival == 0:
             Cm = np.zeros((M, N))
         else:
-            Cl = np.stack([f32(w.vget(c, "b32", r)) for r in range(nreg)], 1).astype(F64)
+            w.in_mfma_srcc = c.kind == d.kind and c.idx == d.idx
+            try:
+                Cl = np.stack([f32(w.vget(c, "b32", r)) for r in range(nreg)], 1).astype(F64)
+            finally:
+                w.in_mfma_srcc = False
             Cm = np.zeros((M, N))
             Cm[d_m, d_n] = Cl
         D = (Am @ Bm + Cm).astype(F32)
@@ -1310,6 +1326,12 @@ def _mfma(M):
         full = np.ones(64, bool)
         for r in range(nreg):
             w.vset(d, out[:, r].view(U32), r, mask=full)
+        if i.in_asm:
+            for r in range(nreg):
+                w.xdl_write[w.vrow(d, r)] = w.clock
+        else:
+            for r in range(nreg):
+                w.xdl_write.pop(w.vrow(d, r), None)
     return run
 
 
@@ -1644,6 +1666,62 @@ def _gload_lds(nb):
 
 HANDLERS["global_load_lds_dword"] = _gload_lds(4)
 HANDLERS["global_load_lds_dwordx4"] = _gload_lds(16)
+
+
+def _bload_lds(nb):
+    """buffer_load_dword{,x4} vaddr, s[r:r+3], soffset offen lds: a raw
+    (stride 0) buffer load into LDS at M0 + nb * lane.  Only the forms the
+    kernels use are accepted; an access that leaves the descriptor's range is
+    an error here (the hardware would return zeros), as is a descriptor with
+    the zero data format (which reads zeros)."""
+    def run(w, i):
+        if not i.mods.get("lds"):
+            raise EmuError(f"buffer load without lds is not modelled: {i.text}")
+        if i.mods.get("idxen") or int(i.mods.get("offset", 0)) != 0:
+            raise EmuError(f"buffer load form not modelled (idxen / offset): {i.text}")
+        v, rs, so = i.ops[0], i.ops[1], i.ops[2]
+        if rs.kind != "s" or rs.n != 4:
+            raise EmuError(f"buffer descriptor must be 4 SGPRs: {i.text}")
+        check_vmem_sgpr_hazard(w, i, [rs, so])
+        if w.clock - w.salu_m0_write - 1 < 1 and i.in_asm:
+            raise EmuError("LDS DMA issued right after an M0 write (needs 1 wait state)")
+        w._check_pend_s(rs.idx, 4, "read of")
+        d = [int(w.S[rs.idx + k]) for k in range(4)]
+        base = d[0] | ((d[1] & 0xFFFF) << 32)
+        stride = (d[1] >> 16) & 0x3FFF
+        num_records = d[2]
+        if stride != 0:
+            raise EmuError(f"strided buffer descriptor not modelled ({stride}): {i.text}")
+        if ((d[3] >> 15) & 0xF) == 0:
+            raise EmuError(f"buffer descriptor with data format 0 reads zeros: {i.text}")
+        m = w.exec_mask()
+        soff = np.int64(w.sget(so))
+        voff = (w.vget(v).astype(np.int64) if i.mods.get("offen")
+                else np.zeros(64, np.int64))
+        off = voff + soff
+        if ((off + nb > num_records) | (off < 0))[m].any():
+            raise EmuError(f"buffer load outside its descriptor's {num_records} bytes "
+                           f"(offset up to {int(off[m].max())}): {i.text}")
+        addrs = (np.int64(base) + off).astype(np.uint64)
+        data = w.emu.mem.read(addrs[m], nb, i.text)
+        m0 = w.S[124] & 0x3FFFF
+        lds_off = (m0 + nb * np.arange(64))[m].astype(np.int64)
+        wg = w.wg
+        if (lds_off + nb > wg.lds_size).any() or (lds_off < 0).any():
+            raise EmuError(f"LDS DMA target {int(lds_off.max())}+{nb} outside "
+                           f"{wg.lds_size}-byte LDS (M0={m0:#x})")
+        idx = (lds_off[:, None] // 4 + np.arange(nb // 4)[None, :]).reshape(-1)
+        if (wg.dma_pending[idx] > 0).any():
+            raise EmuError("LDS DMA into bytes with another DMA still in flight")
+        lds_mark(w, np.unique(idx), "w", i.text + " (issue)")
+        wg.dma_pending[idx] += 1
+        w.emu.stats.lds_dma += 1
+        push_vm(w, Pend(w, dma=(idx, data.reshape(-1, 4)), what=i.text))
+    return run
+
+
+HANDLERS["buffer_load_dword"] = _bload_lds(4)
+HANDLERS["buffer_load_dwordx4"] = _bload_lds(16)
 
 
 def _flat_split(w, addrs):

@@ -305,15 +305,17 @@ __device__ __forceinline__ void soft_step(int s, Wave& w, Soft& sf, int wave) {
       lds_restart[wave] = 1;
     }
   } else if (s < 22) {
+    // weight j, and each pair as soon as it is complete to bf16 (so that the
+    // fp32 weights are not all live at once)
     const int j = s - 6;
     sf.e[j] = __builtin_amdgcn_exp2f(sf.lg[j] - w.m_ref);
-    asm volatile("" : "+v"(sf.e[j]));
-  } else if (s < 30) {
-    const int k = s - 22;  // weights 2k, 2k + 1
-    sf.pb[k >> 2][2 * (k & 3)] = (__bf16)sf.e[2 * k];
-    sf.pb[k >> 2][2 * (k & 3) + 1] = (__bf16)sf.e[2 * k + 1];
-    if ((k & 3) == 3) asm volatile("" : "+v"(sf.pb[k >> 2]));
-  } else if (s < 32) {
+    if (j & 1) {
+      const int k = j >> 1;  // weights 2k, 2k + 1
+      sf.pb[k >> 2][2 * (k & 3)] = (__bf16)sf.e[2 * k];
+      sf.pb[k >> 2][2 * (k & 3) + 1] = (__bf16)sf.e[2 * k + 1];
+      if ((k & 3) == 3) asm volatile("" : "+v"(sf.pb[k >> 2]));
+    }
+  } else if (s >= 30 && s < 32) {
     // l sums the weights as rounded for P.C: each dword holds two bf16,
     // whose fp32 values are the dword's high half and its low half shifted up
     const uint32_t* u = (const uint32_t*)&sf.pb[s - 30];
@@ -331,10 +333,25 @@ __device__ __forceinline__ void soft_step(int s, Wave& w, Soft& sf, int wave) {
 // A operand of step s + kQkAhead is read while step s multiplies); then the
 // row-column scaling l = S_c * alpha^k + S_r (QK norm) or S_c + S_r (plain
 // MLA), and the mask of a sequence's last tile.  With SOFT, the softmax of
-// the previous tile (sf) runs between the MFMAs.  The RoPE sum is finished
-// first and moved to VGPRs, so the latent chain reuses its accumulator
-// registers: every MFMA result lands in AGPRs, which the O^T accumulator
-// otherwise fills, so each extra live accumulator costs moves.
+// the previous tile (sf) runs between the MFMAs.
+// The logits' MFMAs as inline asm, so that their accumulators can be VGPRs:
+// the compiler gives every builtin MFMA an AGPR accumulator, and with the
+// AGPRs full of O^T it would move a block of O^T out and back around every
+// tile.  The compiler does not see these as MFMAs, so the one hazard that
+// concerns them is handled here: a VALU access to an MFMA result needs wait
+// states after the MFMA (mfma_results_ready gives 24, more than the 16-pass
+// case needs).  Back-to-back MFMAs on the same accumulator need none, and the
+// operands come from LDS reads, which the wait counts order.
+__device__ __forceinline__ void mfma_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_next(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_results_ready(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+
 template <bool QKN, bool SOFT, int S>
 __device__ __forceinline__ void qk_tile(Wave& w, Soft& sf, float* lg_out, bool last, int tail,
                                         int wave, int lane, int g) {
@@ -347,8 +364,6 @@ __device__ __forceinline__ void qk_tile(Wave& w, Soft& sf, float* lg_out, bool l
     return (const bf16x8*)(s < kRopeSteps ? rrow + s * 1024 : row + (s - kRopeSteps) * 32);
   };
   f32x16 sc, sr;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) { sc[j] = 0.f; sr[j] = 0.f; }
   f32x4 ak[4];
   const float* al = (const float*)(st + kLatBytes + kRopeBytes) + g * 32 + 4 * hf;
   bf16x8 av[kQkAhead];
@@ -362,11 +377,10 @@ __device__ __forceinline__ void qk_tile(Wave& w, Soft& sf, float* lg_out, bool l
 #pragma unroll
   for (int s = 0; s < kQkSteps; ++s) {
     fence();
-    if (s == kRopeSteps) asm volatile("" : "+v"(sr));  // RoPE sum to VGPRs
-    if (s < kRopeSteps)
-      sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], qr[s], sr, 0, 0, 0);
-    else
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s % kQkAhead], w.qt[s - kRopeSteps], sc, 0, 0, 0);
+    if (s == 0) mfma_first(sr, av[0], qr[0]);
+    else if (s < kRopeSteps) mfma_next(sr, av[s % kQkAhead], qr[s]);
+    else if (s == kRopeSteps) mfma_first(sc, av[s % kQkAhead], w.qt[0]);
+    else mfma_next(sc, av[s % kQkAhead], w.qt[s - kRopeSteps]);
     if (s + kQkAhead < kQkSteps) av[s % kQkAhead] = *qk_a(s + kQkAhead);
     else if (QKN && s + kQkAhead - kQkSteps < 4) {
       const int q = s + kQkAhead - kQkSteps;  // alpha^k of the lane's tokens 8q+4hf..+3
@@ -375,6 +389,7 @@ __device__ __forceinline__ void qk_tile(Wave& w, Soft& sf, float* lg_out, bool l
     if constexpr (SOFT) soft_step(s, w, sf, wave);
   }
   fence();
+  mfma_results_ready(sc, sr);
   // reg j holds token 8*(j/4) + 4*hf + j%4
   if constexpr (QKN) {
 #pragma unroll
@@ -462,14 +477,19 @@ __device__ __forceinline__ void pipe_step(Wave& w, Soft& sf, const Seq& sq, cons
   pv_tile<SP>(w, sf.pb, lane);
 }
 
-template <bool QKN, int NW>
+template <bool QKN, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
+  // Contiguous caches get their own instantiation, in which the block-table
+  // test folds away (a runtime flag would be one more value held in registers
+  // across the segment loop).
+  Paging pg = a.pg;
+  if constexpr (!PAGED) pg.bt = nullptr;
   // The tile prefix takes LDS offset 0 (largest alignment is placed first): a
   // stage buffer at offset 0 loses the alias information that lets its reads
   // run ahead of the loads in flight into the other stages.
   __shared__ __attribute__((aligned(2048))) int P[kMaxBatch + 1];
   if (threadIdx.x < 4) lds_restart[threadIdx.x] = 0;
-  build_tile_prefix(a.seq_lens, a.B, a.s_q, a.pg.capacity(), P);
+  build_tile_prefix(a.seq_lens, a.B, a.s_q, pg.capacity(), P);
   if (blockIdx.x == 0)  // the merge reads the prefix instead of rebuilding it per block
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.plan[i] = P[i];
 
@@ -490,7 +510,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
     // b: virtual sequence (query row b % s_q of cache b / s_q)
     const int b = __builtin_amdgcn_readfirstlane(seq_of(P, a.B, x));
     Seq sq;
-    sq.L = __builtin_amdgcn_readfirstlane(virt_len(a.seq_lens, b, a.s_q, a.pg.capacity()));
+    sq.L = __builtin_amdgcn_readfirstlane(virt_len(a.seq_lens, b, a.s_q, pg.capacity()));
     const int64_t s0 = __builtin_amdgcn_readfirstlane(P[b]);
     const int64_t s1 = __builtin_amdgcn_readfirstlane(P[b + 1]);
     const int64_t seg_end = e < s1 ? e : s1;
@@ -503,21 +523,37 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
     sq.alpha = QKN ? (const char*)a.alpha : nullptr;
     const size_t qrow = (size_t)b * a.H + head;
 
-    // The segment's first two tiles go out first, so that their latency
-    // overlaps the query loads below.
-    issue_tile<QKN, NW, 0>(sq, a.pg, a.G, tile0, wave, lane);
-    if (nt > 1) issue_tile<QKN, NW, 1>(sq, a.pg, a.G, tile0 + 1, wave, lane);
-    // Query operands for this sequence: q~ in registers, the RoPE query in
-    // LDS, both kept for the segment.
-#pragma unroll
-    for (int s = 0; s < kR / 16; ++s)
-      w.qt[s] = *(const bf16x8*)(a.q_tilde + qrow * kR + s * 16 + hf * 8);
+    // The segment's loads, in the order the first tile's logits need them:
+    // the RoPE query (straight into LDS: its operand-order rows are the LDS
+    // layout) and tile 0; then q~ into registers (operand order: each load
+    // reads the wave's 1 KB of one K-step); then tile 1.  Loads complete in
+    // order, so the first logits wait only for the first group, and the q~
+    // loads land while the MFMAs run (the compiler waits for each as it is
+    // used).  The fences keep the groups in this order.
     {
-      bf16x8* qrl = (bf16x8*)(lds_qrope + (wave * (kDr / 16) * 64 + lane) * 16);
+      const __amdgpu_buffer_rsrc_t qr_rsrc = tile_rsrc(
+          a.q_rope + qop_index(b, a.H, kDr, wave * 32, 0), (kDr / 16) * 64 * 16);
 #pragma unroll
       for (int s = 0; s < kDr / 16; ++s)
-        qrl[s * 64] = *(const bf16x8*)(a.q_rope + qrow * kDr + s * 16 + hf * 8);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            qr_rsrc, QK_LDS(void, lds_qrope + (wave * (kDr / 16) + s) * 1024), 16, lane << 4,
+            s * 1024, 0, 0);
     }
+    issue_tile<QKN, NW, 0>(sq, pg, a.G, tile0, wave, lane);
+    fence();
+    {
+      // scalar base (the wave's block) plus a lane offset recomputed here, so
+      // that no per-lane address is kept, or spilled, across the segments
+      const char* qbase = (const char*)(a.q_tilde + qop_index(b, a.H, kR, wave * 32, 0));
+      uint32_t ln16;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
+                   "v_lshlrev_b32 %0, 4, %0" : "=v"(ln16));
+#pragma unroll
+      for (int s = 0; s < kR / 16; ++s) w.qt[s] = *(const bf16x8*)(qbase + s * 1024 + ln16);
+    }
+    fence();
+    if (nt > 1) issue_tile<QKN, NW, 1>(sq, pg, a.G, tile0 + 1, wave, lane);
+    bool q_in_flight = true;
     w.m_ref = -INFINITY;
     w.have_ref = false;
     for (;;) {  // one pass over the segment; repeated only if a logit overflows the reference
@@ -528,17 +564,23 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
       w.l_run = 0.f;
       Soft sf;
       {  // the first tile's logits; stage 2 is free, so tile 2 goes out now
-        wait_vmcnt<0>();
+        // Wait for tile 0 (and the RoPE query): on a segment's first pass the
+        // q~ loads and tile 1 may still be in flight behind them.
+        constexpr int kQtLoads = kR / 16;
+        if (!q_in_flight) wait_vmcnt<0>();
+        else if (nt > 1) wait_vmcnt<kQtLoads + TileLoads<QKN, NW>::total>();
+        else wait_vmcnt<kQtLoads>();
+        q_in_flight = false;
         block_sync();
-        if (nt > 2) issue_tile<QKN, NW, 2>(sq, a.pg, a.G, tile0 + 2, wave, lane);
+        if (nt > 2) issue_tile<QKN, NW, 2>(sq, pg, a.G, tile0 + 2, wave, lane);
         const bool last = tile0 == sq.last_tile;
         const int tail = last ? __builtin_amdgcn_readfirstlane(sq.L - tile0 * kTile) : kTile;
         qk_tile<QKN, false, 0>(w, sf, sf.lg, last, tail, wave, lane, g);
       }
       for (int i = 0; i < nt; i += kStages) {
-        pipe_step<QKN, NW, 0, 1, 2>(w, sf, sq, a.pg, a.G, tile0, i, nt, wave, lane, g);
-        if (i + 1 < nt) pipe_step<QKN, NW, 1, 2, 0>(w, sf, sq, a.pg, a.G, tile0, i + 1, nt, wave, lane, g);
-        if (i + 2 < nt) pipe_step<QKN, NW, 2, 0, 1>(w, sf, sq, a.pg, a.G, tile0, i + 2, nt, wave, lane, g);
+        pipe_step<QKN, NW, 0, 1, 2>(w, sf, sq, pg, a.G, tile0, i, nt, wave, lane, g);
+        if (i + 1 < nt) pipe_step<QKN, NW, 1, 2, 0>(w, sf, sq, pg, a.G, tile0, i + 1, nt, wave, lane, g);
+        if (i + 2 < nt) pipe_step<QKN, NW, 2, 0, 1>(w, sf, sq, pg, a.G, tile0, i + 2, nt, wave, lane, g);
       }
       block_sync();
       if (!(lds_restart[0] | lds_restart[1] | lds_restart[2] | lds_restart[3])) break;
@@ -547,8 +589,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
       // normalised logits).
       block_sync();
       if (lane == 0) lds_restart[wave] = 0;
-      issue_tile<QKN, NW, 0>(sq, a.pg, a.G, tile0, wave, lane);
-      if (nt > 1) issue_tile<QKN, NW, 1>(sq, a.pg, a.G, tile0 + 1, wave, lane);
+      issue_tile<QKN, NW, 0>(sq, pg, a.G, tile0, wave, lane);
+      if (nt > 1) issue_tile<QKN, NW, 1>(sq, pg, a.G, tile0 + 1, wave, lane);
     }
     // ---- segment epilogue ----
     // The accumulator holds, in lane (head 32 wave + lane % 32, hf = lane / 32)
@@ -648,14 +690,19 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* s
   a.o_lat = o_lat;
   a.lse = lse;
   const int nw = c.H / 32;
+  const bool paged = pg.bt != nullptr;
   dim3 grid(n_wg), block(nw * 64);
   if (c.qk_norm) {
-    if (nw == 4) decode_mfma_kernel<true, 4><<<grid, block, 0, s>>>(a);
-    else if (nw == 2) decode_mfma_kernel<true, 2><<<grid, block, 0, s>>>(a);
+    if (nw == 4 && paged) decode_mfma_kernel<true, 4, true><<<grid, block, 0, s>>>(a);
+    else if (nw == 4) decode_mfma_kernel<true, 4, false><<<grid, block, 0, s>>>(a);
+    else if (nw == 2 && paged) decode_mfma_kernel<true, 2, true><<<grid, block, 0, s>>>(a);
+    else if (nw == 2) decode_mfma_kernel<true, 2, false><<<grid, block, 0, s>>>(a);
     else return hipErrorInvalidValue;  // one-wavefront variant switched off
   } else {
-    if (nw == 4) decode_mfma_kernel<false, 4><<<grid, block, 0, s>>>(a);
-    else if (nw == 2) decode_mfma_kernel<false, 2><<<grid, block, 0, s>>>(a);
+    if (nw == 4 && paged) decode_mfma_kernel<false, 4, true><<<grid, block, 0, s>>>(a);
+    else if (nw == 4) decode_mfma_kernel<false, 4, false><<<grid, block, 0, s>>>(a);
+    else if (nw == 2 && paged) decode_mfma_kernel<false, 2, true><<<grid, block, 0, s>>>(a);
+    else if (nw == 2) decode_mfma_kernel<false, 2, false><<<grid, block, 0, s>>>(a);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

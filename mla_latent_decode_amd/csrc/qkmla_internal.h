@@ -44,11 +44,22 @@ __host__ __device__ constexpr size_t kPartialSlotBytes(int H, int r) {
   return (size_t)H * 8 + (size_t)H * r * 2;
 }
 
+// Index of element (head h, dim d) of sequence b's bf16 query operands, q~
+// (D = r) or the RoPE query (D = d_r), as the MFMA decode reads them: for each
+// wavefront's 32 heads and each K-step of 16 dims, the 64 lanes' 16-byte B
+// operands lie contiguous (lane n + 32 hf: head 32 j + n, dims 16 s + 8 hf ..
+// + 8), so that one load instruction reads 1 KB in one piece.
+__host__ __device__ __forceinline__ size_t qop_index(int b, int H, int D, int h, int d) {
+  return ((((size_t)b * (H / 32) + h / 32) * (D / 16) + d / 16) * 64 + ((d >> 3) & 1) * 32 +
+          (h & 31)) * 8 + (d & 7);
+}
+
 // ---- workspace layout of the bf16 MFMA decode ------------------------------
 struct WsLayout {
-  size_t q_tilde;    // bf16 [B][H][r]
+  size_t q_tilde;    // bf16 operand order (qop_index, D = r); fp32 path: f32 [B][H][r]
   size_t alpha_q;    // f32  [B][H]   (tau*log2e folded in)
-  size_t q_rope;     // bf16 / f32 [B][H][d_r] (normalised, rotated, tau*log2e folded in)
+  size_t q_rope;     // bf16 operand order (qop_index, D = d_r); fp32 path: f32 [B][H][d_r]
+                     // (normalised, rotated, tau*log2e folded in)
   size_t partials;   // [n_wg][kSlotsPerWg] slots of kPartialSlotBytes(H, r):
                      //   m[H] f32, l[H] f32, O[H][r] bf16
   size_t plan;       // i32  [B+1]  tile prefix of the split plan (written by the decode)

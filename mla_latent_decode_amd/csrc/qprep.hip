@@ -114,7 +114,6 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
       for (int o = 1; o < 16; o <<= 1) rs += __shfl_xor(rs, o, 64);
       const float rscale = qk_norm ? 1.0f / sqrtf(rs / (float)dr + eps) : 1.0f;
       const int pos = clamp_pos(L[sq], L_cap);
-      uint16_t* qo = q_rope_out + ((size_t)b * H + h0 + hh) * dr;
 #pragma unroll
       for (int k = 0; k < kQpRopeSlots; ++k) {
         const int pi = p0 + 16 * k;
@@ -126,8 +125,9 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
           }
           float c, sn;
           rope_cos_sin_freq(pos, fr[k], &c, &sn);
-          *(uint32_t*)(qo + 2 * pi) = (uint32_t)f32_to_bf16((x0 * c - x1 * sn) * sl) |
-                                      ((uint32_t)f32_to_bf16((x0 * sn + x1 * c) * sl) << 16);
+          *(uint32_t*)(q_rope_out + qop_index(b, H, dr, h0 + hh, 2 * pi)) =
+              (uint32_t)f32_to_bf16((x0 * c - x1 * sn) * sl) |
+              ((uint32_t)f32_to_bf16((x0 * sn + x1 * c) * sl) << 16);
         }
       }
     }
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
     const int row = it * 16 + (tid >> 4), c8 = (tid & 15) * 8;
     const int b = b0 + row / 16;
     if (b < nv)
-      *(uint4*)(q_tilde + ((size_t)b * H + h0 + row % 16) * r + z * kQpCols + c8) =
+      *(uint4*)(q_tilde + qop_index(b, H, r, h0 + row % 16, z * kQpCols + c8)) =
           *(const uint4*)&tile[row][c8];
   }
 }

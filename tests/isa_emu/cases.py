@@ -919,6 +919,47 @@ def hazard_checker(dev):
     run(4)
     print("[ok] wait-state check: reported below 5 wait states, clean at 5", flush=True)
 
+    # An inline-asm MFMA's result read by a VALU instruction: needs
+    # XDL_RESULT_WAITS wait states (s_nop N gives N + 1); a VALU write of an
+    # MFMA operand needs VALU_TO_XDL_WAITS before the MFMA.
+    from isa_emu.machine import VALU_TO_XDL_WAITS, XDL_RESULT_WAITS, Wave, Workgroup
+
+    def run_mfma(nops, valu_first=False, gap=0):
+        insts = []
+        if valu_first:
+            insts.append(parse_inst("v_mov_b32 v0, v1", 0))
+            insts += [parse_inst("s_nop 0", 1)] * gap
+        asm = ["v_mfma_f32_32x32x16_bf16 v[16:31], v[0:3], v[4:7], 0"] + [f"s_nop {n}" for n in nops]
+        for t in asm:
+            inst = parse_inst(t, len(insts))
+            inst.in_asm = True
+            insts.append(inst)
+        insts += [parse_inst("v_mov_b32 v40, v16", 80), parse_inst("s_endpgm", 81)]
+        k = Kernel("probe", insts, {}, {"group_segment_fixed_size": 0, "user_sgpr_count": 0}, {})
+        emu = Emulator(mem)
+        emu.prepare(k)
+        w = Wave(emu, k, Workgroup(0), 0, (0, 0, 0), (64, 1, 1), 0, 64)
+        emu._run_group(k, Workgroup(0), [w], (0, 0, 0), 100)
+
+    for nops in ([], [7], [7, 7]):
+        if sum(n + 1 for n in nops) >= XDL_RESULT_WAITS:
+            continue
+        try:
+            run_mfma(nops)
+        except EmuError as e:
+            assert "wait states after an inline-asm MFMA" in str(e), e
+        else:
+            raise AssertionError(f"MFMA result read after s_nop {nops} not reported")
+    run_mfma([7, 7, 7])
+    try:
+        run_mfma([7, 7, 7], valu_first=True, gap=VALU_TO_XDL_WAITS - 2)
+    except EmuError as e:
+        assert "after a VALU wrote it" in str(e), e
+    else:
+        raise AssertionError("VALU write just before an inline-asm MFMA not reported")
+    run_mfma([7, 7, 7], valu_first=True, gap=VALU_TO_XDL_WAITS)
+    print("[ok] inline-asm MFMA wait states: result reads and operand writes checked", flush=True)
+
 
 @case
 def isa_semantics(dev):

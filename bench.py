@@ -15,10 +15,13 @@ is used (and said) if capture fails or a replay differs.  The eager figures
 are reported beside them.
 
 Prints ONE JSON line: value = algorithmic cache bytes per step / step time
-(GB/s) for the batch-16 x 4096 workload, with microseconds per step, the
-overhead against the same kernels with the normalisation compiled out (plain
-MLA), the hot kernel's roofline position, the fp64 oracle timed on the host,
-and the same figures for the 32k, 256k and ragged workloads under "sweep".
+(GB/s) for the one-sequence 262 144-token workload (--workload picks
+another), with microseconds per step, the overhead against the same kernels
+with the normalisation compiled out (plain MLA), the split-KV kernel's
+roofline position (its per-launch time from the library's HIP events, each
+kernel launched several times back to back between them), the fp64 oracle
+timed on the host, and the same figures for the 4k, 32k and ragged workloads
+under "sweep".
 Under "next_rows": bulk append, s_q = 2 decode, paged-cache decode and the
 explicit-form training forward and backward, each timed on its own.
 
@@ -227,10 +230,13 @@ class Bench:
         recorded by the library around each launch on the launch stream)."""
         return self.kernel_breakdown_ms(steps, plain)[1]
 
-    def kernel_breakdown_ms(self, steps, plain=False):
-        """Average (q-prep, split-KV, merge) durations per decode call over
-        `steps` steps, from the library's events on the launch stream."""
-        self.ops.profile_begin()
+    def kernel_breakdown_ms(self, steps, plain=False, reps=8):
+        """Average (q-prep, split-KV, merge) durations per launch over `steps`
+        decode calls, from the library's HIP events on the launch stream, each
+        kernel launched `reps` times back to back between its two events (the
+        events' own latency, some microseconds, is spread over reps kernels;
+        back-to-back kernels have no gap between them)."""
+        self.ops.profile_begin(reps)
         for _ in range(steps):
             self.step(plain)
         ms, n = self.ops.profile_end_detail()
@@ -584,11 +590,11 @@ def _progress(out, name):
     print(f"[bench] {name} {out[name]}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cid, budget_s=15.0, max_tokens=65536):
-    """The fp64 oracle on the host: sequences of the same workload (each cut to
-    at most `max_tokens` tokens, so one sequence of a long-context workload
-    stays within the budget), one at a time, until about `budget_s` seconds of
-    CPU work; returns its cache GB/s."""
+def cpu_baseline(cid, budget_s=15.0, max_rounds=64):
+    """The fp64 oracle on the host: the workload's sequences, whole, one at a
+    time with fresh seeds (going round the workload again when it has fewer
+    sequences than the budget takes), until about `budget_s` seconds of oracle
+    decode time; returns its cache GB/s."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -598,8 +604,8 @@ def cpu_baseline(cid, budget_s=15.0, max_tokens=65536):
     w = WORKLOADS[cid]
     lengths = _lengths(w)
     done_tokens, elapsed, n, t_alpha = 0, 0.0, 0, 0.0
-    for i, L in enumerate(lengths):
-        L = min(L, max_tokens)
+    for i in range(max_rounds):
+        L = lengths[i % len(lengths)]
         inp = make_inputs(w.shape, [L], seed=4000 + i, row_scale_log10_clip=w.row_scale_log10_clip)
         t0 = time.perf_counter()
         oracle.explicit_decode(inp.q_c, inp.q_rope, inp.latents, inp.k_rope_raw, inp.w_uk, inp.w_uv,
@@ -612,7 +618,7 @@ def cpu_baseline(cid, budget_s=15.0, max_tokens=65536):
         t_alpha += time.perf_counter() - t0
         done_tokens += L
         n += 1
-        if elapsed + t_alpha >= budget_s:
+        if elapsed >= budget_s:
             break
     info = threadpool_info()
     threads = max([p.get("num_threads", 1) for p in info] + [1])
@@ -626,9 +632,8 @@ def cpu_baseline(cid, budget_s=15.0, max_tokens=65536):
         pass
     gbps = done_tokens * cache_bytes_per_token(w.shape, True) / elapsed / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {len(lengths)} sequences ({done_tokens} cached tokens, each cut to "
-                      f"at most {max_tokens}) of the same workload, fp64 explicit form, "
-                      f"{elapsed:.1f} s",
+            "sample": f"{n} whole sequences of the workload's {len(lengths)} (fresh seeds; "
+                      f"{done_tokens} cached tokens), fp64 explicit form, {elapsed:.1f} s",
             "us_per_step_extrapolated": round(elapsed / done_tokens * sum(lengths) * 1e6, 1),
             "alpha_append_us_per_step_extrapolated":
                 round(t_alpha / done_tokens * sum(lengths) * 1e6, 1),

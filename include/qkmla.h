@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define QKMLA_ABI_VERSION 7
+#define QKMLA_ABI_VERSION 8
 
 typedef enum {
   QKMLA_OK = 0,
@@ -274,6 +274,10 @@ int qkmla_decode_paged(const qkmla_config* cfg, int32_t batch, int32_t s_q, cons
  * V up-projection: out[b][h][:] = o_lat[b][h][:] W^UV_{g(h)}.
  *   o_lat device float [B][H][r];  w_uv device dtype [G][r][d_v];
  *   out   device float [B][H][d_v].
+ * Pointers must be aligned to their element size; for bf16 with 16 heads per
+ * group, r a multiple of 128 and d_v of 16 (the MFMA kernel, which reads
+ * 16-byte vectors) o_lat and w_uv must be 16-byte aligned.  A violation
+ * returns QKMLA_ERR_INVALID_ARG before anything is launched.
  */
 int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, const void* w_uv,
                    float* out, void* stream);
@@ -396,15 +400,22 @@ int qkmla_plan_merge_sources(int32_t batch, const int32_t* seq_lens, int32_t cac
 
 /*
  * Measurement hook.  Between qkmla_profile_begin() and qkmla_profile_end(),
- * every decode call (qkmla_decode, _multi, _paged) of this host thread
- * records HIP events on its stream around its q-prep, split-KV and merge
- * launches.
+ * every decode call (qkmla_decode, _multi, _paged, _noalloc) of this host
+ * thread records HIP events on its stream before and after each of its
+ * q-prep, split-KV and merge launches.  qkmla_profile_begin_reps(reps), reps
+ * in 1..64, makes every decode call launch each of the three kernels reps
+ * times back to back between its two events (each launch rewrites the same
+ * outputs from the same inputs, so the call's results are unchanged) and
+ * report the time per launch: the events' own latency, some microseconds,
+ * is then spread over reps kernels.
  * qkmla_profile_end() waits for the recorded events and returns the summed
- * kernel time in milliseconds and the number of launches.  At most 4096
- * launches are recorded per begin/end window; the events are created on first
- * use and kept for the life of the process.
+ * kernel time in milliseconds and the number of decode calls.  At most 4096
+ * calls are recorded per begin/end window; the events are created on first
+ * use and kept for the life of the process.  Not for use under stream
+ * capture.
  */
 int qkmla_profile_begin(void);
+int qkmla_profile_begin_reps(int32_t reps);
 int qkmla_profile_end(double* split_kv_ms_total, int32_t* launches);
 /* The same window split by kernel: ms_total[0] q-prep, [1] the split-KV
  * kernel (the row-parallel decode for float storage), [2] the merge (0 for

@@ -124,31 +124,33 @@ int device_cu_count() {
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-// Measurement hook state (per host thread): per recorded decode call, events
-// before q-prep (0), before the split-KV kernel (1), after it (2) and after
-// the merge (3).
+// Measurement hook state (per host thread): per recorded decode call, HIP
+// events on its stream before and after each of its three kernels (q-prep 0,
+// split-KV 1, merge 2).  With reps > 1 each kernel is launched reps times back
+// to back between its two events (every launch rewrites the same outputs from
+// the same inputs), so that the events' own latency is spread over reps
+// kernels.  A path without a merge records that pair back to back.
 constexpr int kTimedMax = 4096;
 struct KernelTimer {
   bool on = false;
+  int reps = 1;
   int n = 0;
-  hipEvent_t ev[4][kTimedMax];
+  hipEvent_t ev[3][2][kTimedMax];
   int created = 0;
 };
 thread_local KernelTimer g_timer;
 
-hipError_t timer_record(hipStream_t s, int which) {
+hipError_t timer_record(hipStream_t s, int which, int edge) {
   KernelTimer& t = g_timer;
-  if (!t.on || t.n >= kTimedMax) return hipSuccess;
   if (t.n >= t.created) {
-    for (int k = 0; k < 4; ++k) {
-      const hipError_t e = hipEventCreate(&t.ev[k][t.n]);
-      if (e != hipSuccess) return e;
-    }
+    for (int k = 0; k < 3; ++k)
+      for (int j = 0; j < 2; ++j) {
+        const hipError_t e = hipEventCreate(&t.ev[k][j][t.n]);
+        if (e != hipSuccess) return e;
+      }
     t.created = t.n + 1;
   }
-  const hipError_t e = hipEventRecord(t.ev[which][t.n], s);
-  if (which == 3) ++t.n;
-  return e;
+  return hipEventRecord(t.ev[which][edge][t.n], s);
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -184,8 +186,12 @@ extern "C" {
 
 int qkmla_abi_version(void) { return QKMLA_ABI_VERSION; }
 
-int qkmla_profile_begin(void) {
+int qkmla_profile_begin(void) { return qkmla_profile_begin_reps(1); }
+
+int qkmla_profile_begin_reps(int32_t reps) {
+  if (reps < 1 || reps > 64) return fail(QKMLA_ERR_INVALID_ARG, "profile: reps must be in 1..64");
   g_timer.on = true;
+  g_timer.reps = reps;
   g_timer.n = 0;
   return ok();
 }
@@ -195,11 +201,11 @@ int qkmla_profile_end_detail(double* ms_total, int32_t* launches) {
   t.on = false;
   double total[3] = {0.0, 0.0, 0.0};
   for (int i = 0; i < t.n; ++i) {
-    hipError_t e = hipEventSynchronize(t.ev[3][i]);
+    hipError_t e = hipEventSynchronize(t.ev[2][1][i]);
     for (int k = 0; k < 3 && e == hipSuccess; ++k) {
       float ms = 0.f;
-      e = hipEventElapsedTime(&ms, t.ev[k][i], t.ev[k + 1][i]);
-      total[k] += ms;
+      e = hipEventElapsedTime(&ms, t.ev[k][0][i], t.ev[k][1][i]);
+      total[k] += ms / t.reps;
     }
     if (e != hipSuccess) return hip_status(e, "profile_end");
   }
@@ -432,26 +438,37 @@ static int decode_impl(const Cfg& c, int32_t batch, int32_t s_q, const void* q_c
     return fail(QKMLA_ERR_WORKSPACE, "decode: workspace %zu bytes, need %zu", workspace_bytes,
                 ws.total);
   const bool timed = g_timer.on && g_timer.n < kTimedMax;
+  const int reps = timed ? g_timer.reps : 1;
   hipError_t e = hipSuccess;
-  if (timed && (e = timer_record(s, 0)) != hipSuccess) return hip_status(e, "decode/timer");
-  e = launch_qprep(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens, pg, ws, workspace,
-                   status, s);
+  if (timed && (e = timer_record(s, 0, 0)) != hipSuccess) return hip_status(e, "decode/timer");
+  for (int i = 0; i < reps && e == hipSuccess; ++i)
+    e = launch_qprep(c, batch, s_q, q_c, q_rope, w_qabs, gamma_q_rope, seq_lens, pg, ws, workspace,
+                     status, s);
   if (e != hipSuccess) return hip_status(e, "decode/qprep");
-  if (timed && (e = timer_record(s, 1)) != hipSuccess) return hip_status(e, "decode/timer");
+  if (timed && ((e = timer_record(s, 0, 1)) != hipSuccess || (e = timer_record(s, 1, 0)) != hipSuccess))
+    return hip_status(e, "decode/timer");
   if (c.dtype == QKMLA_BF16) {
-    e = launch_decode_mfma(c, batch, s_q, seq_lens, pg, latent_cache, rope_cache, alpha_cache, ws,
-                           workspace, n_wg, o_lat, lse, s);
+    for (int i = 0; i < reps && e == hipSuccess; ++i)
+      e = launch_decode_mfma(c, batch, s_q, seq_lens, pg, latent_cache, rope_cache, alpha_cache, ws,
+                             workspace, n_wg, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/splitkv");
-    if (timed && (e = timer_record(s, 2)) != hipSuccess) return hip_status(e, "decode/timer");
-    e = launch_merge(c, batch, s_q, ws, workspace, n_wg, o_lat, lse, s);
+    if (timed && ((e = timer_record(s, 1, 1)) != hipSuccess || (e = timer_record(s, 2, 0)) != hipSuccess))
+      return hip_status(e, "decode/timer");
+    for (int i = 0; i < reps && e == hipSuccess; ++i)
+      e = launch_merge(c, batch, s_q, ws, workspace, n_wg, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/merge");
   } else {
-    e = launch_decode_generic(c, batch, s_q, seq_lens, pg, latent_cache, rope_cache, alpha_cache,
-                              ws, workspace, o_lat, lse, s);
+    for (int i = 0; i < reps && e == hipSuccess; ++i)
+      e = launch_decode_generic(c, batch, s_q, seq_lens, pg, latent_cache, rope_cache, alpha_cache,
+                                ws, workspace, o_lat, lse, s);
     if (e != hipSuccess) return hip_status(e, "decode/generic");
-    if (timed && (e = timer_record(s, 2)) != hipSuccess) return hip_status(e, "decode/timer");
+    if (timed && ((e = timer_record(s, 1, 1)) != hipSuccess || (e = timer_record(s, 2, 0)) != hipSuccess))
+      return hip_status(e, "decode/timer");
   }
-  if (timed && (e = timer_record(s, 3)) != hipSuccess) return hip_status(e, "decode/timer");
+  if (timed) {
+    if ((e = timer_record(s, 2, 1)) != hipSuccess) return hip_status(e, "decode/timer");
+    ++g_timer.n;
+  }
   return ok();
 }
 
@@ -740,6 +757,8 @@ int qkmla_out_proj(const qkmla_config* cfg, int32_t batch, const float* o_lat, c
   if (!o_lat || !w_uv || !out) return fail(QKMLA_ERR_INVALID_ARG, "out_proj: NULL pointer");
   if (!aligned(o_lat, 4) || !aligned(w_uv, elem_size(c)) || !aligned(out, 4))
     return fail(QKMLA_ERR_INVALID_ARG, "out_proj: pointers must be aligned to their element size");
+  if (out_proj_uses_mfma(c) && (!aligned(o_lat, 16) || !aligned(w_uv, 16)))
+    return fail(QKMLA_ERR_INVALID_ARG, "out_proj: o_lat and w_uv must be 16-byte aligned");
   return hip_status(launch_out_proj(c, batch, o_lat, w_uv, out, as_stream(stream)), "out_proj");
 }
 

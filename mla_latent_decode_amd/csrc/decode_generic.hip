@@ -105,11 +105,10 @@ hipError_t launch_decode_generic(const Cfg& c, int batch, int s_q, const int32_t
                                  const WsLayout& ws, void* workspace, float* o_lat, float* lse,
                                  hipStream_t s) {
   char* wsb = (char*)workspace;
-  decode_generic_kernel<<<dim3(batch * s_q, c.H), 256, 0, s>>>(
-      seq_lens, s_q, pg, c.H, c.G, c.r, c.dr, c.qk_norm, (const float*)lat, (const float*)rope,
-      alpha, (const float*)(wsb + ws.q_tilde), (const float*)(wsb + ws.alpha_q),
-      (const float*)(wsb + ws.q_rope), o_lat, lse);
-  return hipGetLastError();
+  return launch_kernel(decode_generic_kernel, dim3(batch * s_q, c.H), dim3(256), s, seq_lens, s_q,
+                       pg, c.H, c.G, c.r, c.dr, c.qk_norm, (const float*)lat, (const float*)rope,
+                       alpha, (const float*)(wsb + ws.q_tilde), (const float*)(wsb + ws.alpha_q),
+                       (const float*)(wsb + ws.q_rope), o_lat, lse);
 }
 
 }  // namespace qkmla

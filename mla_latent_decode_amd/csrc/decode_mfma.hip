@@ -692,20 +692,16 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* s
   const int nw = c.H / 32;
   const bool paged = pg.bt != nullptr;
   dim3 grid(n_wg), block(nw * 64);
+  void (*k)(Args) = nullptr;
   if (c.qk_norm) {
-    if (nw == 4 && paged) decode_mfma_kernel<true, 4, true><<<grid, block, 0, s>>>(a);
-    else if (nw == 4) decode_mfma_kernel<true, 4, false><<<grid, block, 0, s>>>(a);
-    else if (nw == 2 && paged) decode_mfma_kernel<true, 2, true><<<grid, block, 0, s>>>(a);
-    else if (nw == 2) decode_mfma_kernel<true, 2, false><<<grid, block, 0, s>>>(a);
-    else return hipErrorInvalidValue;  // one-wavefront variant switched off
+    if (nw == 4) k = paged ? decode_mfma_kernel<true, 4, true> : decode_mfma_kernel<true, 4, false>;
+    else if (nw == 2) k = paged ? decode_mfma_kernel<true, 2, true> : decode_mfma_kernel<true, 2, false>;
   } else {
-    if (nw == 4 && paged) decode_mfma_kernel<false, 4, true><<<grid, block, 0, s>>>(a);
-    else if (nw == 4) decode_mfma_kernel<false, 4, false><<<grid, block, 0, s>>>(a);
-    else if (nw == 2 && paged) decode_mfma_kernel<false, 2, true><<<grid, block, 0, s>>>(a);
-    else if (nw == 2) decode_mfma_kernel<false, 2, false><<<grid, block, 0, s>>>(a);
-    else return hipErrorInvalidValue;
+    if (nw == 4) k = paged ? decode_mfma_kernel<false, 4, true> : decode_mfma_kernel<false, 4, false>;
+    else if (nw == 2) k = paged ? decode_mfma_kernel<false, 2, true> : decode_mfma_kernel<false, 2, false>;
   }
-  return hipGetLastError();
+  if (!k) return hipErrorInvalidValue;  // one-wavefront variant switched off
+  return launch_kernel(k, grid, block, s, a);
 }
 
 }  // namespace qkmla

@@ -14,40 +14,45 @@
 namespace qkmla {
 
 // The log-sum-exp merge.  WPH wavefronts share head h of virtual sequence
-// b; a block holds max(4, WPH) wavefronts, so 4 / WPH heads when WPH < 4.
-// The block first lists the sequence's partial slots in LDS (the slot each
-// workgroup holding its tiles wrote, one thread per workgroup, so the slot
-// arithmetic is off the load path).  Wave w of a head folds the sources w,
-// w + WPH, ... with a running maximum, kMergeBatch at a time with all of
-// their loads in flight; lane l holds latent dims 8l..8l+7, one 16-byte piece
-// of the source's 1 KB bf16 O row (r = 512).  The WPH waves of a head meet in LDS.
-// The host picks WPH so that a wave folds about kMergeBatch sources and the
-// grid is resident at once: the kernel's time is then about one round of
-// loads rather than several.  The tile prefix of the plan comes from the
-// workspace, where the split-KV kernel left it.
-constexpr int kMergeBatch = 8;     // sources in flight per wave
+// b; a block holds max(4, WPH) wavefronts, so 4 / WPH heads when WPH < 4, and
+// covers r / ZD of the latent dims (grid z: which part).  The block first
+// lists the sequence's partial slots in LDS (the slot each workgroup holding
+// its tiles wrote, one thread per workgroup, so the slot arithmetic is off the
+// load path).  Wave w of a head folds the sources w, w + WPH, ... with a
+// running maximum, kMergeBatch at a time with all of their loads in flight;
+// lane l holds 8 / ZD latent dims, one 16 / ZD-byte piece of the source's
+// bf16 O row (r = 512).  The WPH waves of a head meet in LDS.  The host picks
+// WPH so that a wave folds at most kMergeBatch sources, and ZD = 2 when the
+// sequences and heads alone give fewer blocks than CUs: the kernel's time is
+// then about one round of loads, spread over the whole chip.  The tile prefix
+// of the plan comes from the workspace, where the split-KV kernel left it.
+constexpr int kMergeBatch = 16;    // sources in flight per wave
 constexpr int kMergeList = 1024;   // sources listed per pass
 
-template <int WPH>
+template <int WPH, int ZD>
 __global__ __launch_bounds__((WPH < 4 ? 4 : WPH) * 64) void merge_kernel(
     const int32_t* __restrict__ plan, int B, int H, int r, int n_wg,
     const char* __restrict__ part, float* __restrict__ o_lat, float* __restrict__ lse) {
+  static_assert(ZD == 1 || ZD == 2, "one or two parts of the latent dims");
   constexpr int kWaves = WPH < 4 ? 4 : WPH;
   constexpr int kHeads = kWaves / WPH;  // heads per block
+  constexpr int kDl = 8 / ZD;           // latent dims per lane
   __shared__ int src[kMergeList];       // slot index p * kSlotsPerWg + slot, or -1 (nothing written)
-  __shared__ f32x4 red[WPH > 1 ? kWaves : 1][2][64];
+  __shared__ f32x4 red[WPH > 1 ? kWaves : 1][kDl / 4][64];
   __shared__ float red_m[kWaves], red_l[kWaves];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = blockIdx.y * kHeads + wave / WPH;  // this wave's head
   const int wi = wave % WPH;                        // its index among the head's waves
-  float* out = o_lat + ((size_t)b * H + h) * r + 8 * lane;
+  const int d0 = blockIdx.z * (r / ZD) + kDl * lane;  // the lane's first latent dim
+  float* out = o_lat + ((size_t)b * H + h) * r + d0;
+  const bool lse_block = blockIdx.z == 0;
   const int Pb = plan[b], Pb1 = plan[b + 1];
   if (Pb1 == Pb) {  // invalid length: zeros and lse = -inf
     if (wi == 0) {
-      *(f32x4*)out = f32x4{0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)(out + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (lane == 0 && lse) lse[(size_t)b * H + h] = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kDl / 4; ++q) *(f32x4*)(out + 4 * q) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (lane == 0 && lse && lse_block) lse[(size_t)b * H + h] = -INFINITY;
     }
     return;
   }
@@ -56,9 +61,11 @@ __global__ __launch_bounds__((WPH < 4 ? 4 : WPH) * 64) void merge_kernel(
   const int p_hi = wg_of(Pb1 - 1, N, n_wg);
   if (p_lo == p_hi) return;  // written directly by the decode kernel
   const size_t slot_bytes = kPartialSlotBytes(H, r);
-  const size_t o_off = (size_t)H * 8 + ((size_t)h * r + 8 * lane) * 2;
+  const size_t o_off = (size_t)H * 8 + ((size_t)h * r + d0) * 2;
   float M = -INFINITY, lsum = 0.f;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[kDl / 4];
+#pragma unroll
+  for (int q = 0; q < kDl / 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int n_src = p_hi - p_lo + 1;
   const int first = p_lo * kSlotsPerWg + merge_slot_of(Pb, p_lo, N, n_wg, p_lo);
   for (int c0 = 0; c0 < n_src; c0 += kMergeList) {
@@ -76,7 +83,7 @@ __global__ __launch_bounds__((WPH < 4 ? 4 : WPH) * 64) void merge_kernel(
       // first workgroup's slot (always written) and gets weight 0, so the
       // loads of all kMergeBatch sources are issued before the first fold.
       float m[kMergeBatch], l[kMergeBatch];
-      uint4 ob[kMergeBatch];
+      uint32_t ob[kMergeBatch][kDl / 2];
       bool ok[kMergeBatch];
 #pragma unroll
       for (int u = 0; u < kMergeBatch; ++u) {
@@ -86,20 +93,28 @@ __global__ __launch_bounds__((WPH < 4 ? 4 : WPH) * 64) void merge_kernel(
         const char* sp = part + (size_t)(ok[u] ? e : first) * slot_bytes;
         m[u] = ((const float*)sp)[h];
         l[u] = ((const float*)sp)[H + h];
-        ob[u] = *(const uint4*)(sp + o_off);
+        if constexpr (ZD == 1) {
+          const uint4 v = *(const uint4*)(sp + o_off);
+          ob[u][0] = v.x; ob[u][1] = v.y; ob[u][2] = v.z; ob[u][3] = v.w;
+        } else {
+          const uint2 v = *(const uint2*)(sp + o_off);
+          ob[u][0] = v.x; ob[u][1] = v.y;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the folds
 #pragma unroll
       for (int u = 0; u < kMergeBatch; ++u) {
-        const f32x4 v0 = {__uint_as_float(ob[u].x << 16), __uint_as_float(ob[u].x & 0xFFFF0000u),
-                          __uint_as_float(ob[u].y << 16), __uint_as_float(ob[u].y & 0xFFFF0000u)};
-        const f32x4 v1 = {__uint_as_float(ob[u].z << 16), __uint_as_float(ob[u].z & 0xFFFF0000u),
-                          __uint_as_float(ob[u].w << 16), __uint_as_float(ob[u].w & 0xFFFF0000u)};
         const float Mn = ok[u] ? fmaxf(M, m[u]) : M;
         const float keep = Mn == M ? 1.f : exp2f(M - Mn);  // also M = Mn = -inf
         const float w = ok[u] ? exp2f(m[u] - Mn) : 0.f;
-        acc0 = acc0 * keep + v0 * w;
-        acc1 = acc1 * keep + v1 * w;
+#pragma unroll
+        for (int q = 0; q < kDl / 4; ++q) {
+          const f32x4 v = {__uint_as_float(ob[u][2 * q] << 16),
+                           __uint_as_float(ob[u][2 * q] & 0xFFFF0000u),
+                           __uint_as_float(ob[u][2 * q + 1] << 16),
+                           __uint_as_float(ob[u][2 * q + 1] & 0xFFFF0000u)};
+          acc[q] = acc[q] * keep + v * w;
+        }
         lsum = lsum * keep + l[u] * w;
         M = Mn;
       }
@@ -107,8 +122,8 @@ __global__ __launch_bounds__((WPH < 4 ? 4 : WPH) * 64) void merge_kernel(
     if (c0 + kMergeList < n_src) __syncthreads();  // the list is rewritten by the next pass
   }
   if constexpr (WPH > 1) {
-    red[wave][0][lane] = acc0;
-    red[wave][1][lane] = acc1;
+#pragma unroll
+    for (int q = 0; q < kDl / 4; ++q) red[wave][q][lane] = acc[q];
     if (lane == 0) {
       red_m[wave] = M;
       red_l[wave] = lsum;
@@ -118,35 +133,49 @@ __global__ __launch_bounds__((WPH < 4 ? 4 : WPH) * 64) void merge_kernel(
     float Mt = -INFINITY;
 #pragma unroll
     for (int k = 0; k < WPH; ++k) Mt = fmaxf(Mt, red_m[wave + k]);
-    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 t[kDl / 4];
+#pragma unroll
+    for (int q = 0; q < kDl / 4; ++q) t[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     float lt = 0.f;
 #pragma unroll
     for (int k = 0; k < WPH; ++k) {
       const float mk = red_m[wave + k];
       if (mk == -INFINITY) continue;  // a wave that held no source
       const float w = exp2f(mk - Mt);
-      t0 += red[wave + k][0][lane] * w;
-      t1 += red[wave + k][1][lane] * w;
+#pragma unroll
+      for (int q = 0; q < kDl / 4; ++q) t[q] += red[wave + k][q][lane] * w;
       lt += red_l[wave + k] * w;
     }
-    acc0 = t0;
-    acc1 = t1;
+#pragma unroll
+    for (int q = 0; q < kDl / 4; ++q) acc[q] = t[q];
     lsum = lt;
     M = Mt;
   }
   const float inv = 1.0f / lsum;
-  *(f32x4*)out = acc0 * inv;
-  *(f32x4*)(out + 4) = acc1 * inv;
-  if (lane == 0 && lse) lse[(size_t)b * H + h] = (M + log2f(lsum)) * kLn2;
+#pragma unroll
+  for (int q = 0; q < kDl / 4; ++q) *(f32x4*)(out + 4 * q) = acc[q] * inv;
+  if (lane == 0 && lse && lse_block) lse[(size_t)b * H + h] = (M + log2f(lsum)) * kLn2;
 }
 
-template <int WPH>
-static void launch_merge_wph(int nv, int H, int r, int n_wg, const int32_t* plan,
+template <int WPH, int ZD>
+static hipError_t launch_merge_wph(int nv, int H, int r, int n_wg, const int32_t* plan,
                              const char* part, float* o_lat, float* lse, hipStream_t s) {
   constexpr int kWaves = WPH < 4 ? 4 : WPH;
   constexpr int kHeads = kWaves / WPH;
-  merge_kernel<WPH><<<dim3(nv, H / kHeads), kWaves * 64, 0, s>>>(plan, nv, H, r, n_wg, part,
-                                                                 o_lat, lse);
+  return launch_kernel(merge_kernel<WPH, ZD>, dim3(nv, H / kHeads, ZD), dim3(kWaves * 64), s,
+                       plan, nv, H, r, n_wg, part, o_lat, lse);
+}
+
+template <int ZD>
+static hipError_t launch_merge_zd(int wph, int nv, int H, int r, int n_wg, const int32_t* plan,
+                                  const char* part, float* o_lat, float* lse, hipStream_t s) {
+  switch (wph) {
+    case 1: return launch_merge_wph<1, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
+    case 2: return launch_merge_wph<2, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
+    case 4: return launch_merge_wph<4, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
+    case 8: return launch_merge_wph<8, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
+    default: return launch_merge_wph<16, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
+  }
 }
 
 hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, void* workspace,
@@ -157,19 +186,17 @@ hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, vo
   // Sources of a sequence: the workgroups its tiles span, about n_wg / nv + 1
   // when the lengths are even.  WPH = the power of two that gives each wave
   // about kMergeBatch of them (at most 16 waves per head).
-  const int per_seq = (n_wg + nv - 1) / nv + 1;
+  // (a sequence of exactly n_wg / nv workgroups' tiles has no extra source)
+  const int per_seq = n_wg % nv == 0 ? n_wg / nv : n_wg / nv + 2;
   int wph = 1;
   while (wph < 16 && wph * kMergeBatch < per_seq) wph *= 2;
   const int32_t* plan = (const int32_t*)(wsb + ws.plan);
   const char* part = (const char*)(wsb + ws.partials);
-  switch (wph) {
-    case 1: launch_merge_wph<1>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
-    case 2: launch_merge_wph<2>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
-    case 4: launch_merge_wph<4>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
-    case 8: launch_merge_wph<8>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
-    default: launch_merge_wph<16>(nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s); break;
-  }
-  return hipGetLastError();
+  const int heads_per_block = wph < 4 ? 4 / wph : 1;
+  const long blocks = (long)nv * (c.H / heads_per_block);
+  if (blocks < 256)  // too few to fill the CUs: split the latent dims in two
+    return launch_merge_zd<2>(wph, nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s);
+  return launch_merge_zd<1>(wph, nv, c.H, c.r, n_wg, plan, part, o_lat, lse, s);
 }
 
 // One block per (b, h); threads over the d_v outputs.
@@ -256,9 +283,13 @@ __global__ __launch_bounds__(256) void out_proj_mfma_kernel(const float* __restr
   }
 }
 
+bool out_proj_uses_mfma(const Cfg& c) {
+  return c.dtype == QKMLA_BF16 && c.hpg == 16 && c.r % kOpChunkK == 0 && c.dv % 16 == 0;
+}
+
 hipError_t launch_out_proj(const Cfg& c, int batch, const float* o_lat, const void* w_uv,
                            float* out, hipStream_t s) {
-  if (c.dtype == QKMLA_BF16 && c.hpg == 16 && c.r % kOpChunkK == 0 && c.dv % 16 == 0) {
+  if (out_proj_uses_mfma(c)) {
     out_proj_mfma_kernel<<<dim3(batch, c.G, (c.dv + kOpChunkN - 1) / kOpChunkN), 256, 0, s>>>(
         o_lat, (const uint16_t*)w_uv, out, c.H, c.r, c.dv);
   } else if (c.dtype == QKMLA_BF16)

@@ -191,6 +191,16 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* s
                               const Paging& pg, const void* lat, const void* rope,
                               const float* alpha, const WsLayout& ws, void* workspace, int n_wg,
                               float* o_lat, float* lse, hipStream_t s);
+// Launch k on stream s and return the launch's status.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, A... a) {
+  k<<<grid, block, 0, s>>>(static_cast<P>(a)...);
+  return hipGetLastError();
+}
+
+// Whether launch_out_proj takes the MFMA kernel, which reads o_lat and W^UV
+// as 16-byte vectors (so both must be 16-byte aligned).
+bool out_proj_uses_mfma(const Cfg& c);
 hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, void* workspace,
                         int n_wg, float* o_lat, float* lse, hipStream_t s);
 hipError_t launch_decode_generic(const Cfg& c, int batch, int s_q, const int32_t* seq_lens,

@@ -204,29 +204,29 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
 }
 
 template <int SPB, int KS>
-static void launch_qprep_bf16(const Cfg& c, int nv, int s_q, const void* q_c, const void* q_rope,
+static hipError_t launch_qprep_bf16(const Cfg& c, int nv, int s_q, const void* q_c, const void* q_rope,
                               const void* w_qabs, const float* gqr, const int32_t* seq_lens,
                               const Paging& pg, const RopeFreq& rf, char* wsb, const WsLayout& ws,
                               int32_t* status, hipStream_t s) {
-  qprep_mfma_kernel<SPB, KS><<<dim3((nv + SPB - 1) / SPB, c.G, c.r / kQpCols + 1), 256, 0, s>>>(
-      (const uint16_t*)q_c, (const uint16_t*)q_rope, (const uint16_t*)w_qabs, gqr, seq_lens, nv,
-      s_q, pg, c.H, c.r, c.dr, c.eps, c.tau, c.qk_norm, rf, (uint16_t*)(wsb + ws.q_tilde),
-      (float*)(wsb + ws.alpha_q), (uint16_t*)(wsb + ws.q_rope), status);
+  return launch_kernel(qprep_mfma_kernel<SPB, KS>,
+                       dim3((nv + SPB - 1) / SPB, c.G, c.r / kQpCols + 1), dim3(256), s, (const uint16_t*)q_c, (const uint16_t*)q_rope,
+                (const uint16_t*)w_qabs, gqr, seq_lens, nv, s_q, pg, c.H, c.r, c.dr, c.eps, c.tau,
+                c.qk_norm, rf, (uint16_t*)(wsb + ws.q_tilde), (float*)(wsb + ws.alpha_q),
+                (uint16_t*)(wsb + ws.q_rope), status);
 }
 
 template <int SPB>
-static void launch_qprep_spb(const Cfg& c, int nv, int s_q, const void* q_c, const void* q_rope,
+static hipError_t launch_qprep_spb(const Cfg& c, int nv, int s_q, const void* q_c, const void* q_rope,
                              const void* w_qabs, const float* gqr, const int32_t* seq_lens,
                              const Paging& pg, const RopeFreq& rf, char* wsb, const WsLayout& ws,
                              int32_t* status, hipStream_t s) {
-#define QP_CASE(K)                                                                            \
-  case K:                                                                                     \
-    launch_qprep_bf16<SPB, K>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws, \
-                              status, s);                                                     \
-    break;
+#define QP_CASE(K)                                                                           \
+  case K:                                                                                    \
+    return launch_qprep_bf16<SPB, K>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, \
+                                     wsb, ws, status, s);
   switch (c.dc / 32) {
     QP_CASE(1) QP_CASE(2) QP_CASE(3) QP_CASE(4) QP_CASE(5) QP_CASE(6) QP_CASE(7) QP_CASE(8)
-    default: break;
+    default: return hipErrorInvalidValue;
   }
 #undef QP_CASE
 }
@@ -290,16 +290,16 @@ hipError_t launch_qprep(const Cfg& c, int batch, int s_q, const void* q_c, const
   if (c.dtype == QKMLA_BF16) {
     // SPB sequences share a block's W~ loads once the batch gives enough blocks.
     if (nv >= 16)
-      launch_qprep_spb<4>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws, status, s);
-    else
-      launch_qprep_spb<1>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws, status, s);
+      return launch_qprep_spb<4>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws,
+                                 status, s);
+    return launch_qprep_spb<1>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws,
+                               status, s);
   } else {
-    qprep_generic_kernel<<<dim3(nv, c.H), 256, 0, s>>>(
-        (const float*)q_c, (const float*)q_rope, (const float*)w_qabs, gqr, seq_lens, s_q, pg, c.H,
-        c.G, c.r, c.dc, c.dr, c.eps, c.tau, c.qk_norm, rf, (float*)(wsb + ws.q_tilde),
-        (float*)(wsb + ws.alpha_q), (float*)(wsb + ws.q_rope), status);
+    return launch_kernel(qprep_generic_kernel, dim3(nv, c.H), dim3(256), s, (const float*)q_c,
+                  (const float*)q_rope, (const float*)w_qabs, gqr, seq_lens, s_q, pg, c.H, c.G,
+                  c.r, c.dc, c.dr, c.eps, c.tau, c.qk_norm, rf, (float*)(wsb + ws.q_tilde),
+                  (float*)(wsb + ws.alpha_q), (float*)(wsb + ws.q_rope), status);
   }
-  return hipGetLastError();
 }
 
 }  // namespace qkmla

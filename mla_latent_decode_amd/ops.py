@@ -93,6 +93,7 @@ def _load():
         "qkmla_plan_segments": (I32, [I32, P, I32, I32, P, I32, ctypes.POINTER(I32)]),
         "qkmla_plan_merge_sources": (I32, [I32, P, I32, I32, I32, P, I32, ctypes.POINTER(I32)]),
         "qkmla_profile_begin": (I32, []),
+        "qkmla_profile_begin_reps": (I32, [I32]),
         "qkmla_profile_end": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
         "qkmla_profile_end_detail": (I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]),
     }
@@ -171,10 +172,11 @@ def abi_version() -> int:
     return _lib.qkmla_abi_version()
 
 
-def profile_begin():
+def profile_begin(reps: int = 1):
     """Start recording HIP events around the q-prep, split-KV and merge
-    launches of each decode call."""
-    _check(_lib.qkmla_profile_begin(), "qkmla_profile_begin")
+    launches of each decode call; with reps > 1 each kernel is launched reps
+    times back to back between its events and the figures are per launch."""
+    _check(_lib.qkmla_profile_begin_reps(int(reps)), "qkmla_profile_begin_reps")
 
 
 def profile_end():

@@ -80,6 +80,12 @@ hipError_t hipLaunchKernel(const void* f, dim3 g, dim3 b, void** args, size_t sh
   fprintf(stderr, "fakehip: launch of an unregistered function\n");
   abort();
 }
+/* the timed launch of the measurement hook: events are not modelled */
+hipError_t hipExtLaunchKernel(const void* f, dim3 g, dim3 b, void** args, size_t shmem,
+                              void* stream, void* start, void* stop, int flags) {
+  (void)start; (void)stop; (void)flags;
+  return hipLaunchKernel(f, g, b, args, shmem, stream);
+}
 hipError_t hipGetLastError(void) { int e = g_last_err; g_last_err = 0; return e; }
 const char* hipGetErrorString(hipError_t e) { return e ? "emulated launch failed" : "no error"; }
 hipError_t hipGetDevice(int* d) { *d = 0; return 0; }

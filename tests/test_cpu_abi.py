@@ -37,7 +37,7 @@ def _ops():
 
 def test_abi_version_and_status_strings():
     ops = _ops()
-    assert ops.abi_version() == 7
+    assert ops.abi_version() == 8
     assert ops._lib.qkmla_status_string(0) == b"ok"
     assert ops._lib.qkmla_status_string(3) == b"workspace too small"
 
@@ -100,6 +100,20 @@ def test_null_and_misaligned_pointers_are_rejected():
     fake = ctypes.c_void_p(0x1000 + 2)  # misaligned for float, never dereferenced
     st = lib.qkmla_out_proj(ctypes.byref(cfg.c()), 1, fake, fake, fake, None)
     assert st == 1 and b"aligned" in lib.qkmla_last_error()
+
+
+def test_mfma_out_proj_requires_16_byte_alignment():
+    """The bf16 V up-projection of the DeepSeek-V3-like layer reads o_lat and
+    W^UV as 16-byte vectors: pointers aligned to their element size but not to
+    16 bytes are rejected before any launch."""
+    ops = _ops()
+    cfg = _cfg(dtype="bf16")
+    lib = ops._lib
+    ok16 = ctypes.c_void_p(0x10000)
+    off4 = ctypes.c_void_p(0x10000 + 4)  # float-aligned, not 16-byte aligned; never dereferenced
+    for o_lat, w_uv in ((off4, ok16), (ok16, off4)):
+        st = lib.qkmla_out_proj(ctypes.byref(cfg.c()), 1, o_lat, w_uv, ok16, None)
+        assert st == 1 and b"16-byte" in lib.qkmla_last_error()
 
 
 def test_decode_rejects_bad_length_bound():

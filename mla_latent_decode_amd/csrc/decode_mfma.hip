@@ -58,6 +58,7 @@ constexpr int kStageBytes = kLatBytes + kRopeBytes + kAlphaBytes;
 // regions per stage buffer.
 constexpr int kEpiRow = 512 + 16;
 constexpr int kEpiRegion = 32 * kEpiRow;
+constexpr int kEpiBatch = 8;  // LDS rows read ahead of their stores
 static_assert(2 * kEpiRegion <= kStageBytes, "two epilogue regions per stage buffer");
 // p = 2^(logit - m_ref) may exceed 1; a segment is streamed again with a
 // raised reference only if some p would exceed 2^kOverflowLog2.
@@ -609,11 +610,17 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
     asm volatile("" : "+v"(ln));
     const int en = ln & 31, ehf = ln >> 5;
     char* region = (wave >> 1 == 0 ? stage_buf<0>() : stage_buf<1>()) + (wave & 1) * kEpiRegion;
+    // Each round reads its 16 LDS rows kEpiBatch at a time into registers
+    // before their stores, so the reads overlap and a store does not wait on
+    // the read just before it.  A store's address is the wave's row block
+    // (scalar) plus a 32-bit lane offset.
     if (complete) {  // normalised o_lat, fp32 rows of 2 KB: four rounds of 128 dims
       const float inv = 1.0f / l_tot;
       char* out = (char*)(a.o_lat + (size_t)b * a.H * kR) + (size_t)(wave * 32) * kR * 4;
+      const uint32_t lane_off = (uint32_t)ehf * (kR * 4) + (uint32_t)en * 16;
 #pragma unroll
       for (int rnd = 0; rnd < kR / 128; ++rnd) {
+        fence();  // one round at a time: its accumulator reads are not hoisted
 #pragma unroll
         for (int mbl = 0; mbl < 4; ++mbl)
 #pragma unroll
@@ -622,12 +629,20 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
             const f32x4 v = {w.O[mb][4 * q] * inv, w.O[mb][4 * q + 1] * inv,
                              w.O[mb][4 * q + 2] * inv, w.O[mb][4 * q + 3] * inv};
             *(f32x4*)(region + en * kEpiRow + (32 * mbl + 8 * q + 4 * ehf) * 4) = v;
+            fence();  // a few accumulator registers in flight at a time
           }
+        fence();
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
-          const int row = 2 * it + ehf;
-          *(uint4*)(out + (size_t)row * kR * 4 + rnd * 512 + en * 16) =
-              *(const uint4*)(region + row * kEpiRow + en * 16);
+        for (int i0 = 0; i0 < 16; i0 += kEpiBatch) {
+          uint4 rows[kEpiBatch];
+#pragma unroll
+          for (int it = 0; it < kEpiBatch; ++it)
+            rows[it] = *(const uint4*)(region + (2 * (i0 + it) + ehf) * kEpiRow + en * 16);
+#pragma unroll
+          for (int it = 0; it < kEpiBatch; ++it)
+            *(uint4*)(out + (size_t)(2 * (i0 + it)) * kR * 4 + rnd * 512 + lane_off) = rows[it];
+          __builtin_amdgcn_sched_group_barrier(0x100, kEpiBatch, 0);  // the LDS reads first,
+          __builtin_amdgcn_sched_group_barrier(0x040, kEpiBatch, 0);  // then the stores
         }
       }
       if (hf == 0 && a.lse) a.lse[qrow] = (m_run + log2f(l_tot)) * kLn2;
@@ -639,8 +654,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
         ((float*)sp)[a.H + head] = l_tot;
       }
       char* Op = sp + (size_t)a.H * 8 + (size_t)(wave * 32) * kR * 2;
+      const uint32_t lane_off = (uint32_t)ehf * (kR * 2) + (uint32_t)en * 16;
 #pragma unroll
       for (int rnd = 0; rnd < kR / 256; ++rnd) {
+        fence();  // one round at a time: its accumulator reads are not hoisted
 #pragma unroll
         for (int mbl = 0; mbl < 8; ++mbl)
 #pragma unroll
@@ -650,12 +667,20 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = (__bf16)w.O[mb][4 * q + j];
             *(bf16x4*)(region + en * kEpiRow + (32 * mbl + 8 * q + 4 * ehf) * 2) = v;
+            fence();  // a few accumulator registers in flight at a time
           }
+        fence();
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
-          const int row = 2 * it + ehf;
-          *(uint4*)(Op + (size_t)row * kR * 2 + rnd * 512 + en * 16) =
-              *(const uint4*)(region + row * kEpiRow + en * 16);
+        for (int i0 = 0; i0 < 16; i0 += kEpiBatch) {
+          uint4 rows[kEpiBatch];
+#pragma unroll
+          for (int it = 0; it < kEpiBatch; ++it)
+            rows[it] = *(const uint4*)(region + (2 * (i0 + it) + ehf) * kEpiRow + en * 16);
+#pragma unroll
+          for (int it = 0; it < kEpiBatch; ++it)
+            *(uint4*)(Op + (size_t)(2 * (i0 + it)) * kR * 2 + rnd * 512 + lane_off) = rows[it];
+          __builtin_amdgcn_sched_group_barrier(0x100, kEpiBatch, 0);  // the LDS reads first,
+          __builtin_amdgcn_sched_group_barrier(0x040, kEpiBatch, 0);  // then the stores
         }
       }
     }

@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
   }
 
   // ---- q~ columns [z kQpCols, (z+1) kQpCols) of SPB sequences ----
-  __shared__ __attribute__((aligned(16))) uint16_t tile[16 * SPB][kQpCols];
+  // (rows padded by 16 bytes: the column-wise reads below hit distinct banks)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[16 * SPB][kQpCols + 8];
   const int m = lane & 15, kq = lane >> 4;
   const uint16_t* W = w_qabs + (size_t)g * r * dc;
   const int n0 = z * kQpCols + wave * 32;
@@ -192,13 +193,15 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(
       tile[16 * sq + hh][wave * 32 + 16 + m] = f32_to_bf16(acc[sq][1][i] * sc);
     }
   __syncthreads();
-  // 16 SPB rows x 128 columns of bf16, 16 bytes per thread and step
+  // 16 SPB rows x 128 columns of bf16, 16 bytes per thread and step; the 16
+  // threads of a group take the 16 heads of one 8-column chunk, which lie
+  // contiguous in the operand order (256 bytes per group).
 #pragma unroll
   for (int it = 0; it < SPB; ++it) {
-    const int row = it * 16 + (tid >> 4), c8 = (tid & 15) * 8;
-    const int b = b0 + row / 16;
+    const int row = it * 16 + (tid & 15), c8 = (tid >> 4) * 8;
+    const int b = b0 + it;
     if (b < nv)
-      *(uint4*)(q_tilde + qop_index(b, H, r, h0 + row % 16, z * kQpCols + c8)) =
+      *(uint4*)(q_tilde + qop_index(b, H, r, h0 + (tid & 15), z * kQpCols + c8)) =
           *(const uint4*)&tile[row][c8];
   }
 }

@@ -154,6 +154,33 @@ class Bench:
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
 
+    def time_steps_paired(self, steps, warmup, block=5):
+        """Eager step times of QK-norm and plain MLA, taken in alternating
+        blocks of `block` steps (HIP events around each block), so that both
+        modes run under the same clock state: under sustained load the chip
+        lowers its clock within a millisecond or two, and two back-to-back
+        runs would compare a cool mode with a throttled one.  Returns
+        (ms per QK-norm step, ms per plain step)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+            self.step(plain=True)
+        torch.cuda.synchronize()
+        n_blocks = max(1, -(-steps // block))
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_blocks)] for _ in range(2)]
+        for k in range(n_blocks):
+            for mode in (0, 1):
+                e0, e1 = ev[mode][k]
+                e0.record()
+                for _ in range(block):
+                    self.step(plain=bool(mode))
+                e1.record()
+        torch.cuda.synchronize()
+        per = [sum(e0.elapsed_time(e1) for e0, e1 in ev[mode]) / (n_blocks * block)
+               for mode in (0, 1)]
+        return per[0], per[1]
+
     def step_spread(self, steps, rotate=True):
         """Per-step times (eager launches, a HIP event pair around each step):
         (p10, p50, p90) in ms.  rotate=False streams one cache copy every
@@ -178,14 +205,10 @@ class Bench:
         return _event_ms(self.torch, lambda: self.ops.out_proj(self.cfg, self.o_lat, self.w_uv,
                                                                self.o_out), steps)
 
-    def graph_time(self, steps, plain=False):
-        """Step time with the step captured in HIP graphs: one step per cache
-        copy captured in turn (torch.cuda.graph on its capture stream, where
-        the library launches), then replayed.  This takes the host's launch
-        overhead out of the timeline, as a serving loop replaying a captured
-        decode step would.  Every checked replay must reproduce the eager
-        step's o_lat and lse bit for bit.  Returns (ms per step, None), or
-        (None, reason) when capture fails or a replay differs."""
+    def _capture(self, plain):
+        """One HIP graph of n_copies steps (one per cache copy), checked bit
+        for bit against the eager step over three replays.  Returns
+        (graph, None) or (None, reason)."""
         torch = self.torch
         try:
             self.i = self.n_copies - 1
@@ -214,21 +237,61 @@ class Bench:
                 torch.cuda.synchronize()
                 if not (torch.equal(self.o_lat, ref_lat) and torch.equal(self.lse, ref_lse)):
                     return None, "a graph replay differs from the eager step"
-            reps = max(1, -(-steps // self.n_copies))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / (reps * self.n_copies), None
+            return g, None
         except Exception as ex:  # noqa: BLE001 -- reported in the JSON line, eager timing stands
             return None, f"graph capture failed: {type(ex).__name__}: {ex}"
+
+    def graph_time_paired(self, steps):
+        """Graph-replayed step times of QK-norm and plain MLA, replays of the
+        two graphs alternating (HIP events around each replay), for the same
+        reason as time_steps_paired.  Returns ((ms QK-norm, ms plain), None)
+        or (None, reason)."""
+        torch = self.torch
+        gq, why = self._capture(False)
+        if gq is None:
+            return None, why
+        gp, why = self._capture(True)
+        if gp is None:
+            return None, why
+        reps = max(1, -(-steps // self.n_copies))
+        for _ in range(2):
+            gq.replay()
+            gp.replay()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)] for _ in range(2)]
+        torch.cuda.synchronize()
+        for k in range(reps):
+            for mode, g in ((0, gq), (1, gp)):
+                e0, e1 = ev[mode][k]
+                e0.record()
+                g.replay()
+                e1.record()
+        torch.cuda.synchronize()
+        per = [sum(e0.elapsed_time(e1) for e0, e1 in ev[mode]) / (reps * self.n_copies)
+               for mode in (0, 1)]
+        return (per[0], per[1]), None
 
     def kernel_ms(self, steps, plain=False):
         """Average duration of the split-KV kernel over `steps` steps (HIP events
         recorded by the library around each launch on the launch stream)."""
         return self.kernel_breakdown_ms(steps, plain)[1]
+
+    def kernel_breakdown_paired(self, steps, reps=8, block=2):
+        """kernel_breakdown_ms for QK-norm and plain MLA in alternating blocks
+        of `block` decode calls, for the same reason as time_steps_paired.
+        Returns ((q-prep, split-KV, merge) ms QK-norm, the same for plain)."""
+        tot = [[0.0, 0.0, 0.0], [0.0, 0.0, 0.0]]
+        cnt = [0, 0]
+        for _ in range(max(1, -(-steps // block))):
+            for mode in (0, 1):
+                self.ops.profile_begin(reps)
+                for _ in range(block):
+                    self.step(plain=bool(mode))
+                ms, n = self.ops.profile_end_detail()
+                for j in range(3):
+                    tot[mode][j] += ms[j]
+                cnt[mode] += n
+        return tuple(tuple(t / max(c, 1) for t in tot[m]) for m, c in zip((0, 1), cnt))
 
     def kernel_breakdown_ms(self, steps, plain=False, reps=8):
         """Average (q-prep, split-KV, merge) durations per launch over `steps`
@@ -283,8 +346,8 @@ def pmc_workload(steps=5, cid=1):
                       "algorithmic_bytes_per_launch": b.bytes_qk}), flush=True)
 
 
-def _pmc_per_dispatch(csv_path, counter):
-    """{kernel name: [counter value of each dispatch, in dispatch order]} from a
+def _pmc_dispatches(csv_path, counter):
+    """[(dispatch id, kernel name, counter value)] in dispatch order from a
     rocprofv3 counter-collection CSV (columns Dispatch_Id, Kernel_Name,
     Counter_Name, Counter_Value; several rows of one dispatch are summed)."""
     import csv
@@ -293,10 +356,15 @@ def _pmc_per_dispatch(csv_path, counter):
         for row in csv.DictReader(f):
             if row.get("Counter_Name", "").split("[")[0] != counter:
                 continue
-            key = (row["Kernel_Name"], int(row.get("Dispatch_Id", "0") or 0))
+            key = (int(row.get("Dispatch_Id", "0") or 0), row["Kernel_Name"])
             per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    return [(d, name, v) for (d, name), v in sorted(per.items())]
+
+
+def _pmc_per_dispatch(csv_path, counter):
+    """{kernel name: [counter value of each dispatch, in dispatch order]}."""
     out = {}
-    for (name, _), v in sorted(per.items(), key=lambda kv: kv[0][1]):
+    for _, name, v in _pmc_dispatches(csv_path, counter):
         out.setdefault(name, []).append(v)
     return out
 
@@ -310,20 +378,31 @@ def traffic_from_pmc(fetch_csv, write_csv, workload, algorithmic_bytes):
     """HBM bytes per launch of the QK-norm split-KV kernel: its FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
     for the plain copy of COPY_BYTES in the same run."""
-    fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
-    write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    fetch_seq = _pmc_dispatches(fetch_csv, "FETCH_SIZE")
+    write_seq = _pmc_dispatches(write_csv, "WRITE_SIZE")
+    fetch, write = {}, {}
+    for seq, d in ((fetch_seq, fetch), (write_seq, write)):
+        for _, name, v in seq:
+            d.setdefault(name, []).append(v)
 
     def pick(d, want, what):
         names = [k for k in d if want(k)]
         if len(names) != 1:
             raise ValueError(f"expected one {what} kernel, found {names}")
         return d[names[0]]
-    # the calibration copies are the workload's last three copy dispatches
-    # (the cache fill before the decode steps also copies, in other sizes)
+    # the calibration copies are the run's last three copy dispatches, whatever
+    # kernel torch picks for them (the cache set-up before the decode steps
+    # copies too, through other kernels and in other sizes)
     is_copy = lambda k: "copy" in k.lower() and "decode" not in k  # noqa: E731
     mean = lambda v: sum(v) / len(v)  # noqa: E731
+
+    def calibration(seq, what):
+        cps = [v for _, name, v in seq if is_copy(name)][-3:]
+        if len(cps) != 3:
+            raise ValueError(f"expected three calibration copies in the {what} run, found {len(cps)}")
+        return mean(cps)
     f_dec, w_dec = mean(pick(fetch, _is_qk_splitkv, "split-KV")), mean(pick(write, _is_qk_splitkv, "split-KV"))
-    f_cp, w_cp = mean(pick(fetch, is_copy, "copy")[-3:]), mean(pick(write, is_copy, "copy")[-3:])
+    f_cp, w_cp = calibration(fetch_seq, "FETCH_SIZE"), calibration(write_seq, "WRITE_SIZE")
     kf, kw = COPY_BYTES / (f_cp * 1024.0), COPY_BYTES / (w_cp * 1024.0)
     hbm = f_dec * 1024.0 * kf + w_dec * 1024.0 * kw
     return {workload: {"hbm_bytes_per_launch": round(hbm), "fetch_KiB": f_dec, "write_KiB": w_dec,
@@ -336,16 +415,19 @@ def traffic_from_pmc(fetch_csv, write_csv, workload, algorithmic_bytes):
 
 def measure(cid, steps, warmup, graph=True):
     b = Bench(cid)
-    ms_eager, wall = b.time_steps(steps, warmup)
-    ms_plain_eager, _ = b.time_steps(steps, warmup, plain=True)
-    qp_ms, k_ms, mg_ms = b.kernel_breakdown_ms(steps)
-    k_ms_plain = b.kernel_ms(steps, plain=True)
+    t0 = time.perf_counter()
+    ms_eager, ms_plain_eager = b.time_steps_paired(steps, warmup)
+    wall = time.perf_counter() - t0
+    (qp_ms, k_ms, mg_ms), (_, k_ms_plain, _) = b.kernel_breakdown_paired(steps)
     p10, p50, p90 = b.step_spread(steps)
     w10, w50, w90 = b.step_spread(steps, rotate=False)
     op_ms = b.out_proj_ms(steps)
-    g_ms, g_note = b.graph_time(steps) if graph else (None, "not requested")
-    g_ms_plain, g_note_plain = b.graph_time(steps, plain=True) if g_ms else (None, g_note)
-    use_graph = g_ms is not None and g_ms_plain is not None
+    if graph:
+        g_pair, g_note = b.graph_time_paired(steps)
+    else:
+        g_pair, g_note = None, "not requested"
+    g_ms, g_ms_plain = g_pair if g_pair else (None, None)
+    use_graph = g_pair is not None
     ms_qk = g_ms if use_graph else ms_eager
     ms_plain = g_ms_plain if use_graph else ms_plain_eager
     us = ms_qk * 1e3
@@ -355,7 +437,7 @@ def measure(cid, steps, warmup, graph=True):
         "context": b.lengths[0] if len(set(b.lengths)) == 1 else f"ragged sum={b.tokens}",
         "us_per_step": round(us, 2),
         "step_timing": "graph replay" if use_graph else "eager launches",
-        "graph_note": None if use_graph else (g_note or g_note_plain),
+        "graph_note": None if use_graph else g_note,
         "us_per_step_eager": round(ms_eager * 1e3, 2),
         "us_per_step_eager_p10_p50_p90": [round(x * 1e3, 2) for x in (p10, p50, p90)],
         "warm_us_per_step_eager_p50": round(w50 * 1e3, 2),

@@ -137,6 +137,27 @@ struct Args {
   float* lse;
 };
 
+// Row m of a tile's logits (the QK accumulator's token index) is token
+// slot_token(m) of the tile: bits (m4 m3 m2 m1 m0) -> (m4 m1 m0 m3 m2).  The
+// RoPE and alpha parts of a stage are stored in this slot order; latent rows
+// are stored in token order and the QK reads pick row slot_token(m).  With
+// the 1072-byte row stride (268 dwords, 12 mod 64 banks) this keeps both
+// latent read patterns free of LDS bank conflicts:
+//   QK (ds_read_b128, 16 lanes a pass): lanes m = 0..15 read rows
+//     slot_token(m), 16 distinct values mod 16, so 16 distinct 4-bank groups;
+//   PV (ds_read_b64_tr_b16, 32 lanes a pass): the four token rows that one
+//     16-lane group transposes are accumulator rows 4e + c0 (e = 0..3), i.e.
+//     latent rows 4e' + c1, 48 banks apart mod 64: four disjoint 16-bank runs.
+__host__ __device__ constexpr int slot_token(int m) {
+  return (m & 16) | ((m & 3) << 2) | ((m >> 2) & 3);
+}
+constexpr bool slot_token_is_a_permutation() {
+  unsigned seen = 0;
+  for (int m = 0; m < kTile; ++m) seen |= 1u << slot_token(m);
+  return kTile == 32 && seen == 0xffffffffu;
+}
+static_assert(slot_token_is_a_permutation(), "slot order covers the 32 tokens of a tile");
+
 // Loads per wavefront per tile (all wavefronts issue the same count).
 template <bool QKN, int NW>
 struct TileLoads {
@@ -179,11 +200,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
 // Issue the direct global->LDS loads of tile `tile` (of its sequence) into
 // stage S.  LDS layout of a stage:
 //   latent: token-major rows of kLatRow bytes (1 KB of data + 48 B pad); one
-//           load instruction moves one row.  The 1072-byte stride (67 16-byte
-//           units, 3 mod 16) spreads both the QK row reads and the transposed
-//           PV reads over distinct bank groups.
-//   rope:   chunk-major, position 32*c + t for 16-byte chunk c of token t.
-//   alpha:  [g][32 tokens] floats.
+//           load instruction moves one row.
+//   rope:   chunk-major, position 32*c + m for 16-byte chunk c of the token
+//           in slot m (token slot_token(m)).
+//   alpha:  [g][32 slots] floats, slot m holding token slot_token(m).
 // Rows past the end of the sequence repeat its last row (masked later).
 template <bool QKN, int NW, int S>
 __device__ __forceinline__ void issue_tile(const Seq& sq, const Paging& pg, int G, int tile,
@@ -231,8 +251,9 @@ __device__ __forceinline__ void issue_tile(const Seq& sq, const Paging& pg, int 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rsrc, QK_LDS(void, st + tr * kLatRow), 16,
                                              (int)lane16, min(tr, last) * (kR * 2), 0, 0);
   }
-  const int t = lane & 31;
-  const uint32_t rr = (uint32_t)min(t, last);
+  int slot = lane & 31;
+  asm volatile("" : "+v"(slot));  // recomputed per tile rather than held live
+  const uint32_t rr = (uint32_t)min(slot_token(slot), last);
   const __amdgpu_buffer_rsrc_t rope_rsrc =
       tile_rsrc(sq.rope + prow0 * (kDr * 2), kTile * kDr * 2);
   const uint32_t rope_off = rr * (kDr * 2) + ((uint32_t)(lane >> 5) << 4);
@@ -258,6 +279,31 @@ __device__ __forceinline__ void issue_tile(const Seq& sq, const Paging& pg, int 
   }
 }
 
+// The two halves of a head (lanes l and l ^ 32) combined: v_permlane32_swap
+// trades lanes 32..63 of one register with lanes 0..31 of another, so with x
+// in both, the two results hold x of this lane and of its partner in some
+// order in every lane; their sum or max is the same in both lanes.  No LDS
+// and no lane index are needed.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// This lane's index in its wavefront, computed where it is used: an opaque
+// computation that the compiler cannot share with an earlier one, which it
+// would otherwise keep live (in a spilled register) across the tile loop.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Order fence: the compiler's scheduler keeps instructions on their side, so
 // the software pipelines below issue in the order they are written.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -269,18 +315,24 @@ constexpr int kPvSteps = 2 * (kR / 32);         // 32: 2 token halves x 16 dim b
 constexpr int kPvAhead = 3;                     // C^T operands in flight ahead of the PV MFMAs
 
 // Softmax weights of one tile (exp2 domain), computed a few instructions at a
-// time between the MFMAs of the next tile's logits.  In: lg, the lane's 16
-// logits (reg j: token 8(j/4) + 4hf + j%4 of its head), row-column scaled and
-// masked.  Out: pb, the bf16 weights p = 2^(lg - m_ref) as the B operand of
-// P.C, and the running sum of the weights as rounded.
+// time between the MFMAs of the previous tile's P.C (whose MFMAs leave the
+// issue slots free; the logits' MFMAs are busy with their own operands).  In:
+// lg, the lane's 16 logits (reg j: logits row 8(j/4) + 4hf + j%4 of its head),
+// row-column scaled and masked.  Out: pn, the bf16 weights p = 2^(lg - m_ref)
+// as the B operand of the tile's P.C (pb once that starts), and the running
+// sum of the weights as rounded.
 struct Soft {
   float lg[16];
   float mx[4];
   float e[16];
-  bf16x8 pb[2];
+  bf16x8 pb[2];  // weights of the tile whose P.C runs now
+  bf16x8 pn[2];  // weights of the next tile, being computed
 };
 
-// Step s (0 <= s < kQkSteps) of the softmax schedule.  The first tile of a
+constexpr int kSoftSteps = 30;  // the schedule below, spread over the P.C steps
+static_assert(kSoftSteps <= kPvSteps, "softmax schedule fits the P.C steps");
+
+// Step s (0 <= s < kSoftSteps) of the softmax schedule.  The first tile of a
 // segment sets the per-head reference m_ref (the only place where the two
 // halves of a head, lanes l and l ^ 32, exchange their maxima); a later tile
 // only checks its own lanes against it: a logit more than 2^kOverflowLog2
@@ -296,13 +348,13 @@ __device__ __forceinline__ void soft_step(int s, Wave& w, Soft& sf, int wave) {
   } else if (s == 4) {
     const float mt = fmaxf(fmaxf(sf.mx[0], sf.mx[1]), fmaxf(sf.mx[2], sf.mx[3]));
     if (!w.have_ref) {  // first tile of the segment: the per-head reference
-      w.m_ref = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      w.m_ref = halves_max(mt);
       w.have_ref = true;
     }
     sf.mx[0] = mt;
   } else if (s == 5) {
     if (__ballot(sf.mx[0] > w.m_ref + kOverflowLog2) != 0) {
-      w.m_ref = fmaxf(w.m_ref, fmaxf(sf.mx[0], __shfl_xor(sf.mx[0], 32, 64)));
+      w.m_ref = fmaxf(w.m_ref, halves_max(sf.mx[0]));
       lds_restart[wave] = 1;
     }
   } else if (s < 22) {
@@ -312,19 +364,16 @@ __device__ __forceinline__ void soft_step(int s, Wave& w, Soft& sf, int wave) {
     sf.e[j] = __builtin_amdgcn_exp2f(sf.lg[j] - w.m_ref);
     if (j & 1) {
       const int k = j >> 1;  // weights 2k, 2k + 1
-      sf.pb[k >> 2][2 * (k & 3)] = (__bf16)sf.e[2 * k];
-      sf.pb[k >> 2][2 * (k & 3) + 1] = (__bf16)sf.e[2 * k + 1];
-      if ((k & 3) == 3) asm volatile("" : "+v"(sf.pb[k >> 2]));
+      sf.pn[k >> 2][2 * (k & 3)] = (__bf16)sf.e[2 * k];
+      sf.pn[k >> 2][2 * (k & 3) + 1] = (__bf16)sf.e[2 * k + 1];
+      if ((k & 3) == 3) asm volatile("" : "+v"(sf.pn[k >> 2]));
     }
-  } else if (s >= 30 && s < 32) {
-    // l sums the weights as rounded for P.C: each dword holds two bf16,
-    // whose fp32 values are the dword's high half and its low half shifted up
-    const uint32_t* u = (const uint32_t*)&sf.pb[s - 30];
-    float ls = 0.f;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      ls += __uint_as_float(u[d] << 16) + __uint_as_float(u[d] & 0xFFFF0000u);
-    w.l_run += ls;
+  } else if (s < kSoftSteps) {
+    // l sums the weights as rounded for P.C, one dword (two bf16) a step: the
+    // fp32 values are the dword's high half and its low half shifted up
+    const int d = s - 22;
+    const uint32_t u = ((const uint32_t*)&sf.pn[d >> 2])[d & 3];
+    w.l_run += __uint_as_float(u << 16) + __uint_as_float(u & 0xFFFF0000u);
     asm volatile("" : "+v"(w.l_run));
   }
 }
@@ -333,8 +382,7 @@ __device__ __forceinline__ void soft_step(int s, Wave& w, Soft& sf, int wave) {
 // 0..3 over the 64 RoPE dims into sr, then 32 over the latent into sc (the
 // A operand of step s + kQkAhead is read while step s multiplies); then the
 // row-column scaling l = S_c * alpha^k + S_r (QK norm) or S_c + S_r (plain
-// MLA), and the mask of a sequence's last tile.  With SOFT, the softmax of
-// the previous tile (sf) runs between the MFMAs.
+// MLA), and the mask of a sequence's last tile.
 // The logits' MFMAs as inline asm, so that their accumulators can be VGPRs:
 // the compiler gives every builtin MFMA an AGPR accumulator, and with the
 // AGPRs full of O^T it would move a block of O^T out and back around every
@@ -353,13 +401,13 @@ __device__ __forceinline__ void mfma_results_ready(f32x16& x, f32x16& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
 
-template <bool QKN, bool SOFT, int S>
-__device__ __forceinline__ void qk_tile(Wave& w, Soft& sf, float* lg_out, bool last, int tail,
-                                        int wave, int lane, int g) {
+template <bool QKN, int S>
+__device__ __forceinline__ void qk_tile(Wave& w, float* lg_out, bool last, int tail, int wave,
+                                        int lane, int g) {
   const char* st = stage_buf<S>();
   const int hf = lane >> 5;
   const int m = lane & 31;
-  const char* row = st + m * kLatRow + hf * 16;
+  const char* row = st + slot_token(m) * kLatRow + hf * 16;
   const char* rrow = st + kLatBytes + (32 * hf + m) * 16;
   auto qk_a = [&](int s) -> const bf16x8* {
     return (const bf16x8*)(s < kRopeSteps ? rrow + s * 1024 : row + (s - kRopeSteps) * 32);
@@ -387,7 +435,6 @@ __device__ __forceinline__ void qk_tile(Wave& w, Soft& sf, float* lg_out, bool l
       const int q = s + kQkAhead - kQkSteps;  // alpha^k of the lane's tokens 8q+4hf..+3
       ak[q] = *(const f32x4*)(al + 8 * q);
     }
-    if constexpr (SOFT) soft_step(s, w, sf, wave);
   }
   fence();
   mfma_results_ready(sc, sr);
@@ -403,24 +450,28 @@ __device__ __forceinline__ void qk_tile(Wave& w, Soft& sf, float* lg_out, bool l
   // sequence, wave-uniform), and the uniform test keeps the mask code off the
   // other tiles' path.
   if (last) {
-    const int thr = tail - 4 * hf;  // token 4*hf + c is real iff c < thr
+    // reg j is logits row 8*(j/4) + 4*hf + j%4, i.e. token
+    // slot_token(8*(j/4) + j%4) + hf; it is real iff that is below tail
+    const int thr = tail - hf;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (8 * (j >> 2) + (j & 3) >= thr) lg_out[j] = -INFINITY;
+      if (slot_token(8 * (j >> 2) + (j & 3)) >= thr) lg_out[j] = -INFINITY;
   }
 }
 
 // O^T[512 dims][32 heads] += C^T . P^T over the tile in stage S, with B = P
 // straight from the softmax registers (token order permuted to match) and
-// A = C^T from ds_read_b64_tr_b16: lane (in its 16-lane group) reads token
-// 4*hf + (s16>>2) of the 16-token step, 4 dims at 32*mb + 16*dblk +
-// 4*(s16&3); step k = 16*ks + mb.
-template <int S>
-__device__ __forceinline__ void pv_tile(Wave& w, const bf16x8 (&pb)[2], int lane) {
+// A = C^T from ds_read_b64_tr_b16: for step k = 16*ks + mb, lane (in its
+// 16-lane group) reads the token of logits row 16*ks + 4*hf + (s16>>2), which
+// is latent row 16*ks + 4*(s16>>2) + hf (row + 2 for logits rows 8 further
+// on), 4 dims at 32*mb + 16*dblk + 4*(s16&3).  With SOFT, the softmax of the
+// next tile (sf.lg -> sf.pn) runs between the MFMAs.
+template <bool SOFT, int S>
+__device__ __forceinline__ void pv_tile(Wave& w, Soft& sf, int wave, int lane) {
   const char* st = stage_buf<S>();
   const int hf = lane >> 5;
   const int s16 = lane & 15, dblk = (lane >> 4) & 1;
-  const char* pvb = st + (4 * hf + (s16 >> 2)) * kLatRow + 32 * dblk + 8 * (s16 & 3);
+  const char* pvb = st + (4 * (s16 >> 2) + hf) * kLatRow + 32 * dblk + 8 * (s16 & 3);
   auto pv_a = [&](int k) -> const char* {
     return pvb + (16 * (k / (kR / 32))) * kLatRow + 64 * (k % (kR / 32));
   };
@@ -429,7 +480,7 @@ __device__ __forceinline__ void pv_tile(Wave& w, const bf16x8 (&pb)[2], int lane
 #pragma unroll
   for (int k = 0; k < kPvAhead; ++k) {
     plo[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k)));
-    phi[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k) + 8 * kLatRow));
+    phi[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k) + 2 * kLatRow));
   }
 #pragma unroll
   for (int k = 0; k < kPvSteps; ++k) {
@@ -438,11 +489,14 @@ __device__ __forceinline__ void pv_tile(Wave& w, const bf16x8 (&pb)[2], int lane
     const bf16x8 a8 = {plo[slot][0], plo[slot][1], plo[slot][2], plo[slot][3],
                        phi[slot][0], phi[slot][1], phi[slot][2], phi[slot][3]};
     const int mb = k % (kR / 32);
-    w.O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[k / (kR / 32)], w.O[mb], 0, 0, 0);
+    w.O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, sf.pb[k / (kR / 32)], w.O[mb], 0, 0, 0);
     if (k + kPvAhead < kPvSteps) {
       plo[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, pv_a(k + kPvAhead)));
       phi[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          QK_LDS(bf16x4, pv_a(k + kPvAhead) + 8 * kLatRow));
+          QK_LDS(bf16x4, pv_a(k + kPvAhead) + 2 * kLatRow));
+    }
+    if constexpr (SOFT) {
+      if (k < kSoftSteps) soft_step(k, w, sf, wave);
     }
   }
   fence();
@@ -452,10 +506,11 @@ __device__ __forceinline__ void pv_tile(Wave& w, const bf16x8 (&pb)[2], int lane
 // stage i % 3 (SP), tile i + 1 in SQ, the stage of tile i - 1 free (SN):
 //   wait for tile i + 1 and synchronise the workgroup (every wave is past
 //   tile i - 1, so stage SN is free), prefetch tile i + 2 into SN; the logits
-//   of tile i + 1 on MFMA with the softmax of tile i between them; then the
-//   P.C of tile i.  lg holds the logits of tile i on entry and of tile i + 1
-//   on exit.  The prefetch of tile 2 is issued by the segment's first step
-//   (stage 2 is free from the start), so step 0 does not issue one.
+//   of tile i + 1 on MFMA; then the P.C of tile i with the softmax of tile
+//   i + 1 between its MFMAs.  pb holds the weights of tile i on entry and of
+//   tile i + 1 on exit.  The prefetch of tile 2 is issued by the segment's
+//   first step (stage 2 is free from the start), so step 0 does not issue
+//   one.
 template <bool QKN, int NW, int SP, int SQ, int SN>
 __device__ __forceinline__ void pipe_step(Wave& w, Soft& sf, const Seq& sq, const Paging& pg,
                                           int G, int tile0, int i, int nt, int wave, int lane,
@@ -467,15 +522,16 @@ __device__ __forceinline__ void pipe_step(Wave& w, Soft& sf, const Seq& sq, cons
     const int t = tile0 + i + 1;
     const bool last = t == sq.last_tile;
     const int tail = last ? __builtin_amdgcn_readfirstlane(sq.L - t * kTile) : kTile;
-    float lg_next[16];
-    qk_tile<QKN, true, SQ>(w, sf, lg_next, last, tail, wave, lane, g);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) sf.lg[j] = lg_next[j];
+    qk_tile<QKN, SQ>(w, sf.lg, last, tail, wave, lane, g);
   } else {
+    // no next tile: its softmax sees only masked logits, so it adds nothing
+    // (one P.C code path for all steps keeps the accumulators in place)
 #pragma unroll
-    for (int s = 0; s < kQkSteps; ++s) soft_step(s, w, sf, wave);
+    for (int j = 0; j < 16; ++j) sf.lg[j] = -INFINITY;
   }
-  pv_tile<SP>(w, sf.pb, lane);
+  pv_tile<true, SP>(w, sf, wave, lane);
+  sf.pb[0] = sf.pn[0];
+  sf.pb[1] = sf.pn[1];
 }
 
 template <bool QKN, int NW, bool PAGED>
@@ -522,7 +578,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
     sq.lat = (const char*)a.lat;
     sq.rope = (const char*)a.rope;
     sq.alpha = QKN ? (const char*)a.alpha : nullptr;
-    const size_t qrow = (size_t)b * a.H + head;
 
     // The segment's loads, in the order the first tile's logits need them:
     // the RoPE query (straight into LDS: its operand-order rows are the LDS
@@ -576,7 +631,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
         if (nt > 2) issue_tile<QKN, NW, 2>(sq, pg, a.G, tile0 + 2, wave, lane);
         const bool last = tile0 == sq.last_tile;
         const int tail = last ? __builtin_amdgcn_readfirstlane(sq.L - tile0 * kTile) : kTile;
-        qk_tile<QKN, false, 0>(w, sf, sf.lg, last, tail, wave, lane, g);
+        qk_tile<QKN, 0>(w, sf.lg, last, tail, wave, lane, g);
+#pragma unroll
+        for (int s = 0; s < kSoftSteps; ++s) soft_step(s, w, sf, wave);
+        sf.pb[0] = sf.pn[0];
+        sf.pb[1] = sf.pn[1];
       }
       for (int i = 0; i < nt; i += kStages) {
         pipe_step<QKN, NW, 0, 1, 2>(w, sf, sq, pg, a.G, tile0, i, nt, wave, lane, g);
@@ -589,7 +648,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
       // segment again with the raised reference (exact; never taken for
       // normalised logits).
       block_sync();
-      if (lane == 0) lds_restart[wave] = 0;
+      if (lane_here() == 0) lds_restart[wave] = 0;
       issue_tile<QKN, NW, 0>(sq, pg, a.G, tile0, wave, lane);
       if (nt > 1) issue_tile<QKN, NW, 1>(sq, pg, a.G, tile0 + 1, wave, lane);
     }
@@ -600,15 +659,14 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
     // stage buffers are idle here (every wave is past the segment's last
     // tile), and wave w transposes through its own 32-row region of them,
     // one round of kEpiDims dims at a time.
-    const float l_tot = w.l_run + __shfl_xor(w.l_run, 32, 64);
+    const float l_tot = halves_sum(w.l_run);
     const float m_run = w.m_ref;
     const bool complete = (x == s0) && (seg_end == s1);
-    // The lane values are re-derived through an opaque copy, so that the
-    // epilogue's addresses are formed here rather than hoisted above the tile
-    // loop (where they would stay live, in spilled registers).
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    // The lane values are re-derived here, so that the epilogue's addresses
+    // are formed here rather than kept live across the tile loop.
+    const int ln = lane_here();
     const int en = ln & 31, ehf = ln >> 5;
+    const int ehead = wave * 32 + en;
     char* region = (wave >> 1 == 0 ? stage_buf<0>() : stage_buf<1>()) + (wave & 1) * kEpiRegion;
     // Each round reads its 16 LDS rows kEpiBatch at a time into registers
     // before their stores, so the reads overlap and a store does not wait on
@@ -645,13 +703,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
           __builtin_amdgcn_sched_group_barrier(0x040, kEpiBatch, 0);  // then the stores
         }
       }
-      if (hf == 0 && a.lse) a.lse[qrow] = (m_run + log2f(l_tot)) * kLn2;
+      if (ehf == 0 && a.lse) a.lse[(size_t)b * a.H + ehead] = (m_run + log2f(l_tot)) * kLn2;
     } else {  // partial: m, l and the unnormalised O in bf16, rows of 1 KB: two rounds of 256 dims
       const int slot = first_seg ? 0 : 1;
       char* sp = a.part + ((size_t)p * kSlotsPerWg + slot) * kPartialSlotBytes(a.H, kR);
-      if (hf == 0) {
-        ((float*)sp)[head] = m_run;
-        ((float*)sp)[a.H + head] = l_tot;
+      if (ehf == 0) {
+        ((float*)sp)[ehead] = m_run;
+        ((float*)sp)[a.H + ehead] = l_tot;
       }
       char* Op = sp + (size_t)a.H * 8 + (size_t)(wave * 32) * kR * 2;
       const uint32_t lane_off = (uint32_t)ehf * (kR * 2) + (uint32_t)en * 16;

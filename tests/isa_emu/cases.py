@@ -966,8 +966,8 @@ def isa_semantics(dev):
     """Emulator semantics that the compiled kernels lean on, against numpy on
     random registers: SDWA source selects (word / byte of a VGPR or SGPR
     source) on integer VOP ops, the gfx9 16-bit integer ops (low halves in,
-    high half of the destination zeroed) and v_bitop3_b32's truth table (bit
-    4a + 2b + c)."""
+    high half of the destination zeroed), v_bitop3_b32's truth table (bit
+    4a + 2b + c) and the half-wave swap of v_permlane32_swap_b32."""
     from isa_emu.machine import Wave, Workgroup
     lines = [
         "v_mul_lo_u16_sdwa v3, v1, v2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 "
@@ -987,6 +987,10 @@ def isa_semantics(dev):
         "v_or_b32_sdwa v11, s3, v2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
         "src1_sel:WORD_1",
         "v_bitop3_b32 v12, v1, v2, s3 bitop3:0x78",
+        # lanes 32..63 of the first operand trade places with lanes 0..31 of the second
+        "v_mov_b32_e32 v13, v1",
+        "v_mov_b32_e32 v14, v2",
+        "v_permlane32_swap_b32_e32 v13, v14",
         "s_endpgm",
     ]
     insts = [parse_inst(t, k) for k, t in enumerate(lines)]
@@ -1020,8 +1024,10 @@ def isa_semantics(dev):
     }
     for r, e in expect.items():
         assert np.array_equal(w.V[r].astype(np.uint64), e), f"v{r}: {lines[r - 3]}"
-    print("[ok] SDWA source selects (VGPR and SGPR sources), 16-bit integer ops and the "
-          "three-input bit table match numpy", flush=True)
+    assert np.array_equal(w.V[13], np.concatenate([a[:32], b[:32]])), "permlane32_swap vdst"
+    assert np.array_equal(w.V[14], np.concatenate([a[32:], b[32:]])), "permlane32_swap vsrc"
+    print("[ok] SDWA source selects (VGPR and SGPR sources), 16-bit integer ops, the "
+          "three-input bit table and the half-wave swap match numpy", flush=True)
 
 
 def main(argv):

@@ -543,6 +543,23 @@ def _(w, i):
     w.note_valu_sgpr(d)
 
 
+@h("v_permlane32_swap_b32")
+def _(w, i):
+    """Swap lanes 32..63 of the destination with lanes 0..31 of the source
+    (both operands are written)."""
+    d, src = i.ops
+    if not w.exec_mask().all():
+        raise EmuError("v_permlane32_swap with partial exec not modelled")
+    if i.mods.get("bound_ctrl") or i.mods.get("fi"):
+        raise EmuError(f"v_permlane32_swap modifiers not modelled: {i.text}")
+    vd, vs = w.vget(d).copy(), w.vget(src).copy()
+    nd, ns = vd.copy(), vs.copy()
+    nd[32:] = vs[:32]
+    ns[:32] = vd[32:]
+    w.vset(d, nd)
+    w.vset(src, ns)
+
+
 @h("v_readfirstlane_b32")
 def _(w, i):
     d, src = i.ops

@@ -42,16 +42,19 @@ def test_traffic_from_pmc_counters(tmp_path):
     head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
     dec = "void qkmla::(anonymous namespace)::decode_mfma_kernel<true, 4>(Args)"
     plain = "void qkmla::(anonymous namespace)::decode_mfma_kernel<false, 4>(Args)"
-    cp = "void at::native::direct_copy_kernel_cuda(at::TensorIteratorBase&)"
+    cp = "__amd_rocclr_copyBuffer"
+    conv = "void at::native::vectorized_elementwise_kernel<4, bfloat16_copy_kernel_cuda>(int)"
     gib_kib = (1 << 30) / 1024
     fetch = head + "".join([
+        f'0,"{conv}",FETCH_SIZE,7\n', f'0,"{cp}",FETCH_SIZE,5\n',  # set-up copies, other sizes
         f'1,"{dec}",FETCH_SIZE,60000\n', f'1,"{dec}",FETCH_SIZE,20000\n',  # one dispatch, 2 rows
         f'2,"{dec}",FETCH_SIZE,82000\n',
-        f'3,"{plain}",FETCH_SIZE,1\n',
-        f'4,"{cp}",FETCH_SIZE,{gib_kib * 1.25}\n'])   # the counter reads 25% high
+        f'3,"{plain}",FETCH_SIZE,1\n'] +
+        [f'{d},"{cp}",FETCH_SIZE,{gib_kib * 1.25}\n' for d in (4, 5, 6)])  # counter reads 25% high
     write = head + "".join([
-        f'1,"{dec}",WRITE_SIZE,4000\n', f'2,"{dec}",WRITE_SIZE,6000\n',
-        f'4,"{cp}",WRITE_SIZE,{gib_kib}\n'])
+        f'0,"{conv}",WRITE_SIZE,7\n', f'0,"{cp}",WRITE_SIZE,5\n',
+        f'1,"{dec}",WRITE_SIZE,4000\n', f'2,"{dec}",WRITE_SIZE,6000\n'] +
+        [f'{d},"{cp}",WRITE_SIZE,{gib_kib}\n' for d in (4, 5, 6)])
     (tmp_path / "f.csv").write_text(fetch)
     (tmp_path / "w.csv").write_text(write)
     t = bench.traffic_from_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "w1", 77594624)

@@ -309,7 +309,10 @@ constexpr int kStepThreads = 1024;
 constexpr int kStepMaxDc = 256;
 constexpr int kStepMaxRowsPerThread = 16;  // r / RG
 
-template <typename T>
+// DC, R > 0: the layer shape fixed at compile time (every loop below has a
+// static trip count, so all of its loads go out together); 0: read d_c and r
+// from the arguments.
+template <typename T, int DC, int R>
 __global__ __launch_bounds__(kStepThreads) void append_step_kernel(
     int batch, int n_new, const T* __restrict__ c_new, const T* __restrict__ kr_new,
     const float* __restrict__ w_uk, const float* __restrict__ gkr,
@@ -330,19 +333,65 @@ __global__ __launch_bounds__(kStepThreads) void append_step_kernel(
     return;
   }
   const int g = duty;
+  if constexpr (DC > 0) dc = DC;
+  if constexpr (R > 0) r = R;
   const int nq = dc / 4;               // column quads
   const int RG = kStepThreads / nq;    // row groups
   const int rg = tid / nq, c4 = tid % nq;
   const int rows = r / RG;             // rows per thread (<= kStepMaxRowsPerThread)
   const float* W = w_uk + (size_t)g * r * dc + 4 * c4;
+  // The loads go out in the order they are needed (they complete in that
+  // order): the new latent rows, the tokens' positions, then W^UK_g, so the
+  // LDS copy of the rows and the row lookup do not wait for the weights.
+  constexpr int kCs = R > 0 ? (kStepTok * R + kStepThreads - 1) / kStepThreads : 1;
+  T cv[kCs];  // raw elements, converted when they go to LDS (after the weights' loads)
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int u = 0; u < kCs; ++u) {  // unconditional loads (clamped), selected later
+      const int i = tid + u * kStepThreads;
+      cv[u] = c_new[(size_t)tok0 * R + min(i, ntok * R - 1)];
+    }
+  } else {
+    for (int i = tid; i < kStepTok * r; i += kStepThreads) {
+      const int k = i / r, e = i % r;
+      cs[k][e] = k < ntok ? Elem<T>::load(c_new, (size_t)(tok0 + k) * r + e) : 0.f;
+    }
+  }
+  // Wavefront k writes token k's alpha: its position (and, for a paged cache,
+  // the block-table entry) through scalar loads, which the weights' vector
+  // loads in flight do not hold up.
+  const int wv_id = __builtin_amdgcn_readfirstlane(wave);
+  const __attribute__((address_space(4))) int32_t* pos_s =
+      (const __attribute__((address_space(4))) int32_t*)positions;
+  const int pos0 = wv_id < ntok ? pos_s[(tok0 + wv_id) / n_new] : 0;
   // Branch-free: rows past r / RG re-read the last one and are not summed.
   f32x4 wv[kStepMaxRowsPerThread];
 #pragma unroll
   for (int n = 0; n < kStepMaxRowsPerThread; ++n)
     wv[n] = *(const f32x4*)(W + (size_t)(rg + min(n, rows - 1) * RG) * dc);
-  for (int i = tid; i < kStepTok * r; i += kStepThreads) {
-    const int k = i / r, e = i % r;
-    cs[k][e] = k < ntok ? Elem<T>::load(c_new, (size_t)(tok0 + k) * r + e) : 0.f;
+  if constexpr (R > 0) {
+    __builtin_amdgcn_sched_barrier(0);  // every load is issued before the first use
+#pragma unroll
+    for (int u = 0; u < kCs; ++u) {
+      const int i = tid + u * kStepThreads;
+      if (i < kStepTok * R) cs[i / R][i % R] = i / R < ntok ? Elem<T>::load(cv, u) : 0.f;
+    }
+  }
+  int64_t prow = -1;
+  if (wv_id < ntok) {
+    const int tok = tok0 + wv_id;
+    const int b = tok / n_new, i = tok % n_new;
+    const bool bad = pos0 < 0 || (int64_t)pos0 + n_new > pg.capacity();
+    if (!bad) {
+      const int t = pos0 + i, blk = t / pg.page_size;
+      int page = b;
+      if (pg.bt) {
+        page = ((const __attribute__((address_space(4))) int32_t*)pg.bt)[(size_t)b * pg.max_blocks +
+                                                                          blk];
+        page = (page >= 0 && page < pg.num_pages) ? page : -1;
+      }
+      prow = page < 0 ? -1 : (int64_t)page * pg.page_size + (t - blk * pg.page_size);
+    }
   }
   __syncthreads();
   f32x4 acc[kStepTok];
@@ -361,11 +410,13 @@ __global__ __launch_bounds__(kStepThreads) void append_step_kernel(
 #pragma unroll
   for (int k = 0; k < kStepTok; ++k) {
     f32x4 v = acc[k];
-    if (pair) {
-      v[0] += __shfl_xor(v[0], 32, 64);
-      v[1] += __shfl_xor(v[1], 32, 64);
-      v[2] += __shfl_xor(v[2], 32, 64);
-      v[3] += __shfl_xor(v[3], 32, 64);
+    if (pair) {  // lanes l and l ^ 32: one half-wave swap each, no LDS round trip
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[q]),
+                                                         __float_as_uint(v[q]), false, false);
+        v[q] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
     }
     if (!pair || lane < 32) *(f32x4*)&kp[wave][k][4 * c4] = v;
   }
@@ -375,22 +426,27 @@ __global__ __launch_bounds__(kStepThreads) void append_step_kernel(
   // nq / 64-th one (a row group spans nq / 64 wavefronts).
   // Every sum has a fixed order, so the result is the same on every call.
   const int wstep = pair ? 1 : nq / 64;
-  for (int i = tid; i < kStepTok * dc; i += kStepThreads) {
-    const int k = i / dc, j = i % dc;
-    float v = 0.f;
-    for (int w = pair ? 0 : (j / 4) / 64; w < kStepThreads / 64; w += wstep) v += kp[w][k][j];
-    sqv[k][j] = v * v;
+  if constexpr (DC == 128) {  // the pair case: every wavefront holds every column
+    if (tid < kStepTok * DC) {
+      const int k = tid / DC, j = tid % DC;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kStepThreads / 64; ++w) v += kp[w][k][j];
+      sqv[k][j] = v * v;
+    }
+  } else {
+    for (int i = tid; i < kStepTok * dc; i += kStepThreads) {
+      const int k = i / dc, j = i % dc;
+      float v = 0.f;
+      for (int w = pair ? 0 : (j / 4) / 64; w < kStepThreads / 64; w += wstep) v += kp[w][k][j];
+      sqv[k][j] = v * v;
+    }
   }
   __syncthreads();
   if (wave < ntok) {  // wavefront k: sum over d_c of token k's k^2
     float ss = 0.f;
     for (int j = lane; j < dc; j += 64) ss += sqv[wave][j];
     ss = wave_sum(ss);
-    const int tok = tok0 + wave;
-    const int b = tok / n_new, i = tok % n_new;
-    const int pos0 = positions[b];
-    const bool bad = pos0 < 0 || (int64_t)pos0 + n_new > pg.capacity();
-    const int64_t prow = bad ? -1 : pg.phys_row(b, pos0 + i);
     if (lane == 0 && prow >= 0) alpha[(size_t)prow * G + g] = 1.0f / sqrtf(ss / (float)dc + eps);
   }
 }
@@ -409,13 +465,19 @@ hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
       c.r / (kStepThreads / nq) <= kStepMaxRowsPerThread &&
       ((uintptr_t)w_uk % 16 == 0 || !c.qk_norm)) {
     dim3 g1((unsigned)((T_total + kStepTok - 1) / kStepTok), c.qk_norm ? c.G + 1 : 1);
-    if (c.dtype == QKMLA_BF16)
-      append_step_kernel<uint16_t><<<g1, kStepThreads, 0, s>>>(
+    const bool dsv3 = c.dc == 128 && c.r == 512;  // the DeepSeek-V3-like layer's shape
+    if (c.dtype == QKMLA_BF16 && dsv3)
+      append_step_kernel<uint16_t, 128, 512><<<g1, kStepThreads, 0, s>>>(
+          batch, n_new, (const uint16_t*)c_new, (const uint16_t*)k_rope_new, w_uk, gkr,
+          positions, pg, (uint16_t*)lat, (uint16_t*)rope, alpha, status, c.G, c.r, c.dc, c.dr,
+          c.eps, rf, c.qk_norm);
+    else if (c.dtype == QKMLA_BF16)
+      append_step_kernel<uint16_t, 0, 0><<<g1, kStepThreads, 0, s>>>(
           batch, n_new, (const uint16_t*)c_new, (const uint16_t*)k_rope_new, w_uk, gkr,
           positions, pg, (uint16_t*)lat, (uint16_t*)rope, alpha, status, c.G, c.r, c.dc, c.dr,
           c.eps, rf, c.qk_norm);
     else
-      append_step_kernel<float><<<g1, kStepThreads, 0, s>>>(
+      append_step_kernel<float, 0, 0><<<g1, kStepThreads, 0, s>>>(
           batch, n_new, (const float*)c_new, (const float*)k_rope_new, w_uk, gkr, positions, pg,
           (float*)lat, (float*)rope, alpha, status, c.G, c.r, c.dc, c.dr, c.eps, rf, c.qk_norm);
     return hipGetLastError();

@@ -291,9 +291,11 @@ hipError_t launch_qprep(const Cfg& c, int batch, int s_q, const void* q_c, const
   const int nv = batch * s_q;  // virtual sequences, one per query row
   const RopeFreq rf = rope_freq(c.dr, c.base);
   if (c.dtype == QKMLA_BF16) {
-    // SPB sequences share a block's W~ loads once the batch gives enough blocks.
+    // Two sequences share a block's W~ loads once the batch gives enough
+    // blocks (measured on the 128-head layer: at 16 and 64 sequences two per
+    // block beat one and four).
     if (nv >= 16)
-      return launch_qprep_spb<4>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws,
+      return launch_qprep_spb<2>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws,
                                  status, s);
     return launch_qprep_spb<1>(c, nv, s_q, q_c, q_rope, w_qabs, gqr, seq_lens, pg, rf, wsb, ws,
                                status, s);

@@ -82,7 +82,7 @@ typedef enum { QKMLA_F32 = 0, QKMLA_BF16 = 1 } qkmla_dtype;
  *     weights and W^UV.  The alpha cache, W^UK, all gammas and every output are
  *     float32.  All arithmetic accumulates in float32.
  *     QKMLA_F32: any shape with r <= 1024, d_c <= 1024, d_r <= 256, d_v <= 1024.
- *     QKMLA_BF16: r = 512, d_r = 64, H in {64, 128}, H/G = 16, d_c a multiple
+ *     QKMLA_BF16: r = 512, d_r = 64, H in {32, 64, 128}, H/G = 16, d_c a multiple
  *     of 32 up to 256 (the DeepSeek-V3-like MLA layer); d_v <= 1024.
  *   qk_norm: 1 = QK-Normed MLA; 0 = plain MLA (no gammas, no alpha, no RoPE
  *     norm) -- the same kernels with the normalisation compiled out.

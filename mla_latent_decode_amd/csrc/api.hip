@@ -61,15 +61,11 @@ int check_cfg(const qkmla_config* cfg, Cfg* out, bool decode_shapes = true) {
     return fail(QKMLA_ERR_UNSUPPORTED, "dimension above the compiled limits (r, d_c, d_v <= 1024, d_r <= 256)");
   if (c.dtype == QKMLA_BF16 && decode_shapes) {
     const int hpg = c.n_heads / c.n_groups;
-    // H = 32 (one wavefront per workgroup) is switched off: that instantiation
-    // faulted on the GPU when the tile loads were inline asm (a VALU write of the
-    // load's scalar base too few wait states ahead of it). The builtin loads used
-    // now do not have that hazard, but this variant has not run on a GPU since.
-    const bool h_ok = c.n_heads == 64 || c.n_heads == 128;
+    const bool h_ok = c.n_heads == 32 || c.n_heads == 64 || c.n_heads == 128;
     if (c.latent_rank != 512 || c.rope_dim != 64 || !h_ok || hpg != 16 || c.head_dim % 32 != 0 ||
         c.head_dim > 256)
       return fail(QKMLA_ERR_UNSUPPORTED,
-                  "bf16 path is compiled for r=512, d_r=64, H in {64,128}, H/G=16, d_c in "
+                  "bf16 path is compiled for r=512, d_r=64, H in {32,64,128}, H/G=16, d_c in "
                   "{32,64,...,256} "
                   "(got r=%d d_r=%d H=%d G=%d d_c=%d)",
                   c.latent_rank, c.rope_dim, c.n_heads, c.n_groups, c.head_dim);

@@ -624,7 +624,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(Args a) {
         // q~ loads and tile 1 may still be in flight behind them.
         constexpr int kQtLoads = kR / 16;
         if (!q_in_flight) wait_vmcnt<0>();
-        else if (nt > 1) wait_vmcnt<kQtLoads + TileLoads<QKN, NW>::total>();
+        else if (nt > 1) {
+          // (the counter holds at most 63: with one wavefront, 72 loads follow
+          // tile 0, and waiting for nine more of them costs nothing that matters)
+          constexpr int kAfter = kQtLoads + TileLoads<QKN, NW>::total;
+          wait_vmcnt<(kAfter < 64 ? kAfter : 63)>();
+        }
         else wait_vmcnt<kQtLoads>();
         q_in_flight = false;
         block_sync();
@@ -779,11 +784,13 @@ hipError_t launch_decode_mfma(const Cfg& c, int batch, int s_q, const int32_t* s
   if (c.qk_norm) {
     if (nw == 4) k = paged ? decode_mfma_kernel<true, 4, true> : decode_mfma_kernel<true, 4, false>;
     else if (nw == 2) k = paged ? decode_mfma_kernel<true, 2, true> : decode_mfma_kernel<true, 2, false>;
+    else if (nw == 1) k = paged ? decode_mfma_kernel<true, 1, true> : decode_mfma_kernel<true, 1, false>;
   } else {
     if (nw == 4) k = paged ? decode_mfma_kernel<false, 4, true> : decode_mfma_kernel<false, 4, false>;
     else if (nw == 2) k = paged ? decode_mfma_kernel<false, 2, true> : decode_mfma_kernel<false, 2, false>;
+    else if (nw == 1) k = paged ? decode_mfma_kernel<false, 1, true> : decode_mfma_kernel<false, 1, false>;
   }
-  if (!k) return hipErrorInvalidValue;  // one-wavefront variant switched off
+  if (!k) return hipErrorInvalidValue;
   return launch_kernel(k, grid, block, s, a);
 }
 

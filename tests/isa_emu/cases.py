@@ -193,6 +193,16 @@ def bf16_64_heads(dev):
               n_wg=2, heads=(0, 37))  # the merge runs heads 0, 37 (and 127)
 
 
+@case
+def bf16_32_heads(dev):
+    """The one-wavefront split-KV variant (32 heads in 2 KV groups), caches
+    from qkmla_append, 7 tiles over two workgroups (two segments, a slot-1
+    partial)."""
+    shape = Shape(32, 2, 512, 128, 64, 128, "bf16")
+    run_layer(dev, shape, (150, 70), 507, "bf16 H=32 over 2 workgroups", host_fill=False,
+              n_wg=2, heads=(0, 3))  # the merge runs the block of heads 0..3 (37, 127 are past H)
+
+
 def run_multi(dev, shape, lens, s_q, seed, label, n_wg=None, heads=None):
     """Decode of s_q causal query rows per sequence against the oracle; rows
     whose causal prefix is empty must come back as zeros with lse = -inf."""

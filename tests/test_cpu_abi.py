@@ -54,8 +54,8 @@ def _cfg(**kw):
     (dict(rope_dim=63), 1),                    # odd rope dim
     (dict(n_heads=0), 1),
     (dict(latent_rank=256), 2),                # bf16 path compiled for r = 512
-    (dict(n_heads=96, n_groups=6), 2),         # H not in {64, 128}
-    (dict(n_heads=32, n_groups=2), 2),         # one-wavefront variant switched off
+    (dict(n_heads=96, n_groups=6), 2),         # H not in {32, 64, 128}
+    (dict(n_heads=16, n_groups=1), 2),         # fewer heads than one wavefront's 32
     (dict(latent_rank=2048, dtype="f32"), 2),  # above the compiled limits
     (dict(eps=-1.0), 1),
     (dict(rope_base=0.0), 1),

@@ -34,11 +34,12 @@ def runtime(tmp_path_factory):
     return build_runtime(str(tmp_path_factory.mktemp("hip_stand_in")))
 
 
-# longest first; all start together (at most _WORKERS at a time) when the
-# first case is asked for, so the module takes about as long as its longest case
+# longest first; the selected cases all start together (at most _WORKERS at a
+# time) when the first one is asked for, so the module takes about as long as
+# its longest case
 CASES = ["train_mfma", "train_varlen", "train_fwd_bwd", "paged_caches", "bf16_long_segments",
          "bf16_max_batch", "bf16_ragged_full", "bf16_32k_step", "bf16_long_context", "bf16_headline_sequence", "bf16_many_splits", "multi_query",
-         "bf16_split", "bf16_append_caches", "bf16_64_heads", "bf16_plain_overflow",
+         "bf16_split", "bf16_append_caches", "bf16_64_heads", "bf16_32_heads", "bf16_plain_overflow",
          "bf16_plain_hold", "fp32_tiny", "hazard_checker", "isa_semantics"]
 _WORKERS = max(1, min(6, (os.cpu_count() or 2) - 1))
 _futures = {}
@@ -53,19 +54,31 @@ def _run_case(runtime, case):
     return r.returncode, out
 
 
-def _result(runtime, case):
+def _selected_cases(session):
+    """The emulator cases this session will run (after -k / -m selection)."""
+    names = []
+    for item in session.items:
+        cs = getattr(item, "callspec", None)
+        if item.originalname == "test_kernels_on_the_emulator" and cs is not None:
+            names.append(cs.params["case"])
+    return [c for c in CASES if c in names] or CASES
+
+
+def _result(runtime, case, session):
     if os.environ.get("PYTEST_XDIST_WORKER"):  # under xdist each worker runs its own cases
         return _run_case(runtime, case)
     if not _futures:
         pool = concurrent.futures.ThreadPoolExecutor(max_workers=_WORKERS)
-        for c in CASES:
+        for c in _selected_cases(session):
             _futures[c] = pool.submit(_run_case, runtime, c)
+    if case not in _futures:
+        return _run_case(runtime, case)
     return _futures[case].result()
 
 
 @pytest.mark.parametrize("case", CASES)
-def test_kernels_on_the_emulator(runtime, case):
-    rc, out = _result(runtime, case)
+def test_kernels_on_the_emulator(runtime, case, request):
+    rc, out = _result(runtime, case, request.session)
     print(out)
     assert rc == 0, out[-4000:]
 

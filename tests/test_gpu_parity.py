@@ -171,9 +171,7 @@ def test_dsv3_bf16_log_normal_scales():
     _full_check(cfg, inp, "dsv3 bf16 log-normal rows")
 
 
-@pytest.mark.parametrize("heads", [64, pytest.param(32, marks=pytest.mark.skip(
-    reason="H=32 (one-wavefront decode variant) faulted the GPU with the asm tile loads; "
-           "switched off (qkmla_config returns UNSUPPORTED) until its cause is found"))])
+@pytest.mark.parametrize("heads", [64, 32])
 def test_dsv3_fewer_heads(heads):
     shape = Shape(heads, heads // 16, 512, 128, 64, 128, "bf16")
     inp = make_inputs(shape, (45, 200), seed=320 + heads)

@@ -184,101 +184,154 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
-// bf16 caches: one workgroup per (kAlphaTok new tokens, duty).  Duty y < G
-// computes alpha^k of group y on MFMA; duty y == G (0 in plain mode) copies
-// the latent rows and writes the RoPE keys.
+// bf16 caches: one workgroup per (32 TB new tokens, duty).  Duty y < G
+// computes alpha^k of group y on MFMA; duties y >= G (y == 0 .. TB - 1 in
+// plain mode) copy 32 latent rows each and write their RoPE keys.
 //   k^T[n][t] = sum_i W^UK_g[i][n] c_t[i]          (mfma_f32_32x32x16_bf16)
 //   alpha^k_{t,g} = 1 / sqrt(mean_n k^T[n][t]^2 + eps)
-// The four waves take output dims n in blocks of 32 (wave w: blocks w, w+4).
-// W^UK stays accurate to about 2^-16: each weight is split into
+// The four waves take output dims n in blocks of 32 (wave w: blocks w, w+4)
+// for all TB token blocks, so each W^UK_g chunk staged in LDS serves 32 TB
+// tokens.  W^UK stays accurate to about 2^-16: each weight is split into
 // hi = bf16(W) and lo = bf16(W - hi), and both products with the bf16
-// latent are exact, accumulated in fp32.  W^UK_g is staged in LDS in chunks
-// of 32 rows as row-major hi / lo tiles and read with ds_read_b64_tr_b16,
-// which gives the A operand W^T[n][k] with k contiguous: in each 16-lane
-// group lane i receives element i%4 of the 8-byte loads of lanes 4e + i/4.
+// latent are exact, accumulated in fp32.  The chunks of 32 rows are double
+// buffered: chunk k + 1's weights and latent operands are loaded into
+// registers while chunk k is converted into the LDS buffer k % 2 and
+// multiplied, so one barrier per chunk suffices and the loads' latency hides
+// behind the MFMAs.  The A operand W^T[n][k] comes from ds_read_b64_tr_b16 of
+// the row-major hi / lo tiles: in each 16-lane group lane i receives element
+// i%4 of the 8-byte loads of lanes 4e + i/4.
 // MFMA 32x32x16 layouts: A lane l holds A[m=l%32][k=8(l/32)+j]; B lane l
 // holds B[k=8(l/32)+j][n=l%32]; D lane l reg i holds D[8(i/4)+4(l/32)+i%4][l%32].
-constexpr int kAlphaTok = 32;
 constexpr int kAlphaChunk = 32;
 constexpr int kAlphaMaxDc = 256;
-
-__global__ __launch_bounds__(256) void append_bf16_kernel(
+// WQ: W^UK quads per thread and chunk, kAlphaChunk * d_c / 4 / 256 rounded up
+// to 4 or 8 (d_c <= 128 or <= 256).
+// (with d_c <= 128, two workgroups share a CU: measured 420 against 560 us
+// for 64 Ki tokens with one, the phases of one workgroup (loads, conversion,
+// barrier, MFMAs) then overlapping with the other's)
+template <int TB, int WQ>
+__global__ __launch_bounds__(256, WQ == 4 ? 2 : 1) void append_bf16_kernel(
     int batch, int n_new, const uint16_t* __restrict__ c_new, const uint16_t* __restrict__ kr_new,
     const float* __restrict__ w_uk, const float* __restrict__ gkr,
     const int32_t* __restrict__ positions, const Paging pg, uint16_t* __restrict__ lat,
     uint16_t* __restrict__ rope, float* __restrict__ alpha, int32_t* status, int G, int r,
     int dc, int dr, float eps, const RopeFreq rf, int qk_norm) {
-  __shared__ __attribute__((aligned(16))) uint16_t w_hi[kAlphaChunk][kAlphaMaxDc];
-  __shared__ __attribute__((aligned(16))) uint16_t w_lo[kAlphaChunk][kAlphaMaxDc];
-  __shared__ float ssq[4][kAlphaTok];
+  __shared__ __attribute__((aligned(16))) uint16_t w_hi[2][kAlphaChunk][kAlphaMaxDc];
+  __shared__ __attribute__((aligned(16))) uint16_t w_lo[2][kAlphaChunk][kAlphaMaxDc];
+  __shared__ float ssq[4][32 * TB];
   const int T_total = batch * n_new;
-  const int tok0 = blockIdx.x * kAlphaTok;
+  const int tok0 = blockIdx.x * 32 * TB;
   const int duty = blockIdx.y;
-  if (qk_norm ? duty == G : duty == 0) {
-    copy_rows_and_rope<uint16_t>(tok0, kAlphaTok, batch, n_new, c_new, kr_new, gkr, positions,
-                                 pg, lat, rope, status, r, dr, eps, rf, qk_norm);
+  const int copy0 = qk_norm ? G : 0;
+  if (duty >= copy0) {
+    copy_rows_and_rope<uint16_t>(tok0 + 32 * (duty - copy0), 32, batch, n_new, c_new, kr_new, gkr,
+                                 positions, pg, lat, rope, status, r, dr, eps, rf, qk_norm);
     return;
   }
   const int g = duty;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hf = lane >> 5, t = lane & 31;
   const int nblk = dc / 32;  // 1..8
-  // B operand: token t's latent row (rows past the last token repeat it)
-  const uint16_t* crow = c_new + (size_t)min(tok0 + t, T_total - 1) * r + hf * 8;
+  const int nq = dc / 4;     // column quads of a W^UK row
   // A operand through the transposing read: this lane loads row e (+4) of the
   // K-step's 16, columns 4q..4q+3 of its 16-column half
   const int q16 = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
   const int a_row = 8 * (q16 >> 1) + e;
   const int a_col = 16 * (q16 & 1) + 4 * q;
   const float* W = w_uk + (size_t)g * r * dc;
-  f32x16 acc[2];
+  // B operand: token tb*32 + t's latent row, elements 8 hf .. 8 hf + 7 of each
+  // K-step (rows past the last token repeat it)
+  const uint16_t* crow[TB];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) { acc[0][j] = 0.f; acc[1][j] = 0.f; }
-  for (int k0 = 0; k0 < r; k0 += kAlphaChunk) {
-    for (int i = tid; i < kAlphaChunk * dc / 4; i += 256) {
-      const int row = i / (dc / 4), c4 = (i % (dc / 4)) * 4;
-      const f32x4 v = *(const f32x4*)(W + (size_t)(k0 + row) * dc + c4);
-      uint16_t hi[4], lo[4];
+  for (int tb = 0; tb < TB; ++tb)
+    crow[tb] = c_new + (size_t)min(tok0 + 32 * tb + t, T_total - 1) * r + hf * 8;
+  f32x16 acc[2][TB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hi[j] = f32_to_bf16(v[j]);
-        lo[j] = f32_to_bf16(v[j] - bf16_to_f32(hi[j]));
-      }
-      *(uint2*)&w_hi[row][c4] = uint2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
-      *(uint2*)&w_lo[row][c4] = uint2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[bi][tb][j] = 0.f;
+  struct Chunk {
+    f32x4 w[WQ];
+    bf16x8 c[TB][kAlphaChunk / 16];
+  };
+  auto load = [&](int k0, Chunk& ch) {
+#pragma unroll
+    for (int u = 0; u < WQ; ++u) {
+      const int i = tid + 256 * u;  // the test is uniform: i < 256 (u + 1) <= chunk quads
+      if (i < kAlphaChunk * nq) ch.w[u] = *(const f32x4*)(W + (size_t)(k0 + i / nq) * dc + (i % nq) * 4);
     }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < kAlphaChunk / 16; ++ks)
+        ch.c[tb][ks] = *(const bf16x8*)(crow[tb] + k0 + ks * 16);
+  };
+  Chunk cur, nxt;
+  load(0, cur);
+  const int nchunk = r / kAlphaChunk;
+  for (int kc = 0; kc < nchunk; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nchunk) load((kc + 1) * kAlphaChunk, nxt);
+#pragma unroll
+    for (int u = 0; u < WQ; ++u) {
+      const int i = tid + 256 * u;
+      if (i < kAlphaChunk * nq) {
+        const int row = i / nq, c4 = (i % nq) * 4;
+        bf16x4 hi, lo;  // hardware round-to-nearest-even conversions
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hi[j] = (__bf16)cur.w[u][j];
+          lo[j] = (__bf16)(cur.w[u][j] - (float)hi[j]);
+        }
+        *(bf16x4*)&w_hi[buf][row][c4] = hi;
+        *(bf16x4*)&w_lo[buf][row][c4] = lo;
+      }
+    }
+    // chunk kc is in LDS buffer buf; every wave is past chunk kc - 1's reads
+    // of the other buffer (the previous barrier), which chunk kc + 1 rewrites
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < kAlphaChunk / 16; ++ks) {
-      const bf16x8 bv = *(const bf16x8*)(crow + k0 + ks * 16);
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi) {
         const int blk = wave + 4 * bi;
         if (blk < nblk) {
           const int rr = ks * 16 + a_row, cc = blk * 32 + a_col;
-          const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_hi[rr][cc]));
-          const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_hi[rr + 4][cc]));
-          const bf16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_lo[rr][cc]));
-          const bf16x4 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_lo[rr + 4][cc]));
+          const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_hi[buf][rr][cc]));
+          const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_hi[buf][rr + 4][cc]));
+          const bf16x4 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_lo[buf][rr][cc]));
+          const bf16x4 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &w_lo[buf][rr + 4][cc]));
           const bf16x8 ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
           const bf16x8 alo = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-          acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc[bi], 0, 0, 0);
-          acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bv, acc[bi], 0, 0, 0);
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) {
+            acc[bi][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, cur.c[tb][ks], acc[bi][tb], 0, 0, 0);
+            acc[bi][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, cur.c[tb][ks], acc[bi][tb], 0, 0, 0);
+          }
         }
       }
     }
-    __syncthreads();  // the chunk is consumed before the next one overwrites it
+    cur = nxt;
   }
-  // lane l holds k^T[n][t] for 16 dims n of each of its blocks and token t
-  float sq = 0.f;
+  // lane l holds k^T[n][t] for 16 dims n of each of its blocks and token t of
+  // each token block; the two halves of a column (lanes l, l ^ 32) meet by a
+  // half-wave swap
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int tb = 0; tb < TB; ++tb) {
+    float sq = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sq += acc[bi][j] * acc[bi][j];
-  sq += __shfl_xor(sq, 32, 64);
-  if (hf == 0) ssq[wave][t] = sq;
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sq += acc[bi][tb][j] * acc[bi][tb][j];
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sq), __float_as_uint(sq),
+                                                     false, false);
+    sq = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (hf == 0) ssq[wave][32 * tb + t] = sq;
+  }
   __syncthreads();
-  if (tid < kAlphaTok) {
+  if (tid < 32 * TB) {
     const int tok = tok0 + tid;
     if (tok < T_total) {
       const int b = tok / n_new, i = tok % n_new;
@@ -486,11 +539,25 @@ hipError_t launch_append(const Cfg& c, int batch, int n_new, const void* c_new,
   const bool vec_ok = ((uintptr_t)c_new % 16 == 0) && ((uintptr_t)w_uk % 16 == 0 || !c.qk_norm);
   if (c.dtype == QKMLA_BF16 && vec_ok && c.dc % 32 == 0 && c.dc <= kAlphaMaxDc &&
       c.r % kAlphaChunk == 0) {
-    dim3 g2((unsigned)((T_total + kAlphaTok - 1) / kAlphaTok), c.qk_norm ? c.G + 1 : 1);
-    append_bf16_kernel<<<g2, 256, 0, s>>>(batch, n_new, (const uint16_t*)c_new,
-                                          (const uint16_t*)k_rope_new, w_uk, gkr, positions,
-                                          pg, (uint16_t*)lat, (uint16_t*)rope, alpha, status,
-                                          c.G, c.r, c.dc, c.dr, c.eps, rf, c.qk_norm);
+    // Four token blocks per workgroup once the tokens give each group's
+    // blocks the chip several times over: each W^UK_g chunk then serves 128
+    // tokens instead of 32 (a quarter of the weight traffic and conversions).
+    const bool wide = T_total >= 4096;
+    const int per_wg = wide ? 128 : 32;
+    dim3 g2((unsigned)((T_total + per_wg - 1) / per_wg),
+            (c.qk_norm ? c.G : 0) + per_wg / 32);
+#define QKMLA_APPEND_BF16(TB, WQ)                                                           \
+  append_bf16_kernel<TB, WQ><<<g2, 256, 0, s>>>(batch, n_new, (const uint16_t*)c_new,         \
+                                                (const uint16_t*)k_rope_new, w_uk, gkr,       \
+                                                positions, pg, (uint16_t*)lat,                \
+                                                (uint16_t*)rope, alpha, status, c.G, c.r,     \
+                                                c.dc, c.dr, c.eps, rf, c.qk_norm)
+    const bool narrow_dc = c.dc <= 128;
+    if (wide && narrow_dc) QKMLA_APPEND_BF16(4, 4);
+    else if (wide) QKMLA_APPEND_BF16(4, 8);
+    else if (narrow_dc) QKMLA_APPEND_BF16(1, 4);
+    else QKMLA_APPEND_BF16(1, 8);
+#undef QKMLA_APPEND_BF16
     return hipGetLastError();
   }
   dim3 grid((unsigned)((T_total + kAppendTok - 1) / kAppendTok), c.qk_norm ? c.G + 1 : 1);

@@ -54,6 +54,10 @@ def _merge_heads_only(name, grid):
     if "merge_kernel" in name:
         return [(x, y, z) for z in range(grid[2]) for y in _merge_rows(name, grid)
                 for x in range(grid[0])]
+    # the wide bulk append: the first and the last (ragged) 128-token chunk
+    if "append_bf16_kernelILi4E" in name:
+        return [(x, y, z) for z in range(grid[2]) for y in range(grid[1])
+                for x in sorted({0, grid[0] - 1})]
     return None
 
 
@@ -182,6 +186,29 @@ def bf16_append_caches(dev):
     print(f"[{'ok' if wa <= 1e-3 and wr <= 1e-2 else 'FAIL'}] append caches: alpha {wa:.2e} "
           f"(bound 1e-3) rope {wr:.2e} (bound 1e-2)", flush=True)
     assert wa <= 1e-3 and wr <= 1e-2, (wa, wr)
+
+
+@case
+def bf16_bulk_append_wide(dev):
+    """The wide bulk append (4 token blocks per workgroup, from 4096 tokens on):
+    4100 tokens of one sequence in one qkmla_append call; the first and the
+    last (ragged, 4 tokens) 128-token chunks run and are checked against the
+    oracle's append: alpha^k, the RoPE key and the latent copy."""
+    lens = (4100,)
+    inp = make_inputs(DSV3, lens, seed=508)
+    s = Session(dev, DSV3, inp, host_fill=False)
+    rows = list(range(128)) + list(range(4096, 4100))
+    a_ref, r_ref = oracle.append_ref(inp.latents[0][rows], inp.k_rope_raw[0][rows],
+                                     np.array(rows), inp.w_uk, inp.gamma_k_rope, 1e-6, 10000.0,
+                                     qk_norm=True)
+    wa = float(np.max(np.abs(s.alpha[0, rows] - a_ref) / np.abs(a_ref)))
+    rope = (s.rope[0, rows].astype(np.uint32) << 16).view(np.float32)
+    wr = float(np.max(oracle.rowwise_rel_err(rope, r_ref)))
+    assert np.array_equal(s.lat[0, rows], s.store(inp.latents[0][rows])), "latent rows not copied"
+    print(f"[{'ok' if wa <= 1e-3 and wr <= 1e-2 else 'FAIL'}] wide bulk append: alpha {wa:.2e} "
+          f"(bound 1e-3) rope {wr:.2e} (bound 1e-2)", flush=True)
+    assert wa <= 1e-3 and wr <= 1e-2, (wa, wr)
+    assert s.status[0] == 0, f"device status {s.status[0]}"
 
 
 @case

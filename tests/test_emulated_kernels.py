@@ -39,7 +39,7 @@ def runtime(tmp_path_factory):
 # its longest case
 CASES = ["train_mfma", "train_varlen", "train_fwd_bwd", "paged_caches", "bf16_long_segments",
          "bf16_max_batch", "bf16_ragged_full", "bf16_32k_step", "bf16_long_context", "bf16_headline_sequence", "bf16_many_splits", "multi_query",
-         "bf16_split", "bf16_append_caches", "bf16_64_heads", "bf16_32_heads", "bf16_plain_overflow",
+         "bf16_split", "bf16_append_caches", "bf16_bulk_append_wide", "bf16_64_heads", "bf16_32_heads", "bf16_plain_overflow",
          "bf16_plain_hold", "fp32_tiny", "hazard_checker", "isa_semantics"]
 _WORKERS = max(1, min(6, (os.cpu_count() or 2) - 1))
 _futures = {}

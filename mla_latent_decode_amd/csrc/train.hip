@@ -31,7 +31,15 @@ constexpr int kKvTok = 8;     // tokens per workgroup of the key/value projectio
 constexpr int kLatTok = 4;    // tokens per workgroup of the latent gradient
 constexpr int kWgRows = 16;   // latent rows per workgroup of the weight gradients
 constexpr int kWgTok = 32;    // tokens per LDS chunk of the weight gradients
-constexpr int kGammaSplit = 64;
+constexpr int kGammaSplit = 512;  // most row ranges of the RMSNorm weight gradients
+static_assert(kGammaSplit % 16 == 0, "gamma_final_kernel gives each of 16 lanes a share");
+
+// Row ranges for an RMSNorm weight gradient over `rows` rows: about 128 rows
+// each, a multiple of 16, at least 16 and at most kGammaSplit.
+static int gamma_splits(int rows) {
+  const int want = ((rows + 127) / 128 + 15) / 16 * 16;
+  return want < 16 ? 16 : want > kGammaSplit ? kGammaSplit : want;
+}
 
 // Token rows are packed: sequence s holds rows [start_s, start_s + len_s).
 struct TrainDims {
@@ -700,30 +708,52 @@ __global__ __launch_bounds__(256) void weight_grad_kernel(TrainDims d, int n_row
 }
 
 // ---- backward: RMSNorm weight gradients ------------------------------------------------
-// dgamma[x] = sum_rows dy[row][x] x[row][x] a[row]; kGammaSplit partial sums
-// per column (blockIdx.y), then gamma_final_kernel adds them in order.
+// dgamma[x] = sum_rows dy[row][x] x[row][x] a[row]; one partial sum per column
+// and row range, then gamma_final_kernel adds them in order.  Block (x, y) takes
+// columns 64 x .. 64 x + 63 of the y-th of gridDim.y contiguous row ranges:
+// each wave reads 64 consecutive columns of a row (coalesced), the four waves
+// interleave rows and meet in LDS.  Every sum has a fixed order.
 template <typename X>
 __global__ __launch_bounds__(256) void gamma_partial_kernel(int rows, int n, const float* dy,
                                                             int dy_stride, const X* x,
                                                             int x_stride, const float* a,
                                                             float* partial) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= n) return;
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + c;
+  const int r0 = (int)((int64_t)blockIdx.y * rows / gridDim.y);
+  const int r1 = (int)((int64_t)(blockIdx.y + 1) * rows / gridDim.y);
   float s = 0.f;
-  for (int row = blockIdx.y; row < rows; row += kGammaSplit)
-    s += dy[(size_t)row * dy_stride + col] * Elem<X>::load(x, (size_t)row * x_stride + col) *
-         a[row];
-  partial[(size_t)blockIdx.y * n + col] = s;
+  if (col < n)
+    for (int row = r0 + rl; row < r1; row += 4)
+      s += dy[(size_t)row * dy_stride + col] * Elem<X>::load(x, (size_t)row * x_stride + col) *
+           a[row];
+  red[rl][c] = s;
+  __syncthreads();
+  if (rl == 0 && col < n)
+    partial[(size_t)blockIdx.y * n + col] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
 }
 
-__global__ __launch_bounds__(256) void gamma_final_kernel(int n, const float* partial,
+// Block x adds the partials of columns 16 x .. 16 x + 15: lane group k
+// (16 groups of 16 threads) takes partials k, k + 16, ..., and the groups meet
+// in LDS in a fixed order.
+__global__ __launch_bounds__(256) void gamma_final_kernel(int n, int splits, const float* partial,
                                                           float* out, int zero) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= n) return;
+  __shared__ float red[16][16];
+  const int c = threadIdx.x & 15, k0 = threadIdx.x >> 4;
+  const int col = blockIdx.x * 16 + c;
   float s = 0.f;
-  if (!zero)
-    for (int k = 0; k < kGammaSplit; ++k) s += partial[(size_t)k * n + col];
-  out[col] = s;
+  if (!zero && col < n)
+#pragma unroll 8
+    for (int k = k0; k < splits; k += 16) s += partial[(size_t)k * n + col];
+  red[k0][c] = s;
+  __syncthreads();
+  if (k0 == 0 && col < n) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += red[k][c];
+    out[col] = t;
+  }
 }
 
 // ---- MFMA path: keys and values from the GEMM results ------------------------------
@@ -1047,17 +1077,18 @@ static hipError_t backward_impl(const Cfg& c, const TrainSeqs& q, const TrainPtr
        gr.d_gamma_k_rope},
   };
   for (const G4& q : gs) {
-    const int nb = (q.n + 255) / 256;
+    const int splits = gamma_splits(q.rows);
+    const dim3 grid((q.n + 63) / 64, splits);
     if (d.qk_norm) {
       if (q.x_f32)
-        hipLaunchKernelGGL(gamma_partial_kernel<float>, dim3(nb, kGammaSplit), dim3(256), 0, s,
-                           q.rows, q.n, q.dy, q.dys, (const float*)q.x, q.xs, q.a, part);
+        hipLaunchKernelGGL(gamma_partial_kernel<float>, grid, dim3(256), 0, s, q.rows, q.n, q.dy,
+                           q.dys, (const float*)q.x, q.xs, q.a, part);
       else
-        hipLaunchKernelGGL(gamma_partial_kernel<T>, dim3(nb, kGammaSplit), dim3(256), 0, s,
-                           q.rows, q.n, q.dy, q.dys, (const T*)q.x, q.xs, q.a, part);
+        hipLaunchKernelGGL(gamma_partial_kernel<T>, grid, dim3(256), 0, s, q.rows, q.n, q.dy,
+                           q.dys, (const T*)q.x, q.xs, q.a, part);
     }
-    hipLaunchKernelGGL(gamma_final_kernel, dim3(nb), dim3(256), 0, s, q.n, part, q.out,
-                       d.qk_norm ? 0 : 1);
+    hipLaunchKernelGGL(gamma_final_kernel, dim3((q.n + 15) / 16), dim3(256), 0, s, q.n, splits,
+                       part, q.out, d.qk_norm ? 0 : 1);
   }
   return hipGetLastError();
 }

@@ -136,6 +136,7 @@ struct TrainWs {
   size_t dQh, dKh, dV, Dsum, dK, dKr, gamma_partial;
   size_t dOb, stat;  // MFMA backward: d_o bf16 [BT][H][d_v], (lse*log2 e, D) [BT][H]
   size_t dKb, dVb;   // MFMA backward: dk, dV in bf16 [BT][G][d_c], [BT][G][d_v]
+  size_t fb_part;    // MFMA backward, split key side: [S][BT][G][d_c + d_r], then [S][BT][G][d_v]
   size_t total;
 };
 TrainWs train_ws_layout(const Cfg& c, const TrainSeqs& q);
@@ -145,11 +146,15 @@ bool train_mfma_shape(const Cfg& c);
 hipError_t launch_flash_fwd(const Cfg& c, const FlashSeqs& q, const void* Qb, const void* Kb,
                             const void* Vb, float* o, float* lse, hipStream_t s);
 // dK^ and dV (key side) and dQ^ (query side) of the attention, fp32, in the
-// row-major layouts of the row-parallel kernels.
+// row-major layouts of the row-parallel kernels.  The key side runs in
+// S = flash_bwd_splits(...) token ranges; when S > 1 `part` holds their
+// partial sums (S (d_c + d_r + d_v) floats per row and group), added in a
+// fixed order.
+int flash_bwd_splits(int n_seq, int max_len, int G);
 hipError_t launch_flash_bwd(const Cfg& c, const FlashSeqs& q, const void* Qb, const void* Kb,
                             const void* Vb, const float* o, const float* lse, const float* d_o,
                             void* dOb, void* stat, float* dKh, float* dV, float* dQh,
-                            hipStream_t s);
+                            float* part, hipStream_t s);
 
 // ---- bf16 MFMA GEMM (training projections) --------------------------------------
 // Operand element (mn, k) of batch z sits at p + z*batch_stride +

@@ -195,6 +195,77 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
   }
 }
 
+// The same for the MFMA attention's shape (bf16, d_c = 128, d_r = 64), with
+// vector accesses: lanes 0..31 take four content dims each, lanes 32..63 one
+// RoPE pair each.  Needs q_c 8-byte, q_rope 4-byte and gamma_q 16-byte
+// aligned (checked by the launcher).
+__global__ __launch_bounds__(256) void prep_q_mf_kernel(TrainDims d,
+                                                        const uint16_t* __restrict__ q_c,
+                                                        const uint16_t* __restrict__ q_rope,
+                                                        const float* __restrict__ gq,
+                                                        const float* __restrict__ gqr,
+                                                        uint16_t* __restrict__ Qb,
+                                                        float* __restrict__ aq,
+                                                        float* __restrict__ aqr) {
+  const size_t row = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (h >= d.H) return;
+  const size_t qh = row * d.H + h;
+  const bool rp = lane >= 32;
+  const int j = lane & 31;
+  float x[4];
+  if (!rp) {
+    const uint2 v = *(const uint2*)(q_c + qh * 128 + 4 * j);
+    x[0] = __uint_as_float(v.x << 16);
+    x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(v.y << 16);
+    x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  } else {
+    const uint32_t v = *(const uint32_t*)(q_rope + qh * 64 + 2 * j);
+    x[0] = __uint_as_float(v << 16);
+    x[1] = __uint_as_float(v & 0xFFFF0000u);
+    x[2] = x[3] = 0.f;
+  }
+  float a = 1.f, ar = 1.f;
+  if (d.qk_norm) {
+    const float sq = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    const float ss = wave_sum(rp ? 0.f : sq), sr = wave_sum(rp ? sq : 0.f);
+    a = 1.0f / sqrtf(ss / 128.f + d.eps);
+    ar = 1.0f / sqrtf(sr / 64.f + d.eps);
+    if (lane == 0) {
+      aq[qh] = a;
+      aqr[qh] = ar;
+    }
+  }
+  const float qs = d.tau * kLog2e;
+  uint16_t* out = Qb + qh * 192;
+  if (!rp) {
+    float y[4];
+    if (d.qk_norm) {
+      const f32x4 g = *(const f32x4*)(gq + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = x[e] * (g[e] * a);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = x[e];
+    }
+    uint2 v;
+    v.x = f32_to_bf16(y[0] * qs) | ((uint32_t)f32_to_bf16(y[1] * qs) << 16);
+    v.y = f32_to_bf16(y[2] * qs) | ((uint32_t)f32_to_bf16(y[3] * qs) << 16);
+    *(uint2*)(out + 4 * j) = v;
+  } else {
+    float x0 = x[0], x1 = x[1];
+    if (d.qk_norm) {
+      x0 *= gqr[2 * j] * ar;
+      x1 *= gqr[2 * j + 1] * ar;
+    }
+    float cs, sn;
+    rope_at(d, d.rpos[row], j, &cs, &sn);
+    *(uint32_t*)(out + 128 + 2 * j) = f32_to_bf16((x0 * cs - x1 * sn) * qs) |
+                                      ((uint32_t)f32_to_bf16((x0 * sn + x1 * cs) * qs) << 16);
+  }
+}
+
 // ---- forward: keys and values -----------------------------------------------
 // Workgroup = kKvTok token rows x one group g.  Thread e owns output dim e of
 // k = c W^UK_g and v = c W^UV_g for the workgroup's tokens.  Writes the raw
@@ -548,6 +619,77 @@ __global__ __launch_bounds__(256) void q_norm_bwd_kernel(
   }
 }
 
+// The same for the MFMA attention's shape (bf16, d_c = 128, d_r = 64), with
+// vector accesses: lanes 0..31 take four content dims each, lanes 32..63 one
+// RoPE pair each.  Needs q_c 8-byte, q_rope 4-byte, gamma_q and d_q_c
+// 16-byte and d_q_rope 8-byte aligned (checked by the launcher).
+__global__ __launch_bounds__(256) void q_norm_bwd_mf_kernel(
+    TrainDims d, const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ q_rope,
+    const float* __restrict__ gq, const float* __restrict__ gqr, const float* __restrict__ aq,
+    const float* __restrict__ aqr, float* __restrict__ dQh, float* __restrict__ d_q_c,
+    float* __restrict__ d_q_rope) {
+  const size_t row = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (h >= d.H) return;
+  const size_t qh = row * d.H + h;
+  const bool rp = lane >= 32;
+  const int j = lane & 31;
+  float* dy = dQh + qh * 192;
+  float y[4], x[4];
+  if (!rp) {
+    const f32x4 v = *(const f32x4*)(dy + 4 * j);
+    const uint2 xv = *(const uint2*)(q_c + qh * 128 + 4 * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = v[e];
+    x[0] = __uint_as_float(xv.x << 16);
+    x[1] = __uint_as_float(xv.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(xv.y << 16);
+    x[3] = __uint_as_float(xv.y & 0xFFFF0000u);
+  } else {
+    // turn the RoPE-part gradient back (transposed rotation) and keep it in
+    // dQ^ for the gamma reduction
+    const float2 v = *(const float2*)(dy + 128 + 2 * j);
+    float cs, sn;
+    rope_at(d, d.rpos[row], j, &cs, &sn);
+    y[0] = v.x * cs + v.y * sn;
+    y[1] = -v.x * sn + v.y * cs;
+    y[2] = y[3] = 0.f;
+    *(float2*)(dy + 128 + 2 * j) = make_float2(y[0], y[1]);
+    const uint32_t xv = *(const uint32_t*)(q_rope + qh * 64 + 2 * j);
+    x[0] = __uint_as_float(xv << 16);
+    x[1] = __uint_as_float(xv & 0xFFFF0000u);
+    x[2] = x[3] = 0.f;
+  }
+  if (!d.qk_norm) {
+    if (!rp) *(f32x4*)(d_q_c + qh * 128 + 4 * j) = f32x4{y[0], y[1], y[2], y[3]};
+    else *(float2*)(d_q_rope + qh * 64 + 2 * j) = make_float2(y[0], y[1]);
+    return;
+  }
+  float g[4];
+  if (!rp) {
+    const f32x4 gv = *(const f32x4*)(gq + 4 * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = gv[e];
+  } else {
+    g[0] = gqr[2 * j];
+    g[1] = gqr[2 * j + 1];
+    g[2] = g[3] = 0.f;
+  }
+  float sp = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sp += g[e] * y[e] * x[e];
+  const float sc = wave_sum(rp ? 0.f : sp), sr = wave_sum(rp ? sp : 0.f);
+  const float a = rp ? aqr[qh] : aq[qh];
+  const float k = a * a * a * (rp ? sr / 64.f : sc / 128.f);
+  if (!rp)
+    *(f32x4*)(d_q_c + qh * 128 + 4 * j) =
+        f32x4{a * g[0] * y[0] - x[0] * k, a * g[1] * y[1] - x[1] * k, a * g[2] * y[2] - x[2] * k,
+              a * g[3] * y[3] - x[3] * k};
+  else
+    *(float2*)(d_q_rope + qh * 64 + 2 * j) =
+        make_float2(a * g[0] * y[0] - x[0] * k, a * g[1] * y[1] - x[1] * k);
+}
+
 // ---- backward: key norms and the shared RoPE key -------------------------------------
 // One workgroup per token row.  Wave w runs the content-key RMSNorm backward
 // of groups w, w+4, ...; then the RoPE key gradient is summed over the
@@ -874,6 +1016,8 @@ TrainWs train_ws_layout(const Cfg& c, const TrainSeqs& q) {
   w.stat = take(mf ? BT * c.H * 8 : 0);
   w.dKb = take(mf ? BT * c.G * c.dc * 2 : 0);
   w.dVb = take(mf ? BT * c.G * c.dv * 2 : 0);
+  const int fbs = mf ? flash_bwd_splits(q.n_seq, q.max_len, c.G) : 1;
+  w.fb_part = take(fbs > 1 ? fbs * BT * c.G * (dqk + c.dv) * 4 : 0);
   w.total = off;
   return w;
 }
@@ -902,6 +1046,16 @@ static TrainDims launch_tables(const Cfg& c, const TrainSeqs& q, const TrainWs& 
 template <typename T, bool MF>
 static void launch_prep_q(const TrainDims& d, const TrainPtrs& in, const TrainWs& ws, char* wsb,
                           hipStream_t s) {
+  if constexpr (MF) {
+    if (d.dc == 128 && d.dr == 64 &&
+        (((uintptr_t)in.q_c & 7) | ((uintptr_t)in.q_rope & 3) | ((uintptr_t)in.gamma_q & 15)) ==
+            0) {
+      hipLaunchKernelGGL(prep_q_mf_kernel, dim3(d.n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
+                         (const uint16_t*)in.q_c, (const uint16_t*)in.q_rope, in.gamma_q,
+                         in.gamma_q_rope, WS(uint16_t, Qb), WS(float, aq), WS(float, aqr));
+      return;
+    }
+  }
   hipLaunchKernelGGL((prep_q_kernel<T, MF>), dim3(d.n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
                      (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
                      WS(float, Qh), WS(uint16_t, Qb), WS(float, aq), WS(float, aqr));
@@ -1023,7 +1177,7 @@ static hipError_t backward_impl(const Cfg& c, const TrainSeqs& q, const TrainPtr
     if (e != hipSuccess) return e;
     e = launch_flash_bwd(c, flash_seqs(d, ws, wsb), wsb + ws.Qb, wsb + ws.Kb, wsb + ws.Vb, o,
                          lse, d_o, wsb + ws.dOb, wsb + ws.stat, WS(float, dKh), WS(float, dV),
-                         WS(float, dQh), s);
+                         WS(float, dQh), WS(float, fb_part), s);
     if (e != hipSuccess) return e;
   } else {
     launch_prep<T>(d, in, ws, wsb, s);
@@ -1036,10 +1190,18 @@ static hipError_t backward_impl(const Cfg& c, const TrainSeqs& q, const TrainPtr
                        WS(const float, Kh), WS(const float, V), lse, d_o, WS(const float, Dsum),
                        WS(float, dKh), WS(float, dV));
   }
-  hipLaunchKernelGGL(q_norm_bwd_kernel<T>, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
-                     (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
-                     WS(const float, aq), WS(const float, aqr), WS(float, dQh), gr.d_q_c,
-                     gr.d_q_rope);
+  if (mf && d.dc == 128 && d.dr == 64 &&
+      (((uintptr_t)in.q_c & 7) | ((uintptr_t)in.q_rope & 3) | ((uintptr_t)in.gamma_q & 15) |
+       ((uintptr_t)gr.d_q_c & 15) | ((uintptr_t)gr.d_q_rope & 7)) == 0)
+    hipLaunchKernelGGL(q_norm_bwd_mf_kernel, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
+                       (const uint16_t*)in.q_c, (const uint16_t*)in.q_rope, in.gamma_q,
+                       in.gamma_q_rope, WS(const float, aq), WS(const float, aqr), WS(float, dQh),
+                       gr.d_q_c, gr.d_q_rope);
+  else
+    hipLaunchKernelGGL(q_norm_bwd_kernel<T>, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
+                       (const T*)in.q_c, (const T*)in.q_rope, in.gamma_q, in.gamma_q_rope,
+                       WS(const float, aq), WS(const float, aqr), WS(float, dQh), gr.d_q_c,
+                       gr.d_q_rope);
   hipLaunchKernelGGL(k_norm_bwd_kernel<T>, dim3(n_rows), dim3(256), 0, s, d, (const T*)in.k_rope,
                      in.gamma_k, in.gamma_k_rope, WS(const float, Kraw), WS(const float, ak),
                      WS(const float, akr), WS(const float, dKh), WS(float, dK), WS(float, dKr),

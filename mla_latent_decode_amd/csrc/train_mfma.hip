@@ -42,6 +42,11 @@ constexpr int kKChunks = kFaKeys * kFaDqk * 2 / 16;  // 768 16-byte chunks per K
 constexpr int kVChunks = kFaKeys * kFaDv * 2 / 16;   // 512 per V tile
 constexpr int kQkSteps = kFaDqk / 16;       // 12
 constexpr int kDvBlocks = kFaDv / 32;       // 4
+// Key side of the backward: each 128-key block's causal token range is cut
+// into up to kFbMaxSplits pieces, as many as bring the grid to about
+// kFbTargetWgs workgroups (two per CU).
+constexpr int kFbMaxSplits = 8;
+constexpr int kFbTargetWgs = 512;
 
 // Token rows are packed: sequence s holds rows seqs[s].x .. + seqs[s].y - 1.
 struct FaArgs {
@@ -254,13 +259,19 @@ struct FbArgs {
   const int2* seqs;     // [n_seq] (start row, length)
   int n_rows, H, G;
   float tau;
+  // Key side split over `splits` token ranges: range c writes its dK^ / dV
+  // into dKp + c [rows][G][192] / dVp + c [rows][G][128] (dKh / dV when 1).
+  float* dKp;
+  float* dVp;
+  int splits;
 };
 
-// Key side: workgroup = (sequence, group, 128 keys); wave w owns the 32-key
-// tile 4*blockIdx.x + w, whose K^ and V stay in its registers as B operands.
-// All four waves share the query rows, which stream through a double-buffered
-// LDS stage two tokens (x 16 heads = 32 rows) at a time from the block's
-// first key on; the next step's rows are in flight during each step.
+// Key side: workgroup = (sequence, group, 128 keys, token range); wave w
+// owns the block's w-th 32-key tile, whose K^ and V stay in its registers as
+// B operands.  All four waves share the query rows, which stream through a
+// double-buffered LDS stage two tokens (x 16 heads = 32 rows) at a time over
+// the workgroup's share of the tokens from the block's first key on; the
+// next two steps' rows are in flight during each step.
 //   S  (rows x keys) = Q^ . K^T,  dP = d_o . V^T       (lane = key, regs = rows)
 //   p = 2^(S - lse2) (0 where key > token), dS = p (dP - D)
 //   dV^T (128 x keys) += d_o^T . P,   dK^T (192 x keys) += Q^T . dS
@@ -308,11 +319,20 @@ __global__ __launch_bounds__(256) void flash_bwd_kv_kernel(FbArgs a) {
   __shared__ __attribute__((aligned(16))) char q_st[2][32 * kKPitch];
   __shared__ __attribute__((aligned(16))) char o_st[2][32 * kVPitch];
   __shared__ float2 st_s[2][32];
-  const int g = blockIdx.y;
+  // blockIdx.x = (key block * G + g) * splits + split: the longest token
+  // ranges (the first key blocks) are dispatched first
+  const unsigned bx = blockIdx.x, sp = a.splits, gn = a.G;
+  const int split = (int)(bx % sp);  // which token range of the key block
+  const int g = (int)(bx / sp % gn);
   const int2 sq = a.seqs[blockIdx.z];  // (start row, length), uniform
   const int T = sq.y;
-  const int kblk0 = blockIdx.x * 4 * kFaKeys;  // first key of the workgroup
+  const int kblk0 = (int)(bx / (sp * gn)) * 4 * kFaKeys;  // first key of the workgroup
   if (kblk0 >= T) return;  // whole workgroup: past this sequence
+  // The key block's tokens kblk0 .. T-1 form n2 two-token steps; this
+  // workgroup takes steps [n2 split / splits, n2 (split + 1) / splits).
+  const int n2 = (T - kblk0 + 1) / 2;
+  const int i_lo = kblk0 + 2 * (int)((int64_t)n2 * split / a.splits);
+  const int i_hi = kblk0 + 2 * (int)((int64_t)n2 * (split + 1) / a.splits);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hf = lane >> 5, n = lane & 31;
@@ -343,12 +363,15 @@ __global__ __launch_bounds__(256) void flash_bwd_kv_kernel(FbArgs a) {
 
   const size_t seq_row0 = sq.x;
   const int s16 = lane & 15, dblk = (lane >> 4) & 1;
-  RowStage rs;
-  rs.load(a, seq_row0, T, g, kblk0, tid);
-  rs.store(q_st[0], o_st[0], st_s[0], tid);
+  // Rows of step i0 + 2 wait in registers while step i0 is computed, and
+  // those of step i0 + 4 are on their way: two steps of load latency hidden.
+  RowStage ra, rb;
+  ra.load(a, seq_row0, T, g, i_lo, tid);
+  ra.store(q_st[0], o_st[0], st_s[0], tid);
+  if (i_lo + 2 < i_hi) ra.load(a, seq_row0, T, g, i_lo + 2, tid);
   __syncthreads();
-  for (int i0 = kblk0, buf = 0; i0 < T; i0 += 2, buf ^= 1) {
-    if (i0 + 2 < T) rs.load(a, seq_row0, T, g, i0 + 2, tid);
+  auto step = [&](int i0, int buf, RowStage& next, RowStage& after) {
+    if (i0 + 4 < i_hi) after.load(a, seq_row0, T, g, i0 + 4, tid);
     // wave-uniform: the step's tokens all precede this wave's keys
     if (i0 + 1 >= key0 && key0 < T) {
       const char* qs = q_st[buf];
@@ -408,15 +431,20 @@ __global__ __launch_bounds__(256) void flash_bwd_kv_kernel(FbArgs a) {
         }
       }
     }
-    if (i0 + 2 < T) rs.store(q_st[buf ^ 1], o_st[buf ^ 1], st_s[buf ^ 1], tid);
+    if (i0 + 2 < i_hi) next.store(q_st[buf ^ 1], o_st[buf ^ 1], st_s[buf ^ 1], tid);
     __syncthreads();
+  };
+  for (int i0 = i_lo; i0 < i_hi; i0 += 4) {
+    step(i0, 0, ra, rb);
+    if (i0 + 2 >= i_hi) break;
+    step(i0 + 2, 1, rb, ra);
   }
-  if (key >= T) return;
+  if (key >= T) return;  // (an empty token range still writes its zeros)
   // lane holds column `key`; reg r of block mb is dim 32mb + 8(r/4) + 4hf + r%4.
   // Q^ carries tau*log2(e): dK^ = tau sum dS Q^ = (sum dS Qb) / log2(e).
-  const size_t out_row = (seq_row0 + key) * a.G + g;
-  float* dk = a.dKh + out_row * kFaDqk + 4 * hf;
-  float* dv = a.dV + out_row * kFaDv + 4 * hf;
+  const size_t out_row = (size_t)split * a.n_rows * a.G + (seq_row0 + key) * a.G + g;
+  float* dk = a.dKp + out_row * kFaDqk + 4 * hf;
+  float* dv = a.dVp + out_row * kFaDv + 4 * hf;
 #pragma unroll
   for (int mb = 0; mb < kFaDqk / 32; ++mb)
 #pragma unroll
@@ -437,6 +465,17 @@ __global__ __launch_bounds__(256) void flash_bwd_kv_kernel(FbArgs a) {
     }
 }
 
+// out[i] = sum over the splits c of part[c n4 + i], in order of c.
+__global__ __launch_bounds__(256) void split_sum_kernel(size_t n4, int splits,
+                                                        const f32x4* __restrict__ part,
+                                                        f32x4* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 acc = part[i];
+  for (int c = 1; c < splits; ++c) acc += part[(size_t)c * n4 + i];
+  out[i] = acc;
+}
+
 // Query side: the forward's workgroup shape (8 tokens x 16 heads, four
 // wavefronts sharing each 32-key tile).  Per key tile:
 //   S^T = K^ . Q^T,  dP^T = V . d_o^T                  (lane = row, regs = keys)
@@ -445,7 +484,10 @@ __global__ __launch_bounds__(256) void flash_bwd_kv_kernel(FbArgs a) {
 __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
   __shared__ __attribute__((aligned(16))) char k_st[2][kFaKeys * kKPitch];
   __shared__ __attribute__((aligned(16))) char v_st[2][kFaKeys * kVPitch];
-  const int qb = blockIdx.x, g = blockIdx.y;
+  // blockIdx.x = (last query block - qb) * G + g: the blocks with the most
+  // key tiles are dispatched first
+  const unsigned bx = blockIdx.x, gn = a.G;
+  const int qb = (int)(gridDim.x / gn - 1 - bx / gn), g = (int)(bx % gn);
   const int2 sq = a.seqs[blockIdx.z];  // (start row, length), uniform
   const int T = sq.y;
   if (qb * kFaTok >= T) return;  // whole workgroup: past this sequence
@@ -479,12 +521,15 @@ __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dQT[mb][r] = 0.f;
   const int s16 = lane & 15, dblk = (lane >> 4) & 1;
+  // Tile kt + 1 waits in registers while tile kt is computed, and tile
+  // kt + 2 is on its way: two tiles of load latency hidden.
+  KvStage sb;
   stage.load(kbase, vbase, 0, T, tid);
   stage.store(k_st[0], v_st[0], tid);
+  if (1 < n_kt) stage.load(kbase, vbase, 1, T, tid);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) stage.load(kbase, vbase, kt + 1, T, tid);
+  auto tile = [&](int kt, int buf, KvStage& next, KvStage& after) {
+    if (kt + 2 < n_kt) after.load(kbase, vbase, kt + 2, T, tid);
     const char* ks = k_st[buf];
     const char* vs = v_st[buf];
     f32x16 sacc, dpacc;
@@ -524,8 +569,13 @@ __global__ __launch_bounds__(256) void flash_bwd_q_kernel(FbArgs a) {
         const bf16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         dQT[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, db[kk], dQT[mb], 0, 0, 0);
       }
-    if (kt + 1 < n_kt) stage.store(k_st[buf ^ 1], v_st[buf ^ 1], tid);
+    if (kt + 1 < n_kt) next.store(k_st[buf ^ 1], v_st[buf ^ 1], tid);
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile(kt, 0, stage, sb);
+    if (kt + 1 >= n_kt) break;
+    tile(kt + 1, 1, sb, stage);
   }
   if (!valid) return;
   // dQ^ = tau sum dS K^ (the logits' scale of dS is the natural one)
@@ -560,20 +610,38 @@ hipError_t launch_flash_fwd(const Cfg& c, const FlashSeqs& q, const void* Qb, co
 
 namespace qkmla {
 
+int flash_bwd_splits(int n_seq, int max_len, int G) {
+  const int64_t blocks = (int64_t)(max_len + 4 * kFaKeys - 1) / (4 * kFaKeys) * G * n_seq;
+  int sp = 1;
+  while (sp < kFbMaxSplits && blocks * sp < kFbTargetWgs) sp *= 2;
+  return sp;
+}
+
 hipError_t launch_flash_bwd(const Cfg& c, const FlashSeqs& q, const void* Qb, const void* Kb,
                             const void* Vb, const float* o, const float* lse, const float* d_o,
                             void* dOb, void* stat, float* dKh, float* dV, float* dQh,
-                            hipStream_t s) {
+                            float* part, hipStream_t s) {
   const int rows_h = q.n_rows * c.H;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((rows_h + 3) / 4), dim3(256), 0, s, rows_h, o, lse,
                      d_o, (uint16_t*)dOb, (float2*)stat);
+  const int sp = flash_bwd_splits(q.n_seq, q.max_len, c.G);
+  const size_t nk = (size_t)q.n_rows * c.G * kFaDqk, nv = (size_t)q.n_rows * c.G * kFaDv;
+  float* dKp = sp > 1 ? part : dKh;
+  float* dVp = sp > 1 ? part + sp * nk : dV;
   FbArgs a{(const uint16_t*)Qb, (const uint16_t*)Kb, (const uint16_t*)Vb, (const uint16_t*)dOb,
-           (const float2*)stat, dKh, dV, dQh, q.seqs, q.n_rows, c.H, c.G, c.tau};
+           (const float2*)stat, dKh, dV, dQh, q.seqs, q.n_rows, c.H, c.G, c.tau, dKp, dVp, sp};
   hipLaunchKernelGGL(flash_bwd_kv_kernel,
-                     dim3((q.max_len + 4 * kFaKeys - 1) / (4 * kFaKeys), c.G, q.n_seq), dim3(256),
-                     0, s, a);
-  hipLaunchKernelGGL(flash_bwd_q_kernel, dim3((q.max_len + kFaTok - 1) / kFaTok, c.G, q.n_seq),
+                     dim3((q.max_len + 4 * kFaKeys - 1) / (4 * kFaKeys) * c.G * sp, 1, q.n_seq),
                      dim3(256), 0, s, a);
+  if (sp > 1) {
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((nk / 4 + 255) / 256)), dim3(256), 0, s,
+                       nk / 4, sp, (const f32x4*)dKp, (f32x4*)dKh);
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((nv / 4 + 255) / 256)), dim3(256), 0, s,
+                       nv / 4, sp, (const f32x4*)dVp, (f32x4*)dV);
+  }
+  hipLaunchKernelGGL(flash_bwd_q_kernel,
+                     dim3((q.max_len + kFaTok - 1) / kFaTok * c.G, 1, q.n_seq), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -693,6 +693,12 @@ for _n, (_f, _k) in _V.items():
     HANDLERS[_n] = _vop(_f, _k)
 
 
+@h("v_mul_hi_i32")
+def _(w, i):
+    d, a, b = i.ops
+    w.vset(d, ((_i(w, a) * _i(w, b)) >> 32) & M32)
+
+
 @h("v_ashrrev_i32")
 def _(w, i):
     d, a, b = i.ops

@@ -87,16 +87,19 @@ def test_train_deepseek_like_layer_mfma(B, T, qk_norm):
     _run(DSV3, B, T, 703 + T, qk_norm=qk_norm, tol=BF16_TOL)
 
 
-def test_train_full_length_sampled_and_invariants():
-    """2048 tokens of the bf16 layer: sampled forward rows against the decode
-    oracle over their prefix (a training row is a decode step), and the
-    backward against properties that hold at any size: the RMSNorm scale
-    invariance makes each gradient row of q_c, q_rope and k_rope, and each
-    group's W^UK gradient, orthogonal to its input (up to eps = 1e-6)."""
+@pytest.mark.parametrize("T", [2048, 8192])
+def test_train_full_length_sampled_and_invariants(T):
+    """2048 and 8192 tokens of the bf16 layer (at 8192 the projection GEMMs
+    take their 128 x 128 tiles, below it 64 x 64): sampled forward rows
+    against the decode oracle over their prefix (a training row is a decode
+    step), and the backward against properties that hold at any size: the
+    RMSNorm scale invariance makes each gradient row of q_c, q_rope and
+    k_rope, and each group's W^UK gradient, orthogonal to its input (up to
+    eps = 1e-6)."""
     import oracle
-    B, T = 1, 2048
+    B = 1
     cfg = ops.Config.from_shape(DSV3)
-    inp = train_inputs(DSV3, B, T, 720)
+    inp = train_inputs(DSV3, B, T, {2048: 720, 8192: 721}[T])
     d_o = inp.pop("d_o")
     dt = cfg.torch_dtype
     dev = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).to(

@@ -97,7 +97,10 @@ struct KvStage {
 __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
   __shared__ __attribute__((aligned(16))) char k_st[2][kFaKeys * kKPitch];
   __shared__ __attribute__((aligned(16))) char v_st[2][kFaKeys * kVPitch];
-  const int qb = blockIdx.x, g = blockIdx.y;
+  // blockIdx.x = (last query block - qb) * G + g: the blocks with the most
+  // key tiles are dispatched first
+  const unsigned bx = blockIdx.x, gn = a.G;
+  const int qb = (int)(gridDim.x / gn - 1 - bx / gn), g = (int)(bx % gn);
   const int2 sq = a.seqs[blockIdx.z];  // (start row, length), uniform
   const int T = sq.y;
   if (qb * kFaTok >= T) return;  // whole workgroup: past this sequence
@@ -133,12 +136,15 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
     for (int r = 0; r < 16; ++r) O[mb][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // Tile kt + 1 waits in registers while tile kt is computed, and tile
+  // kt + 2 is on its way: two tiles of load latency hidden.
+  KvStage sb;
   stage.load(kbase, vbase, 0, T, tid);
   stage.store(k_st[0], v_st[0], tid);
+  if (1 < n_kt) stage.load(kbase, vbase, 1, T, tid);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) stage.load(kbase, vbase, kt + 1, T, tid);
+  auto tile = [&](int kt, int buf, KvStage& next, KvStage& after) {
+    if (kt + 2 < n_kt) after.load(kbase, vbase, kt + 2, T, tid);
     const char* ks = k_st[buf];
     const char* vs = v_st[buf];
 
@@ -207,8 +213,13 @@ __global__ __launch_bounds__(256, 2) void flash_fwd_kernel(FaArgs a) {
         O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[kk], O[mb], 0, 0, 0);
       }
     }
-    if (kt + 1 < n_kt) stage.store(k_st[buf ^ 1], v_st[buf ^ 1], tid);
+    if (kt + 1 < n_kt) next.store(k_st[buf ^ 1], v_st[buf ^ 1], tid);
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile(kt, 0, stage, sb);
+    if (kt + 1 >= n_kt) break;
+    tile(kt + 1, 1, sb, stage);
   }
 
   // ---- epilogue: lane holds O^T[32mb + 8(r/4) + 4hf + r%4][its row] ----
@@ -601,8 +612,9 @@ hipError_t launch_flash_fwd(const Cfg& c, const FlashSeqs& q, const void* Qb, co
                             const void* Vb, float* o, float* lse, hipStream_t s) {
   FaArgs a{(const uint16_t*)Qb, (const uint16_t*)Kb, (const uint16_t*)Vb, o, lse, q.seqs,
            q.n_rows, c.H, c.G};
-  hipLaunchKernelGGL(flash_fwd_kernel, dim3((q.max_len + kFaTok - 1) / kFaTok, c.G, q.n_seq),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL(flash_fwd_kernel,
+                     dim3((q.max_len + kFaTok - 1) / kFaTok * c.G, 1, q.n_seq), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 

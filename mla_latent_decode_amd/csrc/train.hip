@@ -197,8 +197,12 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
 
 // The same for the MFMA attention's shape (bf16, d_c = 128, d_r = 64), with
 // vector accesses: lanes 0..31 take four content dims each, lanes 32..63 one
-// RoPE pair each.  Needs q_c 8-byte, q_rope 4-byte and gamma_q 16-byte
+// RoPE pair each.  A wave takes kMfHeads heads of one row, with all of their
+// loads in flight together; the gammas, position and rotation are loaded
+// once per wave.  Needs q_c and q_rope 4-byte and both gammas 8-byte
 // aligned (checked by the launcher).
+constexpr int kMfHeads = 8;  // heads per wave of the vector row kernels
+
 __global__ __launch_bounds__(256) void prep_q_mf_kernel(TrainDims d,
                                                         const uint16_t* __restrict__ q_c,
                                                         const uint16_t* __restrict__ q_rope,
@@ -208,61 +212,73 @@ __global__ __launch_bounds__(256) void prep_q_mf_kernel(TrainDims d,
                                                         float* __restrict__ aq,
                                                         float* __restrict__ aqr) {
   const size_t row = blockIdx.x;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (h >= d.H) return;
-  const size_t qh = row * d.H + h;
+  const int lane = threadIdx.x & 63;
+  const int h0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kMfHeads;
+  if (h0 >= d.H) return;
+  const int nh = min(kMfHeads, d.H - h0);
   const bool rp = lane >= 32;
   const int j = lane & 31;
-  float x[4];
-  if (!rp) {
-    const uint2 v = *(const uint2*)(q_c + qh * 128 + 4 * j);
-    x[0] = __uint_as_float(v.x << 16);
-    x[1] = __uint_as_float(v.x & 0xFFFF0000u);
-    x[2] = __uint_as_float(v.y << 16);
-    x[3] = __uint_as_float(v.y & 0xFFFF0000u);
-  } else {
-    const uint32_t v = *(const uint32_t*)(q_rope + qh * 64 + 2 * j);
-    x[0] = __uint_as_float(v << 16);
-    x[1] = __uint_as_float(v & 0xFFFF0000u);
-    x[2] = x[3] = 0.f;
+  // Branch-free loads (two dwords per lane; a RoPE lane reads its pair twice)
+  // so that the loads of all kMfHeads heads stay in flight together.
+  uint2 raw[kMfHeads];
+#pragma unroll
+  for (int u = 0; u < kMfHeads; ++u) {
+    const size_t qh = row * d.H + h0 + (u < nh ? u : 0);
+    const uint32_t* p0 = rp ? (const uint32_t*)(q_rope + qh * 64 + 2 * j)
+                            : (const uint32_t*)(q_c + qh * 128 + 4 * j);
+    const uint32_t v0 = p0[0], v1 = p0[rp ? 0 : 1];
+    raw[u] = make_uint2(v0, rp ? 0u : v1);
   }
-  float a = 1.f, ar = 1.f;
+  float g[4] = {1.f, 1.f, 1.f, 1.f};
   if (d.qk_norm) {
-    const float sq = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-    const float ss = wave_sum(rp ? 0.f : sq), sr = wave_sum(rp ? sq : 0.f);
-    a = 1.0f / sqrtf(ss / 128.f + d.eps);
-    ar = 1.0f / sqrtf(sr / 64.f + d.eps);
-    if (lane == 0) {
-      aq[qh] = a;
-      aqr[qh] = ar;
-    }
+    const float2* pg = rp ? (const float2*)(gqr + 2 * j) : (const float2*)(gq + 4 * j);
+    const float2 g0 = pg[0], g1 = pg[rp ? 0 : 1];
+    g[0] = g0.x;
+    g[1] = g0.y;
+    g[2] = g1.x;
+    g[3] = g1.y;
   }
+  float cs = 1.f, sn = 0.f;
+  if (rp) rope_at(d, d.rpos[row], j, &cs, &sn);
   const float qs = d.tau * kLog2e;
-  uint16_t* out = Qb + qh * 192;
-  if (!rp) {
-    float y[4];
-    if (d.qk_norm) {
-      const f32x4 g = *(const f32x4*)(gq + 4 * j);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = x[e] * (g[e] * a);
+  for (int u = 0; u < kMfHeads; ++u) {
+    if (u >= nh) break;
+    const size_t qh = row * d.H + h0 + u;
+    float x[4];
+    x[0] = __uint_as_float(raw[u].x << 16);
+    x[1] = __uint_as_float(raw[u].x & 0xFFFF0000u);
+    x[2] = __uint_as_float(raw[u].y << 16);
+    x[3] = __uint_as_float(raw[u].y & 0xFFFF0000u);
+    float a = 1.f, ar = 1.f;
+    if (d.qk_norm) {
+      const float sq = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      const float ss = wave_sum(rp ? 0.f : sq), sr = wave_sum(rp ? sq : 0.f);
+      a = 1.0f / sqrtf(ss / 128.f + d.eps);
+      ar = 1.0f / sqrtf(sr / 64.f + d.eps);
+      if (lane == 0) {
+        aq[qh] = a;
+        aqr[qh] = ar;
+      }
+    }
+    uint16_t* out = Qb + qh * 192;
+    if (!rp) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = d.qk_norm ? x[e] * (g[e] * a) : x[e];
+      uint2 v;
+      v.x = f32_to_bf16(y[0] * qs) | ((uint32_t)f32_to_bf16(y[1] * qs) << 16);
+      v.y = f32_to_bf16(y[2] * qs) | ((uint32_t)f32_to_bf16(y[3] * qs) << 16);
+      *(uint2*)(out + 4 * j) = v;
     } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = x[e];
+      float x0 = x[0], x1 = x[1];
+      if (d.qk_norm) {
+        x0 *= g[0] * ar;
+        x1 *= g[1] * ar;
+      }
+      *(uint32_t*)(out + 128 + 2 * j) = f32_to_bf16((x0 * cs - x1 * sn) * qs) |
+                                        ((uint32_t)f32_to_bf16((x0 * sn + x1 * cs) * qs) << 16);
     }
-    uint2 v;
-    v.x = f32_to_bf16(y[0] * qs) | ((uint32_t)f32_to_bf16(y[1] * qs) << 16);
-    v.y = f32_to_bf16(y[2] * qs) | ((uint32_t)f32_to_bf16(y[3] * qs) << 16);
-    *(uint2*)(out + 4 * j) = v;
-  } else {
-    float x0 = x[0], x1 = x[1];
-    if (d.qk_norm) {
-      x0 *= gqr[2 * j] * ar;
-      x1 *= gqr[2 * j + 1] * ar;
-    }
-    float cs, sn;
-    rope_at(d, d.rpos[row], j, &cs, &sn);
-    *(uint32_t*)(out + 128 + 2 * j) = f32_to_bf16((x0 * cs - x1 * sn) * qs) |
-                                      ((uint32_t)f32_to_bf16((x0 * sn + x1 * cs) * qs) << 16);
   }
 }
 
@@ -621,73 +637,83 @@ __global__ __launch_bounds__(256) void q_norm_bwd_kernel(
 
 // The same for the MFMA attention's shape (bf16, d_c = 128, d_r = 64), with
 // vector accesses: lanes 0..31 take four content dims each, lanes 32..63 one
-// RoPE pair each.  Needs q_c 8-byte, q_rope 4-byte, gamma_q and d_q_c
-// 16-byte and d_q_rope 8-byte aligned (checked by the launcher).
+// RoPE pair each; a wave takes kMfHeads heads of one row, with all of their
+// loads in flight together.  Needs q_c and q_rope 4-byte, both gammas and
+// d_q_rope 8-byte and d_q_c 16-byte aligned (checked by the launcher).
 __global__ __launch_bounds__(256) void q_norm_bwd_mf_kernel(
     TrainDims d, const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ q_rope,
     const float* __restrict__ gq, const float* __restrict__ gqr, const float* __restrict__ aq,
     const float* __restrict__ aqr, float* __restrict__ dQh, float* __restrict__ d_q_c,
     float* __restrict__ d_q_rope) {
   const size_t row = blockIdx.x;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (h >= d.H) return;
-  const size_t qh = row * d.H + h;
+  const int lane = threadIdx.x & 63;
+  const int h0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kMfHeads;
+  if (h0 >= d.H) return;
+  const int nh = min(kMfHeads, d.H - h0);
   const bool rp = lane >= 32;
   const int j = lane & 31;
-  float* dy = dQh + qh * 192;
-  float y[4], x[4];
-  if (!rp) {
-    const f32x4 v = *(const f32x4*)(dy + 4 * j);
-    const uint2 xv = *(const uint2*)(q_c + qh * 128 + 4 * j);
+  f32x4 dyv[kMfHeads];
+  uint2 xv[kMfHeads];
+  float sc[kMfHeads], sr[kMfHeads];
+  // Branch-free loads (a RoPE lane reads its pair twice) so that the loads of
+  // all kMfHeads heads stay in flight together.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = v[e];
-    x[0] = __uint_as_float(xv.x << 16);
-    x[1] = __uint_as_float(xv.x & 0xFFFF0000u);
-    x[2] = __uint_as_float(xv.y << 16);
-    x[3] = __uint_as_float(xv.y & 0xFFFF0000u);
-  } else {
-    // turn the RoPE-part gradient back (transposed rotation) and keep it in
-    // dQ^ for the gamma reduction
-    const float2 v = *(const float2*)(dy + 128 + 2 * j);
-    float cs, sn;
-    rope_at(d, d.rpos[row], j, &cs, &sn);
-    y[0] = v.x * cs + v.y * sn;
-    y[1] = -v.x * sn + v.y * cs;
-    y[2] = y[3] = 0.f;
-    *(float2*)(dy + 128 + 2 * j) = make_float2(y[0], y[1]);
-    const uint32_t xv = *(const uint32_t*)(q_rope + qh * 64 + 2 * j);
-    x[0] = __uint_as_float(xv << 16);
-    x[1] = __uint_as_float(xv & 0xFFFF0000u);
-    x[2] = x[3] = 0.f;
+  for (int u = 0; u < kMfHeads; ++u) {
+    const size_t qh = row * d.H + h0 + (u < nh ? u : 0);
+    const float2* py = (const float2*)(dQh + qh * 192 + (rp ? 128 + 2 * j : 4 * j));
+    const float2 y0 = py[0], y1 = py[rp ? 0 : 1];
+    dyv[u] = rp ? f32x4{y0.x, y0.y, 0.f, 0.f} : f32x4{y0.x, y0.y, y1.x, y1.y};
+    const uint32_t* px = rp ? (const uint32_t*)(q_rope + qh * 64 + 2 * j)
+                            : (const uint32_t*)(q_c + qh * 128 + 4 * j);
+    const uint32_t x0 = px[0], x1 = px[rp ? 0 : 1];
+    xv[u] = make_uint2(x0, rp ? 0u : x1);
+    sc[u] = aq[qh];
+    sr[u] = aqr[qh];
   }
-  if (!d.qk_norm) {
-    if (!rp) *(f32x4*)(d_q_c + qh * 128 + 4 * j) = f32x4{y[0], y[1], y[2], y[3]};
-    else *(float2*)(d_q_rope + qh * 64 + 2 * j) = make_float2(y[0], y[1]);
-    return;
-  }
-  float g[4];
-  if (!rp) {
-    const f32x4 gv = *(const f32x4*)(gq + 4 * j);
+  const float2* pg = rp ? (const float2*)(gqr + 2 * j) : (const float2*)(gq + 4 * j);
+  const float2 g0 = pg[0], g1 = pg[rp ? 0 : 1];
+  const float g[4] = {g0.x, g0.y, rp ? 0.f : g1.x, rp ? 0.f : g1.y};
+  float cs = 1.f, sn = 0.f;
+  if (rp) rope_at(d, d.rpos[row], j, &cs, &sn);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) g[e] = gv[e];
-  } else {
-    g[0] = gqr[2 * j];
-    g[1] = gqr[2 * j + 1];
-    g[2] = g[3] = 0.f;
-  }
-  float sp = 0.f;
+  for (int u = 0; u < kMfHeads; ++u) {
+    if (u >= nh) break;
+    const size_t qh = row * d.H + h0 + u;
+    float y[4], x[4];
+    if (!rp) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) sp += g[e] * y[e] * x[e];
-  const float sc = wave_sum(rp ? 0.f : sp), sr = wave_sum(rp ? sp : 0.f);
-  const float a = rp ? aqr[qh] : aq[qh];
-  const float k = a * a * a * (rp ? sr / 64.f : sc / 128.f);
-  if (!rp)
-    *(f32x4*)(d_q_c + qh * 128 + 4 * j) =
-        f32x4{a * g[0] * y[0] - x[0] * k, a * g[1] * y[1] - x[1] * k, a * g[2] * y[2] - x[2] * k,
-              a * g[3] * y[3] - x[3] * k};
-  else
-    *(float2*)(d_q_rope + qh * 64 + 2 * j) =
-        make_float2(a * g[0] * y[0] - x[0] * k, a * g[1] * y[1] - x[1] * k);
+      for (int e = 0; e < 4; ++e) y[e] = dyv[u][e];
+    } else {
+      // turn the RoPE-part gradient back (transposed rotation) and keep it in
+      // dQ^ for the gamma reduction
+      y[0] = dyv[u][0] * cs + dyv[u][1] * sn;
+      y[1] = -dyv[u][0] * sn + dyv[u][1] * cs;
+      y[2] = y[3] = 0.f;
+      *(float2*)(dQh + qh * 192 + 128 + 2 * j) = make_float2(y[0], y[1]);
+    }
+    x[0] = __uint_as_float(xv[u].x << 16);
+    x[1] = __uint_as_float(xv[u].x & 0xFFFF0000u);
+    x[2] = __uint_as_float(xv[u].y << 16);
+    x[3] = __uint_as_float(xv[u].y & 0xFFFF0000u);
+    if (!d.qk_norm) {
+      if (!rp) *(f32x4*)(d_q_c + qh * 128 + 4 * j) = f32x4{y[0], y[1], y[2], y[3]};
+      else *(float2*)(d_q_rope + qh * 64 + 2 * j) = make_float2(y[0], y[1]);
+      continue;
+    }
+    float sp = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sp += g[e] * y[e] * x[e];
+    const float tc = wave_sum(rp ? 0.f : sp), tr = wave_sum(rp ? sp : 0.f);
+    const float a = rp ? sr[u] : sc[u];
+    const float k = a * a * a * (rp ? tr / 64.f : tc / 128.f);
+    if (!rp)
+      *(f32x4*)(d_q_c + qh * 128 + 4 * j) =
+          f32x4{a * g[0] * y[0] - x[0] * k, a * g[1] * y[1] - x[1] * k,
+                a * g[2] * y[2] - x[2] * k, a * g[3] * y[3] - x[3] * k};
+    else
+      *(float2*)(d_q_rope + qh * 64 + 2 * j) =
+          make_float2(a * g[0] * y[0] - x[0] * k, a * g[1] * y[1] - x[1] * k);
+  }
 }
 
 // ---- backward: key norms and the shared RoPE key -------------------------------------
@@ -1048,11 +1074,12 @@ static void launch_prep_q(const TrainDims& d, const TrainPtrs& in, const TrainWs
                           hipStream_t s) {
   if constexpr (MF) {
     if (d.dc == 128 && d.dr == 64 &&
-        (((uintptr_t)in.q_c & 7) | ((uintptr_t)in.q_rope & 3) | ((uintptr_t)in.gamma_q & 15)) ==
-            0) {
-      hipLaunchKernelGGL(prep_q_mf_kernel, dim3(d.n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
-                         (const uint16_t*)in.q_c, (const uint16_t*)in.q_rope, in.gamma_q,
-                         in.gamma_q_rope, WS(uint16_t, Qb), WS(float, aq), WS(float, aqr));
+        (((uintptr_t)in.q_c & 3) | ((uintptr_t)in.q_rope & 3) | ((uintptr_t)in.gamma_q & 7) |
+         ((uintptr_t)in.gamma_q_rope & 7)) == 0) {
+      const dim3 grid(d.n_rows, (d.H + 4 * kMfHeads - 1) / (4 * kMfHeads));
+      hipLaunchKernelGGL(prep_q_mf_kernel, grid, dim3(256), 0, s, d, (const uint16_t*)in.q_c,
+                         (const uint16_t*)in.q_rope, in.gamma_q, in.gamma_q_rope,
+                         WS(uint16_t, Qb), WS(float, aq), WS(float, aqr));
       return;
     }
   }
@@ -1191,9 +1218,11 @@ static hipError_t backward_impl(const Cfg& c, const TrainSeqs& q, const TrainPtr
                        WS(float, dKh), WS(float, dV));
   }
   if (mf && d.dc == 128 && d.dr == 64 &&
-      (((uintptr_t)in.q_c & 7) | ((uintptr_t)in.q_rope & 3) | ((uintptr_t)in.gamma_q & 15) |
-       ((uintptr_t)gr.d_q_c & 15) | ((uintptr_t)gr.d_q_rope & 7)) == 0)
-    hipLaunchKernelGGL(q_norm_bwd_mf_kernel, dim3(n_rows, (d.H + 3) / 4), dim3(256), 0, s, d,
+      (((uintptr_t)in.q_c & 3) | ((uintptr_t)in.q_rope & 3) | ((uintptr_t)in.gamma_q & 7) |
+       ((uintptr_t)in.gamma_q_rope & 7) | ((uintptr_t)gr.d_q_c & 15) |
+       ((uintptr_t)gr.d_q_rope & 7)) == 0)
+    hipLaunchKernelGGL(q_norm_bwd_mf_kernel,
+                       dim3(n_rows, (d.H + 4 * kMfHeads - 1) / (4 * kMfHeads)), dim3(256), 0, s, d,
                        (const uint16_t*)in.q_c, (const uint16_t*)in.q_rope, in.gamma_q,
                        in.gamma_q_rope, WS(const float, aq), WS(const float, aqr), WS(float, dQh),
                        gr.d_q_c, gr.d_q_rope);

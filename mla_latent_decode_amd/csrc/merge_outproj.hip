@@ -218,79 +218,100 @@ __global__ __launch_bounds__(256) void out_proj_kernel(const float* __restrict__
   }
 }
 
-// bf16 weights, 16 heads per KV group: one block per (b, g, 128 outputs),
-// o[16 heads][128] = o_lat[16][r] . W^UV_g[r][128] on mfma_f32_16x16x32_bf16
-// (o_lat rounded to bf16 for the A operand, fp32 accumulation).  Wave w owns
-// outputs 32w..32w+31 (two 16-wide blocks).  W^UV_g is staged through LDS in
-// chunks of 128 rows and read with ds_read_b64_tr_b16, which turns its
-// row-major [k][n] layout into the k-contiguous B operand: in each 16-lane
-// group, lane i receives element i%4 of the 8-byte loads of lanes 4e + i/4, so
-// lane 4e + q reads row k0+e, columns 4q..4q+3, and lane i ends with rows
-// k0..k0+3 of column i.
+// bf16 weights, 16 heads per KV group: one block per (b, g, 32 outputs),
+// o[16 heads][32] = o_lat[16][r] . W^UV_g[r][32 columns] on
+// mfma_f32_16x16x32_bf16 (o_lat rounded to bf16 for the A operand, fp32
+// accumulation).  Wave w takes the K range [w r/4, (w+1) r/4): it stages its
+// own 128 x 32 slice of W^UV_g in LDS (every load in flight at once), reads it
+// back with ds_read_b64_tr_b16, which turns the row-major [k][n] layout into
+// the k-contiguous B operand (in each 16-lane group lane i receives element
+// i%4 of the 8-byte loads of lanes 4e + i/4, so lane 4e + q reads row k0+e,
+// columns 4q..4q+3, and lane i ends with rows k0..k0+3 of column i), and the
+// four partial sums meet in LDS in a fixed order.  Many small blocks: the
+// projection of one sequence is a few hundred KB of weights, and spreading it
+// over 4 G workgroups keeps each one's load to one round trip.
 // Layouts (gfx950, 16x16x32): A lane l holds A[m=l%16][k=8(l/16)+j], B lane l
 // holds B[k=8(l/16)+j][n=l%16], D lane l reg i holds D[4(l/16)+i][l%16].
-constexpr int kOpChunkK = 128;
-constexpr int kOpChunkN = 128;
+constexpr int kOpK = 128;    // K rows per wave (r = 4 kOpK = 512)
+constexpr int kOpN = 32;     // output columns per block
 
 __global__ __launch_bounds__(256) void out_proj_mfma_kernel(const float* __restrict__ o_lat,
                                                             const uint16_t* __restrict__ w_uv,
                                                             float* __restrict__ out, int H,
                                                             int r, int dv) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[kOpChunkK][kOpChunkN];  // 32 KB
-  const int b = blockIdx.x, g = blockIdx.y, n0 = blockIdx.z * kOpChunkN;
+  __shared__ __attribute__((aligned(16))) uint16_t wt[4][kOpK][kOpN];  // 32 KB
+  __shared__ f32x4 red[3][2][64];
+  const int b = blockIdx.x, g = blockIdx.y, n0 = blockIdx.z * kOpN;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h0 = g * 16;
   const int m = lane & 15, kq = lane >> 4;
+  const int kw = wave * kOpK;  // this wave's first K row
   const uint16_t* W = w_uv + (size_t)g * r * dv;
-  const float* A = o_lat + ((size_t)b * H + h0 + m) * r;
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  const int e = (lane & 15) >> 2, q = lane & 3;
-  for (int k0 = 0; k0 < r; k0 += kOpChunkK) {
-    // stage rows k0..k0+127, columns n0..n0+127 (zero past d_v): 16 B per
-    // thread and step, 8 steps
-    for (int i = tid; i < kOpChunkK * (kOpChunkN / 8); i += 256) {
-      const int row = i / (kOpChunkN / 8), c8 = (i % (kOpChunkN / 8)) * 8;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (n0 + c8 < dv) v = *(const uint4*)(W + (size_t)(k0 + row) * dv + n0 + c8);
-      *(uint4*)&wt[row][c8] = v;
-    }
-    __syncthreads();
+  const float* A = o_lat + ((size_t)b * H + h0 + m) * r + kw;
+  // the wave's slice: 128 rows x 4 chunks of 16 B = 512 chunks, 8 per lane
+  uint4 v[8];
 #pragma unroll
-    for (int ks = 0; ks < kOpChunkK / 32; ++ks) {
-      const float* ap = A + k0 + ks * 32 + kq * 8;
-      const f32x4 a0 = *(const f32x4*)ap, a1 = *(const f32x4*)(ap + 4);
-      const bf16x8 av = {(__bf16)a0[0], (__bf16)a0[1], (__bf16)a0[2], (__bf16)a0[3],
-                         (__bf16)a1[0], (__bf16)a1[1], (__bf16)a1[2], (__bf16)a1[3]};
+  for (int u = 0; u < 8; ++u) {
+    const int c = lane + 64 * u, row = c >> 2, c8 = (c & 3) * 8;
+    v[u] = n0 + c8 < dv ? *(const uint4*)(W + (size_t)(kw + row) * dv + n0 + c8)
+                        : make_uint4(0u, 0u, 0u, 0u);
+  }
+  f32x4 a[kOpK / 32][2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = wave * 32 + nb * 16 + 4 * q;
-        const int row = ks * 32 + kq * 8 + e;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &wt[row][col]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &wt[row + 4][col]));
-        const bf16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nb], 0, 0, 0);
-      }
-    }
-    __syncthreads();  // every wave is done with the chunk before it is overwritten
+  for (int ks = 0; ks < kOpK / 32; ++ks) {
+    a[ks][0] = *(const f32x4*)(A + ks * 32 + kq * 8);
+    a[ks][1] = *(const f32x4*)(A + ks * 32 + kq * 8 + 4);
   }
 #pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = lane + 64 * u, row = c >> 2, c8 = (c & 3) * 8;
+    *(uint4*)&wt[wave][row][c8] = v[u];
+  }
+  __syncthreads();
+  const int e = (lane & 15) >> 2, q = lane & 3;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < kOpK / 32; ++ks) {
+    const f32x4 a0 = a[ks][0], a1 = a[ks][1];
+    const bf16x8 av = {(__bf16)a0[0], (__bf16)a0[1], (__bf16)a0[2], (__bf16)a0[3],
+                       (__bf16)a1[0], (__bf16)a1[1], (__bf16)a1[2], (__bf16)a1[3]};
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = nb * 16 + 4 * q;
+      const int row = ks * 32 + kq * 8 + e;
+      const bf16x4 lo =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &wt[wave][row][col]));
+      const bf16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16(QK_LDS(bf16x4, &wt[wave][row + 4][col]));
+      const bf16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nb], 0, 0, 0);
+    }
+  }
+  if (wave > 0) {
+    red[wave - 1][0][lane] = acc[0];
+    red[wave - 1][1][lane] = acc[1];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + wave * 32 + nb * 16 + m;
+    const f32x4 t = ((acc[nb] + red[0][nb][lane]) + red[1][nb][lane]) + red[2][nb][lane];
+    const int n = n0 + nb * 16 + m;
     if (n < dv) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[((size_t)b * H + h0 + 4 * kq + i) * dv + n] = acc[nb][i];
+      for (int i = 0; i < 4; ++i) out[((size_t)b * H + h0 + 4 * kq + i) * dv + n] = t[i];
     }
   }
 }
 
 bool out_proj_uses_mfma(const Cfg& c) {
-  return c.dtype == QKMLA_BF16 && c.hpg == 16 && c.r % kOpChunkK == 0 && c.dv % 16 == 0;
+  return c.dtype == QKMLA_BF16 && c.hpg == 16 && c.r == 4 * kOpK && c.dv % 16 == 0;
 }
 
 hipError_t launch_out_proj(const Cfg& c, int batch, const float* o_lat, const void* w_uv,
                            float* out, hipStream_t s) {
   if (out_proj_uses_mfma(c)) {
-    out_proj_mfma_kernel<<<dim3(batch, c.G, (c.dv + kOpChunkN - 1) / kOpChunkN), 256, 0, s>>>(
+    out_proj_mfma_kernel<<<dim3(batch, c.G, (c.dv + kOpN - 1) / kOpN), 256, 0, s>>>(
         o_lat, (const uint16_t*)w_uv, out, c.H, c.r, c.dv);
   } else if (c.dtype == QKMLA_BF16)
     out_proj_kernel<uint16_t><<<dim3(batch, c.H), 256, 0, s>>>(o_lat, (const uint16_t*)w_uv, out,

@@ -196,12 +196,38 @@ __global__ __launch_bounds__(256) void prep_q_kernel(TrainDims d, const T* __res
 }
 
 // The same for the MFMA attention's shape (bf16, d_c = 128, d_r = 64), with
-// vector accesses: lanes 0..31 take four content dims each, lanes 32..63 one
-// RoPE pair each.  A wave takes kMfHeads heads of one row, with all of their
-// loads in flight together; the gammas, position and rotation are loaded
-// once per wave.  Needs q_c and q_rope 4-byte and both gammas 8-byte
-// aligned (checked by the launcher).
+// 16-byte accesses.  A wave takes kMfHeads = 8 heads of one row: lane l holds
+// content dims 8(l%16)..8(l%16)+7 of heads l/16 and 4 + l/16, and RoPE dims
+// 8(l%8)..8(l%8)+7 (four pairs) of head l/8, so every load and store moves
+// 16 bytes per lane and the RMS sums close within 16- and 8-lane groups.  The
+// gammas and the rotation of the row's position are loaded once per wave.
+// Needs q_c, q_rope and both gammas 16-byte aligned (checked by the launcher).
 constexpr int kMfHeads = 8;  // heads per wave of the vector row kernels
+
+__device__ __forceinline__ void bf16x8_to_f32(uint4 v, float* x) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 f32_to_bf16x8(const float* y) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = f32_to_bf16(y[2 * i]) | ((uint32_t)f32_to_bf16(y[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Sum over aligned groups of `width` lanes (a power of two up to 16).
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < WIDTH; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 
 __global__ __launch_bounds__(256) void prep_q_mf_kernel(TrainDims d,
                                                         const uint16_t* __restrict__ q_c,
@@ -211,75 +237,74 @@ __global__ __launch_bounds__(256) void prep_q_mf_kernel(TrainDims d,
                                                         uint16_t* __restrict__ Qb,
                                                         float* __restrict__ aq,
                                                         float* __restrict__ aqr) {
+  static_assert(kMfHeads == 8, "the lane map covers eight heads");
   const size_t row = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int h0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kMfHeads;
   if (h0 >= d.H) return;
-  const int nh = min(kMfHeads, d.H - h0);
-  const bool rp = lane >= 32;
-  const int j = lane & 31;
-  // Branch-free loads (two dwords per lane; a RoPE lane reads its pair twice)
-  // so that the loads of all kMfHeads heads stay in flight together.
-  uint2 raw[kMfHeads];
+  const int c16 = lane & 15, c8 = lane & 7;
+  const size_t qa = row * d.H + h0 + (lane >> 4);  // content head of the first load
+  const size_t qr = row * d.H + h0 + (lane >> 3);  // RoPE head
+  const uint4 va = *(const uint4*)(q_c + qa * 128 + 8 * c16);
+  const uint4 vb = *(const uint4*)(q_c + (qa + 4) * 128 + 8 * c16);
+  const uint4 vr = *(const uint4*)(q_rope + qr * 64 + 8 * c8);
+  float g[8], gr[8];
 #pragma unroll
-  for (int u = 0; u < kMfHeads; ++u) {
-    const size_t qh = row * d.H + h0 + (u < nh ? u : 0);
-    const uint32_t* p0 = rp ? (const uint32_t*)(q_rope + qh * 64 + 2 * j)
-                            : (const uint32_t*)(q_c + qh * 128 + 4 * j);
-    const uint32_t v0 = p0[0], v1 = p0[rp ? 0 : 1];
-    raw[u] = make_uint2(v0, rp ? 0u : v1);
-  }
-  float g[4] = {1.f, 1.f, 1.f, 1.f};
+  for (int i = 0; i < 8; ++i) g[i] = gr[i] = 1.f;
   if (d.qk_norm) {
-    const float2* pg = rp ? (const float2*)(gqr + 2 * j) : (const float2*)(gq + 4 * j);
-    const float2 g0 = pg[0], g1 = pg[rp ? 0 : 1];
-    g[0] = g0.x;
-    g[1] = g0.y;
-    g[2] = g1.x;
-    g[3] = g1.y;
+    const f32x4 g0 = *(const f32x4*)(gq + 8 * c16), g1 = *(const f32x4*)(gq + 8 * c16 + 4);
+    const f32x4 r0 = *(const f32x4*)(gqr + 8 * c8), r1 = *(const f32x4*)(gqr + 8 * c8 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      g[i] = g0[i];
+      g[4 + i] = g1[i];
+      gr[i] = r0[i];
+      gr[4 + i] = r1[i];
+    }
   }
-  float cs = 1.f, sn = 0.f;
-  if (rp) rope_at(d, d.rpos[row], j, &cs, &sn);
+  // rotation of pairs 4 c8 .. 4 c8 + 3 at the row's position
+  const float4* cs4 = (const float4*)(d.rope_cs + (size_t)d.rpos[row] * 32 + 4 * c8);
+  const float4 t0 = cs4[0], t1 = cs4[1];
+  const float cs[4] = {t0.x, t0.z, t1.x, t1.z}, sn[4] = {t0.y, t0.w, t1.y, t1.w};
   const float qs = d.tau * kLog2e;
+  float x[8], y[8];
+  // content, heads h0 + l/16 and h0 + 4 + l/16
 #pragma unroll
-  for (int u = 0; u < kMfHeads; ++u) {
-    if (u >= nh) break;
-    const size_t qh = row * d.H + h0 + u;
-    float x[4];
-    x[0] = __uint_as_float(raw[u].x << 16);
-    x[1] = __uint_as_float(raw[u].x & 0xFFFF0000u);
-    x[2] = __uint_as_float(raw[u].y << 16);
-    x[3] = __uint_as_float(raw[u].y & 0xFFFF0000u);
-    float a = 1.f, ar = 1.f;
+  for (int half = 0; half < 2; ++half) {
+    bf16x8_to_f32(half ? vb : va, x);
+    float a = 1.f;
     if (d.qk_norm) {
-      const float sq = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-      const float ss = wave_sum(rp ? 0.f : sq), sr = wave_sum(rp ? sq : 0.f);
-      a = 1.0f / sqrtf(ss / 128.f + d.eps);
-      ar = 1.0f / sqrtf(sr / 64.f + d.eps);
-      if (lane == 0) {
-        aq[qh] = a;
-        aqr[qh] = ar;
-      }
-    }
-    uint16_t* out = Qb + qh * 192;
-    if (!rp) {
-      float y[4];
+      float sq = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = d.qk_norm ? x[e] * (g[e] * a) : x[e];
-      uint2 v;
-      v.x = f32_to_bf16(y[0] * qs) | ((uint32_t)f32_to_bf16(y[1] * qs) << 16);
-      v.y = f32_to_bf16(y[2] * qs) | ((uint32_t)f32_to_bf16(y[3] * qs) << 16);
-      *(uint2*)(out + 4 * j) = v;
-    } else {
-      float x0 = x[0], x1 = x[1];
-      if (d.qk_norm) {
-        x0 *= g[0] * ar;
-        x1 *= g[1] * ar;
-      }
-      *(uint32_t*)(out + 128 + 2 * j) = f32_to_bf16((x0 * cs - x1 * sn) * qs) |
-                                        ((uint32_t)f32_to_bf16((x0 * sn + x1 * cs) * qs) << 16);
+      for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
+      a = 1.0f / sqrtf(group_sum<16>(sq) / 128.f + d.eps);
+      if (c16 == 0) aq[qa + 4 * half] = a;
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (d.qk_norm ? x[e] * (g[e] * a) : x[e]) * qs;
+    *(uint4*)(Qb + (qa + 4 * half) * 192 + 8 * c16) = f32_to_bf16x8(y);
   }
+  // RoPE part, head h0 + l/8
+  bf16x8_to_f32(vr, x);
+  float ar = 1.f;
+  if (d.qk_norm) {
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
+    ar = 1.0f / sqrtf(group_sum<8>(sq) / 64.f + d.eps);
+    if (c8 == 0) aqr[qr] = ar;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x0 = x[2 * i], x1 = x[2 * i + 1];
+    if (d.qk_norm) {
+      x0 *= gr[2 * i] * ar;
+      x1 *= gr[2 * i + 1] * ar;
+    }
+    y[2 * i] = (x0 * cs[i] - x1 * sn[i]) * qs;
+    y[2 * i + 1] = (x0 * sn[i] + x1 * cs[i]) * qs;
+  }
+  *(uint4*)(Qb + qr * 192 + 128 + 8 * c8) = f32_to_bf16x8(y);
 }
 
 // ---- forward: keys and values -----------------------------------------------
@@ -1073,9 +1098,9 @@ template <typename T, bool MF>
 static void launch_prep_q(const TrainDims& d, const TrainPtrs& in, const TrainWs& ws, char* wsb,
                           hipStream_t s) {
   if constexpr (MF) {
-    if (d.dc == 128 && d.dr == 64 &&
-        (((uintptr_t)in.q_c & 3) | ((uintptr_t)in.q_rope & 3) | ((uintptr_t)in.gamma_q & 7) |
-         ((uintptr_t)in.gamma_q_rope & 7)) == 0) {
+    if (d.dc == 128 && d.dr == 64 && d.H % kMfHeads == 0 &&
+        (((uintptr_t)in.q_c | (uintptr_t)in.q_rope | (uintptr_t)in.gamma_q |
+          (uintptr_t)in.gamma_q_rope) & 15) == 0) {
       const dim3 grid(d.n_rows, (d.H + 4 * kMfHeads - 1) / (4 * kMfHeads));
       hipLaunchKernelGGL(prep_q_mf_kernel, grid, dim3(256), 0, s, d, (const uint16_t*)in.q_c,
                          (const uint16_t*)in.q_rope, in.gamma_q, in.gamma_q_rope,

@@ -661,84 +661,103 @@ __global__ __launch_bounds__(256) void q_norm_bwd_kernel(
 }
 
 // The same for the MFMA attention's shape (bf16, d_c = 128, d_r = 64), with
-// vector accesses: lanes 0..31 take four content dims each, lanes 32..63 one
-// RoPE pair each; a wave takes kMfHeads heads of one row, with all of their
-// loads in flight together.  Needs q_c and q_rope 4-byte, both gammas and
-// d_q_rope 8-byte and d_q_c 16-byte aligned (checked by the launcher).
+// 16-byte accesses and the lane map of prep_q_mf_kernel: lane l holds content
+// dims 8(l%16)..+7 of heads l/16 and 4 + l/16 and RoPE dims 8(l%8)..+7 of
+// head l/8 of the wave's kMfHeads heads.  Needs q_c, q_rope, both gammas,
+// d_q_c and d_q_rope 16-byte aligned (checked by the launcher).
 __global__ __launch_bounds__(256) void q_norm_bwd_mf_kernel(
     TrainDims d, const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ q_rope,
     const float* __restrict__ gq, const float* __restrict__ gqr, const float* __restrict__ aq,
     const float* __restrict__ aqr, float* __restrict__ dQh, float* __restrict__ d_q_c,
     float* __restrict__ d_q_rope) {
+  static_assert(kMfHeads == 8, "the lane map covers eight heads");
   const size_t row = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int h0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * kMfHeads;
   if (h0 >= d.H) return;
-  const int nh = min(kMfHeads, d.H - h0);
-  const bool rp = lane >= 32;
-  const int j = lane & 31;
-  f32x4 dyv[kMfHeads];
-  uint2 xv[kMfHeads];
-  float sc[kMfHeads], sr[kMfHeads];
-  // Branch-free loads (a RoPE lane reads its pair twice) so that the loads of
-  // all kMfHeads heads stay in flight together.
+  const int c16 = lane & 15, c8 = lane & 7;
+  const size_t qa = row * d.H + h0 + (lane >> 4);  // content heads qa, qa + 4
+  const size_t qr = row * d.H + h0 + (lane >> 3);  // RoPE head
+  f32x4 dy[2][2], dr[2];
+  uint4 xc[2];
 #pragma unroll
-  for (int u = 0; u < kMfHeads; ++u) {
-    const size_t qh = row * d.H + h0 + (u < nh ? u : 0);
-    const float2* py = (const float2*)(dQh + qh * 192 + (rp ? 128 + 2 * j : 4 * j));
-    const float2 y0 = py[0], y1 = py[rp ? 0 : 1];
-    dyv[u] = rp ? f32x4{y0.x, y0.y, 0.f, 0.f} : f32x4{y0.x, y0.y, y1.x, y1.y};
-    const uint32_t* px = rp ? (const uint32_t*)(q_rope + qh * 64 + 2 * j)
-                            : (const uint32_t*)(q_c + qh * 128 + 4 * j);
-    const uint32_t x0 = px[0], x1 = px[rp ? 0 : 1];
-    xv[u] = make_uint2(x0, rp ? 0u : x1);
-    sc[u] = aq[qh];
-    sr[u] = aqr[qh];
+  for (int half = 0; half < 2; ++half) {
+    const float* p = dQh + (qa + 4 * half) * 192 + 8 * c16;
+    dy[half][0] = *(const f32x4*)p;
+    dy[half][1] = *(const f32x4*)(p + 4);
+    xc[half] = *(const uint4*)(q_c + (qa + 4 * half) * 128 + 8 * c16);
   }
-  const float2* pg = rp ? (const float2*)(gqr + 2 * j) : (const float2*)(gq + 4 * j);
-  const float2 g0 = pg[0], g1 = pg[rp ? 0 : 1];
-  const float g[4] = {g0.x, g0.y, rp ? 0.f : g1.x, rp ? 0.f : g1.y};
-  float cs = 1.f, sn = 0.f;
-  if (rp) rope_at(d, d.rpos[row], j, &cs, &sn);
+  float* pr = dQh + qr * 192 + 128 + 8 * c8;
+  dr[0] = *(const f32x4*)pr;
+  dr[1] = *(const f32x4*)(pr + 4);
+  const uint4 xr = *(const uint4*)(q_rope + qr * 64 + 8 * c8);
+  const float a_c[2] = {aq[qa], aq[qa + 4]}, a_r = aqr[qr];
+  float g[8], gr[8];
+  {
+    const f32x4 g0 = *(const f32x4*)(gq + 8 * c16), g1 = *(const f32x4*)(gq + 8 * c16 + 4);
+    const f32x4 r0 = *(const f32x4*)(gqr + 8 * c8), r1 = *(const f32x4*)(gqr + 8 * c8 + 4);
 #pragma unroll
-  for (int u = 0; u < kMfHeads; ++u) {
-    if (u >= nh) break;
-    const size_t qh = row * d.H + h0 + u;
-    float y[4], x[4];
-    if (!rp) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = dyv[u][e];
-    } else {
-      // turn the RoPE-part gradient back (transposed rotation) and keep it in
-      // dQ^ for the gamma reduction
-      y[0] = dyv[u][0] * cs + dyv[u][1] * sn;
-      y[1] = -dyv[u][0] * sn + dyv[u][1] * cs;
-      y[2] = y[3] = 0.f;
-      *(float2*)(dQh + qh * 192 + 128 + 2 * j) = make_float2(y[0], y[1]);
+    for (int i = 0; i < 4; ++i) {
+      g[i] = g0[i];
+      g[4 + i] = g1[i];
+      gr[i] = r0[i];
+      gr[4 + i] = r1[i];
     }
-    x[0] = __uint_as_float(xv[u].x << 16);
-    x[1] = __uint_as_float(xv[u].x & 0xFFFF0000u);
-    x[2] = __uint_as_float(xv[u].y << 16);
-    x[3] = __uint_as_float(xv[u].y & 0xFFFF0000u);
+  }
+  const float4* cs4 = (const float4*)(d.rope_cs + (size_t)d.rpos[row] * 32 + 4 * c8);
+  const float4 t0 = cs4[0], t1 = cs4[1];
+  const float cs[4] = {t0.x, t0.z, t1.x, t1.z}, sn[4] = {t0.y, t0.w, t1.y, t1.w};
+  float x[8], y[8], o[8];
+  // content: the RMSNorm backward of heads qa and qa + 4
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = dy[half][0][i];
+      y[4 + i] = dy[half][1][i];
+    }
+    float* out = d_q_c + (qa + 4 * half) * 128 + 8 * c16;
     if (!d.qk_norm) {
-      if (!rp) *(f32x4*)(d_q_c + qh * 128 + 4 * j) = f32x4{y[0], y[1], y[2], y[3]};
-      else *(float2*)(d_q_rope + qh * 64 + 2 * j) = make_float2(y[0], y[1]);
+      *(f32x4*)out = dy[half][0];
+      *(f32x4*)(out + 4) = dy[half][1];
       continue;
     }
+    bf16x8_to_f32(xc[half], x);
     float sp = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sp += g[e] * y[e] * x[e];
-    const float tc = wave_sum(rp ? 0.f : sp), tr = wave_sum(rp ? sp : 0.f);
-    const float a = rp ? sr[u] : sc[u];
-    const float k = a * a * a * (rp ? tr / 64.f : tc / 128.f);
-    if (!rp)
-      *(f32x4*)(d_q_c + qh * 128 + 4 * j) =
-          f32x4{a * g[0] * y[0] - x[0] * k, a * g[1] * y[1] - x[1] * k,
-                a * g[2] * y[2] - x[2] * k, a * g[3] * y[3] - x[3] * k};
-    else
-      *(float2*)(d_q_rope + qh * 64 + 2 * j) =
-          make_float2(a * g[0] * y[0] - x[0] * k, a * g[1] * y[1] - x[1] * k);
+    for (int e = 0; e < 8; ++e) sp += g[e] * y[e] * x[e];
+    const float a = a_c[half];
+    const float k = a * a * a * group_sum<16>(sp) / 128.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = a * g[e] * y[e] - x[e] * k;
+    *(f32x4*)out = f32x4{o[0], o[1], o[2], o[3]};
+    *(f32x4*)(out + 4) = f32x4{o[4], o[5], o[6], o[7]};
   }
+  // RoPE part of head qr: turn the gradient back (transposed rotation), keep
+  // it in dQ^ for the gamma reduction, then its RMSNorm backward
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v0 = dr[i >> 1][2 * (i & 1)], v1 = dr[i >> 1][2 * (i & 1) + 1];
+    y[2 * i] = v0 * cs[i] + v1 * sn[i];
+    y[2 * i + 1] = -v0 * sn[i] + v1 * cs[i];
+  }
+  *(f32x4*)pr = f32x4{y[0], y[1], y[2], y[3]};
+  *(f32x4*)(pr + 4) = f32x4{y[4], y[5], y[6], y[7]};
+  float* outr = d_q_rope + qr * 64 + 8 * c8;
+  if (!d.qk_norm) {
+    *(f32x4*)outr = f32x4{y[0], y[1], y[2], y[3]};
+    *(f32x4*)(outr + 4) = f32x4{y[4], y[5], y[6], y[7]};
+    return;
+  }
+  bf16x8_to_f32(xr, x);
+  float sp = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sp += gr[e] * y[e] * x[e];
+  const float k = a_r * a_r * a_r * group_sum<8>(sp) / 64.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = a_r * gr[e] * y[e] - x[e] * k;
+  *(f32x4*)outr = f32x4{o[0], o[1], o[2], o[3]};
+  *(f32x4*)(outr + 4) = f32x4{o[4], o[5], o[6], o[7]};
 }
 
 // ---- backward: key norms and the shared RoPE key -------------------------------------
@@ -1242,10 +1261,9 @@ static hipError_t backward_impl(const Cfg& c, const TrainSeqs& q, const TrainPtr
                        WS(const float, Kh), WS(const float, V), lse, d_o, WS(const float, Dsum),
                        WS(float, dKh), WS(float, dV));
   }
-  if (mf && d.dc == 128 && d.dr == 64 &&
-      (((uintptr_t)in.q_c & 3) | ((uintptr_t)in.q_rope & 3) | ((uintptr_t)in.gamma_q & 7) |
-       ((uintptr_t)in.gamma_q_rope & 7) | ((uintptr_t)gr.d_q_c & 15) |
-       ((uintptr_t)gr.d_q_rope & 7)) == 0)
+  if (mf && d.dc == 128 && d.dr == 64 && d.H % kMfHeads == 0 &&
+      (((uintptr_t)in.q_c | (uintptr_t)in.q_rope | (uintptr_t)in.gamma_q |
+        (uintptr_t)in.gamma_q_rope | (uintptr_t)gr.d_q_c | (uintptr_t)gr.d_q_rope) & 15) == 0)
     hipLaunchKernelGGL(q_norm_bwd_mf_kernel,
                        dim3(n_rows, (d.H + 4 * kMfHeads - 1) / (4 * kMfHeads)), dim3(256), 0, s, d,
                        (const uint16_t*)in.q_c, (const uint16_t*)in.q_rope, in.gamma_q,

@@ -22,11 +22,11 @@ namespace qkmla {
 // running maximum, kMergeBatch at a time with all of their loads in flight;
 // lane l holds 8 / ZD latent dims, one 16 / ZD-byte piece of the source's
 // bf16 O row (r = 512).  The WPH waves of a head meet in LDS.  The host picks
-// WPH so that a wave folds at most kMergeBatch sources, and ZD = 2 when the
+// WPH (at most 8) so that a wave folds about kMergeBatch sources, and ZD = 2 when the
 // sequences and heads alone give fewer blocks than CUs: the kernel's time is
 // then about one round of loads, spread over the whole chip.  The tile prefix
 // of the plan comes from the workspace, where the split-KV kernel left it.
-constexpr int kMergeBatch = 16;    // sources in flight per wave
+constexpr int kMergeBatch = 8;     // sources in flight per wave (8 measured faster than 4 or 16)
 constexpr int kMergeList = 1024;   // sources listed per pass
 
 template <int WPH, int ZD>
@@ -173,8 +173,7 @@ static hipError_t launch_merge_zd(int wph, int nv, int H, int r, int n_wg, const
     case 1: return launch_merge_wph<1, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
     case 2: return launch_merge_wph<2, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
     case 4: return launch_merge_wph<4, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
-    case 8: return launch_merge_wph<8, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
-    default: return launch_merge_wph<16, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
+    default: return launch_merge_wph<8, ZD>(nv, H, r, n_wg, plan, part, o_lat, lse, s);
   }
 }
 
@@ -185,11 +184,12 @@ hipError_t launch_merge(const Cfg& c, int batch, int s_q, const WsLayout& ws, vo
   if (c.r != 8 * 64 || c.H % 4 != 0) return hipErrorInvalidValue;  // one 16-byte piece per lane
   // Sources of a sequence: the workgroups its tiles span, about n_wg / nv + 1
   // when the lengths are even.  WPH = the power of two that gives each wave
-  // about kMergeBatch of them (at most 16 waves per head).
+  // about kMergeBatch of them, at most 8 waves per head (a wave then folds
+  // several batches: at one sequence of 256 workgroups, 4 x 8 sources).
   // (a sequence of exactly n_wg / nv workgroups' tiles has no extra source)
   const int per_seq = n_wg % nv == 0 ? n_wg / nv : n_wg / nv + 2;
   int wph = 1;
-  while (wph < 16 && wph * kMergeBatch < per_seq) wph *= 2;
+  while (wph < 8 && wph * kMergeBatch < per_seq) wph *= 2;
   const int32_t* plan = (const int32_t*)(wsb + ws.plan);
   const char* part = (const char*)(wsb + ws.partials);
   const int heads_per_block = wph < 4 ? 4 / wph : 1;
